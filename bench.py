@@ -1,0 +1,271 @@
+"""Benchmark of the int8-state gated delta-rule decode step on one MI355X.
+
+Workload (the one the headline metric is quoted on): one decode token for
+each of B=64 sequences x H=32 heads, d_k = d_v = 128, window W = 64, bf16
+q/k/v, int8 state (N(0, 0.5) entries quantized per row) and per-sequence
+window fills drawn from U{0..63} holding fp32 (k, v, alpha, beta).
+
+A "step" is one gdnq_decode_step launch over the whole batch.  The state of
+one step (codes, scales, buffer: ~106 MB) fits in the 256 MB Infinity Cache,
+so steps rotate over `--replicas` copies of it (>= 4 by default, ~424 MB)
+and every step reads its state cold from HBM.  Fills advance by one per step
+per replica (f -> f+1, or 0 after a window close), as in a real decode loop.
+
+Prints ONE JSON line.  `value` = tokens/s (B tokens per step); the roofline
+object uses the algorithmic bytes of each launch (computed from the realized
+fills) divided by the measured launch time; `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.  `--prefill` adds the GDN
+and SSD chunked-prefill measurements as secondary objects.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+
+B, H, DK, DV, W = 64, 32, 128, 128, 64
+
+
+def decode_bytes_per_head(f, W=W, dk=DK, dv=DV, e_in=2, e_out=2):
+    """Algorithmic HBM bytes of one decode token for one head with fill f:
+    int8 rows + scales read, f buffered writes read, the token's q, k, v,
+    alpha, beta read, o written, and either the token's write appended
+    (window open) or the requantized rows + scales written (window close)."""
+    rd = dv * dk + 4 * dv + (4 * dk + 4 * dv + 8) * f + e_in * (2 * dk + dv) + 8
+    wr = e_out * dv + ((4 * dk + 4 * dv + 8) if f + 1 < W else (dv * dk + 4 * dv))
+    return rd + wr
+
+
+def decode_bytes(fills, heads=H):
+    per_seq_fill = 8  # fill_in read + fill_out write
+    return int(sum(heads * decode_bytes_per_head(int(f)) + per_seq_fill for f in fills))
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "quantized_recurrent_state_gdnq_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, kernel_sources, per_launch_units):
+    """Measured HBM bytes per launch from a committed rocprofv3 counter summary,
+    or None when the summary is absent or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_hash") != source_hash(*kernel_sources):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline_decode(seconds=12.0):
+    """The CPU oracle on a bounded sample: the first sequences of the same
+    workload, one decode call at a time, until `seconds` have elapsed."""
+    import oracle
+    import workloads as wl
+
+    nseq = 4
+    d = wl.decode_batch(B=nseq, H=H, dk=DK, dv=DV, W=W, seed=0)
+    codes, scales = oracle.quantize_rows(d["state"])
+    bufs = [d["buf_k"], d["buf_v"], d["buf_alpha"], d["buf_beta"]]
+    fill = d["fill"]
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        x = wl.decode_tokens(B=nseq, H=H, dk=DK, dv=DV, step=steps, seed=1)
+        out = oracle.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], codes, scales,
+                                 *bufs, fill, W)
+        _, codes, scales, *bufs, fill = out
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    return {"value": nseq * steps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nseq} of {B} sequences x {H} heads, {steps} consecutive decode steps "
+                      f"({el:.1f} s), numpy fp32 oracle"}
+
+
+def bench_decode(args, torch, ops, wl, rep_count):
+    dev = torch.device("cuda:0")
+    d = wl.decode_batch(B=B, H=H, dk=DK, dv=DV, W=W, seed=0)
+    state = torch.from_numpy(d["state"]).to(dev)
+    codes0, scales0 = ops.quantize_state(state)  # the library's own codec
+    del state
+    reps = []
+    for i in range(rep_count):
+        rep = ops.DecodeState(codes0.clone(), scales0.clone(), W,
+                              fill=torch.from_numpy(d["fill"]).to(dev))
+        rep.buf_k.copy_(torch.from_numpy(d["buf_k"]))
+        rep.buf_v.copy_(torch.from_numpy(d["buf_v"]))
+        rep.buf_alpha.copy_(torch.from_numpy(d["buf_alpha"]))
+        rep.buf_beta.copy_(torch.from_numpy(d["buf_beta"]))
+        reps.append(rep)
+    host_fills = [d["fill"].astype(np.int64).copy() for _ in range(rep_count)]
+    # a small pool of per-step token inputs (bf16 q/k/v, fp32 alpha/beta)
+    pool = []
+    for s in range(4):
+        x = wl.decode_tokens(B=B, H=H, dk=DK, dv=DV, step=s, seed=1)
+        pool.append([torch.from_numpy(x["q"]).to(dev).bfloat16(),
+                     torch.from_numpy(x["k"]).to(dev).bfloat16(),
+                     torch.from_numpy(x["v"]).to(dev).bfloat16(),
+                     torch.from_numpy(x["alpha"]).to(dev), torch.from_numpy(x["beta"]).to(dev)])
+    o = torch.empty((B, H, DV), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        r = i % rep_count
+        reps[r].step(*pool[i % len(pool)], o=o)
+        f = host_fills[r]
+        nbytes = decode_bytes(f)
+        host_fills[r] = np.where(f + 1 == W, 0, f + 1)
+        return nbytes
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    total_bytes = 0
+    e0.record(stream)
+    for i in range(args.warmup, args.warmup + args.steps):
+        total_bytes += step(i)
+    e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_step = ms / args.steps
+    tokens_s = B * args.steps / (ms / 1e3)
+    bytes_launch = total_bytes / args.steps
+    gbps = bytes_launch / (ms_step * 1e-3) / 1e9
+    return {"ms_per_step": ms_step, "tokens_s": tokens_s, "bytes_per_launch": bytes_launch,
+            "gbps": gbps}
+
+
+def bench_prefill(torch, ops, wl, steps=5, warmup=2):
+    """Secondary: GDN chunked prefill B=4, T=8192, H=16, d=128, C=W=64 and
+    SSD prefill B=2, T=4096, H=80, d_k=128, d_v=64 with WHT + int8 q/k."""
+    dev = torch.device("cuda:0")
+    res = {}
+    cases = [
+        ("gdn_prefill", dict(B=4, T=8192, H=16, dk=128, dv=128), False),
+        ("ssd_prefill", dict(B=2, T=4096, H=80, dk=128, dv=64), True),
+    ]
+    for name, shp, ssd in cases:
+        x = (wl.ssd_prefill if ssd else wl.gdn_prefill)(**shp, seed=0)
+        q = torch.from_numpy(x["q"]).to(dev).bfloat16()
+        k = torch.from_numpy(x["k"]).to(dev).bfloat16()
+        v = torch.from_numpy(x["v"]).to(dev).bfloat16()
+        a = torch.from_numpy(x["alpha"]).to(dev)
+        bt = None if ssd else torch.from_numpy(x["beta"]).to(dev)
+        kw = dict(ssd=True, wht=True, int8_qk=True) if ssd else dict(window=64)
+        try:
+            for _ in range(warmup):
+                ops.prefill_chunked(q, k, v, a, bt, **kw)
+        except Exception as e:  # prefill kernels may be unavailable in a partial build
+            res[name] = {"error": str(e)}
+            continue
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            ops.prefill_chunked(q, k, v, a, bt, **kw)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        Bq, T, Hh, dk = q.shape
+        dv = v.shape[-1]
+        toks = Bq * T
+        th = Bq * T * Hh
+        if ssd:
+            flops = th * (4 * dk * dv + 64 * (2 * dk + 2 * dv))
+            nbytes = th * (2 * (2 * dk + dv) + 4 + 2 * dv) + Bq * Hh * dv * dk * 4
+        else:
+            flops = th * (6 * dk * dv + 64 * (6 * dk + 4 * dv))
+            nbytes = th * (2 * (2 * dk + dv) + 8 + 2 * dv) + Bq * Hh * (dv * dk + 4 * dv)
+        res[name] = {"workload": f"B={Bq} T={T} H={Hh} d_k={dk} d_v={dv} C=64",
+                     "ms": ms, "tokens_s": toks / (ms * 1e-3),
+                     "tflops": flops / (ms * 1e-3) / 1e12,
+                     "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                     "gbps": nbytes / (ms * 1e-3) / 1e9,
+                     "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        del q, k, v, a, bt
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--prefill", action="store_true", help="also time the chunked prefills")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on "
+              "one GPU only).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as wl
+    from quantized_recurrent_state_gdnq_amd import ops
+
+    r = bench_decode(args, torch, ops, wl, max(1, args.replicas))
+    traffic = load_traffic("decode_b64_h32_traffic.json", ["decode.hip", "device_common.h"], 1)
+    line = {
+        "metric": "int8-state GDN decode tokens/s + achieved HBM GB/s; prefill tokens/s",
+        "value": round(r["tokens_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"decode step B={B} H={H} d_k=d_v={DK} W={W} bf16 q/k/v, int8 "
+                               f"state, fills U{{0..{W - 1}}}, {args.replicas} state replicas "
+                               "(cold HBM)",
+                   "state": "int8 codes + fp32 per-row scales", "window_buffer": "fp32"},
+        "hbm_gbps": round(r["gbps"], 1),
+        "roofline": {"bound": "hbm", "achieved": round(r["gbps"], 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(r["gbps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(r["bytes_per_launch"])},
+    }
+    if args.prefill:
+        line["prefill"] = bench_prefill(torch, ops, wl)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

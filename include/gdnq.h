@@ -1,0 +1,200 @@
+/*
+ * gdnq.h -- C ABI of the int8-state gated delta-rule (Gated DeltaNet) library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes
+ *   The recurrence (the pages name it; this is the standard gated delta rule)
+ *       S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *       o_t = S_t q_t,                      S in R^{d_v x d_k},
+ *   with the state held as int8 codes plus one fp32 scale per row (a row is
+ *   one v index: d_k codes).  The state is requantized once per window of W
+ *   tokens; inside a window the window's writes (k, v, alpha, beta) are kept
+ *   in fp32 and replayed on top of the dequantized state.
+ *     - "LeapQuant: Efficient Linear Attention with Accurate Recurrent State
+ *       Quantization", abstract: 8-bit recurrent state, per-window
+ *       quantization (quantize once at the window's end; outputs inside the
+ *       window from the fixed low-bit state plus high-precision buffered
+ *       updates).
+ *     - "Low-Bit GDN Recurrent-State Quantization: Global Gradient-aware
+ *       Allocation and Pure-Write Sliding Windows", abstract: buffered writes
+ *       go through the full GDN transition and are merged into the low-bit
+ *       state when they leave the window.
+ *     - "LinQuant: Functional Invariances for Low-Precision Linear
+ *       Recurrences", abstract: chunkwise-parallel prefill as dense matrix
+ *       products; rotations as invariances; SSD (Mamba-2) prefill with
+ *       low-precision operands.
+ *     - "Influence-Inspired Spectral Rotations for Extreme Low-Bit LLM
+ *       Quantization", abstract: the Walsh-Hadamard rotation.
+ *
+ * Codec (all entry points): per row, scale = max|x| / 127 (fp32, IEEE
+ * division); code = clamp(round_half_even(x / scale), -127, 127); a row with
+ * max|x| = 0 gets scale 0 and codes 0.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers, owned by the caller.  The library
+ *     allocates no device memory and keeps no per-call state.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL means the default stream).
+ *   - Arguments are validated on the host before anything is launched.  On any
+ *     status other than GDNQ_OK nothing has been launched and nothing written;
+ *     gdnq_last_error() gives a one-line reason (thread-local).
+ *   - Every pointer must be 16-byte aligned; layouts are dense row-major with
+ *     the innermost dimension listed last.
+ *   - Floating-point data errors (NaN/Inf inputs, ||k|| != 1, beta outside
+ *     [0,1]) are not checked; results are then unspecified.
+ *   - No C++ exception crosses this interface.  Calls are reentrant.
+ *   - Device faults surface on the caller's next synchronisation.
+ */
+#ifndef GDNQ_H
+#define GDNQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDNQ_OK = 0,
+  GDNQ_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  GDNQ_ERR_SHAPE = 2,     /* unsupported size / size combination              */
+  GDNQ_ERR_DTYPE = 3,     /* unsupported dtype code                            */
+  GDNQ_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                  */
+  GDNQ_ERR_ALIAS = 5,     /* an output aliases an input it must not alias      */
+  GDNQ_ERR_WORKSPACE = 6, /* workspace missing or too small                    */
+  GDNQ_ERR_HIP = 7,       /* the HIP runtime refused the launch               */
+  GDNQ_ERR_FLAGS = 8      /* unknown or unsupported flag bits                  */
+} gdnq_status;
+
+/* Element types of q, k, v (in_dtype) and of o (out_dtype). */
+enum { GDNQ_F32 = 0, GDNQ_BF16 = 1 };
+
+/* Flag bits. */
+enum {
+  GDNQ_FLAG_WHT = 1u,     /* rotate q and k by the normalised Walsh-Hadamard
+                             matrix H/sqrt(d_k) (Sylvester order) before use;
+                             the state then lives in the rotated basis S H    */
+  GDNQ_FLAG_SSD = 2u,     /* prefill only: scalar-decay SSD recurrence
+                             S_t = a_t S_{t-1} + v_t k_t^T (no delta term);
+                             state kept in fp32, not quantized                */
+  GDNQ_FLAG_INT8_QK = 4u  /* prefill + SSD only: quantize each token's
+                             (rotated) q and k row to int8 with the codec
+                             above and use the dequantized operands         */
+};
+
+/* ------------------------------------------------------------------------
+ * gdnq_quantize_state -- codec (int8 codes + per-row fp32 scales).
+ *   LeapQuant, abstract (8-bit recurrent state).
+ *
+ *   S       [rows, d_k] fp32, read only
+ *   codes   [rows, d_k] int8, written
+ *   scales  [rows]      fp32, written
+ *   flags   0 or GDNQ_FLAG_WHT (rotate each row x -> H x / sqrt(d_k) first,
+ *           i.e. quantize S H, the state in the rotated basis)
+ *   d_k in {64, 128}; rows >= 0 (rows == 0 is a no-op).
+ *   Errors: NULL (any pointer, rows > 0), SHAPE, ALIGN, FLAGS, HIP.
+ * ------------------------------------------------------------------------ */
+gdnq_status gdnq_quantize_state(const float* S, int64_t rows, int32_t d_k, int8_t* codes,
+                                float* scales, uint32_t flags, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdnq_decode_step -- one token per sequence, per-window quantized state.
+ *   LeapQuant, abstract (per-window quantization; outputs from the low-bit
+ *   state plus buffered high-precision updates); Low-Bit GDN ..., abstract
+ *   (writes propagate through the full transition, merge on window exit).
+ *
+ *   For every sequence b with f = fill_in[b] writes already buffered (the
+ *   same f for all its heads), and every head h:
+ *     S := dequant(codes, scales); replay buffered writes 0..f-1 on S (oldest
+ *     first); apply the current token; o = S q.
+ *     If f + 1 < W: append (k, v, alpha, beta) of the token to slot f of the
+ *       buffer (k in the rotated basis under GDNQ_FLAG_WHT), fill_out[b] = f+1;
+ *       codes and scales are left untouched.
+ *     If f + 1 == W (window closes): codes and scales of the sequence are
+ *       rewritten with the requantized S; fill_out[b] = 0.  Buffer contents
+ *       at slots >= fill_out are unspecified afterwards.
+ *   The output of a closing token uses S before requantization.
+ *
+ *   p->batch B >= 0 (0: no-op), p->heads H >= 1, p->d_k, p->d_v in {64,128},
+ *   1 <= p->window W <= 64, p->in_dtype (q,k,v) and p->out_dtype (o) in
+ *   {GDNQ_F32, GDNQ_BF16}, p->flags in {0, GDNQ_FLAG_WHT}.
+ *     q, k      [B,H,d_k] in_dtype      v [B,H,d_v] in_dtype
+ *     alpha, beta [B,H] fp32
+ *     codes     [B,H,d_v,d_k] int8      scales [B,H,d_v] fp32   (in/out)
+ *     buf_k     [B,H,W,d_k] fp32        buf_v [B,H,W,d_v] fp32  (in/out)
+ *     buf_alpha, buf_beta [B,H,W] fp32                           (in/out)
+ *     fill_in   [B] int32 in [0, W-1]   fill_out [B] int32 (written)
+ *     o         [B,H,d_v] out_dtype (written)
+ *   fill_in and fill_out must be distinct buffers (every head of a sequence
+ *   reads fill_in while the call runs): equal pointers give GDNQ_ERR_ALIAS.
+ *   A fill_in value outside [0, W-1] is a data error (result unspecified,
+ *   memory accesses stay inside the buffers).
+ *   Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, FLAGS, HIP.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t batch, heads, d_k, d_v, window;
+  int32_t in_dtype, out_dtype;
+  uint32_t flags;
+} gdnq_decode_params;
+
+gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const void* k,
+                             const void* v, const float* alpha, const float* beta,
+                             int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                             float* buf_alpha, float* buf_beta, const int32_t* fill_in,
+                             int32_t* fill_out, void* o, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdnq_prefill_chunked -- chunkwise-parallel prefill of whole windows.
+ *   LinQuant, abstract (chunkwise-parallel prefill as dense matrix products;
+ *   SSD prefill with int8 operands; rotations); LeapQuant, abstract
+ *   (requantize once per window).
+ *
+ *   GDN (flags without GDNQ_FLAG_SSD): the gated delta rule over T tokens
+ *   from the stored state (init_codes/init_scales, or zero when both are
+ *   NULL), requantizing at every window end, windows aligned to token 0.
+ *   Supported: d_k = d_v = 128, chunk = window = 64, T a multiple of 64.
+ *   Writes o and the final codes/scales (the state after the last window).
+ *   state_f32 must be NULL.  Flags: GDNQ_FLAG_WHT allowed.
+ *
+ *   SSD (GDNQ_FLAG_SSD): S_t = a_t S_{t-1} + v_t k_t^T from a zero state, no
+ *   requantization (window ignored); beta, init_codes, init_scales, codes and
+ *   scales must be NULL; writes o and the final fp32 state (in the rotated
+ *   basis under GDNQ_FLAG_WHT).  Supported: d_k = 128, d_v in {64, 128},
+ *   chunk = 64, T a multiple of 64.  Flags: GDNQ_FLAG_WHT, GDNQ_FLAG_INT8_QK.
+ *
+ *   p->in_dtype must be GDNQ_BF16, p->out_dtype GDNQ_BF16 or GDNQ_F32.
+ *     q, k   [B,T,H,d_k] in_dtype     v [B,T,H,d_v] in_dtype
+ *     alpha  [B,T,H] fp32             beta [B,T,H] fp32 (GDN only)
+ *     init_codes [B,H,d_v,d_k] int8, init_scales [B,H,d_v] fp32 (GDN; may
+ *       alias codes/scales for an in-place continuation)
+ *     o      [B,T,H,d_v] out_dtype    (written)
+ *     codes  [B,H,d_v,d_k] int8, scales [B,H,d_v] fp32 (GDN, written)
+ *     state_f32 [B,H,d_v,d_k] fp32 (SSD, written)
+ *   workspace: gdnq_prefill_workspace_size(p) bytes of device memory (may be
+ *   NULL when that size is 0).
+ *   Errors: NULL, SHAPE, DTYPE, ALIGN, FLAGS, WORKSPACE, HIP.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t batch, seqlen, heads, d_k, d_v, chunk, window;
+  int32_t in_dtype, out_dtype;
+  uint32_t flags;
+} gdnq_prefill_params;
+
+size_t gdnq_prefill_workspace_size(const gdnq_prefill_params* p);
+
+gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const int8_t* init_codes, const float* init_scales, void* o,
+                                 int8_t* codes, float* scales, float* state_f32,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Status text, last error detail (thread-local, "" if none), library version. */
+const char* gdnq_status_string(gdnq_status s);
+const char* gdnq_last_error(void);
+int32_t gdnq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDNQ_H */

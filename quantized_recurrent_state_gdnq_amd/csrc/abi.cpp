@@ -1,0 +1,257 @@
+// C ABI of the library: argument validation, error reporting and dispatch to
+// the gfx950 kernels.  Validation is complete before anything is launched;
+// on any error nothing is launched and nothing is written.
+#include "../../include/gdnq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdnq_status fail(gdnq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+gdnq_status ok() {
+  g_err[0] = '\0';
+  return GDNQ_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  const char* name;
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+gdnq_status check_ptrs(const Span* s, int n) {
+  for (int i = 0; i < n; ++i)
+    if (!s[i].p) return fail(GDNQ_ERR_NULL, "%s is NULL", s[i].name);
+  for (int i = 0; i < n; ++i)
+    if (!aligned16(s[i].p)) return fail(GDNQ_ERR_ALIGN, "%s is not 16-byte aligned", s[i].name);
+  return GDNQ_OK;
+}
+
+// HIP keeps the last error of any runtime call per thread until it is read;
+// clear it before a launch so that the status reported is the launch's own.
+void clear_stale_hip_error() { (void)hipGetLastError(); }
+
+gdnq_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GDNQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool dim_ok(int d) { return d == 64 || d == 128; }
+size_t esize(int32_t dt) { return dt == GDNQ_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gdnq_status_string(gdnq_status s) {
+  switch (s) {
+    case GDNQ_OK: return "ok";
+    case GDNQ_ERR_NULL: return "null pointer";
+    case GDNQ_ERR_SHAPE: return "unsupported shape";
+    case GDNQ_ERR_DTYPE: return "unsupported dtype";
+    case GDNQ_ERR_ALIGN: return "misaligned pointer";
+    case GDNQ_ERR_ALIAS: return "aliased buffers";
+    case GDNQ_ERR_WORKSPACE: return "workspace too small";
+    case GDNQ_ERR_HIP: return "HIP runtime error";
+    case GDNQ_ERR_FLAGS: return "unsupported flags";
+  }
+  return "unknown status";
+}
+
+const char* gdnq_last_error(void) { return g_err; }
+
+int32_t gdnq_version(void) { return 100; }
+
+gdnq_status gdnq_quantize_state(const float* S, int64_t rows, int32_t d_k, int8_t* codes,
+                                float* scales, uint32_t flags, void* stream) {
+  if (rows < 0) return fail(GDNQ_ERR_SHAPE, "rows = %lld < 0", (long long)rows);
+  if (!dim_ok(d_k)) return fail(GDNQ_ERR_SHAPE, "d_k = %d, expected 64 or 128", d_k);
+  if (flags & ~uint32_t(GDNQ_FLAG_WHT)) return fail(GDNQ_ERR_FLAGS, "flags 0x%x: only GDNQ_FLAG_WHT allowed", flags);
+  if (rows > (int64_t(1) << 35)) return fail(GDNQ_ERR_SHAPE, "rows = %lld too large", (long long)rows);
+  if (rows == 0) return ok();
+  const Span sp[] = {{"S", S, size_t(rows) * d_k * 4}, {"codes", codes, size_t(rows) * d_k},
+                     {"scales", scales, size_t(rows) * 4}};
+  if (gdnq_status st = check_ptrs(sp, 3)) return st;
+  if (overlap(sp[0], sp[1]) || overlap(sp[0], sp[2]) || overlap(sp[1], sp[2]))
+    return fail(GDNQ_ERR_ALIAS, "S, codes and scales must not overlap");
+  clear_stale_hip_error();
+  gdnq::QuantizeLaunch L{S, rows, d_k, codes, scales, (flags & GDNQ_FLAG_WHT) != 0};
+  return hip_status(gdnq::launch_quantize(L, static_cast<hipStream_t>(stream)), "quantize launch");
+}
+
+gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const void* k,
+                             const void* v, const float* alpha, const float* beta,
+                             int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                             float* buf_alpha, float* buf_beta, const int32_t* fill_in,
+                             int32_t* fill_out, void* o, void* stream) {
+  if (!p) return fail(GDNQ_ERR_NULL, "params is NULL");
+  const int B = p->batch, H = p->heads, dk = p->d_k, dv = p->d_v, W = p->window;
+  if (B < 0) return fail(GDNQ_ERR_SHAPE, "batch = %d < 0", B);
+  if (H < 1) return fail(GDNQ_ERR_SHAPE, "heads = %d < 1", H);
+  if (!dim_ok(dk) || !dim_ok(dv)) return fail(GDNQ_ERR_SHAPE, "d_k = %d, d_v = %d: each must be 64 or 128", dk, dv);
+  if (W < 1 || W > 64) return fail(GDNQ_ERR_SHAPE, "window = %d, expected 1..64", W);
+  if ((p->in_dtype != GDNQ_F32 && p->in_dtype != GDNQ_BF16) ||
+      (p->out_dtype != GDNQ_F32 && p->out_dtype != GDNQ_BF16))
+    return fail(GDNQ_ERR_DTYPE, "in_dtype = %d, out_dtype = %d", p->in_dtype, p->out_dtype);
+  if (p->flags & ~uint32_t(GDNQ_FLAG_WHT))
+    return fail(GDNQ_ERR_FLAGS, "flags 0x%x: decode accepts only GDNQ_FLAG_WHT", p->flags);
+  if (int64_t(B) * H * gdnq::decode_row_split() > 0x7fffffffLL)
+    return fail(GDNQ_ERR_SHAPE, "batch * heads = %lld too large", (long long)B * H);
+  if (B == 0) return ok();
+  const size_t bh = size_t(B) * H, ei = esize(p->in_dtype), eo = esize(p->out_dtype);
+  const Span sp[] = {{"q", q, bh * dk * ei},
+                     {"k", k, bh * dk * ei},
+                     {"v", v, bh * dv * ei},
+                     {"alpha", alpha, bh * 4},
+                     {"beta", beta, bh * 4},
+                     {"codes", codes, bh * dv * dk},
+                     {"scales", scales, bh * dv * 4},
+                     {"buf_k", buf_k, bh * W * dk * 4},
+                     {"buf_v", buf_v, bh * W * dv * 4},
+                     {"buf_alpha", buf_alpha, bh * W * 4},
+                     {"buf_beta", buf_beta, bh * W * 4},
+                     {"fill_in", fill_in, size_t(B) * 4},
+                     {"fill_out", fill_out, size_t(B) * 4},
+                     {"o", o, bh * dv * eo}};
+  constexpr int N = sizeof(sp) / sizeof(sp[0]);
+  if (gdnq_status st = check_ptrs(sp, N)) return st;
+  // every written buffer (codes .. fill_out, o) must be disjoint from every other buffer
+  for (int i = 5; i < N; ++i) {
+    if (i == 11) continue;  // fill_in is read-only
+    for (int j = 0; j < N; ++j)
+      if (j != i && overlap(sp[i], sp[j]))
+        return fail(GDNQ_ERR_ALIAS, "%s overlaps %s", sp[i].name, sp[j].name);
+  }
+  clear_stale_hip_error();
+  gdnq::DecodeLaunch L{q,        k,        v,       alpha, beta, codes, scales, buf_k,
+                       buf_v,    buf_alpha, buf_beta, fill_in, fill_out, o,   B,      H,
+                       dk,       dv,       W,       p->in_dtype == GDNQ_BF16,
+                       p->out_dtype == GDNQ_BF16, (p->flags & GDNQ_FLAG_WHT) != 0};
+  return hip_status(gdnq::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillLaunch& L) {
+  if (!p) return fail(GDNQ_ERR_NULL, "params is NULL");
+  const int B = p->batch, T = p->seqlen, H = p->heads, dk = p->d_k, dv = p->d_v;
+  if (B < 0 || T < 0 || H < 1) return fail(GDNQ_ERR_SHAPE, "batch = %d, seqlen = %d, heads = %d", B, T, H);
+  if (p->in_dtype != GDNQ_BF16) return fail(GDNQ_ERR_DTYPE, "prefill in_dtype must be GDNQ_BF16");
+  if (p->out_dtype != GDNQ_F32 && p->out_dtype != GDNQ_BF16) return fail(GDNQ_ERR_DTYPE, "out_dtype = %d", p->out_dtype);
+  if (p->chunk != 64) return fail(GDNQ_ERR_SHAPE, "chunk = %d, expected 64", p->chunk);
+  if (T % 64) return fail(GDNQ_ERR_SHAPE, "seqlen = %d is not a multiple of the chunk (64)", T);
+  const bool ssd = (p->flags & GDNQ_FLAG_SSD) != 0;
+  if (ssd) {
+    if (p->flags & ~uint32_t(GDNQ_FLAG_SSD | GDNQ_FLAG_WHT | GDNQ_FLAG_INT8_QK))
+      return fail(GDNQ_ERR_FLAGS, "flags 0x%x", p->flags);
+    if (dk != 128 || (dv != 64 && dv != 128)) return fail(GDNQ_ERR_SHAPE, "SSD: d_k = %d (128), d_v = %d (64 or 128)", dk, dv);
+  } else {
+    if (p->flags & ~uint32_t(GDNQ_FLAG_WHT))
+      return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill accepts only GDNQ_FLAG_WHT", p->flags);
+    if (dk != 128 || dv != 128) return fail(GDNQ_ERR_SHAPE, "GDN prefill: d_k = d_v = 128 required (got %d, %d)", dk, dv);
+    if (p->window != p->chunk) return fail(GDNQ_ERR_SHAPE, "GDN prefill: window = %d must equal chunk = %d", p->window, p->chunk);
+  }
+  if (int64_t(B) * H * 8 > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "batch * heads too large");
+  L = gdnq::PrefillLaunch{};
+  L.B = B; L.T = T; L.H = H; L.d_k = dk; L.d_v = dv; L.C = p->chunk; L.W = p->window;
+  L.out_bf16 = p->out_dtype == GDNQ_BF16;
+  L.wht = (p->flags & GDNQ_FLAG_WHT) != 0;
+  L.ssd = ssd;
+  L.int8_qk = (p->flags & GDNQ_FLAG_INT8_QK) != 0;
+  return GDNQ_OK;
+}
+
+size_t gdnq_prefill_workspace_size(const gdnq_prefill_params* p) {
+  gdnq::PrefillLaunch L;
+  if (prefill_validate(p, L) != GDNQ_OK) return 0;
+  return gdnq::prefill_workspace_bytes(L);
+}
+
+gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const int8_t* init_codes, const float* init_scales, void* o,
+                                 int8_t* codes, float* scales, float* state_f32,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  gdnq::PrefillLaunch L;
+  if (gdnq_status st = prefill_validate(p, L)) return st;
+  if (L.B == 0) return ok();
+  const size_t bth = size_t(L.B) * L.T * L.H, bh = size_t(L.B) * L.H;
+  const size_t eo = L.out_bf16 ? 2 : 4;
+  if (L.ssd) {
+    if (beta || init_codes || init_scales || codes || scales)
+      return fail(GDNQ_ERR_SHAPE, "SSD prefill: beta, init_codes, init_scales, codes, scales must be NULL");
+    const Span sp[] = {{"q", q, bth * L.d_k * 2}, {"k", k, bth * L.d_k * 2},
+                       {"v", v, bth * L.d_v * 2}, {"alpha", alpha, bth * 4},
+                       {"o", o, bth * L.d_v * eo}, {"state_f32", state_f32, bh * L.d_v * L.d_k * 4}};
+    constexpr int N = sizeof(sp) / sizeof(sp[0]);
+    if (L.T > 0) {
+      if (gdnq_status st = check_ptrs(sp, N)) return st;
+    } else {
+      if (gdnq_status st = check_ptrs(sp + 5, 1)) return st;
+    }
+    for (int i = 4; i < N; ++i)
+      for (int j = 0; j < N; ++j)
+        if (j != i && overlap(sp[i], sp[j])) return fail(GDNQ_ERR_ALIAS, "%s overlaps %s", sp[i].name, sp[j].name);
+  } else {
+    if (state_f32) return fail(GDNQ_ERR_SHAPE, "GDN prefill: state_f32 must be NULL");
+    if ((init_codes == nullptr) != (init_scales == nullptr))
+      return fail(GDNQ_ERR_NULL, "init_codes and init_scales must be both NULL or both set");
+    const Span sp[] = {{"q", q, bth * L.d_k * 2},         {"k", k, bth * L.d_k * 2},
+                       {"v", v, bth * L.d_v * 2},         {"alpha", alpha, bth * 4},
+                       {"beta", beta, bth * 4},           {"o", o, bth * L.d_v * eo},
+                       {"codes", codes, bh * L.d_v * L.d_k}, {"scales", scales, bh * L.d_v * 4}};
+    constexpr int N = sizeof(sp) / sizeof(sp[0]);
+    if (L.T > 0) {
+      if (gdnq_status st = check_ptrs(sp, N)) return st;
+    } else {
+      if (gdnq_status st = check_ptrs(sp + 6, 2)) return st;
+    }
+    if (init_codes) {
+      const Span ip[] = {{"init_codes", init_codes, bh * L.d_v * L.d_k}, {"init_scales", init_scales, bh * L.d_v * 4}};
+      if (gdnq_status st = check_ptrs(ip, 2)) return st;
+      // an in-place continuation (init == final) is allowed; partial overlap is not
+      if (init_codes != codes && overlap(ip[0], sp[6])) return fail(GDNQ_ERR_ALIAS, "init_codes partially overlaps codes");
+      if (init_scales != scales && overlap(ip[1], sp[7])) return fail(GDNQ_ERR_ALIAS, "init_scales partially overlaps scales");
+    }
+    for (int i = 5; i < N; ++i)
+      for (int j = 0; j < N; ++j)
+        if (j != i && overlap(sp[i], sp[j])) return fail(GDNQ_ERR_ALIAS, "%s overlaps %s", sp[i].name, sp[j].name);
+    L.beta = beta;
+    L.init_codes = init_codes;
+    L.init_scales = init_scales;
+    L.codes = codes;
+    L.scales = scales;
+  }
+  const size_t need = gdnq::prefill_workspace_bytes(L);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(GDNQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace_bytes);
+  if (workspace && !aligned16(workspace)) return fail(GDNQ_ERR_ALIGN, "workspace is not 16-byte aligned");
+  L.q = q; L.k = k; L.v = v; L.alpha = alpha; L.o = o; L.state_f32 = state_f32; L.workspace = workspace;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  clear_stale_hip_error();
+  return hip_status(L.ssd ? gdnq::launch_prefill_ssd(L, s) : gdnq::launch_prefill_gdn(L, s), "prefill launch");
+}
+
+}  // extern "C"

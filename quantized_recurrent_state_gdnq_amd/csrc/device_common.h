@@ -1,0 +1,174 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversion, wave-level
+// reductions (DPP inside a row of 16 lanes, cross-row swizzles above), the
+// register/cross-lane fast Walsh-Hadamard transform and the int8 row codec.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdnq {
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_at(const uint16_t* p, int i) {
+  return __uint_as_float(uint32_t(p[i]) << 16);
+}
+// fp32 -> bf16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---------------------------------------------------------------- DPP / reductions
+// DPP control words (GFX9 encoding).
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 1..64); every lane of a
+// group receives the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<DPP_XOR1>(x);
+  if constexpr (N >= 4) x += dpp<DPP_XOR2>(x);
+  if constexpr (N >= 8) x += dpp<DPP_ROW_HALF_MIRROR>(x);
+  if constexpr (N >= 16) x += dpp<DPP_ROW_MIRROR>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp<DPP_XOR1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<DPP_XOR2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<DPP_ROW_HALF_MIRROR>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<DPP_ROW_MIRROR>(x));
+  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16, 64));
+  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
+// Full-wave sum returned as a wave-uniform value: DPP inside each row of 16
+// lanes, then the four row sums are read out of lanes 0/16/32/48.
+__device__ __forceinline__ float wave_sum_uniform(float x) {
+  x = group_sum<16>(x);
+  float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (a + b) + (c + d);
+}
+
+// ---------------------------------------------------------------- FWHT
+// Fast Walsh-Hadamard transform of a d-vector spread over a group of lanes:
+// lane j of the group holds elements [j*E, j*E + E) in v[0..E).  The
+// butterfly (x_i, x_{i+s}) -> (x_i + x_{i+s}, x_i - x_{i+s}) over every
+// stride s = 1, 2, ..., d/2 yields H x with H the Sylvester Hadamard matrix
+// H[i][j] = (-1)^popcount(i & j); the result is then scaled by 1/sqrt(d).
+// The group is `lanes = d / E` consecutive lanes, aligned.
+template <int E>
+__device__ __forceinline__ void fwht_local(float (&v)[E]) {
+#pragma unroll
+  for (int s = 1; s < E; s <<= 1) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if ((i & s) == 0) {
+        float a = v[i], b = v[i + s];
+        v[i] = a + b;
+        v[i + s] = a - b;
+      }
+    }
+  }
+}
+
+template <int E, int LANES>
+__device__ __forceinline__ void fwht_group(float (&v)[E], int lane_in_group) {
+  fwht_local<E>(v);
+#pragma unroll
+  for (int m = 1; m < LANES; m <<= 1) {
+    const bool upper = (lane_in_group & m) != 0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      float other = __shfl_xor(v[i], m, 64);
+      v[i] = upper ? (other - v[i]) : (v[i] + other);
+    }
+  }
+  constexpr float inv_sqrt = (E * LANES == 128) ? 0.08838834764831845f
+                             : (E * LANES == 64) ? 0.125f
+                             : (E * LANES == 256) ? 0.0625f
+                                                  : 0.0f;
+  static_assert(inv_sqrt != 0.0f, "unsupported FWHT length");
+#pragma unroll
+  for (int i = 0; i < E; ++i) v[i] *= inv_sqrt;
+}
+
+// ---------------------------------------------------------------- codec
+// scale = absmax / 127 (IEEE division); code = clamp(rne(x / scale), -127, 127).
+__device__ __forceinline__ float codec_scale(float absmax) { return __fdiv_rn(absmax, 127.0f); }
+
+__device__ __forceinline__ int codec_code(float x, float scale) {
+  if (scale == 0.0f) return 0;
+  float r = __builtin_rintf(__fdiv_rn(x, scale));
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return int(r);
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t(a) & 0xffu) | ((uint32_t(b) & 0xffu) << 8) | ((uint32_t(c) & 0xffu) << 16) |
+         ((uint32_t(d) & 0xffu) << 24);
+}
+
+__device__ __forceinline__ float i8_at(uint32_t w, int byte) {
+  return float(int32_t(w << (24 - 8 * byte)) >> 24);
+}
+
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer loads through a resource whose size limits the access: a lane
+// whose byte offset is at or past `nbytes` reads 0 and causes no memory
+// traffic.  This predicates loads without branches (dword 3 = 0x00020000 is
+// the gfx9-family raw-buffer format word).
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ float4 bload_f4(rsrc_t r, uint32_t off) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  float4 f;
+  __builtin_memcpy(&f, &v, 16);
+  return f;
+}
+__device__ __forceinline__ uint4 bload_u4(rsrc_t r, uint32_t off) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  uint4 u;
+  __builtin_memcpy(&u, &v, 16);
+  return u;
+}
+__device__ __forceinline__ uint2 bload_u2(rsrc_t r, uint32_t off) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  uint2 u;
+  __builtin_memcpy(&u, &v, 8);
+  return u;
+}
+__device__ __forceinline__ float bload_f1(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// XCD-aware workgroup id: workgroups are dispatched round-robin over the 8
+// XCDs, so block x runs on XCD x % 8.  This remaps ids so that consecutive
+// logical ids share one XCD (and its L2): logical = (x % 8) * (n / 8) + x / 8.
+// Valid when n is a multiple of 8; otherwise the identity is used.
+__device__ __forceinline__ int xcd_swizzle(int x, int n) {
+  if (n & 7) return x;
+  return (x & 7) * (n >> 3) + (x >> 3);
+}
+
+}  // namespace gdnq

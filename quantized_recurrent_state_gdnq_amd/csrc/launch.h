@@ -1,0 +1,63 @@
+// Internal launch interface between the C ABI (abi.cpp) and the kernels.
+// Shapes are validated by the ABI before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdnq {
+
+struct QuantizeLaunch {
+  const float* S;
+  int64_t rows;
+  int d_k;
+  int8_t* codes;
+  float* scales;
+  bool wht;
+};
+hipError_t launch_quantize(const QuantizeLaunch& L, hipStream_t stream);
+
+struct DecodeLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  int8_t* codes;
+  float* scales;
+  float* buf_k;
+  float* buf_v;
+  float* buf_alpha;
+  float* buf_beta;
+  const int32_t* fill_in;
+  int32_t* fill_out;
+  void* o;
+  int B, H, d_k, d_v, W;
+  bool in_bf16, out_bf16, wht;
+};
+hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
+size_t decode_lds_bytes(int d_k, int d_v, int W);
+int decode_row_split();
+
+struct PrefillLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const int8_t* init_codes;
+  const float* init_scales;
+  void* o;
+  int8_t* codes;
+  float* scales;
+  float* state_f32;
+  void* workspace;
+  int B, T, H, d_k, d_v, C, W;
+  bool out_bf16, wht, ssd, int8_qk;
+};
+hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream);
+hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream);
+size_t prefill_workspace_bytes(const PrefillLaunch& L);
+
+}  // namespace gdnq

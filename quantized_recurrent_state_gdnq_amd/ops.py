@@ -1,0 +1,192 @@
+"""Torch-facing wrappers around the C ABI (include/gdnq.h).
+
+PyTorch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's gfx950 kernels.  These functions only check
+dtype/device/contiguity, allocate outputs the caller did not pass, and hand
+raw pointers to the library.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.GDNQ_F32, torch.bfloat16: _lib.GDNQ_BF16}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t, name, dtype=None, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def quantize_state(S, codes=None, scales=None, wht=False):
+    """Per-row int8 codec of S[..., d_k] (fp32): returns (codes int8, scales fp32[...])."""
+    _need(S, "S", torch.float32)
+    d_k = S.shape[-1]
+    rows = S.numel() // d_k if d_k else 0
+    if codes is None:
+        codes = torch.empty(S.shape, dtype=torch.int8, device=S.device)
+    if scales is None:
+        scales = torch.empty(S.shape[:-1], dtype=torch.float32, device=S.device)
+    _need(codes, "codes", torch.int8, S.device)
+    _need(scales, "scales", torch.float32, S.device)
+    if codes.shape != S.shape or scales.numel() != rows:
+        raise ValueError("codes must match S; scales must hold one value per row")
+    _lib.check(_lib.quantize_state(_ptr(S), rows, d_k, _ptr(codes), _ptr(scales),
+                                   _lib.GDNQ_FLAG_WHT if wht else 0, _stream(S.device)))
+    return codes, scales
+
+
+def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, buf_beta,
+                fill_in, fill_out, o=None, *, wht=False, out_dtype=None):
+    """One decode token per sequence (see gdnq_decode_step in include/gdnq.h).
+
+    q, k [B,H,d_k], v [B,H,d_v] (fp32 or bf16); alpha, beta [B,H] fp32;
+    codes [B,H,d_v,d_k] int8 and scales [B,H,d_v] fp32 (updated in place for
+    sequences whose window closes); buf_k [B,H,W,d_k], buf_v [B,H,W,d_v],
+    buf_alpha, buf_beta [B,H,W] fp32 (slot fill_in[b] receives the write);
+    fill_in, fill_out [B] int32 (distinct).  Returns o [B,H,d_v].
+    """
+    dev = q.device
+    B, H, d_k = q.shape
+    d_v = v.shape[-1]
+    W = buf_k.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype, dev)
+    for name, t in (("alpha", alpha), ("beta", beta), ("scales", scales), ("buf_k", buf_k),
+                    ("buf_v", buf_v), ("buf_alpha", buf_alpha), ("buf_beta", buf_beta)):
+        _need(t, name, torch.float32, dev)
+    _need(codes, "codes", torch.int8, dev)
+    _need(fill_in, "fill_in", torch.int32, dev)
+    _need(fill_out, "fill_out", torch.int32, dev)
+    if q.dtype not in _DT:
+        raise ValueError("q, k, v must be float32 or bfloat16")
+    if o is None:
+        o = torch.empty((B, H, d_v), dtype=out_dtype or q.dtype, device=dev)
+    _need(o, "o", None, dev)
+    if o.dtype not in _DT:
+        raise ValueError("o must be float32 or bfloat16")
+    if (tuple(k.shape) != (B, H, d_k) or tuple(v.shape) != (B, H, d_v)
+            or tuple(codes.shape) != (B, H, d_v, d_k) or tuple(scales.shape) != (B, H, d_v)
+            or tuple(buf_k.shape) != (B, H, W, d_k) or tuple(buf_v.shape) != (B, H, W, d_v)
+            or tuple(buf_alpha.shape) != (B, H, W) or tuple(buf_beta.shape) != (B, H, W)
+            or tuple(alpha.shape) != (B, H) or tuple(beta.shape) != (B, H)
+            or fill_in.numel() != B or fill_out.numel() != B or tuple(o.shape) != (B, H, d_v)):
+        raise ValueError("inconsistent decode shapes")
+    p = _lib.DecodeParams(B, H, d_k, d_v, W, _DT[q.dtype], _DT[o.dtype],
+                          _lib.GDNQ_FLAG_WHT if wht else 0)
+    _lib.check(_lib.decode_step(p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(codes),
+                                _ptr(scales), _ptr(buf_k), _ptr(buf_v), _ptr(buf_alpha),
+                                _ptr(buf_beta), _ptr(fill_in), _ptr(fill_out), _ptr(o),
+                                _stream(dev)))
+    return o
+
+
+def _prefill_params(q, v, *, window, chunk, wht, ssd, int8_qk, out_dtype):
+    B, T, H, d_k = q.shape
+    d_v = v.shape[-1]
+    flags = ((_lib.GDNQ_FLAG_WHT if wht else 0) | (_lib.GDNQ_FLAG_SSD if ssd else 0)
+             | (_lib.GDNQ_FLAG_INT8_QK if int8_qk else 0))
+    return _lib.PrefillParams(B, T, H, d_k, d_v, chunk, window, _DT[q.dtype], _DT[out_dtype], flags)
+
+
+def prefill_workspace_size(q, v, *, window=64, chunk=64, wht=False, ssd=False, int8_qk=False,
+                           out_dtype=torch.bfloat16):
+    p = _prefill_params(q, v, window=window, chunk=chunk, wht=wht, ssd=ssd, int8_qk=int8_qk,
+                        out_dtype=out_dtype)
+    return int(_lib.prefill_workspace_size(p))
+
+
+def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_codes=None,
+                    init_scales=None, wht=False, ssd=False, int8_qk=False,
+                    out_dtype=torch.bfloat16, o=None, codes=None, scales=None, state_f32=None,
+                    workspace=None):
+    """Chunkwise prefill (see gdnq_prefill_chunked in include/gdnq.h).
+
+    q, k [B,T,H,d_k], v [B,T,H,d_v] bf16; alpha (and beta for GDN) [B,T,H] fp32.
+    GDN returns (o, codes, scales); SSD (ssd=True) returns (o, state_f32).
+    """
+    dev = q.device
+    B, T, H, d_k = q.shape
+    d_v = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, dev)
+    _need(alpha, "alpha", torch.float32, dev)
+    if tuple(k.shape) != (B, T, H, d_k) or tuple(v.shape) != (B, T, H, d_v) or tuple(alpha.shape) != (B, T, H):
+        raise ValueError("inconsistent prefill shapes")
+    p = _prefill_params(q, v, window=window, chunk=chunk, wht=wht, ssd=ssd, int8_qk=int8_qk,
+                        out_dtype=out_dtype)
+    if o is None:
+        o = torch.empty((B, T, H, d_v), dtype=out_dtype, device=dev)
+    _need(o, "o", out_dtype, dev)
+    if ssd:
+        if state_f32 is None:
+            state_f32 = torch.empty((B, H, d_v, d_k), dtype=torch.float32, device=dev)
+        _need(state_f32, "state_f32", torch.float32, dev)
+    else:
+        _need(beta, "beta", torch.float32, dev)
+        if tuple(beta.shape) != (B, T, H):
+            raise ValueError("beta must be [B,T,H]")
+        if codes is None:
+            codes = torch.empty((B, H, d_v, d_k), dtype=torch.int8, device=dev)
+        if scales is None:
+            scales = torch.empty((B, H, d_v), dtype=torch.float32, device=dev)
+        _need(codes, "codes", torch.int8, dev)
+        _need(scales, "scales", torch.float32, dev)
+        if init_codes is not None:
+            _need(init_codes, "init_codes", torch.int8, dev)
+            _need(init_scales, "init_scales", torch.float32, dev)
+    need = int(_lib.prefill_workspace_size(p))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _lib.check(_lib.prefill_chunked(p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                    None if ssd else _ptr(beta), _ptr(init_codes),
+                                    _ptr(init_scales), _ptr(o), None if ssd else _ptr(codes),
+                                    None if ssd else _ptr(scales), _ptr(state_f32) if ssd else None,
+                                    _ptr(workspace), ws_bytes, _stream(dev)))
+    if ssd:
+        return o, state_f32
+    return o, codes, scales
+
+
+class DecodeState:
+    """Per-request state of a batch of sequences: int8 codes, per-row scales,
+    the window buffer and the fill counters (ping-ponged between two arrays,
+    since every head of a sequence reads the fill while the step runs)."""
+
+    def __init__(self, codes, scales, window, fill=None, wht=False):
+        B, H, d_v, d_k = codes.shape
+        dev = codes.device
+        self.codes, self.scales, self.window, self.wht = codes, scales, window, wht
+        self.buf_k = torch.empty((B, H, window, d_k), dtype=torch.float32, device=dev)
+        self.buf_v = torch.empty((B, H, window, d_v), dtype=torch.float32, device=dev)
+        self.buf_alpha = torch.empty((B, H, window), dtype=torch.float32, device=dev)
+        self.buf_beta = torch.empty((B, H, window), dtype=torch.float32, device=dev)
+        self.fill = torch.zeros(B, dtype=torch.int32, device=dev) if fill is None else fill
+        self._fill_next = torch.empty_like(self.fill)
+
+    def step(self, q, k, v, alpha, beta, o=None, out_dtype=None):
+        o = decode_step(q, k, v, alpha, beta, self.codes, self.scales, self.buf_k, self.buf_v,
+                        self.buf_alpha, self.buf_beta, self.fill, self._fill_next, o,
+                        wht=self.wht, out_dtype=out_dtype)
+        self.fill, self._fill_next = self._fill_next, self.fill
+        return o

@@ -1,0 +1,166 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before launching anything.
+
+Pointers here are fake addresses that the host code compares but never
+dereferences; every call below fails validation, so no kernel is launched.
+"""
+
+import os
+import re
+
+import pytest
+
+from quantized_recurrent_state_gdnq_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = _lib.lib
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "gdnq.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdnq_[a-z_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert L.gdnq_version() >= 100
+    for s in range(9):
+        assert L.gdnq_status_string(s)
+
+
+class Fake:
+    """Distinct, 16-byte-aligned, never-dereferenced addresses."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def __call__(self, nbytes=1 << 24):
+        p = self.next
+        self.next += ((nbytes + (1 << 20)) // (1 << 20) + 1) << 20
+        return p
+
+
+def _decode_args(fake, B=2, H=2, d=128, W=8):
+    return dict(q=fake(), k=fake(), v=fake(), alpha=fake(), beta=fake(), codes=fake(),
+                scales=fake(), buf_k=fake(), buf_v=fake(), buf_alpha=fake(), buf_beta=fake(),
+                fill_in=fake(), fill_out=fake(), o=fake())
+
+
+def _decode(params, a, stream=None):
+    return _lib.decode_step(params, a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["codes"],
+                            a["scales"], a["buf_k"], a["buf_v"], a["buf_alpha"], a["buf_beta"],
+                            a["fill_in"], a["fill_out"], a["o"], stream)
+
+
+def _p(B=2, H=2, dk=128, dv=128, W=8, ind=1, outd=1, flags=0):
+    return _lib.DecodeParams(B, H, dk, dv, W, ind, outd, flags)
+
+
+@pytest.mark.parametrize("params,status", [
+    (_p(dk=96), 2), (_p(dv=32), 2), (_p(W=0), 2), (_p(W=65), 2), (_p(H=0), 2), (_p(B=-1), 2),
+    (_p(ind=2), 3), (_p(outd=5), 3), (_p(flags=2), 8), (_p(flags=16), 8),
+])
+def test_decode_rejects_bad_params(params, status):
+    a = _decode_args(Fake())
+    assert _decode(params, a) == status
+    assert L.gdnq_last_error()
+
+
+def test_decode_null_params_and_pointers():
+    assert L.gdnq_decode_step(None, *([None] * 15)) == 1
+    for name in ["q", "codes", "buf_beta", "fill_in", "fill_out", "o"]:
+        a = _decode_args(Fake())
+        a[name] = None
+        assert _decode(_p(), a) == 1, name
+        assert name.encode() in L.gdnq_last_error()
+
+
+def test_decode_misaligned():
+    a = _decode_args(Fake())
+    a["buf_v"] += 4
+    assert _decode(_p(), a) == 4
+    assert b"buf_v" in L.gdnq_last_error()
+
+
+def test_decode_aliasing():
+    a = _decode_args(Fake())
+    a["fill_out"] = a["fill_in"]
+    assert _decode(_p(), a) == 5
+    a = _decode_args(Fake())
+    a["o"] = a["q"]
+    assert _decode(_p(), a) == 5
+    a = _decode_args(Fake())
+    a["buf_v"] = a["buf_k"] + 256  # partial overlap
+    assert _decode(_p(), a) == 5
+
+
+def test_decode_empty_batch_is_noop():
+    a = {k: None for k in _decode_args(Fake())}
+    assert _decode(_p(B=0), a) == 0
+
+
+def _pp(B=1, T=128, H=2, dk=128, dv=128, C=64, W=64, ind=1, outd=1, flags=0):
+    return _lib.PrefillParams(B, T, H, dk, dv, C, W, ind, outd, flags)
+
+
+def _prefill(params, fake, **over):
+    a = dict(q=fake(), k=fake(), v=fake(), alpha=fake(), beta=fake(), init_codes=None,
+             init_scales=None, o=fake(), codes=fake(), scales=fake(), state_f32=None,
+             workspace=None, ws=0)
+    a.update(over)
+    return _lib.prefill_chunked(params, a["q"], a["k"], a["v"], a["alpha"], a["beta"],
+                                a["init_codes"], a["init_scales"], a["o"], a["codes"],
+                                a["scales"], a["state_f32"], a["workspace"], a["ws"], None)
+
+
+@pytest.mark.parametrize("params,status", [
+    (_pp(C=32, W=32), 2), (_pp(T=100), 2), (_pp(dk=64, dv=64), 2), (_pp(W=128), 2),
+    (_pp(ind=0), 3), (_pp(outd=3), 3), (_pp(flags=4), 8), (_pp(flags=8), 8),
+])
+def test_prefill_rejects_bad_params(params, status):
+    assert _prefill(params, Fake()) == status
+
+
+def test_prefill_gdn_contract():
+    f = Fake()
+    assert _prefill(_pp(), f, beta=None) == 1
+    assert _prefill(_pp(), f, state_f32=f()) == 2
+    c = f()
+    assert _prefill(_pp(), f, init_codes=c) == 1           # init_scales missing
+    assert _prefill(_pp(), f, o=None) == 1
+    q = f()
+    assert _prefill(_pp(), f, q=q, o=q) == 5               # output over an input
+
+
+def test_prefill_ssd_contract():
+    f = Fake()
+    ssd = _pp(dv=64, flags=2 | 1 | 4)
+    assert _prefill(ssd, f, beta=None, codes=None, scales=None) == 1          # state_f32 missing
+    assert _prefill(ssd, f, codes=None, scales=None, state_f32=f()) == 2      # beta given
+    assert _prefill(_pp(dk=64, dv=64, flags=2), f, beta=None, codes=None, scales=None,
+                    state_f32=f()) == 2
+
+
+def test_workspace_size_is_queryable():
+    assert L.gdnq_prefill_workspace_size(None) == 0
+    p = _pp()
+    assert _lib.prefill_workspace_size(p) >= 0
+
+
+def test_quantize_validation():
+    f = Fake()
+    assert L.gdnq_quantize_state(f(), 0, 128, f(), f(), 0, None) == 0     # empty is a no-op
+    assert L.gdnq_quantize_state(f(), 4, 96, f(), f(), 0, None) == 2
+    assert L.gdnq_quantize_state(f(), -1, 128, f(), f(), 0, None) == 2
+    assert L.gdnq_quantize_state(f(), 4, 128, f(), f(), 2, None) == 8
+    assert L.gdnq_quantize_state(None, 4, 128, f(), f(), 0, None) == 1
+    assert L.gdnq_quantize_state(f() + 8, 4, 128, f(), f(), 0, None) == 4
+    s = f()
+    assert L.gdnq_quantize_state(s, 4, 128, s, f(), 0, None) == 5

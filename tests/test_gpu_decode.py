@@ -1,0 +1,231 @@
+"""GPU parity of the codec and the decode step against the CPU oracle,
+through the C ABI (ops -> ctypes -> libgdnq.so)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as wl
+from conftest import read_golden
+from gpu_util import (DEV, OUT_TOL_BF16, OUT_TOL_F32, Guarded, assert_codes, assert_scales,
+                      dev, host, max_rel_err)
+
+pytestmark = pytest.mark.gpu
+
+if DEV is not None:
+    from quantized_recurrent_state_gdnq_amd import ops
+
+
+# ---------------------------------------------------------------- codec
+@pytest.mark.parametrize("d", [64, 128])
+def test_codec_golden_rows_bitwise(d):
+    g = read_golden("codec_rows.txt")
+    rows = []
+    for row in g["row"]:
+        x = np.zeros(d, np.float32)
+        vals = [float(v) for v in row.split()]
+        x[:len(vals)] = vals
+        rows.append(x)
+    S = np.stack(rows)
+    codes, scales = ops.quantize_state(dev(S))
+    torch.cuda.synchronize()
+    for i, (sc, cd) in enumerate(zip(g["scale"], g["codes"])):
+        exp = [int(v) for v in cd.split()]
+        assert host(codes)[i, :len(exp)].tolist() == exp
+        assert np.all(host(codes)[i, len(exp):] == 0)
+        assert host(scales)[i] == np.float32(float(sc))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rows", [1, 17, 4099])
+@pytest.mark.parametrize("wht", [False, True])
+def test_codec_random(d, rows, wht):
+    g = np.random.default_rng(rows + d)
+    S = (g.standard_normal((rows, d)) * np.exp(g.uniform(-4, 4, (rows, 1)))).astype(np.float32)
+    S[rows // 2] = 0.0
+    if rows > 100:
+        S[3, 5] = 40.0  # an outlier channel
+    St = Guarded((rows, d), torch.float32).set(S)
+    C = Guarded((rows, d), torch.int8)
+    Sc = Guarded((rows,), torch.float32)
+    ops.quantize_state(St.t, C.t, Sc.t, wht=wht)
+    torch.cuda.synchronize()
+    assert C.guards_intact() and Sc.guards_intact()
+    ref_in = O.gdnq_oracle.rotate(S, np.float32) if wht else S
+    rc, rs = O.quantize_rows(ref_in)
+    if wht:
+        assert_codes(host(C.t), rc, "codec+wht")
+        assert_scales(host(Sc.t), rs, "codec+wht")
+    else:
+        assert np.array_equal(host(C.t), rc)
+        assert np.array_equal(host(Sc.t), rs)
+
+
+# ---------------------------------------------------------------- decode
+def _run_decode(d, W, in_dt, out_dt, wht=False):
+    """One GPU decode step on generator output `d`; returns host results and
+    the quantized initial state (the oracle's codec quantizes it)."""
+    B, H, dv, dk = d["state"].shape
+    codes, scales = O.quantize_rows(O.gdnq_oracle.rotate(d["state"], np.float32) if wht
+                                    else d["state"])
+    g = {
+        "codes": Guarded((B, H, dv, dk), torch.int8).set(codes),
+        "scales": Guarded((B, H, dv), torch.float32).set(scales),
+        "buf_k": Guarded((B, H, W, dk), torch.float32).set(d["buf_k"]),
+        "buf_v": Guarded((B, H, W, dv), torch.float32).set(d["buf_v"]),
+        "buf_alpha": Guarded((B, H, W), torch.float32).set(d["buf_alpha"]),
+        "buf_beta": Guarded((B, H, W), torch.float32).set(d["buf_beta"]),
+        "fill_out": Guarded((B,), torch.int32),
+        "o": Guarded((B, H, dv), out_dt),
+    }
+    fin = dev(d["fill"])
+    ops.decode_step(dev(d["q"], in_dt), dev(d["k"], in_dt), dev(d["v"], in_dt), dev(d["alpha"]),
+                    dev(d["beta"]), g["codes"].t, g["scales"].t, g["buf_k"].t, g["buf_v"].t,
+                    g["buf_alpha"].t, g["buf_beta"].t, fin, g["fill_out"].t, g["o"].t, wht=wht)
+    torch.cuda.synchronize()
+    for name, x in g.items():
+        assert x.guards_intact(), f"write outside {name}"
+    assert np.array_equal(host(fin), d["fill"]), "fill_in was modified"
+    return {k: host(v.t) for k, v in g.items()}, codes, scales
+
+
+def _check_decode(d, W, got, codes, scales, tol, wht=False):
+    ref = O.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], codes, scales, d["buf_k"],
+                        d["buf_v"], d["buf_alpha"], d["buf_beta"], d["fill"], W, rot=wht)
+    o, rc, rs, rbk, rbv, rba, rbb, rfill = ref
+    err = max_rel_err(got["o"], o)
+    assert err <= tol, f"o max relative error {err:.3e} > {tol}"
+    assert np.array_equal(got["fill_out"], rfill)
+    closing = d["fill"] + 1 == W
+    # untouched sequences: state bitwise unchanged, appended slot exact
+    assert np.array_equal(got["codes"][~closing], codes[~closing])
+    assert np.array_equal(got["scales"][~closing], scales[~closing])
+    for bi in np.nonzero(~closing)[0]:
+        f = d["fill"][bi]
+        if wht:
+            np.testing.assert_allclose(got["buf_k"][bi, :, f], rbk[bi, :, f], rtol=0, atol=2e-6)
+        else:
+            assert np.array_equal(got["buf_k"][bi, :, f], rbk[bi, :, f])
+        assert np.array_equal(got["buf_v"][bi, :, f], rbv[bi, :, f])
+        assert np.array_equal(got["buf_alpha"][bi, :, f], rba[bi, :, f])
+        assert np.array_equal(got["buf_beta"][bi, :, f], rbb[bi, :, f])
+        # slots below the fill are not touched
+        assert np.array_equal(got["buf_k"][bi, :, :f], d["buf_k"][bi, :, :f])
+    if closing.any():
+        assert_codes(got["codes"][closing], rc[closing], "closing codes")
+        assert_scales(got["scales"][closing], rs[closing], "closing scales")
+    return err
+
+
+DECODE_CASES = [
+    # (B, H, dk, dv, W, in_dtype, out_dtype, wht, forced fills)
+    (4, 3, 128, 128, 8, torch.bfloat16, torch.bfloat16, False, [0, 3, 7, 7]),
+    (4, 3, 128, 128, 8, torch.bfloat16, torch.float32, True, [7, 1, 6, 0]),
+    (3, 2, 128, 64, 5, torch.bfloat16, torch.bfloat16, False, [4, 2, 0]),
+    (3, 2, 64, 128, 5, torch.float32, torch.float32, False, [4, 2, 0]),
+    (2, 5, 64, 64, 16, torch.float32, torch.float32, True, [15, 9]),
+    (3, 2, 128, 128, 1, torch.bfloat16, torch.bfloat16, False, [0, 0, 0]),
+    (2, 2, 128, 128, 64, torch.bfloat16, torch.bfloat16, False, [63, 62]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"B{c[0]}H{c[1]}dk{c[2]}dv{c[3]}W{c[4]}wht{int(c[7])}")
+def test_decode_step_cases(case):
+    B, H, dk, dv, W, in_dt, out_dt, wht, fills = case
+    d = wl.decode_batch(B=B, H=H, dk=dk, dv=dv, W=W, seed=B * 7 + W, fill=np.array(fills))
+    if in_dt == torch.float32:  # fp32 inputs need not be bf16-representable
+        g = np.random.default_rng(W)
+        d["q"] = wl.l2norm(g.standard_normal(d["q"].shape).astype(np.float32))
+        d["k"] = wl.l2norm(g.standard_normal(d["k"].shape).astype(np.float32))
+        d["v"] = g.standard_normal(d["v"].shape).astype(np.float32)
+    got, codes, scales = _run_decode(d, W, in_dt, out_dt, wht)
+    tol = OUT_TOL_F32 if (in_dt == torch.float32 and out_dt == torch.float32) else OUT_TOL_BF16
+    _check_decode(d, W, got, codes, scales, tol, wht)
+
+
+def test_decode_batch64_heads32_window64():
+    """The one-step decode workload at its full size: B=64, H=32, d=128,
+    W=64, drawn fills in 0..63 (sequences at fill 63 close their window)."""
+    fill = wl.decode_batch(B=64, H=32, dk=128, dv=128, W=64, seed=0)["fill"]
+    fill[:2] = 63  # make sure at least two sequences close
+    d = wl.decode_batch(B=64, H=32, dk=128, dv=128, W=64, seed=0, fill=fill)
+    got, codes, scales = _run_decode(d, 64, torch.bfloat16, torch.bfloat16)
+    err = _check_decode(d, 64, got, codes, scales, OUT_TOL_BF16)
+    print(f"B64 H32 decode: max rel err {err:.3e}")
+
+
+def test_decode_single_head_fp32_256_steps():
+    """Single head, d=64, W=16, fp32 inputs, 256 decode steps from a zero
+    state: every output within 1e-3 of the oracle, final state within the
+    code bar after 16 requantizations."""
+    T, d, W = 256, 64, 16
+    x = wl.single_head_fp32(T=T, d=d, seed=0)
+    ref = O.run_windowed(x["q"][:, None], x["k"][:, None], x["v"][:, None], x["alpha"][:, None],
+                         x["beta"][:, None], W=W)
+    st = ops.DecodeState(torch.zeros((1, 1, d, d), dtype=torch.int8, device=DEV),
+                         torch.zeros((1, 1, d), dtype=torch.float32, device=DEV), W)
+    outs = []
+    for t in range(T):
+        o = st.step(dev(x["q"][t][None, None]), dev(x["k"][t][None, None]),
+                    dev(x["v"][t][None, None]), dev(x["alpha"][t:t + 1][None]),
+                    dev(x["beta"][t:t + 1][None]))
+        outs.append(o)
+    torch.cuda.synchronize()
+    got = np.stack([host(o)[0, 0] for o in outs])
+    err = max_rel_err(got, ref["o"][:, 0])
+    assert err <= OUT_TOL_F32, err
+    assert_codes(host(st.codes)[0, 0], ref["codes"][0], "final codes")
+    assert_scales(host(st.scales)[0, 0], ref["scale"][0], "final scales")
+    assert int(host(st.fill)[0]) == 0
+
+
+@pytest.mark.parametrize("wht", [False, True])
+def test_decode_multi_window(wht):
+    """40 consecutive decode steps (5 windows of 8) on a small batch carrying
+    codes, scales, buffer and fills, staggered fills so windows close at
+    different steps.
+
+    Teacher-forced: every step, the oracle starts from the GPU's state before
+    the step, so each requantization is compared on identical inputs (codes
+    +-1 on <= 0.1%, scales 1e-5).  Free-running: the oracle also runs on its
+    own; outputs stay within 2e-2 and codes within +-1 on <= 0.1%.  (A +-1
+    flip at one window close legitimately moves later scales by about
+    1e-4, so scales are held to 1e-3 free-running.)"""
+    B, H, dk, dv, W, T = 3, 2, 128, 128, 8, 40
+    d0 = wl.decode_batch(B=B, H=H, dk=dk, dv=dv, W=W, seed=5, fill=np.array([0, 3, 7]))
+    S0 = O.gdnq_oracle.rotate(d0["state"], np.float32) if wht else d0["state"]
+    codes, scales = O.quantize_rows(S0)
+    st = ops.DecodeState(dev(codes), dev(scales), W, fill=dev(d0["fill"]), wht=wht)
+    st.buf_k.copy_(dev(d0["buf_k"]))
+    st.buf_v.copy_(dev(d0["buf_v"]))
+    st.buf_alpha.copy_(dev(d0["buf_alpha"]))
+    st.buf_beta.copy_(dev(d0["buf_beta"]))
+    fr = [codes, scales, d0["buf_k"], d0["buf_v"], d0["buf_alpha"], d0["buf_beta"], d0["fill"]]
+    worst_tf = worst_fr = 0.0
+    for t in range(T):
+        x = wl.decode_tokens(B=B, H=H, dk=dk, dv=dv, step=t, seed=11)
+        before = [host(z).copy() for z in (st.codes, st.scales, st.buf_k, st.buf_v, st.buf_alpha,
+                                           st.buf_beta, st.fill)]
+        o = st.step(dev(x["q"], torch.bfloat16), dev(x["k"], torch.bfloat16),
+                    dev(x["v"], torch.bfloat16), dev(x["alpha"]), dev(x["beta"]),
+                    out_dtype=torch.float32)
+        go = host(o)
+        # teacher-forced
+        ro, rc, rs, _, _, _, _, rfill = O.decode_step(x["q"], x["k"], x["v"], x["alpha"],
+                                                      x["beta"], *before, W, rot=wht)
+        worst_tf = max(worst_tf, max_rel_err(go, ro))
+        assert np.array_equal(host(st.fill), rfill)
+        closing = before[6] + 1 == W
+        assert np.array_equal(host(st.codes)[~closing], before[0][~closing])
+        if closing.any():
+            assert_codes(host(st.codes)[closing], rc[closing], f"step {t} codes")
+            assert_scales(host(st.scales)[closing], rs[closing], f"step {t} scales")
+        # free-running
+        fo, *fr = O.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], *fr, W, rot=wht)
+        worst_fr = max(worst_fr, max_rel_err(go, fo))
+    assert worst_tf <= OUT_TOL_BF16, worst_tf
+    assert worst_fr <= OUT_TOL_BF16, worst_fr
+    assert_codes(host(st.codes), fr[0], "free-running codes after 5 windows")
+    rel = np.max(np.abs(host(st.scales) - fr[1]) / np.where(fr[1] > 0, fr[1], 1))
+    assert rel <= 1e-3, rel
