@@ -116,7 +116,7 @@ gdnq_status gdnq_quantize_state(const float* S, int64_t rows, int32_t d_k, int8_
  *       at slots >= fill_out are unspecified afterwards.
  *   The output of a closing token uses S before requantization.
  *
- *   p->batch B >= 0 (0: no-op), p->heads H >= 1, p->d_k, p->d_v in {64,128},
+ *   0 <= p->batch B <= 1024 (0: no-op), p->heads H >= 1, p->d_k, p->d_v in {64,128},
  *   1 <= p->window W <= 64, p->in_dtype (q,k,v) and p->out_dtype (o) in
  *   {GDNQ_F32, GDNQ_BF16}, p->flags in {0, GDNQ_FLAG_WHT}.
  *     q, k      [B,H,d_k] in_dtype      v [B,H,d_v] in_dtype

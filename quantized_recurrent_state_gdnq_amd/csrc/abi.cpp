@@ -119,6 +119,8 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
     return fail(GDNQ_ERR_DTYPE, "in_dtype = %d, out_dtype = %d", p->in_dtype, p->out_dtype);
   if (p->flags & ~uint32_t(GDNQ_FLAG_WHT))
     return fail(GDNQ_ERR_FLAGS, "flags 0x%x: decode accepts only GDNQ_FLAG_WHT", p->flags);
+  if (B > gdnq::decode_max_batch())
+    return fail(GDNQ_ERR_SHAPE, "batch = %d, at most %d sequences per call", B, gdnq::decode_max_batch());
   if (int64_t(B) * H * gdnq::decode_row_split() > 0x7fffffffLL)
     return fail(GDNQ_ERR_SHAPE, "batch * heads = %lld too large", (long long)B * H);
   if (B == 0) return ok();

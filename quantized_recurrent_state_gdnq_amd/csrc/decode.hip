@@ -5,20 +5,25 @@
 // state is requantized once, when the window closes.  Low-Bit GDN ...
 // (abstract): the buffered writes go through the full GDN transition.
 //
-// Open window (f + 1 < W), one 256-thread workgroup per (sequence, head):
-//   with A_j = alpha_j (I - beta_j k_j k_j^T) (symmetric), the replay
-//   S_t = S_0 A_1..A_t + sum_j beta_j v_j k_j^T A_{j+1}..A_t gives
-//       o = S_t q = S_0 y_0 + sum_j c_j v_j,
-//       y = q, then for j = t, t-1, ..., 1:  c_j = beta_j (k_j . y),
-//                                             y <- alpha_j (y - c_j k_j),
-//   so the d_v x d_k state is read once, as int8, and never rebuilt.
-//   Wave 0 runs that backward sweep over the buffered keys (staged in LDS);
-//   the other waves have already issued the int8 rows and buffered values.
-// Window close (f + 1 == W), R workgroups per head, each owning d_v / R rows
-//   (rows of the state evolve independently): replay the W writes on the
-//   dequantized rows in fp32, take the output from that state, requantize
-//   the rows (absmax/127, round-half-even) in place.
+// Work is a list of jobs built on the device from the fills, identical in
+// every workgroup of a persistent grid (workgroup g takes jobs g, g+G, ...):
+//   * close jobs first: a sequence whose window closes (f + 1 == W) has each
+//     head split into row blocks (rows of the state evolve independently);
+//     a close job replays the W writes on its dequantized rows in fp32,
+//     takes the output from that state and requantizes the rows in place;
+//   * then one open job per remaining head: with A_j = alpha_j (I - beta_j
+//     k_j k_j^T) (symmetric) the replay unrolls to
+//         o = S_t q = S_0 y_0 + sum_j c_j v_j,
+//         y = q, then for j = t, t-1, ..., 1:  c_j = beta_j (k_j . y),
+//                                               y <- alpha_j (y - c_j k_j),
+//     so the d_v x d_k state is read once, as int8, and never rebuilt.  One
+//     wave runs that backward sweep; every wave streams int8 rows.
+// Buffered keys and values are loaded into registers at the start of a job
+// (bounded buffer loads: slots past the fill cost no traffic) and pass
+// through LDS 16 slots at a time.
 #include <hip/hip_runtime.h>
+
+#include <cstdlib>
 
 #include "device_common.h"
 #include "launch.h"
@@ -26,7 +31,8 @@
 namespace gdnq {
 
 constexpr int DEC_THREADS = 256;
-constexpr int DEC_R = 8;  // workgroups per head (row split) for the window close
+constexpr int DEC_MAXB = 1024;   // sequences per call (fill scan results in LDS)
+constexpr int PH = 16;           // buffer slots staged in LDS per phase
 
 struct DecodeArgs {
   const void* q;
@@ -52,173 +58,518 @@ __device__ __forceinline__ float load_in(const void* p, size_t i) {
   else return static_cast<const float*>(p)[i];
 }
 
+// N consecutive inputs starting at element i (N = 4 or 8, i a multiple of N)
+template <bool BF16, int N>
+__device__ __forceinline__ void load_in_vec(const void* p, size_t i, float (&x)[N]) {
+  if constexpr (BF16) {
+    const uint16_t* b = static_cast<const uint16_t*>(p) + i;
+    if constexpr (N == 8) {
+      const uint4 w = *reinterpret_cast<const uint4*>(b);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_lo(ww[e]);
+        x[2 * e + 1] = bf16_hi(ww[e]);
+      }
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(b);
+      x[0] = bf16_lo(w.x);
+      x[1] = bf16_hi(w.x);
+      x[2] = bf16_lo(w.y);
+      x[3] = bf16_hi(w.y);
+    }
+  } else {
+    const float4* f = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+#pragma unroll
+    for (int e = 0; e < N / 4; ++e) {
+      const float4 v = f[e];
+      x[4 * e] = v.x;
+      x[4 * e + 1] = v.y;
+      x[4 * e + 2] = v.z;
+      x[4 * e + 3] = v.w;
+    }
+  }
+}
+
+// N consecutive inputs kept as raw words (RAW_WORDS<BF16, N> of them).
+template <bool BF16, int N>
+struct RawVec {
+  static constexpr int WORDS = BF16 ? N / 2 : N;
+  uint32_t w[WORDS];
+};
+template <bool BF16, int N>
+__device__ __forceinline__ void load_raw_vec(const void* p, size_t i, RawVec<BF16, N>& r) {
+  constexpr int WORDS = RawVec<BF16, N>::WORDS;
+  const char* src = static_cast<const char*>(p) + i * (BF16 ? 2 : 4);
+  if constexpr (WORDS == 1) {
+    r.w[0] = *reinterpret_cast<const uint32_t*>(src);
+  } else if constexpr (WORDS == 2) {
+    const uint2 u = *reinterpret_cast<const uint2*>(src);
+    r.w[0] = u.x;
+    r.w[1] = u.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < WORDS / 4; ++q) {
+      const uint4 u = reinterpret_cast<const uint4*>(src)[q];
+      r.w[4 * q] = u.x;
+      r.w[4 * q + 1] = u.y;
+      r.w[4 * q + 2] = u.z;
+      r.w[4 * q + 3] = u.w;
+    }
+  }
+}
+// Converts after an empty asm that "redefines" the words: no conversion, and
+// so no wait for the load, can be scheduled before this point.
+template <bool BF16, int N>
+__device__ __forceinline__ void unpack_raw_vec(RawVec<BF16, N>& r, float (&x)[N]) {
+#pragma unroll
+  for (int q = 0; q < RawVec<BF16, N>::WORDS; ++q) asm volatile("" : "+v"(r.w[q]));
+#pragma unroll
+  for (int q = 0; q < RawVec<BF16, N>::WORDS; ++q) {
+    if constexpr (BF16) {
+      x[2 * q] = bf16_lo(r.w[q]);
+      x[2 * q + 1] = bf16_hi(r.w[q]);
+    } else {
+      x[q] = __uint_as_float(r.w[q]);
+    }
+  }
+}
+
+// Raw input bits (bf16 pattern or fp32 bits): loading without converting keeps
+// the compiler from waiting on the load where it is issued.
+template <bool BF16>
+__device__ __forceinline__ uint32_t load_raw(const void* p, size_t i) {
+  if constexpr (BF16) return static_cast<const uint16_t*>(p)[i];
+  else return static_cast<const uint32_t*>(p)[i];
+}
+template <bool BF16>
+__device__ __forceinline__ float raw_to_f32(uint32_t r) {
+  asm volatile("" : "+v"(r));
+  return BF16 ? __uint_as_float(r << 16) : __uint_as_float(r);
+}
+
 template <bool BF16>
 __device__ __forceinline__ void store_out(void* p, size_t i, float x) {
   if constexpr (BF16) static_cast<uint16_t*>(p)[i] = uint16_t(f32_to_bf16_bits(x));
   else static_cast<float*>(p)[i] = x;
 }
 
-// LDS layout (floats), shared by both paths; the host sizes it with the same
-// formula (decode_lds_bytes).
+// A value the compiler cannot prove wave-uniform (it comes from LDS) but is:
+// moving it to a scalar register keeps all address arithmetic scalar.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ float lane_value(float x, int j) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
+}
+
+// Marks a loaded register as consumed here, so that no load of this job is
+// still pending when the next job starts reusing registers (a pending load
+// would make the next job wait, in order, for everything issued before it).
+__device__ __forceinline__ void consume(float4 x) { asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w)); }
+__device__ __forceinline__ void consume(float x) { asm volatile("" ::"v"(x)); }
+
+// k-th set bit (0-based) of m; m must have more than k bits set.
+__device__ __forceinline__ int kth_bit(uint64_t m, int k) {
+  for (int i = 0; i < k; ++i) m &= m - 1;
+  return __builtin_ctzll(m);
+}
+
 template <int DK, int DV>
-struct DecLds {
-  static constexpr int RW = DV / DEC_R;
-  __device__ static int k_off() { return 0; }                  // [W][DK] keys
-  __device__ static int ab_off(int W) { return W * DK; }       // alpha[64], beta[64]
-  __device__ static int y_off(int W) { return W * DK + 128; }  // [DK] y (open) / q (close)
-  __device__ static int c_off(int W) { return W * DK + 128 + DK; }       // [64] c_j
-  __device__ static int v_off(int W) { return W * DK + 192 + DK; }  // partial sums [NT*4] | v rows [W][RW]
-  __device__ static int dot_off(int W) {
-    const int vsz = (4 * DEC_THREADS > W * RW) ? 4 * DEC_THREADS : W * RW;
-    return W * DK + 192 + DK + vsz;
-  }
+struct DecShape {
+  static constexpr int NT = DEC_THREADS;
+  static constexpr int CPR = DK / 16;            // 16-code chunks per row
+  static constexpr int NC = DV * CPR / NT;       // chunks per thread (open job)
+  static constexpr int EK = DK / 64;             // elements of q, k per lane of a wave
+  static constexpr int KF4 = DK / 4;             // float4 per key
+  static constexpr int KREG = 64 * KF4 / NT;     // key float4 loads per thread
+  static constexpr int VRG = DV / 4;             // float4 row groups of values
+  static constexpr int VNG = NT / VRG;           // slot groups (open job)
+  static constexpr int VREG = 64 / VNG;          // value float4 registers (open job)
+  static constexpr int CR = NT / CPR;            // rows per close job
+  static constexpr int RC = DV / CR;             // close jobs per head
+  static constexpr int CVF4 = CR / 4;            // float4 per slot of a close job's values
+  static constexpr int CVREG = (64 * CVF4 + NT - 1) / NT;
+  static_assert(NC >= 1 && KREG >= 1 && VREG >= 1 && RC >= 1, "decode tiling");
+  // static LDS (floats); the keys [W][DK] live in dynamic LDS
+  static constexpr int XSZ = (VNG * DV > PH * CR) ? VNG * DV : PH * CR;
+  static constexpr int L_X = 0;                   // open: partial sums [VNG][DV]; close: values [PH][CR]
+  static constexpr int L_Y = L_X + XSZ;           // [DK] y (open) / q (close)
+  static constexpr int L_C = L_Y + DK;            // [64] c_j
+  static constexpr int L_D = L_C + 64;            // [DV] row dots
+  static constexpr int L_END = L_D + DV;
 };
 
-template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT>
-__global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
-  constexpr int NT = DEC_THREADS;
-  constexpr int EK = DK / 64;  // elements of a d_k vector per lane in a wave
-  extern __shared__ float4 smem4[];
-  float* smem = reinterpret_cast<float*>(smem4);
+// Job list shared by every workgroup: closing sequences first (bit masks and
+// prefix counts per 64 sequences), plus each sequence's fill.
+struct JobList {
+  uint64_t* cmask;
+  int* cpre;
+  uint8_t* fills;
+  int B, H, RC, n_close_jobs, n_jobs;
+};
 
-  const int nblk = a.B * a.H * DEC_R;
-  const int logical = xcd_swizzle(blockIdx.x, nblk);
-  const int bh = logical / DEC_R;
-  const int r = logical % DEC_R;
-  const int b = bh / a.H;
-  const int h = bh % a.H;
+struct JobId {
+  int seq, h, rb, f;
+};
+
+__device__ __forceinline__ JobId job_id(const JobList& L, int job) {
+  JobId j;
+  if (job < L.n_close_jobs) {
+    const int rank = job / (L.H * L.RC);
+    j.h = (job / L.RC) % L.H;
+    j.rb = job % L.RC;
+    int c = 0;
+    while (uniform(L.cpre[c + 1]) <= rank) ++c;
+    j.seq = uniform(c * 64 + kth_bit(L.cmask[c], rank - L.cpre[c]));
+  } else {
+    const int oj = job - L.n_close_jobs;
+    const int rank = oj / L.H;
+    j.h = oj % L.H;
+    j.rb = 0;
+    int c = 0;
+    while ((c + 1) * 64 - uniform(L.cpre[c + 1]) <= rank) ++c;
+    const uint64_t valid = (c * 64 + 64 <= L.B) ? ~0ull : ((1ull << (L.B - c * 64)) - 1);
+    j.seq = uniform(c * 64 + kth_bit(~L.cmask[c] & valid, rank - (c * 64 - L.cpre[c])));
+  }
+  j.f = uniform(L.fills[j.seq]);
+  return j;
+}
+
+// Everything an open job loads from memory, issued at once (registers).
+template <int DK, int DV, bool IN_BF16>
+struct OpenRegs {
+  using S = DecShape<DK, DV>;
+  float4 kt[S::KREG];     // buffered keys
+  uint4 cw[S::NC];        // int8 chunks
+  float4 vt[S::VREG];     // buffered values
+  RawVec<IN_BF16, S::EK> qraw, kraw;
+  uint32_t vcur_raw;
+  float srow, a_slot, b_slot, alpha_t, beta_t;
+};
+
+template <int DK, int DV, bool IN_BF16>
+__device__ __forceinline__ void load_open(const DecodeArgs& a, const JobId& j, int tid,
+                                          OpenRegs<DK, DV, IN_BF16>& R) {
+  using S = DecShape<DK, DV>;
+  constexpr int NT = S::NT;
   const int W = a.W;
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-
-  int f = a.fill_in[b];
-  f = f < 0 ? 0 : (f > W - 1 ? W - 1 : f);  // out-of-range fill is a data error; stay in bounds
-  const bool closing = (f + 1 == W);
-  if (!closing && r != 0) return;
-
-  float* k_lds = smem + DecLds<DK, DV>::k_off();
-  float* ab_lds = smem + DecLds<DK, DV>::ab_off(W);
-  float* y_lds = smem + DecLds<DK, DV>::y_off(W);
-  float* c_lds = smem + DecLds<DK, DV>::c_off(W);
-  float* v_lds = smem + DecLds<DK, DV>::v_off(W);
-  float* dot_lds = smem + DecLds<DK, DV>::dot_off(W);
-
+  const int bh = j.seq * a.H + j.h;
   const size_t qk_base = size_t(bh) * DK;
   const size_t v_base = size_t(bh) * DV;
-  const size_t bufk_base = size_t(bh) * W * DK;
-  const size_t bufv_base = size_t(bh) * W * DV;
   const size_t bufs_base = size_t(bh) * W;
-  const float alpha_t = a.alpha[bh];
-  const float beta_t = a.beta[bh];
-
-  // Buffered keys of slots 0..f-1 (both paths), bounded so that lanes past
-  // the fill fetch nothing.
-  constexpr int KMAX = (64 * DK / 4 + NT - 1) / NT;
-  const rsrc_t rk = make_rsrc(a.buf_k + bufk_base, uint32_t(f) * DK * 4);
-  const rsrc_t ra = make_rsrc(a.buf_alpha + bufs_base, uint32_t(f) * 4);
-  const rsrc_t rb = make_rsrc(a.buf_beta + bufs_base, uint32_t(f) * 4);
-  float4 kt[KMAX];
+  R.alpha_t = a.alpha[bh];
+  R.beta_t = a.beta[bh];
+  load_raw_vec<IN_BF16, S::EK>(a.q, qk_base + lane * S::EK, R.qraw);
+  load_raw_vec<IN_BF16, S::EK>(a.k, qk_base + lane * S::EK, R.kraw);
+  // buffered keys: float4 t + NT*i of slots 0..f-1 (bounded: no traffic past the fill);
+  // one per-lane offset, the register index in the scalar offset
+  const rsrc_t rk = make_rsrc(a.buf_k + size_t(bh) * W * DK, uint32_t(j.f) * DK * 4);
 #pragma unroll
-  for (int i = 0; i < KMAX; ++i) kt[i] = bload_f4(rk, uint32_t(tid + i * NT) * 16);
-  const float a_slot = bload_f1(ra, uint32_t(tid & 63) * 4);
-  const float b_slot = bload_f1(rb, uint32_t(tid & 63) * 4);
-
-  // current q, k in wave 0
-  float qv[EK], kv[EK];
-  if (wave == 0) {
+  for (int i = 0; i < S::KREG; ++i) R.kt[i] = bload_f4(rk, uint32_t(tid) * 16, uint32_t(i * NT * 16));
+  R.a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs_base, uint32_t(j.f) * 4), uint32_t(lane) * 4);
+  R.b_slot = bload_f1(make_rsrc(a.buf_beta + bufs_base, uint32_t(j.f) * 4), uint32_t(lane) * 4);
+  const rsrc_t rc = make_rsrc(a.codes + v_base * DK, uint32_t(DV) * DK);
 #pragma unroll
-    for (int e = 0; e < EK; ++e) {
-      qv[e] = load_in<IN_BF16>(a.q, qk_base + lane * EK + e);
-      kv[e] = load_in<IN_BF16>(a.k, qk_base + lane * EK + e);
+  for (int i = 0; i < S::NC; ++i) R.cw[i] = bload_u4(rc, uint32_t(tid) * 16, uint32_t(i * NT * 16));
+  const int rg = tid % S::VRG;
+  const int g = tid / S::VRG;
+  const rsrc_t rv = make_rsrc(a.buf_v + size_t(bh) * W * DV, uint32_t(j.f) * DV * 4);
+#pragma unroll
+  for (int i = 0; i < S::VREG; ++i)
+    R.vt[i] = bload_f4(rv, uint32_t(g * DV + rg * 4) * 4, uint32_t(i * S::VNG * DV * 4));
+  R.vcur_raw = 0;
+  R.srow = 0.f;
+  if (tid < DV) {
+    R.vcur_raw = load_raw<IN_BF16>(a.v, v_base + tid);
+    R.srow = a.scales[v_base + tid];
+  }
+}
+
+template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT>
+__global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
+  using S = DecShape<DK, DV>;
+  constexpr int NT = S::NT;
+  __shared__ float4 smem4[(S::L_END + 3) / 4];
+  __shared__ uint64_t cmask[DEC_MAXB / 64];
+  __shared__ int cpre[DEC_MAXB / 64 + 1];
+  __shared__ uint8_t fills[DEC_MAXB];
+  extern __shared__ float4 dyn4[];  // buffered keys [W][DK]
+  float* smem = reinterpret_cast<float*>(smem4);
+  float* k_lds = reinterpret_cast<float*>(dyn4);
+  float* x_lds = smem + S::L_X;
+  float* y_lds = smem + S::L_Y;
+  float* c_lds = smem + S::L_C;
+  float* d_lds = smem + S::L_D;
+
+  const int B = a.B, H = a.H, W = a.W;
+
+  // ---- job list: which sequences close their window at this step
+  const int nchunk = (B + 63) >> 6;
+  if (threadIdx.x < 64) {
+    for (int c = 0; c < nchunk; ++c) {
+      const int s = c * 64 + threadIdx.x;
+      int f = s < B ? a.fill_in[s] : 0;
+      f = f < 0 ? 0 : (f > W - 1 ? W - 1 : f);  // out-of-range fill is a data error; stay in bounds
+      if (s < B) fills[s] = uint8_t(f);
+      const uint64_t m = __ballot(s < B && f == W - 1);
+      if (threadIdx.x == 0) cmask[c] = m;
+    }
+    if (threadIdx.x == 0) {
+      int acc = 0;
+      for (int c = 0; c < nchunk; ++c) {
+        cpre[c] = acc;
+        acc += __popcll(cmask[c]);
+      }
+      cpre[nchunk] = acc;
     }
   }
+  __syncthreads();
+  JobList L;
+  L.cmask = cmask;
+  L.cpre = cpre;
+  L.fills = fills;
+  L.B = B;
+  L.H = H;
+  L.RC = S::RC;
+  const int ncs = uniform(cpre[nchunk]);
+  L.n_close_jobs = ncs * H * S::RC;
+  L.n_jobs = L.n_close_jobs + (B - ncs) * H;
 
-  if (!closing) {
-    // ================================================================ open window
-    constexpr int CPR = DK / 16;                  // 16-byte code chunks per row
-    constexpr int NC = DV * DK / (16 * NT);       // chunks per thread
-    constexpr int RG = DV / 4;                    // float4 row groups of v
-    constexpr int NG = NT / RG;                   // slot groups
-    constexpr int VMAX = (64 + NG - 1) / NG;
-    static_assert(NC >= 1, "state too small for the tiling");
+  int job = blockIdx.x;
 
-    const uint4* gc = reinterpret_cast<const uint4*>(a.codes + v_base * DK);
-    uint4 cw[NC];
+  // ================================================================ close jobs
+  // thread t: row rb*CR + t / CPR, columns [(t % CPR) * 16, +16).  Each row
+  // replays the W writes from its dequantized value.  Carrying u = s / G_j
+  // (G_j = alpha_1 .. alpha_j) turns
+  //   s <- alpha s + beta (v - alpha (s.k)) k
+  // into one FMA per entry:  u <- u + (beta (v - alpha G_{j-1} (u.k)) / G_j) k.
+  for (; job < L.n_close_jobs; job += gridDim.x) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // keep per-thread offsets from being hoisted out of the loop
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const JobId J = job_id(L, job);
+    const int f = J.f;  // == W - 1
+    const int bh = J.seq * H + J.h;
+    const size_t qk_base = size_t(bh) * DK;
+    const size_t v_base = size_t(bh) * DV;
+    const size_t bufs_base = size_t(bh) * W;
+    const int rr = tid / S::CPR;
+    const int seg = tid % S::CPR;
+    const int row = J.rb * S::CR + rr;
+    const float alpha_t = a.alpha[bh];
+    const float beta_t = a.beta[bh];
+    RawVec<IN_BF16, S::EK> qraw, kraw;
+    load_raw_vec<IN_BF16, S::EK>(a.q, qk_base + lane * S::EK, qraw);
+    load_raw_vec<IN_BF16, S::EK>(a.k, qk_base + lane * S::EK, kraw);
+    const rsrc_t rk = make_rsrc(a.buf_k + size_t(bh) * W * DK, uint32_t(f) * DK * 4);
+    float4 kt[S::KREG];
 #pragma unroll
-    for (int i = 0; i < NC; ++i) cw[i] = gc[tid + i * NT];
-
-    const int rg = tid % RG;
-    const int g = tid / RG;
-    const rsrc_t rv = make_rsrc(a.buf_v + bufv_base, uint32_t(f) * DV * 4);
-    float4 vt[VMAX];
+    for (int i = 0; i < S::KREG; ++i) kt[i] = bload_f4(rk, uint32_t(tid) * 16, uint32_t(i * NT * 16));
+    const float a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
+    const float b_slot = bload_f1(make_rsrc(a.buf_beta + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
+    const uint4 cwr = *reinterpret_cast<const uint4*>(a.codes + (v_base + row) * DK + seg * 16);
+    const float srow = a.scales[v_base + row];
+    const rsrc_t rv = make_rsrc(a.buf_v + size_t(bh) * W * DV, uint32_t(W - 1) * DV * 4);
+    float4 vt[S::CVREG];
 #pragma unroll
-    for (int i = 0; i < VMAX; ++i) vt[i] = bload_f4(rv, uint32_t((g + i * NG) * DV + rg * 4) * 4);
-    float vcur = 0.f, srow = 0.f;
-    if (tid < DV) {
-      vcur = load_in<IN_BF16>(a.v, v_base + tid);
-      srow = a.scales[v_base + tid];
-    }
+    for (int i = 0; i < S::CVREG; ++i)  // slot (tid + NT*i) / CVF4, rows 4*((tid + NT*i) % CVF4)
+      vt[i] = bload_f4(rv, uint32_t((tid / S::CVF4) * DV + (tid % S::CVF4) * 4) * 4,
+                       uint32_t(((i * NT / S::CVF4) * DV + J.rb * S::CR) * 4));
+    uint32_t vcur_raw = 0;
+    if (tid < S::CR) vcur_raw = load_raw<IN_BF16>(a.v, v_base + J.rb * S::CR + tid);
 
-    // stage keys and slot scalars in LDS
+    float qv[S::EK], kv[S::EK];
+    unpack_raw_vec<IN_BF16, S::EK>(qraw, qv);
+    unpack_raw_vec<IN_BF16, S::EK>(kraw, kv);
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
+    for (int i = 0; i < S::KREG; ++i) {
       const int idx = tid + i * NT;
-      if (idx < f * (DK / 4)) reinterpret_cast<float4*>(k_lds)[idx] = kt[i];
+      if (idx < f * S::KF4) reinterpret_cast<float4*>(k_lds)[idx] = kt[i];
+      consume(kt[i]);
     }
-    if (tid < 64) {
-      ab_lds[tid] = a_slot;
-      ab_lds[64 + tid] = b_slot;
+    if constexpr (WHT) {
+      fwht_group<S::EK, 64>(qv, lane);
+      fwht_group<S::EK, 64>(kv, lane);
     }
-    if (wave == 0) {
-      if constexpr (WHT) {
-        fwht_group<EK, 64>(qv, lane);
-        fwht_group<EK, 64>(kv, lane);
+    if (wave == 0) {  // the current token's key is the window's last write; q for the output
+#pragma unroll
+      for (int e = 0; e < S::EK; ++e) {
+        k_lds[(W - 1) * DK + lane * S::EK + e] = kv[e];
+        y_lds[lane * S::EK + e] = qv[e];
       }
+    }
+    float u[16];
+    {
+      const uint32_t w[4] = {cwr.x, cwr.y, cwr.z, cwr.w};
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) u[4 * q4 + c] = i8_at(w[q4], c) * srow;
+    }
+    const float vcur = raw_to_f32<IN_BF16>(vcur_raw);
+    float G = 1.f;
+#pragma unroll
+    for (int ph = 0; ph < 64 / PH; ++ph) {
+      if (ph * PH < W) {  // uniform
+        __syncthreads();  // keys staged / previous phase's values consumed
+#pragma unroll
+        for (int i = 0; i < S::CVREG; ++i) {
+          const int idx = tid + i * NT;
+          const int slot = idx / S::CVF4;
+          if (slot >= ph * PH && slot < ph * PH + PH && slot < W - 1)
+            reinterpret_cast<float4*>(x_lds)[idx - ph * PH * S::CVF4] = vt[i];
+        }
+        if (W - 1 >= ph * PH && W - 1 < ph * PH + PH && tid < S::CR)
+          x_lds[(W - 1 - ph * PH) * S::CR + tid] = vcur;
+        __syncthreads();
+        const int jhi = min(W, ph * PH + PH);
+        for (int j = ph * PH; j < jhi; ++j) {
+          float kj[16];
+          const float4* k4 = reinterpret_cast<const float4*>(k_lds + j * DK + seg * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float4 x = k4[e];
+            kj[4 * e] = x.x;
+            kj[4 * e + 1] = x.y;
+            kj[4 * e + 2] = x.z;
+            kj[4 * e + 3] = x.w;
+          }
+          const float aj = (j == W - 1) ? alpha_t : lane_value(a_slot, j);
+          const float bj = (j == W - 1) ? beta_t : lane_value(b_slot, j);
+          const float vj = x_lds[(j - ph * PH) * S::CR + rr];
+          float p = 0.f;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) p += u[c] * kj[c];
+          const float sk = G * group_sum<S::CPR>(p);  // s . k_j
+          const float Gn = G * aj;
+          const float coef = __fdividef(bj * (vj - aj * sk), Gn);
+#pragma unroll
+          for (int c = 0; c < 16; ++c) u[c] = fmaf(coef, kj[c], u[c]);
+          G = Gn;
+        }
+      }
+    }
+    float po = 0.f, amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      u[c] *= G;  // back to the state s
+      po += u[c] * y_lds[seg * 16 + c];
+      amax = fmaxf(amax, fabsf(u[c]));
+    }
+    po = group_sum<S::CPR>(po);
+    amax = group_max<S::CPR>(amax);
+    const float scale = codec_scale(amax);
+    uint4 wout;
+    wout.x = pack4_i8(codec_code(u[0], scale), codec_code(u[1], scale), codec_code(u[2], scale), codec_code(u[3], scale));
+    wout.y = pack4_i8(codec_code(u[4], scale), codec_code(u[5], scale), codec_code(u[6], scale), codec_code(u[7], scale));
+    wout.z = pack4_i8(codec_code(u[8], scale), codec_code(u[9], scale), codec_code(u[10], scale), codec_code(u[11], scale));
+    wout.w = pack4_i8(codec_code(u[12], scale), codec_code(u[13], scale), codec_code(u[14], scale), codec_code(u[15], scale));
+    *reinterpret_cast<uint4*>(a.codes + (v_base + row) * DK + seg * 16) = wout;
+    if (seg == 0) {
+      a.scales[v_base + row] = scale;
+      store_out<OUT_BF16>(a.o, v_base + row, po);
+    }
+    if (tid == 0 && J.rb == 0 && J.h == 0) a.fill_out[J.seq] = 0;
+    __syncthreads();  // LDS is reused by the next job
+  }
+
+  // ================================================================ open jobs
+  // Software-pipelined: the next job's loads are issued as soon as this job
+  // has consumed its registers, before this job's stores.
+  if (job >= L.n_jobs) return;
+  OpenRegs<DK, DV, IN_BF16> R;
+  JobId J = job_id(L, job);
+  {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    load_open<DK, DV, IN_BF16>(a, J, tid, R);
+  }
+  while (true) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // keep per-thread offsets from being hoisted out of the loop
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int next = job + gridDim.x;
+    const bool has_next = next < L.n_jobs;
+    const int f = J.f;
+    const int bh = J.seq * H + J.h;
+    const size_t v_base = size_t(bh) * DV;
+    const size_t bufk_base = size_t(bh) * W * DK;
+    const size_t bufv_base = size_t(bh) * W * DV;
+    const size_t bufs_base = size_t(bh) * W;
+    const float alpha_t = R.alpha_t;
+    const float beta_t = R.beta_t;
+    float qv[S::EK], kv[S::EK];
+    unpack_raw_vec<IN_BF16, S::EK>(R.qraw, qv);
+    unpack_raw_vec<IN_BF16, S::EK>(R.kraw, kv);
+#pragma unroll
+    for (int i = 0; i < S::KREG; ++i) {
+      const int idx = tid + i * NT;
+      if (idx < f * S::KF4) reinterpret_cast<float4*>(k_lds)[idx] = R.kt[i];
+      consume(R.kt[i]);
+    }
+    consume(R.a_slot);
+    consume(R.b_slot);
+    if constexpr (WHT) {
+      fwht_group<S::EK, 64>(qv, lane);
+      fwht_group<S::EK, 64>(kv, lane);
     }
     __syncthreads();
 
-    if (wave == 0) {
-      // backward sweep: current write first, then buffered writes newest -> oldest
-      float y[EK];
+    // The sweeping wave rotates with the workgroup id so that the sweeps of
+    // the workgroups resident on one CU spread over its four SIMDs.
+    if (wave == (blockIdx.x & 3)) {
+      // backward sweep, carried as yt = y / (product of the alphas swept so far):
+      //   t = k_j . yt;  c_j = beta_j t G;  yt -= beta_j t k_j;  G *= alpha_j
+      float yt[S::EK];
 #pragma unroll
-      for (int e = 0; e < EK; ++e) y[e] = qv[e];
-      float part = 0.f;
+      for (int e = 0; e < S::EK; ++e) yt[e] = qv[e];
+      float p = 0.f;
 #pragma unroll
-      for (int e = 0; e < EK; ++e) part += kv[e] * y[e];
-      float c = beta_t * wave_sum_uniform(part);
-      if (lane == 0) c_lds[63] = c;
+      for (int e = 0; e < S::EK; ++e) p += kv[e] * yt[e];
+      const float c_cur = beta_t * wave_allreduce_sum(p);
 #pragma unroll
-      for (int e = 0; e < EK; ++e) y[e] = alpha_t * (y[e] - c * kv[e]);
+      for (int e = 0; e < S::EK; ++e) yt[e] -= c_cur * kv[e];
+      float G = alpha_t, c_reg = 0.f;
+      const float* krow = k_lds + lane * S::EK;
+      float kn[S::EK];  // the next step's key, read one step ahead
+      if (f > 0) {
+#pragma unroll
+        for (int e = 0; e < S::EK; ++e) kn[e] = krow[(f - 1) * DK + e];
+      }
       for (int j = f - 1; j >= 0; --j) {
-        float kj[EK];
+        float kj[S::EK];
 #pragma unroll
-        for (int e = 0; e < EK; ++e) kj[e] = k_lds[j * DK + lane * EK + e];
-        float p = 0.f;
+        for (int e = 0; e < S::EK; ++e) kj[e] = kn[e];
+        const int jn = j > 0 ? j - 1 : 0;
 #pragma unroll
-        for (int e = 0; e < EK; ++e) p += kj[e] * y[e];
-        const float cj = ab_lds[64 + j] * wave_sum_uniform(p);
-        if (lane == 0) c_lds[j] = cj;
-        const float aj = ab_lds[j];
+        for (int e = 0; e < S::EK; ++e) kn[e] = krow[jn * DK + e];
+        float pp = 0.f;
 #pragma unroll
-        for (int e = 0; e < EK; ++e) y[e] = aj * (y[e] - cj * kj[e]);
+        for (int e = 0; e < S::EK; ++e) pp += kj[e] * yt[e];
+        const float bt = lane_value(R.b_slot, j) * wave_allreduce_sum(pp);
+#pragma unroll
+        for (int e = 0; e < S::EK; ++e) yt[e] -= bt * kj[e];
+        c_reg = (lane == j) ? bt * G : c_reg;
+        G *= lane_value(R.a_slot, j);
       }
 #pragma unroll
-      for (int e = 0; e < EK; ++e) {
-        y_lds[lane * EK + e] = y[e];
-        a.buf_k[bufk_base + size_t(f) * DK + lane * EK + e] = kv[e];  // append k
-      }
+      for (int e = 0; e < S::EK; ++e) y_lds[lane * S::EK + e] = G * yt[e];
+      if (lane < f) c_lds[lane] = c_reg;
+      if (lane == 0) c_lds[63] = c_cur;
     }
     __syncthreads();
 
-    // int8 rows . y  (row = chunk / CPR, 16 codes per chunk)
+    // int8 rows . y  (chunk = tid + NT*i: row chunk / CPR, 16 codes)
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
+    for (int i = 0; i < S::NC; ++i) {
       const int chunk = tid + i * NT;
-      const int row = chunk / CPR;
-      const int seg = chunk % CPR;
+      const int row = chunk / S::CPR;
+      const int seg = chunk % S::CPR;
       const float4* y4 = reinterpret_cast<const float4*>(y_lds + seg * 16);
-      const uint32_t w[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
+      const uint32_t w[4] = {R.cw[i].x, R.cw[i].y, R.cw[i].z, R.cw[i].w};
       float p = 0.f;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -226,177 +577,80 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
         p += i8_at(w[q4], 0) * yy.x + i8_at(w[q4], 1) * yy.y + i8_at(w[q4], 2) * yy.z +
              i8_at(w[q4], 3) * yy.w;
       }
-      p = group_sum<CPR>(p);
-      if (seg == 0) dot_lds[row] = p;
+      p = group_sum<S::CPR>(p);
+      if (seg == 0) d_lds[row] = p;
     }
     // buffered values weighted by c_j
     {
+      const int rg = tid % S::VRG;
+      const int g = tid / S::VRG;
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int i = 0; i < VMAX; ++i) {
-        const int j = g + i * NG;
+      for (int i = 0; i < S::VREG; ++i) {
+        const int j = g + i * S::VNG;
         const float cj = (j < f) ? c_lds[j] : 0.f;
-        acc.x += cj * vt[i].x;
-        acc.y += cj * vt[i].y;
-        acc.z += cj * vt[i].z;
-        acc.w += cj * vt[i].w;
+        acc.x += cj * R.vt[i].x;
+        acc.y += cj * R.vt[i].y;
+        acc.z += cj * R.vt[i].z;
+        acc.w += cj * R.vt[i].w;
       }
-      reinterpret_cast<float4*>(v_lds + g * DV)[rg] = acc;
+      reinterpret_cast<float4*>(x_lds + g * DV)[rg] = acc;
     }
     __syncthreads();
-
+    float out = 0.f, vcur = 0.f;
     if (tid < DV) {
       float vsum = 0.f;
 #pragma unroll
-      for (int gg = 0; gg < NG; ++gg) vsum += v_lds[gg * DV + tid];
-      const float out = srow * dot_lds[tid] + vsum + c_lds[63] * vcur;
+      for (int gg = 0; gg < S::VNG; ++gg) vsum += x_lds[gg * DV + tid];
+      vcur = raw_to_f32<IN_BF16>(R.vcur_raw);
+      out = R.srow * d_lds[tid] + vsum + c_lds[63] * vcur;
+    }
+    // the next job's loads go out before this job's stores
+    JobId JN = J;
+    if (has_next) {
+      JN = job_id(L, next);
+      load_open<DK, DV, IN_BF16>(a, JN, tid, R);
+    }
+    if (tid < DV) {
       store_out<OUT_BF16>(a.o, v_base + tid, out);
       a.buf_v[bufv_base + size_t(f) * DV + tid] = vcur;  // append v
+    }
+    if (wave == 0) {  // append k (rotated basis under WHT)
+      float* dst = a.buf_k + bufk_base + size_t(f) * DK + lane * S::EK;
+#pragma unroll
+      for (int e = 0; e < S::EK; ++e) dst[e] = kv[e];
     }
     if (tid == 0) {
       a.buf_alpha[bufs_base + f] = alpha_t;
       a.buf_beta[bufs_base + f] = beta_t;
-      if (h == 0) a.fill_out[b] = f + 1;
+      if (J.h == 0) a.fill_out[J.seq] = f + 1;
     }
-    return;
+    if (!has_next) break;
+    job = next;
+    J = JN;
+    __syncthreads();  // LDS is reused by the next job
   }
-
-  // ================================================================ window close
-  constexpr int RW = DV / DEC_R;        // rows owned by this workgroup
-  constexpr int LPR = NT / RW;          // lanes per row
-  constexpr int CPL = DK / LPR;         // columns per lane
-  constexpr int VCL = (64 * RW + NT - 1) / NT;
-  static_assert(CPL >= 2 && CPL % 2 == 0, "close tiling");
-  const int rr = tid / LPR;
-  const int col0 = (tid % LPR) * CPL;
-  const int row = r * RW + rr;
-
-  // this workgroup's rows of the buffered values, all W-1 buffered slots
-  const rsrc_t rv = make_rsrc(a.buf_v + bufv_base, uint32_t(W - 1) * DV * 4);
-  float vb[VCL];
-#pragma unroll
-  for (int i = 0; i < VCL; ++i) {
-    const int idx = tid + i * NT;
-    vb[i] = bload_f1(rv, uint32_t((idx / RW) * DV + r * RW + idx % RW) * 4);
-  }
-  float vcur = 0.f;
-  if (tid < RW) vcur = load_in<IN_BF16>(a.v, v_base + r * RW + tid);
-  // dequantized rows in registers
-  const float srow = a.scales[v_base + row];
-  float s[CPL];
-  {
-    const int8_t* crow = a.codes + (v_base + row) * DK + col0;
-    if constexpr (CPL == 8) {
-      const uint2 w = *reinterpret_cast<const uint2*>(crow);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        s[c] = i8_at(w.x, c) * srow;
-        s[4 + c] = i8_at(w.y, c) * srow;
-      }
-    } else if constexpr (CPL == 4) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(crow);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) s[c] = i8_at(w, c) * srow;
-    } else {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) s[c] = float(crow[c]) * srow;
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i) {
-    const int idx = tid + i * NT;
-    if (idx < f * (DK / 4)) reinterpret_cast<float4*>(k_lds)[idx] = kt[i];
-  }
-  if (tid < 64) {
-    ab_lds[tid] = a_slot;
-    ab_lds[64 + tid] = b_slot;
-  }
-#pragma unroll
-  for (int i = 0; i < VCL; ++i) {
-    const int idx = tid + i * NT;
-    if (idx < (W - 1) * RW) v_lds[idx] = vb[i];
-  }
-  if (tid < RW) v_lds[(W - 1) * RW + tid] = vcur;
-  __syncthreads();  // slot scalars are in place before wave 0 adds the current token's
-  if (wave == 0) {
-    if constexpr (WHT) {
-      fwht_group<EK, 64>(qv, lane);
-      fwht_group<EK, 64>(kv, lane);
-    }
-#pragma unroll
-    for (int e = 0; e < EK; ++e) {
-      k_lds[(W - 1) * DK + lane * EK + e] = kv[e];
-      y_lds[lane * EK + e] = qv[e];
-    }
-    if (lane == 0) {
-      ab_lds[W - 1] = alpha_t;
-      ab_lds[64 + W - 1] = beta_t;
-    }
-  }
-  __syncthreads();
-
-  for (int j = 0; j < W; ++j) {
-    float kj[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) kj[c] = k_lds[j * DK + col0 + c];
-    float p = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) p += s[c] * kj[c];
-    const float sk = group_sum<LPR>(p);
-    const float aj = ab_lds[j];
-    const float bj = ab_lds[64 + j];
-    const float erase = bj * sk;
-    const float write = bj * v_lds[j * RW + rr];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) s[c] = aj * (s[c] - erase * kj[c]) + write * kj[c];
-  }
-
-  float po = 0.f, amax = 0.f;
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    po += s[c] * y_lds[col0 + c];
-    amax = fmaxf(amax, fabsf(s[c]));
-  }
-  po = group_sum<LPR>(po);
-  amax = group_max<LPR>(amax);
-  const float scale = codec_scale(amax);
-  int8_t* crow = a.codes + (v_base + row) * DK + col0;
-  if constexpr (CPL == 8) {
-    uint2 w;
-    w.x = pack4_i8(codec_code(s[0], scale), codec_code(s[1], scale), codec_code(s[2], scale),
-                   codec_code(s[3], scale));
-    w.y = pack4_i8(codec_code(s[4], scale), codec_code(s[5], scale), codec_code(s[6], scale),
-                   codec_code(s[7], scale));
-    *reinterpret_cast<uint2*>(crow) = w;
-  } else if constexpr (CPL == 4) {
-    *reinterpret_cast<uint32_t*>(crow) = pack4_i8(codec_code(s[0], scale), codec_code(s[1], scale),
-                                                  codec_code(s[2], scale), codec_code(s[3], scale));
-  } else {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) crow[c] = int8_t(codec_code(s[c], scale));
-  }
-  if ((tid % LPR) == 0) {
-    a.scales[v_base + row] = scale;
-    store_out<OUT_BF16>(a.o, v_base + row, po);
-  }
-  if (tid == 0 && r == 0 && h == 0) a.fill_out[b] = 0;
 }
 
-size_t decode_lds_bytes(int d_k, int d_v, int W) {
-  const int RW = d_v / DEC_R;
-  const int vsz = (4 * DEC_THREADS > W * RW) ? 4 * DEC_THREADS : W * RW;
-  return sizeof(float) * size_t(W * d_k + 192 + d_k + vsz + d_v);
+int decode_row_split() { return 4; }  // close jobs per head at most (grid validation)
+int decode_max_batch() { return DEC_MAXB; }
+// Persistent grid: about four resident workgroups per CU on 256 CUs, never
+// more workgroups than jobs.  GDNQ_DECODE_GRID overrides it (tuning).
+static unsigned decode_grid(int B, int H, int rc) {
+  const long jobs_max = long(B) * H * rc;
+  long g = 1024;
+  if (const char* e = getenv("GDNQ_DECODE_GRID")) {
+    const long v = atol(e);
+    if (v > 0) g = v;
+  }
+  return unsigned(jobs_max < g ? jobs_max : g);
 }
-
-int decode_row_split() { return DEC_R; }
 
 template <int DK, int DV, bool IB, bool OB, bool WHT>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  const size_t lds = decode_lds_bytes(DK, DV, a.W);
-  const unsigned grid = unsigned(a.B) * unsigned(a.H) * DEC_R;
-  hipLaunchKernelGGL((decode_kernel<DK, DV, IB, OB, WHT>), dim3(grid), dim3(DEC_THREADS), lds, s,
-                     a);
+  const unsigned grid = decode_grid(a.B, a.H, DecShape<DK, DV>::RC);
+  const size_t lds = size_t(a.W) * DK * sizeof(float);  // buffered keys
+  hipLaunchKernelGGL((decode_kernel<DK, DV, IB, OB, WHT>), dim3(grid), dim3(DEC_THREADS), lds, s, a);
   return hipGetLastError();
 }
 

@@ -68,6 +68,16 @@ __device__ __forceinline__ float wave_sum_uniform(float x) {
   return (a + b) + (c + d);
 }
 
+// Full-wave sum in every lane, all in VALU: DPP inside each row of 16 lanes,
+// then v_permlane16_swap (row pairs) and v_permlane32_swap (halves), gfx950.
+__device__ __forceinline__ float wave_allreduce_sum(float x) {
+  x = group_sum<16>(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---------------------------------------------------------------- FWHT
 // Fast Walsh-Hadamard transform of a d-vector spread over a group of lanes:
 // lane j of the group holds elements [j*E, j*E + E) in v[0..E).  The
@@ -140,14 +150,14 @@ using rsrc_t = __amdgpu_buffer_rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
 }
-__device__ __forceinline__ float4 bload_f4(rsrc_t r, uint32_t off) {
-  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+__device__ __forceinline__ float4 bload_f4(rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
   float4 f;
   __builtin_memcpy(&f, &v, 16);
   return f;
 }
-__device__ __forceinline__ uint4 bload_u4(rsrc_t r, uint32_t off) {
-  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+__device__ __forceinline__ uint4 bload_u4(rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
   uint4 u;
   __builtin_memcpy(&u, &v, 16);
   return u;

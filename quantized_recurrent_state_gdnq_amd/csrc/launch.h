@@ -37,8 +37,8 @@ struct DecodeLaunch {
   bool in_bf16, out_bf16, wht;
 };
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
-size_t decode_lds_bytes(int d_k, int d_v, int W);
 int decode_row_split();
+int decode_max_batch();
 
 struct PrefillLaunch {
   const void* q;

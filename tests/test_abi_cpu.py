@@ -64,7 +64,7 @@ def _p(B=2, H=2, dk=128, dv=128, W=8, ind=1, outd=1, flags=0):
 
 
 @pytest.mark.parametrize("params,status", [
-    (_p(dk=96), 2), (_p(dv=32), 2), (_p(W=0), 2), (_p(W=65), 2), (_p(H=0), 2), (_p(B=-1), 2),
+    (_p(dk=96), 2), (_p(dv=32), 2), (_p(B=1025), 2), (_p(W=0), 2), (_p(W=65), 2), (_p(H=0), 2), (_p(B=-1), 2),
     (_p(ind=2), 3), (_p(outd=5), 3), (_p(flags=2), 8), (_p(flags=16), 8),
 ])
 def test_decode_rejects_bad_params(params, status):
