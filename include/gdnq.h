@@ -155,7 +155,8 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
  *   NULL), requantizing at every window end, windows aligned to token 0.
  *   Supported: d_k = d_v = 128, chunk = window = 64, T a multiple of 64.
  *   Writes o and the final codes/scales (the state after the last window).
- *   state_f32 must be NULL.  Flags: GDNQ_FLAG_WHT allowed.
+ *   state_f32 must be NULL.  Flags: none (a rotated GDN state is produced by
+ *   rotating q and k before the call and the state with gdnq_quantize_state).
  *
  *   SSD (GDNQ_FLAG_SSD): S_t = a_t S_{t-1} + v_t k_t^T from a zero state, no
  *   requantization (window ignored); beta, init_codes, init_scales, codes and

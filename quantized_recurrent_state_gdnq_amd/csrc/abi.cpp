@@ -170,8 +170,7 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
       return fail(GDNQ_ERR_FLAGS, "flags 0x%x", p->flags);
     if (dk != 128 || (dv != 64 && dv != 128)) return fail(GDNQ_ERR_SHAPE, "SSD: d_k = %d (128), d_v = %d (64 or 128)", dk, dv);
   } else {
-    if (p->flags & ~uint32_t(GDNQ_FLAG_WHT))
-      return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill accepts only GDNQ_FLAG_WHT", p->flags);
+    if (p->flags) return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill takes no flags", p->flags);
     if (dk != 128 || dv != 128) return fail(GDNQ_ERR_SHAPE, "GDN prefill: d_k = d_v = 128 required (got %d, %d)", dk, dv);
     if (p->window != p->chunk) return fail(GDNQ_ERR_SHAPE, "GDN prefill: window = %d must equal chunk = %d", p->window, p->chunk);
   }

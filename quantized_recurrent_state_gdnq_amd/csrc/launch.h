@@ -58,6 +58,10 @@ struct PrefillLaunch {
 };
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream);
 hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream);
-size_t prefill_workspace_bytes(const PrefillLaunch& L);
+size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L);
+size_t prefill_ssd_workspace_bytes(const PrefillLaunch& L);
+inline size_t prefill_workspace_bytes(const PrefillLaunch& L) {
+  return L.ssd ? prefill_ssd_workspace_bytes(L) : prefill_gdn_workspace_bytes(L);
+}
 
 }  // namespace gdnq

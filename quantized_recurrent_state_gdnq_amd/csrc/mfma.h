@@ -1,0 +1,54 @@
+// bf16 MFMA helpers for gfx950 (v_mfma_f32_16x16x32_bf16).
+//
+// Lane layout of one 16x16x32 product D[16][16] += A[16][32] * B[32][16]:
+//   A: lane l holds row (l % 16), k = 8 * (l / 16) .. +8   (8 bf16)
+//   B: lane l holds column (l % 16), k = 8 * (l / 16) .. +8 (8 bf16)
+//   D: lane l holds column (l % 16), rows 4 * (l / 16) .. +4 (4 fp32)
+// Storing every operand k-contiguous ([row][k] for A, [column][k] for B)
+// makes each fragment one 16-byte LDS read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdnq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds_bf16x8(const __bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// 8 int8 codes -> 8 bf16 (exact: |code| <= 127)
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint2 w) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (__bf16)float(int32_t(w.x << (24 - 8 * e)) >> 24);
+    r[4 + e] = (__bf16)float(int32_t(w.y << (24 - 8 * e)) >> 24);
+  }
+  return r;
+}
+
+// x = hi + mid + lo with each part a bf16: hi = bf16(x), mid = bf16(x - hi),
+// lo = bf16(x - hi - mid).  The three carry 24 significant bits, so a product
+// with an exact bf16 operand summed over the three parts matches fp32.
+__device__ __forceinline__ void split3(const float (&x)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = (__bf16)x[e];
+    const float r1 = x[e] - float(h);
+    const __bf16 m = (__bf16)r1;
+    const float r2 = r1 - float(m);
+    hi[e] = h;
+    mid[e] = m;
+    lo[e] = (__bf16)r2;
+  }
+}
+
+}  // namespace gdnq
