@@ -132,6 +132,30 @@ __device__ __forceinline__ int codec_code(float x, float scale) {
   return int(r);
 }
 
+// Codes of N elements of one row, as floats, equal element by element to
+// codec_code.  With inv = fl(1/scale), q = fl(x * inv) is within
+// |x/scale| * 2^-23 <= 1.6e-5 of the exact quotient and fl(x/scale) within
+// 7.6e-6 of it, so their nearest integers can differ only when q lies within
+// 2.4e-5 of a half-integer; only then (rarely) the IEEE divisions are done.
+template <int N>
+__device__ __forceinline__ void codec_codes(const float (&x)[N], float scale, float (&c)[N]) {
+  const float inv = scale > 0.0f ? __frcp_rn(scale) : 0.0f;
+  bool near = false;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const float q = x[e] * inv;
+    const float r = __builtin_rintf(q);
+    near |= fabsf(fabsf(q - r) - 0.5f) < 3.0e-5f;
+    c[e] = r;
+  }
+  if (near) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) c[e] = __builtin_rintf(__fdiv_rn(x[e], scale));
+  }
+#pragma unroll
+  for (int e = 0; e < N; ++e) c[e] = fminf(fmaxf(c[e], -127.0f), 127.0f);
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t(a) & 0xffu) | ((uint32_t(b) & 0xffu) << 8) | ((uint32_t(c) & 0xffu) << 16) |
          ((uint32_t(d) & 0xffu) << 24);

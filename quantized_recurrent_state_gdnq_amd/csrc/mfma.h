@@ -38,17 +38,30 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16(uint2 w) {
 // x = hi + mid + lo with each part a bf16: hi = bf16(x), mid = bf16(x - hi),
 // lo = bf16(x - hi - mid).  The three carry 24 significant bits, so a product
 // with an exact bf16 operand summed over the three parts matches fp32.
-__device__ __forceinline__ void split3(const float (&x)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+template <int N, typename V>
+__device__ __forceinline__ void split3(const float (&x)[N], V& hi, V& mid, V& lo) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < N; ++e) {
     const __bf16 h = (__bf16)x[e];
     const float r1 = x[e] - float(h);
     const __bf16 m = (__bf16)r1;
-    const float r2 = r1 - float(m);
     hi[e] = h;
     mid[e] = m;
-    lo[e] = (__bf16)r2;
+    lo[e] = (__bf16)(r1 - float(m));
   }
 }
+
+// x = hi + lo (16 significant bits)
+template <int N, typename V>
+__device__ __forceinline__ void split2(const float (&x)[N], V& hi, V& lo) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const __bf16 h = (__bf16)x[e];
+    hi[e] = h;
+    lo[e] = (__bf16)(x[e] - float(h));
+  }
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 }  // namespace gdnq

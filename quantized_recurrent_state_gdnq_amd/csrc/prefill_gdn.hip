@@ -14,13 +14,16 @@
 // Two kernels:
 //   prep  -- one workgroup per chunk-head, all in parallel: K K^T on bf16
 //            MFMA (bf16 inputs, exact products), A, and T by blocked forward
-//            substitution in fp32; T and g go to the workspace.
+//            substitution (diagonal 16x16 blocks on the VALU, off-diagonal
+//            blocks on fp32 MFMA); T (as three bf16 parts) and g go to the
+//            workspace.
 //   state -- one workgroup per (sequence, head, block of 32 rows): rows of
 //            the state evolve independently, so each workgroup carries its
-//            rows (int8 codes + scales in LDS) through all chunks.  K S0^T and
-//            Q S0^T use exact bf16 products with the int8 codes; the state
-//            update multiplies an fp32 operand split into three bf16 parts
-//            (24 significant bits) by exact bf16 keys.
+//            rows (codes + scales in LDS) through all chunks, four barriers
+//            per chunk, the next chunk's inputs prefetched into registers.
+//            Every product runs on bf16 MFMA: K S0^T and Q S0^T take the codes
+//            exactly; T (rhs), (U o d)^T K and M U split their fp32 operands
+//            into two or three bf16 parts, which keeps fp32-level accuracy.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -31,40 +34,50 @@ namespace gdnq {
 
 constexpr int PC = 64;    // chunk = window
 constexpr int PD = 128;   // d_k = d_v
-constexpr int KP = 136;   // LDS pitch (bf16) of [token][dim] tiles (padding spreads banks)
-constexpr int KTP = 72;   // LDS pitch (bf16) of [dim][token]
-constexpr int AP = 65;    // LDS pitch (fp32) of A in the prep kernel
-constexpr int RWS = 32;   // state rows per workgroup
-constexpr int CP = 144;   // LDS pitch (bytes) of the int8 rows
-constexpr int UTP = 68;   // LDS pitch (fp32) of U^T
-constexpr int SP = 132;   // LDS pitch (fp32) of the new state rows
+constexpr int RWS = 32;   // state rows per state-pass workgroup
 
 __device__ __forceinline__ void tile_of(int tt, int& it, int& jt) {
-  it = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;  // lower tiles (it >= jt), row-major
+  it = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;  // lower 16x16 tiles (it >= jt), row-major
   jt = tt - it * (it + 1) / 2;
 }
+
+// exp for the output-only decay factors (arguments <= 0): one v_exp_f32,
+// relative error ~1e-6, far inside the output tolerance
+__device__ __forceinline__ float exp_out(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- prep
+constexpr int KP = 136;  // bf16 pitch of [token][dim] tiles
+constexpr int AP = 65;   // fp32 pitch of A
+constexpr int PREP_KT = PC * KP * 2 > (PC * PC + 3 * 256) * 4 ? PC * KP * 2 : (PC * PC + 3 * 256) * 4;
 
 struct PrepArgs {
   const uint16_t* k;
   const float* alpha;
   const float* beta;
-  float* T_ws;  // [B*NC*H][64][64]
+  __bf16* T_ws;  // [B*NC*H][3][64][64]: T as hi/mid/lo bf16 planes
   float* g_ws;  // [B*NC*H][64]
   int B, T, H;
 };
 
 __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 Kl[PC * KP];
+  // K is only needed for K K^T; T and the level products reuse its space
+  __shared__ __attribute__((aligned(16))) unsigned char kt_raw[PREP_KT];
   __shared__ float Al[PC * AP];
-  __shared__ __attribute__((aligned(16))) float Tl[PC * PC];
-  __shared__ float Pl[3 * 256];
   __shared__ float gl[PC], bl[PC];
+  __bf16* Kl = reinterpret_cast<__bf16*>(kt_raw);
+  float* Tl = reinterpret_cast<float*>(kt_raw);
+  float* Pl = Tl + PC * PC;
   const int NC = a.T / PC;
   const int idx = blockIdx.x;  // (b * NC + c) * H + h
   const int h = idx % a.H;
   const int c = (idx / a.H) % NC;
   const int b = idx / (a.H * NC);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
   const size_t tok0 = size_t(b) * a.T + size_t(c) * PC;
 
   {  // keys of the chunk: thread -> token tid / 4, dims [(tid % 4) * 32, +32)
@@ -89,26 +102,47 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
     gl[tid] = la;
     a.g_ws[size_t(idx) * PC + tid] = la;
   }
-  for (int e = tid; e < PC * PC; e += 256) Tl[e] = 0.f;
   __syncthreads();
 
-  // A from the lower 16x16 tiles of K K^T
-  for (int tt = wave; tt < 10; tt += 4) {
-    int it, jt;
-    tile_of(tt, it, jt);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // A from the lower 16x16 tiles of K K^T (kept in registers until K is dead)
+  float av[3][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kk = ks * 32 + 8 * (lane >> 4);
-      acc = mfma16(lds_bf16x8(Kl + (it * 16 + (lane & 15)) * KP + kk),
-                   lds_bf16x8(Kl + (jt * 16 + (lane & 15)) * KP + kk), acc);
-    }
-    const int j = jt * 16 + (lane & 15);
+  for (int n = 0; n < 3; ++n) {
+    const int tt = wave + 4 * n;
+    if (tt < 10) {
+      int it, jt;
+      tile_of(tt, it, jt);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = it * 16 + 4 * (lane >> 4) + q;
-      Al[i * AP + j] = (j < i) ? bl[i] * expf(gl[i] - gl[j]) * acc[q] : 0.f;
+      for (int ks = 0; ks < 4; ++ks) {
+        const int kk = ks * 32 + 8 * lq;
+        acc = mfma16(lds_bf16x8(Kl + (it * 16 + lr) * KP + kk), lds_bf16x8(Kl + (jt * 16 + lr) * KP + kk), acc);
+      }
+      const int j = jt * 16 + lr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = it * 16 + 4 * lq + q;
+        av[n][q] = (j < i) ? bl[i] * expf(gl[i] - gl[j]) * acc[q] : 0.f;
+      }
     }
+  }
+  __syncthreads();  // K dead from here; its space becomes T
+#pragma unroll
+  for (int n = 0; n < 3; ++n) {
+    const int tt = wave + 4 * n;
+    if (tt < 10) {
+      int it, jt;
+      tile_of(tt, it, jt);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Al[(it * 16 + 4 * lq + q) * AP + jt * 16 + lr] = av[n][q];
+    }
+  }
+  // strictly upper blocks of T are zero
+  for (int e = tid; e < 6 * 256; e += 256) {
+    const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+    const int bi = blk < 3 ? 0 : blk < 5 ? 1 : 2;
+    const int bj = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+    Tl[(bi * 16 + rr) * PC + bj * 16 + cc] = 0.f;
   }
   __syncthreads();
 
@@ -128,40 +162,71 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
   }
   __syncthreads();
 
-  // off-diagonal blocks, one block-diagonal at a time:
-  //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+  // off-diagonal blocks, one block-diagonal at a time (fp32 MFMA):
+  //   P = sum_{k=j}^{i-1} A_ik T_kj,   T_ij = -T_ii P
   for (int d = 1; d <= 3; ++d) {
     const int nb = 4 - d;
-    const int r = tid >> 4, cc = tid & 15;
-    for (int m = 0; m < nb; ++m) {
-      const int i = d + m, j = m;
-      float s = 0.f;
+    if (wave < nb) {
+      const int i = d + wave, j = wave;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int kb = j; kb < i; ++kb)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) s += Al[(i * 16 + r) * AP + kb * 16 + x] * Tl[(kb * 16 + x) * PC + j * 16 + cc];
-      Pl[m * 256 + r * 16 + cc] = s;
+        for (int kk = 0; kk < 4; ++kk)
+          acc = mfma4(Al[(i * 16 + lr) * AP + kb * 16 + 4 * kk + lq], Tl[(kb * 16 + 4 * kk + lq) * PC + j * 16 + lr], acc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Pl[wave * 256 + (4 * lq + q) * 16 + lr] = acc[q];
     }
     __syncthreads();
-    for (int m = 0; m < nb; ++m) {
-      const int i = d + m, j = m;
-      float s = 0.f;
+    if (wave < nb) {
+      const int i = d + wave, j = wave;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int x = 0; x < 16; ++x) s += Tl[(i * 16 + r) * PC + i * 16 + x] * Pl[m * 256 + x * 16 + cc];
-      Tl[(i * 16 + r) * PC + j * 16 + cc] = -s;
+      for (int kk = 0; kk < 4; ++kk)
+        acc = mfma4(Tl[(i * 16 + lr) * PC + i * 16 + 4 * kk + lq], Pl[wave * 256 + (4 * kk + lq) * 16 + lr], acc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Tl[(i * 16 + 4 * lq + q) * PC + j * 16 + lr] = -acc[q];
     }
     __syncthreads();
   }
 
-  float4* dst = reinterpret_cast<float4*>(a.T_ws + size_t(idx) * PC * PC);
-  for (int e = tid; e < PC * PC / 4; e += 256) dst[e] = reinterpret_cast<const float4*>(Tl)[e];
+  {  // T as three bf16 planes: thread -> row tid / 4, columns [(tid % 4) * 16, +16)
+    const int i = tid >> 2, c0 = (tid & 3) * 16;
+    float x[16];
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      const float4 t4 = *reinterpret_cast<const float4*>(Tl + i * PC + c0 + e);
+      x[e] = t4.x;
+      x[e + 1] = t4.y;
+      x[e + 2] = t4.z;
+      x[e + 3] = t4.w;
+    }
+    bf16x8 p[3][2];
+    {
+      float lo8[8], hi8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo8[e] = x[e];
+        hi8[e] = x[8 + e];
+      }
+      split3(lo8, p[0][0], p[1][0], p[2][0]);
+      split3(hi8, p[0][1], p[1][1], p[2][1]);
+    }
+    __bf16* dst = a.T_ws + size_t(idx) * 3 * PC * PC + i * PC + c0;
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) {
+      *reinterpret_cast<bf16x8*>(dst + pl * PC * PC) = p[pl][0];
+      *reinterpret_cast<bf16x8*>(dst + pl * PC * PC + 8) = p[pl][1];
+    }
+  }
 }
 
+// ---------------------------------------------------------------- state pass
 struct StateArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   const float* beta;
-  const float* T_ws;
+  const __bf16* T_ws;
   const float* g_ws;
   const int8_t* init_codes;
   const float* init_scales;
@@ -171,25 +236,56 @@ struct StateArgs {
   int B, T, H;
 };
 
+constexpr int TP = 72;    // bf16 pitch of [64][64] planes (T, M) and [32][64] planes (rhs^T, U^T)
+constexpr int SNP = 132;  // fp32 pitch of the new rows [32][128]
+constexpr int CBP = 136;  // bf16 pitch of the codes [32][128]
+
+// LDS carve (bytes)
+constexpr int OFF_K = 0;                           // K  [64][KP] bf16
+constexpr int OFF_Q = OFF_K + PC * KP * 2;         // Q  [64][KP] bf16
+constexpr int OFF_KT = OFF_Q + PC * KP * 2;        // K^T [128][64] bf16, 16-byte granules xor-swizzled
+constexpr int OFF_T = OFF_KT + PD * PC * 2;        // T   hi/mid/lo [3][64][TP] bf16
+constexpr int OFF_M = OFF_T + 3 * PC * TP * 2;     // M   hi/lo [2][64][TP] bf16
+constexpr int OFF_R = OFF_M + 2 * PC * TP * 2;     // rhs^T hi/mid/lo [3][32][TP] bf16 (plane 0 holds V^T until rhs)
+constexpr int OFF_UD = OFF_R + 3 * RWS * TP * 2;   // (U o d)^T hi/mid/lo [3][32][TP] bf16
+constexpr int OFF_U = OFF_UD + 3 * RWS * TP * 2;   // U^T hi/lo [2][32][TP] bf16
+constexpr int OFF_SN = OFF_U + 2 * RWS * TP * 2;   // new rows [32][SNP] fp32
+constexpr int OFF_CB = OFF_SN + RWS * SNP * 4;     // codes [32][CBP] bf16 (exact)
+constexpr int OFF_G = OFF_CB + RWS * CBP * 2;      // per chunk parity: g, exp(g), beta [2][3][64]
+constexpr int OFF_D = OFF_G + 2 * 3 * PC * 4;      // exp(g_C - g) [64], row scales [32]
+constexpr int STATE_LDS = OFF_D + (PC + RWS) * 4;
+static_assert(STATE_LDS <= 160 * 1024, "state-pass LDS");
+
+__device__ __forceinline__ int kt_index(int d, int j) {  // bf16 index of K^T[d][j]
+  return d * PC + ((((j >> 3) ^ (d >> 3)) & 7) << 3) + (j & 7);
+}
+
+__device__ __forceinline__ uint2 as_u2(const bf16x4& v) { return __builtin_bit_cast(uint2, v); }
+
+// Per chunk the state pass runs four phases between barriers:
+//   A  X = K S0^T, Q S0^T; rhs; output base             | d = exp(g_C - g)
+//   B  U = T rhs; U^T and (U o d)^T parts               | stage K, Q of the next chunk; load K, Q two ahead
+//   C  S_C^T = gamma_C S0^T + K^T (U o d); O = base + M U | stage T, V, g, beta of the next chunk; load two ahead
+//   D  requantize S_C                                    | next chunk's K^T and M = L o Q K^T
+// so memory traffic, LDS staging and VALU work sit beside the MFMA work of
+// each phase, and every prefetched register is consumed one chunk after it
+// is loaded.
 template <bool OUT_BF16>
-__global__ __launch_bounds__(512) void gdn_state_kernel(StateArgs a) {
+__global__ __launch_bounds__(512, 1) void gdn_state_kernel(StateArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  __bf16* Kl = reinterpret_cast<__bf16*>(lds);                       // [64][KP]
-  __bf16* KTl = Kl + PC * KP;                                         // [128][KTP]
-  __bf16* Ql = KTl + PD * KTP;                                        // [64][KP]
-  __bf16* Vl = Ql + PC * KP;                                          // [64][32]
-  float* Tl = reinterpret_cast<float*>(Vl + PC * RWS);                // [64][64]
-  float* Rl = Tl + PC * PC;                                           // [64][32] rhs
-  float* Ul = Rl + PC * RWS;                                          // [64][32]
-  float* UTl = Ul + PC * RWS;                                         // [32][UTP]
-  float* OSl = UTl + RWS * UTP;                                       // [64][32]
-  float* Ml = OSl + PC * RWS;                                         // [64][64], then new rows [32][SP]
-  float* gl = Ml + RWS * SP;                                          // [64] g
-  float* el = gl + PC;                                                // [64] exp(g)
-  float* dl = el + PC;                                                // [64] exp(g_C - g)
-  float* bl = dl + PC;                                                // [64] beta
-  float* sl = bl + PC;                                                // [32] row scales
-  int8_t* cl = reinterpret_cast<int8_t*>(sl + RWS);                   // [32][CP] int8 rows
+  __bf16* Kl = reinterpret_cast<__bf16*>(lds + OFF_K);
+  __bf16* Ql = reinterpret_cast<__bf16*>(lds + OFF_Q);
+  __bf16* KT = reinterpret_cast<__bf16*>(lds + OFF_KT);
+  __bf16* Tp = reinterpret_cast<__bf16*>(lds + OFF_T);
+  __bf16* Mp = reinterpret_cast<__bf16*>(lds + OFF_M);
+  __bf16* Rp = reinterpret_cast<__bf16*>(lds + OFF_R);
+  __bf16* Dp = reinterpret_cast<__bf16*>(lds + OFF_UD);
+  __bf16* Up = reinterpret_cast<__bf16*>(lds + OFF_U);
+  float* Sn = reinterpret_cast<float*>(lds + OFF_SN);
+  __bf16* Cb = reinterpret_cast<__bf16*>(lds + OFF_CB);
+  float* G = reinterpret_cast<float*>(lds + OFF_G);  // parity p: g at G + 192 p, exp(g) +64, beta +128
+  float* dl = reinterpret_cast<float*>(lds + OFF_D);
+  float* sl = dl + PC;
 
   const int nblk = a.B * a.H * (PD / RWS);
   const int logical = xcd_swizzle(blockIdx.x, nblk);  // the 4 row blocks of a head share an XCD
@@ -198,203 +294,330 @@ __global__ __launch_bounds__(512) void gdn_state_kernel(StateArgs a) {
   const int b = chain / a.H, h = chain % a.H;
   const int r0 = rb * RWS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
   const int NC = a.T / PC;
+  const size_t HD = size_t(a.H) * PD;
   const size_t state_row0 = (size_t(b) * a.H + h) * PD + r0;
+
+  const int it = wave >> 1, rt = wave & 1;  // this wave's (token tile, row tile) of X, U, O
+  const int nks = (it >> 1) + 1;            // 32-token steps reaching the diagonal of tile it
+  const int r = rt * 16 + lr;
+  const int i0 = it * 16 + 4 * lq;
+
+  // load mapping: K/Q token pair pm, dims [8 ps, +8); T row ti, columns
+  // [8 tc, +8) of each plane; V in this lane's MFMA output layout
+  const int pm = tid & 31, ps = tid >> 5;
+  const int ti = tid >> 3, tc = tid & 7;
+  const size_t tokb = size_t(b) * a.T;
+  const uint16_t* kb = a.k + (tokb + 2 * pm) * HD + size_t(h) * PD + 8 * ps;
+  const uint16_t* qb = a.q + (tokb + 2 * pm) * HD + size_t(h) * PD + 8 * ps;
+  const uint16_t* vb = a.v + (tokb + i0) * HD + size_t(h) * PD + r0 + r;
+  const __bf16* tb = a.T_ws + (size_t(b) * NC * a.H + h) * 3 * PC * PC + ti * PC + 8 * tc;
+  const float* gb = a.g_ws + (size_t(b) * NC * a.H + h) * PC + (tid & 63);
+  const float* bb = a.beta + (tokb + (tid & 63)) * a.H + h;
+  const size_t tok_step = PC * HD;                   // q/k/v elements per chunk
+  const size_t ch_step = size_t(a.H) * 3 * PC * PC;  // T elements per chunk (all heads)
+
+  uint4 k0, k1, q0, q1;  // K, Q of the next chunk (or the one after)
+  uint4 t0, t1, t2;      // T parts, V, g, beta likewise
+  uint32_t v4[4];
+  float gv = 0.f, bv = 0.f;
+  auto load_kq = [&](int c) {
+    const size_t o = size_t(c) * tok_step;
+    k0 = *reinterpret_cast<const uint4*>(kb + o);
+    k1 = *reinterpret_cast<const uint4*>(kb + o + HD);
+    q0 = *reinterpret_cast<const uint4*>(qb + o);
+    q1 = *reinterpret_cast<const uint4*>(qb + o + HD);
+  };
+  auto load_tv = [&](int c) {
+    const __bf16* tp = tb + size_t(c) * ch_step;
+    t0 = *reinterpret_cast<const uint4*>(tp);
+    t1 = *reinterpret_cast<const uint4*>(tp + PC * PC);
+    t2 = *reinterpret_cast<const uint4*>(tp + 2 * PC * PC);
+    const size_t o = size_t(c) * tok_step;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v4[q] = vb[o + q * HD];
+    if (tid < 64) {
+      gv = gb[size_t(c) * a.H * PC];
+      bv = bb[size_t(c) * PC * a.H];
+    }
+  };
+  auto stage_kq = [&]() {
+    *reinterpret_cast<uint4*>(Kl + (2 * pm) * KP + 8 * ps) = k0;
+    *reinterpret_cast<uint4*>(Kl + (2 * pm + 1) * KP + 8 * ps) = k1;
+    *reinterpret_cast<uint4*>(Ql + (2 * pm) * KP + 8 * ps) = q0;
+    *reinterpret_cast<uint4*>(Ql + (2 * pm + 1) * KP + 8 * ps) = q1;
+  };
+  auto stage_tv = [&](int par) {
+    *reinterpret_cast<uint4*>(Tp + ti * TP + 8 * tc) = t0;
+    *reinterpret_cast<uint4*>(Tp + PC * TP + ti * TP + 8 * tc) = t1;
+    *reinterpret_cast<uint4*>(Tp + 2 * PC * TP + ti * TP + 8 * tc) = t2;
+    // V^T of this lane's (row, 4 tokens) into the slots of the first rhs^T
+    // plane: the same lane reads them back and overwrites them with rhs
+    *reinterpret_cast<uint2*>(Rp + r * TP + i0) = make_uint2(v4[0] | (v4[1] << 16), v4[2] | (v4[3] << 16));
+    if (tid < 64) {
+      float* gp = G + 192 * par;
+      gp[tid] = gv;
+      gp[64 + tid] = expf(gv);
+      gp[128 + tid] = bv;
+    }
+  };
+  // K^T of the staged K (tokens 2 pm, 2 pm + 1 of dims [8 ps, +8) per thread)
+  auto stage_kt = [&]() {
+    const uint4 w0 = *reinterpret_cast<const uint4*>(Kl + (2 * pm) * KP + 8 * ps);
+    const uint4 w1 = *reinterpret_cast<const uint4*>(Kl + (2 * pm + 1) * KP + 8 * ps);
+    const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w};
+    const uint32_t a1[4] = {w1.x, w1.y, w1.z, w1.w};
+    uint32_t* kt = reinterpret_cast<uint32_t*>(KT);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of both words
+      kt[kt_index(8 * ps + e, 2 * pm) >> 1] = __builtin_amdgcn_perm(a1[e >> 1], a0[e >> 1], sel);
+    }
+  };
+  // M = L o Q K^T of the staged chunk: lower 16x16 tiles as M^T tiles
+  // D[j][i] = k_j . q_i, stored as M[i][j] (hi and lo parts), plus the two
+  // zero tiles above the diagonal that the 32-token steps of M U reach
+  auto build_m = [&](const float* gc) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int tt = wave + 8 * n;
+      if (tt < 12) {
+        int mi, mj;
+        float m4[4] = {0.f, 0.f, 0.f, 0.f};
+        if (tt < 10) {
+          tile_of(tt, mi, mj);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int kk = ks * 32 + 8 * lq;
+            acc = mfma16(lds_bf16x8(Kl + (mj * 16 + lr) * KP + kk), lds_bf16x8(Ql + (mi * 16 + lr) * KP + kk), acc);
+          }
+          const int i = mi * 16 + lr;
+          const float gi = gc[i];
+          const float4 g4 = *reinterpret_cast<const float4*>(gc + mj * 16 + 4 * lq);
+          const float gj[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int j = mj * 16 + 4 * lq + q;
+            m4[q] = (j <= i) ? exp_out(gi - gj[q]) * acc[q] : 0.f;
+          }
+        } else {
+          mi = tt == 10 ? 0 : 2;
+          mj = mi + 1;
+        }
+        bf16x4 h1, h2;
+        split2(m4, h1, h2);
+        const int i = mi * 16 + lr, j0 = mj * 16 + 4 * lq;
+        *reinterpret_cast<uint2*>(Mp + i * TP + j0) = as_u2(h1);
+        *reinterpret_cast<uint2*>(Mp + PC * TP + i * TP + j0) = as_u2(h2);
+      }
+    }
+  };
 
   // stored rows at the start (zero state without init)
   {
-    const int r = tid >> 4, seg = tid & 15;  // 32 rows x 16 segments of 8 codes
+    const int rq = tid >> 4, seg = tid & 15;  // 32 rows x 16 segments of 8 codes
     uint2 w = make_uint2(0u, 0u);
-    if (a.init_codes) w = *reinterpret_cast<const uint2*>(a.init_codes + (state_row0 + r) * PD + seg * 8);
-    *reinterpret_cast<uint2*>(cl + r * CP + seg * 8) = w;
-    if (seg == 0) sl[r] = a.init_scales ? a.init_scales[state_row0 + r] : 0.f;
+    if (a.init_codes) w = *reinterpret_cast<const uint2*>(a.init_codes + (state_row0 + rq) * PD + seg * 8);
+    *reinterpret_cast<bf16x8*>(Cb + rq * CBP + seg * 8) = i8x8_to_bf16(w);
+    if (seg == 0) sl[rq] = a.init_scales ? a.init_scales[state_row0 + rq] : 0.f;
   }
-
-  for (int c = 0; c < NC; ++c) {
-    const size_t tok0 = size_t(b) * a.T + size_t(c) * PC;
-    const size_t ch = (size_t(b) * NC + c) * a.H + h;
-    __syncthreads();  // previous chunk done with every buffer
-    {  // K (row-major and transposed) and Q: thread -> token tid / 8, dims [(tid % 8) * 16, +16)
-      const int i = tid >> 3, s8 = tid & 7;
-      const uint4* ks = reinterpret_cast<const uint4*>(a.k + ((tok0 + i) * a.H + h) * PD + s8 * 16);
-      const uint4* qs = reinterpret_cast<const uint4*>(a.q + ((tok0 + i) * a.H + h) * PD + s8 * 16);
-      const uint4 k0 = ks[0], k1 = ks[1], q0 = qs[0], q1 = qs[1];
-      uint4* kd = reinterpret_cast<uint4*>(Kl + i * KP + s8 * 16);
-      kd[0] = k0;
-      kd[1] = k1;
-      uint4* qd = reinterpret_cast<uint4*>(Ql + i * KP + s8 * 16);
-      qd[0] = q0;
-      qd[1] = q1;
-      const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-      uint16_t* kt = reinterpret_cast<uint16_t*>(KTl);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kt[(s8 * 16 + 2 * e) * KTP + i] = uint16_t(kw[e] & 0xffffu);
-        kt[(s8 * 16 + 2 * e + 1) * KTP + i] = uint16_t(kw[e] >> 16);
-      }
-    }
-    if (tid < 256) {  // this workgroup's rows of V: token tid / 4, rows [(tid % 4) * 8, +8)
-      const int i = tid >> 2, q4 = tid & 3;
-      *reinterpret_cast<uint4*>(Vl + i * RWS + q4 * 8) =
-          *reinterpret_cast<const uint4*>(a.v + ((tok0 + i) * a.H + h) * PD + r0 + q4 * 8);
-    }
-    {  // T of the chunk
-      const float4* ts = reinterpret_cast<const float4*>(a.T_ws + ch * PC * PC);
-      float4* td = reinterpret_cast<float4*>(Tl);
-      td[tid] = ts[tid];
-      td[tid + 512] = ts[tid + 512];
-    }
-    if (tid < 64) {
-      const float g = a.g_ws[ch * PC + tid];
-      gl[tid] = g;
-      el[tid] = expf(g);
-      bl[tid] = a.beta[(tok0 + tid) * a.H + h];
+  if (NC > 0) {
+    load_kq(0);
+    load_tv(0);
+    stage_kq();
+    stage_tv(0);
+    if (NC > 1) {
+      load_kq(1);
+      load_tv(1);
     }
     __syncthreads();
-    if (tid < 64) dl[tid] = expf(gl[PC - 1] - gl[tid]);
+    stage_kt();
+    build_m(G);
+  }
+  __syncthreads();
 
-    {  // X = K S0^T and Q S0^T for token tile it, row tile rt; then rhs and the output base
-      const int it = wave >> 1, rt = wave & 1;
+  for (int c = 0; c < NC; ++c) {
+    const size_t tok0 = tokb + size_t(c) * PC;
+    const float* gc = G + 192 * (c & 1);
+    // ---- A: K S0^T and Q S0^T (codes exact), rhs, output base
+    float os[4];
+    {
       f32x4 xacc = {0.f, 0.f, 0.f, 0.f}, qacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int kk = ks * 32 + 8 * (lane >> 4);
-        const bf16x8 bc = i8x8_to_bf16(*reinterpret_cast<const uint2*>(cl + (rt * 16 + (lane & 15)) * CP + kk));
-        xacc = mfma16(lds_bf16x8(Kl + (it * 16 + (lane & 15)) * KP + kk), bc, xacc);
-        qacc = mfma16(lds_bf16x8(Ql + (it * 16 + (lane & 15)) * KP + kk), bc, qacc);
+        const int kk = ks * 32 + 8 * lq;
+        const bf16x8 bc = lds_bf16x8(Cb + r * CBP + kk);
+        xacc = mfma16(lds_bf16x8(Kl + (it * 16 + lr) * KP + kk), bc, xacc);
+        qacc = mfma16(lds_bf16x8(Ql + (it * 16 + lr) * KP + kk), bc, qacc);
       }
-      const int r = rt * 16 + (lane & 15);
       const float sr = sl[r];
+      const float4 e4 = *reinterpret_cast<const float4*>(gc + 64 + i0);
+      const float4 b4 = *reinterpret_cast<const float4*>(gc + 128 + i0);
+      const float ge[4] = {e4.x, e4.y, e4.z, e4.w}, be[4] = {b4.x, b4.y, b4.z, b4.w};
+      const uint2 vw = *reinterpret_cast<const uint2*>(Rp + r * TP + i0);
+      const float vv[4] = {__uint_as_float(vw.x << 16), __uint_as_float(vw.x & 0xffff0000u),
+                           __uint_as_float(vw.y << 16), __uint_as_float(vw.y & 0xffff0000u)};
+      float rh[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int i = it * 16 + 4 * (lane >> 4) + q;
-        const float gi = el[i];
-        Rl[i * RWS + r] = bl[i] * (float(Vl[i * RWS + r]) - gi * (sr * xacc[q]));
-        OSl[i * RWS + r] = gi * (sr * qacc[q]);
+        rh[q] = be[q] * (vv[q] - ge[q] * (sr * xacc[q]));
+        os[q] = ge[q] * (sr * qacc[q]);
       }
+      bf16x4 h1, h2, h3;
+      split3(rh, h1, h2, h3);
+      *reinterpret_cast<uint2*>(Rp + r * TP + i0) = as_u2(h1);
+      *reinterpret_cast<uint2*>(Rp + RWS * TP + r * TP + i0) = as_u2(h2);
+      *reinterpret_cast<uint2*>(Rp + 2 * RWS * TP + r * TP + i0) = as_u2(h3);
+    }
+    if (tid < 64) dl[tid] = expf(gc[PC - 1] - gc[tid]);
+    __syncthreads();
+
+    // ---- B: U = T rhs (T unit lower triangular; six split products), then
+    //      U^T (two parts) and (U o d)^T (three parts)
+    {
+      f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = {0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < nks; ++ks) {
+        const int kk = ks * 32 + 8 * lq;
+        const __bf16* tr = Tp + (it * 16 + lr) * TP + kk;
+        const __bf16* rr = Rp + r * TP + kk;
+        const bf16x8 t1 = lds_bf16x8(tr), t2 = lds_bf16x8(tr + PC * TP), t3 = lds_bf16x8(tr + 2 * PC * TP);
+        const bf16x8 b1 = lds_bf16x8(rr), b2 = lds_bf16x8(rr + RWS * TP), b3 = lds_bf16x8(rr + 2 * RWS * TP);
+        ua = mfma16(t2, b2, ua);
+        ub = mfma16(t3, b1, ub);
+        ua = mfma16(t1, b3, ua);
+        ub = mfma16(t2, b1, ub);
+        ua = mfma16(t1, b2, ua);
+        ub = mfma16(t1, b1, ub);
+      }
+      const float4 d4 = *reinterpret_cast<const float4*>(dl + i0);
+      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+      float u[4], ud[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u[q] = ua[q] + ub[q];
+        ud[q] = u[q] * dd[q];
+      }
+      bf16x4 h1, h2, h3;
+      split2(u, h1, h2);
+      *reinterpret_cast<uint2*>(Up + r * TP + i0) = as_u2(h1);
+      *reinterpret_cast<uint2*>(Up + RWS * TP + r * TP + i0) = as_u2(h2);
+      split3(ud, h1, h2, h3);
+      *reinterpret_cast<uint2*>(Dp + r * TP + i0) = as_u2(h1);
+      *reinterpret_cast<uint2*>(Dp + RWS * TP + r * TP + i0) = as_u2(h2);
+      *reinterpret_cast<uint2*>(Dp + 2 * RWS * TP + r * TP + i0) = as_u2(h3);
+    }
+    if (c + 1 < NC) {  // K and Q of this chunk are no longer read
+      stage_kq();
+      if (c + 2 < NC) load_kq(c + 2);
     }
     __syncthreads();
 
-    {  // U = T rhs (T unit lower triangular)
-      const int r = tid & 31, ib = tid >> 5;
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int i = ib + 16 * qq;
-        float s = 0.f;
-        for (int j = 0; j <= i; ++j) s += Tl[i * PC + j] * Rl[j * RWS + r];
-        Ul[i * RWS + r] = s;
-        UTl[r * UTP + i] = s;
-      }
-    }
-    // M = L o Q K^T on the lower tiles (upper tiles are never read)
-    for (int tt = wave; tt < 10; tt += 8) {
-      int it, jt;
-      tile_of(tt, it, jt);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kk = ks * 32 + 8 * (lane >> 4);
-        acc = mfma16(lds_bf16x8(Ql + (it * 16 + (lane & 15)) * KP + kk),
-                     lds_bf16x8(Kl + (jt * 16 + (lane & 15)) * KP + kk), acc);
-      }
-      const int j = jt * 16 + (lane & 15);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = it * 16 + 4 * (lane >> 4) + q;
-        Ml[i * PC + j] = (j <= i) ? expf(gl[i] - gl[j]) * acc[q] : 0.f;
-      }
-    }
-    __syncthreads();
-
-    {  // O = O_base + M U
-      const int r = tid & 31, ib = tid >> 5;
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int i = ib + 16 * qq;
-        float s = OSl[i * RWS + r];
-        for (int j = 0; j <= i; ++j) s += Ml[i * PC + j] * Ul[j * RWS + r];
-        const size_t oi = ((tok0 + i) * a.H + h) * PD + r0 + r;
-        if constexpr (OUT_BF16) static_cast<uint16_t*>(a.o)[oi] = uint16_t(f32_to_bf16_bits(s));
-        else static_cast<float*>(a.o)[oi] = s;
-      }
-    }
-    __syncthreads();  // M is overwritten by the new rows below
-
-    {  // S_C = gamma_C S0 + (U o d)^T K: row tile rt, column tiles ct0, ct0 + 1
-      const int rt = wave >> 2, ct0 = (wave & 3) * 2;
-      const int r = rt * 16 + (lane & 15);
-      bf16x8 a1[2], a2[2], a3[2];
+    // ---- C: new rows S_C^T = gamma_C S0^T + K^T (U o d), and O = base + M U
+    {
+      const int rt2 = wave & 1, dt0 = (wave >> 1) * 2;
+      const int r2 = rt2 * 16 + lr;
+      bf16x8 u1[2], u2[2], u3[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int kk = ks * 32 + 8 * (lane >> 4);
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = UTl[r * UTP + kk + e] * dl[kk + e];
-        split3(x, a1[ks], a2[ks], a3[ks]);
+        const __bf16* dp = Dp + r2 * TP + ks * 32 + 8 * lq;
+        u1[ks] = lds_bf16x8(dp);
+        u2[ks] = lds_bf16x8(dp + RWS * TP);
+        u3[ks] = lds_bf16x8(dp + 2 * RWS * TP);
       }
-      const float gC = el[PC - 1];
+      const float gs = gc[64 + PC - 1] * sl[r2];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        const int ct = ct0 + cc;
+        const int dt = dt0 + cc;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 bk = lds_bf16x8(KTl + (ct * 16 + (lane & 15)) * KTP + ks * 32 + 8 * (lane >> 4));
-          acc = mfma16(a1[ks], bk, acc);
-          acc = mfma16(a2[ks], bk, acc);
-          acc = mfma16(a3[ks], bk, acc);
+          const bf16x8 ak = lds_bf16x8(KT + kt_index(dt * 16 + lr, ks * 32 + 8 * lq));
+          acc = mfma16(ak, u3[ks], acc);
+          acc = mfma16(ak, u2[ks], acc);
+          acc = mfma16(ak, u1[ks], acc);
         }
-        const int col = ct * 16 + (lane & 15);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int rr = rt * 16 + 4 * (lane >> 4) + q;
-          const float s0 = float(cl[rr * CP + col]) * sl[rr];
-          Ml[rr * SP + col] = gC * s0 + acc[q];
-        }
+        const int d0 = dt * 16 + 4 * lq;
+        const bf16x4 c4 = *reinterpret_cast<const bf16x4*>(Cb + r2 * CBP + d0);
+        float4 sn;
+        sn.x = gs * float(c4[0]) + acc[0];
+        sn.y = gs * float(c4[1]) + acc[1];
+        sn.z = gs * float(c4[2]) + acc[2];
+        sn.w = gs * float(c4[3]) + acc[3];
+        *reinterpret_cast<float4*>(Sn + r2 * SNP + d0) = sn;
       }
+    }
+    {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < nks; ++ks) {
+        const int kk = ks * 32 + 8 * lq;
+        const bf16x8 m1 = lds_bf16x8(Mp + (it * 16 + lr) * TP + kk);
+        const bf16x8 m2 = lds_bf16x8(Mp + PC * TP + (it * 16 + lr) * TP + kk);
+        const bf16x8 v1 = lds_bf16x8(Up + r * TP + kk);
+        const bf16x8 v2 = lds_bf16x8(Up + RWS * TP + r * TP + kk);
+        acc = mfma16(m2, v1, acc);
+        acc = mfma16(m1, v2, acc);
+        acc = mfma16(m1, v1, acc);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const size_t oi = (tok0 + i0 + q) * HD + size_t(h) * PD + r0 + r;
+        const float ov = os[q] + acc[q];
+        if constexpr (OUT_BF16) static_cast<uint16_t*>(a.o)[oi] = uint16_t(f32_to_bf16_bits(ov));
+        else static_cast<float*>(a.o)[oi] = ov;
+      }
+    }
+    if (c + 1 < NC) {  // T and the rhs planes were last read in B; the other g parity is free
+      stage_tv((c + 1) & 1);
+      if (c + 2 < NC) load_tv(c + 2);
     }
     __syncthreads();
 
-    {  // requantize the new rows: row tid / 16, columns [(tid % 16) * 8, +8)
-      const int r = tid >> 4, seg = tid & 15;
-      float x[8];
+    // ---- D: requantize the new rows; K^T and M of the next chunk
+    {
+      const int rq = tid >> 4, seg = tid & 15;
+      const float4 s0 = *reinterpret_cast<const float4*>(Sn + rq * SNP + seg * 8);
+      const float4 s1 = *reinterpret_cast<const float4*>(Sn + rq * SNP + seg * 8 + 4);
+      const float x[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
       float amax = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = Ml[r * SP + seg * 8 + e];
-        amax = fmaxf(amax, fabsf(x[e]));
-      }
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
       amax = group_max<16>(amax);
       const float scale = codec_scale(amax);
-      uint2 w;
-      w.x = pack4_i8(codec_code(x[0], scale), codec_code(x[1], scale), codec_code(x[2], scale), codec_code(x[3], scale));
-      w.y = pack4_i8(codec_code(x[4], scale), codec_code(x[5], scale), codec_code(x[6], scale), codec_code(x[7], scale));
-      *reinterpret_cast<uint2*>(cl + r * CP + seg * 8) = w;
-      if (seg == 0) sl[r] = scale;
+      float cf[8];
+      codec_codes(x, scale, cf);
+      bf16x8 cv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cv[e] = (__bf16)cf[e];
+      *reinterpret_cast<bf16x8*>(Cb + rq * CBP + seg * 8) = cv;
+      if (seg == 0) sl[rq] = scale;
     }
+    if (c + 1 < NC) {
+      stage_kt();
+      build_m(G + 192 * ((c + 1) & 1));
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  {  // final rows
-    const int r = tid >> 4, seg = tid & 15;
-    *reinterpret_cast<uint2*>(a.codes + (state_row0 + r) * PD + seg * 8) =
-        *reinterpret_cast<const uint2*>(cl + r * CP + seg * 8);
-    if (seg == 0) a.scales[state_row0 + r] = sl[r];
+
+  {  // final rows (codes back to int8)
+    const int rq = tid >> 4, seg = tid & 15;
+    const bf16x8 cv = lds_bf16x8(Cb + rq * CBP + seg * 8);
+    uint2 w;
+    w.x = pack4_i8(int(float(cv[0])), int(float(cv[1])), int(float(cv[2])), int(float(cv[3])));
+    w.y = pack4_i8(int(float(cv[4])), int(float(cv[5])), int(float(cv[6])), int(float(cv[7])));
+    *reinterpret_cast<uint2*>(a.codes + (state_row0 + rq) * PD + seg * 8) = w;
+    if (seg == 0) a.scales[state_row0 + rq] = sl[rq];
   }
 }
 
-static size_t state_lds_bytes() {
-  return size_t(PC * KP + PD * KTP + PC * KP + PC * RWS) * 2 +
-         size_t(PC * PC + 3 * PC * RWS + RWS * UTP + PC * RWS + RWS * SP + 4 * PC + RWS) * 4 +
-         size_t(RWS * CP);
-}
-
-static size_t gdn_ws_T(const PrefillLaunch& L) { return size_t(L.B) * (L.T / PC) * L.H * PC * PC * 4; }
+static size_t gdn_ws_T(const PrefillLaunch& L) { return size_t(L.B) * (L.T / PC) * L.H * 3 * PC * PC * 2; }
 static size_t gdn_ws_g(const PrefillLaunch& L) { return size_t(L.B) * (L.T / PC) * L.H * PC * 4; }
 
 size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L) { return gdn_ws_T(L) + gdn_ws_g(L); }
 
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
-  float* T_ws = static_cast<float*>(L.workspace);
+  __bf16* T_ws = static_cast<__bf16*>(L.workspace);
   float* g_ws = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + gdn_ws_T(L));
   const int NC = L.T / PC;
   if (NC > 0) {
@@ -405,17 +628,12 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
   StateArgs s{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k),
               static_cast<const uint16_t*>(L.v), L.beta, T_ws, g_ws, L.init_codes, L.init_scales,
               L.o, L.codes, L.scales, L.B, L.T, L.H};
-  const size_t lds = state_lds_bytes();
   const unsigned grid = unsigned(L.B) * L.H * (PD / RWS);
-  if (L.out_bf16) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_state_kernel<true>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    hipLaunchKernelGGL(gdn_state_kernel<true>, dim3(grid), dim3(512), lds, stream, s);
-  } else {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_state_kernel<false>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    hipLaunchKernelGGL(gdn_state_kernel<false>, dim3(grid), dim3(512), lds, stream, s);
-  }
+  auto kern = L.out_bf16 ? &gdn_state_kernel<true> : &gdn_state_kernel<false>;
+  if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, STATE_LDS))
+    return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(512), STATE_LDS, stream, s);
   return hipGetLastError();
 }
 
