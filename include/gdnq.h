@@ -162,7 +162,9 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
  *   requantization (window ignored); beta, init_codes, init_scales, codes and
  *   scales must be NULL; writes o and the final fp32 state (in the rotated
  *   basis under GDNQ_FLAG_WHT).  Supported: d_k = 128, d_v in {64, 128},
- *   chunk = 64, T a multiple of 64.  Flags: GDNQ_FLAG_WHT, GDNQ_FLAG_INT8_QK.
+ *   chunk = 64, T a multiple of 64.  Flags: GDNQ_FLAG_INT8_QK, optionally
+ *   with GDNQ_FLAG_WHT (the rotation is applied only on the way to the int8
+ *   operands; GDNQ_FLAG_WHT alone is GDNQ_ERR_FLAGS).
  *
  *   p->in_dtype must be GDNQ_BF16, p->out_dtype GDNQ_BF16 or GDNQ_F32.
  *     q, k   [B,T,H,d_k] in_dtype     v [B,T,H,d_v] in_dtype

@@ -168,6 +168,8 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   if (ssd) {
     if (p->flags & ~uint32_t(GDNQ_FLAG_SSD | GDNQ_FLAG_WHT | GDNQ_FLAG_INT8_QK))
       return fail(GDNQ_ERR_FLAGS, "flags 0x%x", p->flags);
+    if ((p->flags & GDNQ_FLAG_WHT) && !(p->flags & GDNQ_FLAG_INT8_QK))
+      return fail(GDNQ_ERR_FLAGS, "SSD: GDNQ_FLAG_WHT requires GDNQ_FLAG_INT8_QK");
     if (dk != 128 || (dv != 64 && dv != 128)) return fail(GDNQ_ERR_SHAPE, "SSD: d_k = %d (128), d_v = %d (64 or 128)", dk, dv);
   } else {
     if (p->flags) return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill takes no flags", p->flags);

@@ -123,6 +123,8 @@ def _prefill(params, fake, **over):
 @pytest.mark.parametrize("params,status", [
     (_pp(C=32, W=32), 2), (_pp(T=100), 2), (_pp(dk=64, dv=64), 2), (_pp(W=128), 2),
     (_pp(ind=0), 3), (_pp(outd=3), 3), (_pp(flags=4), 8), (_pp(flags=8), 8),
+    (_pp(flags=1), 8),                   # GDN prefill takes no rotation flag
+    (_pp(dv=64, flags=2 | 1), 8),        # SSD rotation only on the way to int8 operands
 ])
 def test_prefill_rejects_bad_params(params, status):
     assert _prefill(params, Fake()) == status
@@ -152,6 +154,17 @@ def test_workspace_size_is_queryable():
     assert L.gdnq_prefill_workspace_size(None) == 0
     p = _pp()
     assert _lib.prefill_workspace_size(p) >= 0
+
+
+def test_workspace_sizes():
+    """GDN: per chunk-head, T as three bf16 planes (24 KiB) and g (256 B);
+    SSD int8: codes and scales of q and k per token row; plain SSD: none."""
+    B, T, H = 2, 256, 3
+    nch = B * (T // 64) * H
+    assert _lib.prefill_workspace_size(_pp(B=B, T=T, H=H)) == nch * (3 * 64 * 64 * 2 + 64 * 4)
+    rows = B * T * H
+    assert _lib.prefill_workspace_size(_pp(B=B, T=T, H=H, dv=64, flags=2 | 4 | 1)) == rows * (2 * 128 + 8)
+    assert _lib.prefill_workspace_size(_pp(B=B, T=T, H=H, dv=64, flags=2)) == 0
 
 
 def test_quantize_validation():
