@@ -14,8 +14,9 @@ per replica (f -> f+1, or 0 after a window close), as in a real decode loop.
 Prints ONE JSON line.  `value` = tokens/s (B tokens per step); the roofline
 object uses the algorithmic bytes of each launch (computed from the realized
 fills) divided by the measured launch time; `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.  `--prefill` adds the GDN
-and SSD chunked-prefill measurements as secondary objects.
+oracle on a bounded sample of the same workload.  The GDN and SSD
+chunked-prefill measurements follow as secondary objects (`--no-prefill`
+skips them).
 """
 
 from __future__ import annotations
@@ -163,9 +164,40 @@ def bench_decode(args, torch, ops, wl, rep_count):
             "gbps": gbps}
 
 
+def gdn_prefill_flops(B, T, H, dk=DK, dv=DV, C=64):
+    """Useful FLOPs of the chunked GDN prefill (2 per multiply-add): per
+    chunk-head K K^T (strictly lower), T = (I + A)^-1 (C^3/6), K S0^T, Q S0^T,
+    T rhs (lower), Q K^T (lower with diagonal), M U (lower), state update."""
+    tri, tri0 = C * (C + 1) // 2, C * (C - 1) // 2
+    macs = dk * tri0 + C ** 3 / 6 + 3 * C * dk * dv + dv * tri + dk * tri + dv * tri
+    return 2.0 * macs * B * (T // C) * H
+
+
+def ssd_prefill_flops(B, T, H, dk=128, dv=64, C=64):
+    """Useful FLOPs of the chunked SSD prefill: Q K^T (lower with diagonal),
+    Q S0^T, M V (lower), state update (the rotation and operand quantization
+    are O(d log d) per row and not counted)."""
+    tri = C * (C + 1) // 2
+    macs = dk * tri + 2 * C * dk * dv + dv * tri
+    return 2.0 * macs * B * (T // C) * H
+
+
+def gdn_prefill_bytes(B, T, H, dk=DK, dv=DV):
+    """Algorithmic HBM bytes: bf16 q, k, v and fp32 alpha, beta read, bf16 o
+    written, the final int8 rows + scales written (zero initial state)."""
+    return B * T * H * (2 * (2 * dk + dv) + 8 + 2 * dv) + B * H * dv * (dk + 4)
+
+
+def ssd_prefill_bytes(B, T, H, dk=128, dv=64):
+    """bf16 q, k, v and fp32 a read, bf16 o written, the final fp32 state written."""
+    return B * T * H * (2 * (2 * dk + dv) + 4 + 2 * dv) + B * H * dv * dk * 4
+
+
 def bench_prefill(torch, ops, wl, steps=5, warmup=2):
-    """Secondary: GDN chunked prefill B=4, T=8192, H=16, d=128, C=W=64 and
-    SSD prefill B=2, T=4096, H=80, d_k=128, d_v=64 with WHT + int8 q/k."""
+    """Secondary: GDN chunked prefill B=4, T=8192, H=16, d=128, C=W=64 (bf16
+    output, zero initial state) and SSD prefill B=2, T=4096, H=80, d_k=128,
+    d_v=64 with WHT-rotated int8 q/k (bf16 output).  Inputs and workspace
+    are resident before timing; each call is timed whole (all its kernels)."""
     dev = torch.device("cuda:0")
     res = {}
     cases = [
@@ -179,40 +211,58 @@ def bench_prefill(torch, ops, wl, steps=5, warmup=2):
         v = torch.from_numpy(x["v"]).to(dev).bfloat16()
         a = torch.from_numpy(x["alpha"]).to(dev)
         bt = None if ssd else torch.from_numpy(x["beta"]).to(dev)
+        del x
         kw = dict(ssd=True, wht=True, int8_qk=True) if ssd else dict(window=64)
-        try:
-            for _ in range(warmup):
-                ops.prefill_chunked(q, k, v, a, bt, **kw)
-        except Exception as e:  # prefill kernels may be unavailable in a partial build
-            res[name] = {"error": str(e)}
-            continue
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            ops.prefill_chunked(q, k, v, a, bt, **kw)
-        e1.record()
-        e1.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        kw["workspace"] = torch.empty(ops.prefill_workspace_size(q, v, **kw), dtype=torch.uint8, device=dev)
         Bq, T, Hh, dk = q.shape
         dv = v.shape[-1]
-        toks = Bq * T
-        th = Bq * T * Hh
+        kw["o"] = torch.empty((Bq, T, Hh, dv), dtype=torch.bfloat16, device=dev)
         if ssd:
-            flops = th * (4 * dk * dv + 64 * (2 * dk + 2 * dv))
-            nbytes = th * (2 * (2 * dk + dv) + 4 + 2 * dv) + Bq * Hh * dv * dk * 4
+            kw["state_f32"] = torch.empty((Bq, Hh, dv, dk), dtype=torch.float32, device=dev)
         else:
-            flops = th * (6 * dk * dv + 64 * (6 * dk + 4 * dv))
-            nbytes = th * (2 * (2 * dk + dv) + 8 + 2 * dv) + Bq * Hh * (dv * dk + 4 * dv)
-        res[name] = {"workload": f"B={Bq} T={T} H={Hh} d_k={dk} d_v={dv} C=64",
-                     "ms": ms, "tokens_s": toks / (ms * 1e-3),
-                     "tflops": flops / (ms * 1e-3) / 1e12,
-                     "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                     "gbps": nbytes / (ms * 1e-3) / 1e9,
-                     "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-        del q, k, v, a, bt
+            kw["codes"] = torch.empty((Bq, Hh, dv, dk), dtype=torch.int8, device=dev)
+            kw["scales"] = torch.empty((Bq, Hh, dv), dtype=torch.float32, device=dev)
+        for _ in range(warmup):
+            ops.prefill_chunked(q, k, v, a, bt, **kw)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(dev)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            ops.prefill_chunked(q, k, v, a, bt, **kw)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        flops = (ssd_prefill_flops if ssd else gdn_prefill_flops)(Bq, T, Hh, dk, dv)
+        nbytes = (ssd_prefill_bytes if ssd else gdn_prefill_bytes)(Bq, T, Hh, dk, dv)
+        tflops = flops / (ms * 1e-3) / 1e12
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {
+            "workload": (f"B={Bq} T={T} H={Hh} d_k={dk} d_v={dv} chunk=64"
+                         + (" WHT+int8 q/k, fp32 state" if ssd else " window=64, int8 state")),
+            "ms": round(ms, 4), "tokens_s": round(Bq * T / (ms * 1e-3), 1),
+            "tflops": round(tflops, 2), "gbps": round(gbps, 1),
+            "flops_per_call": flops, "bytes_per_call": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)},
+            "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        }
+        del q, k, v, a, bt, kw
+        torch.cuda.empty_cache()
     return res
+
+
+def copy_probe(torch, mib):
+    """One plain device copy of `mib` MiB (read + write), the reference the
+    HBM byte counters are scaled by."""
+    dev = torch.device("cuda:0")
+    src = torch.empty(mib * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def main():
@@ -223,7 +273,11 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--prefill", action="store_true", help="also time the chunked prefills")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurements")
+    ap.add_argument("--skip-decode", action="store_true",
+                    help="profiling aid: time only the prefills (the printed line then has no decode value)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="profiling aid: run one plain copy of MIB MiB first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on "
@@ -234,6 +288,12 @@ def main():
 
     import workloads as wl
     from quantized_recurrent_state_gdnq_amd import ops
+
+    if args.copy_probe:
+        copy_probe(torch, args.copy_probe)
+    if args.skip_decode:
+        print(json.dumps({"prefill": bench_prefill(torch, ops, wl)}), flush=True)
+        return
 
     r = bench_decode(args, torch, ops, wl, max(1, args.replicas))
     traffic = load_traffic("decode_b64_h32_traffic.json", ["decode.hip", "device_common.h"], 1)
@@ -260,7 +320,7 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(r["bytes_per_launch"])},
     }
-    if args.prefill:
+    if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, ops, wl)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(args.cpu_seconds)

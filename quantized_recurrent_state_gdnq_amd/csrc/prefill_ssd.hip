@@ -13,9 +13,9 @@
 // In plain bf16 mode cq, ck are q, k themselves and sq = sk = 1.
 //
 // Kernels:
-//   operand -- (int8 mode) one 16-lane group per token row of q or k: FWHT
-//              in registers, row absmax, codec; codes and scales to the
-//              workspace.
+//   operand -- (int8 mode) four lanes per token row of q or k: FWHT in
+//              registers, row absmax, codec; codes and scales to the
+//              workspace (one launch for both operands).
 //   state   -- one workgroup per (sequence, head, 64 rows of d_v), the state
 //              rows held in LDS as three bf16 parts (hi + mid + lo equals the
 //              fp32 value exactly), three barriers per chunk.  All products on
@@ -37,45 +37,73 @@ constexpr int SDK = 128;  // d_k
 constexpr int SRW = 64;   // state rows (of d_v) per workgroup
 
 // ---------------------------------------------------------------- operand
+// Four lanes per 128-element row (32 elements each): five butterfly stages
+// inside the lane, the last two across the lane quad through DPP.
 constexpr int OP_THREADS = 256;
-constexpr int OP_LPR = 16;  // lanes per 128-element row
+constexpr int OP_LPR = 4;
+constexpr int OP_E = SDK / OP_LPR;
 
 struct OperandArgs {
-  const uint16_t* x;  // [rows][128] bf16
-  int8_t* codes;      // [rows][128]
-  float* scales;      // [rows]
+  const uint16_t* x[2];  // q, k rows [rows][128] bf16
+  int8_t* codes[2];      // [rows][128]
+  float* scales[2];      // [rows]
   int64_t rows;
   bool wht;
 };
 
 __global__ __launch_bounds__(OP_THREADS) void ssd_operand_kernel(OperandArgs a) {
-  constexpr int E = SDK / OP_LPR;
+  const int op = blockIdx.y;
   const int tid = threadIdx.x;
   const int li = tid % OP_LPR;
   const int64_t row = int64_t(blockIdx.x) * (OP_THREADS / OP_LPR) + tid / OP_LPR;
   const bool valid = row < a.rows;
-  float v[E];
-  uint4 w = make_uint4(0u, 0u, 0u, 0u);
-  if (valid) w = *reinterpret_cast<const uint4*>(a.x + row * SDK + li * E);
-  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  float v[OP_E];
+  const uint4* src = reinterpret_cast<const uint4*>(a.x[op] + row * SDK + li * OP_E);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16_lo(ww[i]);
-    v[2 * i + 1] = bf16_hi(ww[i]);
+  for (int p = 0; p < OP_E / 8; ++p) {
+    const uint4 w = valid ? src[p] : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[8 * p + 2 * i] = bf16_lo(ww[i]);
+      v[8 * p + 2 * i + 1] = bf16_hi(ww[i]);
+    }
   }
-  if (a.wht) fwht_group<E, OP_LPR>(v, li);
+  if (a.wht) {
+    fwht_local<OP_E>(v);
+    const bool up1 = (li & 1) != 0, up2 = (li & 2) != 0;
+#pragma unroll
+    for (int i = 0; i < OP_E; ++i) {
+      const float o = dpp<DPP_XOR1>(v[i]);
+      v[i] = up1 ? (o - v[i]) : (v[i] + o);
+    }
+#pragma unroll
+    for (int i = 0; i < OP_E; ++i) {
+      const float o = dpp<DPP_XOR2>(v[i]);
+      v[i] = up2 ? (o - v[i]) : (v[i] + o);
+    }
+#pragma unroll
+    for (int i = 0; i < OP_E; ++i) v[i] *= 0.08838834764831845f;  // 1/sqrt(128)
+  }
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int i = 0; i < OP_E; ++i) amax = fmaxf(amax, fabsf(v[i]));
   amax = group_max<OP_LPR>(amax);
   const float scale = codec_scale(amax);
-  float cf[E];
+  float cf[OP_E];
   codec_codes(v, scale, cf);
   if (!valid) return;
-  const uint2 out = make_uint2(pack4_i8(int(cf[0]), int(cf[1]), int(cf[2]), int(cf[3])),
-                               pack4_i8(int(cf[4]), int(cf[5]), int(cf[6]), int(cf[7])));
-  *reinterpret_cast<uint2*>(a.codes + row * SDK + li * E) = out;
-  if (li == 0) a.scales[row] = scale;
+  uint4* dst = reinterpret_cast<uint4*>(a.codes[op] + row * SDK + li * OP_E);
+#pragma unroll
+  for (int p = 0; p < OP_E / 16; ++p) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = pack4_i8(int(cf[16 * p + 4 * i]), int(cf[16 * p + 4 * i + 1]), int(cf[16 * p + 4 * i + 2]),
+                      int(cf[16 * p + 4 * i + 3]));
+    dst[p] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (li == 0) a.scales[op][row] = scale;
 }
 
 // ---------------------------------------------------------------- state pass
@@ -442,10 +470,9 @@ hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream) {
     float* fq = reinterpret_cast<float*>(ck + rows * SDK);
     float* fk = fq + rows;
     const unsigned grid = unsigned((rows + OP_THREADS / OP_LPR - 1) / (OP_THREADS / OP_LPR));
-    OperandArgs oq{static_cast<const uint16_t*>(L.q), cq, fq, int64_t(rows), L.wht};
-    OperandArgs ok{static_cast<const uint16_t*>(L.k), ck, fk, int64_t(rows), L.wht};
-    hipLaunchKernelGGL(ssd_operand_kernel, dim3(grid), dim3(OP_THREADS), 0, stream, oq);
-    hipLaunchKernelGGL(ssd_operand_kernel, dim3(grid), dim3(OP_THREADS), 0, stream, ok);
+    OperandArgs oa{{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k)}, {cq, ck}, {fq, fk},
+                   int64_t(rows), L.wht};
+    hipLaunchKernelGGL(ssd_operand_kernel, dim3(grid, 2), dim3(OP_THREADS), 0, stream, oa);
     if (hipError_t e = hipGetLastError()) return e;
     qsrc = cq;
     ksrc = ck;
