@@ -94,14 +94,16 @@ __device__ __forceinline__ void load_in_vec(const void* p, size_t i, float (&x)[
 // N consecutive inputs kept as raw words (RAW_WORDS<BF16, N> of them).
 template <bool BF16, int N>
 struct RawVec {
-  static constexpr int WORDS = BF16 ? N / 2 : N;
+  static constexpr int WORDS = BF16 ? (N + 1) / 2 : N;
   uint32_t w[WORDS];
 };
 template <bool BF16, int N>
 __device__ __forceinline__ void load_raw_vec(const void* p, size_t i, RawVec<BF16, N>& r) {
   constexpr int WORDS = RawVec<BF16, N>::WORDS;
   const char* src = static_cast<const char*>(p) + i * (BF16 ? 2 : 4);
-  if constexpr (WORDS == 1) {
+  if constexpr (BF16 && N == 1) {  // one bf16 in the low half
+    r.w[0] = *reinterpret_cast<const uint16_t*>(src);
+  } else if constexpr (WORDS == 1) {
     r.w[0] = *reinterpret_cast<const uint32_t*>(src);
   } else if constexpr (WORDS == 2) {
     const uint2 u = *reinterpret_cast<const uint2*>(src);
@@ -126,7 +128,9 @@ __device__ __forceinline__ void unpack_raw_vec(RawVec<BF16, N>& r, float (&x)[N]
   for (int q = 0; q < RawVec<BF16, N>::WORDS; ++q) asm volatile("" : "+v"(r.w[q]));
 #pragma unroll
   for (int q = 0; q < RawVec<BF16, N>::WORDS; ++q) {
-    if constexpr (BF16) {
+    if constexpr (BF16 && N == 1) {
+      x[0] = bf16_lo(r.w[0]);
+    } else if constexpr (BF16) {
       x[2 * q] = bf16_lo(r.w[q]);
       x[2 * q + 1] = bf16_hi(r.w[q]);
     } else {
@@ -193,8 +197,8 @@ struct DecShape {
   // static LDS (floats); the keys [W][DK] live in dynamic LDS
   static constexpr int XSZ = (VNG * DV > PH * CR) ? VNG * DV : PH * CR;
   static constexpr int L_X = 0;                   // open: partial sums [VNG][DV]; close: values [PH][CR]
-  static constexpr int L_Y = L_X + XSZ;           // [DK] y (open) / q (close)
-  static constexpr int L_C = L_Y + DK;            // [64] c_j
+  static constexpr int L_Y = L_X + XSZ;           // [NT/64][DK] y per wave (open) / q (close)
+  static constexpr int L_C = L_Y + (NT / 64) * DK;  // [64] c_j
   static constexpr int L_D = L_C + 64;            // [DV] row dots
   static constexpr int L_END = L_D + DV;
 };
@@ -235,55 +239,175 @@ __device__ __forceinline__ JobId job_id(const JobList& L, int job) {
   return j;
 }
 
-// Everything an open job loads from memory, issued at once (registers).
-template <int DK, int DV, bool IN_BF16>
-struct OpenRegs {
-  using S = DecShape<DK, DV>;
-  float4 kt[S::KREG];     // buffered keys
-  uint4 cw[S::NC];        // int8 chunks
-  float4 vt[S::VREG];     // buffered values
-  RawVec<IN_BF16, S::EK> qraw, kraw;
-  uint32_t vcur_raw;
-  float srow, a_slot, b_slot, alpha_t, beta_t;
-};
-
-template <int DK, int DV, bool IN_BF16>
-__device__ __forceinline__ void load_open(const DecodeArgs& a, const JobId& j, int tid,
-                                          OpenRegs<DK, DV, IN_BF16>& R) {
-  using S = DecShape<DK, DV>;
-  constexpr int NT = S::NT;
+// One open head on one wave.  With A_j = alpha_j (I - beta_j k_j k_j^T)
+// (symmetric) the window replay unrolls to
+//     o = S_0 y_0 + sum_j c_j v_j,   y = q;  for j = t, t-1, ..., 1:
+//     c_j = beta_j (k_j . y),  y <- alpha_j (y - c_j k_j),
+// so the int8 rows are read once and the state is never rebuilt.  The sweep
+// reads each buffered key and value straight from memory through a P-deep
+// register queue (bounded buffer loads: slots past the fill cost nothing)
+// and accumulates c_j v_j as it goes; the int8 rows are loaded while it runs.
+template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT>
+__device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, int lane, float* wy) {
+  constexpr int EK = DK / 64;    // key / query elements per lane
+  constexpr int RPL = DV / 64;   // state rows per lane
+  constexpr int CPR = DK / 16;   // 16-code chunks per row
+  constexpr int P = 12;          // queue depth (sweep steps loaded ahead)
   const int W = a.W;
-  const int lane = tid & 63;
-  const int bh = j.seq * a.H + j.h;
+  const int f = J.f;
+  const int bh = J.seq * a.H + J.h;
   const size_t qk_base = size_t(bh) * DK;
   const size_t v_base = size_t(bh) * DV;
   const size_t bufs_base = size_t(bh) * W;
-  R.alpha_t = a.alpha[bh];
-  R.beta_t = a.beta[bh];
-  load_raw_vec<IN_BF16, S::EK>(a.q, qk_base + lane * S::EK, R.qraw);
-  load_raw_vec<IN_BF16, S::EK>(a.k, qk_base + lane * S::EK, R.kraw);
-  // buffered keys: float4 t + NT*i of slots 0..f-1 (bounded: no traffic past the fill);
-  // one per-lane offset, the register index in the scalar offset
-  const rsrc_t rk = make_rsrc(a.buf_k + size_t(bh) * W * DK, uint32_t(j.f) * DK * 4);
+  const rsrc_t rk = make_rsrc(a.buf_k + size_t(bh) * W * DK, uint32_t(f) * DK * 4);
+  const rsrc_t rv = make_rsrc(a.buf_v + size_t(bh) * W * DV, uint32_t(f) * DV * 4);
+  const uint32_t ko = uint32_t(lane) * EK * 4, vo = uint32_t(lane) * RPL * 4;
+  auto load_k = [&](int j, float (&x)[EK]) {  // j < 0 lands past the bound: reads 0, no traffic
+    const uint32_t so = uint32_t(j) * DK * 4;
+    if constexpr (EK == 2) {
+      const uint2 w = bload_u2s(rk, ko, so);
+      x[0] = __uint_as_float(w.x);
+      x[1] = __uint_as_float(w.y);
+    } else {
+      x[0] = bload_f1s(rk, ko, so);
+    }
+  };
+  auto load_v = [&](int j, float (&x)[RPL]) {
+    const uint32_t so = uint32_t(j) * DV * 4;
+    if constexpr (RPL == 2) {
+      const uint2 w = bload_u2s(rv, vo, so);
+      x[0] = __uint_as_float(w.x);
+      x[1] = __uint_as_float(w.y);
+    } else {
+      x[0] = bload_f1s(rv, vo, so);
+    }
+  };
+  // queue first (oldest loads): the first sweep steps wait for nothing else
+  float kq[P][EK], vq[P][RPL];
 #pragma unroll
-  for (int i = 0; i < S::KREG; ++i) R.kt[i] = bload_f4(rk, uint32_t(tid) * 16, uint32_t(i * NT * 16));
-  R.a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs_base, uint32_t(j.f) * 4), uint32_t(lane) * 4);
-  R.b_slot = bload_f1(make_rsrc(a.buf_beta + bufs_base, uint32_t(j.f) * 4), uint32_t(lane) * 4);
-  const rsrc_t rc = make_rsrc(a.codes + v_base * DK, uint32_t(DV) * DK);
-#pragma unroll
-  for (int i = 0; i < S::NC; ++i) R.cw[i] = bload_u4(rc, uint32_t(tid) * 16, uint32_t(i * NT * 16));
-  const int rg = tid % S::VRG;
-  const int g = tid / S::VRG;
-  const rsrc_t rv = make_rsrc(a.buf_v + size_t(bh) * W * DV, uint32_t(j.f) * DV * 4);
-#pragma unroll
-  for (int i = 0; i < S::VREG; ++i)
-    R.vt[i] = bload_f4(rv, uint32_t(g * DV + rg * 4) * 4, uint32_t(i * S::VNG * DV * 4));
-  R.vcur_raw = 0;
-  R.srow = 0.f;
-  if (tid < DV) {
-    R.vcur_raw = load_raw<IN_BF16>(a.v, v_base + tid);
-    R.srow = a.scales[v_base + tid];
+  for (int u = 0; u < P; ++u) {
+    load_k(f - 1 - u, kq[u]);
+    load_v(f - 1 - u, vq[u]);
   }
+  const float a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
+  const float b_slot = bload_f1(make_rsrc(a.buf_beta + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
+  const float alpha_t = a.alpha[bh];
+  const float beta_t = a.beta[bh];
+  RawVec<IN_BF16, EK> qraw, kraw;
+  load_raw_vec<IN_BF16, EK>(a.q, qk_base + lane * EK, qraw);
+  load_raw_vec<IN_BF16, EK>(a.k, qk_base + lane * EK, kraw);
+  RawVec<IN_BF16, RPL> vraw;
+  load_raw_vec<IN_BF16, RPL>(a.v, v_base + lane * RPL, vraw);
+  float srow[RPL];
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) srow[i] = a.scales[v_base + lane * RPL + i];
+  uint4 cw[RPL][CPR];
+#pragma unroll
+  for (int i = 0; i < RPL; ++i)
+#pragma unroll
+    for (int c = 0; c < CPR; ++c)
+      cw[i][c] = *reinterpret_cast<const uint4*>(a.codes + (v_base + lane * RPL + i) * DK + 16 * c);
+
+  float qv[EK], kv[EK], vcur[RPL];
+  unpack_raw_vec<IN_BF16, EK>(qraw, qv);
+  unpack_raw_vec<IN_BF16, EK>(kraw, kv);
+  unpack_raw_vec<IN_BF16, RPL>(vraw, vcur);
+  if constexpr (WHT) {
+    fwht_group<EK, 64>(qv, lane);
+    fwht_group<EK, 64>(kv, lane);
+  }
+  // the current token first, then the buffered writes newest to oldest;
+  // carried as yt = y / (product of the alphas swept so far)
+  float yt[EK];
+  float p = 0.f;
+#pragma unroll
+  for (int e = 0; e < EK; ++e) {
+    yt[e] = qv[e];
+    p += kv[e] * qv[e];
+  }
+  const float c_cur = beta_t * wave_allreduce_sum(p);
+#pragma unroll
+  for (int e = 0; e < EK; ++e) yt[e] -= c_cur * kv[e];
+  float G = alpha_t;
+  float acc[RPL];
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) acc[i] = c_cur * vcur[i];
+  // one sweep step on queue slot u (write j): the slot is copied out first so
+  // that its registers can take the load of write j - P at once
+  auto step = [&](int u, int j, bool refill) {
+    float kj[EK], vj[RPL];
+#pragma unroll
+    for (int e = 0; e < EK; ++e) asm volatile("v_mov_b32 %0, %1" : "=v"(kj[e]) : "v"(kq[u][e]));
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) asm volatile("v_mov_b32 %0, %1" : "=v"(vj[i]) : "v"(vq[u][i]));
+    if (refill) {
+      load_k(j - P, kq[u]);
+      load_v(j - P, vq[u]);
+    }
+    float pp = 0.f;
+#pragma unroll
+    for (int e = 0; e < EK; ++e) pp += kj[e] * yt[e];
+    const float bt = lane_value(b_slot, j) * wave_allreduce_sum(pp);
+#pragma unroll
+    for (int e = 0; e < EK; ++e) yt[e] -= bt * kj[e];
+    const float cj = bt * G;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) acc[i] = fmaf(cj, vj[i], acc[i]);
+    G *= lane_value(a_slot, j);
+  };
+  int base = f - 1;
+  for (; base >= P - 1; base -= P) {  // whole blocks of P writes: every step refills its slot
+#pragma unroll
+    for (int u = 0; u < P; ++u) step(u, base - u, true);
+  }
+#pragma unroll
+  for (int u = 0; u < P - 1; ++u)  // the last base + 1 < P writes are already in the queue
+    if (u <= base) step(u, base - u, false);
+#pragma unroll
+  for (int e = 0; e < EK; ++e) wy[lane * EK + e] = G * yt[e];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // int8 rows . y
+  float d[RPL];
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) d[i] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPR; ++c) {
+    const float4* y4 = reinterpret_cast<const float4*>(wy + 16 * c);
+    float yy[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 t = y4[q4];
+      yy[4 * q4] = t.x;
+      yy[4 * q4 + 1] = t.y;
+      yy[4 * q4 + 2] = t.z;
+      yy[4 * q4 + 3] = t.w;
+    }
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const uint32_t w[4] = {cw[i][c].x, cw[i][c].y, cw[i][c].z, cw[i][c].w};
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int b8 = 0; b8 < 4; ++b8) d[i] = fmaf(i8_at(w[q4], b8), yy[4 * q4 + b8], d[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) {
+    const int row = lane * RPL + i;
+    store_out<OUT_BF16>(a.o, v_base + row, srow[i] * d[i] + acc[i]);
+    a.buf_v[(bufs_base + f) * DV + row] = vcur[i];  // append v
+  }
+  float* dk = a.buf_k + (bufs_base + f) * DK + lane * EK;  // append k (rotated basis under WHT)
+#pragma unroll
+  for (int e = 0; e < EK; ++e) dk[e] = kv[e];
+  if (lane == 0) {
+    a.buf_alpha[bufs_base + f] = alpha_t;
+    a.buf_beta[bufs_base + f] = beta_t;
+    if (J.h == 0) a.fill_out[J.seq] = f + 1;
+  }
+  __builtin_amdgcn_wave_barrier();  // the next head reuses wy
 }
 
 template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT>
@@ -476,169 +600,32 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
   }
 
   // ================================================================ open jobs
-  // Software-pipelined: the next job's loads are issued as soon as this job
-  // has consumed its registers, before this job's stores.
-  if (job >= L.n_jobs) return;
-  OpenRegs<DK, DV, IN_BF16> R;
-  JobId J = job_id(L, job);
+  // One wave per head.  Wave slots are numbered from the first workgroup
+  // without a close job, so open heads go to idle waves first.
   {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    load_open<DK, DV, IN_BF16>(a, J, tid, R);
-  }
-  while (true) {
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));  // keep per-thread offsets from being hoisted out of the loop
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int next = job + gridDim.x;
-    const bool has_next = next < L.n_jobs;
-    const int f = J.f;
-    const int bh = J.seq * H + J.h;
-    const size_t v_base = size_t(bh) * DV;
-    const size_t bufk_base = size_t(bh) * W * DK;
-    const size_t bufv_base = size_t(bh) * W * DV;
-    const size_t bufs_base = size_t(bh) * W;
-    const float alpha_t = R.alpha_t;
-    const float beta_t = R.beta_t;
-    float qv[S::EK], kv[S::EK];
-    unpack_raw_vec<IN_BF16, S::EK>(R.qraw, qv);
-    unpack_raw_vec<IN_BF16, S::EK>(R.kraw, kv);
-#pragma unroll
-    for (int i = 0; i < S::KREG; ++i) {
-      const int idx = tid + i * NT;
-      if (idx < f * S::KF4) reinterpret_cast<float4*>(k_lds)[idx] = R.kt[i];
-      consume(R.kt[i]);
+    const int wave = uniform(tid >> 6);
+    const int G = int(gridDim.x);
+    const int ncb = L.n_close_jobs < G ? L.n_close_jobs : G;
+    const int slot = ((int(blockIdx.x) - ncb + G) % G) * (NT / 64) + wave;
+    const int n_open = L.n_jobs - L.n_close_jobs;
+    float* wy = y_lds + wave * DK;
+    for (int o = slot; o < n_open; o += G * (NT / 64)) {
+      const JobId J = job_id(L, L.n_close_jobs + o);
+      open_head<DK, DV, IN_BF16, OUT_BF16, WHT>(a, J, lane, wy);
     }
-    consume(R.a_slot);
-    consume(R.b_slot);
-    if constexpr (WHT) {
-      fwht_group<S::EK, 64>(qv, lane);
-      fwht_group<S::EK, 64>(kv, lane);
-    }
-    __syncthreads();
-
-    // The sweeping wave rotates with the workgroup id so that the sweeps of
-    // the workgroups resident on one CU spread over its four SIMDs.
-    if (wave == (blockIdx.x & 3)) {
-      // backward sweep, carried as yt = y / (product of the alphas swept so far):
-      //   t = k_j . yt;  c_j = beta_j t G;  yt -= beta_j t k_j;  G *= alpha_j
-      float yt[S::EK];
-#pragma unroll
-      for (int e = 0; e < S::EK; ++e) yt[e] = qv[e];
-      float p = 0.f;
-#pragma unroll
-      for (int e = 0; e < S::EK; ++e) p += kv[e] * yt[e];
-      const float c_cur = beta_t * wave_allreduce_sum(p);
-#pragma unroll
-      for (int e = 0; e < S::EK; ++e) yt[e] -= c_cur * kv[e];
-      float G = alpha_t, c_reg = 0.f;
-      const float* krow = k_lds + lane * S::EK;
-      float kn[S::EK];  // the next step's key, read one step ahead
-      if (f > 0) {
-#pragma unroll
-        for (int e = 0; e < S::EK; ++e) kn[e] = krow[(f - 1) * DK + e];
-      }
-      for (int j = f - 1; j >= 0; --j) {
-        float kj[S::EK];
-#pragma unroll
-        for (int e = 0; e < S::EK; ++e) kj[e] = kn[e];
-        const int jn = j > 0 ? j - 1 : 0;
-#pragma unroll
-        for (int e = 0; e < S::EK; ++e) kn[e] = krow[jn * DK + e];
-        float pp = 0.f;
-#pragma unroll
-        for (int e = 0; e < S::EK; ++e) pp += kj[e] * yt[e];
-        const float bt = lane_value(R.b_slot, j) * wave_allreduce_sum(pp);
-#pragma unroll
-        for (int e = 0; e < S::EK; ++e) yt[e] -= bt * kj[e];
-        c_reg = (lane == j) ? bt * G : c_reg;
-        G *= lane_value(R.a_slot, j);
-      }
-#pragma unroll
-      for (int e = 0; e < S::EK; ++e) y_lds[lane * S::EK + e] = G * yt[e];
-      if (lane < f) c_lds[lane] = c_reg;
-      if (lane == 0) c_lds[63] = c_cur;
-    }
-    __syncthreads();
-
-    // int8 rows . y  (chunk = tid + NT*i: row chunk / CPR, 16 codes)
-#pragma unroll
-    for (int i = 0; i < S::NC; ++i) {
-      const int chunk = tid + i * NT;
-      const int row = chunk / S::CPR;
-      const int seg = chunk % S::CPR;
-      const float4* y4 = reinterpret_cast<const float4*>(y_lds + seg * 16);
-      const uint32_t w[4] = {R.cw[i].x, R.cw[i].y, R.cw[i].z, R.cw[i].w};
-      float p = 0.f;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 yy = y4[q4];
-        p += i8_at(w[q4], 0) * yy.x + i8_at(w[q4], 1) * yy.y + i8_at(w[q4], 2) * yy.z +
-             i8_at(w[q4], 3) * yy.w;
-      }
-      p = group_sum<S::CPR>(p);
-      if (seg == 0) d_lds[row] = p;
-    }
-    // buffered values weighted by c_j
-    {
-      const int rg = tid % S::VRG;
-      const int g = tid / S::VRG;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int i = 0; i < S::VREG; ++i) {
-        const int j = g + i * S::VNG;
-        const float cj = (j < f) ? c_lds[j] : 0.f;
-        acc.x += cj * R.vt[i].x;
-        acc.y += cj * R.vt[i].y;
-        acc.z += cj * R.vt[i].z;
-        acc.w += cj * R.vt[i].w;
-      }
-      reinterpret_cast<float4*>(x_lds + g * DV)[rg] = acc;
-    }
-    __syncthreads();
-    float out = 0.f, vcur = 0.f;
-    if (tid < DV) {
-      float vsum = 0.f;
-#pragma unroll
-      for (int gg = 0; gg < S::VNG; ++gg) vsum += x_lds[gg * DV + tid];
-      vcur = raw_to_f32<IN_BF16>(R.vcur_raw);
-      out = R.srow * d_lds[tid] + vsum + c_lds[63] * vcur;
-    }
-    // the next job's loads go out before this job's stores
-    JobId JN = J;
-    if (has_next) {
-      JN = job_id(L, next);
-      load_open<DK, DV, IN_BF16>(a, JN, tid, R);
-    }
-    if (tid < DV) {
-      store_out<OUT_BF16>(a.o, v_base + tid, out);
-      a.buf_v[bufv_base + size_t(f) * DV + tid] = vcur;  // append v
-    }
-    if (wave == 0) {  // append k (rotated basis under WHT)
-      float* dst = a.buf_k + bufk_base + size_t(f) * DK + lane * S::EK;
-#pragma unroll
-      for (int e = 0; e < S::EK; ++e) dst[e] = kv[e];
-    }
-    if (tid == 0) {
-      a.buf_alpha[bufs_base + f] = alpha_t;
-      a.buf_beta[bufs_base + f] = beta_t;
-      if (J.h == 0) a.fill_out[J.seq] = f + 1;
-    }
-    if (!has_next) break;
-    job = next;
-    J = JN;
-    __syncthreads();  // LDS is reused by the next job
   }
 }
 
 int decode_row_split() { return 4; }  // close jobs per head at most (grid validation)
 int decode_max_batch() { return DEC_MAXB; }
-// Persistent grid: about four resident workgroups per CU on 256 CUs, never
+// Persistent grid: three resident workgroups per CU on 256 CUs, never
 // more workgroups than jobs.  GDNQ_DECODE_GRID overrides it (tuning).
 static unsigned decode_grid(int B, int H, int rc) {
   const long jobs_max = long(B) * H * rc;
-  long g = 1024;
+  long g = 768;  // three resident workgroups per CU
   if (const char* e = getenv("GDNQ_DECODE_GRID")) {
     const long v = atol(e);
     if (v > 0) g = v;

@@ -195,6 +195,16 @@ __device__ __forceinline__ uint2 bload_u2(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ float bload_f1(rsrc_t r, uint32_t off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+// per-lane offset plus a scalar offset (wave-uniform)
+__device__ __forceinline__ uint2 bload_u2s(rsrc_t r, uint32_t off, uint32_t soff) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+  uint2 u;
+  __builtin_memcpy(&u, &v, 8);
+  return u;
+}
+__device__ __forceinline__ float bload_f1s(rsrc_t r, uint32_t off, uint32_t soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+}
 
 // XCD-aware workgroup id: workgroups are dispatched round-robin over the 8
 // XCDs, so block x runs on XCD x % 8.  This remaps ids so that consecutive

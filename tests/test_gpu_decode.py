@@ -127,6 +127,9 @@ DECODE_CASES = [
     (2, 5, 64, 64, 16, torch.float32, torch.float32, True, [15, 9]),
     (3, 2, 128, 128, 1, torch.bfloat16, torch.bfloat16, False, [0, 0, 0]),
     (2, 2, 128, 128, 64, torch.bfloat16, torch.bfloat16, False, [63, 62]),
+    (3, 2, 64, 64, 8, torch.bfloat16, torch.float32, False, [7, 3, 0]),
+    (3, 2, 64, 128, 8, torch.bfloat16, torch.bfloat16, True, [2, 7, 5]),
+    (2, 3, 128, 64, 64, torch.bfloat16, torch.float32, True, [63, 40]),
 ]
 
 
