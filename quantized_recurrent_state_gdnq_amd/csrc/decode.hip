@@ -33,6 +33,12 @@ namespace gdnq {
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_MAXB = 1024;   // sequences per call (fill scan results in LDS)
 constexpr int PH = 16;           // buffer slots staged in LDS per phase
+#ifndef DEC_CODE_LEAD
+#define DEC_CODE_LEAD 2
+#endif
+#ifndef DEC_QUEUE
+#define DEC_QUEUE 12
+#endif
 
 struct DecodeArgs {
   const void* q;
@@ -252,7 +258,8 @@ __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, i
   constexpr int EK = DK / 64;    // key / query elements per lane
   constexpr int RPL = DV / 64;   // state rows per lane
   constexpr int CPR = DK / 16;   // 16-code chunks per row
-  constexpr int P = 12;          // queue depth (sweep steps loaded ahead)
+  constexpr int P = DEC_QUEUE;   // queue depth (sweep steps loaded ahead)
+  constexpr int CODE_LEAD = DEC_CODE_LEAD;
   const int W = a.W;
   const int f = J.f;
   const int bh = J.seq * a.H + J.h;
@@ -301,12 +308,17 @@ __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, i
   float srow[RPL];
 #pragma unroll
   for (int i = 0; i < RPL; ++i) srow[i] = a.scales[v_base + lane * RPL + i];
+  // the int8 rows are needed last: their loads go out when at most CODE_LEAD
+  // blocks of sweep steps remain, so that early bandwidth feeds the sweeps of
+  // the heads with the longest windows (they bound the step)
   uint4 cw[RPL][CPR];
+  auto load_codes = [&]() {
 #pragma unroll
-  for (int i = 0; i < RPL; ++i)
+    for (int i = 0; i < RPL; ++i)
 #pragma unroll
-    for (int c = 0; c < CPR; ++c)
-      cw[i][c] = *reinterpret_cast<const uint4*>(a.codes + (v_base + lane * RPL + i) * DK + 16 * c);
+      for (int c = 0; c < CPR; ++c)
+        cw[i][c] = *reinterpret_cast<const uint4*>(a.codes + (v_base + lane * RPL + i) * DK + 16 * c);
+  };
 
   float qv[EK], kv[EK], vcur[RPL];
   unpack_raw_vec<IN_BF16, EK>(qraw, qv);
@@ -355,14 +367,66 @@ __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, i
     for (int i = 0; i < RPL; ++i) acc[i] = fmaf(cj, vj[i], acc[i]);
     G *= lane_value(a_slot, j);
   };
+  // two writes at a time (slots u, u + 1 = writes j, j - 1): with
+  // d_a = k_j . yt, d_b = k_{j-1} . yt and g = k_j . k_{j-1} (three
+  // overlapped reductions), bt_a = beta_j d_a and
+  // bt_b = beta_{j-1} (k_{j-1} . (yt - bt_a k_j)) = beta_{j-1} (d_b - bt_a g)
+  auto step2 = [&](int u, int j, bool refill) {
+    float ka[EK], kb[EK], va[RPL], vb[RPL];
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+      asm volatile("v_mov_b32 %0, %1" : "=v"(ka[e]) : "v"(kq[u][e]));
+      asm volatile("v_mov_b32 %0, %1" : "=v"(kb[e]) : "v"(kq[u + 1][e]));
+    }
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      asm volatile("v_mov_b32 %0, %1" : "=v"(va[i]) : "v"(vq[u][i]));
+      asm volatile("v_mov_b32 %0, %1" : "=v"(vb[i]) : "v"(vq[u + 1][i]));
+    }
+    if (refill) {
+      load_k(j - P, kq[u]);
+      load_v(j - P, vq[u]);
+      load_k(j - 1 - P, kq[u + 1]);
+      load_v(j - 1 - P, vq[u + 1]);
+    }
+    float da = 0.f, db = 0.f, g = 0.f;
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+      da += ka[e] * yt[e];
+      db += kb[e] * yt[e];
+      g += ka[e] * kb[e];
+    }
+    wave_allreduce_sum3(da, db, g);
+    const float bta = lane_value(b_slot, j) * da;
+    const float btb = lane_value(b_slot, j - 1) * (db - bta * g);
+#pragma unroll
+    for (int e = 0; e < EK; ++e) yt[e] = fmaf(-btb, kb[e], fmaf(-bta, ka[e], yt[e]));
+    const float ca = bta * G;
+    G *= lane_value(a_slot, j);
+    const float cb = btb * G;
+    G *= lane_value(a_slot, j - 1);
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) acc[i] = fmaf(cb, vb[i], fmaf(ca, va[i], acc[i]));
+  };
+  static_assert(P % 2 == 0, "queue depth is even");
   int base = f - 1;
-  for (; base >= P - 1; base -= P) {  // whole blocks of P writes: every step refills its slot
+  for (; base >= CODE_LEAD * P - 1 && base >= P - 1; base -= P) {  // whole blocks: every slot is refilled
 #pragma unroll
-    for (int u = 0; u < P; ++u) step(u, base - u, true);
+    for (int u = 0; u < P; u += 2) step2(u, base - u, true);
   }
+  if constexpr (CODE_LEAD > 0) load_codes();  // at most CODE_LEAD blocks (plus the tail) before the rows are needed
+  for (; base >= P - 1; base -= P) {
 #pragma unroll
-  for (int u = 0; u < P - 1; ++u)  // the last base + 1 < P writes are already in the queue
-    if (u <= base) step(u, base - u, false);
+    for (int u = 0; u < P; u += 2) step2(u, base - u, true);
+  }
+  // the last base + 1 < P writes are already in the queue: pairs, then one
+#pragma unroll
+  for (int u = 0; u + 1 < P; u += 2)
+    if (u + 1 <= base) step2(u, base - u, false);
+#pragma unroll
+  for (int u = 0; u < P; u += 2)
+    if (u == base) step(u, 0, false);
+  if constexpr (CODE_LEAD == 0) load_codes();
 #pragma unroll
   for (int e = 0; e < EK; ++e) wy[lane * EK + e] = G * yt[e];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

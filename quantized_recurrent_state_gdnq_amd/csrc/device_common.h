@@ -78,6 +78,35 @@ __device__ __forceinline__ float wave_allreduce_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Three independent full-wave sums, stage by stage, so that their latencies
+// overlap.
+__device__ __forceinline__ void wave_allreduce_sum3(float& x, float& y, float& z) {
+  x += dpp<DPP_XOR1>(x);
+  y += dpp<DPP_XOR1>(y);
+  z += dpp<DPP_XOR1>(z);
+  x += dpp<DPP_XOR2>(x);
+  y += dpp<DPP_XOR2>(y);
+  z += dpp<DPP_XOR2>(z);
+  x += dpp<DPP_ROW_HALF_MIRROR>(x);
+  y += dpp<DPP_ROW_HALF_MIRROR>(y);
+  z += dpp<DPP_ROW_HALF_MIRROR>(z);
+  x += dpp<DPP_ROW_MIRROR>(x);
+  y += dpp<DPP_ROW_MIRROR>(y);
+  z += dpp<DPP_ROW_MIRROR>(z);
+  const auto a1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const auto b1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  const auto c1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+  x = __uint_as_float(a1[0]) + __uint_as_float(a1[1]);
+  y = __uint_as_float(b1[0]) + __uint_as_float(b1[1]);
+  z = __uint_as_float(c1[0]) + __uint_as_float(c1[1]);
+  const auto a2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  const auto c2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+  x = __uint_as_float(a2[0]) + __uint_as_float(a2[1]);
+  y = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+  z = __uint_as_float(c2[0]) + __uint_as_float(c2[1]);
+}
+
 // ---------------------------------------------------------------- FWHT
 // Fast Walsh-Hadamard transform of a d-vector spread over a group of lanes:
 // lane j of the group holds elements [j*E, j*E + E) in v[0..E).  The

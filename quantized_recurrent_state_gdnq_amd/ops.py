@@ -8,6 +8,8 @@ raw pointers to the library.
 
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -56,7 +58,7 @@ def quantize_state(S, codes=None, scales=None, wht=False):
 
 
 def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, buf_beta,
-                fill_in, fill_out, o=None, *, wht=False, out_dtype=None):
+                fill_in, fill_out, o=None, *, wht=False, out_dtype=None, _bind_only=False):
     """One decode token per sequence (see gdnq_decode_step in include/gdnq.h).
 
     q, k [B,H,d_k], v [B,H,d_v] (fp32 or bf16); alpha, beta [B,H] fp32;
@@ -93,10 +95,12 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
         raise ValueError("inconsistent decode shapes")
     p = _lib.DecodeParams(B, H, d_k, d_v, W, _DT[q.dtype], _DT[o.dtype],
                           _lib.GDNQ_FLAG_WHT if wht else 0)
-    _lib.check(_lib.decode_step(p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(codes),
-                                _ptr(scales), _ptr(buf_k), _ptr(buf_v), _ptr(buf_alpha),
-                                _ptr(buf_beta), _ptr(fill_in), _ptr(fill_out), _ptr(o),
-                                _stream(dev)))
+    args = (p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(codes), _ptr(scales),
+            _ptr(buf_k), _ptr(buf_v), _ptr(buf_alpha), _ptr(buf_beta), _ptr(fill_in), _ptr(fill_out),
+            _ptr(o), _stream(dev))
+    if _bind_only:
+        return o, args
+    _lib.check(_lib.decode_step(*args))
     return o
 
 
@@ -183,6 +187,28 @@ class DecodeState:
         self.buf_beta = torch.empty((B, H, window), dtype=torch.float32, device=dev)
         self.fill = torch.zeros(B, dtype=torch.int32, device=dev) if fill is None else fill
         self._fill_next = torch.empty_like(self.fill)
+
+    def bind(self, q, k, v, alpha, beta, o):
+        """Validate once for token buffers that are reused every step (a
+        serving loop writes each new token into them) and return a
+        zero-argument callable that launches one step on the current stream
+        and advances the fill ping-pong."""
+        _, a0 = decode_step(q, k, v, alpha, beta, self.codes, self.scales, self.buf_k, self.buf_v,
+                            self.buf_alpha, self.buf_beta, self.fill, self._fill_next, o,
+                            wht=self.wht, _bind_only=True)
+        _, a1 = decode_step(q, k, v, alpha, beta, self.codes, self.scales, self.buf_k, self.buf_v,
+                            self.buf_alpha, self.buf_beta, self._fill_next, self.fill, o,
+                            wht=self.wht, _bind_only=True)
+        f0 = self.fill
+        orient = [(ctypes.byref(a[0]),) + tuple(a[1:]) for a in (a0, a1)]
+        fn = _lib.lib.gdnq_decode_step
+
+        def launch():
+            st = fn(*orient[0 if self.fill is f0 else 1])
+            if st:
+                _lib.check(st)
+            self.fill, self._fill_next = self._fill_next, self.fill
+        return launch
 
     def step(self, q, k, v, alpha, beta, o=None, out_dtype=None):
         o = decode_step(q, k, v, alpha, beta, self.codes, self.scales, self.buf_k, self.buf_v,

@@ -245,3 +245,36 @@ def test_decode_every_row_split(R, monkeypatch):
                         fill=np.array([15, 0, 7, 15, 14, 3]))
     got, codes, scales = _run_decode(d, 16, torch.bfloat16, torch.float32)
     _check_decode(d, 16, got, codes, scales, OUT_TOL_BF16)
+
+
+def test_decode_bound_launcher_matches_step():
+    """DecodeState.bind (validated once, prebuilt arguments) runs the same
+    steps as DecodeState.step: 20 steps over three windows of 8, bitwise."""
+    B, H, d, W = 3, 2, 128, 8
+    d0 = wl.decode_batch(B=B, H=H, dk=d, dv=d, W=W, seed=21, fill=np.array([0, 5, 7]))
+    codes, scales = O.quantize_rows(d0["state"])
+    sts = []
+    for _ in range(2):
+        st = ops.DecodeState(dev(codes), dev(scales), W, fill=dev(d0["fill"]))
+        for name in ("buf_k", "buf_v", "buf_alpha", "buf_beta"):
+            getattr(st, name).copy_(dev(d0[name]))
+        sts.append(st)
+    tok = [torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    ab = [torch.empty((B, H), dtype=torch.float32, device=DEV) for _ in range(2)]
+    o_b = torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV)
+    launch = sts[1].bind(*tok, *ab, o=o_b)
+    for t in range(20):
+        x = wl.decode_tokens(B=B, H=H, dk=d, dv=d, step=t, seed=22)
+        for dst, name in zip(tok, ("q", "k", "v")):
+            dst.copy_(dev(x[name], torch.bfloat16))
+        for dst, name in zip(ab, ("alpha", "beta")):
+            dst.copy_(dev(x[name]))
+        o_s = sts[0].step(*tok, *ab)
+        launch()
+        torch.cuda.synchronize()
+        assert torch.equal(o_s, o_b), f"step {t}"
+    for name in ("codes", "scales", "fill"):
+        assert torch.equal(getattr(sts[0], name), getattr(sts[1], name)), name
+    for name in ("buf_k", "buf_v"):  # slots never written keep their NaN poison
+        assert torch.allclose(getattr(sts[0], name), getattr(sts[1], name), rtol=0, atol=0,
+                              equal_nan=True), name
