@@ -33,6 +33,26 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
+// DPP move with a row mask: rows left out, and lanes whose source falls
+// outside the row, read 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_rows(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, all in DPP: row_shr by
+// 1, 2, 4, 8 inside each row of 16, then row_bcast:15 adds the last lane of
+// rows 0 and 2 to rows 1 and 3, and row_bcast:31 adds lane 31 to rows 2, 3.
+__device__ __forceinline__ float wave_scan_incl(float x) {
+  x += dpp_rows<0x111, 0xF>(x);
+  x += dpp_rows<0x112, 0xF>(x);
+  x += dpp_rows<0x114, 0xF>(x);
+  x += dpp_rows<0x118, 0xF>(x);
+  x += dpp_rows<0x142, 0xA>(x);
+  x += dpp_rows<0x143, 0xC>(x);
+  return x;
+}
+
 // Sum over aligned groups of N consecutive lanes (N = 1..64); every lane of a
 // group receives the group's sum.
 template <int N>
