@@ -16,6 +16,7 @@ from .gdnq_oracle import (  # noqa: F401
     ssd_step,
     run_windowed,
     decode_step,
+    round_bf16,
     prefill,
     chunked_fp64,
     ssd_closed_form,

@@ -235,8 +235,20 @@ def run_windowed(q, k, v, alpha, beta=None, *, W, codes0=None, scale0=None,
             "scale": scale if W is not None else None, "buf": bufs, "n": n, "S": S}
 
 
+def round_bf16(x):
+    """Nearest bf16 value of each fp32 entry, ties to even (finite inputs).
+
+    bf16 keeps the top 16 bits of an fp32 word; rounding to nearest even on
+    the dropped 16 bits is: add 0x7FFF plus the lowest kept bit, then clear
+    the dropped bits.
+    """
+    u = np.ascontiguousarray(np.asarray(x, dtype=F32)).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(F32)
+
+
 def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha,
-                buf_beta, fill, W, rot=False, dtype=F32):
+                buf_beta, fill, W, rot=False, dtype=F32, buf_bf16=False):
     """One decode token for a batch of sequences ([LQ] per-window quantization).
 
     q, k: [B,H,dk]; v: [B,H,dv]; alpha, beta: [B,H]; codes [B,H,dv,dk];
@@ -244,6 +256,13 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha,
     buf_beta [B,H,W]; fill [B] = writes already buffered for the sequence.
     With rot, q and k are rotated before use; buffered keys are already in
     the rotated basis.
+
+    buf_bf16 (the low-precision window buffer, a variant the pages list as a
+    storage option, not their default): the buffered keys and values are
+    kept as bf16.  The token's own write enters this step exactly; the copy
+    appended to the buffer is rounded to bf16 (round_bf16), so later steps
+    and the window's close replay the rounded write.  Alpha and beta stay
+    fp32.  With bf16 inputs and no rotation this is lossless.
 
     Returns (o, codes_out, scales_out, buf_k, buf_v, buf_alpha, buf_beta,
     fill_out).  The buffer slot `fill` receives the token's write unless its
@@ -285,8 +304,12 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha,
         fill_out[seqs] = r["n"]
         if r["n"] > 0:
             slot = r["n"] - 1
-            bk_out[seqs, :, slot] = r["buf"]["k"][slot].reshape(nb, H, dk)
-            bv_out[seqs, :, slot] = r["buf"]["v"][slot].reshape(nb, H, dv)
+            wk = r["buf"]["k"][slot].reshape(nb, H, dk)
+            wv = r["buf"]["v"][slot].reshape(nb, H, dv)
+            if buf_bf16:
+                wk, wv = round_bf16(wk), round_bf16(wv)
+            bk_out[seqs, :, slot] = wk
+            bv_out[seqs, :, slot] = wv
             ba_out[seqs, :, slot] = r["buf"]["alpha"][slot].reshape(nb, H)
             bb_out[seqs, :, slot] = r["buf"]["beta"][slot].reshape(nb, H)
     return o, codes_out, scales_out, bk_out, bv_out, ba_out, bb_out, fill_out

@@ -126,3 +126,23 @@ def test_window_off_by_one_is_caught(monkeypatch):
     W, q, k, v, a, b, o, c2, s2, cf, sf = _worked()
     r = G.run_windowed(q[:, None], k[:, None], v[:, None], a[:, None], b[:, None], W=W + 1)
     assert not np.array_equal(r["o"][:, 0], o.astype(F32))
+
+
+# ---------------------------------------------------------------- bf16 buffer rounding
+def _mut_round_truncate(x):  # drop the low bits (round toward zero)
+    u = np.ascontiguousarray(np.asarray(x, dtype=F32)).view(np.uint32) & np.uint32(0xFFFF0000)
+    return u.view(F32)
+
+
+def _mut_round_half_up(x):  # ties away from zero instead of to even
+    u = np.ascontiguousarray(np.asarray(x, dtype=F32)).view(np.uint32).astype(np.uint64)
+    return (((u + 0x8000) & 0xFFFF0000).astype(np.uint32)).view(F32)
+
+
+@pytest.mark.parametrize("mut", [_mut_round_truncate, _mut_round_half_up])
+def test_bf16_rounding_mutants_are_caught(mut, monkeypatch):
+    import test_oracle_pins as P
+    monkeypatch.setattr(G, "round_bf16", mut)
+    monkeypatch.setattr(P.O, "round_bf16", mut)
+    with pytest.raises(AssertionError):
+        P.test_round_bf16_golden()

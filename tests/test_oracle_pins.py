@@ -476,3 +476,83 @@ def test_decode_buffer_is_the_window_and_poison_is_not_read():
             assert np.array_equal(c2[bi], codes[bi])
         else:
             assert np.all(np.isfinite(s2[bi]))
+
+
+# ---------------------------------------------------------------- bf16 window buffer (variant)
+def test_round_bf16_golden():
+    """Round-to-nearest-even onto bf16, values worked by hand from the bit
+    patterns: exact ties go to the even neighbour, a carry can reach the
+    exponent, bf16 values are fixed points."""
+    cases = [
+        (1.0, 1.0),
+        (1.0 + 2.0 ** -8, 1.0),                      # 0x3F808000: tie, kept LSB 0 -> down
+        (1.0 + 3 * 2.0 ** -8, 1.015625),             # 0x3F818000: tie, kept LSB 1 -> up
+        (1.0 + 2.0 ** -8 + 2.0 ** -20, 1.0078125),   # just above the tie -> up
+        (-2.5, -2.5),                                # already bf16
+        (np.float32(np.pi), 3.140625),               # 0x40490FDB -> 0x40490000
+        (np.uint32(0x3FFFFFFF).view(F32), 2.0),      # carry into the exponent
+        (0.0, 0.0),
+    ]
+    x = np.array([c[0] for c in cases], F32)
+    want = np.array([c[1] for c in cases], F32)
+    assert np.array_equal(O.round_bf16(x), want)
+
+
+def test_round_bf16_matches_torch_cast():
+    """The same rounding as torch's fp32 -> bfloat16 cast (a library routine)."""
+    import torch
+    g = np.random.default_rng(31)
+    x = (g.standard_normal(4096) * np.exp(g.uniform(-20, 20, 4096))).astype(F32)
+    t = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(O.round_bf16(x), t)
+
+
+def test_buf_bf16_lossless_for_bf16_inputs():
+    """Without rotation, bf16 inputs make the bf16 buffer lossless: every
+    output of a step (o, codes, scales, buffers, fill) equals the fp32-buffer
+    step bit for bit, over several steps and a window close."""
+    W = 6
+    d = wl.decode_batch(B=3, H=2, dk=16, dv=16, W=W, seed=5, fill=np.array([0, 3, 5]), poison=False)
+    codes, scales = O.quantize_rows(d["state"])
+    bufs = [O.round_bf16(d["buf_k"]), O.round_bf16(d["buf_v"]), d["buf_alpha"], d["buf_beta"]]
+    st32 = [codes, scales] + [np.copy(x) for x in bufs] + [d["fill"]]
+    st16 = [codes, scales] + [np.copy(x) for x in bufs] + [d["fill"]]
+    for t in range(8):
+        x = wl.decode_tokens(B=3, H=2, dk=16, dv=16, step=t, seed=6)
+        a = O.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], *st32[:6], st32[6], W)
+        b = O.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], *st16[:6], st16[6], W,
+                          buf_bf16=True)
+        for u, w in zip(a, b):
+            assert np.array_equal(u, w, equal_nan=True)
+        st32, st16 = list(a[1:]), list(b[1:])
+
+
+def test_buf_bf16_rotated_write_is_rounded_when_stored():
+    """With rotation the rotated key is not a bf16 value: the step's own
+    output uses it exactly (same as the fp32 buffer), the stored copy is its
+    bf16 rounding, and the next step replays the rounded copy."""
+    W = 8
+    d = wl.decode_batch(B=2, H=2, dk=16, dv=16, W=W, seed=7, fill=np.array([1, 2]), poison=False)
+    codes, scales = O.quantize_rows(d["state"])
+    bk, bv = O.round_bf16(d["buf_k"]), O.round_bf16(d["buf_v"])
+    args = (codes, scales, bk, bv, d["buf_alpha"], d["buf_beta"], d["fill"], W)
+    a = O.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], *args, rot=True)
+    b = O.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], *args, rot=True, buf_bf16=True)
+    assert np.array_equal(a[0], b[0])
+    for s_ in range(2):
+        f = int(d["fill"][s_])
+        assert np.array_equal(b[3][s_, :, f], O.round_bf16(a[3][s_, :, f]))
+        assert np.array_equal(b[4][s_, :, f], O.round_bf16(a[4][s_, :, f]))
+        assert not np.array_equal(b[3][s_, :, f], a[3][s_, :, f])
+    # the next step from the bf16-buffer state equals a replay of the rounded writes
+    x = wl.decode_tokens(B=2, H=2, dk=16, dv=16, step=1, seed=8)
+    c = O.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], *b[1:7], b[7], W, rot=True,
+                      buf_bf16=True)
+    for s_ in range(2):
+        f = int(b[7][s_])
+        buf = {"k": np.moveaxis(b[3][s_, :, :f], 1, 0), "v": np.moveaxis(b[4][s_, :, :f], 1, 0),
+               "alpha": b[5][s_, :, :f].T, "beta": b[6][s_, :, :f].T}
+        r = O.run_windowed(x["q"][s_][None], x["k"][s_][None], x["v"][s_][None],
+                           x["alpha"][s_][None], x["beta"][s_][None], W=W, codes0=b[1][s_],
+                           scale0=b[2][s_], buffer0=buf, rot=True)
+        assert np.array_equal(c[0][s_], r["o"][0])
