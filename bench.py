@@ -39,19 +39,21 @@ BF16_PEAK_TFLOPS = 2516.6
 B, H, DK, DV, W = 64, 32, 128, 128, 64
 
 
-def decode_bytes_per_head(f, W=W, dk=DK, dv=DV, e_in=2, e_out=2):
+def decode_bytes_per_head(f, W=W, dk=DK, dv=DV, e_in=2, e_out=2, e_buf=4):
     """Algorithmic HBM bytes of one decode token for one head with fill f:
-    int8 rows + scales read, f buffered writes read, the token's q, k, v,
-    alpha, beta read, o written, and either the token's write appended
-    (window open) or the requantized rows + scales written (window close)."""
-    rd = dv * dk + 4 * dv + (4 * dk + 4 * dv + 8) * f + e_in * (2 * dk + dv) + 8
-    wr = e_out * dv + ((4 * dk + 4 * dv + 8) if f + 1 < W else (dv * dk + 4 * dv))
+    int8 rows + scales read, f buffered writes read (k, v at e_buf bytes per
+    entry, alpha and beta fp32), the token's q, k, v, alpha, beta read, o
+    written, and either the token's write appended (window open) or the
+    requantized rows + scales written (window close)."""
+    w = e_buf * (dk + dv) + 8
+    rd = dv * dk + 4 * dv + w * f + e_in * (2 * dk + dv) + 8
+    wr = e_out * dv + (w if f + 1 < W else (dv * dk + 4 * dv))
     return rd + wr
 
 
-def decode_bytes(fills, heads=H):
+def decode_bytes(fills, heads=H, e_buf=4):
     per_seq_fill = 8  # fill_in read + fill_out write
-    return int(sum(heads * decode_bytes_per_head(int(f)) + per_seq_fill for f in fills))
+    return int(sum(heads * decode_bytes_per_head(int(f), e_buf=e_buf) + per_seq_fill for f in fills))
 
 
 def source_hash(*names):
@@ -108,7 +110,11 @@ def cpu_baseline_decode(seconds=12.0):
                       f"({el:.1f} s), numpy fp32 oracle"}
 
 
-def bench_decode(args, torch, ops, wl, rep_count):
+def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None):
+    """Timed decode steps; buf_dtype torch.bfloat16 runs the low-precision
+    window buffer (writes stored as bf16) on the same workload."""
+    buf_dtype = buf_dtype or torch.float32
+    e_buf = 2 if buf_dtype == torch.bfloat16 else 4
     dev = torch.device("cuda:0")
     d = wl.decode_batch(B=B, H=H, dk=DK, dv=DV, W=W, seed=0)
     state = torch.from_numpy(d["state"]).to(dev)
@@ -117,9 +123,9 @@ def bench_decode(args, torch, ops, wl, rep_count):
     reps = []
     for i in range(rep_count):
         rep = ops.DecodeState(codes0.clone(), scales0.clone(), W,
-                              fill=torch.from_numpy(d["fill"]).to(dev))
-        rep.buf_k.copy_(torch.from_numpy(d["buf_k"]))
-        rep.buf_v.copy_(torch.from_numpy(d["buf_v"]))
+                              fill=torch.from_numpy(d["fill"]).to(dev), buf_dtype=buf_dtype)
+        rep.buf_k.copy_(torch.from_numpy(d["buf_k"]).to(buf_dtype))
+        rep.buf_v.copy_(torch.from_numpy(d["buf_v"]).to(buf_dtype))
         rep.buf_alpha.copy_(torch.from_numpy(d["buf_alpha"]))
         rep.buf_beta.copy_(torch.from_numpy(d["buf_beta"]))
         reps.append(rep)
@@ -140,7 +146,7 @@ def bench_decode(args, torch, ops, wl, rep_count):
         r = i % rep_count
         launchers[r][0]()
         f = host_fills[r]
-        nbytes = decode_bytes(f)
+        nbytes = decode_bytes(f, e_buf=e_buf)
         host_fills[r] = np.where(f + 1 == W, 0, f + 1)
         return nbytes
 
@@ -276,6 +282,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurements")
+    ap.add_argument("--no-bf16-buffer", action="store_true",
+                    help="skip the decode measurement with the bf16 window buffer")
     ap.add_argument("--skip-decode", action="store_true",
                     help="profiling aid: time only the prefills (the printed line then has no decode value)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -322,6 +330,18 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(r["bytes_per_launch"])},
     }
+    if not args.no_bf16_buffer:
+        rb = bench_decode(args, torch, ops, wl, max(1, args.replicas), buf_dtype=torch.bfloat16)
+        line["decode_bf16_buffer"] = {
+            "workload": "the same decode step with the window buffer's keys and values stored "
+                        "as bf16 (GDNQ_FLAG_BUF_BF16; lossless for bf16 inputs without WHT)",
+            "ms_per_step": round(rb["ms_per_step"], 5),
+            "tokens_s": round(rb["tokens_s"], 1),
+            "gbps": round(rb["gbps"], 1),
+            "roofline": {"bound": "hbm", "achieved": round(rb["gbps"], 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(rb["gbps"] / HBM_PEAK_GBPS, 4),
+                         "algorithmic_bytes_per_launch": int(rb["bytes_per_launch"])},
+        }
     if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, ops, wl)
     if not args.no_cpu_baseline:

@@ -78,9 +78,16 @@ enum {
   GDNQ_FLAG_SSD = 2u,     /* prefill only: scalar-decay SSD recurrence
                              S_t = a_t S_{t-1} + v_t k_t^T (no delta term);
                              state kept in fp32, not quantized                */
-  GDNQ_FLAG_INT8_QK = 4u  /* prefill + SSD only: quantize each token's
+  GDNQ_FLAG_INT8_QK = 4u, /* prefill + SSD only: quantize each token's
                              (rotated) q and k row to int8 with the codec
                              above and use the dequantized operands         */
+  GDNQ_FLAG_BUF_BF16 = 16u /* decode only: the window buffer keeps keys and
+                             values as bf16 (buf_k, buf_v element type).  A
+                             token's write enters its own step exactly and is
+                             stored rounded to nearest even, so later steps
+                             and the window's close replay the rounded write;
+                             alpha and beta stay fp32.  Lossless when q, k, v
+                             are bf16 and GDNQ_FLAG_WHT is off.              */
 };
 
 /* ------------------------------------------------------------------------
@@ -118,11 +125,14 @@ gdnq_status gdnq_quantize_state(const float* S, int64_t rows, int32_t d_k, int8_
  *
  *   0 <= p->batch B <= 1024 (0: no-op), p->heads H >= 1, p->d_k, p->d_v in {64,128},
  *   1 <= p->window W <= 64, p->in_dtype (q,k,v) and p->out_dtype (o) in
- *   {GDNQ_F32, GDNQ_BF16}, p->flags in {0, GDNQ_FLAG_WHT}.
+ *   {GDNQ_F32, GDNQ_BF16}, p->flags a combination of GDNQ_FLAG_WHT and
+ *   GDNQ_FLAG_BUF_BF16 (the low-precision window buffer, an option the
+ *   Low-Bit GDN page lists among buffer storage formats).
  *     q, k      [B,H,d_k] in_dtype      v [B,H,d_v] in_dtype
  *     alpha, beta [B,H] fp32
  *     codes     [B,H,d_v,d_k] int8      scales [B,H,d_v] fp32   (in/out)
- *     buf_k     [B,H,W,d_k] fp32        buf_v [B,H,W,d_v] fp32  (in/out)
+ *     buf_k     [B,H,W,d_k]             buf_v [B,H,W,d_v]       (in/out)
+ *               fp32, or bf16 under GDNQ_FLAG_BUF_BF16
  *     buf_alpha, buf_beta [B,H,W] fp32                           (in/out)
  *     fill_in   [B] int32 in [0, W-1]   fill_out [B] int32 (written)
  *     o         [B,H,d_v] out_dtype (written)
@@ -140,7 +150,7 @@ typedef struct {
 
 gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const void* k,
                              const void* v, const float* alpha, const float* beta,
-                             int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                             int8_t* codes, float* scales, void* buf_k, void* buf_v,
                              float* buf_alpha, float* buf_beta, const int32_t* fill_in,
                              int32_t* fill_out, void* o, void* stream);
 

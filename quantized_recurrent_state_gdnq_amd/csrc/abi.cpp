@@ -105,7 +105,7 @@ gdnq_status gdnq_quantize_state(const float* S, int64_t rows, int32_t d_k, int8_
 
 gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const void* k,
                              const void* v, const float* alpha, const float* beta,
-                             int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                             int8_t* codes, float* scales, void* buf_k, void* buf_v,
                              float* buf_alpha, float* buf_beta, const int32_t* fill_in,
                              int32_t* fill_out, void* o, void* stream) {
   if (!p) return fail(GDNQ_ERR_NULL, "params is NULL");
@@ -117,8 +117,9 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
   if ((p->in_dtype != GDNQ_F32 && p->in_dtype != GDNQ_BF16) ||
       (p->out_dtype != GDNQ_F32 && p->out_dtype != GDNQ_BF16))
     return fail(GDNQ_ERR_DTYPE, "in_dtype = %d, out_dtype = %d", p->in_dtype, p->out_dtype);
-  if (p->flags & ~uint32_t(GDNQ_FLAG_WHT))
-    return fail(GDNQ_ERR_FLAGS, "flags 0x%x: decode accepts only GDNQ_FLAG_WHT", p->flags);
+  if (p->flags & ~uint32_t(GDNQ_FLAG_WHT | GDNQ_FLAG_BUF_BF16))
+    return fail(GDNQ_ERR_FLAGS, "flags 0x%x: decode accepts GDNQ_FLAG_WHT and GDNQ_FLAG_BUF_BF16", p->flags);
+  const bool buf_bf16 = (p->flags & GDNQ_FLAG_BUF_BF16) != 0;
   if (B > gdnq::decode_max_batch())
     return fail(GDNQ_ERR_SHAPE, "batch = %d, at most %d sequences per call", B, gdnq::decode_max_batch());
   if (int64_t(B) * H * gdnq::decode_row_split() > 0x7fffffffLL)
@@ -132,8 +133,8 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
                      {"beta", beta, bh * 4},
                      {"codes", codes, bh * dv * dk},
                      {"scales", scales, bh * dv * 4},
-                     {"buf_k", buf_k, bh * W * dk * 4},
-                     {"buf_v", buf_v, bh * W * dv * 4},
+                     {"buf_k", buf_k, bh * W * dk * (buf_bf16 ? 2 : 4)},
+                     {"buf_v", buf_v, bh * W * dv * (buf_bf16 ? 2 : 4)},
                      {"buf_alpha", buf_alpha, bh * W * 4},
                      {"buf_beta", buf_beta, bh * W * 4},
                      {"fill_in", fill_in, size_t(B) * 4},
@@ -152,7 +153,7 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
   gdnq::DecodeLaunch L{q,        k,        v,       alpha, beta, codes, scales, buf_k,
                        buf_v,    buf_alpha, buf_beta, fill_in, fill_out, o,   B,      H,
                        dk,       dv,       W,       p->in_dtype == GDNQ_BF16,
-                       p->out_dtype == GDNQ_BF16, (p->flags & GDNQ_FLAG_WHT) != 0};
+                       p->out_dtype == GDNQ_BF16, (p->flags & GDNQ_FLAG_WHT) != 0, buf_bf16};
   return hip_status(gdnq::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch");
 }
 

@@ -39,6 +39,9 @@ constexpr int PH = 16;           // buffer slots staged in LDS per phase
 #ifndef DEC_QUEUE
 #define DEC_QUEUE 12
 #endif
+#ifndef DEC_QUEUE_BF16
+#define DEC_QUEUE_BF16 24  // bf16 window buffer: half the queue registers per slot
+#endif
 
 struct DecodeArgs {
   const void* q;
@@ -48,8 +51,8 @@ struct DecodeArgs {
   const float* beta;
   int8_t* codes;
   float* scales;
-  float* buf_k;
-  float* buf_v;
+  void* buf_k;  // fp32, or bf16 (BB)
+  void* buf_v;
   float* buf_alpha;
   float* buf_beta;
   const int32_t* fill_in;
@@ -253,12 +256,15 @@ __device__ __forceinline__ JobId job_id(const JobList& L, int job) {
 // reads each buffered key and value straight from memory through a P-deep
 // register queue (bounded buffer loads: slots past the fill cost nothing)
 // and accumulates c_j v_j as it goes; the int8 rows are loaded while it runs.
-template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT>
+template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT, bool BB>
 __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, int lane, float* wy) {
   constexpr int EK = DK / 64;    // key / query elements per lane
   constexpr int RPL = DV / 64;   // state rows per lane
   constexpr int CPR = DK / 16;   // 16-code chunks per row
-  constexpr int P = DEC_QUEUE;   // queue depth (sweep steps loaded ahead)
+  constexpr int EB = BB ? 2 : 4;                 // bytes per buffered element
+  constexpr int KWD = BB ? (EK + 1) / 2 : EK;    // queue words per buffered key (per lane)
+  constexpr int VWD = BB ? (RPL + 1) / 2 : RPL;  // and per buffered value
+  constexpr int P = BB ? DEC_QUEUE_BF16 : DEC_QUEUE;  // queue depth (sweep steps loaded ahead)
   constexpr int CODE_LEAD = DEC_CODE_LEAD;
   const int W = a.W;
   const int f = J.f;
@@ -266,31 +272,48 @@ __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, i
   const size_t qk_base = size_t(bh) * DK;
   const size_t v_base = size_t(bh) * DV;
   const size_t bufs_base = size_t(bh) * W;
-  const rsrc_t rk = make_rsrc(a.buf_k + size_t(bh) * W * DK, uint32_t(f) * DK * 4);
-  const rsrc_t rv = make_rsrc(a.buf_v + size_t(bh) * W * DV, uint32_t(f) * DV * 4);
-  const uint32_t ko = uint32_t(lane) * EK * 4, vo = uint32_t(lane) * RPL * 4;
-  auto load_k = [&](int j, float (&x)[EK]) {  // j < 0 lands past the bound: reads 0, no traffic
-    const uint32_t so = uint32_t(j) * DK * 4;
-    if constexpr (EK == 2) {
-      const uint2 w = bload_u2s(rk, ko, so);
-      x[0] = __uint_as_float(w.x);
-      x[1] = __uint_as_float(w.y);
+  const rsrc_t rk = make_rsrc(static_cast<const char*>(a.buf_k) + size_t(bh) * W * DK * EB, uint32_t(f) * DK * EB);
+  const rsrc_t rv = make_rsrc(static_cast<const char*>(a.buf_v) + size_t(bh) * W * DV * EB, uint32_t(f) * DV * EB);
+  const uint32_t ko = uint32_t(lane) * EK * EB, vo = uint32_t(lane) * RPL * EB;
+  // raw words of a buffered key / value (fp32 bits, or packed bf16): the
+  // queue holds these and they are widened at the step that consumes them
+  auto load_raw = [&](const rsrc_t& r, uint32_t o, uint32_t so, int n, uint32_t* x) __attribute__((always_inline)) {
+    if (!BB && n == 2) {
+      const uint2 w = bload_u2s(r, o, so);
+      x[0] = w.x;
+      x[1] = w.y;
+    } else if (!BB || n == 2) {
+      x[0] = __float_as_uint(bload_f1s(r, o, so));
     } else {
-      x[0] = bload_f1s(rk, ko, so);
+      x[0] = bload_h1s(r, o, so);
     }
   };
-  auto load_v = [&](int j, float (&x)[RPL]) {
-    const uint32_t so = uint32_t(j) * DV * 4;
-    if constexpr (RPL == 2) {
-      const uint2 w = bload_u2s(rv, vo, so);
-      x[0] = __uint_as_float(w.x);
-      x[1] = __uint_as_float(w.y);
+  auto load_k = [&](int j, uint32_t (&x)[KWD]) {  // j < 0 lands past the bound: reads 0, no traffic
+    load_raw(rk, ko, uint32_t(j) * DK * EB, EK, x);
+  };
+  auto load_v = [&](int j, uint32_t (&x)[VWD]) {
+    load_raw(rv, vo, uint32_t(j) * DV * EB, RPL, x);
+  };
+  auto widen_k = [&](const uint32_t (&x)[KWD], float (&y)[EK]) __attribute__((always_inline)) {
+    if constexpr (!BB) {
+#pragma unroll
+      for (int e = 0; e < EK; ++e) y[e] = __uint_as_float(x[e]);
     } else {
-      x[0] = bload_f1s(rv, vo, so);
+      y[0] = bf16_lo(x[0]);
+      if constexpr (EK == 2) y[1] = bf16_hi(x[0]);
+    }
+  };
+  auto widen_v = [&](const uint32_t (&x)[VWD], float (&y)[RPL]) __attribute__((always_inline)) {
+    if constexpr (!BB) {
+#pragma unroll
+      for (int e = 0; e < RPL; ++e) y[e] = __uint_as_float(x[e]);
+    } else {
+      y[0] = bf16_lo(x[0]);
+      if constexpr (RPL == 2) y[1] = bf16_hi(x[0]);
     }
   };
   // queue first (oldest loads): the first sweep steps wait for nothing else
-  float kq[P][EK], vq[P][RPL];
+  uint32_t kq[P][KWD], vq[P][VWD];
 #pragma unroll
   for (int u = 0; u < P; ++u) {
     load_k(f - 1 - u, kq[u]);
@@ -347,11 +370,14 @@ __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, i
   // one sweep step on queue slot u (write j): the slot is copied out first so
   // that its registers can take the load of write j - P at once
   auto step = [&](int u, int j, bool refill) {
+    uint32_t kw[KWD], vw[VWD];
+#pragma unroll
+    for (int e = 0; e < KWD; ++e) asm volatile("v_mov_b32 %0, %1" : "=v"(kw[e]) : "v"(kq[u][e]));
+#pragma unroll
+    for (int i = 0; i < VWD; ++i) asm volatile("v_mov_b32 %0, %1" : "=v"(vw[i]) : "v"(vq[u][i]));
     float kj[EK], vj[RPL];
-#pragma unroll
-    for (int e = 0; e < EK; ++e) asm volatile("v_mov_b32 %0, %1" : "=v"(kj[e]) : "v"(kq[u][e]));
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) asm volatile("v_mov_b32 %0, %1" : "=v"(vj[i]) : "v"(vq[u][i]));
+    widen_k(kw, kj);
+    widen_v(vw, vj);
     if (refill) {
       load_k(j - P, kq[u]);
       load_v(j - P, vq[u]);
@@ -372,17 +398,22 @@ __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, i
   // overlapped reductions), bt_a = beta_j d_a and
   // bt_b = beta_{j-1} (k_{j-1} . (yt - bt_a k_j)) = beta_{j-1} (d_b - bt_a g)
   auto step2 = [&](int u, int j, bool refill) {
+    uint32_t kwa[KWD], kwb[KWD], vwa[VWD], vwb[VWD];
+#pragma unroll
+    for (int e = 0; e < KWD; ++e) {
+      asm volatile("v_mov_b32 %0, %1" : "=v"(kwa[e]) : "v"(kq[u][e]));
+      asm volatile("v_mov_b32 %0, %1" : "=v"(kwb[e]) : "v"(kq[u + 1][e]));
+    }
+#pragma unroll
+    for (int i = 0; i < VWD; ++i) {
+      asm volatile("v_mov_b32 %0, %1" : "=v"(vwa[i]) : "v"(vq[u][i]));
+      asm volatile("v_mov_b32 %0, %1" : "=v"(vwb[i]) : "v"(vq[u + 1][i]));
+    }
     float ka[EK], kb[EK], va[RPL], vb[RPL];
-#pragma unroll
-    for (int e = 0; e < EK; ++e) {
-      asm volatile("v_mov_b32 %0, %1" : "=v"(ka[e]) : "v"(kq[u][e]));
-      asm volatile("v_mov_b32 %0, %1" : "=v"(kb[e]) : "v"(kq[u + 1][e]));
-    }
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      asm volatile("v_mov_b32 %0, %1" : "=v"(va[i]) : "v"(vq[u][i]));
-      asm volatile("v_mov_b32 %0, %1" : "=v"(vb[i]) : "v"(vq[u + 1][i]));
-    }
+    widen_k(kwa, ka);
+    widen_k(kwb, kb);
+    widen_v(vwa, va);
+    widen_v(vwb, vb);
     if (refill) {
       load_k(j - P, kq[u]);
       load_v(j - P, vq[u]);
@@ -461,11 +492,28 @@ __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, i
   for (int i = 0; i < RPL; ++i) {
     const int row = lane * RPL + i;
     store_out<OUT_BF16>(a.o, v_base + row, srow[i] * d[i] + acc[i]);
-    a.buf_v[(bufs_base + f) * DV + row] = vcur[i];  // append v
   }
-  float* dk = a.buf_k + (bufs_base + f) * DK + lane * EK;  // append k (rotated basis under WHT)
+  // append v and k (k in the rotated basis under WHT); a bf16 buffer keeps
+  // them rounded to nearest even
+  if constexpr (BB) {
+    uint16_t* bv = static_cast<uint16_t*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
+    uint16_t* bk = static_cast<uint16_t*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
+    if constexpr (RPL == 2)
+      *reinterpret_cast<uint32_t*>(bv) = f32_to_bf16_bits(vcur[0]) | (f32_to_bf16_bits(vcur[1]) << 16);
+    else
+      bv[0] = uint16_t(f32_to_bf16_bits(vcur[0]));
+    if constexpr (EK == 2)
+      *reinterpret_cast<uint32_t*>(bk) = f32_to_bf16_bits(kv[0]) | (f32_to_bf16_bits(kv[1]) << 16);
+    else
+      bk[0] = uint16_t(f32_to_bf16_bits(kv[0]));
+  } else {
+    float* bv = static_cast<float*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
+    float* bk = static_cast<float*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
 #pragma unroll
-  for (int e = 0; e < EK; ++e) dk[e] = kv[e];
+    for (int i = 0; i < RPL; ++i) bv[i] = vcur[i];
+#pragma unroll
+    for (int e = 0; e < EK; ++e) bk[e] = kv[e];
+  }
   if (lane == 0) {
     a.buf_alpha[bufs_base + f] = alpha_t;
     a.buf_beta[bufs_base + f] = beta_t;
@@ -474,7 +522,7 @@ __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, i
   __builtin_amdgcn_wave_barrier();  // the next head reuses wy
 }
 
-template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT>
+template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT, bool BB>
 __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
   using S = DecShape<DK, DV>;
   constexpr int NT = S::NT;
@@ -551,20 +599,30 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
     RawVec<IN_BF16, S::EK> qraw, kraw;
     load_raw_vec<IN_BF16, S::EK>(a.q, qk_base + lane * S::EK, qraw);
     load_raw_vec<IN_BF16, S::EK>(a.k, qk_base + lane * S::EK, kraw);
-    const rsrc_t rk = make_rsrc(a.buf_k + size_t(bh) * W * DK, uint32_t(f) * DK * 4);
+    constexpr int EB = BB ? 2 : 4;  // bytes per buffered element
+    const rsrc_t rk = make_rsrc(static_cast<const char*>(a.buf_k) + size_t(bh) * W * DK * EB, uint32_t(f) * DK * EB);
+    // four consecutive buffered elements at element offset e0 (+ e1 scalar)
+    auto load4 = [&](const rsrc_t& r, uint32_t e0, uint32_t e1) __attribute__((always_inline)) {
+      if constexpr (BB) {
+        const uint2 w = bload_u2s(r, e0 * 2, e1 * 2);
+        return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+      } else {
+        return bload_f4(r, e0 * 4, e1 * 4);
+      }
+    };
     float4 kt[S::KREG];
 #pragma unroll
-    for (int i = 0; i < S::KREG; ++i) kt[i] = bload_f4(rk, uint32_t(tid) * 16, uint32_t(i * NT * 16));
+    for (int i = 0; i < S::KREG; ++i) kt[i] = load4(rk, uint32_t(tid) * 4, uint32_t(i * NT * 4));
     const float a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
     const float b_slot = bload_f1(make_rsrc(a.buf_beta + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
     const uint4 cwr = *reinterpret_cast<const uint4*>(a.codes + (v_base + row) * DK + seg * 16);
     const float srow = a.scales[v_base + row];
-    const rsrc_t rv = make_rsrc(a.buf_v + size_t(bh) * W * DV, uint32_t(W - 1) * DV * 4);
+    const rsrc_t rv = make_rsrc(static_cast<const char*>(a.buf_v) + size_t(bh) * W * DV * EB, uint32_t(W - 1) * DV * EB);
     float4 vt[S::CVREG];
 #pragma unroll
     for (int i = 0; i < S::CVREG; ++i)  // slot (tid + NT*i) / CVF4, rows 4*((tid + NT*i) % CVF4)
-      vt[i] = bload_f4(rv, uint32_t((tid / S::CVF4) * DV + (tid % S::CVF4) * 4) * 4,
-                       uint32_t(((i * NT / S::CVF4) * DV + J.rb * S::CR) * 4));
+      vt[i] = load4(rv, uint32_t((tid / S::CVF4) * DV + (tid % S::CVF4) * 4),
+                    uint32_t((i * NT / S::CVF4) * DV + J.rb * S::CR));
     uint32_t vcur_raw = 0;
     if (tid < S::CR) vcur_raw = load_raw<IN_BF16>(a.v, v_base + J.rb * S::CR + tid);
 
@@ -678,7 +736,7 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
     float* wy = y_lds + wave * DK;
     for (int o = slot; o < n_open; o += G * (NT / 64)) {
       const JobId J = job_id(L, L.n_close_jobs + o);
-      open_head<DK, DV, IN_BF16, OUT_BF16, WHT>(a, J, lane, wy);
+      open_head<DK, DV, IN_BF16, OUT_BF16, WHT, BB>(a, J, lane, wy);
     }
   }
 }
@@ -697,32 +755,37 @@ static unsigned decode_grid(int B, int H, int rc) {
   return unsigned(jobs_max < g ? jobs_max : g);
 }
 
-template <int DK, int DV, bool IB, bool OB, bool WHT>
+template <int DK, int DV, bool IB, bool OB, bool WHT, bool BB>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   const unsigned grid = decode_grid(a.B, a.H, DecShape<DK, DV>::RC);
   const size_t lds = size_t(a.W) * DK * sizeof(float);  // buffered keys
-  hipLaunchKernelGGL((decode_kernel<DK, DV, IB, OB, WHT>), dim3(grid), dim3(DEC_THREADS), lds, s, a);
+  hipLaunchKernelGGL((decode_kernel<DK, DV, IB, OB, WHT, BB>), dim3(grid), dim3(DEC_THREADS), lds, s, a);
   return hipGetLastError();
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool BB>
 static hipError_t launch_dkdv(const DecodeArgs& a, bool ib, bool ob, bool wht, hipStream_t s) {
   if (ib) {
-    if (ob) return wht ? launch_t<DK, DV, true, true, true>(a, s) : launch_t<DK, DV, true, true, false>(a, s);
-    return wht ? launch_t<DK, DV, true, false, true>(a, s) : launch_t<DK, DV, true, false, false>(a, s);
+    if (ob) return wht ? launch_t<DK, DV, true, true, true, BB>(a, s) : launch_t<DK, DV, true, true, false, BB>(a, s);
+    return wht ? launch_t<DK, DV, true, false, true, BB>(a, s) : launch_t<DK, DV, true, false, false, BB>(a, s);
   }
-  if (ob) return wht ? launch_t<DK, DV, false, true, true>(a, s) : launch_t<DK, DV, false, true, false>(a, s);
-  return wht ? launch_t<DK, DV, false, false, true>(a, s) : launch_t<DK, DV, false, false, false>(a, s);
+  if (ob) return wht ? launch_t<DK, DV, false, true, true, BB>(a, s) : launch_t<DK, DV, false, true, false, BB>(a, s);
+  return wht ? launch_t<DK, DV, false, false, true, BB>(a, s) : launch_t<DK, DV, false, false, false, BB>(a, s);
+}
+
+template <bool BB>
+static hipError_t launch_bb(const DecodeLaunch& L, const DecodeArgs& a, hipStream_t stream) {
+  if (L.d_k == 128 && L.d_v == 128) return launch_dkdv<128, 128, BB>(a, L.in_bf16, L.out_bf16, L.wht, stream);
+  if (L.d_k == 128 && L.d_v == 64) return launch_dkdv<128, 64, BB>(a, L.in_bf16, L.out_bf16, L.wht, stream);
+  if (L.d_k == 64 && L.d_v == 128) return launch_dkdv<64, 128, BB>(a, L.in_bf16, L.out_bf16, L.wht, stream);
+  return launch_dkdv<64, 64, BB>(a, L.in_bf16, L.out_bf16, L.wht, stream);
 }
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   DecodeArgs a{L.q,        L.k,        L.v,       L.alpha,   L.beta,   L.codes, L.scales, L.buf_k,
                L.buf_v,    L.buf_alpha, L.buf_beta, L.fill_in, L.fill_out, L.o,   L.B,      L.H,
                L.W};
-  if (L.d_k == 128 && L.d_v == 128) return launch_dkdv<128, 128>(a, L.in_bf16, L.out_bf16, L.wht, stream);
-  if (L.d_k == 128 && L.d_v == 64) return launch_dkdv<128, 64>(a, L.in_bf16, L.out_bf16, L.wht, stream);
-  if (L.d_k == 64 && L.d_v == 128) return launch_dkdv<64, 128>(a, L.in_bf16, L.out_bf16, L.wht, stream);
-  return launch_dkdv<64, 64>(a, L.in_bf16, L.out_bf16, L.wht, stream);
+  return L.buf_bf16 ? launch_bb<true>(L, a, stream) : launch_bb<false>(L, a, stream);
 }
 
 }  // namespace gdnq

@@ -254,6 +254,9 @@ __device__ __forceinline__ uint2 bload_u2s(rsrc_t r, uint32_t off, uint32_t soff
 __device__ __forceinline__ float bload_f1s(rsrc_t r, uint32_t off, uint32_t soff) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
 }
+__device__ __forceinline__ uint32_t bload_h1s(rsrc_t r, uint32_t off, uint32_t soff) {  // 16 bits, zero-extended
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
+}
 
 // XCD-aware workgroup id: workgroups are dispatched round-robin over the 8
 // XCDs, so block x runs on XCD x % 8.  This remaps ids so that consecutive

@@ -26,15 +26,15 @@ struct DecodeLaunch {
   const float* beta;
   int8_t* codes;
   float* scales;
-  float* buf_k;
-  float* buf_v;
+  void* buf_k;    // fp32, or bf16 with buf_bf16
+  void* buf_v;
   float* buf_alpha;
   float* buf_beta;
   const int32_t* fill_in;
   int32_t* fill_out;
   void* o;
   int B, H, d_k, d_v, W;
-  bool in_bf16, out_bf16, wht;
+  bool in_bf16, out_bf16, wht, buf_bf16;
 };
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 int decode_row_split();

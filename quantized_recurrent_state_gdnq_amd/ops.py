@@ -63,7 +63,8 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
 
     q, k [B,H,d_k], v [B,H,d_v] (fp32 or bf16); alpha, beta [B,H] fp32;
     codes [B,H,d_v,d_k] int8 and scales [B,H,d_v] fp32 (updated in place for
-    sequences whose window closes); buf_k [B,H,W,d_k], buf_v [B,H,W,d_v],
+    sequences whose window closes); buf_k [B,H,W,d_k], buf_v [B,H,W,d_v]
+    (both fp32, or both bf16 for the low-precision window buffer),
     buf_alpha, buf_beta [B,H,W] fp32 (slot fill_in[b] receives the write);
     fill_in, fill_out [B] int32 (distinct).  Returns o [B,H,d_v].
     """
@@ -73,9 +74,14 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
     W = buf_k.shape[2]
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype, dev)
-    for name, t in (("alpha", alpha), ("beta", beta), ("scales", scales), ("buf_k", buf_k),
-                    ("buf_v", buf_v), ("buf_alpha", buf_alpha), ("buf_beta", buf_beta)):
+    for name, t in (("alpha", alpha), ("beta", beta), ("scales", scales),
+                    ("buf_alpha", buf_alpha), ("buf_beta", buf_beta)):
         _need(t, name, torch.float32, dev)
+    if buf_k.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("buf_k must be float32 or bfloat16")
+    _need(buf_k, "buf_k", buf_k.dtype, dev)
+    _need(buf_v, "buf_v", buf_k.dtype, dev)
+    buf_bf16 = buf_k.dtype == torch.bfloat16
     _need(codes, "codes", torch.int8, dev)
     _need(fill_in, "fill_in", torch.int32, dev)
     _need(fill_out, "fill_out", torch.int32, dev)
@@ -94,7 +100,7 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
             or fill_in.numel() != B or fill_out.numel() != B or tuple(o.shape) != (B, H, d_v)):
         raise ValueError("inconsistent decode shapes")
     p = _lib.DecodeParams(B, H, d_k, d_v, W, _DT[q.dtype], _DT[o.dtype],
-                          _lib.GDNQ_FLAG_WHT if wht else 0)
+                          (_lib.GDNQ_FLAG_WHT if wht else 0) | (_lib.GDNQ_FLAG_BUF_BF16 if buf_bf16 else 0))
     args = (p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(codes), _ptr(scales),
             _ptr(buf_k), _ptr(buf_v), _ptr(buf_alpha), _ptr(buf_beta), _ptr(fill_in), _ptr(fill_out),
             _ptr(o), _stream(dev))
@@ -177,12 +183,14 @@ class DecodeState:
     the window buffer and the fill counters (ping-ponged between two arrays,
     since every head of a sequence reads the fill while the step runs)."""
 
-    def __init__(self, codes, scales, window, fill=None, wht=False):
+    def __init__(self, codes, scales, window, fill=None, wht=False, buf_dtype=torch.float32):
+        """buf_dtype: torch.float32 (the method's fp32 window buffer) or
+        torch.bfloat16 (the low-precision buffer: writes stored rounded)."""
         B, H, d_v, d_k = codes.shape
         dev = codes.device
         self.codes, self.scales, self.window, self.wht = codes, scales, window, wht
-        self.buf_k = torch.empty((B, H, window, d_k), dtype=torch.float32, device=dev)
-        self.buf_v = torch.empty((B, H, window, d_v), dtype=torch.float32, device=dev)
+        self.buf_k = torch.empty((B, H, window, d_k), dtype=buf_dtype, device=dev)
+        self.buf_v = torch.empty((B, H, window, d_v), dtype=buf_dtype, device=dev)
         self.buf_alpha = torch.empty((B, H, window), dtype=torch.float32, device=dev)
         self.buf_beta = torch.empty((B, H, window), dtype=torch.float32, device=dev)
         self.fill = torch.zeros(B, dtype=torch.int32, device=dev) if fill is None else fill
