@@ -32,12 +32,11 @@ namespace gdnq {
 
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_MAXB = 1024;   // sequences per call (fill scan results in LDS)
-constexpr int PH = 16;           // buffer slots staged in LDS per phase
 #ifndef DEC_CODE_LEAD
-#define DEC_CODE_LEAD 2
+#define DEC_CODE_LEAD 1
 #endif
 #ifndef DEC_QUEUE
-#define DEC_QUEUE 12
+#define DEC_QUEUE 14
 #endif
 #ifndef DEC_QUEUE_BF16
 #define DEC_QUEUE_BF16 24  // bf16 window buffer: half the queue registers per slot
@@ -198,14 +197,16 @@ struct DecShape {
   static constexpr int VRG = DV / 4;             // float4 row groups of values
   static constexpr int VNG = NT / VRG;           // slot groups (open job)
   static constexpr int VREG = 64 / VNG;          // value float4 registers (open job)
-  static constexpr int CR = NT / CPR;            // rows per close job
+  static constexpr int CCOL = 8;                 // state columns per thread (close job)
+  static constexpr int CSEG = DK / CCOL;         // threads per state row (close job)
+  static constexpr int CR = NT / CSEG;           // rows per close job
   static constexpr int RC = DV / CR;             // close jobs per head
   static constexpr int CVF4 = CR / 4;            // float4 per slot of a close job's values
   static constexpr int CVREG = (64 * CVF4 + NT - 1) / NT;
   static_assert(NC >= 1 && KREG >= 1 && VREG >= 1 && RC >= 1, "decode tiling");
   // static LDS (floats); the keys [W][DK] live in dynamic LDS
-  static constexpr int XSZ = (VNG * DV > PH * CR) ? VNG * DV : PH * CR;
-  static constexpr int L_X = 0;                   // open: partial sums [VNG][DV]; close: values [PH][CR]
+  static constexpr int XSZ = (VNG * DV > 64 * CR) ? VNG * DV : 64 * CR;
+  static constexpr int L_X = 0;                   // open: partial sums [VNG][DV]; close: values [W][CR]
   static constexpr int L_Y = L_X + XSZ;           // [NT/64][DK] y per wave (open) / q (close)
   static constexpr int L_C = L_Y + (NT / 64) * DK;  // [64] c_j
   static constexpr int L_D = L_C + 64;            // [DV] row dots
@@ -367,6 +368,33 @@ __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, i
   float acc[RPL];
 #pragma unroll
   for (int i = 0; i < RPL; ++i) acc[i] = c_cur * vcur[i];
+  // append v and k (k in the rotated basis under WHT; a bf16 buffer keeps
+  // them rounded to nearest even) now, so that neither stays live through the
+  // sweep: the sweep never reads slot f (its loads are bounded at f writes)
+  if constexpr (BB) {
+    uint16_t* bv = static_cast<uint16_t*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
+    uint16_t* bk = static_cast<uint16_t*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
+    if constexpr (RPL == 2)
+      *reinterpret_cast<uint32_t*>(bv) = f32_to_bf16_bits(vcur[0]) | (f32_to_bf16_bits(vcur[1]) << 16);
+    else
+      bv[0] = uint16_t(f32_to_bf16_bits(vcur[0]));
+    if constexpr (EK == 2)
+      *reinterpret_cast<uint32_t*>(bk) = f32_to_bf16_bits(kv[0]) | (f32_to_bf16_bits(kv[1]) << 16);
+    else
+      bk[0] = uint16_t(f32_to_bf16_bits(kv[0]));
+  } else {
+    float* bv = static_cast<float*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
+    float* bk = static_cast<float*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) bv[i] = vcur[i];
+#pragma unroll
+    for (int e = 0; e < EK; ++e) bk[e] = kv[e];
+  }
+  if (lane == 0) {
+    a.buf_alpha[bufs_base + f] = alpha_t;
+    a.buf_beta[bufs_base + f] = beta_t;
+    if (J.h == 0) a.fill_out[J.seq] = f + 1;
+  }
   // one sweep step on queue slot u (write j): the slot is copied out first so
   // that its registers can take the load of write j - P at once
   auto step = [&](int u, int j, bool refill) {
@@ -493,32 +521,6 @@ __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, i
     const int row = lane * RPL + i;
     store_out<OUT_BF16>(a.o, v_base + row, srow[i] * d[i] + acc[i]);
   }
-  // append v and k (k in the rotated basis under WHT); a bf16 buffer keeps
-  // them rounded to nearest even
-  if constexpr (BB) {
-    uint16_t* bv = static_cast<uint16_t*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
-    uint16_t* bk = static_cast<uint16_t*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
-    if constexpr (RPL == 2)
-      *reinterpret_cast<uint32_t*>(bv) = f32_to_bf16_bits(vcur[0]) | (f32_to_bf16_bits(vcur[1]) << 16);
-    else
-      bv[0] = uint16_t(f32_to_bf16_bits(vcur[0]));
-    if constexpr (EK == 2)
-      *reinterpret_cast<uint32_t*>(bk) = f32_to_bf16_bits(kv[0]) | (f32_to_bf16_bits(kv[1]) << 16);
-    else
-      bk[0] = uint16_t(f32_to_bf16_bits(kv[0]));
-  } else {
-    float* bv = static_cast<float*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
-    float* bk = static_cast<float*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) bv[i] = vcur[i];
-#pragma unroll
-    for (int e = 0; e < EK; ++e) bk[e] = kv[e];
-  }
-  if (lane == 0) {
-    a.buf_alpha[bufs_base + f] = alpha_t;
-    a.buf_beta[bufs_base + f] = beta_t;
-    if (J.h == 0) a.fill_out[J.seq] = f + 1;
-  }
   __builtin_amdgcn_wave_barrier();  // the next head reuses wy
 }
 
@@ -575,11 +577,12 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
   int job = blockIdx.x;
 
   // ================================================================ close jobs
-  // thread t: row rb*CR + t / CPR, columns [(t % CPR) * 16, +16).  Each row
-  // replays the W writes from its dequantized value.  Carrying u = s / G_j
-  // (G_j = alpha_1 .. alpha_j) turns
-  //   s <- alpha s + beta (v - alpha (s.k)) k
-  // into one FMA per entry:  u <- u + (beta (v - alpha G_{j-1} (u.k)) / G_j) k.
+  // thread t: row rb*CR + t / CSEG, columns [(t % CSEG) * CCOL, +CCOL).  The
+  // window's keys and this job's slice of its values are staged in LDS once;
+  // each row then replays the W writes on its dequantized value in fp32,
+  //   s <- alpha s + beta (v - alpha (s . k)) k,
+  // where alpha s is formed while s . k is reduced, and the next write's key
+  // and value are read from LDS while the current one is applied.
   for (; job < L.n_close_jobs; job += gridDim.x) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));  // keep per-thread offsets from being hoisted out of the loop
@@ -591,8 +594,8 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
     const size_t qk_base = size_t(bh) * DK;
     const size_t v_base = size_t(bh) * DV;
     const size_t bufs_base = size_t(bh) * W;
-    const int rr = tid / S::CPR;
-    const int seg = tid % S::CPR;
+    const int rr = tid / S::CSEG;
+    const int seg = tid % S::CSEG;
     const int row = J.rb * S::CR + rr;
     const float alpha_t = a.alpha[bh];
     const float beta_t = a.beta[bh];
@@ -613,11 +616,12 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
     float4 kt[S::KREG];
 #pragma unroll
     for (int i = 0; i < S::KREG; ++i) kt[i] = load4(rk, uint32_t(tid) * 4, uint32_t(i * NT * 4));
-    const float a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
-    const float b_slot = bload_f1(make_rsrc(a.buf_beta + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
-    const uint4 cwr = *reinterpret_cast<const uint4*>(a.codes + (v_base + row) * DK + seg * 16);
+    // lane j: alpha_j, beta_j of write j; the current token's in lane W - 1
+    float a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
+    float b_slot = bload_f1(make_rsrc(a.buf_beta + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
+    const uint2 cwr = *reinterpret_cast<const uint2*>(a.codes + (v_base + row) * DK + seg * S::CCOL);
     const float srow = a.scales[v_base + row];
-    const rsrc_t rv = make_rsrc(static_cast<const char*>(a.buf_v) + size_t(bh) * W * DV * EB, uint32_t(W - 1) * DV * EB);
+    const rsrc_t rv = make_rsrc(static_cast<const char*>(a.buf_v) + size_t(bh) * W * DV * EB, uint32_t(f) * DV * EB);
     float4 vt[S::CVREG];
 #pragma unroll
     for (int i = 0; i < S::CVREG; ++i)  // slot (tid + NT*i) / CVF4, rows 4*((tid + NT*i) % CVF4)
@@ -635,6 +639,16 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
       if (idx < f * S::KF4) reinterpret_cast<float4*>(k_lds)[idx] = kt[i];
       consume(kt[i]);
     }
+#pragma unroll
+    for (int i = 0; i < S::CVREG; ++i) {
+      const int idx = tid + i * NT;
+      if (idx / S::CVF4 < f) reinterpret_cast<float4*>(x_lds)[idx] = vt[i];
+    }
+    if (tid < S::CR) x_lds[f * S::CR + tid] = raw_to_f32<IN_BF16>(vcur_raw);
+    if (lane == f) {
+      a_slot = alpha_t;
+      b_slot = beta_t;
+    }
     if constexpr (WHT) {
       fwht_group<S::EK, 64>(qv, lane);
       fwht_group<S::EK, 64>(kv, lane);
@@ -642,77 +656,71 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
     if (wave == 0) {  // the current token's key is the window's last write; q for the output
 #pragma unroll
       for (int e = 0; e < S::EK; ++e) {
-        k_lds[(W - 1) * DK + lane * S::EK + e] = kv[e];
+        k_lds[f * DK + lane * S::EK + e] = kv[e];
         y_lds[lane * S::EK + e] = qv[e];
       }
     }
-    float u[16];
+    constexpr int CC = S::CCOL;
+    float sv[CC];
     {
-      const uint32_t w[4] = {cwr.x, cwr.y, cwr.z, cwr.w};
+      const uint32_t w[2] = {cwr.x, cwr.y};
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) u[4 * q4 + c] = i8_at(w[q4], c) * srow;
+        for (int c = 0; c < 4; ++c) sv[4 * h + c] = i8_at(w[h], c) * srow;
     }
-    const float vcur = raw_to_f32<IN_BF16>(vcur_raw);
-    float G = 1.f;
+    __syncthreads();  // keys and values staged
+    auto read_kv = [&](int j, float (&kk)[CC], float& vv) __attribute__((always_inline)) {
+      const float4* k4 = reinterpret_cast<const float4*>(k_lds + j * DK + seg * CC);
 #pragma unroll
-    for (int ph = 0; ph < 64 / PH; ++ph) {
-      if (ph * PH < W) {  // uniform
-        __syncthreads();  // keys staged / previous phase's values consumed
-#pragma unroll
-        for (int i = 0; i < S::CVREG; ++i) {
-          const int idx = tid + i * NT;
-          const int slot = idx / S::CVF4;
-          if (slot >= ph * PH && slot < ph * PH + PH && slot < W - 1)
-            reinterpret_cast<float4*>(x_lds)[idx - ph * PH * S::CVF4] = vt[i];
-        }
-        if (W - 1 >= ph * PH && W - 1 < ph * PH + PH && tid < S::CR)
-          x_lds[(W - 1 - ph * PH) * S::CR + tid] = vcur;
-        __syncthreads();
-        const int jhi = min(W, ph * PH + PH);
-        for (int j = ph * PH; j < jhi; ++j) {
-          float kj[16];
-          const float4* k4 = reinterpret_cast<const float4*>(k_lds + j * DK + seg * 16);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float4 x = k4[e];
-            kj[4 * e] = x.x;
-            kj[4 * e + 1] = x.y;
-            kj[4 * e + 2] = x.z;
-            kj[4 * e + 3] = x.w;
-          }
-          const float aj = (j == W - 1) ? alpha_t : lane_value(a_slot, j);
-          const float bj = (j == W - 1) ? beta_t : lane_value(b_slot, j);
-          const float vj = x_lds[(j - ph * PH) * S::CR + rr];
-          float p = 0.f;
-#pragma unroll
-          for (int c = 0; c < 16; ++c) p += u[c] * kj[c];
-          const float sk = G * group_sum<S::CPR>(p);  // s . k_j
-          const float Gn = G * aj;
-          const float coef = __fdividef(bj * (vj - aj * sk), Gn);
-#pragma unroll
-          for (int c = 0; c < 16; ++c) u[c] = fmaf(coef, kj[c], u[c]);
-          G = Gn;
-        }
+      for (int e = 0; e < CC / 4; ++e) {
+        const float4 x = k4[e];
+        kk[4 * e] = x.x;
+        kk[4 * e + 1] = x.y;
+        kk[4 * e + 2] = x.z;
+        kk[4 * e + 3] = x.w;
       }
+      vv = x_lds[j * S::CR + rr];
+    };
+    auto apply = [&](int j, const float (&kk)[CC], float vv) __attribute__((always_inline)) {
+      const float aj = lane_value(a_slot, j);
+      const float bj = lane_value(b_slot, j);
+      float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+      for (int c = 0; c < CC; c += 2) {
+        p0 = fmaf(sv[c], kk[c], p0);
+        p1 = fmaf(sv[c + 1], kk[c + 1], p1);
+      }
+      const float sk = group_sum<S::CSEG>(p0 + p1);  // s . k_j
+      const float coef = bj * fmaf(-aj, sk, vv);
+#pragma unroll
+      for (int c = 0; c < CC; ++c) sv[c] = fmaf(coef, kk[c], aj * sv[c]);
+    };
+    {
+      float ka[CC], kb[CC], va, vb;
+      read_kv(0, ka, va);
+      int j = 0;
+      for (; j + 2 <= W; j += 2) {  // the look-ahead reads are clamped into the window
+        read_kv(j + 1, kb, vb);
+        apply(j, ka, va);
+        read_kv(min(j + 2, W - 1), ka, va);
+        apply(j + 1, kb, vb);
+      }
+      if (j < W) apply(j, ka, va);
     }
     float po = 0.f, amax = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      u[c] *= G;  // back to the state s
-      po += u[c] * y_lds[seg * 16 + c];
-      amax = fmaxf(amax, fabsf(u[c]));
+    for (int c = 0; c < CC; ++c) {
+      po += sv[c] * y_lds[seg * CC + c];
+      amax = fmaxf(amax, fabsf(sv[c]));
     }
-    po = group_sum<S::CPR>(po);
-    amax = group_max<S::CPR>(amax);
+    po = group_sum<S::CSEG>(po);
+    amax = group_max<S::CSEG>(amax);
     const float scale = codec_scale(amax);
-    uint4 wout;
-    wout.x = pack4_i8(codec_code(u[0], scale), codec_code(u[1], scale), codec_code(u[2], scale), codec_code(u[3], scale));
-    wout.y = pack4_i8(codec_code(u[4], scale), codec_code(u[5], scale), codec_code(u[6], scale), codec_code(u[7], scale));
-    wout.z = pack4_i8(codec_code(u[8], scale), codec_code(u[9], scale), codec_code(u[10], scale), codec_code(u[11], scale));
-    wout.w = pack4_i8(codec_code(u[12], scale), codec_code(u[13], scale), codec_code(u[14], scale), codec_code(u[15], scale));
-    *reinterpret_cast<uint4*>(a.codes + (v_base + row) * DK + seg * 16) = wout;
+    uint2 wout;
+    wout.x = pack4_i8(codec_code(sv[0], scale), codec_code(sv[1], scale), codec_code(sv[2], scale), codec_code(sv[3], scale));
+    wout.y = pack4_i8(codec_code(sv[4], scale), codec_code(sv[5], scale), codec_code(sv[6], scale), codec_code(sv[7], scale));
+    *reinterpret_cast<uint2*>(a.codes + (v_base + row) * DK + seg * CC) = wout;
     if (seg == 0) {
       a.scales[v_base + row] = scale;
       store_out<OUT_BF16>(a.o, v_base + row, po);
@@ -741,7 +749,7 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
   }
 }
 
-int decode_row_split() { return 4; }  // close jobs per head at most (grid validation)
+int decode_row_split() { return 8; }  // close jobs per head at most (grid validation)
 int decode_max_batch() { return DEC_MAXB; }
 // Persistent grid: three resident workgroups per CU on 256 CUs, never
 // more workgroups than jobs.  GDNQ_DECODE_GRID overrides it (tuning).

@@ -158,6 +158,22 @@ def test_decode_batch64_heads32_window64():
     print(f"B64 H32 decode: max rel err {err:.3e}")
 
 
+@pytest.mark.parametrize("wht", [False, True])
+def test_decode_strong_decay_full_window(wht):
+    """Fast-forgetting heads: decays drawn from U(0.02, 0.2), so the product
+    of a full window's 64 decays (~1e-64) is far below fp32's range.  Closing
+    and open sequences must stay finite and match the oracle."""
+    W = 64
+    d = wl.decode_batch(B=4, H=2, dk=128, dv=128, W=W, seed=77, fill=np.array([63, 63, 40, 10]))
+    g = np.random.default_rng(78)
+    live = ~np.isnan(d["buf_alpha"])
+    d["buf_alpha"] = np.where(live, g.uniform(0.02, 0.2, live.shape), np.nan).astype(np.float32)
+    d["alpha"] = g.uniform(0.02, 0.2, d["alpha"].shape).astype(np.float32)
+    got, codes, scales = _run_decode(d, W, torch.bfloat16, torch.float32, wht)
+    assert np.isfinite(got["o"]).all() and np.isfinite(got["scales"]).all()
+    _check_decode(d, W, got, codes, scales, OUT_TOL_BF16, wht)
+
+
 def test_decode_single_head_fp32_256_steps():
     """Single head, d=64, W=16, fp32 inputs, 256 decode steps from a zero
     state: every output within 1e-3 of the oracle, final state within the
