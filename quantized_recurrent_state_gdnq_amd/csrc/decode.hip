@@ -38,6 +38,12 @@ constexpr int DEC_MAXB = 1024;   // sequences per call (fill scan results in LDS
 #ifndef DEC_QUEUE
 #define DEC_QUEUE 14
 #endif
+#ifndef DEC_WG_PER_CU
+#define DEC_WG_PER_CU 3  // resident workgroups per CU (sets the register budget)
+#endif
+#ifndef DEC_OPEN_WAVES
+#define DEC_OPEN_WAVES 1024
+#endif
 #ifndef DEC_QUEUE_BF16
 #define DEC_QUEUE_BF16 24  // bf16 window buffer: half the queue registers per slot
 #endif
@@ -58,6 +64,7 @@ struct DecodeArgs {
   int32_t* fill_out;
   void* o;
   int B, H, W;
+  int open_waves;  // waves that take open heads (the rest of the grid's waves idle)
 };
 
 template <bool BF16>
@@ -214,11 +221,13 @@ struct DecShape {
 };
 
 // Job list shared by every workgroup: closing sequences first (bit masks and
-// prefix counts per 64 sequences), plus each sequence's fill.
+// prefix counts per 64 sequences), then the open heads, their sequences sorted
+// by fill, longest first; plus each sequence's fill.
 struct JobList {
   uint64_t* cmask;
   int* cpre;
   uint8_t* fills;
+  uint16_t* order;  // open sequences, longest window first
   int B, H, RC, n_close_jobs, n_jobs;
 };
 
@@ -237,28 +246,28 @@ __device__ __forceinline__ JobId job_id(const JobList& L, int job) {
     j.seq = uniform(c * 64 + kth_bit(L.cmask[c], rank - L.cpre[c]));
   } else {
     const int oj = job - L.n_close_jobs;
-    const int rank = oj / L.H;
     j.h = oj % L.H;
     j.rb = 0;
-    int c = 0;
-    while ((c + 1) * 64 - uniform(L.cpre[c + 1]) <= rank) ++c;
-    const uint64_t valid = (c * 64 + 64 <= L.B) ? ~0ull : ((1ull << (L.B - c * 64)) - 1);
-    j.seq = uniform(c * 64 + kth_bit(~L.cmask[c] & valid, rank - (c * 64 - L.cpre[c])));
+    j.seq = uniform(int(L.order[oj / L.H]));
   }
   j.f = uniform(L.fills[j.seq]);
   return j;
 }
 
-// One open head on one wave.  With A_j = alpha_j (I - beta_j k_j k_j^T)
-// (symmetric) the window replay unrolls to
+// The open heads of one wave, one after another.  With A_j = alpha_j (I -
+// beta_j k_j k_j^T) (symmetric) the window replay unrolls to
 //     o = S_0 y_0 + sum_j c_j v_j,   y = q;  for j = t, t-1, ..., 1:
 //     c_j = beta_j (k_j . y),  y <- alpha_j (y - c_j k_j),
 // so the int8 rows are read once and the state is never rebuilt.  The sweep
 // reads each buffered key and value straight from memory through a P-deep
 // register queue (bounded buffer loads: slots past the fill cost nothing)
 // and accumulates c_j v_j as it goes; the int8 rows are loaded while it runs.
+// The wave takes positions slot, 2NW-1-slot, 2NW+slot, ... of the open-head
+// list.  (Issuing the next head's loads before a head's rows . y work was
+// measured slower: the extra in-flight loads only queue behind HBM.)
 template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT, bool BB>
-__device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, int lane, float* wy) {
+__device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L, int slot, int NW, int n_open,
+                                          int lane, float* wy) {
   constexpr int EK = DK / 64;    // key / query elements per lane
   constexpr int RPL = DV / 64;   // state rows per lane
   constexpr int CPR = DK / 16;   // 16-code chunks per row
@@ -268,14 +277,11 @@ __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, i
   constexpr int P = BB ? DEC_QUEUE_BF16 : DEC_QUEUE;  // queue depth (sweep steps loaded ahead)
   constexpr int CODE_LEAD = DEC_CODE_LEAD;
   const int W = a.W;
-  const int f = J.f;
-  const int bh = J.seq * a.H + J.h;
-  const size_t qk_base = size_t(bh) * DK;
-  const size_t v_base = size_t(bh) * DV;
-  const size_t bufs_base = size_t(bh) * W;
-  const rsrc_t rk = make_rsrc(static_cast<const char*>(a.buf_k) + size_t(bh) * W * DK * EB, uint32_t(f) * DK * EB);
-  const rsrc_t rv = make_rsrc(static_cast<const char*>(a.buf_v) + size_t(bh) * W * DV * EB, uint32_t(f) * DV * EB);
   const uint32_t ko = uint32_t(lane) * EK * EB, vo = uint32_t(lane) * RPL * EB;
+  // the head being swept (filled by fetch while the previous head finishes)
+  JobId J;
+  int bh;
+  rsrc_t rk, rv;
   // raw words of a buffered key / value (fp32 bits, or packed bf16): the
   // queue holds these and they are widened at the step that consumes them
   auto load_raw = [&](const rsrc_t& r, uint32_t o, uint32_t so, int n, uint32_t* x) __attribute__((always_inline)) {
@@ -313,225 +319,249 @@ __device__ __forceinline__ void open_head(const DecodeArgs& a, const JobId& J, i
       if constexpr (RPL == 2) y[1] = bf16_hi(x[0]);
     }
   };
-  // queue first (oldest loads): the first sweep steps wait for nothing else
   uint32_t kq[P][KWD], vq[P][VWD];
-#pragma unroll
-  for (int u = 0; u < P; ++u) {
-    load_k(f - 1 - u, kq[u]);
-    load_v(f - 1 - u, vq[u]);
-  }
-  const float a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
-  const float b_slot = bload_f1(make_rsrc(a.buf_beta + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
-  const float alpha_t = a.alpha[bh];
-  const float beta_t = a.beta[bh];
+  float a_slot, b_slot, alpha_t, beta_t;
   RawVec<IN_BF16, EK> qraw, kraw;
-  load_raw_vec<IN_BF16, EK>(a.q, qk_base + lane * EK, qraw);
-  load_raw_vec<IN_BF16, EK>(a.k, qk_base + lane * EK, kraw);
   RawVec<IN_BF16, RPL> vraw;
-  load_raw_vec<IN_BF16, RPL>(a.v, v_base + lane * RPL, vraw);
   float srow[RPL];
+  // every load a head needs before its sweep: token inputs, scales and
+  // per-slot decays first, then the first P buffered writes
+  auto fetch = [&](int o) __attribute__((always_inline)) {
+    J = job_id(L, L.n_close_jobs + o);
+    bh = J.seq * a.H + J.h;
+    const int fb = J.f;
+    const size_t bufs = size_t(bh) * W;
+    rk = make_rsrc(static_cast<const char*>(a.buf_k) + bufs * DK * EB, uint32_t(fb) * DK * EB);
+    rv = make_rsrc(static_cast<const char*>(a.buf_v) + bufs * DV * EB, uint32_t(fb) * DV * EB);
+    load_raw_vec<IN_BF16, EK>(a.q, size_t(bh) * DK + lane * EK, qraw);
+    load_raw_vec<IN_BF16, EK>(a.k, size_t(bh) * DK + lane * EK, kraw);
+    load_raw_vec<IN_BF16, RPL>(a.v, size_t(bh) * DV + lane * RPL, vraw);
 #pragma unroll
-  for (int i = 0; i < RPL; ++i) srow[i] = a.scales[v_base + lane * RPL + i];
-  // the int8 rows are needed last: their loads go out when at most CODE_LEAD
-  // blocks of sweep steps remain, so that early bandwidth feeds the sweeps of
-  // the heads with the longest windows (they bound the step)
-  uint4 cw[RPL][CPR];
-  auto load_codes = [&]() {
+    for (int i = 0; i < RPL; ++i) srow[i] = a.scales[size_t(bh) * DV + lane * RPL + i];
+    alpha_t = a.alpha[bh];
+    beta_t = a.beta[bh];
+    a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
+    b_slot = bload_f1(make_rsrc(a.buf_beta + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
 #pragma unroll
-    for (int i = 0; i < RPL; ++i)
-#pragma unroll
-      for (int c = 0; c < CPR; ++c)
-        cw[i][c] = *reinterpret_cast<const uint4*>(a.codes + (v_base + lane * RPL + i) * DK + 16 * c);
+    for (int u = 0; u < P; ++u) {
+      load_k(J.f - 1 - u, kq[u]);
+      load_v(J.f - 1 - u, vq[u]);
+    }
   };
+  int k = 0;
+  int o = slot;
+  fetch(o);
+  for (;;) {
+    const int f = J.f;
+    const size_t v_base = size_t(bh) * DV;
+    const size_t bufs_base = size_t(bh) * W;
+    // the int8 rows are needed last: their loads go out when at most CODE_LEAD
+    // blocks of sweep steps remain, so that early bandwidth feeds the sweeps of
+    // the heads with the longest windows (they bound the step)
+    uint4 cw[RPL][CPR];
+    auto load_codes = [&]() {
+#pragma unroll
+      for (int i = 0; i < RPL; ++i)
+#pragma unroll
+        for (int c = 0; c < CPR; ++c)
+          cw[i][c] = *reinterpret_cast<const uint4*>(a.codes + (v_base + lane * RPL + i) * DK + 16 * c);
+    };
 
-  float qv[EK], kv[EK], vcur[RPL];
-  unpack_raw_vec<IN_BF16, EK>(qraw, qv);
-  unpack_raw_vec<IN_BF16, EK>(kraw, kv);
-  unpack_raw_vec<IN_BF16, RPL>(vraw, vcur);
-  if constexpr (WHT) {
-    fwht_group<EK, 64>(qv, lane);
-    fwht_group<EK, 64>(kv, lane);
-  }
-  // the current token first, then the buffered writes newest to oldest;
-  // carried as yt = y / (product of the alphas swept so far)
-  float yt[EK];
-  float p = 0.f;
-#pragma unroll
-  for (int e = 0; e < EK; ++e) {
-    yt[e] = qv[e];
-    p += kv[e] * qv[e];
-  }
-  const float c_cur = beta_t * wave_allreduce_sum(p);
-#pragma unroll
-  for (int e = 0; e < EK; ++e) yt[e] -= c_cur * kv[e];
-  float G = alpha_t;
-  float acc[RPL];
-#pragma unroll
-  for (int i = 0; i < RPL; ++i) acc[i] = c_cur * vcur[i];
-  // append v and k (k in the rotated basis under WHT; a bf16 buffer keeps
-  // them rounded to nearest even) now, so that neither stays live through the
-  // sweep: the sweep never reads slot f (its loads are bounded at f writes)
-  if constexpr (BB) {
-    uint16_t* bv = static_cast<uint16_t*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
-    uint16_t* bk = static_cast<uint16_t*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
-    if constexpr (RPL == 2)
-      *reinterpret_cast<uint32_t*>(bv) = f32_to_bf16_bits(vcur[0]) | (f32_to_bf16_bits(vcur[1]) << 16);
-    else
-      bv[0] = uint16_t(f32_to_bf16_bits(vcur[0]));
-    if constexpr (EK == 2)
-      *reinterpret_cast<uint32_t*>(bk) = f32_to_bf16_bits(kv[0]) | (f32_to_bf16_bits(kv[1]) << 16);
-    else
-      bk[0] = uint16_t(f32_to_bf16_bits(kv[0]));
-  } else {
-    float* bv = static_cast<float*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
-    float* bk = static_cast<float*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) bv[i] = vcur[i];
-#pragma unroll
-    for (int e = 0; e < EK; ++e) bk[e] = kv[e];
-  }
-  if (lane == 0) {
-    a.buf_alpha[bufs_base + f] = alpha_t;
-    a.buf_beta[bufs_base + f] = beta_t;
-    if (J.h == 0) a.fill_out[J.seq] = f + 1;
-  }
-  // one sweep step on queue slot u (write j): the slot is copied out first so
-  // that its registers can take the load of write j - P at once
-  auto step = [&](int u, int j, bool refill) {
-    uint32_t kw[KWD], vw[VWD];
-#pragma unroll
-    for (int e = 0; e < KWD; ++e) asm volatile("v_mov_b32 %0, %1" : "=v"(kw[e]) : "v"(kq[u][e]));
-#pragma unroll
-    for (int i = 0; i < VWD; ++i) asm volatile("v_mov_b32 %0, %1" : "=v"(vw[i]) : "v"(vq[u][i]));
-    float kj[EK], vj[RPL];
-    widen_k(kw, kj);
-    widen_v(vw, vj);
-    if (refill) {
-      load_k(j - P, kq[u]);
-      load_v(j - P, vq[u]);
+    float qv[EK], kv[EK], vcur[RPL];
+    unpack_raw_vec<IN_BF16, EK>(qraw, qv);
+    unpack_raw_vec<IN_BF16, EK>(kraw, kv);
+    unpack_raw_vec<IN_BF16, RPL>(vraw, vcur);
+    if constexpr (WHT) {
+      fwht_group<EK, 64>(qv, lane);
+      fwht_group<EK, 64>(kv, lane);
     }
-    float pp = 0.f;
-#pragma unroll
-    for (int e = 0; e < EK; ++e) pp += kj[e] * yt[e];
-    const float bt = lane_value(b_slot, j) * wave_allreduce_sum(pp);
-#pragma unroll
-    for (int e = 0; e < EK; ++e) yt[e] -= bt * kj[e];
-    const float cj = bt * G;
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) acc[i] = fmaf(cj, vj[i], acc[i]);
-    G *= lane_value(a_slot, j);
-  };
-  // two writes at a time (slots u, u + 1 = writes j, j - 1): with
-  // d_a = k_j . yt, d_b = k_{j-1} . yt and g = k_j . k_{j-1} (three
-  // overlapped reductions), bt_a = beta_j d_a and
-  // bt_b = beta_{j-1} (k_{j-1} . (yt - bt_a k_j)) = beta_{j-1} (d_b - bt_a g)
-  auto step2 = [&](int u, int j, bool refill) {
-    uint32_t kwa[KWD], kwb[KWD], vwa[VWD], vwb[VWD];
-#pragma unroll
-    for (int e = 0; e < KWD; ++e) {
-      asm volatile("v_mov_b32 %0, %1" : "=v"(kwa[e]) : "v"(kq[u][e]));
-      asm volatile("v_mov_b32 %0, %1" : "=v"(kwb[e]) : "v"(kq[u + 1][e]));
-    }
-#pragma unroll
-    for (int i = 0; i < VWD; ++i) {
-      asm volatile("v_mov_b32 %0, %1" : "=v"(vwa[i]) : "v"(vq[u][i]));
-      asm volatile("v_mov_b32 %0, %1" : "=v"(vwb[i]) : "v"(vq[u + 1][i]));
-    }
-    float ka[EK], kb[EK], va[RPL], vb[RPL];
-    widen_k(kwa, ka);
-    widen_k(kwb, kb);
-    widen_v(vwa, va);
-    widen_v(vwb, vb);
-    if (refill) {
-      load_k(j - P, kq[u]);
-      load_v(j - P, vq[u]);
-      load_k(j - 1 - P, kq[u + 1]);
-      load_v(j - 1 - P, vq[u + 1]);
-    }
-    float da = 0.f, db = 0.f, g = 0.f;
+    // the current token first, then the buffered writes newest to oldest;
+    // carried as yt = y / (product of the alphas swept so far)
+    float yt[EK];
+    float p = 0.f;
 #pragma unroll
     for (int e = 0; e < EK; ++e) {
-      da += ka[e] * yt[e];
-      db += kb[e] * yt[e];
-      g += ka[e] * kb[e];
+      yt[e] = qv[e];
+      p += kv[e] * qv[e];
     }
-    wave_allreduce_sum3(da, db, g);
-    const float bta = lane_value(b_slot, j) * da;
-    const float btb = lane_value(b_slot, j - 1) * (db - bta * g);
+    const float c_cur = beta_t * wave_allreduce_sum(p);
 #pragma unroll
-    for (int e = 0; e < EK; ++e) yt[e] = fmaf(-btb, kb[e], fmaf(-bta, ka[e], yt[e]));
-    const float ca = bta * G;
-    G *= lane_value(a_slot, j);
-    const float cb = btb * G;
-    G *= lane_value(a_slot, j - 1);
+    for (int e = 0; e < EK; ++e) yt[e] -= c_cur * kv[e];
+    float G = alpha_t;
+    float acc[RPL];
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) acc[i] = fmaf(cb, vb[i], fmaf(ca, va[i], acc[i]));
-  };
-  static_assert(P % 2 == 0, "queue depth is even");
-  int base = f - 1;
-  for (; base >= CODE_LEAD * P - 1 && base >= P - 1; base -= P) {  // whole blocks: every slot is refilled
+    for (int i = 0; i < RPL; ++i) acc[i] = c_cur * vcur[i];
+    // append v and k (k in the rotated basis under WHT; a bf16 buffer keeps
+    // them rounded to nearest even) now, so that neither stays live through the
+    // sweep: the sweep never reads slot f (its loads are bounded at f writes)
+    if constexpr (BB) {
+      uint16_t* bv = static_cast<uint16_t*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
+      uint16_t* bk = static_cast<uint16_t*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
+      if constexpr (RPL == 2)
+        *reinterpret_cast<uint32_t*>(bv) = f32_to_bf16_bits(vcur[0]) | (f32_to_bf16_bits(vcur[1]) << 16);
+      else
+        bv[0] = uint16_t(f32_to_bf16_bits(vcur[0]));
+      if constexpr (EK == 2)
+        *reinterpret_cast<uint32_t*>(bk) = f32_to_bf16_bits(kv[0]) | (f32_to_bf16_bits(kv[1]) << 16);
+      else
+        bk[0] = uint16_t(f32_to_bf16_bits(kv[0]));
+    } else {
+      float* bv = static_cast<float*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
+      float* bk = static_cast<float*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
 #pragma unroll
-    for (int u = 0; u < P; u += 2) step2(u, base - u, true);
-  }
-  if constexpr (CODE_LEAD > 0) load_codes();  // at most CODE_LEAD blocks (plus the tail) before the rows are needed
-  for (; base >= P - 1; base -= P) {
+      for (int i = 0; i < RPL; ++i) bv[i] = vcur[i];
 #pragma unroll
-    for (int u = 0; u < P; u += 2) step2(u, base - u, true);
-  }
-  // the last base + 1 < P writes are already in the queue: pairs, then one
+      for (int e = 0; e < EK; ++e) bk[e] = kv[e];
+    }
+    if (lane == 0) {
+      a.buf_alpha[bufs_base + f] = alpha_t;
+      a.buf_beta[bufs_base + f] = beta_t;
+      if (J.h == 0) a.fill_out[J.seq] = f + 1;
+    }
+    // one sweep step on queue slot u (write j): the slot is copied out first so
+    // that its registers can take the load of write j - P at once
+    auto step = [&](int u, int j, bool refill) {
+      uint32_t kw[KWD], vw[VWD];
 #pragma unroll
-  for (int u = 0; u + 1 < P; u += 2)
-    if (u + 1 <= base) step2(u, base - u, false);
+      for (int e = 0; e < KWD; ++e) asm volatile("v_mov_b32 %0, %1" : "=v"(kw[e]) : "v"(kq[u][e]));
 #pragma unroll
-  for (int u = 0; u < P; u += 2)
-    if (u == base) step(u, 0, false);
-  if constexpr (CODE_LEAD == 0) load_codes();
+      for (int i = 0; i < VWD; ++i) asm volatile("v_mov_b32 %0, %1" : "=v"(vw[i]) : "v"(vq[u][i]));
+      float kj[EK], vj[RPL];
+      widen_k(kw, kj);
+      widen_v(vw, vj);
+      if (refill) {
+        load_k(j - P, kq[u]);
+        load_v(j - P, vq[u]);
+      }
+      float pp = 0.f;
 #pragma unroll
-  for (int e = 0; e < EK; ++e) wy[lane * EK + e] = G * yt[e];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // int8 rows . y
-  float d[RPL];
+      for (int e = 0; e < EK; ++e) pp += kj[e] * yt[e];
+      const float bt = lane_value(b_slot, j) * wave_allreduce_sum(pp);
 #pragma unroll
-  for (int i = 0; i < RPL; ++i) d[i] = 0.f;
+      for (int e = 0; e < EK; ++e) yt[e] -= bt * kj[e];
+      const float cj = bt * G;
 #pragma unroll
-  for (int c = 0; c < CPR; ++c) {
-    const float4* y4 = reinterpret_cast<const float4*>(wy + 16 * c);
-    float yy[16];
+      for (int i = 0; i < RPL; ++i) acc[i] = fmaf(cj, vj[i], acc[i]);
+      G *= lane_value(a_slot, j);
+    };
+    // two writes at a time (slots u, u + 1 = writes j, j - 1): with
+    // d_a = k_j . yt, d_b = k_{j-1} . yt and g = k_j . k_{j-1} (three
+    // overlapped reductions), bt_a = beta_j d_a and
+    // bt_b = beta_{j-1} (k_{j-1} . (yt - bt_a k_j)) = beta_{j-1} (d_b - bt_a g)
+    auto step2 = [&](int u, int j, bool refill) {
+      uint32_t kwa[KWD], kwb[KWD], vwa[VWD], vwb[VWD];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 t = y4[q4];
-      yy[4 * q4] = t.x;
-      yy[4 * q4 + 1] = t.y;
-      yy[4 * q4 + 2] = t.z;
-      yy[4 * q4 + 3] = t.w;
+      for (int e = 0; e < KWD; ++e) {
+        asm volatile("v_mov_b32 %0, %1" : "=v"(kwa[e]) : "v"(kq[u][e]));
+        asm volatile("v_mov_b32 %0, %1" : "=v"(kwb[e]) : "v"(kq[u + 1][e]));
+      }
+#pragma unroll
+      for (int i = 0; i < VWD; ++i) {
+        asm volatile("v_mov_b32 %0, %1" : "=v"(vwa[i]) : "v"(vq[u][i]));
+        asm volatile("v_mov_b32 %0, %1" : "=v"(vwb[i]) : "v"(vq[u + 1][i]));
+      }
+      float ka[EK], kb[EK], va[RPL], vb[RPL];
+      widen_k(kwa, ka);
+      widen_k(kwb, kb);
+      widen_v(vwa, va);
+      widen_v(vwb, vb);
+      if (refill) {
+        load_k(j - P, kq[u]);
+        load_v(j - P, vq[u]);
+        load_k(j - 1 - P, kq[u + 1]);
+        load_v(j - 1 - P, vq[u + 1]);
+      }
+      float da = 0.f, db = 0.f, g = 0.f;
+#pragma unroll
+      for (int e = 0; e < EK; ++e) {
+        da += ka[e] * yt[e];
+        db += kb[e] * yt[e];
+        g += ka[e] * kb[e];
+      }
+      wave_sum3_uniform(da, db, g);
+      const float bta = lane_value(b_slot, j) * da;
+      const float btb = lane_value(b_slot, j - 1) * (db - bta * g);
+#pragma unroll
+      for (int e = 0; e < EK; ++e) yt[e] = fmaf(-btb, kb[e], fmaf(-bta, ka[e], yt[e]));
+      const float ca = bta * G;
+      G *= lane_value(a_slot, j);
+      const float cb = btb * G;
+      G *= lane_value(a_slot, j - 1);
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) acc[i] = fmaf(cb, vb[i], fmaf(ca, va[i], acc[i]));
+    };
+    static_assert(P % 2 == 0, "queue depth is even");
+    int base = f - 1;
+    for (; base >= CODE_LEAD * P - 1 && base >= P - 1; base -= P) {  // whole blocks: every slot is refilled
+#pragma unroll
+      for (int u = 0; u < P; u += 2) step2(u, base - u, true);
+    }
+    if constexpr (CODE_LEAD > 0) load_codes();  // at most CODE_LEAD blocks (plus the tail) before the rows are needed
+    for (; base >= P - 1; base -= P) {
+#pragma unroll
+      for (int u = 0; u < P; u += 2) step2(u, base - u, true);
+    }
+    // the last base + 1 < P writes are already in the queue: pairs, then one
+#pragma unroll
+    for (int u = 0; u + 1 < P; u += 2)
+      if (u + 1 <= base) step2(u, base - u, false);
+#pragma unroll
+    for (int u = 0; u < P; u += 2)
+      if (u == base) step(u, 0, false);
+    if constexpr (CODE_LEAD == 0) load_codes();
+#pragma unroll
+    for (int e = 0; e < EK; ++e) wy[lane * EK + e] = G * yt[e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // int8 rows . y
+    float d[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) d[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPR; ++c) {
+      const float4* y4 = reinterpret_cast<const float4*>(wy + 16 * c);
+      float yy[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 t = y4[q4];
+        yy[4 * q4] = t.x;
+        yy[4 * q4 + 1] = t.y;
+        yy[4 * q4 + 2] = t.z;
+        yy[4 * q4 + 3] = t.w;
+      }
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        const uint32_t w[4] = {cw[i][c].x, cw[i][c].y, cw[i][c].z, cw[i][c].w};
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int b8 = 0; b8 < 4; ++b8) d[i] = fmaf(i8_at(w[q4], b8), yy[4 * q4 + b8], d[i]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const uint32_t w[4] = {cw[i][c].x, cw[i][c].y, cw[i][c].z, cw[i][c].w};
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-        for (int b8 = 0; b8 < 4; ++b8) d[i] = fmaf(i8_at(w[q4], b8), yy[4 * q4 + b8], d[i]);
+      const int row = lane * RPL + i;
+      store_out<OUT_BF16>(a.o, v_base + row, srow[i] * d[i] + acc[i]);
     }
+    __builtin_amdgcn_wave_barrier();  // the next head reuses wy
+    ++k;
+    o = k * NW + ((k & 1) ? NW - 1 - slot : slot);
+    if (o >= n_open) break;
+    fetch(o);
   }
-#pragma unroll
-  for (int i = 0; i < RPL; ++i) {
-    const int row = lane * RPL + i;
-    store_out<OUT_BF16>(a.o, v_base + row, srow[i] * d[i] + acc[i]);
-  }
-  __builtin_amdgcn_wave_barrier();  // the next head reuses wy
 }
 
 template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT, bool BB>
-__global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void decode_kernel(DecodeArgs a) {
   using S = DecShape<DK, DV>;
   constexpr int NT = S::NT;
   __shared__ float4 smem4[(S::L_END + 3) / 4];
   __shared__ uint64_t cmask[DEC_MAXB / 64];
   __shared__ int cpre[DEC_MAXB / 64 + 1];
   __shared__ uint8_t fills[DEC_MAXB];
+  __shared__ uint16_t order[DEC_MAXB];
+  __shared__ int vbase[64];
   extern __shared__ float4 dyn4[];  // buffered keys [W][DK]
   float* smem = reinterpret_cast<float*>(smem4);
   float* k_lds = reinterpret_cast<float*>(dyn4);
@@ -561,12 +591,41 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
       }
       cpre[nchunk] = acc;
     }
+    // open sequences by fill, longest first, ties in sequence order (a
+    // counting sort; every workgroup derives the same order).  vbase[v] is
+    // first the count of open sequences at fill v, then the next position
+    // for fill v.
+    const int lane = threadIdx.x;
+    vbase[lane] = 0;
+    for (int c = 0; c < nchunk; ++c) {
+      const int s = c * 64 + lane;
+      const int f = s < B ? fills[s] : W - 1;
+      if (f != W - 1) atomicAdd(&vbase[f], 1);
+    }
+    const float incl = wave_scan_incl(float(vbase[lane]));  // open sequences at fill <= lane (exact)
+    const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+    vbase[lane] = int(total - incl);  // open sequences at a longer fill
+    for (int c = 0; c < nchunk; ++c) {
+      const int s = c * 64 + lane;
+      const int f = s < B ? fills[s] : W - 1;
+      const bool open = f != W - 1;
+      uint64_t same = __ballot(open);  // lanes with an open sequence at this lane's fill
+#pragma unroll
+      for (int b = 0; b < 6; ++b) {
+        const uint64_t m = __ballot(open && ((f >> b) & 1));
+        same &= ((f >> b) & 1) ? m : ~m;
+      }
+      const int r = __builtin_amdgcn_mbcnt_hi(uint32_t(same >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(same), 0));
+      if (open) order[vbase[f] + r] = uint16_t(s);
+      if (open && r == 0) vbase[f] += __popcll(same);
+    }
   }
   __syncthreads();
   JobList L;
   L.cmask = cmask;
   L.cpre = cpre;
   L.fills = fills;
+  L.order = order;
   L.B = B;
   L.H = H;
   L.RC = S::RC;
@@ -574,7 +633,17 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
   L.n_close_jobs = ncs * H * S::RC;
   L.n_jobs = L.n_close_jobs + (B - ncs) * H;
 
-  int job = blockIdx.x;
+  // Roles: workgroups [0, OW) take the open heads, the rest the close jobs.
+  // NW waves share the open heads (never more than there are heads); at
+  // least one workgroup is left for close jobs when there are any.
+  const int G = int(gridDim.x);
+  const int n_open = L.n_jobs - L.n_close_jobs;
+  int NW = a.open_waves < n_open ? a.open_waves : n_open;
+  int OW = (NW + NT / 64 - 1) / (NT / 64);
+  const int ow_max = L.n_close_jobs > 0 ? G - 1 : G;
+  if (OW > ow_max) OW = ow_max;
+  if (NW > OW * (NT / 64)) NW = OW * (NT / 64);
+  int job = int(blockIdx.x) - OW;
 
   // ================================================================ close jobs
   // thread t: row rb*CR + t / CSEG, columns [(t % CSEG) * CCOL, +CCOL).  The
@@ -583,7 +652,7 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
   //   s <- alpha s + beta (v - alpha (s . k)) k,
   // where alpha s is formed while s . k is reduced, and the next write's key
   // and value are read from LDS while the current one is applied.
-  for (; job < L.n_close_jobs; job += gridDim.x) {
+  for (; job >= 0 && job < L.n_close_jobs; job += G - OW) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));  // keep per-thread offsets from being hoisted out of the loop
     const int lane = tid & 63;
@@ -730,37 +799,44 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void decode_kernel(DecodeArgs a) {
   }
 
   // ================================================================ open jobs
-  // One wave per head.  Wave slots are numbered from the first workgroup
-  // without a close job, so open heads go to idle waves first.
-  {
+  // One wave per head at a time.  Taken longest window first, wave `slot`
+  // gets positions slot, 2NW-1-slot, 2NW+slot, ... (a serpentine deal, so
+  // every wave's total window length is about the same).  Fewer waves than
+  // heads keeps the loads in flight near what saturates HBM, so the longest
+  // windows are not starved behind the short ones.
+  if (int(blockIdx.x) < OW) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
-    const int G = int(gridDim.x);
-    const int ncb = L.n_close_jobs < G ? L.n_close_jobs : G;
-    const int slot = ((int(blockIdx.x) - ncb + G) % G) * (NT / 64) + wave;
-    const int n_open = L.n_jobs - L.n_close_jobs;
+    const int slot = int(blockIdx.x) * (NT / 64) + wave;
     float* wy = y_lds + wave * DK;
-    for (int o = slot; o < n_open; o += G * (NT / 64)) {
-      const JobId J = job_id(L, L.n_close_jobs + o);
-      open_head<DK, DV, IN_BF16, OUT_BF16, WHT, BB>(a, J, lane, wy);
-    }
+    if (slot < NW) open_wave<DK, DV, IN_BF16, OUT_BF16, WHT, BB>(a, L, slot, NW, n_open, lane, wy);
   }
 }
 
 int decode_row_split() { return 8; }  // close jobs per head at most (grid validation)
 int decode_max_batch() { return DEC_MAXB; }
-// Persistent grid: three resident workgroups per CU on 256 CUs, never
+// Persistent grid: DEC_WG_PER_CU resident workgroups per CU on 256 CUs, never
 // more workgroups than jobs.  GDNQ_DECODE_GRID overrides it (tuning).
 static unsigned decode_grid(int B, int H, int rc) {
   const long jobs_max = long(B) * H * rc;
-  long g = 768;  // three resident workgroups per CU
+  long g = 256 * DEC_WG_PER_CU;  // resident workgroups on 256 CUs
   if (const char* e = getenv("GDNQ_DECODE_GRID")) {
     const long v = atol(e);
     if (v > 0) g = v;
   }
   return unsigned(jobs_max < g ? jobs_max : g);
+}
+
+// Waves that take open heads.  GDNQ_DECODE_OPEN_WAVES overrides it (tuning).
+static int decode_open_waves() {
+  static const int nw = [] {
+    const char* e = getenv("GDNQ_DECODE_OPEN_WAVES");
+    const long v = e ? atol(e) : 0;
+    return v > 0 ? int(v) : DEC_OPEN_WAVES;
+  }();
+  return nw;
 }
 
 template <int DK, int DV, bool IB, bool OB, bool WHT, bool BB>
@@ -792,7 +868,7 @@ static hipError_t launch_bb(const DecodeLaunch& L, const DecodeArgs& a, hipStrea
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   DecodeArgs a{L.q,        L.k,        L.v,       L.alpha,   L.beta,   L.codes, L.scales, L.buf_k,
                L.buf_v,    L.buf_alpha, L.buf_beta, L.fill_in, L.fill_out, L.o,   L.B,      L.H,
-               L.W};
+               L.W,        decode_open_waves()};
   return L.buf_bf16 ? launch_bb<true>(L, a, stream) : launch_bb<false>(L, a, stream);
 }
 

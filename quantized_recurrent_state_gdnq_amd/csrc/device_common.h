@@ -100,6 +100,42 @@ __device__ __forceinline__ float wave_allreduce_sum(float x) {
 
 // Three independent full-wave sums, stage by stage, so that their latencies
 // overlap.
+// Three independent full-wave sums returned as wave-uniform values: DPP
+// inside each row of 16, then row_bcast:15 / row_bcast:31 fold the row sums
+// into lane 63, which is read into a scalar register.  The additions pair the
+// row sums as (r0 + r1) + (r2 + r3), as wave_allreduce_sum3 does.
+__device__ __forceinline__ void wave_sum3_uniform(float& x, float& y, float& z) {
+  x += dpp<DPP_XOR1>(x);
+  y += dpp<DPP_XOR1>(y);
+  z += dpp<DPP_XOR1>(z);
+  x += dpp<DPP_XOR2>(x);
+  y += dpp<DPP_XOR2>(y);
+  z += dpp<DPP_XOR2>(z);
+  x += dpp<DPP_ROW_HALF_MIRROR>(x);
+  y += dpp<DPP_ROW_HALF_MIRROR>(y);
+  z += dpp<DPP_ROW_HALF_MIRROR>(z);
+  x += dpp<DPP_ROW_MIRROR>(x);
+  y += dpp<DPP_ROW_MIRROR>(y);
+  z += dpp<DPP_ROW_MIRROR>(z);
+  // rows 1, 3 += lane 15 of rows 0, 2; then rows 2, 3 += lane 31.  Rows left
+  // out of the row mask keep their value, so each stage is one DPP add (the
+  // compiler emits a move and an add for the masked form).  The leading
+  // s_nop covers the two wait states a DPP read of a just-written VGPR needs;
+  // the second stage of each value is three instructions after its first.
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "v_add_f32_dpp %2, %2, %2 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+      "v_add_f32_dpp %2, %2, %2 row_bcast:31 row_mask:0xc bank_mask:0xf"
+      : "+v"(x), "+v"(y), "+v"(z));
+  x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+  y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(y), 63));
+  z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), 63));
+}
+
 __device__ __forceinline__ void wave_allreduce_sum3(float& x, float& y, float& z) {
   x += dpp<DPP_XOR1>(x);
   y += dpp<DPP_XOR1>(y);
