@@ -340,6 +340,8 @@ def main():
             "gbps": round(rb["gbps"], 1),
             "roofline": {"bound": "hbm", "achieved": round(rb["gbps"], 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(rb["gbps"] / HBM_PEAK_GBPS, 4),
+                         "traffic": load_traffic("decode_b64_h32_bf16buf_traffic.json",
+                                                 ["decode.hip", "device_common.h"], 1),
                          "algorithmic_bytes_per_launch": int(rb["bytes_per_launch"])},
         }
     if not args.no_prefill:
