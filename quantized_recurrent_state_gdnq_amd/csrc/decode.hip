@@ -829,14 +829,12 @@ static unsigned decode_grid(int B, int H, int rc) {
   return unsigned(jobs_max < g ? jobs_max : g);
 }
 
-// Waves that take open heads.  GDNQ_DECODE_OPEN_WAVES overrides it (tuning).
+// Waves that take open heads.  GDNQ_DECODE_OPEN_WAVES overrides it (tuning,
+// and the schedule tests).
 static int decode_open_waves() {
-  static const int nw = [] {
-    const char* e = getenv("GDNQ_DECODE_OPEN_WAVES");
-    const long v = e ? atol(e) : 0;
-    return v > 0 ? int(v) : DEC_OPEN_WAVES;
-  }();
-  return nw;
+  const char* e = getenv("GDNQ_DECODE_OPEN_WAVES");
+  const long v = e ? atol(e) : 0;
+  return v > 0 && v < (1L << 30) ? int(v) : DEC_OPEN_WAVES;
 }
 
 template <int DK, int DV, bool IB, bool OB, bool WHT, bool BB>
