@@ -262,16 +262,22 @@ __device__ __forceinline__ int kt_index(int d, int j) {  // bf16 index of K^T[d]
 
 __device__ __forceinline__ uint2 as_u2(const bf16x4& v) { return __builtin_bit_cast(uint2, v); }
 
-// Per chunk the state pass runs four phases between barriers:
-//   A  X = K S0^T, Q S0^T; rhs; output base             | d = exp(g_C - g)
-//   B  U = T rhs; U^T and (U o d)^T parts               | stage K, Q of the next chunk; load K, Q two ahead
-//   C  S_C^T = gamma_C S0^T + K^T (U o d); O = base + M U | stage T, V, g, beta of the next chunk; load two ahead
-//   D  requantize S_C                                    | next chunk's K^T and M = L o Q K^T
-// so memory traffic, LDS staging and VALU work sit beside the MFMA work of
-// each phase, and every prefetched register is consumed one chunk after it
-// is loaded.
+// Per chunk the state pass runs four phases between barriers, on two roles:
+//   eight chain waves (the recurrence itself)      eight side waves
+//   A  X = K S0^T; rhs                             Q S0^T, scaled: output base
+//   B  U = T rhs; U^T and (U o d)^T parts          stage K, Q of the next chunk; load two ahead
+//   C  S_C^T = gamma_C S0^T + K^T (U o d)          O = base + M U; stage T, V, g, beta of the
+//                                                  next chunk; load two ahead
+//   D  requantize S_C (and two tiles of M)         next chunk's K^T and M = L o Q K^T
+// Everything the recurrence does not wait on (the output, staging, memory
+// traffic, the next chunk's K^T and M) runs on the side waves, so a phase
+// lasts as long as the longer of the two roles' work, not their sum.  Every
+// prefetched register is consumed one chunk after it is loaded.
+constexpr int SNT = 1024;   // state-pass threads
+constexpr int NCRIT = 512;  // threads of the chain waves
+
 template <bool OUT_BF16>
-__global__ __launch_bounds__(512, 1) void gdn_state_kernel(StateArgs a) {
+__global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __bf16* Kl = reinterpret_cast<__bf16*>(lds + OFF_K);
   __bf16* Ql = reinterpret_cast<__bf16*>(lds + OFF_Q);
@@ -298,316 +304,345 @@ __global__ __launch_bounds__(512, 1) void gdn_state_kernel(StateArgs a) {
   const int NC = a.T / PC;
   const size_t HD = size_t(a.H) * PD;
   const size_t state_row0 = (size_t(b) * a.H + h) * PD + r0;
-
-  const int it = wave >> 1, rt = wave & 1;  // this wave's (token tile, row tile) of X, U, O
-  const int nks = (it >> 1) + 1;            // 32-token steps reaching the diagonal of tile it
-  const int r = rt * 16 + lr;
-  const int i0 = it * 16 + 4 * lq;
-
-  // load mapping: K/Q token pair pm, dims [8 ps, +8); T row ti, columns
-  // [8 tc, +8) of each plane; V in this lane's MFMA output layout
-  const int pm = tid & 31, ps = tid >> 5;
-  const int ti = tid >> 3, tc = tid & 7;
   const size_t tokb = size_t(b) * a.T;
+
+  // one 16x16 tile of M = L o Q K^T of the staged chunk: tiles 0..9 are the
+  // lower tiles, D[j][i] = k_j . q_i stored as M[i][j] (hi and lo parts);
+  // tiles 10 and 11 the two zero tiles above the diagonal that the 32-token
+  // steps of M U reach
+  auto build_m_tile = [&](int tt, const float* gc) __attribute__((always_inline)) {
+    int mi, mj;
+    float m4[4] = {0.f, 0.f, 0.f, 0.f};
+    if (tt < 10) {
+      tile_of(tt, mi, mj);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int kk = ks * 32 + 8 * lq;
+        acc = mfma16(lds_bf16x8(Kl + (mj * 16 + lr) * KP + kk), lds_bf16x8(Ql + (mi * 16 + lr) * KP + kk), acc);
+      }
+      const int i = mi * 16 + lr;
+      const float gi = gc[i];
+      const float4 g4 = *reinterpret_cast<const float4*>(gc + mj * 16 + 4 * lq);
+      const float gj[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = mj * 16 + 4 * lq + q;
+        m4[q] = (j <= i) ? exp_out(gi - gj[q]) * acc[q] : 0.f;
+      }
+    } else {
+      mi = tt == 10 ? 0 : 2;
+      mj = mi + 1;
+    }
+    bf16x4 h1, h2;
+    split2(m4, h1, h2);
+    const int i = mi * 16 + lr, j0 = mj * 16 + 4 * lq;
+    *reinterpret_cast<uint2*>(Mp + i * TP + j0) = as_u2(h1);
+    *reinterpret_cast<uint2*>(Mp + PC * TP + i * TP + j0) = as_u2(h2);
+  };
+
+  if (tid < NCRIT) {
+    // ================================================================ chain waves
+    const int it = wave >> 1, rt = wave & 1;  // this wave's (token tile, row tile) of X and U
+    const int nks = (it >> 1) + 1;            // 32-token steps reaching the diagonal of tile it
+    const int r = rt * 16 + lr;
+    const int i0 = it * 16 + 4 * lq;
+    {  // stored rows at the start (zero state without init)
+      const int rq = tid >> 4, seg = tid & 15;  // 32 rows x 16 segments of 8 codes
+      uint2 w = make_uint2(0u, 0u);
+      if (a.init_codes) w = *reinterpret_cast<const uint2*>(a.init_codes + (state_row0 + rq) * PD + seg * 8);
+      *reinterpret_cast<bf16x8*>(Cb + rq * CBP + seg * 8) = i8x8_to_bf16(w);
+      if (seg == 0) sl[rq] = a.init_scales ? a.init_scales[state_row0 + rq] : 0.f;
+    }
+    if (NC > 0) {
+      __syncthreads();  // the side waves stage chunk 0
+      if (wave < 2) build_m_tile(8 + wave, G);
+    }
+    __syncthreads();  // ... and build its K^T and the rest of M
+
+    for (int c = 0; c < NC; ++c) {
+      const float* gc = G + 192 * (c & 1);
+      // ---- A: X = K S0^T (codes exact), rhs
+      {
+        f32x4 xacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int kk = ks * 32 + 8 * lq;
+          xacc = mfma16(lds_bf16x8(Kl + (it * 16 + lr) * KP + kk), lds_bf16x8(Cb + r * CBP + kk), xacc);
+        }
+        const float sr = sl[r];
+        const float4 e4 = *reinterpret_cast<const float4*>(gc + 64 + i0);
+        const float4 b4 = *reinterpret_cast<const float4*>(gc + 128 + i0);
+        const float ge[4] = {e4.x, e4.y, e4.z, e4.w}, be[4] = {b4.x, b4.y, b4.z, b4.w};
+        const uint2 vw = *reinterpret_cast<const uint2*>(Rp + r * TP + i0);
+        const float vv[4] = {__uint_as_float(vw.x << 16), __uint_as_float(vw.x & 0xffff0000u),
+                             __uint_as_float(vw.y << 16), __uint_as_float(vw.y & 0xffff0000u)};
+        float rh[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rh[q] = be[q] * (vv[q] - ge[q] * (sr * xacc[q]));
+        bf16x4 h1, h2, h3;
+        split3(rh, h1, h2, h3);
+        *reinterpret_cast<uint2*>(Rp + r * TP + i0) = as_u2(h1);
+        *reinterpret_cast<uint2*>(Rp + RWS * TP + r * TP + i0) = as_u2(h2);
+        *reinterpret_cast<uint2*>(Rp + 2 * RWS * TP + r * TP + i0) = as_u2(h3);
+      }
+      if (tid < 64) dl[tid] = expf(gc[PC - 1] - gc[tid]);
+      __syncthreads();
+
+      // ---- B: U = T rhs (T unit lower triangular; six split products), then
+      //      U^T (two parts) and (U o d)^T (three parts)
+      {
+        f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = {0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < nks; ++ks) {
+          const int kk = ks * 32 + 8 * lq;
+          const __bf16* tr = Tp + (it * 16 + lr) * TP + kk;
+          const __bf16* rr = Rp + r * TP + kk;
+          const bf16x8 t1 = lds_bf16x8(tr), t2 = lds_bf16x8(tr + PC * TP), t3 = lds_bf16x8(tr + 2 * PC * TP);
+          const bf16x8 b1 = lds_bf16x8(rr), b2 = lds_bf16x8(rr + RWS * TP), b3 = lds_bf16x8(rr + 2 * RWS * TP);
+          ua = mfma16(t2, b2, ua);
+          ub = mfma16(t3, b1, ub);
+          ua = mfma16(t1, b3, ua);
+          ub = mfma16(t2, b1, ub);
+          ua = mfma16(t1, b2, ua);
+          ub = mfma16(t1, b1, ub);
+        }
+        const float4 d4 = *reinterpret_cast<const float4*>(dl + i0);
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+        float u[4], ud[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          u[q] = ua[q] + ub[q];
+          ud[q] = u[q] * dd[q];
+        }
+        bf16x4 h1, h2, h3;
+        split2(u, h1, h2);
+        *reinterpret_cast<uint2*>(Up + r * TP + i0) = as_u2(h1);
+        *reinterpret_cast<uint2*>(Up + RWS * TP + r * TP + i0) = as_u2(h2);
+        split3(ud, h1, h2, h3);
+        *reinterpret_cast<uint2*>(Dp + r * TP + i0) = as_u2(h1);
+        *reinterpret_cast<uint2*>(Dp + RWS * TP + r * TP + i0) = as_u2(h2);
+        *reinterpret_cast<uint2*>(Dp + 2 * RWS * TP + r * TP + i0) = as_u2(h3);
+      }
+      __syncthreads();
+
+      // ---- C: new rows S_C^T = gamma_C S0^T + K^T (U o d)
+      {
+        const int dt0 = (wave >> 1) * 2;
+        bf16x8 u1[2], u2[2], u3[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const __bf16* dp = Dp + r * TP + ks * 32 + 8 * lq;
+          u1[ks] = lds_bf16x8(dp);
+          u2[ks] = lds_bf16x8(dp + RWS * TP);
+          u3[ks] = lds_bf16x8(dp + 2 * RWS * TP);
+        }
+        const float gs = gc[64 + PC - 1] * sl[r];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int dt = dt0 + cc;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 ak = lds_bf16x8(KT + kt_index(dt * 16 + lr, ks * 32 + 8 * lq));
+            acc = mfma16(ak, u3[ks], acc);
+            acc = mfma16(ak, u2[ks], acc);
+            acc = mfma16(ak, u1[ks], acc);
+          }
+          const int d0 = dt * 16 + 4 * lq;
+          const bf16x4 c4 = *reinterpret_cast<const bf16x4*>(Cb + r * CBP + d0);
+          float4 sn;
+          sn.x = gs * float(c4[0]) + acc[0];
+          sn.y = gs * float(c4[1]) + acc[1];
+          sn.z = gs * float(c4[2]) + acc[2];
+          sn.w = gs * float(c4[3]) + acc[3];
+          *reinterpret_cast<float4*>(Sn + r * SNP + d0) = sn;
+        }
+      }
+      __syncthreads();
+
+      // ---- D: requantize the new rows
+      {
+        const int rq = tid >> 4, seg = tid & 15;
+        const float4 s0 = *reinterpret_cast<const float4*>(Sn + rq * SNP + seg * 8);
+        const float4 s1 = *reinterpret_cast<const float4*>(Sn + rq * SNP + seg * 8 + 4);
+        const float x[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+        amax = group_max<16>(amax);
+        const float scale = codec_scale(amax);
+        float cf[8];
+        codec_codes(x, scale, cf);
+        bf16x8 cv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cv[e] = (__bf16)cf[e];
+        *reinterpret_cast<bf16x8*>(Cb + rq * CBP + seg * 8) = cv;
+        if (seg == 0) sl[rq] = scale;
+      }
+      if (wave < 2 && c + 1 < NC) build_m_tile(8 + wave, G + 192 * ((c + 1) & 1));
+      __syncthreads();
+    }
+
+    {  // final rows (codes back to int8)
+      const int rq = tid >> 4, seg = tid & 15;
+      const bf16x8 cv = lds_bf16x8(Cb + rq * CBP + seg * 8);
+      uint2 w;
+      w.x = pack4_i8(int(float(cv[0])), int(float(cv[1])), int(float(cv[2])), int(float(cv[3])));
+      w.y = pack4_i8(int(float(cv[4])), int(float(cv[5])), int(float(cv[6])), int(float(cv[7])));
+      *reinterpret_cast<uint2*>(a.codes + (state_row0 + rq) * PD + seg * 8) = w;
+      if (seg == 0) a.scales[state_row0 + rq] = sl[rq];
+    }
+    return;
+  }
+
+  // ================================================================ side waves
+  const int st = tid - NCRIT;  // 0 .. 511
+  const int sw = st >> 6;      // side wave 0 .. 7: the chain wave whose (token tile, row tile) it outputs
+  // load mapping: K/Q token pair pm, dims [8 ps, +8); T row ti, columns
+  // [8 tc, +8) of each plane; V for chain lane st, in its MFMA output layout
+  const int pm = st & 31, ps = st >> 5;
+  const int ti = st >> 3, tc = st & 7;
+  const int vr = (sw & 1) * 16 + lr, vi = (sw >> 1) * 16 + 4 * lq;
   const uint16_t* kb = a.k + (tokb + 2 * pm) * HD + size_t(h) * PD + 8 * ps;
   const uint16_t* qb = a.q + (tokb + 2 * pm) * HD + size_t(h) * PD + 8 * ps;
-  const uint16_t* vb = a.v + (tokb + i0) * HD + size_t(h) * PD + r0 + r;
+  const uint16_t* vb = a.v + (tokb + vi) * HD + size_t(h) * PD + r0 + vr;
   const __bf16* tb = a.T_ws + (size_t(b) * NC * a.H + h) * 3 * PC * PC + ti * PC + 8 * tc;
-  const float* gb = a.g_ws + (size_t(b) * NC * a.H + h) * PC + (tid & 63);
-  const float* bb = a.beta + (tokb + (tid & 63)) * a.H + h;
+  const float* gb = a.g_ws + (size_t(b) * NC * a.H + h) * PC + (st & 63);
+  const float* bb = a.beta + (tokb + (st & 63)) * a.H + h;
   const size_t tok_step = PC * HD;                   // q/k/v elements per chunk
   const size_t ch_step = size_t(a.H) * 3 * PC * PC;  // T elements per chunk (all heads)
 
-  uint4 k0, k1, q0, q1;  // K, Q of the next chunk (or the one after)
-  uint4 t0, t1, t2;      // T parts, V, g, beta likewise
+  // (clang vector types: arrays of HIP's uint4 are copied through memory)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 k0, k1, q0, q1;  // K, Q of the next chunk (or the one after)
+  u32x4 t0, t1, t2;      // T parts, V, g, beta likewise
   uint32_t v4[4];
   float gv = 0.f, bv = 0.f;
   auto load_kq = [&](int c) {
     const size_t o = size_t(c) * tok_step;
-    k0 = *reinterpret_cast<const uint4*>(kb + o);
-    k1 = *reinterpret_cast<const uint4*>(kb + o + HD);
-    q0 = *reinterpret_cast<const uint4*>(qb + o);
-    q1 = *reinterpret_cast<const uint4*>(qb + o + HD);
+    k0 = *reinterpret_cast<const u32x4*>(kb + o);
+    k1 = *reinterpret_cast<const u32x4*>(kb + o + HD);
+    q0 = *reinterpret_cast<const u32x4*>(qb + o);
+    q1 = *reinterpret_cast<const u32x4*>(qb + o + HD);
   };
   auto load_tv = [&](int c) {
     const __bf16* tp = tb + size_t(c) * ch_step;
-    t0 = *reinterpret_cast<const uint4*>(tp);
-    t1 = *reinterpret_cast<const uint4*>(tp + PC * PC);
-    t2 = *reinterpret_cast<const uint4*>(tp + 2 * PC * PC);
+    t0 = *reinterpret_cast<const u32x4*>(tp);
+    t1 = *reinterpret_cast<const u32x4*>(tp + PC * PC);
+    t2 = *reinterpret_cast<const u32x4*>(tp + 2 * PC * PC);
     const size_t o = size_t(c) * tok_step;
 #pragma unroll
     for (int q = 0; q < 4; ++q) v4[q] = vb[o + q * HD];
-    if (tid < 64) {
-      gv = gb[size_t(c) * a.H * PC];
-      bv = bb[size_t(c) * PC * a.H];
-    }
+    gv = gb[size_t(c) * a.H * PC];  // every side lane loads (one wave's worth is used): no branch
+    bv = bb[size_t(c) * PC * a.H];
   };
   auto stage_kq = [&]() {
-    *reinterpret_cast<uint4*>(Kl + (2 * pm) * KP + 8 * ps) = k0;
-    *reinterpret_cast<uint4*>(Kl + (2 * pm + 1) * KP + 8 * ps) = k1;
-    *reinterpret_cast<uint4*>(Ql + (2 * pm) * KP + 8 * ps) = q0;
-    *reinterpret_cast<uint4*>(Ql + (2 * pm + 1) * KP + 8 * ps) = q1;
+    *reinterpret_cast<u32x4*>(Kl + (2 * pm) * KP + 8 * ps) = k0;
+    *reinterpret_cast<u32x4*>(Kl + (2 * pm + 1) * KP + 8 * ps) = k1;
+    *reinterpret_cast<u32x4*>(Ql + (2 * pm) * KP + 8 * ps) = q0;
+    *reinterpret_cast<u32x4*>(Ql + (2 * pm + 1) * KP + 8 * ps) = q1;
   };
   auto stage_tv = [&](int par) {
-    *reinterpret_cast<uint4*>(Tp + ti * TP + 8 * tc) = t0;
-    *reinterpret_cast<uint4*>(Tp + PC * TP + ti * TP + 8 * tc) = t1;
-    *reinterpret_cast<uint4*>(Tp + 2 * PC * TP + ti * TP + 8 * tc) = t2;
-    // V^T of this lane's (row, 4 tokens) into the slots of the first rhs^T
-    // plane: the same lane reads them back and overwrites them with rhs
-    *reinterpret_cast<uint2*>(Rp + r * TP + i0) = make_uint2(v4[0] | (v4[1] << 16), v4[2] | (v4[3] << 16));
-    if (tid < 64) {
+    *reinterpret_cast<u32x4*>(Tp + ti * TP + 8 * tc) = t0;
+    *reinterpret_cast<u32x4*>(Tp + PC * TP + ti * TP + 8 * tc) = t1;
+    *reinterpret_cast<u32x4*>(Tp + 2 * PC * TP + ti * TP + 8 * tc) = t2;
+    // V^T of the chain lane's (row, 4 tokens) into the slots of the first rhs^T
+    // plane: the chain lane reads them back and overwrites them with rhs
+    *reinterpret_cast<uint2*>(Rp + vr * TP + vi) = make_uint2(v4[0] | (v4[1] << 16), v4[2] | (v4[3] << 16));
+    if (st < 64) {
       float* gp = G + 192 * par;
-      gp[tid] = gv;
-      gp[64 + tid] = expf(gv);
-      gp[128 + tid] = bv;
+      gp[st] = gv;
+      gp[64 + st] = expf(gv);
+      gp[128 + st] = bv;
     }
   };
   // K^T of the staged K (tokens 2 pm, 2 pm + 1 of dims [8 ps, +8) per thread)
   auto stage_kt = [&]() {
-    const uint4 w0 = *reinterpret_cast<const uint4*>(Kl + (2 * pm) * KP + 8 * ps);
-    const uint4 w1 = *reinterpret_cast<const uint4*>(Kl + (2 * pm + 1) * KP + 8 * ps);
-    const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w};
-    const uint32_t a1[4] = {w1.x, w1.y, w1.z, w1.w};
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(Kl + (2 * pm) * KP + 8 * ps);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(Kl + (2 * pm + 1) * KP + 8 * ps);
     uint32_t* kt = reinterpret_cast<uint32_t*>(KT);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of both words
-      kt[kt_index(8 * ps + e, 2 * pm) >> 1] = __builtin_amdgcn_perm(a1[e >> 1], a0[e >> 1], sel);
+      kt[kt_index(8 * ps + e, 2 * pm) >> 1] = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
     }
   };
-  // M = L o Q K^T of the staged chunk: lower 16x16 tiles as M^T tiles
-  // D[j][i] = k_j . q_i, stored as M[i][j] (hi and lo parts), plus the two
-  // zero tiles above the diagonal that the 32-token steps of M U reach
-  auto build_m = [&](const float* gc) {
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int tt = wave + 8 * n;
-      if (tt < 12) {
-        int mi, mj;
-        float m4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (tt < 10) {
-          tile_of(tt, mi, mj);
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const int kk = ks * 32 + 8 * lq;
-            acc = mfma16(lds_bf16x8(Kl + (mj * 16 + lr) * KP + kk), lds_bf16x8(Ql + (mi * 16 + lr) * KP + kk), acc);
-          }
-          const int i = mi * 16 + lr;
-          const float gi = gc[i];
-          const float4 g4 = *reinterpret_cast<const float4*>(gc + mj * 16 + 4 * lq);
-          const float gj[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int j = mj * 16 + 4 * lq + q;
-            m4[q] = (j <= i) ? exp_out(gi - gj[q]) * acc[q] : 0.f;
-          }
-        } else {
-          mi = tt == 10 ? 0 : 2;
-          mj = mi + 1;
-        }
-        bf16x4 h1, h2;
-        split2(m4, h1, h2);
-        const int i = mi * 16 + lr, j0 = mj * 16 + 4 * lq;
-        *reinterpret_cast<uint2*>(Mp + i * TP + j0) = as_u2(h1);
-        *reinterpret_cast<uint2*>(Mp + PC * TP + i * TP + j0) = as_u2(h2);
-      }
-    }
-  };
-
-  // stored rows at the start (zero state without init)
-  {
-    const int rq = tid >> 4, seg = tid & 15;  // 32 rows x 16 segments of 8 codes
-    uint2 w = make_uint2(0u, 0u);
-    if (a.init_codes) w = *reinterpret_cast<const uint2*>(a.init_codes + (state_row0 + rq) * PD + seg * 8);
-    *reinterpret_cast<bf16x8*>(Cb + rq * CBP + seg * 8) = i8x8_to_bf16(w);
-    if (seg == 0) sl[rq] = a.init_scales ? a.init_scales[state_row0 + rq] : 0.f;
-  }
   if (NC > 0) {
     load_kq(0);
     load_tv(0);
     stage_kq();
     stage_tv(0);
-    if (NC > 1) {
-      load_kq(1);
-      load_tv(1);
-    }
+    load_kq(NC > 1 ? 1 : 0);
+    load_tv(NC > 1 ? 1 : 0);
     __syncthreads();
     stage_kt();
-    build_m(G);
+    build_m_tile(sw, G);
+    if (sw == 2 || sw == 3) build_m_tile(sw + 8, G);
   }
   __syncthreads();
 
+  const int it = sw >> 1, i0 = it * 16 + 4 * lq, nks = (it >> 1) + 1;
   for (int c = 0; c < NC; ++c) {
     const size_t tok0 = tokb + size_t(c) * PC;
     const float* gc = G + 192 * (c & 1);
-    // ---- A: K S0^T and Q S0^T (codes exact), rhs, output base
+    // ---- A: output base diag(gamma s) Q S0^T of this wave's (token tile, row tile)
     float os[4];
     {
-      f32x4 xacc = {0.f, 0.f, 0.f, 0.f}, qacc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 qacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int kk = ks * 32 + 8 * lq;
-        const bf16x8 bc = lds_bf16x8(Cb + r * CBP + kk);
-        xacc = mfma16(lds_bf16x8(Kl + (it * 16 + lr) * KP + kk), bc, xacc);
-        qacc = mfma16(lds_bf16x8(Ql + (it * 16 + lr) * KP + kk), bc, qacc);
+        qacc = mfma16(lds_bf16x8(Ql + (it * 16 + lr) * KP + kk), lds_bf16x8(Cb + vr * CBP + kk), qacc);
       }
-      const float sr = sl[r];
+      const float sr = sl[vr];
       const float4 e4 = *reinterpret_cast<const float4*>(gc + 64 + i0);
-      const float4 b4 = *reinterpret_cast<const float4*>(gc + 128 + i0);
-      const float ge[4] = {e4.x, e4.y, e4.z, e4.w}, be[4] = {b4.x, b4.y, b4.z, b4.w};
-      const uint2 vw = *reinterpret_cast<const uint2*>(Rp + r * TP + i0);
-      const float vv[4] = {__uint_as_float(vw.x << 16), __uint_as_float(vw.x & 0xffff0000u),
-                           __uint_as_float(vw.y << 16), __uint_as_float(vw.y & 0xffff0000u)};
-      float rh[4];
+      const float ge[4] = {e4.x, e4.y, e4.z, e4.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        rh[q] = be[q] * (vv[q] - ge[q] * (sr * xacc[q]));
-        os[q] = ge[q] * (sr * qacc[q]);
-      }
-      bf16x4 h1, h2, h3;
-      split3(rh, h1, h2, h3);
-      *reinterpret_cast<uint2*>(Rp + r * TP + i0) = as_u2(h1);
-      *reinterpret_cast<uint2*>(Rp + RWS * TP + r * TP + i0) = as_u2(h2);
-      *reinterpret_cast<uint2*>(Rp + 2 * RWS * TP + r * TP + i0) = as_u2(h3);
-    }
-    if (tid < 64) dl[tid] = expf(gc[PC - 1] - gc[tid]);
-    __syncthreads();
-
-    // ---- B: U = T rhs (T unit lower triangular; six split products), then
-    //      U^T (two parts) and (U o d)^T (three parts)
-    {
-      f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = {0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < nks; ++ks) {
-        const int kk = ks * 32 + 8 * lq;
-        const __bf16* tr = Tp + (it * 16 + lr) * TP + kk;
-        const __bf16* rr = Rp + r * TP + kk;
-        const bf16x8 t1 = lds_bf16x8(tr), t2 = lds_bf16x8(tr + PC * TP), t3 = lds_bf16x8(tr + 2 * PC * TP);
-        const bf16x8 b1 = lds_bf16x8(rr), b2 = lds_bf16x8(rr + RWS * TP), b3 = lds_bf16x8(rr + 2 * RWS * TP);
-        ua = mfma16(t2, b2, ua);
-        ub = mfma16(t3, b1, ub);
-        ua = mfma16(t1, b3, ua);
-        ub = mfma16(t2, b1, ub);
-        ua = mfma16(t1, b2, ua);
-        ub = mfma16(t1, b1, ub);
-      }
-      const float4 d4 = *reinterpret_cast<const float4*>(dl + i0);
-      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-      float u[4], ud[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u[q] = ua[q] + ub[q];
-        ud[q] = u[q] * dd[q];
-      }
-      bf16x4 h1, h2, h3;
-      split2(u, h1, h2);
-      *reinterpret_cast<uint2*>(Up + r * TP + i0) = as_u2(h1);
-      *reinterpret_cast<uint2*>(Up + RWS * TP + r * TP + i0) = as_u2(h2);
-      split3(ud, h1, h2, h3);
-      *reinterpret_cast<uint2*>(Dp + r * TP + i0) = as_u2(h1);
-      *reinterpret_cast<uint2*>(Dp + RWS * TP + r * TP + i0) = as_u2(h2);
-      *reinterpret_cast<uint2*>(Dp + 2 * RWS * TP + r * TP + i0) = as_u2(h3);
-    }
-    if (c + 1 < NC) {  // K and Q of this chunk are no longer read
-      stage_kq();
-      if (c + 2 < NC) load_kq(c + 2);
+      for (int q = 0; q < 4; ++q) os[q] = ge[q] * (sr * qacc[q]);
     }
     __syncthreads();
 
-    // ---- C: new rows S_C^T = gamma_C S0^T + K^T (U o d), and O = base + M U
-    {
-      const int rt2 = wave & 1, dt0 = (wave >> 1) * 2;
-      const int r2 = rt2 * 16 + lr;
-      bf16x8 u1[2], u2[2], u3[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const __bf16* dp = Dp + r2 * TP + ks * 32 + 8 * lq;
-        u1[ks] = lds_bf16x8(dp);
-        u2[ks] = lds_bf16x8(dp + RWS * TP);
-        u3[ks] = lds_bf16x8(dp + 2 * RWS * TP);
-      }
-      const float gs = gc[64 + PC - 1] * sl[r2];
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int dt = dt0 + cc;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 ak = lds_bf16x8(KT + kt_index(dt * 16 + lr, ks * 32 + 8 * lq));
-          acc = mfma16(ak, u3[ks], acc);
-          acc = mfma16(ak, u2[ks], acc);
-          acc = mfma16(ak, u1[ks], acc);
-        }
-        const int d0 = dt * 16 + 4 * lq;
-        const bf16x4 c4 = *reinterpret_cast<const bf16x4*>(Cb + r2 * CBP + d0);
-        float4 sn;
-        sn.x = gs * float(c4[0]) + acc[0];
-        sn.y = gs * float(c4[1]) + acc[1];
-        sn.z = gs * float(c4[2]) + acc[2];
-        sn.w = gs * float(c4[3]) + acc[3];
-        *reinterpret_cast<float4*>(Sn + r2 * SNP + d0) = sn;
-      }
-    }
+    // ---- B: K and Q of this chunk are no longer read.  The loads are
+    //      unconditional (the chunk index is clamped), so the in-order load
+    //      counter never has to assume the shorter path.
+    stage_kq();
+    load_kq(c + 2 < NC ? c + 2 : NC - 1);
+    __syncthreads();
+
+    // ---- C: O = base + M U; T and the rhs planes were last read in B, and
+    //      the other g parity is free
     {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int ks = 0; ks < nks; ++ks) {
         const int kk = ks * 32 + 8 * lq;
         const bf16x8 m1 = lds_bf16x8(Mp + (it * 16 + lr) * TP + kk);
         const bf16x8 m2 = lds_bf16x8(Mp + PC * TP + (it * 16 + lr) * TP + kk);
-        const bf16x8 v1 = lds_bf16x8(Up + r * TP + kk);
-        const bf16x8 v2 = lds_bf16x8(Up + RWS * TP + r * TP + kk);
+        const bf16x8 v1 = lds_bf16x8(Up + vr * TP + kk);
+        const bf16x8 v2 = lds_bf16x8(Up + RWS * TP + vr * TP + kk);
         acc = mfma16(m2, v1, acc);
         acc = mfma16(m1, v2, acc);
         acc = mfma16(m1, v1, acc);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const size_t oi = (tok0 + i0 + q) * HD + size_t(h) * PD + r0 + r;
+        const size_t oi = (tok0 + i0 + q) * HD + size_t(h) * PD + r0 + vr;
         const float ov = os[q] + acc[q];
         if constexpr (OUT_BF16) static_cast<uint16_t*>(a.o)[oi] = uint16_t(f32_to_bf16_bits(ov));
         else static_cast<float*>(a.o)[oi] = ov;
       }
     }
-    if (c + 1 < NC) {  // T and the rhs planes were last read in B; the other g parity is free
-      stage_tv((c + 1) & 1);
-      if (c + 2 < NC) load_tv(c + 2);
-    }
+    stage_tv((c + 1) & 1);
+    load_tv(c + 2 < NC ? c + 2 : NC - 1);
     __syncthreads();
 
-    // ---- D: requantize the new rows; K^T and M of the next chunk
-    {
-      const int rq = tid >> 4, seg = tid & 15;
-      const float4 s0 = *reinterpret_cast<const float4*>(Sn + rq * SNP + seg * 8);
-      const float4 s1 = *reinterpret_cast<const float4*>(Sn + rq * SNP + seg * 8 + 4);
-      const float x[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      float amax = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-      amax = group_max<16>(amax);
-      const float scale = codec_scale(amax);
-      float cf[8];
-      codec_codes(x, scale, cf);
-      bf16x8 cv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) cv[e] = (__bf16)cf[e];
-      *reinterpret_cast<bf16x8*>(Cb + rq * CBP + seg * 8) = cv;
-      if (seg == 0) sl[rq] = scale;
-    }
+    // ---- D: K^T and eight tiles of M of the next chunk (the chain waves 0
+    //      and 1 take tiles 8 and 9 beside the requantization)
     if (c + 1 < NC) {
       stage_kt();
-      build_m(G + 192 * ((c + 1) & 1));
+      build_m_tile(sw, G + 192 * ((c + 1) & 1));
+      if (sw == 2 || sw == 3) build_m_tile(sw + 8, G + 192 * ((c + 1) & 1));
     }
     __syncthreads();
-  }
-
-  {  // final rows (codes back to int8)
-    const int rq = tid >> 4, seg = tid & 15;
-    const bf16x8 cv = lds_bf16x8(Cb + rq * CBP + seg * 8);
-    uint2 w;
-    w.x = pack4_i8(int(float(cv[0])), int(float(cv[1])), int(float(cv[2])), int(float(cv[3])));
-    w.y = pack4_i8(int(float(cv[4])), int(float(cv[5])), int(float(cv[6])), int(float(cv[7])));
-    *reinterpret_cast<uint2*>(a.codes + (state_row0 + rq) * PD + seg * 8) = w;
-    if (seg == 0) a.scales[state_row0 + rq] = sl[rq];
   }
 }
 
@@ -633,7 +668,7 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
   if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, STATE_LDS))
     return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(512), STATE_LDS, stream, s);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(SNT), STATE_LDS, stream, s);
   return hipGetLastError();
 }
 
