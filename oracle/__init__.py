@@ -17,6 +17,8 @@ from .gdnq_oracle import (  # noqa: F401
     run_windowed,
     decode_step,
     round_bf16,
+    round_e4m3,
+    quantize_e4m3_vector,
     prefill,
     chunked_fp64,
     ssd_closed_form,

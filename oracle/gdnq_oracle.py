@@ -43,6 +43,10 @@ design notes):
     buffered writes are replayed on top of the dequantized state (the
     low-bit state takes the window's transitions, [PW]).
   * q and k are used as given (no 1/sqrt(d) scaling, no normalisation).
+  * low-precision window buffers (variants): bf16 keys and values rounded to
+    nearest even, or [PW]'s FP8 vector pairs as OCP E4M3 with one fp32
+    scale absmax/448 per vector (IEEE divisions, ties to even); either way
+    a token's own write enters its step exactly and is stored rounded.
 
 Pins (tests/test_oracle_*.py): every function below is checked against a
 closed form, an invariant, a special case or a hand-derived worked example
@@ -247,8 +251,49 @@ def round_bf16(x):
     return u.astype(np.uint32).view(F32)
 
 
+E4M3_MAX = 448.0
+
+
+def round_e4m3(x):
+    """Nearest value on the OCP FP8 E4M3 grid, ties to even ([PW] keeps
+    recent writes as FP8 vector pairs; the format is the common E4M3).
+
+    E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; the largest
+    finite magnitude is 448 and there is no infinity.  For |x| in
+    [2^e, 2^(e+1)) with e >= -6 the grid step is 2^(e-3); below 2^-6
+    (subnormals) it is 2^-9.  Rounding is rint(|x| / step) * step with
+    rint ties-to-even, exact because step is a power of two.  Finite inputs
+    with |x| <= 448 (larger magnitudes saturate to 448).
+    """
+    x = np.asarray(x, dtype=F32).astype(np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)  # a = m * 2^ex with m in [0.5, 1): e = ex - 1
+    e = np.maximum(ex.astype(np.int64) - 1, -6)
+    step = np.ldexp(1.0, e - 3)
+    r = np.minimum(np.rint(a / step) * step, E4M3_MAX)
+    return (np.sign(x) * r).astype(F32)
+
+
+def quantize_e4m3_vector(x):
+    """One FP8 E4M3 vector with one fp32 scale per vector (last axis).
+
+    scale = absmax / 448 (an IEEE fp32 division); each entry's code is the
+    E4M3 value nearest to x / scale (an IEEE fp32 division, ties to even);
+    the value the buffer holds is code * scale in fp32.  An all-zero vector
+    gets scale 0 and holds zeros.  Returns (values, codes as E4M3 values,
+    scales).
+    """
+    x = np.asarray(x, dtype=F32)
+    amax = np.max(np.abs(x), axis=-1, keepdims=True)
+    scale = (amax / F32(E4M3_MAX)).astype(F32)
+    safe = np.where(scale > 0, scale, F32(1)).astype(F32)
+    c = round_e4m3((x / safe).astype(F32))
+    vals = np.where(scale > 0, (c * scale).astype(F32), F32(0)).astype(F32)
+    return vals, c, scale[..., 0]
+
+
 def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha,
-                buf_beta, fill, W, rot=False, dtype=F32, buf_bf16=False):
+                buf_beta, fill, W, rot=False, dtype=F32, buf_bf16=False, buf_fp8=False):
     """One decode token for a batch of sequences ([LQ] per-window quantization).
 
     q, k: [B,H,dk]; v: [B,H,dv]; alpha, beta: [B,H]; codes [B,H,dv,dk];
@@ -263,6 +308,11 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha,
     appended to the buffer is rounded to bf16 (round_bf16), so later steps
     and the window's close replay the rounded write.  Alpha and beta stay
     fp32.  With bf16 inputs and no rotation this is lossless.
+
+    buf_fp8 (the pages' FP8 vector pairs, [PW]): likewise, but the appended
+    key and value are each stored as an E4M3 vector with one fp32 scale
+    (quantize_e4m3_vector); the buffer arrays returned here hold the values
+    code * scale.
 
     Returns (o, codes_out, scales_out, buf_k, buf_v, buf_alpha, buf_beta,
     fill_out).  The buffer slot `fill` receives the token's write unless its
@@ -308,6 +358,8 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha,
             wv = r["buf"]["v"][slot].reshape(nb, H, dv)
             if buf_bf16:
                 wk, wv = round_bf16(wk), round_bf16(wv)
+            elif buf_fp8:
+                wk, wv = quantize_e4m3_vector(wk)[0], quantize_e4m3_vector(wv)[0]
             bk_out[seqs, :, slot] = wk
             bv_out[seqs, :, slot] = wv
             ba_out[seqs, :, slot] = r["buf"]["alpha"][slot].reshape(nb, H)

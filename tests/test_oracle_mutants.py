@@ -146,3 +146,35 @@ def test_bf16_rounding_mutants_are_caught(mut, monkeypatch):
     monkeypatch.setattr(P.O, "round_bf16", mut)
     with pytest.raises(AssertionError):
         P.test_round_bf16_golden()
+
+
+# ---------------------------------------------------------------- E4M3 buffer rounding
+def _mut_e4m3_truncate(x):  # round toward zero on the E4M3 grid
+    x = np.asarray(x, dtype=F32).astype(np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)
+    step = np.ldexp(1.0, np.maximum(ex.astype(np.int64) - 1, -6) - 3)
+    return (np.sign(x) * np.minimum(np.floor(a / step) * step, 448.0)).astype(F32)
+
+
+def _mut_e4m3_half_up(x):  # ties away from zero
+    x = np.asarray(x, dtype=F32).astype(np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)
+    step = np.ldexp(1.0, np.maximum(ex.astype(np.int64) - 1, -6) - 3)
+    return (np.sign(x) * np.minimum(np.floor(a / step + 0.5) * step, 448.0)).astype(F32)
+
+
+def _mut_e4m3_no_subnormals(x):  # flush the subnormal range to zero
+    r = G.__dict__["_round_e4m3_ref"](x)
+    return np.where(np.abs(r) < 2.0 ** -6, F32(0), r).astype(F32)
+
+
+@pytest.mark.parametrize("mut", [_mut_e4m3_truncate, _mut_e4m3_half_up, _mut_e4m3_no_subnormals])
+def test_e4m3_rounding_mutants_are_caught(mut, monkeypatch):
+    import test_oracle_pins as P
+    monkeypatch.setitem(G.__dict__, "_round_e4m3_ref", G.round_e4m3)
+    monkeypatch.setattr(G, "round_e4m3", mut)
+    monkeypatch.setattr(P.O, "round_e4m3", mut)
+    with pytest.raises(AssertionError):
+        P.test_round_e4m3_golden()

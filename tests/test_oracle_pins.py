@@ -556,3 +556,90 @@ def test_buf_bf16_rotated_write_is_rounded_when_stored():
                            x["alpha"][s_][None], x["beta"][s_][None], W=W, codes0=b[1][s_],
                            scale0=b[2][s_], buffer0=buf, rot=True)
         assert np.array_equal(c[0][s_], r["o"][0])
+
+
+# ---------------------------------------------------------------- FP8 (E4M3) window buffer (variant)
+def test_round_e4m3_golden():
+    """Nearest E4M3 value, ties to even, worked by hand from the format
+    (bias 7, 3 mantissa bits, step 2^(e-3) in [2^e, 2^(e+1)), subnormal
+    step 2^-9, largest finite 448)."""
+    cases = [
+        (1.0, 1.0),
+        (1.0625, 1.0),                # tie between 1.0 (M=000) and 1.125 (M=001): even -> 1.0
+        (1.1875, 1.25),               # tie between 1.125 (001) and 1.25 (010): even -> 1.25
+        (1.07, 1.125),                # just above the tie -> up
+        (17.0, 16.0),                 # step 2 in [16, 32): 8.5 steps -> 8 (even)
+        (19.0, 20.0),                 # 9.5 steps -> 10 (even)
+        (447.0, 448.0),               # step 32 in [256, 512): 13.97 -> 14
+        (-240.0, -240.0),             # on the grid
+        (1.5 * 2.0 ** -9, 2.0 ** -8),  # subnormal tie: 1.5 steps -> 2 (even)
+        (0.5 * 2.0 ** -9, 0.0),       # subnormal tie: 0.5 steps -> 0 (even)
+        (0.75 * 2.0 ** -9, 2.0 ** -9),
+        (2.0 ** -6, 2.0 ** -6),       # smallest normal
+        (0.0, 0.0),
+    ]
+    x = np.array([c[0] for c in cases], F32)
+    want = np.array([c[1] for c in cases], F32)
+    assert np.array_equal(O.round_e4m3(x), want)
+
+
+def test_round_e4m3_matches_torch_cast():
+    """The same rounding as torch's fp32 -> float8_e4m3fn cast (a library
+    routine), over the normal and the subnormal range."""
+    import torch
+    g = np.random.default_rng(33)
+    x = np.concatenate([g.uniform(-448, 448, 20000), g.uniform(-0.03, 0.03, 20000),
+                        g.standard_normal(20000) * np.exp(g.uniform(-12, 5, 20000))])
+    x = np.clip(x, -448, 448).astype(F32)
+    t = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float32).numpy()
+    assert np.array_equal(O.round_e4m3(x), t)
+
+
+def test_quantize_e4m3_vector_properties():
+    """Per-vector E4M3: the largest entry lands on +-448 * scale; every
+    stored value is within half a grid step (times the scale) of its input:
+    at most |x| / 16 on the normal range, 2^-10 * scale below it; a zero
+    vector stores zeros with scale 0."""
+    g = np.random.default_rng(34)
+    x = (g.standard_normal((64, 128)) * np.exp(g.uniform(-6, 6, (64, 1)))).astype(F32)
+    x[5] = 0.0
+    vals, c, s = O.quantize_e4m3_vector(x)
+    assert s[5] == 0 and np.all(vals[5] == 0)
+    nz = s > 0
+    amax_i = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.abs(c[nz, amax_i[nz]]) == 448.0)
+    err = np.abs(vals.astype(np.float64) - x)
+    q = np.abs(x) / np.where(s > 0, s, 1)[:, None]
+    bound = np.where(q >= 2.0 ** -6, np.abs(x) / 16.0, 2.0 ** -10 * s[:, None]) * (1 + 2.0 ** -20)
+    assert np.all(err <= bound + 1e-30)
+    assert np.array_equal(vals, (c * s[:, None]).astype(F32))
+
+
+def test_buf_fp8_current_write_exact_and_stored_quantized():
+    """With the FP8 buffer the step's own write is used exactly (the output
+    equals the fp32 buffer's), the stored slot is the E4M3 vector pair of
+    the write, and the next step replays the stored values."""
+    W = 8
+    d = wl.decode_batch(B=2, H=2, dk=16, dv=16, W=W, seed=9, fill=np.array([1, 3]), poison=False)
+    codes, scales = O.quantize_rows(d["state"])
+    bk = O.quantize_e4m3_vector(d["buf_k"])[0]
+    bv = O.quantize_e4m3_vector(d["buf_v"])[0]
+    args = (codes, scales, bk, bv, d["buf_alpha"], d["buf_beta"], d["fill"], W)
+    a = O.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], *args)
+    b = O.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], *args, buf_fp8=True)
+    assert np.array_equal(a[0], b[0])
+    for s_ in range(2):
+        f = int(d["fill"][s_])
+        assert np.array_equal(b[3][s_, :, f], O.quantize_e4m3_vector(a[3][s_, :, f])[0])
+        assert np.array_equal(b[4][s_, :, f], O.quantize_e4m3_vector(a[4][s_, :, f])[0])
+        assert not np.array_equal(b[3][s_, :, f], a[3][s_, :, f])
+    x = wl.decode_tokens(B=2, H=2, dk=16, dv=16, step=1, seed=10)
+    c = O.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], *b[1:7], b[7], W, buf_fp8=True)
+    for s_ in range(2):
+        f = int(b[7][s_])
+        buf = {"k": np.moveaxis(b[3][s_, :, :f], 1, 0), "v": np.moveaxis(b[4][s_, :, :f], 1, 0),
+               "alpha": b[5][s_, :, :f].T, "beta": b[6][s_, :, :f].T}
+        r = O.run_windowed(x["q"][s_][None], x["k"][s_][None], x["v"][s_][None],
+                           x["alpha"][s_][None], x["beta"][s_][None], W=W, codes0=b[1][s_],
+                           scale0=b[2][s_], buffer0=buf)
+        assert np.array_equal(c[0][s_], r["o"][0])
