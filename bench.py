@@ -42,10 +42,11 @@ B, H, DK, DV, W = 64, 32, 128, 128, 64
 def decode_bytes_per_head(f, W=W, dk=DK, dv=DV, e_in=2, e_out=2, e_buf=4):
     """Algorithmic HBM bytes of one decode token for one head with fill f:
     int8 rows + scales read, f buffered writes read (k, v at e_buf bytes per
-    entry, alpha and beta fp32), the token's q, k, v, alpha, beta read, o
-    written, and either the token's write appended (window open) or the
-    requantized rows + scales written (window close)."""
-    w = e_buf * (dk + dv) + 8
+    entry, alpha and beta fp32, plus two fp32 scales per write with the FP8
+    buffer, e_buf = 1), the token's q, k, v, alpha, beta read, o written, and
+    either the token's write appended (window open) or the requantized rows
+    + scales written (window close)."""
+    w = e_buf * (dk + dv) + 8 + (8 if e_buf == 1 else 0)
     rd = dv * dk + 4 * dv + w * f + e_in * (2 * dk + dv) + 8
     wr = e_out * dv + (w if f + 1 < W else (dv * dk + 4 * dv))
     return rd + wr
@@ -114,7 +115,7 @@ def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None):
     """Timed decode steps; buf_dtype torch.bfloat16 runs the low-precision
     window buffer (writes stored as bf16) on the same workload."""
     buf_dtype = buf_dtype or torch.float32
-    e_buf = 2 if buf_dtype == torch.bfloat16 else 4
+    e_buf = {torch.float32: 4, torch.bfloat16: 2, torch.float8_e4m3fn: 1}[buf_dtype]
     dev = torch.device("cuda:0")
     d = wl.decode_batch(B=B, H=H, dk=DK, dv=DV, W=W, seed=0)
     state = torch.from_numpy(d["state"]).to(dev)
@@ -124,8 +125,15 @@ def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None):
     for i in range(rep_count):
         rep = ops.DecodeState(codes0.clone(), scales0.clone(), W,
                               fill=torch.from_numpy(d["fill"]).to(dev), buf_dtype=buf_dtype)
-        rep.buf_k.copy_(torch.from_numpy(d["buf_k"]).to(buf_dtype))
-        rep.buf_v.copy_(torch.from_numpy(d["buf_v"]).to(buf_dtype))
+        if buf_dtype == torch.float8_e4m3fn:  # E4M3 vector pairs: scale absmax/448, codes by torch's cast
+            for dst, sdst, x in ((rep.buf_k, rep.buf_k_scale, d["buf_k"]), (rep.buf_v, rep.buf_v_scale, d["buf_v"])):
+                t = torch.nan_to_num(torch.from_numpy(x).to(dev))
+                sc = t.abs().amax(dim=-1) / 448.0
+                dst.copy_((t / torch.where(sc > 0, sc, 1.0)[..., None]).to(torch.float8_e4m3fn))
+                sdst.copy_(sc)
+        else:
+            rep.buf_k.copy_(torch.from_numpy(d["buf_k"]).to(buf_dtype))
+            rep.buf_v.copy_(torch.from_numpy(d["buf_v"]).to(buf_dtype))
         rep.buf_alpha.copy_(torch.from_numpy(d["buf_alpha"]))
         rep.buf_beta.copy_(torch.from_numpy(d["buf_beta"]))
         reps.append(rep)
@@ -282,6 +290,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurements")
+    ap.add_argument("--no-fp8-buffer", action="store_true", help="skip the FP8 window-buffer line")
     ap.add_argument("--no-bf16-buffer", action="store_true",
                     help="skip the decode measurement with the bf16 window buffer")
     ap.add_argument("--skip-decode", action="store_true",
@@ -343,6 +352,21 @@ def main():
                          "traffic": load_traffic("decode_b64_h32_bf16buf_traffic.json",
                                                  ["decode.hip", "device_common.h"], 1),
                          "algorithmic_bytes_per_launch": int(rb["bytes_per_launch"])},
+        }
+    if not args.no_fp8_buffer:
+        rf = bench_decode(args, torch, ops, wl, max(1, args.replicas), buf_dtype=torch.float8_e4m3fn)
+        line["decode_fp8_buffer"] = {
+            "workload": "the same decode step with the window buffer's keys and values stored "
+                        "as FP8 vector pairs (GDNQ_FLAG_BUF_FP8: OCP E4M3 codes, one fp32 scale "
+                        "per vector)",
+            "ms_per_step": round(rf["ms_per_step"], 5),
+            "tokens_s": round(rf["tokens_s"], 1),
+            "gbps": round(rf["gbps"], 1),
+            "roofline": {"bound": "hbm", "achieved": round(rf["gbps"], 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(rf["gbps"] / HBM_PEAK_GBPS, 4),
+                         "traffic": load_traffic("decode_b64_h32_fp8buf_traffic.json",
+                                                 ["decode.hip", "device_common.h"], 1),
+                         "algorithmic_bytes_per_launch": int(rf["bytes_per_launch"])},
         }
     if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, ops, wl)

@@ -81,13 +81,24 @@ enum {
   GDNQ_FLAG_INT8_QK = 4u, /* prefill + SSD only: quantize each token's
                              (rotated) q and k row to int8 with the codec
                              above and use the dequantized operands         */
-  GDNQ_FLAG_BUF_BF16 = 16u /* decode only: the window buffer keeps keys and
+  GDNQ_FLAG_BUF_BF16 = 16u, /* decode only: the window buffer keeps keys and
                              values as bf16 (buf_k, buf_v element type).  A
                              token's write enters its own step exactly and is
                              stored rounded to nearest even, so later steps
                              and the window's close replay the rounded write;
                              alpha and beta stay fp32.  Lossless when q, k, v
                              are bf16 and GDNQ_FLAG_WHT is off.              */
+  GDNQ_FLAG_BUF_FP8 = 32u  /* decode only: the window buffer keeps keys and
+                             values as FP8 vector pairs (Low-Bit GDN ...,
+                             abstract): each buffered key and each value is
+                             OCP E4M3 codes (bias 7, largest finite 448) with
+                             one fp32 scale absmax/448; a code is the E4M3
+                             value nearest to x/scale (IEEE fp32 division,
+                             ties to even).  The token's own write enters its
+                             step exactly and is stored quantized.  Layout:
+                             buf_k = B*H*W*d_k code bytes, then B*H*W fp32
+                             scales; buf_v likewise with d_v.  Exclusive with
+                             GDNQ_FLAG_BUF_BF16.                            */
 };
 
 /* ------------------------------------------------------------------------
@@ -125,14 +136,16 @@ gdnq_status gdnq_quantize_state(const float* S, int64_t rows, int32_t d_k, int8_
  *
  *   0 <= p->batch B <= 1024 (0: no-op), p->heads H >= 1, p->d_k, p->d_v in {64,128},
  *   1 <= p->window W <= 64, p->in_dtype (q,k,v) and p->out_dtype (o) in
- *   {GDNQ_F32, GDNQ_BF16}, p->flags a combination of GDNQ_FLAG_WHT and
- *   GDNQ_FLAG_BUF_BF16 (the low-precision window buffer, an option the
- *   Low-Bit GDN page lists among buffer storage formats).
+ *   {GDNQ_F32, GDNQ_BF16}, p->flags a combination of GDNQ_FLAG_WHT and at
+ *   most one of GDNQ_FLAG_BUF_BF16, GDNQ_FLAG_BUF_FP8 (the low-precision
+ *   window buffers; the Low-Bit GDN page keeps recent writes in FP8).
  *     q, k      [B,H,d_k] in_dtype      v [B,H,d_v] in_dtype
  *     alpha, beta [B,H] fp32
  *     codes     [B,H,d_v,d_k] int8      scales [B,H,d_v] fp32   (in/out)
  *     buf_k     [B,H,W,d_k]             buf_v [B,H,W,d_v]       (in/out)
- *               fp32, or bf16 under GDNQ_FLAG_BUF_BF16
+ *               fp32, or bf16 under GDNQ_FLAG_BUF_BF16, or under
+ *               GDNQ_FLAG_BUF_FP8 E4M3 bytes [B,H,W,d] followed by fp32
+ *               scales [B,H,W] in the same buffer
  *     buf_alpha, buf_beta [B,H,W] fp32                           (in/out)
  *     fill_in   [B] int32 in [0, W-1]   fill_out [B] int32 (written)
  *     o         [B,H,d_v] out_dtype (written)

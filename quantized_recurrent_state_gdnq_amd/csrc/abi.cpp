@@ -117,9 +117,13 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
   if ((p->in_dtype != GDNQ_F32 && p->in_dtype != GDNQ_BF16) ||
       (p->out_dtype != GDNQ_F32 && p->out_dtype != GDNQ_BF16))
     return fail(GDNQ_ERR_DTYPE, "in_dtype = %d, out_dtype = %d", p->in_dtype, p->out_dtype);
-  if (p->flags & ~uint32_t(GDNQ_FLAG_WHT | GDNQ_FLAG_BUF_BF16))
-    return fail(GDNQ_ERR_FLAGS, "flags 0x%x: decode accepts GDNQ_FLAG_WHT and GDNQ_FLAG_BUF_BF16", p->flags);
+  if (p->flags & ~uint32_t(GDNQ_FLAG_WHT | GDNQ_FLAG_BUF_BF16 | GDNQ_FLAG_BUF_FP8))
+    return fail(GDNQ_ERR_FLAGS, "flags 0x%x: decode accepts GDNQ_FLAG_WHT, GDNQ_FLAG_BUF_BF16, GDNQ_FLAG_BUF_FP8",
+                p->flags);
   const bool buf_bf16 = (p->flags & GDNQ_FLAG_BUF_BF16) != 0;
+  const bool buf_fp8 = (p->flags & GDNQ_FLAG_BUF_FP8) != 0;
+  if (buf_bf16 && buf_fp8)
+    return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDNQ_FLAG_BUF_BF16 and GDNQ_FLAG_BUF_FP8 are exclusive", p->flags);
   if (B > gdnq::decode_max_batch())
     return fail(GDNQ_ERR_SHAPE, "batch = %d, at most %d sequences per call", B, gdnq::decode_max_batch());
   if (int64_t(B) * H * gdnq::decode_row_split() > 0x7fffffffLL)
@@ -133,8 +137,8 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
                      {"beta", beta, bh * 4},
                      {"codes", codes, bh * dv * dk},
                      {"scales", scales, bh * dv * 4},
-                     {"buf_k", buf_k, bh * W * dk * (buf_bf16 ? 2 : 4)},
-                     {"buf_v", buf_v, bh * W * dv * (buf_bf16 ? 2 : 4)},
+                     {"buf_k", buf_k, bh * W * (buf_fp8 ? dk + 4 : dk * (buf_bf16 ? 2 : 4))},
+                     {"buf_v", buf_v, bh * W * (buf_fp8 ? dv + 4 : dv * (buf_bf16 ? 2 : 4))},
                      {"buf_alpha", buf_alpha, bh * W * 4},
                      {"buf_beta", buf_beta, bh * W * 4},
                      {"fill_in", fill_in, size_t(B) * 4},
@@ -153,7 +157,7 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
   gdnq::DecodeLaunch L{q,        k,        v,       alpha, beta, codes, scales, buf_k,
                        buf_v,    buf_alpha, buf_beta, fill_in, fill_out, o,   B,      H,
                        dk,       dv,       W,       p->in_dtype == GDNQ_BF16,
-                       p->out_dtype == GDNQ_BF16, (p->flags & GDNQ_FLAG_WHT) != 0, buf_bf16};
+                       p->out_dtype == GDNQ_BF16, (p->flags & GDNQ_FLAG_WHT) != 0, buf_bf16, buf_fp8};
   return hip_status(gdnq::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch");
 }
 

@@ -45,7 +45,7 @@ constexpr int DEC_MAXB = 1024;   // sequences per call (fill scan results in LDS
 #define DEC_OPEN_WAVES 1024
 #endif
 #ifndef DEC_QUEUE_BF16
-#define DEC_QUEUE_BF16 24  // bf16 window buffer: half the queue registers per slot
+#define DEC_QUEUE_BF16 24  // bf16 and E4M3 window buffers: half the queue registers per slot
 #endif
 
 struct DecodeArgs {
@@ -56,7 +56,7 @@ struct DecodeArgs {
   const float* beta;
   int8_t* codes;
   float* scales;
-  void* buf_k;  // fp32, or bf16 (BB)
+  void* buf_k;  // fp32, bf16 or E4M3 codes (BUF = 0, 1, 2)
   void* buf_v;
   float* buf_alpha;
   float* buf_beta;
@@ -65,6 +65,8 @@ struct DecodeArgs {
   void* o;
   int B, H, W;
   int open_waves;  // waves that take open heads (the rest of the grid's waves idle)
+  float* ks;       // E4M3 buffer: one scale per buffered key [B*H*W] (else unused)
+  float* vs;       // and per buffered value
 };
 
 template <bool BF16>
@@ -265,16 +267,16 @@ __device__ __forceinline__ JobId job_id(const JobList& L, int job) {
 // The wave takes positions slot, 2NW-1-slot, 2NW+slot, ... of the open-head
 // list.  (Issuing the next head's loads before a head's rows . y work was
 // measured slower: the extra in-flight loads only queue behind HBM.)
-template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT, bool BB>
+template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT, int BUF>
 __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L, int slot, int NW, int n_open,
                                           int lane, float* wy) {
   constexpr int EK = DK / 64;    // key / query elements per lane
   constexpr int RPL = DV / 64;   // state rows per lane
   constexpr int CPR = DK / 16;   // 16-code chunks per row
-  constexpr int EB = BB ? 2 : 4;                 // bytes per buffered element
-  constexpr int KWD = BB ? (EK + 1) / 2 : EK;    // queue words per buffered key (per lane)
-  constexpr int VWD = BB ? (RPL + 1) / 2 : RPL;  // and per buffered value
-  constexpr int P = BB ? DEC_QUEUE_BF16 : DEC_QUEUE;  // queue depth (sweep steps loaded ahead)
+  constexpr int EB = BUF == 0 ? 4 : BUF == 1 ? 2 : 1;  // bytes per buffered element
+  constexpr int KWD = BUF == 0 ? EK : 1;   // queue words per buffered key (per lane)
+  constexpr int VWD = BUF == 0 ? RPL : 1;  // and per buffered value
+  constexpr int P = BUF == 0 ? DEC_QUEUE : DEC_QUEUE_BF16;  // queue depth (sweep steps loaded ahead)
   constexpr int CODE_LEAD = DEC_CODE_LEAD;
   const int W = a.W;
   const uint32_t ko = uint32_t(lane) * EK * EB, vo = uint32_t(lane) * RPL * EB;
@@ -282,17 +284,20 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
   JobId J;
   int bh;
   rsrc_t rk, rv;
-  // raw words of a buffered key / value (fp32 bits, or packed bf16): the
-  // queue holds these and they are widened at the step that consumes them
+  // raw words of a buffered key / value (fp32 bits, packed bf16 or packed
+  // E4M3 codes): the queue holds these and they are widened at the step
+  // that consumes them
   auto load_raw = [&](const rsrc_t& r, uint32_t o, uint32_t so, int n, uint32_t* x) __attribute__((always_inline)) {
-    if (!BB && n == 2) {
+    if (BUF == 0 && n == 2) {
       const uint2 w = bload_u2s(r, o, so);
       x[0] = w.x;
       x[1] = w.y;
-    } else if (!BB || n == 2) {
+    } else if (BUF == 0 || (BUF == 1 && n == 2)) {
       x[0] = __float_as_uint(bload_f1s(r, o, so));
-    } else {
+    } else if (BUF == 1 || n == 2) {
       x[0] = bload_h1s(r, o, so);
+    } else {
+      x[0] = bload_b1s(r, o, so);
     }
   };
   auto load_k = [&](int j, uint32_t (&x)[KWD]) {  // j < 0 lands past the bound: reads 0, no traffic
@@ -301,26 +306,37 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
   auto load_v = [&](int j, uint32_t (&x)[VWD]) {
     load_raw(rv, vo, uint32_t(j) * DV * EB, RPL, x);
   };
-  auto widen_k = [&](const uint32_t (&x)[KWD], float (&y)[EK]) __attribute__((always_inline)) {
-    if constexpr (!BB) {
+  // sc: the vector's scale (E4M3 buffer only): the widened value is
+  // code * scale in fp32, exactly the value the buffer stands for
+  auto widen_k = [&](const uint32_t (&x)[KWD], float (&y)[EK], float sc) __attribute__((always_inline)) {
+    if constexpr (BUF == 0) {
 #pragma unroll
       for (int e = 0; e < EK; ++e) y[e] = __uint_as_float(x[e]);
-    } else {
+    } else if constexpr (BUF == 1) {
       y[0] = bf16_lo(x[0]);
       if constexpr (EK == 2) y[1] = bf16_hi(x[0]);
+    } else {
+      const float2 c = e4m3_unpack2(x[0], false);
+      y[0] = c.x * sc;
+      if constexpr (EK == 2) y[1] = c.y * sc;
     }
   };
-  auto widen_v = [&](const uint32_t (&x)[VWD], float (&y)[RPL]) __attribute__((always_inline)) {
-    if constexpr (!BB) {
+  auto widen_v = [&](const uint32_t (&x)[VWD], float (&y)[RPL], float sc) __attribute__((always_inline)) {
+    if constexpr (BUF == 0) {
 #pragma unroll
       for (int e = 0; e < RPL; ++e) y[e] = __uint_as_float(x[e]);
-    } else {
+    } else if constexpr (BUF == 1) {
       y[0] = bf16_lo(x[0]);
       if constexpr (RPL == 2) y[1] = bf16_hi(x[0]);
+    } else {
+      const float2 c = e4m3_unpack2(x[0], false);
+      y[0] = c.x * sc;
+      if constexpr (RPL == 2) y[1] = c.y * sc;
     }
   };
   uint32_t kq[P][KWD], vq[P][VWD];
   float a_slot, b_slot, alpha_t, beta_t;
+  float ks_slot = 1.f, vs_slot = 1.f;  // lane j: scales of write j (E4M3 buffer)
   RawVec<IN_BF16, EK> qraw, kraw;
   RawVec<IN_BF16, RPL> vraw;
   float srow[RPL];
@@ -342,6 +358,10 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
     beta_t = a.beta[bh];
     a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
     b_slot = bload_f1(make_rsrc(a.buf_beta + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
+    if constexpr (BUF == 2) {
+      ks_slot = bload_f1(make_rsrc(a.ks + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
+      vs_slot = bload_f1(make_rsrc(a.vs + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
+    }
 #pragma unroll
     for (int u = 0; u < P; ++u) {
       load_k(J.f - 1 - u, kq[u]);
@@ -394,7 +414,32 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
     // append v and k (k in the rotated basis under WHT; a bf16 buffer keeps
     // them rounded to nearest even) now, so that neither stays live through the
     // sweep: the sweep never reads slot f (its loads are bounded at f writes)
-    if constexpr (BB) {
+    if constexpr (BUF == 2) {
+      // E4M3 vector pairs: per vector scale = absmax / 448 and codes nearest
+      // to x / scale (IEEE divisions, ties to even)
+      float mk = 0.f, mv = 0.f;
+#pragma unroll
+      for (int e = 0; e < EK; ++e) mk = fmaxf(mk, fabsf(kv[e]));
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) mv = fmaxf(mv, fabsf(vcur[i]));
+      const float sk = __fdiv_rn(group_max<64>(mk), 448.f);
+      const float sv = __fdiv_rn(group_max<64>(mv), 448.f);
+      float ck[2] = {0.f, 0.f}, cv[2] = {0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < EK; ++e) ck[e] = sk > 0.f ? e4m3_round(__fdiv_rn(kv[e], sk)) : 0.f;
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) cv[i] = sv > 0.f ? e4m3_round(__fdiv_rn(vcur[i], sv)) : 0.f;
+      uint8_t* bk = static_cast<uint8_t*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
+      uint8_t* bv = static_cast<uint8_t*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
+      if constexpr (EK == 2) *reinterpret_cast<uint16_t*>(bk) = uint16_t(e4m3_pack2(ck[0], ck[1]));
+      else bk[0] = uint8_t(e4m3_pack2(ck[0], 0.f));
+      if constexpr (RPL == 2) *reinterpret_cast<uint16_t*>(bv) = uint16_t(e4m3_pack2(cv[0], cv[1]));
+      else bv[0] = uint8_t(e4m3_pack2(cv[0], 0.f));
+      if (lane == 0) {
+        a.ks[bufs_base + f] = sk;
+        a.vs[bufs_base + f] = sv;
+      }
+    } else if constexpr (BUF == 1) {
       uint16_t* bv = static_cast<uint16_t*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
       uint16_t* bk = static_cast<uint16_t*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
       if constexpr (RPL == 2)
@@ -427,8 +472,8 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
 #pragma unroll
       for (int i = 0; i < VWD; ++i) asm volatile("v_mov_b32 %0, %1" : "=v"(vw[i]) : "v"(vq[u][i]));
       float kj[EK], vj[RPL];
-      widen_k(kw, kj);
-      widen_v(vw, vj);
+      widen_k(kw, kj, BUF == 2 ? lane_value(ks_slot, j) : 1.f);
+      widen_v(vw, vj, BUF == 2 ? lane_value(vs_slot, j) : 1.f);
       if (refill) {
         load_k(j - P, kq[u]);
         load_v(j - P, vq[u]);
@@ -461,10 +506,10 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
         asm volatile("v_mov_b32 %0, %1" : "=v"(vwb[i]) : "v"(vq[u + 1][i]));
       }
       float ka[EK], kb[EK], va[RPL], vb[RPL];
-      widen_k(kwa, ka);
-      widen_k(kwb, kb);
-      widen_v(vwa, va);
-      widen_v(vwb, vb);
+      widen_k(kwa, ka, BUF == 2 ? lane_value(ks_slot, j) : 1.f);
+      widen_k(kwb, kb, BUF == 2 ? lane_value(ks_slot, j - 1) : 1.f);
+      widen_v(vwa, va, BUF == 2 ? lane_value(vs_slot, j) : 1.f);
+      widen_v(vwb, vb, BUF == 2 ? lane_value(vs_slot, j - 1) : 1.f);
       if (refill) {
         load_k(j - P, kq[u]);
         load_v(j - P, vq[u]);
@@ -552,7 +597,7 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
   }
 }
 
-template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT, bool BB>
+template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT, int BUF>
 __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void decode_kernel(DecodeArgs a) {
   using S = DecShape<DK, DV>;
   constexpr int NT = S::NT;
@@ -671,20 +716,38 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void decode_kernel(Deco
     RawVec<IN_BF16, S::EK> qraw, kraw;
     load_raw_vec<IN_BF16, S::EK>(a.q, qk_base + lane * S::EK, qraw);
     load_raw_vec<IN_BF16, S::EK>(a.k, qk_base + lane * S::EK, kraw);
-    constexpr int EB = BB ? 2 : 4;  // bytes per buffered element
+    constexpr int EB = BUF == 0 ? 4 : BUF == 1 ? 2 : 1;  // bytes per buffered element
     const rsrc_t rk = make_rsrc(static_cast<const char*>(a.buf_k) + size_t(bh) * W * DK * EB, uint32_t(f) * DK * EB);
     // four consecutive buffered elements at element offset e0 (+ e1 scalar)
+    // (E4M3: the codes; the caller applies the vector's scale)
     auto load4 = [&](const rsrc_t& r, uint32_t e0, uint32_t e1) __attribute__((always_inline)) {
-      if constexpr (BB) {
+      if constexpr (BUF == 1) {
         const uint2 w = bload_u2s(r, e0 * 2, e1 * 2);
         return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+      } else if constexpr (BUF == 2) {
+        const uint32_t w = __float_as_uint(bload_f1s(r, e0, e1));
+        const float2 lo = e4m3_unpack2(w, false), hi = e4m3_unpack2(w, true);
+        return make_float4(lo.x, lo.y, hi.x, hi.y);
       } else {
         return bload_f4(r, e0 * 4, e1 * 4);
       }
     };
+    // E4M3: the scale of slot j (slots past the fill read 0)
+    auto slot_scale = [&](const float* sc, int j) __attribute__((always_inline)) {
+      return bload_f1(make_rsrc(sc + bufs_base, uint32_t(f) * 4), uint32_t(j) * 4);
+    };
     float4 kt[S::KREG];
 #pragma unroll
-    for (int i = 0; i < S::KREG; ++i) kt[i] = load4(rk, uint32_t(tid) * 4, uint32_t(i * NT * 4));
+    for (int i = 0; i < S::KREG; ++i) {
+      kt[i] = load4(rk, uint32_t(tid) * 4, uint32_t(i * NT * 4));
+      if constexpr (BUF == 2) {
+        const float sc = slot_scale(a.ks, (tid * 4 + i * NT * 4) / DK);
+        kt[i].x *= sc;
+        kt[i].y *= sc;
+        kt[i].z *= sc;
+        kt[i].w *= sc;
+      }
+    }
     // lane j: alpha_j, beta_j of write j; the current token's in lane W - 1
     float a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
     float b_slot = bload_f1(make_rsrc(a.buf_beta + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
@@ -693,9 +756,17 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void decode_kernel(Deco
     const rsrc_t rv = make_rsrc(static_cast<const char*>(a.buf_v) + size_t(bh) * W * DV * EB, uint32_t(f) * DV * EB);
     float4 vt[S::CVREG];
 #pragma unroll
-    for (int i = 0; i < S::CVREG; ++i)  // slot (tid + NT*i) / CVF4, rows 4*((tid + NT*i) % CVF4)
+    for (int i = 0; i < S::CVREG; ++i) {  // slot (tid + NT*i) / CVF4, rows 4*((tid + NT*i) % CVF4)
       vt[i] = load4(rv, uint32_t((tid / S::CVF4) * DV + (tid % S::CVF4) * 4),
                     uint32_t((i * NT / S::CVF4) * DV + J.rb * S::CR));
+      if constexpr (BUF == 2) {
+        const float sc = slot_scale(a.vs, tid / S::CVF4 + i * NT / S::CVF4);
+        vt[i].x *= sc;
+        vt[i].y *= sc;
+        vt[i].z *= sc;
+        vt[i].w *= sc;
+      }
+    }
     uint32_t vcur_raw = 0;
     if (tid < S::CR) vcur_raw = load_raw<IN_BF16>(a.v, v_base + J.rb * S::CR + tid);
 
@@ -811,7 +882,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void decode_kernel(Deco
     const int wave = uniform(tid >> 6);
     const int slot = int(blockIdx.x) * (NT / 64) + wave;
     float* wy = y_lds + wave * DK;
-    if (slot < NW) open_wave<DK, DV, IN_BF16, OUT_BF16, WHT, BB>(a, L, slot, NW, n_open, lane, wy);
+    if (slot < NW) open_wave<DK, DV, IN_BF16, OUT_BF16, WHT, BUF>(a, L, slot, NW, n_open, lane, wy);
   }
 }
 
@@ -837,7 +908,7 @@ static int decode_open_waves() {
   return v > 0 && v < (1L << 30) ? int(v) : DEC_OPEN_WAVES;
 }
 
-template <int DK, int DV, bool IB, bool OB, bool WHT, bool BB>
+template <int DK, int DV, bool IB, bool OB, bool WHT, int BB>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   const unsigned grid = decode_grid(a.B, a.H, DecShape<DK, DV>::RC);
   const size_t lds = size_t(a.W) * DK * sizeof(float);  // buffered keys
@@ -845,7 +916,7 @@ static hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DK, int DV, bool BB>
+template <int DK, int DV, int BB>
 static hipError_t launch_dkdv(const DecodeArgs& a, bool ib, bool ob, bool wht, hipStream_t s) {
   if (ib) {
     if (ob) return wht ? launch_t<DK, DV, true, true, true, BB>(a, s) : launch_t<DK, DV, true, true, false, BB>(a, s);
@@ -855,7 +926,7 @@ static hipError_t launch_dkdv(const DecodeArgs& a, bool ib, bool ob, bool wht, h
   return wht ? launch_t<DK, DV, false, false, true, BB>(a, s) : launch_t<DK, DV, false, false, false, BB>(a, s);
 }
 
-template <bool BB>
+template <int BB>
 static hipError_t launch_bb(const DecodeLaunch& L, const DecodeArgs& a, hipStream_t stream) {
   if (L.d_k == 128 && L.d_v == 128) return launch_dkdv<128, 128, BB>(a, L.in_bf16, L.out_bf16, L.wht, stream);
   if (L.d_k == 128 && L.d_v == 64) return launch_dkdv<128, 64, BB>(a, L.in_bf16, L.out_bf16, L.wht, stream);
@@ -866,8 +937,14 @@ static hipError_t launch_bb(const DecodeLaunch& L, const DecodeArgs& a, hipStrea
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   DecodeArgs a{L.q,        L.k,        L.v,       L.alpha,   L.beta,   L.codes, L.scales, L.buf_k,
                L.buf_v,    L.buf_alpha, L.buf_beta, L.fill_in, L.fill_out, L.o,   L.B,      L.H,
-               L.W,        decode_open_waves()};
-  return L.buf_bf16 ? launch_bb<true>(L, a, stream) : launch_bb<false>(L, a, stream);
+               L.W,        decode_open_waves(), nullptr,   nullptr};
+  if (L.buf_fp8) {  // the per-vector scales follow the codes in each buffer
+    const size_t nv = size_t(L.B) * L.H * L.W;
+    a.ks = reinterpret_cast<float*>(static_cast<char*>(L.buf_k) + nv * L.d_k);
+    a.vs = reinterpret_cast<float*>(static_cast<char*>(L.buf_v) + nv * L.d_v);
+    return launch_bb<2>(L, a, stream);
+  }
+  return L.buf_bf16 ? launch_bb<1>(L, a, stream) : launch_bb<0>(L, a, stream);
 }
 
 }  // namespace gdnq

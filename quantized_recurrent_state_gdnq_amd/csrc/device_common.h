@@ -293,6 +293,33 @@ __device__ __forceinline__ float bload_f1s(rsrc_t r, uint32_t off, uint32_t soff
 __device__ __forceinline__ uint32_t bload_h1s(rsrc_t r, uint32_t off, uint32_t soff) {  // 16 bits, zero-extended
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
 }
+__device__ __forceinline__ uint32_t bload_b1s(rsrc_t r, uint32_t off, uint32_t soff) {  // 8 bits, zero-extended
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, soff, 0);
+}
+
+// Nearest OCP FP8 E4M3 value of q (1 sign bit, 4 exponent bits with bias 7,
+// 3 mantissa bits, largest finite 448), ties to even.  For |q| in
+// [2^e, 2^(e+1)), e >= -6, the grid step is 2^(e-3); below 2^-6 it is 2^-9.
+// Scaling by a power of two is exact, so rint (ties to even) on |q| / step
+// rounds exactly; the result is a grid value, which the hardware conversion
+// then encodes without rounding.  |q| <= 448 here (it saturates above).
+__device__ __forceinline__ float e4m3_round(float q) {
+  const float a = fabsf(q);
+  const int be = int((__float_as_uint(a) >> 23) & 0xFFu);  // 0 for zero and fp32 subnormals
+  const int e = be - 127 > -6 ? be - 127 : -6;
+  const float r = fminf(ldexpf(rintf(ldexpf(a, 3 - e)), e - 3), 448.f);
+  return copysignf(r, q);
+}
+// two E4M3 grid values -> their two bytes (low 16 bits); exact on grid values
+__device__ __forceinline__ uint32_t e4m3_pack2(float lo, float hi) {
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(lo, hi, 0, false)) & 0xFFFFu;
+}
+// bytes 0, 1 (sel false) or 2, 3 (sel true) of w -> two floats (exact)
+__device__ __forceinline__ float2 e4m3_unpack2(uint32_t w, bool sel) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 v = sel ? __builtin_amdgcn_cvt_pk_f32_fp8(int(w), true) : __builtin_amdgcn_cvt_pk_f32_fp8(int(w), false);
+  return make_float2(v[0], v[1]);
+}
 
 // XCD-aware workgroup id: workgroups are dispatched round-robin over the 8
 // XCDs, so block x runs on XCD x % 8.  This remaps ids so that consecutive

@@ -26,7 +26,7 @@ struct DecodeLaunch {
   const float* beta;
   int8_t* codes;
   float* scales;
-  void* buf_k;    // fp32, or bf16 with buf_bf16
+  void* buf_k;    // fp32, bf16 with buf_bf16, or E4M3 codes + per-vector scales with buf_fp8
   void* buf_v;
   float* buf_alpha;
   float* buf_beta;
@@ -34,7 +34,7 @@ struct DecodeLaunch {
   int32_t* fill_out;
   void* o;
   int B, H, d_k, d_v, W;
-  bool in_bf16, out_bf16, wht, buf_bf16;
+  bool in_bf16, out_bf16, wht, buf_bf16, buf_fp8;
 };
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 int decode_row_split();

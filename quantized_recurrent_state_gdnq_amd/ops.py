@@ -67,6 +67,10 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
     (both fp32, or both bf16 for the low-precision window buffer),
     buf_alpha, buf_beta [B,H,W] fp32 (slot fill_in[b] receives the write);
     fill_in, fill_out [B] int32 (distinct).  Returns o [B,H,d_v].
+
+    FP8 window buffer: buf_k, buf_v of dtype float8_e4m3fn, [B,H,W,d] views
+    at the start of buffers that continue with the per-vector fp32 scales
+    [B,H,W] (fp8_window_buffer() makes such a pair).
     """
     dev = q.device
     B, H, d_k = q.shape
@@ -77,11 +81,18 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
     for name, t in (("alpha", alpha), ("beta", beta), ("scales", scales),
                     ("buf_alpha", buf_alpha), ("buf_beta", buf_beta)):
         _need(t, name, torch.float32, dev)
-    if buf_k.dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("buf_k must be float32 or bfloat16")
+    if buf_k.dtype not in (torch.float32, torch.bfloat16, torch.float8_e4m3fn):
+        raise ValueError("buf_k must be float32, bfloat16 or float8_e4m3fn")
     _need(buf_k, "buf_k", buf_k.dtype, dev)
     _need(buf_v, "buf_v", buf_k.dtype, dev)
     buf_bf16 = buf_k.dtype == torch.bfloat16
+    buf_fp8 = buf_k.dtype == torch.float8_e4m3fn
+    if buf_fp8:
+        for name, t in (("buf_k", buf_k), ("buf_v", buf_v)):
+            need = t.numel() + 4 * (t.numel() // t.shape[-1])
+            if t.storage_offset() + need > t.untyped_storage().nbytes():
+                raise ValueError(f"{name}: an FP8 buffer must be followed in its allocation by "
+                                 "its fp32 scales (see fp8_window_buffer)")
     _need(codes, "codes", torch.int8, dev)
     _need(fill_in, "fill_in", torch.int32, dev)
     _need(fill_out, "fill_out", torch.int32, dev)
@@ -100,7 +111,8 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
             or fill_in.numel() != B or fill_out.numel() != B or tuple(o.shape) != (B, H, d_v)):
         raise ValueError("inconsistent decode shapes")
     p = _lib.DecodeParams(B, H, d_k, d_v, W, _DT[q.dtype], _DT[o.dtype],
-                          (_lib.GDNQ_FLAG_WHT if wht else 0) | (_lib.GDNQ_FLAG_BUF_BF16 if buf_bf16 else 0))
+                          (_lib.GDNQ_FLAG_WHT if wht else 0) | (_lib.GDNQ_FLAG_BUF_BF16 if buf_bf16 else 0)
+                          | (_lib.GDNQ_FLAG_BUF_FP8 if buf_fp8 else 0))
     args = (p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(codes), _ptr(scales),
             _ptr(buf_k), _ptr(buf_v), _ptr(buf_alpha), _ptr(buf_beta), _ptr(fill_in), _ptr(fill_out),
             _ptr(o), _stream(dev))
@@ -178,19 +190,36 @@ def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_code
     return o, codes, scales
 
 
+def fp8_window_buffer(B, H, W, d, device):
+    """One FP8 window buffer: E4M3 codes [B,H,W,d] followed, in the same
+    allocation, by the per-vector fp32 scales [B,H,W].  Returns (codes view,
+    scales view); pass the codes view as buf_k or buf_v."""
+    n = B * H * W
+    raw = torch.empty(n * d + 4 * n, dtype=torch.uint8, device=device)
+    codes = raw[:n * d].view(torch.float8_e4m3fn).view(B, H, W, d)
+    scales = raw[n * d:].view(torch.float32).view(B, H, W)
+    return codes, scales
+
+
 class DecodeState:
     """Per-request state of a batch of sequences: int8 codes, per-row scales,
     the window buffer and the fill counters (ping-ponged between two arrays,
     since every head of a sequence reads the fill while the step runs)."""
 
     def __init__(self, codes, scales, window, fill=None, wht=False, buf_dtype=torch.float32):
-        """buf_dtype: torch.float32 (the method's fp32 window buffer) or
-        torch.bfloat16 (the low-precision buffer: writes stored rounded)."""
+        """buf_dtype: torch.float32 (the method's fp32 window buffer),
+        torch.bfloat16 (writes stored rounded) or torch.float8_e4m3fn (FP8
+        vector pairs: E4M3 codes with a per-vector scale, buf_k_scale and
+        buf_v_scale)."""
         B, H, d_v, d_k = codes.shape
         dev = codes.device
         self.codes, self.scales, self.window, self.wht = codes, scales, window, wht
-        self.buf_k = torch.empty((B, H, window, d_k), dtype=buf_dtype, device=dev)
-        self.buf_v = torch.empty((B, H, window, d_v), dtype=buf_dtype, device=dev)
+        if buf_dtype == torch.float8_e4m3fn:
+            self.buf_k, self.buf_k_scale = fp8_window_buffer(B, H, window, d_k, dev)
+            self.buf_v, self.buf_v_scale = fp8_window_buffer(B, H, window, d_v, dev)
+        else:
+            self.buf_k = torch.empty((B, H, window, d_k), dtype=buf_dtype, device=dev)
+            self.buf_v = torch.empty((B, H, window, d_v), dtype=buf_dtype, device=dev)
         self.buf_alpha = torch.empty((B, H, window), dtype=torch.float32, device=dev)
         self.buf_beta = torch.empty((B, H, window), dtype=torch.float32, device=dev)
         self.fill = torch.zeros(B, dtype=torch.int32, device=dev) if fill is None else fill

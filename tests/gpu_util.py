@@ -27,7 +27,7 @@ def dev(x, dtype=None):
 
 
 def host(t):
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float8_e4m3fn):
         t = t.float()
     return t.detach().cpu().numpy()
 

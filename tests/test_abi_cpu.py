@@ -65,8 +65,8 @@ def _p(B=2, H=2, dk=128, dv=128, W=8, ind=1, outd=1, flags=0):
 
 @pytest.mark.parametrize("params,status", [
     (_p(dk=96), 2), (_p(dv=32), 2), (_p(B=1025), 2), (_p(W=0), 2), (_p(W=65), 2), (_p(H=0), 2), (_p(B=-1), 2),
-    (_p(ind=2), 3), (_p(outd=5), 3), (_p(flags=2), 8), (_p(flags=4), 8), (_p(flags=32), 8),
-    (_p(flags=16 | 2), 8),
+    (_p(ind=2), 3), (_p(outd=5), 3), (_p(flags=2), 8), (_p(flags=4), 8), (_p(flags=64), 8),
+    (_p(flags=16 | 2), 8), (_p(flags=16 | 32), 8),
 ])
 def test_decode_rejects_bad_params(params, status):
     a = _decode_args(Fake())
@@ -124,6 +124,24 @@ def test_decode_bf16_buffer_spans():
     assert b"buf_k overlaps buf_v" in L.gdnq_last_error()
 
 
+def test_decode_fp8_buffer_spans():
+    """Under GDNQ_FLAG_BUF_FP8 each window buffer holds one byte per entry
+    followed by one fp32 scale per vector: a buf_v placed right after
+    B*H*W*(d + 4) bytes of buf_k is disjoint from it, 16 bytes earlier it
+    overlaps the scales."""
+    B, H, d, W = 2, 2, 128, 8
+    a = _decode_args(Fake())
+    a["buf_v"] = a["buf_k"] + B * H * W * (d + 4)
+    a["o"] = a["fill_out"]
+    assert _decode(_p(flags=32), a) == 5
+    err = L.gdnq_last_error()
+    assert b"buf" not in err and b"fill_out overlaps o" in err, err
+    a = _decode_args(Fake())
+    a["buf_v"] = a["buf_k"] + B * H * W * (d + 4) - 16
+    assert _decode(_p(flags=32), a) == 5
+    assert b"buf_k overlaps buf_v" in L.gdnq_last_error()
+
+
 def test_decode_empty_batch_is_noop():
     a = {k: None for k in _decode_args(Fake())}
     assert _decode(_p(B=0), a) == 0
@@ -146,6 +164,7 @@ def _prefill(params, fake, **over):
 @pytest.mark.parametrize("params,status", [
     (_pp(C=32, W=32), 2), (_pp(T=100), 2), (_pp(dk=64, dv=64), 2), (_pp(W=128), 2),
     (_pp(ind=0), 3), (_pp(outd=3), 3), (_pp(flags=4), 8), (_pp(flags=8), 8), (_pp(flags=16), 8),
+    (_pp(flags=32), 8),
     (_pp(flags=1), 8),                   # GDN prefill takes no rotation flag
     (_pp(dv=64, flags=2 | 1), 8),        # SSD rotation only on the way to int8 operands
 ])
