@@ -215,6 +215,35 @@ gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, co
                                  int8_t* codes, float* scales, float* state_f32,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * gdnq_prefill_handoff -- GDN prefill of T tokens (any T >= 0) that leaves
+ *   its last, open window in decode's window buffer, so that
+ *   gdnq_decode_step continues the sequence.  LeapQuant, abstract (outputs
+ *   inside a window from the fixed low-bit state plus buffered writes;
+ *   requantize once at the window's end).
+ *
+ *   Same recurrence, parameters and layouts as gdnq_prefill_chunked in GDN
+ *   mode (flags 0, d_k = d_v = 128, chunk = window = 64, in_dtype bf16),
+ *   except that p->seqlen T need not be a multiple of 64.  With r = T mod 64:
+ *     o          [B,T,H,128] out_dtype, every token (written)
+ *     codes, scales: the state at the last window boundary (token T - r)
+ *     buf_k      [B,H,W,128] fp32     buf_v [B,H,W,128] fp32   (slots < r written)
+ *     buf_alpha, buf_beta [B,H,W] fp32                        (slots < r written)
+ *     fill_out   [B] int32 = r for every sequence (written)
+ *   i.e. exactly decode's state after its last r steps: a decode step with
+ *   fill_in = fill_out continues the sequence (fp32 window buffer).
+ *   workspace: gdnq_prefill_handoff_workspace_size(p) bytes.
+ *   Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, FLAGS, WORKSPACE, HIP.
+ * ------------------------------------------------------------------------ */
+size_t gdnq_prefill_handoff_workspace_size(const gdnq_prefill_params* p);
+
+gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const int8_t* init_codes, const float* init_scales, void* o,
+                                 int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                                 float* buf_alpha, float* buf_beta, int32_t* fill_out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Status text, last error detail (thread-local, "" if none), library version. */
 const char* gdnq_status_string(gdnq_status s);
 const char* gdnq_last_error(void);

@@ -22,7 +22,8 @@ GDNQ_FLAG_WHT, GDNQ_FLAG_SSD, GDNQ_FLAG_INT8_QK, GDNQ_FLAG_BUF_BF16, GDNQ_FLAG_B
 
 # Every function the header declares.
 EXPORTS = ("gdnq_quantize_state", "gdnq_decode_step", "gdnq_prefill_workspace_size",
-           "gdnq_prefill_chunked", "gdnq_status_string", "gdnq_last_error", "gdnq_version")
+           "gdnq_prefill_chunked", "gdnq_prefill_handoff_workspace_size", "gdnq_prefill_handoff",
+           "gdnq_status_string", "gdnq_last_error", "gdnq_version")
 
 
 class DecodeParams(ctypes.Structure):
@@ -65,6 +66,10 @@ def _load():
     lib.gdnq_prefill_workspace_size.restype = sz
     lib.gdnq_prefill_chunked.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 12 + [sz, vp]
     lib.gdnq_prefill_chunked.restype = i32
+    lib.gdnq_prefill_handoff_workspace_size.argtypes = [ctypes.POINTER(PrefillParams)]
+    lib.gdnq_prefill_handoff_workspace_size.restype = sz
+    lib.gdnq_prefill_handoff.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 16 + [sz, vp]
+    lib.gdnq_prefill_handoff.restype = i32
     lib.gdnq_status_string.argtypes = [i32]
     lib.gdnq_status_string.restype = ctypes.c_char_p
     lib.gdnq_last_error.argtypes = []
@@ -102,3 +107,14 @@ def prefill_chunked(params, q, k, v, alpha, beta, init_codes, init_scales, o, co
     return lib.gdnq_prefill_chunked(ctypes.byref(params), q, k, v, alpha, beta, init_codes,
                                     init_scales, o, codes, scales, state_f32, workspace,
                                     workspace_bytes, stream)
+
+
+def prefill_handoff_workspace_size(params):
+    return lib.gdnq_prefill_handoff_workspace_size(ctypes.byref(params))
+
+
+def prefill_handoff(params, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales,
+                    buf_k, buf_v, buf_alpha, buf_beta, fill_out, workspace, workspace_bytes, stream):
+    return lib.gdnq_prefill_handoff(ctypes.byref(params), q, k, v, alpha, beta, init_codes,
+                                    init_scales, o, codes, scales, buf_k, buf_v, buf_alpha,
+                                    buf_beta, fill_out, workspace, workspace_bytes, stream)

@@ -161,15 +161,19 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
   return hip_status(gdnq::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
-static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillLaunch& L) {
+static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillLaunch& L, bool handoff = false) {
   if (!p) return fail(GDNQ_ERR_NULL, "params is NULL");
   const int B = p->batch, T = p->seqlen, H = p->heads, dk = p->d_k, dv = p->d_v;
   if (B < 0 || T < 0 || H < 1) return fail(GDNQ_ERR_SHAPE, "batch = %d, seqlen = %d, heads = %d", B, T, H);
   if (p->in_dtype != GDNQ_BF16) return fail(GDNQ_ERR_DTYPE, "prefill in_dtype must be GDNQ_BF16");
   if (p->out_dtype != GDNQ_F32 && p->out_dtype != GDNQ_BF16) return fail(GDNQ_ERR_DTYPE, "out_dtype = %d", p->out_dtype);
   if (p->chunk != 64) return fail(GDNQ_ERR_SHAPE, "chunk = %d, expected 64", p->chunk);
-  if (T % 64) return fail(GDNQ_ERR_SHAPE, "seqlen = %d is not a multiple of the chunk (64)", T);
+  if (T % 64 && !handoff) return fail(GDNQ_ERR_SHAPE, "seqlen = %d is not a multiple of the chunk (64)", T);
+  if (int64_t(T) * H * 512 >= (int64_t(1) << 32))
+    return fail(GDNQ_ERR_SHAPE, "seqlen * heads = %lld: one sequence's outputs must stay under 4 GiB",
+                (long long)T * H);
   const bool ssd = (p->flags & GDNQ_FLAG_SSD) != 0;
+  if (ssd && handoff) return fail(GDNQ_ERR_FLAGS, "the hand-over to decode is for the GDN recurrence (no GDNQ_FLAG_SSD)");
   if (ssd) {
     if (p->flags & ~uint32_t(GDNQ_FLAG_SSD | GDNQ_FLAG_WHT | GDNQ_FLAG_INT8_QK))
       return fail(GDNQ_ERR_FLAGS, "flags 0x%x", p->flags);
@@ -188,6 +192,7 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   L.wht = (p->flags & GDNQ_FLAG_WHT) != 0;
   L.ssd = ssd;
   L.int8_qk = (p->flags & GDNQ_FLAG_INT8_QK) != 0;
+  L.handoff = handoff;
   return GDNQ_OK;
 }
 
@@ -260,6 +265,59 @@ gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_hip_error();
   return hip_status(L.ssd ? gdnq::launch_prefill_ssd(L, s) : gdnq::launch_prefill_gdn(L, s), "prefill launch");
+}
+
+size_t gdnq_prefill_handoff_workspace_size(const gdnq_prefill_params* p) {
+  gdnq::PrefillLaunch L;
+  if (prefill_validate(p, L, true) != GDNQ_OK) return 0;
+  return gdnq::prefill_workspace_bytes(L);
+}
+
+gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const int8_t* init_codes, const float* init_scales, void* o,
+                                 int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                                 float* buf_alpha, float* buf_beta, int32_t* fill_out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  gdnq::PrefillLaunch L;
+  if (gdnq_status st = prefill_validate(p, L, true)) return st;
+  if (L.B == 0) return ok();
+  const size_t bth = size_t(L.B) * L.T * L.H, bh = size_t(L.B) * L.H;
+  const size_t eo = L.out_bf16 ? 2 : 4, W = size_t(L.W);
+  if ((init_codes == nullptr) != (init_scales == nullptr))
+    return fail(GDNQ_ERR_NULL, "init_codes and init_scales must be both NULL or both set");
+  const Span sp[] = {{"q", q, bth * L.d_k * 2},          {"k", k, bth * L.d_k * 2},
+                     {"v", v, bth * L.d_v * 2},          {"alpha", alpha, bth * 4},
+                     {"beta", beta, bth * 4},            {"o", o, bth * L.d_v * eo},
+                     {"codes", codes, bh * L.d_v * L.d_k}, {"scales", scales, bh * L.d_v * 4},
+                     {"buf_k", buf_k, bh * W * L.d_k * 4}, {"buf_v", buf_v, bh * W * L.d_v * 4},
+                     {"buf_alpha", buf_alpha, bh * W * 4}, {"buf_beta", buf_beta, bh * W * 4},
+                     {"fill_out", fill_out, size_t(L.B) * 4}};
+  constexpr int N = sizeof(sp) / sizeof(sp[0]);
+  if (L.T > 0) {
+    if (gdnq_status st = check_ptrs(sp, N)) return st;
+  } else {
+    if (gdnq_status st = check_ptrs(sp + 6, N - 6)) return st;
+  }
+  if (init_codes) {
+    const Span ip[] = {{"init_codes", init_codes, bh * L.d_v * L.d_k}, {"init_scales", init_scales, bh * L.d_v * 4}};
+    if (gdnq_status st = check_ptrs(ip, 2)) return st;
+    if (init_codes != codes && overlap(ip[0], sp[6])) return fail(GDNQ_ERR_ALIAS, "init_codes partially overlaps codes");
+    if (init_scales != scales && overlap(ip[1], sp[7])) return fail(GDNQ_ERR_ALIAS, "init_scales partially overlaps scales");
+  }
+  for (int i = 5; i < N; ++i)  // every written buffer is disjoint from every other
+    for (int j = 0; j < N; ++j)
+      if (j != i && overlap(sp[i], sp[j])) return fail(GDNQ_ERR_ALIAS, "%s overlaps %s", sp[i].name, sp[j].name);
+  const size_t need = gdnq::prefill_workspace_bytes(L);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(GDNQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace_bytes);
+  if (workspace && !aligned16(workspace)) return fail(GDNQ_ERR_ALIGN, "workspace is not 16-byte aligned");
+  L.q = q; L.k = k; L.v = v; L.alpha = alpha; L.beta = beta; L.o = o;
+  L.init_codes = init_codes; L.init_scales = init_scales; L.codes = codes; L.scales = scales;
+  L.workspace = workspace;
+  L.buf_k = buf_k; L.buf_v = buf_v; L.buf_alpha = buf_alpha; L.buf_beta = buf_beta; L.fill_out = fill_out;
+  clear_stale_hip_error();
+  return hip_status(gdnq::launch_prefill_gdn(L, static_cast<hipStream_t>(stream)), "prefill hand-over launch");
 }
 
 }  // extern "C"

@@ -53,8 +53,13 @@ struct PrefillLaunch {
   float* scales;
   float* state_f32;
   void* workspace;
+  float* buf_k;  // hand-over to decode (GDN): the open window's writes and the fill
+  float* buf_v;
+  float* buf_alpha;
+  float* buf_beta;
+  int32_t* fill_out;
   int B, T, H, d_k, d_v, C, W;
-  bool out_bf16, wht, ssd, int8_qk;
+  bool out_bf16, wht, ssd, int8_qk, handoff;
 };
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream);
 hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream);

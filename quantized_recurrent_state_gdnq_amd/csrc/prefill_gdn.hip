@@ -9,7 +9,12 @@
 //   O    = diag(gamma) Q S0^T + (L o Q K^T) U,        L_ij = exp(g_i - g_j), j <= i
 //   S_C  = gamma_C S0 + U^T diag(exp(g_C - g)) K
 // With the window equal to the chunk, S0 is always a dequantized state
-// (codes * row scale) and S_C is requantized at every chunk end.
+// (codes * row scale) and S_C is requantized at every chunk end.  A last
+// chunk of r < 64 tokens (a sequence handed over to decode with its window
+// still open) is padded with k = 0, alpha = 1, beta = 0, which leaves T's
+// valid block, U and O of the valid tokens unchanged; its state update and
+// requantization are skipped, so the stored state stays at the last window
+// boundary.
 //
 // Two kernels:
 //   prep  -- one workgroup per chunk-head, all in parallel: K K^T on bf16
@@ -71,7 +76,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
   __bf16* Kl = reinterpret_cast<__bf16*>(kt_raw);
   float* Tl = reinterpret_cast<float*>(kt_raw);
   float* Pl = Tl + PC * PC;
-  const int NC = a.T / PC;
+  const int NC = (a.T + PC - 1) / PC;
   const int idx = blockIdx.x;  // (b * NC + c) * H + h
   const int h = idx % a.H;
   const int c = (idx / a.H) % NC;
@@ -80,20 +85,22 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
   const int lr = lane & 15, lq = lane >> 4;
   const size_t tok0 = size_t(b) * a.T + size_t(c) * PC;
 
-  {  // keys of the chunk: thread -> token tid / 4, dims [(tid % 4) * 32, +32)
+  const int nvalid = a.T - c * PC;  // tokens of this chunk in the sequence (< 64 only in a last, partial chunk)
+  {  // keys of the chunk: thread -> token tid / 4, dims [(tid % 4) * 32, +32); padding keys are 0
     const int i = tid >> 2, qq = tid & 3;
-    const uint4* src = reinterpret_cast<const uint4*>(a.k + ((tok0 + i) * a.H + h) * PD + qq * 32);
+    const int ic = i < nvalid ? i : nvalid - 1;
+    const uint4* src = reinterpret_cast<const uint4*>(a.k + ((tok0 + ic) * a.H + h) * PD + qq * 32);
     uint4 w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = src[e];
+    for (int e = 0; e < 4; ++e) w[e] = i < nvalid ? src[e] : make_uint4(0u, 0u, 0u, 0u);
     uint4* dst = reinterpret_cast<uint4*>(Kl + i * KP + qq * 32);
 #pragma unroll
     for (int e = 0; e < 4; ++e) dst[e] = w[e];
   }
-  if (tid < 64) {  // g = inclusive prefix sum of log alpha
-    const size_t r = (tok0 + tid) * a.H + h;
-    float la = logf(a.alpha[r]);
-    bl[tid] = a.beta[r];
+  if (tid < 64) {  // g = inclusive prefix sum of log alpha (padding: alpha = 1, beta = 0)
+    const size_t r = (tok0 + (tid < nvalid ? tid : nvalid - 1)) * a.H + h;
+    float la = tid < nvalid ? logf(a.alpha[r]) : 0.f;
+    bl[tid] = tid < nvalid ? a.beta[r] : 0.f;
 #pragma unroll
     for (int s = 1; s < 64; s <<= 1) {
       const float o = __shfl_up(la, s, 64);
@@ -301,7 +308,8 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   const int r0 = rb * RWS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  const int NC = a.T / PC;
+  const int NC = (a.T + PC - 1) / PC;
+  const bool partial_last = (a.T % PC) != 0;  // the last chunk holds fewer than 64 tokens
   const size_t HD = size_t(a.H) * PD;
   const size_t state_row0 = (size_t(b) * a.H + h) * PD + r0;
   const size_t tokb = size_t(b) * a.T;
@@ -425,8 +433,10 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
       }
       __syncthreads();
 
-      // ---- C: new rows S_C^T = gamma_C S0^T + K^T (U o d)
-      {
+      // ---- C: new rows S_C^T = gamma_C S0^T + K^T (U o d) (not for a partial last chunk:
+      //      its window stays open and the stored state stays at the last boundary)
+      const bool update = !(partial_last && c == NC - 1);
+      if (update) {
         const int dt0 = (wave >> 1) * 2;
         bf16x8 u1[2], u2[2], u3[2];
 #pragma unroll
@@ -461,7 +471,7 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
       __syncthreads();
 
       // ---- D: requantize the new rows
-      {
+      if (update) {
         const int rq = tid >> 4, seg = tid & 15;
         const float4 s0 = *reinterpret_cast<const float4*>(Sn + rq * SNP + seg * 8);
         const float4 s1 = *reinterpret_cast<const float4*>(Sn + rq * SNP + seg * 8 + 4);
@@ -503,14 +513,18 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   const int pm = st & 31, ps = st >> 5;
   const int ti = st >> 3, tc = st & 7;
   const int vr = (sw & 1) * 16 + lr, vi = (sw >> 1) * 16 + 4 * lq;
-  const uint16_t* kb = a.k + (tokb + 2 * pm) * HD + size_t(h) * PD + 8 * ps;
-  const uint16_t* qb = a.q + (tokb + 2 * pm) * HD + size_t(h) * PD + 8 * ps;
-  const uint16_t* vb = a.v + (tokb + vi) * HD + size_t(h) * PD + r0 + vr;
+  const uint16_t* kb = a.k + tokb * HD + size_t(h) * PD + 8 * ps;
+  const uint16_t* qb = a.q + tokb * HD + size_t(h) * PD + 8 * ps;
+  const uint16_t* vb = a.v + tokb * HD + size_t(h) * PD + r0 + vr;
   const __bf16* tb = a.T_ws + (size_t(b) * NC * a.H + h) * 3 * PC * PC + ti * PC + 8 * tc;
   const float* gb = a.g_ws + (size_t(b) * NC * a.H + h) * PC + (st & 63);
-  const float* bb = a.beta + (tokb + (st & 63)) * a.H + h;
-  const size_t tok_step = PC * HD;                   // q/k/v elements per chunk
+  const float* bb = a.beta + tokb * a.H + h;
   const size_t ch_step = size_t(a.H) * 3 * PC * PC;  // T elements per chunk (all heads)
+  // token i of chunk c: whether it is in the sequence, and the token loads
+  // read (clamped into the sequence; padding is zeroed when staged)
+  auto tok_ok = [&](int c, int i) { return c * PC + i < a.T; };
+  auto tok_ld = [&](int c, int i) { return size_t(c * PC + i < a.T ? c * PC + i : a.T - 1); };
+  int kq_c = 0, tv_c = 0;  // the chunks the prefetch registers hold
 
   // (clang vector types: arrays of HIP's uint4 are copied through memory)
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -519,28 +533,30 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   uint32_t v4[4];
   float gv = 0.f, bv = 0.f;
   auto load_kq = [&](int c) {
-    const size_t o = size_t(c) * tok_step;
-    k0 = *reinterpret_cast<const u32x4*>(kb + o);
-    k1 = *reinterpret_cast<const u32x4*>(kb + o + HD);
-    q0 = *reinterpret_cast<const u32x4*>(qb + o);
-    q1 = *reinterpret_cast<const u32x4*>(qb + o + HD);
+    kq_c = c;
+    k0 = *reinterpret_cast<const u32x4*>(kb + tok_ld(c, 2 * pm) * HD);
+    k1 = *reinterpret_cast<const u32x4*>(kb + tok_ld(c, 2 * pm + 1) * HD);
+    q0 = *reinterpret_cast<const u32x4*>(qb + tok_ld(c, 2 * pm) * HD);
+    q1 = *reinterpret_cast<const u32x4*>(qb + tok_ld(c, 2 * pm + 1) * HD);
   };
   auto load_tv = [&](int c) {
+    tv_c = c;
     const __bf16* tp = tb + size_t(c) * ch_step;
     t0 = *reinterpret_cast<const u32x4*>(tp);
     t1 = *reinterpret_cast<const u32x4*>(tp + PC * PC);
     t2 = *reinterpret_cast<const u32x4*>(tp + 2 * PC * PC);
-    const size_t o = size_t(c) * tok_step;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v4[q] = vb[o + q * HD];
+    for (int q = 0; q < 4; ++q) v4[q] = vb[tok_ld(c, vi + q) * HD];
     gv = gb[size_t(c) * a.H * PC];  // every side lane loads (one wave's worth is used): no branch
-    bv = bb[size_t(c) * PC * a.H];
+    bv = bb[tok_ld(c, st & 63) * a.H];
   };
   auto stage_kq = [&]() {
-    *reinterpret_cast<u32x4*>(Kl + (2 * pm) * KP + 8 * ps) = k0;
-    *reinterpret_cast<u32x4*>(Kl + (2 * pm + 1) * KP + 8 * ps) = k1;
-    *reinterpret_cast<u32x4*>(Ql + (2 * pm) * KP + 8 * ps) = q0;
-    *reinterpret_cast<u32x4*>(Ql + (2 * pm + 1) * KP + 8 * ps) = q1;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const bool ok0 = tok_ok(kq_c, 2 * pm), ok1 = tok_ok(kq_c, 2 * pm + 1);
+    *reinterpret_cast<u32x4*>(Kl + (2 * pm) * KP + 8 * ps) = ok0 ? k0 : z;
+    *reinterpret_cast<u32x4*>(Kl + (2 * pm + 1) * KP + 8 * ps) = ok1 ? k1 : z;
+    *reinterpret_cast<u32x4*>(Ql + (2 * pm) * KP + 8 * ps) = ok0 ? q0 : z;
+    *reinterpret_cast<u32x4*>(Ql + (2 * pm + 1) * KP + 8 * ps) = ok1 ? q1 : z;
   };
   auto stage_tv = [&](int par) {
     *reinterpret_cast<u32x4*>(Tp + ti * TP + 8 * tc) = t0;
@@ -548,12 +564,15 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
     *reinterpret_cast<u32x4*>(Tp + 2 * PC * TP + ti * TP + 8 * tc) = t2;
     // V^T of the chain lane's (row, 4 tokens) into the slots of the first rhs^T
     // plane: the chain lane reads them back and overwrites them with rhs
-    *reinterpret_cast<uint2*>(Rp + vr * TP + vi) = make_uint2(v4[0] | (v4[1] << 16), v4[2] | (v4[3] << 16));
+    uint32_t vz[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vz[q] = tok_ok(tv_c, vi + q) ? v4[q] : 0u;
+    *reinterpret_cast<uint2*>(Rp + vr * TP + vi) = make_uint2(vz[0] | (vz[1] << 16), vz[2] | (vz[3] << 16));
     if (st < 64) {
       float* gp = G + 192 * par;
       gp[st] = gv;
       gp[64 + st] = expf(gv);
-      gp[128 + st] = bv;
+      gp[128 + st] = tok_ok(tv_c, st) ? bv : 0.f;  // padding: beta = 0
     }
   };
   // K^T of the staged K (tokens 2 pm, 2 pm + 1 of dims [8 ps, +8) per thread)
@@ -582,8 +601,10 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   __syncthreads();
 
   const int it = sw >> 1, i0 = it * 16 + 4 * lq, nks = (it >> 1) + 1;
+  // this sequence's outputs, bounded at its T tokens
+  const rsrc_t o_rsrc = make_rsrc(static_cast<char*>(a.o) + tokb * HD * (OUT_BF16 ? 2 : 4),
+                                  uint32_t(size_t(a.T) * HD * (OUT_BF16 ? 2 : 4)));
   for (int c = 0; c < NC; ++c) {
-    const size_t tok0 = tokb + size_t(c) * PC;
     const float* gc = G + 192 * (c & 1);
     // ---- A: output base diag(gamma s) Q S0^T of this wave's (token tile, row tile)
     float os[4];
@@ -624,11 +645,13 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
         acc = mfma16(m1, v1, acc);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const size_t oi = (tok0 + i0 + q) * HD + size_t(h) * PD + r0 + vr;
+      for (int q = 0; q < 4; ++q) {  // stores past the sequence (padding tokens) are dropped
+        const uint32_t oi = uint32_t((size_t(c) * PC + i0 + q) * HD + size_t(h) * PD + r0 + vr);
         const float ov = os[q] + acc[q];
-        if constexpr (OUT_BF16) static_cast<uint16_t*>(a.o)[oi] = uint16_t(f32_to_bf16_bits(ov));
-        else static_cast<float*>(a.o)[oi] = ov;
+        if constexpr (OUT_BF16)
+          __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(ov)), o_rsrc, oi * 2, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), o_rsrc, oi * 4, 0, 0);
       }
     }
     stage_tv((c + 1) & 1);
@@ -646,15 +669,50 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   }
 }
 
-static size_t gdn_ws_T(const PrefillLaunch& L) { return size_t(L.B) * (L.T / PC) * L.H * 3 * PC * PC * 2; }
-static size_t gdn_ws_g(const PrefillLaunch& L) { return size_t(L.B) * (L.T / PC) * L.H * PC * 4; }
+static int gdn_chunks(const PrefillLaunch& L) { return (L.T + PC - 1) / PC; }
+static size_t gdn_ws_T(const PrefillLaunch& L) { return size_t(L.B) * gdn_chunks(L) * L.H * 3 * PC * PC * 2; }
+static size_t gdn_ws_g(const PrefillLaunch& L) { return size_t(L.B) * gdn_chunks(L) * L.H * PC * 4; }
+
+// Hand-over to decode: the last r = T mod 64 tokens' writes go to slots
+// 0 .. r-1 of the window buffer (fp32, keys in the state's basis) and every
+// sequence's fill becomes r.  One workgroup per (sequence, head).
+struct HandoffArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* alpha;
+  const float* beta;
+  float* buf_k;
+  float* buf_v;
+  float* buf_alpha;
+  float* buf_beta;
+  int32_t* fill_out;
+  int B, T, H, W;
+};
+
+__global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
+  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  const int r = a.T % PC, t0 = a.T - r;
+  for (int e = threadIdx.x; e < r * PD; e += 256) {
+    const int slot = e / PD, d = e % PD;
+    const size_t src = ((size_t(b) * a.T + t0 + slot) * a.H + h) * PD + d;
+    const size_t dst = (size_t(bh) * a.W + slot) * PD + d;
+    a.buf_k[dst] = __uint_as_float(uint32_t(a.k[src]) << 16);
+    a.buf_v[dst] = __uint_as_float(uint32_t(a.v[src]) << 16);
+  }
+  for (int slot = threadIdx.x; slot < r; slot += 256) {
+    const size_t src = (size_t(b) * a.T + t0 + slot) * a.H + h;
+    a.buf_alpha[size_t(bh) * a.W + slot] = a.alpha[src];
+    a.buf_beta[size_t(bh) * a.W + slot] = a.beta[src];
+  }
+  if (h == 0 && threadIdx.x == 0) a.fill_out[b] = r;
+}
 
 size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L) { return gdn_ws_T(L) + gdn_ws_g(L); }
 
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
   __bf16* T_ws = static_cast<__bf16*>(L.workspace);
   float* g_ws = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + gdn_ws_T(L));
-  const int NC = L.T / PC;
+  const int NC = gdn_chunks(L);
   if (NC > 0) {
     PrepArgs p{static_cast<const uint16_t*>(L.k), L.alpha, L.beta, T_ws, g_ws, L.B, L.T, L.H};
     hipLaunchKernelGGL(gdn_prep_kernel, dim3(unsigned(L.B) * NC * L.H), dim3(256), 0, stream, p);
@@ -669,7 +727,14 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
                                          hipFuncAttributeMaxDynamicSharedMemorySize, STATE_LDS))
     return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(SNT), STATE_LDS, stream, s);
-  return hipGetLastError();
+  if (hipError_t e = hipGetLastError()) return e;
+  if (L.handoff && L.B > 0) {
+    HandoffArgs h{static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v), L.alpha, L.beta,
+                  L.buf_k, L.buf_v, L.buf_alpha, L.buf_beta, L.fill_out, L.B, L.T, L.H, L.W};
+    hipLaunchKernelGGL(gdn_handoff_kernel, dim3(unsigned(L.B) * L.H), dim3(256), 0, stream, h);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace gdnq

@@ -190,6 +190,42 @@ def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_code
     return o, codes, scales
 
 
+def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_scales=None,
+                    out_dtype=torch.bfloat16):
+    """GDN prefill of any T tokens handed over to decode (see
+    gdnq_prefill_handoff in include/gdnq.h): returns (o, DecodeState) whose
+    codes/scales are the state at the last window boundary and whose fp32
+    window buffer holds the last T mod 64 writes, with that fill."""
+    dev = q.device
+    B, T, H, d_k = q.shape
+    d_v = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, dev)
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        _need(t, name, torch.float32, dev)
+    if (tuple(k.shape) != (B, T, H, d_k) or tuple(v.shape) != (B, T, H, d_v)
+            or tuple(alpha.shape) != (B, T, H) or tuple(beta.shape) != (B, T, H)):
+        raise ValueError("inconsistent prefill shapes")
+    p = _prefill_params(q, v, window=window, chunk=64, wht=False, ssd=False, int8_qk=False,
+                        out_dtype=out_dtype)
+    o = torch.empty((B, T, H, d_v), dtype=out_dtype, device=dev)
+    codes = torch.empty((B, H, d_v, d_k), dtype=torch.int8, device=dev)
+    scales = torch.empty((B, H, d_v), dtype=torch.float32, device=dev)
+    if init_codes is not None:
+        _need(init_codes, "init_codes", torch.int8, dev)
+        _need(init_scales, "init_scales", torch.float32, dev)
+    st = DecodeState(codes, scales, window, fill=torch.zeros(B, dtype=torch.int32, device=dev))
+    need = int(_lib.prefill_handoff_workspace_size(p))
+    workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _lib.check(_lib.prefill_handoff(p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                    _ptr(init_codes), _ptr(init_scales), _ptr(o), _ptr(codes),
+                                    _ptr(scales), _ptr(st.buf_k), _ptr(st.buf_v),
+                                    _ptr(st.buf_alpha), _ptr(st.buf_beta), _ptr(st.fill),
+                                    _ptr(workspace), ws_bytes, _stream(dev)))
+    return o, st
+
+
 def fp8_window_buffer(B, H, W, d, device):
     """One FP8 window buffer: E4M3 codes [B,H,W,d] followed, in the same
     allocation, by the per-vector fp32 scales [B,H,W].  Returns (codes view,

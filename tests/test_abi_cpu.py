@@ -219,3 +219,42 @@ def test_quantize_validation():
     assert L.gdnq_quantize_state(f() + 8, 4, 128, f(), f(), 0, None) == 4
     s = f()
     assert L.gdnq_quantize_state(s, 4, 128, s, f(), 0, None) == 5
+
+
+# ---------------------------------------------------------------- prefill hand-over to decode
+def _handoff(params, fake, **over):
+    a = dict(q=fake(), k=fake(), v=fake(), alpha=fake(), beta=fake(), init_codes=None,
+             init_scales=None, o=fake(), codes=fake(), scales=fake(), buf_k=fake(), buf_v=fake(),
+             buf_alpha=fake(), buf_beta=fake(), fill_out=fake(), workspace=None, ws=0)
+    a.update(over)
+    return _lib.prefill_handoff(params, a["q"], a["k"], a["v"], a["alpha"], a["beta"],
+                                a["init_codes"], a["init_scales"], a["o"], a["codes"], a["scales"],
+                                a["buf_k"], a["buf_v"], a["buf_alpha"], a["buf_beta"],
+                                a["fill_out"], a["workspace"], a["ws"], None)
+
+
+@pytest.mark.parametrize("params,status", [
+    (_pp(C=32, W=32), 2), (_pp(dk=64, dv=64), 2), (_pp(W=128), 2), (_pp(ind=0), 3),
+    (_pp(flags=1), 8), (_pp(dv=64, flags=2 | 1 | 4), 8),   # GDN only
+    (_pp(T=1 << 20, H=8192), 2),                           # one sequence's outputs past 4 GiB
+])
+def test_handoff_rejects_bad_params(params, status):
+    assert _handoff(params, Fake()) == status
+
+
+def test_handoff_contract():
+    """Any seqlen is accepted (T = 100 is not a whole number of chunks);
+    every pointer is required, written buffers are disjoint, and the
+    workspace covers ceil(T / 64) chunks."""
+    f = Fake()
+    p = _pp(B=2, T=100, H=3)
+    assert _lib.prefill_handoff_workspace_size(p) == 2 * 2 * 3 * (3 * 64 * 64 * 2 + 64 * 4)
+    assert _handoff(p, f) == 6                                  # workspace missing
+    assert _handoff(p, f, fill_out=None) == 1
+    assert _handoff(p, f, buf_alpha=None) == 1
+    o = f()
+    assert _handoff(p, f, o=o, buf_k=o) == 5                    # buffer over an output
+    k = f()
+    assert _handoff(p, f, k=k, fill_out=k) == 5                 # output over an input
+    assert _handoff(_pp(B=0, T=100), f) == 0                    # empty batch: no-op
+    assert _lib.prefill_workspace_size(p) == 0                  # the chunked prefill rejects T = 100
