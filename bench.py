@@ -219,8 +219,10 @@ def bench_prefill(torch, ops, wl, steps=5, warmup=2):
     cases = [
         ("gdn_prefill", dict(B=4, T=8192, H=16, dk=128, dv=128), False),
         ("ssd_prefill", dict(B=2, T=4096, H=80, dk=128, dv=64), True),
+        ("gdn_prefill_handoff", dict(B=4, T=8192 + 37, H=16, dk=128, dv=128), False),
     ]
     for name, shp, ssd in cases:
+        handoff = name.endswith("handoff")
         x = (wl.ssd_prefill if ssd else wl.gdn_prefill)(**shp, seed=0)
         q = torch.from_numpy(x["q"]).to(dev).bfloat16()
         k = torch.from_numpy(x["k"]).to(dev).bfloat16()
@@ -228,25 +230,34 @@ def bench_prefill(torch, ops, wl, steps=5, warmup=2):
         a = torch.from_numpy(x["alpha"]).to(dev)
         bt = None if ssd else torch.from_numpy(x["beta"]).to(dev)
         del x
-        kw = dict(ssd=True, wht=True, int8_qk=True) if ssd else dict(window=64)
-        kw["workspace"] = torch.empty(ops.prefill_workspace_size(q, v, **kw), dtype=torch.uint8, device=dev)
         Bq, T, Hh, dk = q.shape
         dv = v.shape[-1]
-        kw["o"] = torch.empty((Bq, T, Hh, dv), dtype=torch.bfloat16, device=dev)
-        if ssd:
-            kw["state_f32"] = torch.empty((Bq, Hh, dv, dk), dtype=torch.float32, device=dev)
+        if handoff:  # the open last window (T mod 64 writes) goes to decode's buffer
+            kw = dict(o=torch.empty((Bq, T, Hh, dv), dtype=torch.bfloat16, device=dev))
+            _, kw["state"] = ops.prefill_handoff(q, k, v, a, bt, **kw)
+            call = ops.prefill_handoff
         else:
-            kw["codes"] = torch.empty((Bq, Hh, dv, dk), dtype=torch.int8, device=dev)
-            kw["scales"] = torch.empty((Bq, Hh, dv), dtype=torch.float32, device=dev)
+            kw = dict(ssd=True, wht=True, int8_qk=True) if ssd else dict(window=64)
+            kw["workspace"] = torch.empty(ops.prefill_workspace_size(q, v, **kw), dtype=torch.uint8, device=dev)
+            kw["o"] = torch.empty((Bq, T, Hh, dv), dtype=torch.bfloat16, device=dev)
+            if ssd:
+                kw["state_f32"] = torch.empty((Bq, Hh, dv, dk), dtype=torch.float32, device=dev)
+            else:
+                kw["codes"] = torch.empty((Bq, Hh, dv, dk), dtype=torch.int8, device=dev)
+                kw["scales"] = torch.empty((Bq, Hh, dv), dtype=torch.float32, device=dev)
+            call = ops.prefill_chunked
+        if handoff:
+            kw["workspace"] = torch.empty(ops.prefill_handoff_workspace_size(q, v), dtype=torch.uint8,
+                                          device=dev)
         for _ in range(warmup):
-            ops.prefill_chunked(q, k, v, a, bt, **kw)
+            call(q, k, v, a, bt, **kw)
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream(dev)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
-            ops.prefill_chunked(q, k, v, a, bt, **kw)
+            call(q, k, v, a, bt, **kw)
         e1.record(stream)
         e1.synchronize()
         ms = e0.elapsed_time(e1) / steps
@@ -256,7 +267,9 @@ def bench_prefill(torch, ops, wl, steps=5, warmup=2):
         gbps = nbytes / (ms * 1e-3) / 1e9
         res[name] = {
             "workload": (f"B={Bq} T={T} H={Hh} d_k={dk} d_v={dv} chunk=64"
-                         + (" WHT+int8 q/k, fp32 state" if ssd else " window=64, int8 state")),
+                         + (" WHT+int8 q/k, fp32 state" if ssd else " window=64, int8 state")
+                         + (f", the last {T % 64} tokens' writes handed to decode's window buffer"
+                            if handoff else "")),
             "ms": round(ms, 4), "tokens_s": round(Bq * T / (ms * 1e-3), 1),
             "tflops": round(tflops, 2), "gbps": round(gbps, 1),
             "flops_per_call": flops, "bytes_per_call": nbytes,

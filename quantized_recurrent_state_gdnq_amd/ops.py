@@ -190,12 +190,20 @@ def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_code
     return o, codes, scales
 
 
+def prefill_handoff_workspace_size(q, v, *, window=64, out_dtype=torch.bfloat16):
+    p = _prefill_params(q, v, window=window, chunk=64, wht=False, ssd=False, int8_qk=False,
+                        out_dtype=out_dtype)
+    return int(_lib.prefill_handoff_workspace_size(p))
+
+
 def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_scales=None,
-                    out_dtype=torch.bfloat16):
+                    out_dtype=torch.bfloat16, o=None, state=None, workspace=None):
     """GDN prefill of any T tokens handed over to decode (see
     gdnq_prefill_handoff in include/gdnq.h): returns (o, DecodeState) whose
     codes/scales are the state at the last window boundary and whose fp32
-    window buffer holds the last T mod 64 writes, with that fill."""
+    window buffer holds the last T mod 64 writes, with that fill.  o, state
+    (a DecodeState with an fp32 buffer) and workspace may be given to reuse
+    their memory."""
     dev = q.device
     B, T, H, d_k = q.shape
     d_v = v.shape[-1]
@@ -208,19 +216,26 @@ def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_sc
         raise ValueError("inconsistent prefill shapes")
     p = _prefill_params(q, v, window=window, chunk=64, wht=False, ssd=False, int8_qk=False,
                         out_dtype=out_dtype)
-    o = torch.empty((B, T, H, d_v), dtype=out_dtype, device=dev)
-    codes = torch.empty((B, H, d_v, d_k), dtype=torch.int8, device=dev)
-    scales = torch.empty((B, H, d_v), dtype=torch.float32, device=dev)
+    if o is None:
+        o = torch.empty((B, T, H, d_v), dtype=out_dtype, device=dev)
+    _need(o, "o", out_dtype, dev)
     if init_codes is not None:
         _need(init_codes, "init_codes", torch.int8, dev)
         _need(init_scales, "init_scales", torch.float32, dev)
-    st = DecodeState(codes, scales, window, fill=torch.zeros(B, dtype=torch.int32, device=dev))
+    st = state
+    if st is None:
+        st = DecodeState(torch.empty((B, H, d_v, d_k), dtype=torch.int8, device=dev),
+                         torch.empty((B, H, d_v), dtype=torch.float32, device=dev), window,
+                         fill=torch.zeros(B, dtype=torch.int32, device=dev))
+    if st.buf_k.dtype != torch.float32 or tuple(st.codes.shape) != (B, H, d_v, d_k):
+        raise ValueError("state: a DecodeState of matching shape with an fp32 window buffer")
     need = int(_lib.prefill_handoff_workspace_size(p))
-    workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
-    ws_bytes = 0 if workspace is None else workspace.numel()
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _lib.check(_lib.prefill_handoff(p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                    _ptr(init_codes), _ptr(init_scales), _ptr(o), _ptr(codes),
-                                    _ptr(scales), _ptr(st.buf_k), _ptr(st.buf_v),
+                                    _ptr(init_codes), _ptr(init_scales), _ptr(o), _ptr(st.codes),
+                                    _ptr(st.scales), _ptr(st.buf_k), _ptr(st.buf_v),
                                     _ptr(st.buf_alpha), _ptr(st.buf_beta), _ptr(st.fill),
                                     _ptr(workspace), ws_bytes, _stream(dev)))
     return o, st
