@@ -244,6 +244,40 @@ gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, co
                                  float* buf_alpha, float* buf_beta, int32_t* fill_out,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * gdnq_prefill_varlen -- gdnq_prefill_handoff over a packed batch of
+ *   sequences of different lengths (LeapQuant, abstract: the same
+ *   recurrence, window buffer and boundary requantization per sequence).
+ *
+ *   p->batch B = number of sequences, p->seqlen T = total packed tokens;
+ *   the other fields as for gdnq_prefill_handoff.
+ *     cu_seqlens [B+1] int32, device: sequence b holds packed tokens
+ *                cu_seqlens[b] .. cu_seqlens[b+1]-1.  Expected
+ *                0 = cu[0] <= cu[1] <= ... <= cu[B] = T.  The kernels take
+ *                the running maximum of the values clamped to [0, T], so
+ *                malformed offsets never reach outside the buffers; what
+ *                they compute for such input is not specified.
+ *     q, k [T,H,128] bf16   v [T,H,128] bf16   alpha, beta [T,H] fp32
+ *     o    [T,H,128] out_dtype (every token of every sequence written)
+ *     init_codes, init_scales, codes, scales, buf_*: per sequence, as in
+ *                gdnq_prefill_handoff ([B,H,...]).
+ *     fill_out   [B] int32 = len_b mod 64 per sequence (written)
+ *   A sequence of length 0 copies its initial state (or zeros) to codes,
+ *   scales and sets its fill to 0.
+ *   workspace: gdnq_prefill_varlen_workspace_size(p) bytes (bounded by
+ *   floor(T/64) + B chunks per head, plus 8 (B+1) bytes of sequence map).
+ *   Errors: NULL, SHAPE, DTYPE, ALIGN (cu_seqlens: 4 bytes), ALIAS, FLAGS,
+ *   WORKSPACE, HIP.
+ * ------------------------------------------------------------------------ */
+size_t gdnq_prefill_varlen_workspace_size(const gdnq_prefill_params* p);
+
+gdnq_status gdnq_prefill_varlen(const gdnq_prefill_params* p, const int32_t* cu_seqlens, const void* q,
+                                const void* k, const void* v, const float* alpha, const float* beta,
+                                const int8_t* init_codes, const float* init_scales, void* o,
+                                int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                                float* buf_alpha, float* buf_beta, int32_t* fill_out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Status text, last error detail (thread-local, "" if none), library version. */
 const char* gdnq_status_string(gdnq_status s);
 const char* gdnq_last_error(void);

@@ -169,7 +169,7 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   if (p->out_dtype != GDNQ_F32 && p->out_dtype != GDNQ_BF16) return fail(GDNQ_ERR_DTYPE, "out_dtype = %d", p->out_dtype);
   if (p->chunk != 64) return fail(GDNQ_ERR_SHAPE, "chunk = %d, expected 64", p->chunk);
   if (T % 64 && !handoff) return fail(GDNQ_ERR_SHAPE, "seqlen = %d is not a multiple of the chunk (64)", T);
-  if (int64_t(T) * H * 512 >= (int64_t(1) << 32))
+  if ((int64_t(T) + 64) * H * 512 >= (int64_t(1) << 32))  // 32-bit output offsets, padding tokens included
     return fail(GDNQ_ERR_SHAPE, "seqlen * heads = %lld: one sequence's outputs must stay under 4 GiB",
                 (long long)T * H);
   const bool ssd = (p->flags & GDNQ_FLAG_SSD) != 0;
@@ -273,16 +273,29 @@ size_t gdnq_prefill_handoff_workspace_size(const gdnq_prefill_params* p) {
   return gdnq::prefill_workspace_bytes(L);
 }
 
-gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, const void* k,
-                                 const void* v, const float* alpha, const float* beta,
-                                 const int8_t* init_codes, const float* init_scales, void* o,
-                                 int8_t* codes, float* scales, float* buf_k, float* buf_v,
-                                 float* buf_alpha, float* buf_beta, int32_t* fill_out,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
-  gdnq::PrefillLaunch L;
+// Variable lengths: batch = sequences, seqlen = packed tokens in total.
+static gdnq_status varlen_validate(const gdnq_prefill_params* p, gdnq::PrefillLaunch& L) {
   if (gdnq_status st = prefill_validate(p, L, true)) return st;
+  if ((int64_t(L.T) / 64 + L.B) * L.H > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "too many chunks");
+  L.varlen = true;
+  return GDNQ_OK;
+}
+
+size_t gdnq_prefill_varlen_workspace_size(const gdnq_prefill_params* p) {
+  gdnq::PrefillLaunch L;
+  if (varlen_validate(p, L) != GDNQ_OK) return 0;
+  return gdnq::prefill_workspace_bytes(L);
+}
+
+static gdnq_status prefill_handoff_impl(gdnq::PrefillLaunch& L, const int32_t* cu_seqlens,
+                                        const void* q, const void* k, const void* v, const float* alpha,
+                                        const float* beta, const int8_t* init_codes, const float* init_scales,
+                                        void* o, int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                                        float* buf_alpha, float* buf_beta, int32_t* fill_out,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
   if (L.B == 0) return ok();
-  const size_t bth = size_t(L.B) * L.T * L.H, bh = size_t(L.B) * L.H;
+  // token-indexed arrays: B x T tokens, or T packed tokens of variable-length sequences
+  const size_t bth = (cu_seqlens ? size_t(1) : size_t(L.B)) * L.T * L.H, bh = size_t(L.B) * L.H;
   const size_t eo = L.out_bf16 ? 2 : 4, W = size_t(L.W);
   if ((init_codes == nullptr) != (init_scales == nullptr))
     return fail(GDNQ_ERR_NULL, "init_codes and init_scales must be both NULL or both set");
@@ -308,16 +321,48 @@ gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, co
   for (int i = 5; i < N; ++i)  // every written buffer is disjoint from every other
     for (int j = 0; j < N; ++j)
       if (j != i && overlap(sp[i], sp[j])) return fail(GDNQ_ERR_ALIAS, "%s overlaps %s", sp[i].name, sp[j].name);
+  if (cu_seqlens) {
+    if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return fail(GDNQ_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+    const Span cs{"cu_seqlens", cu_seqlens, (size_t(L.B) + 1) * 4};
+    for (int i = 5; i < N; ++i)
+      if (overlap(cs, sp[i])) return fail(GDNQ_ERR_ALIAS, "cu_seqlens overlaps %s", sp[i].name);
+  }
   const size_t need = gdnq::prefill_workspace_bytes(L);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDNQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace_bytes);
   if (workspace && !aligned16(workspace)) return fail(GDNQ_ERR_ALIGN, "workspace is not 16-byte aligned");
+  L.cu_seqlens = cu_seqlens;
   L.q = q; L.k = k; L.v = v; L.alpha = alpha; L.beta = beta; L.o = o;
   L.init_codes = init_codes; L.init_scales = init_scales; L.codes = codes; L.scales = scales;
   L.workspace = workspace;
   L.buf_k = buf_k; L.buf_v = buf_v; L.buf_alpha = buf_alpha; L.buf_beta = buf_beta; L.fill_out = fill_out;
   clear_stale_hip_error();
   return hip_status(gdnq::launch_prefill_gdn(L, static_cast<hipStream_t>(stream)), "prefill hand-over launch");
+}
+
+gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const int8_t* init_codes, const float* init_scales, void* o,
+                                 int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                                 float* buf_alpha, float* buf_beta, int32_t* fill_out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  gdnq::PrefillLaunch L;
+  if (gdnq_status st = prefill_validate(p, L, true)) return st;
+  return prefill_handoff_impl(L, nullptr, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales,
+                              buf_k, buf_v, buf_alpha, buf_beta, fill_out, workspace, workspace_bytes, stream);
+}
+
+gdnq_status gdnq_prefill_varlen(const gdnq_prefill_params* p, const int32_t* cu_seqlens, const void* q,
+                                const void* k, const void* v, const float* alpha, const float* beta,
+                                const int8_t* init_codes, const float* init_scales, void* o,
+                                int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                                float* buf_alpha, float* buf_beta, int32_t* fill_out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  gdnq::PrefillLaunch L;
+  if (gdnq_status st = varlen_validate(p, L)) return st;
+  if (L.B > 0 && !cu_seqlens) return fail(GDNQ_ERR_NULL, "cu_seqlens is NULL");
+  return prefill_handoff_impl(L, cu_seqlens, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales,
+                              buf_k, buf_v, buf_alpha, buf_beta, fill_out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

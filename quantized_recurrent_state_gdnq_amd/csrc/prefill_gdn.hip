@@ -54,6 +54,19 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Where sequence b's tokens and chunks are: every sequence T tokens
+// (uniform), or variable lengths from the workspace's sanitized cumulative
+// token offsets tok[0..B] (nondecreasing, at most the total) and chunk
+// offsets ch[0..B] (ceil(length / 64) per sequence).
+struct SeqMap {
+  const int32_t* tok;  // nullptr: uniform
+  const int32_t* ch;
+  int T;               // tokens per sequence (uniform) or in total
+  __device__ size_t tok0(int b) const { return tok ? size_t(tok[b]) : size_t(b) * T; }
+  __device__ int len(int b) const { return tok ? tok[b + 1] - tok[b] : T; }
+  __device__ int chunk0(int b) const { return tok ? ch[b] : b * ((T + 63) / 64); }
+};
+
 // ---------------------------------------------------------------- prep
 constexpr int KP = 136;  // bf16 pitch of [token][dim] tiles
 constexpr int AP = 65;   // fp32 pitch of A
@@ -63,9 +76,10 @@ struct PrepArgs {
   const uint16_t* k;
   const float* alpha;
   const float* beta;
-  __bf16* T_ws;  // [B*NC*H][3][64][64]: T as hi/mid/lo bf16 planes
-  float* g_ws;  // [B*NC*H][64]
-  int B, T, H;
+  __bf16* T_ws;  // [chunks*H][3][64][64]: T as hi/mid/lo bf16 planes
+  float* g_ws;  // [chunks*H][64]
+  SeqMap sm;
+  int B, H;
 };
 
 __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
@@ -76,16 +90,27 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
   __bf16* Kl = reinterpret_cast<__bf16*>(kt_raw);
   float* Tl = reinterpret_cast<float*>(kt_raw);
   float* Pl = Tl + PC * PC;
-  const int NC = (a.T + PC - 1) / PC;
-  const int idx = blockIdx.x;  // (b * NC + c) * H + h
+  const int idx = blockIdx.x;  // chunk * H + h, chunks numbered across the sequences
   const int h = idx % a.H;
-  const int c = (idx / a.H) % NC;
-  const int b = idx / (a.H * NC);
+  const int g = idx / a.H;
+  int b;
+  if (a.sm.tok) {  // variable lengths: the grid covers an upper bound of the chunk count
+    if (g >= a.sm.ch[a.B]) return;
+    int lo = 0, hi = a.B - 1;  // last b with ch[b] <= g
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.sm.ch[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  } else {
+    b = g / ((a.sm.T + PC - 1) / PC);
+  }
+  const int c = g - a.sm.chunk0(b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  const size_t tok0 = size_t(b) * a.T + size_t(c) * PC;
+  const size_t tok0 = a.sm.tok0(b) + size_t(c) * PC;
 
-  const int nvalid = a.T - c * PC;  // tokens of this chunk in the sequence (< 64 only in a last, partial chunk)
+  const int nvalid = a.sm.len(b) - c * PC;  // tokens of this chunk in the sequence (< 64 only in a last, partial chunk)
   {  // keys of the chunk: thread -> token tid / 4, dims [(tid % 4) * 32, +32); padding keys are 0
     const int i = tid >> 2, qq = tid & 3;
     const int ic = i < nvalid ? i : nvalid - 1;
@@ -240,7 +265,8 @@ struct StateArgs {
   void* o;
   int8_t* codes;
   float* scales;
-  int B, T, H;
+  SeqMap sm;
+  int B, H;
 };
 
 constexpr int TP = 72;    // bf16 pitch of [64][64] planes (T, M) and [32][64] planes (rhs^T, U^T)
@@ -308,11 +334,12 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   const int r0 = rb * RWS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  const int NC = (a.T + PC - 1) / PC;
-  const bool partial_last = (a.T % PC) != 0;  // the last chunk holds fewer than 64 tokens
+  const int Tb = a.sm.len(b);  // this sequence's tokens
+  const int NC = (Tb + PC - 1) / PC;
+  const bool partial_last = (Tb % PC) != 0;  // the last chunk holds fewer than 64 tokens
   const size_t HD = size_t(a.H) * PD;
   const size_t state_row0 = (size_t(b) * a.H + h) * PD + r0;
-  const size_t tokb = size_t(b) * a.T;
+  const size_t tokb = a.sm.tok0(b);
 
   // one 16x16 tile of M = L o Q K^T of the staged chunk: tiles 0..9 are the
   // lower tiles, D[j][i] = k_j . q_i stored as M[i][j] (hi and lo parts);
@@ -516,14 +543,15 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   const uint16_t* kb = a.k + tokb * HD + size_t(h) * PD + 8 * ps;
   const uint16_t* qb = a.q + tokb * HD + size_t(h) * PD + 8 * ps;
   const uint16_t* vb = a.v + tokb * HD + size_t(h) * PD + r0 + vr;
-  const __bf16* tb = a.T_ws + (size_t(b) * NC * a.H + h) * 3 * PC * PC + ti * PC + 8 * tc;
-  const float* gb = a.g_ws + (size_t(b) * NC * a.H + h) * PC + (st & 63);
+  const size_t wsc = size_t(a.sm.chunk0(b)) * a.H + h;  // workspace index of the first chunk
+  const __bf16* tb = a.T_ws + wsc * 3 * PC * PC + ti * PC + 8 * tc;
+  const float* gb = a.g_ws + wsc * PC + (st & 63);
   const float* bb = a.beta + tokb * a.H + h;
   const size_t ch_step = size_t(a.H) * 3 * PC * PC;  // T elements per chunk (all heads)
   // token i of chunk c: whether it is in the sequence, and the token loads
   // read (clamped into the sequence; padding is zeroed when staged)
-  auto tok_ok = [&](int c, int i) { return c * PC + i < a.T; };
-  auto tok_ld = [&](int c, int i) { return size_t(c * PC + i < a.T ? c * PC + i : a.T - 1); };
+  auto tok_ok = [&](int c, int i) { return c * PC + i < Tb; };
+  auto tok_ld = [&](int c, int i) { return size_t(c * PC + i < Tb ? c * PC + i : Tb - 1); };
   int kq_c = 0, tv_c = 0;  // the chunks the prefetch registers hold
 
   // (clang vector types: arrays of HIP's uint4 are copied through memory)
@@ -603,7 +631,7 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   const int it = sw >> 1, i0 = it * 16 + 4 * lq, nks = (it >> 1) + 1;
   // this sequence's outputs, bounded at its T tokens
   const rsrc_t o_rsrc = make_rsrc(static_cast<char*>(a.o) + tokb * HD * (OUT_BF16 ? 2 : 4),
-                                  uint32_t(size_t(a.T) * HD * (OUT_BF16 ? 2 : 4)));
+                                  uint32_t(size_t(Tb) * HD * (OUT_BF16 ? 2 : 4)));
   for (int c = 0; c < NC; ++c) {
     const float* gc = G + 192 * (c & 1);
     // ---- A: output base diag(gamma s) Q S0^T of this wave's (token tile, row tile)
@@ -669,13 +697,70 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   }
 }
 
-static int gdn_chunks(const PrefillLaunch& L) { return (L.T + PC - 1) / PC; }
-static size_t gdn_ws_T(const PrefillLaunch& L) { return size_t(L.B) * gdn_chunks(L) * L.H * 3 * PC * PC * 2; }
-static size_t gdn_ws_g(const PrefillLaunch& L) { return size_t(L.B) * gdn_chunks(L) * L.H * PC * 4; }
+// Chunks the workspace holds: B ceil(T / 64) for uniform lengths; for
+// variable lengths summing to T, sum ceil(len / 64) <= floor(T / 64) + B.
+static size_t gdn_chunks(const PrefillLaunch& L) {
+  return L.varlen ? size_t(L.T / PC) + size_t(L.B) : size_t(L.B) * ((L.T + PC - 1) / PC);
+}
+static size_t gdn_ws_T(const PrefillLaunch& L) { return gdn_chunks(L) * L.H * 3 * PC * PC * 2; }
+static size_t gdn_ws_g(const PrefillLaunch& L) { return gdn_chunks(L) * L.H * PC * 4; }
+static size_t gdn_ws_map(const PrefillLaunch& L) { return L.varlen ? 2 * (size_t(L.B) + 1) * 4 : 0; }
 
-// Hand-over to decode: the last r = T mod 64 tokens' writes go to slots
-// 0 .. r-1 of the window buffer (fp32, keys in the state's basis) and every
-// sequence's fill becomes r.  One workgroup per (sequence, head).
+// Sequence map of a variable-length batch, one workgroup: token offsets
+// tok[i] = the running maximum of cu[i] clamped to [0, T] (so lengths are
+// never negative and never reach past the tokens), chunk offsets ch[i] =
+// sum over the earlier sequences of ceil(len / 64).  A well-formed cu
+// (0 = cu[0] <= ... <= cu[B] = T) passes through unchanged.
+struct SeqMapArgs {
+  const int32_t* cu;
+  int32_t* tok;
+  int32_t* ch;
+  int B, T;
+};
+
+__global__ __launch_bounds__(1024) void gdn_seqmap_kernel(SeqMapArgs a) {
+  __shared__ int32_t sv[1025];
+  __shared__ int32_t sc[1024];
+  const int t = threadIdx.x;
+  int carry_tok = 0, carry_ch = 0;
+  for (int base = 0; base <= a.B; base += 1024) {
+    // running maximum of the clamped offsets base .. base + 1024
+    const int i = base + t;
+    int x = i <= a.B ? min(max(a.cu[i], 0), a.T) : a.T;
+    if (base > 0) x = max(x, carry_tok);
+    sv[t] = x;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int y = t >= o ? sv[t - o] : 0;
+      __syncthreads();
+      sv[t] = max(sv[t], y);
+      __syncthreads();
+    }
+    if (t == 0) sv[1024] = base + 1024 <= a.B ? max(min(max(a.cu[base + 1024], 0), a.T), sv[1023]) : a.T;
+    __syncthreads();
+    // chunks of sequence i, then their exclusive running sum
+    const int n = i < a.B ? (sv[t + 1] - sv[t] + PC - 1) / PC : 0;
+    sc[t] = n;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int y = t >= o ? sc[t - o] : 0;
+      __syncthreads();
+      sc[t] += y;
+      __syncthreads();
+    }
+    if (i <= a.B) {
+      a.tok[i] = sv[t];
+      a.ch[i] = carry_ch + sc[t] - n;
+    }
+    carry_tok = sv[1023];
+    carry_ch += sc[1023];
+    __syncthreads();
+  }
+}
+
+// Hand-over to decode: the last r = len mod 64 tokens' writes of each
+// sequence go to slots 0 .. r-1 of its window buffer (fp32, keys in the
+// state's basis) and its fill becomes r.  One workgroup per (sequence, head).
 struct HandoffArgs {
   const uint16_t* k;
   const uint16_t* v;
@@ -686,41 +771,54 @@ struct HandoffArgs {
   float* buf_alpha;
   float* buf_beta;
   int32_t* fill_out;
-  int B, T, H, W;
+  SeqMap sm;
+  int B, H, W;
 };
 
 __global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
   const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
-  const int r = a.T % PC, t0 = a.T - r;
+  const int len = a.sm.len(b);
+  const int r = len % PC;
+  const size_t t0 = a.sm.tok0(b) + size_t(len - r);
   for (int e = threadIdx.x; e < r * PD; e += 256) {
     const int slot = e / PD, d = e % PD;
-    const size_t src = ((size_t(b) * a.T + t0 + slot) * a.H + h) * PD + d;
+    const size_t src = ((t0 + slot) * a.H + h) * PD + d;
     const size_t dst = (size_t(bh) * a.W + slot) * PD + d;
     a.buf_k[dst] = __uint_as_float(uint32_t(a.k[src]) << 16);
     a.buf_v[dst] = __uint_as_float(uint32_t(a.v[src]) << 16);
   }
   for (int slot = threadIdx.x; slot < r; slot += 256) {
-    const size_t src = (size_t(b) * a.T + t0 + slot) * a.H + h;
+    const size_t src = (t0 + slot) * a.H + h;
     a.buf_alpha[size_t(bh) * a.W + slot] = a.alpha[src];
     a.buf_beta[size_t(bh) * a.W + slot] = a.beta[src];
   }
   if (h == 0 && threadIdx.x == 0) a.fill_out[b] = r;
 }
 
-size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L) { return gdn_ws_T(L) + gdn_ws_g(L); }
+size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L) { return gdn_ws_T(L) + gdn_ws_g(L) + gdn_ws_map(L); }
 
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
   __bf16* T_ws = static_cast<__bf16*>(L.workspace);
   float* g_ws = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + gdn_ws_T(L));
-  const int NC = gdn_chunks(L);
-  if (NC > 0) {
-    PrepArgs p{static_cast<const uint16_t*>(L.k), L.alpha, L.beta, T_ws, g_ws, L.B, L.T, L.H};
-    hipLaunchKernelGGL(gdn_prep_kernel, dim3(unsigned(L.B) * NC * L.H), dim3(256), 0, stream, p);
+  SeqMap sm{nullptr, nullptr, L.T};
+  if (L.varlen) {
+    int32_t* tok = reinterpret_cast<int32_t*>(static_cast<char*>(L.workspace) + gdn_ws_T(L) + gdn_ws_g(L));
+    int32_t* ch = tok + (L.B + 1);
+    SeqMapArgs m{L.cu_seqlens, tok, ch, L.B, L.T};
+    hipLaunchKernelGGL(gdn_seqmap_kernel, dim3(1), dim3(1024), 0, stream, m);
+    if (hipError_t e = hipGetLastError()) return e;
+    sm.tok = tok;
+    sm.ch = ch;
+  }
+  const size_t nch = gdn_chunks(L);
+  if (nch > 0) {
+    PrepArgs p{static_cast<const uint16_t*>(L.k), L.alpha, L.beta, T_ws, g_ws, sm, L.B, L.H};
+    hipLaunchKernelGGL(gdn_prep_kernel, dim3(unsigned(nch * L.H)), dim3(256), 0, stream, p);
     if (hipError_t e = hipGetLastError()) return e;
   }
   StateArgs s{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k),
               static_cast<const uint16_t*>(L.v), L.beta, T_ws, g_ws, L.init_codes, L.init_scales,
-              L.o, L.codes, L.scales, L.B, L.T, L.H};
+              L.o, L.codes, L.scales, sm, L.B, L.H};
   const unsigned grid = unsigned(L.B) * L.H * (PD / RWS);
   auto kern = L.out_bf16 ? &gdn_state_kernel<true> : &gdn_state_kernel<false>;
   if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -730,7 +828,7 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
   if (hipError_t e = hipGetLastError()) return e;
   if (L.handoff && L.B > 0) {
     HandoffArgs h{static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v), L.alpha, L.beta,
-                  L.buf_k, L.buf_v, L.buf_alpha, L.buf_beta, L.fill_out, L.B, L.T, L.H, L.W};
+                  L.buf_k, L.buf_v, L.buf_alpha, L.buf_beta, L.fill_out, sm, L.B, L.H, L.W};
     hipLaunchKernelGGL(gdn_handoff_kernel, dim3(unsigned(L.B) * L.H), dim3(256), 0, stream, h);
     return hipGetLastError();
   }

@@ -241,6 +241,65 @@ def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_sc
     return o, st
 
 
+def _varlen_params(q, v, n_seqs, *, window, out_dtype):
+    T, H, d_k = q.shape
+    return _lib.PrefillParams(n_seqs, T, H, d_k, v.shape[-1], 64, window, _DT[q.dtype],
+                              _DT[out_dtype], 0)
+
+
+def prefill_varlen_workspace_size(q, v, n_seqs, *, window=64, out_dtype=torch.bfloat16):
+    p = _varlen_params(q, v, n_seqs, window=window, out_dtype=out_dtype)
+    return int(_lib.prefill_varlen_workspace_size(p))
+
+
+def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=None,
+                   init_scales=None, out_dtype=torch.bfloat16, o=None, state=None,
+                   workspace=None):
+    """GDN prefill of a packed batch of variable-length sequences handed over
+    to decode (see gdnq_prefill_varlen in include/gdnq.h).  q, k [T,H,d_k],
+    v [T,H,d_v] bf16 and alpha, beta [T,H] fp32 hold the sequences back to
+    back; cu_seqlens (int32 on the device, B+1 entries) gives where each
+    starts.  Returns (o [T,H,d_v], DecodeState of B sequences)."""
+    dev = q.device
+    T, H, d_k = q.shape
+    d_v = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, dev)
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        _need(t, name, torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens: one dimension of B+1 offsets")
+    B = cu_seqlens.numel() - 1
+    if (tuple(k.shape) != (T, H, d_k) or tuple(v.shape) != (T, H, d_v)
+            or tuple(alpha.shape) != (T, H) or tuple(beta.shape) != (T, H)):
+        raise ValueError("inconsistent packed prefill shapes")
+    p = _varlen_params(q, v, B, window=window, out_dtype=out_dtype)
+    if o is None:
+        o = torch.empty((T, H, d_v), dtype=out_dtype, device=dev)
+    _need(o, "o", out_dtype, dev)
+    if init_codes is not None:
+        _need(init_codes, "init_codes", torch.int8, dev)
+        _need(init_scales, "init_scales", torch.float32, dev)
+    st = state
+    if st is None:
+        st = DecodeState(torch.empty((B, H, d_v, d_k), dtype=torch.int8, device=dev),
+                         torch.empty((B, H, d_v), dtype=torch.float32, device=dev), window,
+                         fill=torch.zeros(B, dtype=torch.int32, device=dev))
+    if st.buf_k.dtype != torch.float32 or tuple(st.codes.shape) != (B, H, d_v, d_k):
+        raise ValueError("state: a DecodeState of matching shape with an fp32 window buffer")
+    need = int(_lib.prefill_varlen_workspace_size(p))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _lib.check(_lib.prefill_varlen(p, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                   _ptr(beta), _ptr(init_codes), _ptr(init_scales), _ptr(o),
+                                   _ptr(st.codes), _ptr(st.scales), _ptr(st.buf_k), _ptr(st.buf_v),
+                                   _ptr(st.buf_alpha), _ptr(st.buf_beta), _ptr(st.fill),
+                                   _ptr(workspace), ws_bytes, _stream(dev)))
+    return o, st
+
+
 def fp8_window_buffer(B, H, W, d, device):
     """One FP8 window buffer: E4M3 codes [B,H,W,d] followed, in the same
     allocation, by the per-vector fp32 scales [B,H,W].  Returns (codes view,

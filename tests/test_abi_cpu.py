@@ -258,3 +258,54 @@ def test_handoff_contract():
     assert _handoff(p, f, k=k, fill_out=k) == 5                 # output over an input
     assert _handoff(_pp(B=0, T=100), f) == 0                    # empty batch: no-op
     assert _lib.prefill_workspace_size(p) == 0                  # the chunked prefill rejects T = 100
+
+
+# ---------------------------------------------------------------- variable-length prefill
+def _varlen(params, fake, cu="fake", **over):
+    a = dict(q=fake(), k=fake(), v=fake(), alpha=fake(), beta=fake(), init_codes=None,
+             init_scales=None, o=fake(), codes=fake(), scales=fake(), buf_k=fake(), buf_v=fake(),
+             buf_alpha=fake(), buf_beta=fake(), fill_out=fake(), workspace=None, ws=0)
+    a.update(over)
+    cu = fake() if cu == "fake" else cu
+    return _lib.prefill_varlen(params, cu, a["q"], a["k"], a["v"], a["alpha"], a["beta"],
+                               a["init_codes"], a["init_scales"], a["o"], a["codes"], a["scales"],
+                               a["buf_k"], a["buf_v"], a["buf_alpha"], a["buf_beta"],
+                               a["fill_out"], a["workspace"], a["ws"], None)
+
+
+@pytest.mark.parametrize("params,status", [
+    (_pp(C=32, W=32), 2), (_pp(dk=64, dv=64), 2), (_pp(ind=0), 3),
+    (_pp(flags=1), 8), (_pp(dv=64, flags=2 | 1 | 4), 8),   # GDN only
+    (_pp(T=1 << 20, H=8192), 2),                           # the packed outputs past 4 GiB
+])
+def test_varlen_rejects_bad_params(params, status):
+    assert _varlen(params, Fake()) == status
+    assert _lib.prefill_varlen_workspace_size(params) == 0
+
+
+def test_varlen_contract():
+    """batch counts sequences and seqlen the packed tokens; the workspace
+    bounds the chunks by floor(T / 64) + B per head and adds the sequence
+    map; cu_seqlens is required and 4-byte aligned, and no written buffer
+    may overlap it."""
+    f = Fake()
+    B, T, H = 5, 300, 3
+    p = _pp(B=B, T=T, H=H)
+    assert _lib.prefill_varlen_workspace_size(p) == (T // 64 + B) * H * (3 * 64 * 64 * 2 + 64 * 4) + 2 * (B + 1) * 4
+    ws = f()
+    need = _lib.prefill_varlen_workspace_size(p)
+    assert _varlen(p, f) == 6                                   # workspace missing
+    assert _varlen(p, f, cu=None, workspace=ws, ws=need) == 1   # cu_seqlens missing
+    assert _varlen(p, f, cu=f() + 2, workspace=ws, ws=need) == 4
+    o = f()
+    assert _varlen(p, f, cu=o, o=o, workspace=ws, ws=need) == 5
+    assert _varlen(p, f, fill_out=None, workspace=ws, ws=need) == 1
+    assert _varlen(_pp(B=0, T=0), f, cu=None) == 0              # no sequences: no-op
+
+
+def test_output_offset_bound_counts_padding():
+    """Outputs are addressed with 32-bit byte offsets, and the last partial
+    chunk's padding tokens are addressed too (their stores are dropped): the
+    limit is (T + 64) H 512 bytes < 4 GiB."""
+    assert _lib.prefill_handoff_workspace_size(_pp(T=(1 << 23) - 64, H=1)) == 0
+    assert _lib.prefill_handoff_workspace_size(_pp(T=(1 << 23) - 128, H=1)) > 0

@@ -142,6 +142,17 @@ def gdn_prefill(B=4, T=8192, H=16, dk=128, dv=128, seed=0):
     return {"q": q, "k": k, "v": v, "alpha": alpha, "beta": beta}
 
 
+def gdn_prefill_varlen(lengths, H=16, dk=128, dv=128, seed=0):
+    """A packed batch of sequences of the given lengths: the gdn_prefill
+    distributions over sum(lengths) tokens laid back to back ([T,H,d],
+    alpha and beta [T,H]) and cu_seqlens (int32, B+1 offsets)."""
+    lengths = [int(n) for n in lengths]
+    x = gdn_prefill(B=1, T=sum(lengths), H=H, dk=dk, dv=dv, seed=seed)
+    out = {key: val[0] for key, val in x.items()}
+    out["cu_seqlens"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return out
+
+
 def ssd_prefill(B=2, T=4096, H=80, dk=128, dv=64, seed=0, outlier_channels=0,
                 outlier_gain=20.0):
     """q, k ~ N(0,1) [B,T,H,dk] and v ~ N(0,1) [B,T,H,dv], rounded to bf16
