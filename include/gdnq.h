@@ -265,7 +265,7 @@ gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, co
  *   A sequence of length 0 copies its initial state (or zeros) to codes,
  *   scales and sets its fill to 0.
  *   workspace: gdnq_prefill_varlen_workspace_size(p) bytes (bounded by
- *   floor(T/64) + B chunks per head, plus 8 (B+1) bytes of sequence map).
+ *   floor(T/64) + B chunks per head, plus 4 (3B+2) bytes of sequence map).
  *   Errors: NULL, SHAPE, DTYPE, ALIGN (cu_seqlens: 4 bytes), ALIAS, FLAGS,
  *   WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */
@@ -276,6 +276,45 @@ gdnq_status gdnq_prefill_varlen(const gdnq_prefill_params* p, const int32_t* cu_
                                 const int8_t* init_codes, const float* init_scales, void* o,
                                 int8_t* codes, float* scales, float* buf_k, float* buf_v,
                                 float* buf_alpha, float* buf_beta, int32_t* fill_out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdnq_prefill_resume -- GDN prefill that continues sequences from their
+ *   decode state at any fill: windows need not start at a chunk boundary
+ *   (LeapQuant, abstract: outputs inside a window from the fixed low-bit
+ *   state plus the buffered writes; one requantization when the window is
+ *   full).  For each sequence the open window's fill_in[b] buffered writes
+ *   and its new tokens form one sequence whose 64-position chunks start at
+ *   the first buffered write, so the first window closes after
+ *   64 - fill_in[b] new tokens, exactly as decode would close it.
+ *
+ *   p->batch B = sequences; p->seqlen = new tokens per sequence (cu_seqlens
+ *   NULL, q [B,T,H,128] ...) or packed new tokens in total (cu_seqlens as
+ *   for gdnq_prefill_varlen, q [T,H,128] ...).  GDN mode only (flags 0,
+ *   d_k = d_v = 128, chunk = window = 64, in_dtype bf16).
+ *     fill_in    [B] int32, device: buffered writes per sequence (0..63;
+ *                other values are clamped into that range).  It may be the
+ *                same array as fill_out.
+ *     codes, scales [B,H,128,128] int8 / [B,H,128] fp32: the state at the
+ *                last window boundary on entry, at the new last boundary on
+ *                return (updated in place).
+ *     buf_k, buf_v [B,H,64,128] fp32, buf_alpha, buf_beta [B,H,64] fp32:
+ *                decode's window buffer on entry (slots < fill_in read; the
+ *                keys and values enter the chunk products at bf16, exact
+ *                when decode's inputs were bf16), the new open window's
+ *                writes on return (slots < fill_out).
+ *     o          new tokens' outputs, out_dtype (every new token written;
+ *                the buffered writes have none: decode gave them).
+ *     fill_out   [B] int32 = (fill_in + new tokens) mod 64 (written).
+ *   workspace: gdnq_prefill_resume_workspace_size(p, cu_seqlens != NULL).
+ *   Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, FLAGS, WORKSPACE, HIP.
+ * ------------------------------------------------------------------------ */
+size_t gdnq_prefill_resume_workspace_size(const gdnq_prefill_params* p, int32_t varlen);
+
+gdnq_status gdnq_prefill_resume(const gdnq_prefill_params* p, const int32_t* cu_seqlens, const int32_t* fill_in,
+                                const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, void* o, int8_t* codes, float* scales, float* buf_k,
+                                float* buf_v, float* buf_alpha, float* buf_beta, int32_t* fill_out,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Status text, last error detail (thread-local, "" if none), library version. */

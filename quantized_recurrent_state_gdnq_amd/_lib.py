@@ -24,6 +24,7 @@ GDNQ_FLAG_WHT, GDNQ_FLAG_SSD, GDNQ_FLAG_INT8_QK, GDNQ_FLAG_BUF_BF16, GDNQ_FLAG_B
 EXPORTS = ("gdnq_quantize_state", "gdnq_decode_step", "gdnq_prefill_workspace_size",
            "gdnq_prefill_chunked", "gdnq_prefill_handoff_workspace_size", "gdnq_prefill_handoff",
            "gdnq_prefill_varlen_workspace_size", "gdnq_prefill_varlen",
+           "gdnq_prefill_resume_workspace_size", "gdnq_prefill_resume",
            "gdnq_status_string", "gdnq_last_error", "gdnq_version")
 
 
@@ -75,6 +76,10 @@ def _load():
     lib.gdnq_prefill_varlen_workspace_size.restype = sz
     lib.gdnq_prefill_varlen.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 17 + [sz, vp]
     lib.gdnq_prefill_varlen.restype = i32
+    lib.gdnq_prefill_resume_workspace_size.argtypes = [ctypes.POINTER(PrefillParams), i32]
+    lib.gdnq_prefill_resume_workspace_size.restype = sz
+    lib.gdnq_prefill_resume.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 16 + [sz, vp]
+    lib.gdnq_prefill_resume.restype = i32
     lib.gdnq_status_string.argtypes = [i32]
     lib.gdnq_status_string.restype = ctypes.c_char_p
     lib.gdnq_last_error.argtypes = []
@@ -136,3 +141,14 @@ def prefill_varlen(params, cu_seqlens, q, k, v, alpha, beta, init_codes, init_sc
                                    init_codes, init_scales, o, codes, scales, buf_k, buf_v,
                                    buf_alpha, buf_beta, fill_out, workspace, workspace_bytes,
                                    stream)
+
+
+def prefill_resume_workspace_size(params, varlen):
+    return lib.gdnq_prefill_resume_workspace_size(ctypes.byref(params), int(varlen))
+
+
+def prefill_resume(params, cu_seqlens, fill_in, q, k, v, alpha, beta, o, codes, scales, buf_k,
+                   buf_v, buf_alpha, buf_beta, fill_out, workspace, workspace_bytes, stream):
+    return lib.gdnq_prefill_resume(ctypes.byref(params), cu_seqlens, fill_in, q, k, v, alpha, beta,
+                                   o, codes, scales, buf_k, buf_v, buf_alpha, buf_beta, fill_out,
+                                   workspace, workspace_bytes, stream)

@@ -288,7 +288,7 @@ size_t gdnq_prefill_varlen_workspace_size(const gdnq_prefill_params* p) {
 }
 
 static gdnq_status prefill_handoff_impl(gdnq::PrefillLaunch& L, const int32_t* cu_seqlens,
-                                        const void* q, const void* k, const void* v, const float* alpha,
+                                        const int32_t* fill_in, const void* q, const void* k, const void* v, const float* alpha,
                                         const float* beta, const int8_t* init_codes, const float* init_scales,
                                         void* o, int8_t* codes, float* scales, float* buf_k, float* buf_v,
                                         float* buf_alpha, float* buf_beta, int32_t* fill_out,
@@ -327,11 +327,20 @@ static gdnq_status prefill_handoff_impl(gdnq::PrefillLaunch& L, const int32_t* c
     for (int i = 5; i < N; ++i)
       if (overlap(cs, sp[i])) return fail(GDNQ_ERR_ALIAS, "cu_seqlens overlaps %s", sp[i].name);
   }
+  if (L.resume) {  // fill_in is read before anything is written: it may be fill_out itself
+    if (!fill_in) return fail(GDNQ_ERR_NULL, "fill_in is NULL");
+    if (reinterpret_cast<uintptr_t>(fill_in) & 3u) return fail(GDNQ_ERR_ALIGN, "fill_in is not 4-byte aligned");
+    const Span fs{"fill_in", fill_in, size_t(L.B) * 4};
+    for (int i = 5; i < N; ++i)
+      if (!(i == N - 1 && fill_in == fill_out) && overlap(fs, sp[i]))
+        return fail(GDNQ_ERR_ALIAS, "fill_in overlaps %s", sp[i].name);
+  }
   const size_t need = gdnq::prefill_workspace_bytes(L);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDNQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace_bytes);
   if (workspace && !aligned16(workspace)) return fail(GDNQ_ERR_ALIGN, "workspace is not 16-byte aligned");
   L.cu_seqlens = cu_seqlens;
+  L.fill_in = fill_in;
   L.q = q; L.k = k; L.v = v; L.alpha = alpha; L.beta = beta; L.o = o;
   L.init_codes = init_codes; L.init_scales = init_scales; L.codes = codes; L.scales = scales;
   L.workspace = workspace;
@@ -348,7 +357,7 @@ gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, co
                                  void* workspace, size_t workspace_bytes, void* stream) {
   gdnq::PrefillLaunch L;
   if (gdnq_status st = prefill_validate(p, L, true)) return st;
-  return prefill_handoff_impl(L, nullptr, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales,
+  return prefill_handoff_impl(L, nullptr, nullptr, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales,
                               buf_k, buf_v, buf_alpha, buf_beta, fill_out, workspace, workspace_bytes, stream);
 }
 
@@ -361,7 +370,37 @@ gdnq_status gdnq_prefill_varlen(const gdnq_prefill_params* p, const int32_t* cu_
   gdnq::PrefillLaunch L;
   if (gdnq_status st = varlen_validate(p, L)) return st;
   if (L.B > 0 && !cu_seqlens) return fail(GDNQ_ERR_NULL, "cu_seqlens is NULL");
-  return prefill_handoff_impl(L, cu_seqlens, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales,
+  return prefill_handoff_impl(L, cu_seqlens, nullptr, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales,
+                              buf_k, buf_v, buf_alpha, buf_beta, fill_out, workspace, workspace_bytes, stream);
+}
+
+// Resuming from decode: batch = sequences; seqlen = new tokens per sequence,
+// or packed new tokens in total with cu_seqlens.
+static gdnq_status resume_validate(const gdnq_prefill_params* p, bool varlen, gdnq::PrefillLaunch& L) {
+  if (gdnq_status st = prefill_validate(p, L, true)) return st;
+  const int64_t tokens = varlen ? int64_t(L.T) : int64_t(L.B) * L.T;
+  if (tokens > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "%lld new tokens: at most 2^31 - 1", (long long)tokens);
+  if ((tokens / 64 + 2 * int64_t(L.B)) * L.H > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "too many chunks");
+  L.varlen = varlen;
+  L.resume = true;
+  return GDNQ_OK;
+}
+
+size_t gdnq_prefill_resume_workspace_size(const gdnq_prefill_params* p, int32_t varlen) {
+  gdnq::PrefillLaunch L;
+  if (resume_validate(p, varlen != 0, L) != GDNQ_OK) return 0;
+  return gdnq::prefill_workspace_bytes(L);
+}
+
+gdnq_status gdnq_prefill_resume(const gdnq_prefill_params* p, const int32_t* cu_seqlens, const int32_t* fill_in,
+                                const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, void* o, int8_t* codes, float* scales, float* buf_k,
+                                float* buf_v, float* buf_alpha, float* buf_beta, int32_t* fill_out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  gdnq::PrefillLaunch L;
+  if (gdnq_status st = resume_validate(p, cu_seqlens != nullptr, L)) return st;
+  if (!codes || !scales) return fail(GDNQ_ERR_NULL, "codes and scales (the stored state) are required");
+  return prefill_handoff_impl(L, cu_seqlens, fill_in, q, k, v, alpha, beta, codes, scales, o, codes, scales,
                               buf_k, buf_v, buf_alpha, buf_beta, fill_out, workspace, workspace_bytes, stream);
 }
 

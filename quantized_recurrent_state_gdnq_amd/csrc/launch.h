@@ -59,8 +59,9 @@ struct PrefillLaunch {
   float* buf_beta;
   int32_t* fill_out;
   const int32_t* cu_seqlens;  // variable lengths (GDN hand-over): B + 1 token offsets on the device, T their total
+  const int32_t* fill_in;     // resuming (GDN hand-over): writes each sequence's window buffer holds
   int B, T, H, d_k, d_v, C, W;
-  bool out_bf16, wht, ssd, int8_qk, handoff, varlen;
+  bool out_bf16, wht, ssd, int8_qk, handoff, varlen, resume;
 };
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream);
 hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream);

@@ -54,17 +54,35 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Where sequence b's tokens and chunks are: every sequence T tokens
-// (uniform), or variable lengths from the workspace's sanitized cumulative
-// token offsets tok[0..B] (nondecreasing, at most the total) and chunk
-// offsets ch[0..B] (ceil(length / 64) per sequence).
+// Where sequence b's tokens and chunks are.  A sequence is the pre_b writes
+// that decode still holds in its window buffer (when resuming; none
+// otherwise) followed by its n_b new tokens, and its chunks of 64 run over
+// that whole sequence from its first buffered write: chunk 0 is the window
+// that is still open.  Uniform: n_b = T, no prefix, nothing mapped.  Mapped
+// (variable lengths or resuming): the workspace's sanitized token offsets
+// tok[0..B], prefix lengths pre[0..B) and chunk offsets ch[0..B].  When
+// resuming, chunk 0 of every sequence (prefix and first new tokens) is read
+// from a staged copy laid out like the tokens ([B][64][H][...]).
 struct SeqMap {
   const int32_t* tok;  // nullptr: uniform
   const int32_t* ch;
+  const int32_t* pre;  // nullptr: no prefix, nothing staged
+  const uint16_t* sk;  // staged chunk 0: k, q, v (bf16) and alpha, beta
+  const uint16_t* sq;
+  const uint16_t* sv;
+  const float* sa;
+  const float* sb;
   int T;               // tokens per sequence (uniform) or in total
   __device__ size_t tok0(int b) const { return tok ? size_t(tok[b]) : size_t(b) * T; }
-  __device__ int len(int b) const { return tok ? tok[b + 1] - tok[b] : T; }
+  __device__ int ntok(int b) const { return tok ? tok[b + 1] - tok[b] : T; }
+  __device__ int npre(int b) const { return pre ? pre[b] : 0; }
+  __device__ int len(int b) const { return npre(b) + ntok(b); }
   __device__ int chunk0(int b) const { return tok ? ch[b] : b * ((T + 63) / 64); }
+  __device__ bool staged(int c) const { return pre != nullptr && c == 0; }
+  // row of position c * 64 in its source: the staged copy, or the tokens
+  __device__ size_t row0(int b, int c) const {
+    return staged(c) ? size_t(b) * 64 : tok0(b) + size_t(c) * 64 - size_t(npre(b));
+  }
 };
 
 // ---------------------------------------------------------------- prep
@@ -108,13 +126,17 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
   const int c = g - a.sm.chunk0(b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  const size_t tok0 = a.sm.tok0(b) + size_t(c) * PC;
+  const size_t tok0 = a.sm.row0(b, c);
+  const bool stg = a.sm.staged(c);
+  const uint16_t* ksrc = stg ? a.sm.sk : a.k;
+  const float* asrc = stg ? a.sm.sa : a.alpha;
+  const float* bsrc = stg ? a.sm.sb : a.beta;
 
   const int nvalid = a.sm.len(b) - c * PC;  // tokens of this chunk in the sequence (< 64 only in a last, partial chunk)
   {  // keys of the chunk: thread -> token tid / 4, dims [(tid % 4) * 32, +32); padding keys are 0
     const int i = tid >> 2, qq = tid & 3;
     const int ic = i < nvalid ? i : nvalid - 1;
-    const uint4* src = reinterpret_cast<const uint4*>(a.k + ((tok0 + ic) * a.H + h) * PD + qq * 32);
+    const uint4* src = reinterpret_cast<const uint4*>(ksrc + ((tok0 + ic) * a.H + h) * PD + qq * 32);
     uint4 w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) w[e] = i < nvalid ? src[e] : make_uint4(0u, 0u, 0u, 0u);
@@ -124,8 +146,8 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
   }
   if (tid < 64) {  // g = inclusive prefix sum of log alpha (padding: alpha = 1, beta = 0)
     const size_t r = (tok0 + (tid < nvalid ? tid : nvalid - 1)) * a.H + h;
-    float la = tid < nvalid ? logf(a.alpha[r]) : 0.f;
-    bl[tid] = tid < nvalid ? a.beta[r] : 0.f;
+    float la = tid < nvalid ? logf(asrc[r]) : 0.f;
+    bl[tid] = tid < nvalid ? bsrc[r] : 0.f;
 #pragma unroll
     for (int s = 1; s < 64; s <<= 1) {
       const float o = __shfl_up(la, s, 64);
@@ -334,7 +356,7 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   const int r0 = rb * RWS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  const int Tb = a.sm.len(b);  // this sequence's tokens
+  const int Tb = a.sm.len(b);  // this sequence's positions (buffered prefix and new tokens)
   const int NC = (Tb + PC - 1) / PC;
   const bool partial_last = (Tb % PC) != 0;  // the last chunk holds fewer than 64 tokens
   const size_t HD = size_t(a.H) * PD;
@@ -540,18 +562,32 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   const int pm = st & 31, ps = st >> 5;
   const int ti = st >> 3, tc = st & 7;
   const int vr = (sw & 1) * 16 + lr, vi = (sw >> 1) * 16 + 4 * lq;
-  const uint16_t* kb = a.k + tokb * HD + size_t(h) * PD + 8 * ps;
-  const uint16_t* qb = a.q + tokb * HD + size_t(h) * PD + 8 * ps;
-  const uint16_t* vb = a.v + tokb * HD + size_t(h) * PD + r0 + vr;
+  const size_t kq_off = size_t(h) * PD + 8 * ps, v_off = size_t(h) * PD + r0 + vr;
   const size_t wsc = size_t(a.sm.chunk0(b)) * a.H + h;  // workspace index of the first chunk
   const __bf16* tb = a.T_ws + wsc * 3 * PC * PC + ti * PC + 8 * tc;
   const float* gb = a.g_ws + wsc * PC + (st & 63);
-  const float* bb = a.beta + tokb * a.H + h;
   const size_t ch_step = size_t(a.H) * 3 * PC * PC;  // T elements per chunk (all heads)
-  // token i of chunk c: whether it is in the sequence, and the token loads
-  // read (clamped into the sequence; padding is zeroed when staged)
+  // position i of chunk c: whether it is in the sequence, and the row the
+  // loads read (clamped into the sequence; padding is zeroed when staged)
+  // the sequence map is read once, here: in the loop a scalar load's wait
+  // would also wait for every LDS access in flight
+  const int npre = a.sm.npre(b);
+  const bool stg0 = a.sm.pre != nullptr;  // chunk 0 is read from the staged copy
+  const size_t row_c0 = stg0 ? size_t(b) * PC : tokb;
+  const size_t row_t = tokb - size_t(npre);  // chunk c >= 1 starts at row row_t + 64 c (wraps back for c >= 1)
+  const uint16_t* const k_c0 = stg0 ? a.sm.sk : a.k;
+  const uint16_t* const q_c0 = stg0 ? a.sm.sq : a.q;
+  const uint16_t* const v_c0 = stg0 ? a.sm.sv : a.v;
+  const float* const b_c0 = stg0 ? a.sm.sb : a.beta;
+  const uint32_t HD32 = uint32_t(HD);
   auto tok_ok = [&](int c, int i) { return c * PC + i < Tb; };
-  auto tok_ld = [&](int c, int i) { return size_t(c * PC + i < Tb ? c * PC + i : Tb - 1); };
+  // chunk c's first row (scalar, 64-bit) and the in-chunk row a lane reads
+  // (32-bit, clamped into the sequence)
+  auto chunk_row = [&](int c) { return c == 0 ? row_c0 : row_t + size_t(c) * PC; };
+  auto in_row = [&](int c, int i) {
+    const int lim = Tb - 1 - c * PC;
+    return uint32_t(i < lim ? i : lim);
+  };
   int kq_c = 0, tv_c = 0;  // the chunks the prefetch registers hold
 
   // (clang vector types: arrays of HIP's uint4 are copied through memory)
@@ -562,10 +598,14 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   float gv = 0.f, bv = 0.f;
   auto load_kq = [&](int c) {
     kq_c = c;
-    k0 = *reinterpret_cast<const u32x4*>(kb + tok_ld(c, 2 * pm) * HD);
-    k1 = *reinterpret_cast<const u32x4*>(kb + tok_ld(c, 2 * pm + 1) * HD);
-    q0 = *reinterpret_cast<const u32x4*>(qb + tok_ld(c, 2 * pm) * HD);
-    q1 = *reinterpret_cast<const u32x4*>(qb + tok_ld(c, 2 * pm + 1) * HD);
+    const size_t cr = chunk_row(c) * HD + kq_off;
+    const uint16_t* kb = (c == 0 ? k_c0 : a.k) + cr;
+    const uint16_t* qb = (c == 0 ? q_c0 : a.q) + cr;
+    const uint32_t o0 = in_row(c, 2 * pm) * HD32, o1 = in_row(c, 2 * pm + 1) * HD32;
+    k0 = *reinterpret_cast<const u32x4*>(kb + o0);
+    k1 = *reinterpret_cast<const u32x4*>(kb + o1);
+    q0 = *reinterpret_cast<const u32x4*>(qb + o0);
+    q1 = *reinterpret_cast<const u32x4*>(qb + o1);
   };
   auto load_tv = [&](int c) {
     tv_c = c;
@@ -573,10 +613,13 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
     t0 = *reinterpret_cast<const u32x4*>(tp);
     t1 = *reinterpret_cast<const u32x4*>(tp + PC * PC);
     t2 = *reinterpret_cast<const u32x4*>(tp + 2 * PC * PC);
+    const size_t cr = chunk_row(c);
+    const uint16_t* vb = (c == 0 ? v_c0 : a.v) + cr * HD + v_off;
+    const float* bb = (c == 0 ? b_c0 : a.beta) + cr * a.H + h;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v4[q] = vb[tok_ld(c, vi + q) * HD];
+    for (int q = 0; q < 4; ++q) v4[q] = vb[in_row(c, vi + q) * HD32];
     gv = gb[size_t(c) * a.H * PC];  // every side lane loads (one wave's worth is used): no branch
-    bv = bb[tok_ld(c, st & 63) * a.H];
+    bv = bb[in_row(c, st & 63) * uint32_t(a.H)];
   };
   auto stage_kq = [&]() {
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -629,9 +672,10 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   __syncthreads();
 
   const int it = sw >> 1, i0 = it * 16 + 4 * lq, nks = (it >> 1) + 1;
-  // this sequence's outputs, bounded at its T tokens
+  // this sequence's outputs, bounded at its new tokens (a buffered prefix has
+  // no outputs here: decode gave them)
   const rsrc_t o_rsrc = make_rsrc(static_cast<char*>(a.o) + tokb * HD * (OUT_BF16 ? 2 : 4),
-                                  uint32_t(size_t(Tb) * HD * (OUT_BF16 ? 2 : 4)));
+                                  uint32_t(size_t(Tb - npre) * HD * (OUT_BF16 ? 2 : 4)));
   for (int c = 0; c < NC; ++c) {
     const float* gc = G + 192 * (c & 1);
     // ---- A: output base diag(gamma s) Q S0^T of this wave's (token tile, row tile)
@@ -674,12 +718,13 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {  // stores past the sequence (padding tokens) are dropped
-        const uint32_t oi = uint32_t((size_t(c) * PC + i0 + q) * HD + size_t(h) * PD + r0 + vr);
+        const int tk = c * PC + i0 + q - npre;  // new token of this position (< 0: buffered, no output)
+        const uint32_t oi = uint32_t(tk) * HD32 + uint32_t(h * PD + r0 + vr);
         const float ov = os[q] + acc[q];
         if constexpr (OUT_BF16)
-          __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(ov)), o_rsrc, oi * 2, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(ov)), o_rsrc, tk >= 0 ? oi * 2 : 0xfffffff0u, 0, 0);
         else
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), o_rsrc, oi * 4, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), o_rsrc, tk >= 0 ? oi * 4 : 0xfffffff0u, 0, 0);
       }
     }
     stage_tv((c + 1) & 1);
@@ -698,23 +743,35 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
 }
 
 // Chunks the workspace holds: B ceil(T / 64) for uniform lengths; for
-// variable lengths summing to T, sum ceil(len / 64) <= floor(T / 64) + B.
+// variable lengths summing to N new tokens, sum ceil(n / 64) <= floor(N / 64)
+// + B, and with a buffered prefix of at most 63 writes per sequence,
+// sum ceil((pre + n) / 64) <= floor(N / 64) + 2 B.
+static size_t gdn_new_tokens(const PrefillLaunch& L) { return L.varlen ? size_t(L.T) : size_t(L.B) * L.T; }
 static size_t gdn_chunks(const PrefillLaunch& L) {
+  if (L.resume) return gdn_new_tokens(L) / PC + 2 * size_t(L.B);
   return L.varlen ? size_t(L.T / PC) + size_t(L.B) : size_t(L.B) * ((L.T + PC - 1) / PC);
 }
 static size_t gdn_ws_T(const PrefillLaunch& L) { return gdn_chunks(L) * L.H * 3 * PC * PC * 2; }
 static size_t gdn_ws_g(const PrefillLaunch& L) { return gdn_chunks(L) * L.H * PC * 4; }
-static size_t gdn_ws_map(const PrefillLaunch& L) { return L.varlen ? 2 * (size_t(L.B) + 1) * 4 : 0; }
+// staged chunk 0 when resuming: k, q, v bf16 [B][64][H][128], alpha, beta fp32 [B][64][H]
+static size_t gdn_ws_stage(const PrefillLaunch& L) {
+  return L.resume ? size_t(L.B) * PC * L.H * (3 * PD * 2 + 2 * 4) : 0;
+}
+static bool gdn_mapped(const PrefillLaunch& L) { return L.varlen || L.resume; }
+static size_t gdn_ws_map(const PrefillLaunch& L) { return gdn_mapped(L) ? (3 * size_t(L.B) + 2) * 4 : 0; }
 
-// Sequence map of a variable-length batch, one workgroup: token offsets
-// tok[i] = the running maximum of cu[i] clamped to [0, T] (so lengths are
-// never negative and never reach past the tokens), chunk offsets ch[i] =
-// sum over the earlier sequences of ceil(len / 64).  A well-formed cu
-// (0 = cu[0] <= ... <= cu[B] = T) passes through unchanged.
+// Sequence map, one workgroup.  Token offsets tok[i]: with cu, the running
+// maximum of cu[i] clamped to [0, T] (so lengths are never negative and
+// never reach past the tokens), else i T.  Prefixes pre[i]: fill[i] clamped
+// to [0, 63], or 0.  Chunk offsets ch[i]: the sum over the earlier sequences
+// of ceil((pre + n) / 64).  A well-formed cu (0 = cu[0] <= ... <= cu[B] = T)
+// and fills in [0, 63] pass through unchanged.
 struct SeqMapArgs {
   const int32_t* cu;
+  const int32_t* fill;
   int32_t* tok;
   int32_t* ch;
+  int32_t* pre;
   int B, T;
 };
 
@@ -722,11 +779,12 @@ __global__ __launch_bounds__(1024) void gdn_seqmap_kernel(SeqMapArgs a) {
   __shared__ int32_t sv[1025];
   __shared__ int32_t sc[1024];
   const int t = threadIdx.x;
+  auto off = [&](int i) { return a.cu ? min(max(a.cu[i], 0), a.T) : i * a.T; };
   int carry_tok = 0, carry_ch = 0;
   for (int base = 0; base <= a.B; base += 1024) {
-    // running maximum of the clamped offsets base .. base + 1024
+    // running maximum of the offsets base .. base + 1024
     const int i = base + t;
-    int x = i <= a.B ? min(max(a.cu[i], 0), a.T) : a.T;
+    int x = i <= a.B ? off(i) : INT_MAX;
     if (base > 0) x = max(x, carry_tok);
     sv[t] = x;
     __syncthreads();
@@ -736,10 +794,11 @@ __global__ __launch_bounds__(1024) void gdn_seqmap_kernel(SeqMapArgs a) {
       sv[t] = max(sv[t], y);
       __syncthreads();
     }
-    if (t == 0) sv[1024] = base + 1024 <= a.B ? max(min(max(a.cu[base + 1024], 0), a.T), sv[1023]) : a.T;
+    if (t == 0) sv[1024] = base + 1024 <= a.B ? max(off(base + 1024), sv[1023]) : INT_MAX;
     __syncthreads();
-    // chunks of sequence i, then their exclusive running sum
-    const int n = i < a.B ? (sv[t + 1] - sv[t] + PC - 1) / PC : 0;
+    // positions of sequence i, its chunks, then their exclusive running sum
+    const int p = i < a.B && a.fill ? min(max(a.fill[i], 0), PC - 1) : 0;
+    const int n = i < a.B ? (p + sv[t + 1] - sv[t] + PC - 1) / PC : 0;
     sc[t] = n;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {
@@ -752,15 +811,81 @@ __global__ __launch_bounds__(1024) void gdn_seqmap_kernel(SeqMapArgs a) {
       a.tok[i] = sv[t];
       a.ch[i] = carry_ch + sc[t] - n;
     }
+    if (i < a.B) a.pre[i] = p;
     carry_tok = sv[1023];
     carry_ch += sc[1023];
     __syncthreads();
   }
 }
 
-// Hand-over to decode: the last r = len mod 64 tokens' writes of each
-// sequence go to slots 0 .. r-1 of its window buffer (fp32, keys in the
-// state's basis) and its fill becomes r.  One workgroup per (sequence, head).
+// Chunk 0 of every sequence when resuming, laid out like the tokens: its
+// pre buffered writes (fp32 in decode's window buffer, entered at bf16 like
+// every prefill token; no query, no output), then its first new tokens, then
+// padding (k = q = v = 0, alpha = 1, beta = 0).  One workgroup per
+// (sequence, head).
+struct StageArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* alpha;
+  const float* beta;
+  const float* buf_k;
+  const float* buf_v;
+  const float* buf_alpha;
+  const float* buf_beta;
+  uint16_t* sk;
+  uint16_t* sq;
+  uint16_t* sv;
+  float* sa;
+  float* sb;
+  SeqMap sm;
+  int B, H, W;
+};
+
+__global__ __launch_bounds__(256) void gdn_stage_kernel(StageArgs a) {
+  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  const int pre = a.sm.npre(b), n = a.sm.ntok(b);
+  const size_t tok0 = a.sm.tok0(b);
+  const size_t HD = size_t(a.H) * PD;
+  for (int e = threadIdx.x; e < PC * PD / 2; e += 256) {  // two dims per thread
+    const int pos = e / (PD / 2), d = 2 * (e % (PD / 2));
+    uint32_t kw = 0u, qw = 0u, vw = 0u;
+    if (pos < pre) {
+      const size_t src = (size_t(bh) * a.W + pos) * PD + d;
+      const float2 kf = *reinterpret_cast<const float2*>(a.buf_k + src);
+      const float2 vf = *reinterpret_cast<const float2*>(a.buf_v + src);
+      kw = f32_to_bf16_bits(kf.x) | (f32_to_bf16_bits(kf.y) << 16);
+      vw = f32_to_bf16_bits(vf.x) | (f32_to_bf16_bits(vf.y) << 16);
+    } else if (pos - pre < n) {
+      const size_t src = (tok0 + (pos - pre)) * HD + size_t(h) * PD + d;
+      kw = *reinterpret_cast<const uint32_t*>(a.k + src);
+      qw = *reinterpret_cast<const uint32_t*>(a.q + src);
+      vw = *reinterpret_cast<const uint32_t*>(a.v + src);
+    }
+    const size_t dst = ((size_t(b) * PC + pos) * a.H + h) * PD + d;
+    *reinterpret_cast<uint32_t*>(a.sk + dst) = kw;
+    *reinterpret_cast<uint32_t*>(a.sq + dst) = qw;
+    *reinterpret_cast<uint32_t*>(a.sv + dst) = vw;
+  }
+  for (int pos = threadIdx.x; pos < PC; pos += 256) {
+    float al = 1.f, be = 0.f;
+    if (pos < pre) {
+      al = a.buf_alpha[size_t(bh) * a.W + pos];
+      be = a.buf_beta[size_t(bh) * a.W + pos];
+    } else if (pos - pre < n) {
+      al = a.alpha[(tok0 + (pos - pre)) * a.H + h];
+      be = a.beta[(tok0 + (pos - pre)) * a.H + h];
+    }
+    a.sa[(size_t(b) * PC + pos) * a.H + h] = al;
+    a.sb[(size_t(b) * PC + pos) * a.H + h] = be;
+  }
+}
+
+// Hand-over to decode: with r = len mod 64 for a sequence of len positions,
+// its last r positions' writes go to slots 0 .. r-1 of its window buffer
+// (fp32, keys in the state's basis) and its fill becomes r.  Slots that
+// already hold a buffered prefix write (when resuming, before any window
+// closed) are left as they are.  One workgroup per (sequence, head).
 struct HandoffArgs {
   const uint16_t* k;
   const uint16_t* v;
@@ -777,38 +902,62 @@ struct HandoffArgs {
 
 __global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
   const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
-  const int len = a.sm.len(b);
+  const int len = a.sm.len(b), pre = a.sm.npre(b);
   const int r = len % PC;
-  const size_t t0 = a.sm.tok0(b) + size_t(len - r);
-  for (int e = threadIdx.x; e < r * PD; e += 256) {
-    const int slot = e / PD, d = e % PD;
-    const size_t src = ((t0 + slot) * a.H + h) * PD + d;
+  const int p0 = len - r;  // position of slot 0
+  const int s0 = max(pre - p0, 0);  // first slot that takes a new token
+  const size_t t0 = a.sm.tok0(b);
+  for (int e = threadIdx.x; e < (r - s0) * PD; e += 256) {
+    const int slot = s0 + e / PD, d = e % PD;
+    const size_t src = ((t0 + (p0 + slot - pre)) * a.H + h) * PD + d;
     const size_t dst = (size_t(bh) * a.W + slot) * PD + d;
     a.buf_k[dst] = __uint_as_float(uint32_t(a.k[src]) << 16);
     a.buf_v[dst] = __uint_as_float(uint32_t(a.v[src]) << 16);
   }
-  for (int slot = threadIdx.x; slot < r; slot += 256) {
-    const size_t src = (t0 + slot) * a.H + h;
+  for (int slot = s0 + threadIdx.x; slot < r; slot += 256) {
+    const size_t src = (t0 + (p0 + slot - pre)) * a.H + h;
     a.buf_alpha[size_t(bh) * a.W + slot] = a.alpha[src];
     a.buf_beta[size_t(bh) * a.W + slot] = a.beta[src];
   }
   if (h == 0 && threadIdx.x == 0) a.fill_out[b] = r;
 }
 
-size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L) { return gdn_ws_T(L) + gdn_ws_g(L) + gdn_ws_map(L); }
+size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L) {
+  return gdn_ws_T(L) + gdn_ws_g(L) + gdn_ws_stage(L) + gdn_ws_map(L);
+}
 
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
-  __bf16* T_ws = static_cast<__bf16*>(L.workspace);
-  float* g_ws = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + gdn_ws_T(L));
-  SeqMap sm{nullptr, nullptr, L.T};
-  if (L.varlen) {
-    int32_t* tok = reinterpret_cast<int32_t*>(static_cast<char*>(L.workspace) + gdn_ws_T(L) + gdn_ws_g(L));
+  char* ws = static_cast<char*>(L.workspace);
+  __bf16* T_ws = reinterpret_cast<__bf16*>(ws);
+  float* g_ws = reinterpret_cast<float*>(ws + gdn_ws_T(L));
+  SeqMap sm{};
+  sm.T = L.T;
+  if (gdn_mapped(L)) {
+    char* st = ws + gdn_ws_T(L) + gdn_ws_g(L);
+    int32_t* tok = reinterpret_cast<int32_t*>(st + gdn_ws_stage(L));
     int32_t* ch = tok + (L.B + 1);
-    SeqMapArgs m{L.cu_seqlens, tok, ch, L.B, L.T};
+    int32_t* pre = ch + (L.B + 1);
+    SeqMapArgs m{L.cu_seqlens, L.resume ? L.fill_in : nullptr, tok, ch, pre, L.B, L.T};
     hipLaunchKernelGGL(gdn_seqmap_kernel, dim3(1), dim3(1024), 0, stream, m);
     if (hipError_t e = hipGetLastError()) return e;
     sm.tok = tok;
     sm.ch = ch;
+    if (L.resume) {
+      const size_t nstage = size_t(L.B) * PC * L.H;
+      uint16_t* sk = reinterpret_cast<uint16_t*>(st);
+      uint16_t* sq = sk + nstage * PD;
+      uint16_t* sv = sq + nstage * PD;
+      float* sa = reinterpret_cast<float*>(sv + nstage * PD);
+      float* sb = sa + nstage;
+      StageArgs g{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k),
+                  static_cast<const uint16_t*>(L.v), L.alpha, L.beta, L.buf_k, L.buf_v, L.buf_alpha,
+                  L.buf_beta, sk, sq, sv, sa, sb, sm, L.B, L.H, L.W};
+      g.sm.pre = pre;  // the staging kernel reads the prefixes, not yet the staged copy
+      hipLaunchKernelGGL(gdn_stage_kernel, dim3(unsigned(L.B) * L.H), dim3(256), 0, stream, g);
+      if (hipError_t e = hipGetLastError()) return e;
+      sm.pre = pre;
+      sm.sk = sk; sm.sq = sq; sm.sv = sv; sm.sa = sa; sm.sb = sb;
+    }
   }
   const size_t nch = gdn_chunks(L);
   if (nch > 0) {

@@ -300,6 +300,54 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=No
     return o, st
 
 
+def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=torch.bfloat16,
+                   o=None, workspace=None):
+    """Continue every sequence of a DecodeState (fp32 window buffer, window
+    64) with new tokens by chunked prefill, at whatever fill each sequence
+    is (see gdnq_prefill_resume in include/gdnq.h).  Uniform: q, k
+    [B,T,H,d_k], v [B,T,H,d_v], alpha, beta [B,T,H]; packed: [T,...] with
+    cu_seqlens (int32, B+1 offsets).  Updates the state in place (codes,
+    scales, buffer, fill) and returns o for the new tokens."""
+    dev = q.device
+    st = state
+    B, H, d_v, d_k = st.codes.shape
+    if st.buf_k.dtype != torch.float32 or st.window != 64:
+        raise ValueError("state: a DecodeState with an fp32 window buffer of 64 slots")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, dev)
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        _need(t, name, torch.float32, dev)
+    if cu_seqlens is None:
+        T = q.shape[1]
+        lead = (B, T)
+        if q.dim() != 4 or q.shape[0] != B:
+            raise ValueError("q: [B,T,H,d_k] for the state's B sequences")
+    else:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() != B + 1:
+            raise ValueError("cu_seqlens: B+1 offsets for the state's B sequences")
+        T = q.shape[0]
+        lead = (T,)
+    if (tuple(q.shape) != lead + (H, d_k) or tuple(k.shape) != lead + (H, d_k)
+            or tuple(v.shape) != lead + (H, d_v) or tuple(alpha.shape) != lead + (H,)
+            or tuple(beta.shape) != lead + (H,)):
+        raise ValueError("inconsistent resume shapes")
+    p = _lib.PrefillParams(B, T, H, d_k, d_v, 64, 64, _DT[q.dtype], _DT[out_dtype], 0)
+    if o is None:
+        o = torch.empty(lead + (H, d_v), dtype=out_dtype, device=dev)
+    _need(o, "o", out_dtype, dev)
+    need = int(_lib.prefill_resume_workspace_size(p, cu_seqlens is not None))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _lib.check(_lib.prefill_resume(p, _ptr(cu_seqlens), _ptr(st.fill), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(alpha), _ptr(beta), _ptr(o), _ptr(st.codes), _ptr(st.scales),
+                                   _ptr(st.buf_k), _ptr(st.buf_v), _ptr(st.buf_alpha),
+                                   _ptr(st.buf_beta), _ptr(st.fill), _ptr(workspace), ws_bytes,
+                                   _stream(dev)))
+    return o
+
+
 def fp8_window_buffer(B, H, W, d, device):
     """One FP8 window buffer: E4M3 codes [B,H,W,d] followed, in the same
     allocation, by the per-vector fp32 scales [B,H,W].  Returns (codes view,

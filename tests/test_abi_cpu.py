@@ -291,7 +291,7 @@ def test_varlen_contract():
     f = Fake()
     B, T, H = 5, 300, 3
     p = _pp(B=B, T=T, H=H)
-    assert _lib.prefill_varlen_workspace_size(p) == (T // 64 + B) * H * (3 * 64 * 64 * 2 + 64 * 4) + 2 * (B + 1) * 4
+    assert _lib.prefill_varlen_workspace_size(p) == (T // 64 + B) * H * (3 * 64 * 64 * 2 + 64 * 4) + (3 * B + 2) * 4
     ws = f()
     need = _lib.prefill_varlen_workspace_size(p)
     assert _varlen(p, f) == 6                                   # workspace missing
@@ -309,3 +309,51 @@ def test_output_offset_bound_counts_padding():
     limit is (T + 64) H 512 bytes < 4 GiB."""
     assert _lib.prefill_handoff_workspace_size(_pp(T=(1 << 23) - 64, H=1)) == 0
     assert _lib.prefill_handoff_workspace_size(_pp(T=(1 << 23) - 128, H=1)) > 0
+
+
+# ---------------------------------------------------------------- resuming from decode
+def _resume(params, fake, cu=None, fill_in="fake", **over):
+    a = dict(q=fake(), k=fake(), v=fake(), alpha=fake(), beta=fake(), o=fake(), codes=fake(),
+             scales=fake(), buf_k=fake(), buf_v=fake(), buf_alpha=fake(), buf_beta=fake(),
+             fill_out=fake(), workspace=None, ws=0)
+    a.update(over)
+    fi = fake() if fill_in == "fake" else fill_in
+    return _lib.prefill_resume(params, cu, fi, a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["o"],
+                               a["codes"], a["scales"], a["buf_k"], a["buf_v"], a["buf_alpha"],
+                               a["buf_beta"], a["fill_out"], a["workspace"], a["ws"], None)
+
+
+@pytest.mark.parametrize("params,status", [
+    (_pp(C=32, W=32), 2), (_pp(dk=64, dv=64), 2), (_pp(ind=0), 3),
+    (_pp(flags=1), 8), (_pp(dv=64, flags=2 | 1 | 4), 8),   # GDN only
+    (_pp(B=1 << 16, T=1 << 16), 2),                        # 2^32 new tokens
+])
+def test_resume_rejects_bad_params(params, status):
+    assert _resume(params, Fake()) == status
+    assert _lib.prefill_resume_workspace_size(params, 0) == 0
+
+
+def test_resume_contract():
+    """The workspace bounds the chunks by floor(N / 64) + 2 B per head for N
+    new tokens (a prefix adds at most one chunk per sequence), plus chunk 0
+    of every sequence staged and the sequence map; fill_in is required and
+    may be fill_out itself but no other written buffer; the stored state is
+    required."""
+    f = Fake()
+    B, T, H = 3, 100, 2
+    p = _pp(B=B, T=T, H=H)
+    stage = B * 64 * H * (3 * 128 * 2 + 2 * 4)
+    need = (B * T // 64 + 2 * B) * H * (3 * 64 * 64 * 2 + 64 * 4) + stage + (3 * B + 2) * 4
+    assert _lib.prefill_resume_workspace_size(p, 0) == need
+    need_v = (T // 64 + 2 * B) * H * (3 * 64 * 64 * 2 + 64 * 4) + stage + (3 * B + 2) * 4
+    assert _lib.prefill_resume_workspace_size(p, 1) == need_v
+    ws = f()
+    assert _resume(p, f) == 6                                    # workspace missing
+    assert _resume(p, f, fill_in=None, workspace=ws, ws=need) == 1
+    assert _resume(p, f, fill_in=f() + 2, workspace=ws, ws=need) == 4
+    o = f()
+    assert _resume(p, f, fill_in=o, o=o, workspace=ws, ws=need) == 5
+    fo = f()
+    assert _resume(p, f, fill_in=fo, fill_out=fo) == 6           # same array: past the alias checks
+    assert _resume(p, f, codes=None, workspace=ws, ws=need) == 1
+    assert _resume(_pp(B=0, T=0), f) == 0                       # no sequences: no-op
