@@ -211,73 +211,137 @@ def ssd_prefill_bytes(B, T, H, dk=128, dv=64):
 
 def bench_prefill(torch, ops, wl, steps=5, warmup=2):
     """Secondary: GDN chunked prefill B=4, T=8192, H=16, d=128, C=W=64 (bf16
-    output, zero initial state) and SSD prefill B=2, T=4096, H=80, d_k=128,
-    d_v=64 with WHT-rotated int8 q/k (bf16 output).  Inputs and workspace
-    are resident before timing; each call is timed whole (all its kernels)."""
+    output, zero initial state); SSD prefill B=2, T=4096, H=80, d_k=128,
+    d_v=64 with WHT-rotated int8 q/k (bf16 output); the GDN hand-over to
+    decode (T = 8192 + 37); a packed batch of 32 sequences of seeded lengths
+    U{1..2047} (H=16); and resuming 4 decode states at fills U{0..63} with
+    8192 new tokens each.  Inputs and workspace are resident before timing;
+    each call is timed whole (all its kernels)."""
     dev = torch.device("cuda:0")
     res = {}
-    cases = [
-        ("gdn_prefill", dict(B=4, T=8192, H=16, dk=128, dv=128), False),
-        ("ssd_prefill", dict(B=2, T=4096, H=80, dk=128, dv=64), True),
-        ("gdn_prefill_handoff", dict(B=4, T=8192 + 37, H=16, dk=128, dv=128), False),
-    ]
-    for name, shp, ssd in cases:
-        handoff = name.endswith("handoff")
-        x = (wl.ssd_prefill if ssd else wl.gdn_prefill)(**shp, seed=0)
-        q = torch.from_numpy(x["q"]).to(dev).bfloat16()
-        k = torch.from_numpy(x["k"]).to(dev).bfloat16()
-        v = torch.from_numpy(x["v"]).to(dev).bfloat16()
-        a = torch.from_numpy(x["alpha"]).to(dev)
-        bt = None if ssd else torch.from_numpy(x["beta"]).to(dev)
-        del x
-        Bq, T, Hh, dk = q.shape
-        dv = v.shape[-1]
-        if handoff:  # the open last window (T mod 64 writes) goes to decode's buffer
-            kw = dict(o=torch.empty((Bq, T, Hh, dv), dtype=torch.bfloat16, device=dev))
-            _, kw["state"] = ops.prefill_handoff(q, k, v, a, bt, **kw)
-            call = ops.prefill_handoff
+    names = ["gdn_prefill", "ssd_prefill", "gdn_prefill_handoff", "gdn_prefill_varlen",
+             "gdn_prefill_resume"]
+    H16, d = 16, 128
+    state_bytes = d * (d + 4)  # int8 rows + fp32 scales of one head
+
+    def t(x, bf16=False):
+        y = torch.from_numpy(x).to(dev)
+        return y.bfloat16() if bf16 else y
+
+    for name in names:
+        ssd = name == "ssd_prefill"
+        if name == "gdn_prefill_varlen":
+            lengths = np.random.default_rng(5).integers(1, 2048, 32)
+            x = wl.gdn_prefill_varlen(lengths, H=H16, dk=d, dv=d, seed=0)
+        elif name == "ssd_prefill":
+            x = wl.ssd_prefill(B=2, T=4096, H=80, dk=128, dv=64, seed=0)
         else:
-            kw = dict(ssd=True, wht=True, int8_qk=True) if ssd else dict(window=64)
-            kw["workspace"] = torch.empty(ops.prefill_workspace_size(q, v, **kw), dtype=torch.uint8, device=dev)
-            kw["o"] = torch.empty((Bq, T, Hh, dv), dtype=torch.bfloat16, device=dev)
-            if ssd:
-                kw["state_f32"] = torch.empty((Bq, Hh, dv, dk), dtype=torch.float32, device=dev)
+            T = 8192 + 37 if name == "gdn_prefill_handoff" else 8192
+            x = wl.gdn_prefill(B=4, T=T, H=H16, dk=d, dv=d, seed=0)
+        q, k, v = t(x["q"], True), t(x["k"], True), t(x["v"], True)
+        a = t(x["alpha"])
+        bt = None if ssd else t(x["beta"])
+        dk, dv = q.shape[-1], v.shape[-1]
+        Hh = q.shape[-2]
+        extra_bytes = 0
+        if name == "gdn_prefill_varlen":
+            cu = t(x["cu_seqlens"])
+            N, nseq = int(q.shape[0]), len(lengths)
+            chunks = int(sum((int(n) + 63) // 64 for n in lengths))
+            o = torch.empty((N, Hh, dv), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(ops.prefill_varlen_workspace_size(q, v, nseq), dtype=torch.uint8, device=dev)
+            _, st = ops.prefill_varlen(q, k, v, a, bt, cu, o=o, workspace=ws)
+
+            def call():
+                ops.prefill_varlen(q, k, v, a, bt, cu, o=o, state=st, workspace=ws)
+            workload = (f"{nseq} packed sequences of seeded lengths U{{1..2047}} ({N} tokens), H={Hh} "
+                        f"d_k={dk} d_v={dv} chunk=window=64, int8 state, each handed over to decode")
+            tokens = N
+        elif name == "gdn_prefill_resume":
+            Bq, T = q.shape[0], q.shape[1]
+            nseq, N = Bq, Bq * T
+            g = np.random.default_rng(6)
+            fills = g.integers(0, 64, Bq).astype(np.int32)
+            S = (g.standard_normal((Bq, Hh, dv, dk)) * 0.5).astype(np.float32)
+            codes = torch.empty((Bq, Hh, dv, dk), dtype=torch.int8, device=dev)
+            scales = torch.empty((Bq, Hh, dv), dtype=torch.float32, device=dev)
+            ops.quantize_state(t(S), codes, scales)
+            st = ops.DecodeState(codes, scales, 64, fill=t(fills))
+            for buf in (st.buf_k, st.buf_v):  # bf16 values, as decode stores from bf16 inputs
+                buf.copy_(torch.nn.functional.normalize(torch.randn(buf.shape, device=dev), dim=-1)
+                          .bfloat16().float())
+            st.buf_alpha.fill_(0.95)
+            st.buf_beta.fill_(0.5)
+            chunks = int(sum((int(f) + T + 63) // 64 for f in fills))
+            o = torch.empty((Bq, T, Hh, dv), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(ops.prefill_resume_workspace_size(q, v, Bq), dtype=torch.uint8, device=dev)
+
+            def call():  # T is whole windows, so every call starts at the same fills
+                ops.prefill_resume(st, q, k, v, a, bt, o=o, workspace=ws)
+            extra_bytes = nseq * Hh * state_bytes + int(fills.sum()) * Hh * (4 * (dk + dv) + 8)
+            workload = (f"B={Bq} decode states at fills U{{0..63}} resumed with T={T} new tokens each, "
+                        f"H={Hh} d_k={dk} d_v={dv} chunk=window=64, int8 state")
+            tokens = N
+        else:
+            Bq, T = q.shape[0], q.shape[1]
+            nseq, N = Bq, Bq * T
+            chunks = Bq * ((T + 63) // 64)
+            o = torch.empty((Bq, T, Hh, dv), dtype=torch.bfloat16, device=dev)
+            if name == "gdn_prefill_handoff":  # the open last window (T mod 64 writes) goes to decode's buffer
+                ws = torch.empty(ops.prefill_handoff_workspace_size(q, v), dtype=torch.uint8, device=dev)
+                _, st = ops.prefill_handoff(q, k, v, a, bt, o=o, workspace=ws)
+
+                def call():
+                    ops.prefill_handoff(q, k, v, a, bt, o=o, state=st, workspace=ws)
             else:
-                kw["codes"] = torch.empty((Bq, Hh, dv, dk), dtype=torch.int8, device=dev)
-                kw["scales"] = torch.empty((Bq, Hh, dv), dtype=torch.float32, device=dev)
-            call = ops.prefill_chunked
-        if handoff:
-            kw["workspace"] = torch.empty(ops.prefill_handoff_workspace_size(q, v), dtype=torch.uint8,
-                                          device=dev)
+                kw = dict(ssd=True, wht=True, int8_qk=True) if ssd else dict(window=64)
+                kw["workspace"] = torch.empty(ops.prefill_workspace_size(q, v, **kw), dtype=torch.uint8,
+                                              device=dev)
+                kw["o"] = o
+                if ssd:
+                    kw["state_f32"] = torch.empty((Bq, Hh, dv, dk), dtype=torch.float32, device=dev)
+                else:
+                    kw["codes"] = torch.empty((Bq, Hh, dv, dk), dtype=torch.int8, device=dev)
+                    kw["scales"] = torch.empty((Bq, Hh, dv), dtype=torch.float32, device=dev)
+
+                def call():
+                    ops.prefill_chunked(q, k, v, a, bt, **kw)
+            workload = (f"B={Bq} T={T} H={Hh} d_k={dk} d_v={dv} chunk=64"
+                        + (" WHT+int8 q/k, fp32 state" if ssd else " window=64, int8 state")
+                        + (f", the last {T % 64} tokens' writes handed to decode's window buffer"
+                           if name == "gdn_prefill_handoff" else ""))
+            tokens = N
+        del x
         for _ in range(warmup):
-            call(q, k, v, a, bt, **kw)
+            call()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream(dev)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
-            call(q, k, v, a, bt, **kw)
+            call()
         e1.record(stream)
         e1.synchronize()
         ms = e0.elapsed_time(e1) / steps
-        flops = (ssd_prefill_flops if ssd else gdn_prefill_flops)(Bq, T, Hh, dk, dv)
-        nbytes = (ssd_prefill_bytes if ssd else gdn_prefill_bytes)(Bq, T, Hh, dk, dv)
+        if ssd:
+            flops = ssd_prefill_flops(1, 64 * chunks, Hh, dk, dv)
+            nbytes = ssd_prefill_bytes(1, N, Hh, dk, dv) + (nseq - 1) * Hh * dv * dk * 4
+        else:
+            flops = gdn_prefill_flops(1, 64 * chunks, Hh, dk, dv)
+            nbytes = gdn_prefill_bytes(1, N, Hh, dk, dv) + (nseq - 1) * Hh * state_bytes + extra_bytes
         tflops = flops / (ms * 1e-3) / 1e12
         gbps = nbytes / (ms * 1e-3) / 1e9
         res[name] = {
-            "workload": (f"B={Bq} T={T} H={Hh} d_k={dk} d_v={dv} chunk=64"
-                         + (" WHT+int8 q/k, fp32 state" if ssd else " window=64, int8 state")
-                         + (f", the last {T % 64} tokens' writes handed to decode's window buffer"
-                            if handoff else "")),
-            "ms": round(ms, 4), "tokens_s": round(Bq * T / (ms * 1e-3), 1),
+            "workload": workload,
+            "ms": round(ms, 4), "tokens_s": round(tokens / (ms * 1e-3), 1),
             "tflops": round(tflops, 2), "gbps": round(gbps, 1),
             "flops_per_call": flops, "bytes_per_call": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)},
             "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
         }
-        del q, k, v, a, bt, kw
+        del q, k, v, a, bt, o, call
         torch.cuda.empty_cache()
     return res
 

@@ -907,12 +907,23 @@ __global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
   const int p0 = len - r;  // position of slot 0
   const int s0 = max(pre - p0, 0);  // first slot that takes a new token
   const size_t t0 = a.sm.tok0(b);
-  for (int e = threadIdx.x; e < (r - s0) * PD; e += 256) {
-    const int slot = s0 + e / PD, d = e % PD;
+  for (int e = threadIdx.x; e < (r - s0) * (PD / 8); e += 256) {  // 8 dims per thread
+    const int slot = s0 + e / (PD / 8), d = 8 * (e % (PD / 8));
     const size_t src = ((t0 + (p0 + slot - pre)) * a.H + h) * PD + d;
     const size_t dst = (size_t(bh) * a.W + slot) * PD + d;
-    a.buf_k[dst] = __uint_as_float(uint32_t(a.k[src]) << 16);
-    a.buf_v[dst] = __uint_as_float(uint32_t(a.v[src]) << 16);
+    const uint4 kw = *reinterpret_cast<const uint4*>(a.k + src);
+    const uint4 vw = *reinterpret_cast<const uint4*>(a.v + src);
+    auto widen = [](uint32_t w, float& lo, float& hi) {
+      lo = __uint_as_float(w << 16);
+      hi = __uint_as_float(w & 0xffff0000u);
+    };
+    float4 k0, k1, v0, v1;
+    widen(kw.x, k0.x, k0.y); widen(kw.y, k0.z, k0.w); widen(kw.z, k1.x, k1.y); widen(kw.w, k1.z, k1.w);
+    widen(vw.x, v0.x, v0.y); widen(vw.y, v0.z, v0.w); widen(vw.z, v1.x, v1.y); widen(vw.w, v1.z, v1.w);
+    *reinterpret_cast<float4*>(a.buf_k + dst) = k0;
+    *reinterpret_cast<float4*>(a.buf_k + dst + 4) = k1;
+    *reinterpret_cast<float4*>(a.buf_v + dst) = v0;
+    *reinterpret_cast<float4*>(a.buf_v + dst + 4) = v1;
   }
   for (int slot = s0 + threadIdx.x; slot < r; slot += 256) {
     const size_t src = (t0 + (p0 + slot - pre)) * a.H + h;

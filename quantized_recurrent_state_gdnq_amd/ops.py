@@ -300,6 +300,15 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=No
     return o, st
 
 
+def prefill_resume_workspace_size(q, v, n_seqs, *, packed=False, out_dtype=torch.bfloat16):
+    """Workspace of prefill_resume: q [B,T,H,d_k] (n_seqs = B), or packed
+    q [T,H,d_k] of n_seqs sequences."""
+    T = q.shape[0] if packed else q.shape[1]
+    p = _lib.PrefillParams(n_seqs, T, q.shape[-2], q.shape[-1], v.shape[-1], 64, 64, _DT[q.dtype],
+                           _DT[out_dtype], 0)
+    return int(_lib.prefill_resume_workspace_size(p, packed))
+
+
 def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=torch.bfloat16,
                    o=None, workspace=None):
     """Continue every sequence of a DecodeState (fp32 window buffer, window
