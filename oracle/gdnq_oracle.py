@@ -64,20 +64,22 @@ F64 = np.float64
 # --------------------------------------------------------------------------
 # Codec  ([LQ] abstract: 8-bit recurrent state)
 # --------------------------------------------------------------------------
-def quantize_rows(x):
-    """Per-row symmetric int8 codec.  x[..., d] -> (codes int8[..., d], scale f32[...]).
+def quantize_rows(x, qmax=127):
+    """Per-row symmetric codec.  x[..., d] -> (codes int8[..., d], scale f32[...]).
 
-    scale = max|x| / 127 (fp32 division); codes = clamp(rne(x / scale), -127, 127);
+    scale = max|x| / qmax (fp32 division); codes = clamp(rne(x / scale), -qmax, qmax);
     a row whose max|x| is 0 gets scale 0 and codes 0.  The decision is taken
-    in fp32 whatever the input precision.
+    in fp32 whatever the input precision.  qmax = 127 is the 8-bit state;
+    qmax = 7 the uniform 4-bit state ([PW]'s "@4" configuration): the same
+    rule with 15 levels.
     """
     x32 = np.asarray(x).astype(F32)
     absmax = np.max(np.abs(x32), axis=-1)
-    scale = (absmax / F32(127.0)).astype(F32)
+    scale = (absmax / F32(qmax)).astype(F32)
     nonzero = scale > 0
     denom = np.where(nonzero, scale, F32(1.0)).astype(F32)
     ratio = (x32 / denom[..., None]).astype(F32)
-    codes = np.clip(np.rint(ratio), -127, 127)
+    codes = np.clip(np.rint(ratio), -qmax, qmax)
     codes = np.where(nonzero[..., None], codes, 0).astype(np.int8)
     return codes, scale
 
@@ -157,7 +159,7 @@ def _prepare_qk(q, k, rot, qk_int8, dtype):
 
 
 def run_windowed(q, k, v, alpha, beta=None, *, W, codes0=None, scale0=None,
-                 buffer0=None, kind="gdn", rot=False, qk_int8=False, dtype=F32):
+                 buffer0=None, kind="gdn", rot=False, qk_int8=False, dtype=F32, qmax=127):
     """Run T tokens of the windowed recurrence for N independent heads.
 
     q, k: [T, N, dk]; v: [T, N, dv]; alpha, beta: [T, N].
@@ -220,7 +222,7 @@ def run_windowed(q, k, v, alpha, beta=None, *, W, codes0=None, scale0=None,
         o[t] = np.matmul(S, q[t][..., :, None])[..., 0]
         n += 1
         if W is not None and n == W:
-            codes, scale = quantize_rows(S)
+            codes, scale = quantize_rows(S, qmax)
             S = dequantize(codes, scale, dtype)
             n = 0
             buf = {"k": [], "v": [], "alpha": [], "beta": []}
@@ -293,7 +295,7 @@ def quantize_e4m3_vector(x):
 
 
 def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha,
-                buf_beta, fill, W, rot=False, dtype=F32, buf_bf16=False, buf_fp8=False):
+                buf_beta, fill, W, rot=False, dtype=F32, buf_bf16=False, buf_fp8=False, qmax=127):
     """One decode token for a batch of sequences ([LQ] per-window quantization).
 
     q, k: [B,H,dk]; v: [B,H,dv]; alpha, beta: [B,H]; codes [B,H,dv,dk];
@@ -346,7 +348,7 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha,
             np.asarray(beta)[seqs].reshape(1, -1), W=W,
             codes0=np.asarray(codes)[seqs].reshape(-1, dv, dk),
             scale0=np.asarray(scales)[seqs].reshape(-1, dv),
-            buffer0=buffer0, kind="gdn", rot=rot, dtype=dtype)
+            buffer0=buffer0, kind="gdn", rot=rot, dtype=dtype, qmax=qmax)
         nb = len(seqs)
         o[seqs] = r["o"][0].reshape(nb, H, dv)
         codes_out[seqs] = r["codes"].reshape(nb, H, dv, dk)

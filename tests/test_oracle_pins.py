@@ -643,3 +643,62 @@ def test_buf_fp8_current_write_exact_and_stored_quantized():
                            x["alpha"][s_][None], x["beta"][s_][None], W=W, codes0=b[1][s_],
                            scale0=b[2][s_], buffer0=buf)
         assert np.array_equal(c[0][s_], r["o"][0])
+
+
+# ---------------------------------------------------------------- uniform 4-bit state
+def test_codec4_golden_rows():
+    """The 4-bit codec (scale = absmax / 7, codes = clamp(rne(x / scale),
+    -7, 7)) on rows worked by hand: with absmax 7 the scale is 1 and the
+    codes are x rounded half to even; with absmax 14 the scale is 2; a zero
+    row gets scale 0 (Low-Bit GDN ..., abstract: the "@4" budget; the
+    rule is the 8-bit one with 15 levels)."""
+    x = np.array([[3.5, -7.0, 1.75, 0.0, 0.25, 2.5, -0.5, 6.5],
+                  [14.0, -3.0, 5.0, 1.0, 0.0, -14.0, 13.0, 3.0],
+                  [0.0] * 8], F32)
+    codes, scale = O.quantize_rows(x, qmax=7)
+    assert scale.tolist() == [1.0, 2.0, 0.0]
+    assert codes.tolist() == [[4, -7, 2, 0, 0, 2, 0, 6],
+                              [7, -2, 2, 0, 0, -7, 6, 2],
+                              [0] * 8]
+
+
+def test_codec4_properties_random():
+    """Every code within [-7, 7]; the absmax entry maps to +-7; each entry
+    within half a step of code * scale."""
+    g = np.random.default_rng(41)
+    x = (g.standard_normal((200, 128)) * g.uniform(0.01, 10, (200, 1))).astype(F32)
+    codes, scale = O.quantize_rows(x, qmax=7)
+    assert np.abs(codes).max() <= 7
+    top = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.abs(codes[np.arange(200), top]) == 7)
+    err = np.abs(x.astype(F64) - codes.astype(F64) * scale[:, None].astype(F64))
+    assert np.all(err <= scale[:, None].astype(F64) * (0.5 + 1e-6))
+
+
+def test_decode_4bit_calls_equal_one_run():
+    """Decode calls with the 4-bit state equal one windowed run with the
+    4-bit codec (the same reading as for 8 bits), and every stored code
+    stays within [-7, 7]."""
+    g = np.random.default_rng(43)
+    B, H, d, W, T = 2, 2, 8, 4, 11
+    q, k, v, a, b = _rand_tokens(g, T, B * H, d, d)
+    r = O.run_windowed(q, k, v, a, b, W=W, qmax=7)
+    codes = np.zeros((B, H, d, d), np.int8)
+    scales = np.zeros((B, H, d), F32)
+    bk = np.full((B, H, W, d), np.nan, F32)
+    bv = np.full((B, H, W, d), np.nan, F32)
+    ba = np.full((B, H, W), np.nan, F32)
+    bb = np.full((B, H, W), np.nan, F32)
+    fill = np.zeros(B, np.int32)
+    rs = lambda x: x.reshape((B, H) + x.shape[1:])  # noqa: E731
+    for t in range(T):
+        ot, codes, scales, bk, bv, ba, bb, fill = O.decode_step(
+            rs(q[t]), rs(k[t]), rs(v[t]), rs(a[t]), rs(b[t]), codes, scales, bk, bv, ba, bb, fill, W,
+            qmax=7)
+        assert np.array_equal(ot.reshape(B * H, d), r["o"][t])
+        assert np.abs(codes).max() <= 7
+    assert np.array_equal(codes.reshape(B * H, d, d), r["codes"])
+    assert np.array_equal(scales.reshape(B * H, d), r["scale"])
+    # the 4-bit state is coarser: the same run at 8 bits differs
+    r8 = O.run_windowed(q, k, v, a, b, W=W)
+    assert not np.array_equal(r8["codes"], r["codes"])
