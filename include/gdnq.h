@@ -88,7 +88,7 @@ enum {
                              and the window's close replay the rounded write;
                              alpha and beta stay fp32.  Lossless when q, k, v
                              are bf16 and GDNQ_FLAG_WHT is off.              */
-  GDNQ_FLAG_BUF_FP8 = 32u  /* decode only: the window buffer keeps keys and
+  GDNQ_FLAG_BUF_FP8 = 32u, /* decode only: the window buffer keeps keys and
                              values as FP8 vector pairs (Low-Bit GDN ...,
                              abstract): each buffered key and each value is
                              OCP E4M3 codes (bias 7, largest finite 448) with
@@ -99,6 +99,15 @@ enum {
                              buf_k = B*H*W*d_k code bytes, then B*H*W fp32
                              scales; buf_v likewise with d_v.  Exclusive with
                              GDNQ_FLAG_BUF_BF16.                            */
+  GDNQ_FLAG_STATE_4BIT = 64u /* quantize and decode: the uniform 4-bit state
+                             (Low-Bit GDN ..., abstract: the "@4" budget of
+                             four bits per state entry).  The codec above with
+                             127 replaced by 7: scale = max|x| / 7, codes =
+                             clamp(round_half_even(x / scale), -7, 7).  Codes
+                             are packed two per byte: row-major [rows, d_k/2]
+                             bytes, column 2j in the low nibble of byte j,
+                             column 2j+1 in the high nibble, each a two's
+                             complement nibble.  Scales are unchanged.      */
 };
 
 /* ------------------------------------------------------------------------
@@ -106,10 +115,12 @@ enum {
  *   LeapQuant, abstract (8-bit recurrent state).
  *
  *   S       [rows, d_k] fp32, read only
- *   codes   [rows, d_k] int8, written
+ *   codes   [rows, d_k] int8, written ([rows, d_k/2] bytes of packed 4-bit
+ *           codes under GDNQ_FLAG_STATE_4BIT)
  *   scales  [rows]      fp32, written
- *   flags   0 or GDNQ_FLAG_WHT (rotate each row x -> H x / sqrt(d_k) first,
- *           i.e. quantize S H, the state in the rotated basis)
+ *   flags   GDNQ_FLAG_WHT (rotate each row x -> H x / sqrt(d_k) first,
+ *           i.e. quantize S H, the state in the rotated basis) and/or
+ *           GDNQ_FLAG_STATE_4BIT
  *   d_k in {64, 128}; rows >= 0 (rows == 0 is a no-op).
  *   Errors: NULL (any pointer, rows > 0), SHAPE, ALIGN, FLAGS, HIP.
  * ------------------------------------------------------------------------ */
@@ -136,12 +147,15 @@ gdnq_status gdnq_quantize_state(const float* S, int64_t rows, int32_t d_k, int8_
  *
  *   0 <= p->batch B <= 1024 (0: no-op), p->heads H >= 1, p->d_k, p->d_v in {64,128},
  *   1 <= p->window W <= 64, p->in_dtype (q,k,v) and p->out_dtype (o) in
- *   {GDNQ_F32, GDNQ_BF16}, p->flags a combination of GDNQ_FLAG_WHT and at
+ *   {GDNQ_F32, GDNQ_BF16}, p->flags a combination of GDNQ_FLAG_WHT, at
  *   most one of GDNQ_FLAG_BUF_BF16, GDNQ_FLAG_BUF_FP8 (the low-precision
- *   window buffers; the Low-Bit GDN page keeps recent writes in FP8).
+ *   window buffers; the Low-Bit GDN page keeps recent writes in FP8), and
+ *   GDNQ_FLAG_STATE_4BIT (the state as packed 4-bit codes, requantized
+ *   with the 4-bit codec when a window closes).
  *     q, k      [B,H,d_k] in_dtype      v [B,H,d_v] in_dtype
  *     alpha, beta [B,H] fp32
  *     codes     [B,H,d_v,d_k] int8      scales [B,H,d_v] fp32   (in/out)
+ *               ([B,H,d_v,d_k/2] bytes under GDNQ_FLAG_STATE_4BIT)
  *     buf_k     [B,H,W,d_k]             buf_v [B,H,W,d_v]       (in/out)
  *               fp32, or bf16 under GDNQ_FLAG_BUF_BF16, or under
  *               GDNQ_FLAG_BUF_FP8 E4M3 bytes [B,H,W,d] followed by fp32

@@ -19,6 +19,7 @@ STATUS_NAMES = {0: "GDNQ_OK", 1: "GDNQ_ERR_NULL", 2: "GDNQ_ERR_SHAPE", 3: "GDNQ_
                 7: "GDNQ_ERR_HIP", 8: "GDNQ_ERR_FLAGS"}
 GDNQ_F32, GDNQ_BF16 = 0, 1
 GDNQ_FLAG_WHT, GDNQ_FLAG_SSD, GDNQ_FLAG_INT8_QK, GDNQ_FLAG_BUF_BF16, GDNQ_FLAG_BUF_FP8 = 1, 2, 4, 16, 32
+GDNQ_FLAG_STATE_4BIT = 64
 
 # Every function the header declares.
 EXPORTS = ("gdnq_quantize_state", "gdnq_decode_step", "gdnq_prefill_workspace_size",

@@ -90,16 +90,18 @@ gdnq_status gdnq_quantize_state(const float* S, int64_t rows, int32_t d_k, int8_
                                 float* scales, uint32_t flags, void* stream) {
   if (rows < 0) return fail(GDNQ_ERR_SHAPE, "rows = %lld < 0", (long long)rows);
   if (!dim_ok(d_k)) return fail(GDNQ_ERR_SHAPE, "d_k = %d, expected 64 or 128", d_k);
-  if (flags & ~uint32_t(GDNQ_FLAG_WHT)) return fail(GDNQ_ERR_FLAGS, "flags 0x%x: only GDNQ_FLAG_WHT allowed", flags);
+  if (flags & ~uint32_t(GDNQ_FLAG_WHT | GDNQ_FLAG_STATE_4BIT))
+    return fail(GDNQ_ERR_FLAGS, "flags 0x%x: only GDNQ_FLAG_WHT and GDNQ_FLAG_STATE_4BIT allowed", flags);
+  const bool q4 = (flags & GDNQ_FLAG_STATE_4BIT) != 0;
   if (rows > (int64_t(1) << 35)) return fail(GDNQ_ERR_SHAPE, "rows = %lld too large", (long long)rows);
   if (rows == 0) return ok();
-  const Span sp[] = {{"S", S, size_t(rows) * d_k * 4}, {"codes", codes, size_t(rows) * d_k},
+  const Span sp[] = {{"S", S, size_t(rows) * d_k * 4}, {"codes", codes, size_t(rows) * d_k / (q4 ? 2 : 1)},
                      {"scales", scales, size_t(rows) * 4}};
   if (gdnq_status st = check_ptrs(sp, 3)) return st;
   if (overlap(sp[0], sp[1]) || overlap(sp[0], sp[2]) || overlap(sp[1], sp[2]))
     return fail(GDNQ_ERR_ALIAS, "S, codes and scales must not overlap");
   clear_stale_hip_error();
-  gdnq::QuantizeLaunch L{S, rows, d_k, codes, scales, (flags & GDNQ_FLAG_WHT) != 0};
+  gdnq::QuantizeLaunch L{S, rows, d_k, codes, scales, (flags & GDNQ_FLAG_WHT) != 0, q4};
   return hip_status(gdnq::launch_quantize(L, static_cast<hipStream_t>(stream)), "quantize launch");
 }
 
@@ -117,9 +119,11 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
   if ((p->in_dtype != GDNQ_F32 && p->in_dtype != GDNQ_BF16) ||
       (p->out_dtype != GDNQ_F32 && p->out_dtype != GDNQ_BF16))
     return fail(GDNQ_ERR_DTYPE, "in_dtype = %d, out_dtype = %d", p->in_dtype, p->out_dtype);
-  if (p->flags & ~uint32_t(GDNQ_FLAG_WHT | GDNQ_FLAG_BUF_BF16 | GDNQ_FLAG_BUF_FP8))
-    return fail(GDNQ_ERR_FLAGS, "flags 0x%x: decode accepts GDNQ_FLAG_WHT, GDNQ_FLAG_BUF_BF16, GDNQ_FLAG_BUF_FP8",
+  if (p->flags & ~uint32_t(GDNQ_FLAG_WHT | GDNQ_FLAG_BUF_BF16 | GDNQ_FLAG_BUF_FP8 | GDNQ_FLAG_STATE_4BIT))
+    return fail(GDNQ_ERR_FLAGS,
+                "flags 0x%x: decode accepts GDNQ_FLAG_WHT, GDNQ_FLAG_BUF_BF16, GDNQ_FLAG_BUF_FP8, GDNQ_FLAG_STATE_4BIT",
                 p->flags);
+  const bool q4 = (p->flags & GDNQ_FLAG_STATE_4BIT) != 0;
   const bool buf_bf16 = (p->flags & GDNQ_FLAG_BUF_BF16) != 0;
   const bool buf_fp8 = (p->flags & GDNQ_FLAG_BUF_FP8) != 0;
   if (buf_bf16 && buf_fp8)
@@ -135,7 +139,7 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
                      {"v", v, bh * dv * ei},
                      {"alpha", alpha, bh * 4},
                      {"beta", beta, bh * 4},
-                     {"codes", codes, bh * dv * dk},
+                     {"codes", codes, bh * dv * dk / (q4 ? 2 : 1)},
                      {"scales", scales, bh * dv * 4},
                      {"buf_k", buf_k, bh * W * (buf_fp8 ? dk + 4 : dk * (buf_bf16 ? 2 : 4))},
                      {"buf_v", buf_v, bh * W * (buf_fp8 ? dv + 4 : dv * (buf_bf16 ? 2 : 4))},
@@ -157,7 +161,7 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
   gdnq::DecodeLaunch L{q,        k,        v,       alpha, beta, codes, scales, buf_k,
                        buf_v,    buf_alpha, buf_beta, fill_in, fill_out, o,   B,      H,
                        dk,       dv,       W,       p->in_dtype == GDNQ_BF16,
-                       p->out_dtype == GDNQ_BF16, (p->flags & GDNQ_FLAG_WHT) != 0, buf_bf16, buf_fp8};
+                       p->out_dtype == GDNQ_BF16, (p->flags & GDNQ_FLAG_WHT) != 0, buf_bf16, buf_fp8, q4};
   return hip_status(gdnq::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch");
 }
 

@@ -208,12 +208,16 @@ __device__ __forceinline__ void fwht_group(float (&v)[E], int lane_in_group) {
 
 // ---------------------------------------------------------------- codec
 // scale = absmax / 127 (IEEE division); code = clamp(rne(x / scale), -127, 127).
-__device__ __forceinline__ float codec_scale(float absmax) { return __fdiv_rn(absmax, 127.0f); }
+// QMAX = 127: the 8-bit state; QMAX = 7: the uniform 4-bit state (15
+// levels, two codes per byte).  Same rule, scale = absmax / QMAX.
+template <int QMAX = 127>
+__device__ __forceinline__ float codec_scale(float absmax) { return __fdiv_rn(absmax, float(QMAX)); }
 
+template <int QMAX = 127>
 __device__ __forceinline__ int codec_code(float x, float scale) {
   if (scale == 0.0f) return 0;
   float r = __builtin_rintf(__fdiv_rn(x, scale));
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  r = fminf(fmaxf(r, -float(QMAX)), float(QMAX));
   return int(r);
 }
 
@@ -222,7 +226,7 @@ __device__ __forceinline__ int codec_code(float x, float scale) {
 // |x/scale| * 2^-23 <= 1.6e-5 of the exact quotient and fl(x/scale) within
 // 7.6e-6 of it, so their nearest integers can differ only when q lies within
 // 2.4e-5 of a half-integer; only then (rarely) the IEEE divisions are done.
-template <int N>
+template <int N, int QMAX = 127>
 __device__ __forceinline__ void codec_codes(const float (&x)[N], float scale, float (&c)[N]) {
   const float inv = scale > 0.0f ? __frcp_rn(scale) : 0.0f;
   bool near = false;
@@ -238,7 +242,7 @@ __device__ __forceinline__ void codec_codes(const float (&x)[N], float scale, fl
     for (int e = 0; e < N; ++e) c[e] = __builtin_rintf(__fdiv_rn(x[e], scale));
   }
 #pragma unroll
-  for (int e = 0; e < N; ++e) c[e] = fminf(fmaxf(c[e], -127.0f), 127.0f);
+  for (int e = 0; e < N; ++e) c[e] = fminf(fmaxf(c[e], -float(QMAX)), float(QMAX));
 }
 
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
@@ -248,6 +252,26 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
 
 __device__ __forceinline__ float i8_at(uint32_t w, int byte) {
   return float(int32_t(w << (24 - 8 * byte)) >> 24);
+}
+
+// 4-bit codes: eight per 32-bit word, code n in bits [4n, 4n + 4) as a two's
+// complement nibble (column 2j in the low nibble of byte j)
+__device__ __forceinline__ uint32_t pack8_i4(const int (&c)[8]) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) w |= (uint32_t(c[n]) & 0xfu) << (4 * n);
+  return w;
+}
+
+__device__ __forceinline__ float i4_at(uint32_t w, int n) {
+  return float(int32_t(w << (28 - 4 * n)) >> 28);
+}
+
+// code n of a word holding 32 / QB codes of QB bits
+template <int QB>
+__device__ __forceinline__ float code_at(uint32_t w, int n) {
+  if constexpr (QB == 8) return i8_at(w, n);
+  else return i4_at(w, n);
 }
 
 // ---------------------------------------------------------------- buffer loads

@@ -15,6 +15,7 @@ struct QuantizeLaunch {
   int8_t* codes;
   float* scales;
   bool wht;
+  bool q4;  // 4-bit codes, two per byte
 };
 hipError_t launch_quantize(const QuantizeLaunch& L, hipStream_t stream);
 
@@ -35,6 +36,7 @@ struct DecodeLaunch {
   void* o;
   int B, H, d_k, d_v, W;
   bool in_bf16, out_bf16, wht, buf_bf16, buf_fp8;
+  bool q4;  // 4-bit state codes, two per byte
 };
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 int decode_row_split();

@@ -1,6 +1,7 @@
 // Row codec on gfx950: per row (d_k fp32 entries, optionally rotated by the
 // normalised Walsh-Hadamard matrix first), scale = absmax / 127 and codes =
 // clamp(round_half_even(x / scale), -127, 127); an all-zero row gets scale 0.
+// The 4-bit state takes absmax / 7 and [-7, 7], two codes per byte.
 // LeapQuant (abstract): the 8-bit recurrent state; LinQuant / Influence-
 // Inspired Spectral Rotations (abstracts): the WHT rotation.
 //
@@ -16,7 +17,7 @@ namespace gdnq {
 constexpr int Q_THREADS = 256;
 constexpr int Q_LPR = 16;
 
-template <int DK, bool WHT>
+template <int DK, bool WHT, int QB>
 __global__ __launch_bounds__(Q_THREADS) void quantize_kernel(const float* __restrict__ S,
                                                              int64_t rows,
                                                              int8_t* __restrict__ codes,
@@ -46,41 +47,53 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_kernel(const float* __rest
 #pragma unroll
   for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(v[i]));
   amax = group_max<Q_LPR>(amax);
-  const float scale = codec_scale(amax);
+  constexpr int QMAX = QB == 8 ? 127 : 7;
+  const float scale = codec_scale<QMAX>(amax);
   if (!valid) return;
-  uint32_t w[E / 4];
+  if constexpr (QB == 8) {
+    uint32_t w[E / 4];
 #pragma unroll
-  for (int i = 0; i < E / 4; ++i)
-    w[i] = pack4_i8(codec_code(v[4 * i], scale), codec_code(v[4 * i + 1], scale),
-                    codec_code(v[4 * i + 2], scale), codec_code(v[4 * i + 3], scale));
-  int8_t* dst = codes + row * DK + li * E;
-  if constexpr (E == 8) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-  } else {
-    *reinterpret_cast<uint32_t*>(dst) = w[0];
+    for (int i = 0; i < E / 4; ++i)
+      w[i] = pack4_i8(codec_code(v[4 * i], scale), codec_code(v[4 * i + 1], scale),
+                      codec_code(v[4 * i + 2], scale), codec_code(v[4 * i + 3], scale));
+    int8_t* dst = codes + row * DK + li * E;
+    if constexpr (E == 8) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    } else {
+      *reinterpret_cast<uint32_t*>(dst) = w[0];
+    }
+  } else {  // E codes in E / 2 bytes
+    int c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < E; ++i) c[i] = codec_code<QMAX>(v[i], scale);
+    const uint32_t w = pack8_i4(c);
+    int8_t* dst = codes + row * (DK / 2) + li * (E / 2);
+    if constexpr (E == 8) {
+      *reinterpret_cast<uint32_t*>(dst) = w;
+    } else {
+      *reinterpret_cast<uint16_t*>(dst) = uint16_t(w);
+    }
   }
   if (li == 0) scales[row] = scale;
+}
+
+template <int DK, int QB>
+static void launch_q(const QuantizeLaunch& L, unsigned grid, hipStream_t stream) {
+  if (L.wht)
+    hipLaunchKernelGGL((quantize_kernel<DK, true, QB>), dim3(grid), dim3(Q_THREADS), 0, stream, L.S, L.rows,
+                       L.codes, L.scales);
+  else
+    hipLaunchKernelGGL((quantize_kernel<DK, false, QB>), dim3(grid), dim3(Q_THREADS), 0, stream, L.S, L.rows,
+                       L.codes, L.scales);
 }
 
 hipError_t launch_quantize(const QuantizeLaunch& L, hipStream_t stream) {
   const int64_t rows_per_blk = Q_THREADS / Q_LPR;
   const unsigned grid = unsigned((L.rows + rows_per_blk - 1) / rows_per_blk);
-  if (L.d_k == 128) {
-    if (L.wht)
-      hipLaunchKernelGGL((quantize_kernel<128, true>), dim3(grid), dim3(Q_THREADS), 0, stream, L.S,
-                         L.rows, L.codes, L.scales);
-    else
-      hipLaunchKernelGGL((quantize_kernel<128, false>), dim3(grid), dim3(Q_THREADS), 0, stream,
-                         L.S, L.rows, L.codes, L.scales);
-  } else {
-    if (L.wht)
-      hipLaunchKernelGGL((quantize_kernel<64, true>), dim3(grid), dim3(Q_THREADS), 0, stream, L.S,
-                         L.rows, L.codes, L.scales);
-    else
-      hipLaunchKernelGGL((quantize_kernel<64, false>), dim3(grid), dim3(Q_THREADS), 0, stream, L.S,
-                         L.rows, L.codes, L.scales);
-  }
+  if (L.d_k == 128)
+    L.q4 ? launch_q<128, 4>(L, grid, stream) : launch_q<128, 8>(L, grid, stream);
+  else
+    L.q4 ? launch_q<64, 4>(L, grid, stream) : launch_q<64, 8>(L, grid, stream);
   return hipGetLastError();
 }
-
 }  // namespace gdnq

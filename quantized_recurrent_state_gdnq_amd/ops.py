@@ -39,21 +39,27 @@ def _need(t, name, dtype=None, device=None):
     return t
 
 
-def quantize_state(S, codes=None, scales=None, wht=False):
-    """Per-row int8 codec of S[..., d_k] (fp32): returns (codes int8, scales fp32[...])."""
+def quantize_state(S, codes=None, scales=None, wht=False, state_bits=8):
+    """Per-row codec of S[..., d_k] (fp32): returns (codes, scales fp32[...]).
+    state_bits 8: int8 codes [..., d_k]; 4: packed 4-bit codes [..., d_k/2]
+    (two per byte, column 2j in the low nibble)."""
     _need(S, "S", torch.float32)
+    if state_bits not in (8, 4):
+        raise ValueError("state_bits must be 8 or 4")
     d_k = S.shape[-1]
     rows = S.numel() // d_k if d_k else 0
+    cshape = S.shape[:-1] + (d_k * state_bits // 8,)
     if codes is None:
-        codes = torch.empty(S.shape, dtype=torch.int8, device=S.device)
+        codes = torch.empty(cshape, dtype=torch.int8, device=S.device)
     if scales is None:
         scales = torch.empty(S.shape[:-1], dtype=torch.float32, device=S.device)
     _need(codes, "codes", torch.int8, S.device)
     _need(scales, "scales", torch.float32, S.device)
-    if codes.shape != S.shape or scales.numel() != rows:
-        raise ValueError("codes must match S; scales must hold one value per row")
-    _lib.check(_lib.quantize_state(_ptr(S), rows, d_k, _ptr(codes), _ptr(scales),
-                                   _lib.GDNQ_FLAG_WHT if wht else 0, _stream(S.device)))
+    if codes.shape != cshape or scales.numel() != rows:
+        raise ValueError("codes must match S (packed for 4 bits); scales must hold one value per row")
+    flags = (_lib.GDNQ_FLAG_WHT if wht else 0) | (_lib.GDNQ_FLAG_STATE_4BIT if state_bits == 4 else 0)
+    _lib.check(_lib.quantize_state(_ptr(S), rows, d_k, _ptr(codes), _ptr(scales), flags,
+                                   _stream(S.device)))
     return codes, scales
 
 
@@ -71,6 +77,9 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
     FP8 window buffer: buf_k, buf_v of dtype float8_e4m3fn, [B,H,W,d] views
     at the start of buffers that continue with the per-vector fp32 scales
     [B,H,W] (fp8_window_buffer() makes such a pair).
+
+    4-bit state: codes [B,H,d_v,d_k/2] int8 holding packed 4-bit codes
+    (inferred from the shape).
     """
     dev = q.device
     B, H, d_k = q.shape
@@ -104,7 +113,8 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
     if o.dtype not in _DT:
         raise ValueError("o must be float32 or bfloat16")
     if (tuple(k.shape) != (B, H, d_k) or tuple(v.shape) != (B, H, d_v)
-            or tuple(codes.shape) != (B, H, d_v, d_k) or tuple(scales.shape) != (B, H, d_v)
+            or tuple(codes.shape) not in ((B, H, d_v, d_k), (B, H, d_v, d_k // 2))
+            or tuple(scales.shape) != (B, H, d_v)
             or tuple(buf_k.shape) != (B, H, W, d_k) or tuple(buf_v.shape) != (B, H, W, d_v)
             or tuple(buf_alpha.shape) != (B, H, W) or tuple(buf_beta.shape) != (B, H, W)
             or tuple(alpha.shape) != (B, H) or tuple(beta.shape) != (B, H)
@@ -112,7 +122,8 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
         raise ValueError("inconsistent decode shapes")
     p = _lib.DecodeParams(B, H, d_k, d_v, W, _DT[q.dtype], _DT[o.dtype],
                           (_lib.GDNQ_FLAG_WHT if wht else 0) | (_lib.GDNQ_FLAG_BUF_BF16 if buf_bf16 else 0)
-                          | (_lib.GDNQ_FLAG_BUF_FP8 if buf_fp8 else 0))
+                          | (_lib.GDNQ_FLAG_BUF_FP8 if buf_fp8 else 0)
+                          | (_lib.GDNQ_FLAG_STATE_4BIT if codes.shape[-1] != d_k else 0))
     args = (p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(codes), _ptr(scales),
             _ptr(buf_k), _ptr(buf_v), _ptr(buf_alpha), _ptr(buf_beta), _ptr(fill_in), _ptr(fill_out),
             _ptr(o), _stream(dev))
@@ -373,12 +384,14 @@ class DecodeState:
     the window buffer and the fill counters (ping-ponged between two arrays,
     since every head of a sequence reads the fill while the step runs)."""
 
-    def __init__(self, codes, scales, window, fill=None, wht=False, buf_dtype=torch.float32):
+    def __init__(self, codes, scales, window, fill=None, wht=False, buf_dtype=torch.float32,
+                 state_bits=8):
         """buf_dtype: torch.float32 (the method's fp32 window buffer),
         torch.bfloat16 (writes stored rounded) or torch.float8_e4m3fn (FP8
         vector pairs: E4M3 codes with a per-vector scale, buf_k_scale and
-        buf_v_scale)."""
+        buf_v_scale).  state_bits 4: codes are packed 4-bit [B,H,d_v,d_k/2]."""
         B, H, d_v, d_k = codes.shape
+        d_k = d_k * 8 // state_bits
         dev = codes.device
         self.codes, self.scales, self.window, self.wht = codes, scales, window, wht
         if buf_dtype == torch.float8_e4m3fn:

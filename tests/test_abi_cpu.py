@@ -65,7 +65,7 @@ def _p(B=2, H=2, dk=128, dv=128, W=8, ind=1, outd=1, flags=0):
 
 @pytest.mark.parametrize("params,status", [
     (_p(dk=96), 2), (_p(dv=32), 2), (_p(B=1025), 2), (_p(W=0), 2), (_p(W=65), 2), (_p(H=0), 2), (_p(B=-1), 2),
-    (_p(ind=2), 3), (_p(outd=5), 3), (_p(flags=2), 8), (_p(flags=4), 8), (_p(flags=64), 8),
+    (_p(ind=2), 3), (_p(outd=5), 3), (_p(flags=2), 8), (_p(flags=4), 8), (_p(flags=128), 8),
     (_p(flags=16 | 2), 8), (_p(flags=16 | 32), 8),
 ])
 def test_decode_rejects_bad_params(params, status):
@@ -219,6 +219,10 @@ def test_quantize_validation():
     assert L.gdnq_quantize_state(f() + 8, 4, 128, f(), f(), 0, None) == 4
     s = f()
     assert L.gdnq_quantize_state(s, 4, 128, s, f(), 0, None) == 5
+    # the 4-bit state flag is accepted (the call goes on to the alignment check), alone or with WHT
+    assert L.gdnq_quantize_state(f(), 4, 128, f(), f() + 8, 64, None) == 4
+    assert L.gdnq_quantize_state(f(), 4, 128, f(), f() + 8, 64 | 1, None) == 4
+    assert L.gdnq_quantize_state(f(), 4, 128, f(), f(), 64 | 2, None) == 8
 
 
 # ---------------------------------------------------------------- prefill hand-over to decode
