@@ -39,22 +39,29 @@ BF16_PEAK_TFLOPS = 2516.6
 B, H, DK, DV, W = 64, 32, 128, 128, 64
 
 
-def decode_bytes_per_head(f, W=W, dk=DK, dv=DV, e_in=2, e_out=2, e_buf=4):
+def decode_bytes_per_head(f, W=W, dk=DK, dv=DV, e_in=2, e_out=2, e_buf=4, state_bits=8):
     """Algorithmic HBM bytes of one decode token for one head with fill f:
-    int8 rows + scales read, f buffered writes read (k, v at e_buf bytes per
-    entry, alpha and beta fp32, plus two fp32 scales per write with the FP8
-    buffer, e_buf = 1), the token's q, k, v, alpha, beta read, o written, and
-    either the token's write appended (window open) or the requantized rows
-    + scales written (window close)."""
+    the state's code rows (dk * state_bits / 8 bytes each) + scales read, f
+    buffered writes read (k, v at e_buf bytes per entry, alpha and beta fp32,
+    plus two fp32 scales per write with the FP8 buffer, e_buf = 1), the
+    token's q, k, v, alpha, beta read, o written, and either the token's
+    write appended (window open) or the requantized rows + scales written
+    (window close)."""
     w = e_buf * (dk + dv) + 8 + (8 if e_buf == 1 else 0)
-    rd = dv * dk + 4 * dv + w * f + e_in * (2 * dk + dv) + 8
-    wr = e_out * dv + (w if f + 1 < W else (dv * dk + 4 * dv))
+    state = dv * dk * state_bits // 8 + 4 * dv
+    rd = state + w * f + e_in * (2 * dk + dv) + 8
+    wr = e_out * dv + (w if f + 1 < W else state)
     return rd + wr
 
 
-def decode_bytes(fills, heads=H, e_buf=4):
+def decode_bytes(fills, heads=H, e_buf=4, state_bits=8):
     per_seq_fill = 8  # fill_in read + fill_out write
-    return int(sum(heads * decode_bytes_per_head(int(f), e_buf=e_buf) + per_seq_fill for f in fills))
+    return int(sum(heads * decode_bytes_per_head(int(f), e_buf=e_buf, state_bits=state_bits) + per_seq_fill
+                   for f in fills))
+
+
+# the sources of the decode kernel (a traffic summary is stale once they change)
+DECODE_SOURCES = ["decode.hip", "decode_impl.h", "device_common.h"]
 
 
 def source_hash(*names):
@@ -111,20 +118,22 @@ def cpu_baseline_decode(seconds=12.0):
                       f"({el:.1f} s), numpy fp32 oracle"}
 
 
-def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None):
+def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None, state_bits=8):
     """Timed decode steps; buf_dtype torch.bfloat16 runs the low-precision
-    window buffer (writes stored as bf16) on the same workload."""
+    window buffer (writes stored as bf16) on the same workload; state_bits 4
+    the uniform 4-bit state."""
     buf_dtype = buf_dtype or torch.float32
     e_buf = {torch.float32: 4, torch.bfloat16: 2, torch.float8_e4m3fn: 1}[buf_dtype]
     dev = torch.device("cuda:0")
     d = wl.decode_batch(B=B, H=H, dk=DK, dv=DV, W=W, seed=0)
     state = torch.from_numpy(d["state"]).to(dev)
-    codes0, scales0 = ops.quantize_state(state)  # the library's own codec
+    codes0, scales0 = ops.quantize_state(state, state_bits=state_bits)  # the library's own codec
     del state
     reps = []
     for i in range(rep_count):
         rep = ops.DecodeState(codes0.clone(), scales0.clone(), W,
-                              fill=torch.from_numpy(d["fill"]).to(dev), buf_dtype=buf_dtype)
+                              fill=torch.from_numpy(d["fill"]).to(dev), buf_dtype=buf_dtype,
+                              state_bits=state_bits)
         if buf_dtype == torch.float8_e4m3fn:  # E4M3 vector pairs: scale absmax/448, codes by torch's cast
             for dst, sdst, x in ((rep.buf_k, rep.buf_k_scale, d["buf_k"]), (rep.buf_v, rep.buf_v_scale, d["buf_v"])):
                 t = torch.nan_to_num(torch.from_numpy(x).to(dev))
@@ -154,7 +163,7 @@ def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None):
         r = i % rep_count
         launchers[r][0]()
         f = host_fills[r]
-        nbytes = decode_bytes(f, e_buf=e_buf)
+        nbytes = decode_bytes(f, e_buf=e_buf, state_bits=state_bits)
         host_fills[r] = np.where(f + 1 == W, 0, f + 1)
         return nbytes
 
@@ -368,6 +377,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurements")
     ap.add_argument("--no-fp8-buffer", action="store_true", help="skip the FP8 window-buffer line")
+    ap.add_argument("--no-state4", action="store_true", help="skip the 4-bit state line")
     ap.add_argument("--no-bf16-buffer", action="store_true",
                     help="skip the decode measurement with the bf16 window buffer")
     ap.add_argument("--skip-decode", action="store_true",
@@ -392,7 +402,7 @@ def main():
         return
 
     r = bench_decode(args, torch, ops, wl, max(1, args.replicas))
-    traffic = load_traffic("decode_b64_h32_traffic.json", ["decode.hip", "device_common.h"], 1)
+    traffic = load_traffic("decode_b64_h32_traffic.json", DECODE_SOURCES, 1)
     line = {
         "metric": "int8-state GDN decode tokens/s + achieved HBM GB/s; prefill tokens/s",
         "value": round(r["tokens_s"], 1),
@@ -427,7 +437,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(rb["gbps"], 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(rb["gbps"] / HBM_PEAK_GBPS, 4),
                          "traffic": load_traffic("decode_b64_h32_bf16buf_traffic.json",
-                                                 ["decode.hip", "device_common.h"], 1),
+                                                 DECODE_SOURCES, 1),
                          "algorithmic_bytes_per_launch": int(rb["bytes_per_launch"])},
         }
     if not args.no_fp8_buffer:
@@ -442,8 +452,22 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(rf["gbps"], 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(rf["gbps"] / HBM_PEAK_GBPS, 4),
                          "traffic": load_traffic("decode_b64_h32_fp8buf_traffic.json",
-                                                 ["decode.hip", "device_common.h"], 1),
+                                                 DECODE_SOURCES, 1),
                          "algorithmic_bytes_per_launch": int(rf["bytes_per_launch"])},
+        }
+    if not args.no_state4:
+        r4 = bench_decode(args, torch, ops, wl, max(1, args.replicas), state_bits=4)
+        line["decode_state4"] = {
+            "workload": "the same decode step with the uniform 4-bit state (GDNQ_FLAG_STATE_4BIT: "
+                        "codes in [-7, 7], two per byte, scale absmax/7) and the fp32 window buffer",
+            "ms_per_step": round(r4["ms_per_step"], 5),
+            "tokens_s": round(r4["tokens_s"], 1),
+            "gbps": round(r4["gbps"], 1),
+            "roofline": {"bound": "hbm", "achieved": round(r4["gbps"], 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(r4["gbps"] / HBM_PEAK_GBPS, 4),
+                         "traffic": load_traffic("decode_b64_h32_state4_traffic.json",
+                                                 DECODE_SOURCES + ["decode_q4.hip"], 1),
+                         "algorithmic_bytes_per_launch": int(r4["bytes_per_launch"])},
         }
     if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, ops, wl)
