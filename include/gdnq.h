@@ -99,7 +99,8 @@ enum {
                              buf_k = B*H*W*d_k code bytes, then B*H*W fp32
                              scales; buf_v likewise with d_v.  Exclusive with
                              GDNQ_FLAG_BUF_BF16.                            */
-  GDNQ_FLAG_STATE_4BIT = 64u /* quantize and decode: the uniform 4-bit state
+  GDNQ_FLAG_STATE_4BIT = 64u /* quantize, decode and GDN prefill (all its
+                             entry points): the uniform 4-bit state
                              (Low-Bit GDN ..., abstract: the "@4" budget of
                              four bits per state entry).  The codec above with
                              127 replaced by 7: scale = max|x| / 7, codes =
@@ -192,8 +193,11 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
  *   NULL), requantizing at every window end, windows aligned to token 0.
  *   Supported: d_k = d_v = 128, chunk = window = 64, T a multiple of 64.
  *   Writes o and the final codes/scales (the state after the last window).
- *   state_f32 must be NULL.  Flags: none (a rotated GDN state is produced by
- *   rotating q and k before the call and the state with gdnq_quantize_state).
+ *   state_f32 must be NULL.  Flags: 0 or GDNQ_FLAG_STATE_4BIT (init_codes and
+ *   codes then hold packed 4-bit codes, [B,H,d_v,d_k/2] bytes, and every
+ *   window end requantizes with the 4-bit codec).  A rotated GDN state is
+ *   produced by rotating q and k before the call and the state with
+ *   gdnq_quantize_state.
  *
  *   SSD (GDNQ_FLAG_SSD): S_t = a_t S_{t-1} + v_t k_t^T from a zero state, no
  *   requantization (window ignored); beta, init_codes, init_scales, codes and
@@ -237,7 +241,8 @@ gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, co
  *   requantize once at the window's end).
  *
  *   Same recurrence, parameters and layouts as gdnq_prefill_chunked in GDN
- *   mode (flags 0, d_k = d_v = 128, chunk = window = 64, in_dtype bf16),
+ *   mode (flags 0 or GDNQ_FLAG_STATE_4BIT, d_k = d_v = 128, chunk = window =
+ *   64, in_dtype bf16),
  *   except that p->seqlen T need not be a multiple of 64.  With r = T mod 64:
  *     o          [B,T,H,128] out_dtype, every token (written)
  *     codes, scales: the state at the last window boundary (token T - r)
@@ -304,7 +309,7 @@ gdnq_status gdnq_prefill_varlen(const gdnq_prefill_params* p, const int32_t* cu_
  *
  *   p->batch B = sequences; p->seqlen = new tokens per sequence (cu_seqlens
  *   NULL, q [B,T,H,128] ...) or packed new tokens in total (cu_seqlens as
- *   for gdnq_prefill_varlen, q [T,H,128] ...).  GDN mode only (flags 0,
+ *   for gdnq_prefill_varlen, q [T,H,128] ...).  GDN mode only (flags 0 or GDNQ_FLAG_STATE_4BIT,
  *   d_k = d_v = 128, chunk = window = 64, in_dtype bf16).
  *     fill_in    [B] int32, device: buffered writes per sequence (0..63;
  *                other values are clamped into that range).  It may be the

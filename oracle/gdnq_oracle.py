@@ -370,7 +370,7 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha,
 
 
 def prefill(q, k, v, alpha, beta=None, *, W, kind="gdn", rot=False, qk_int8=False,
-            codes0=None, scale0=None, dtype=F32):
+            codes0=None, scale0=None, dtype=F32, qmax=127):
     """Prefill of a batch from a stored (or zero) state, token by token.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; alpha, beta: [B,T,H].
@@ -389,7 +389,7 @@ def prefill(q, k, v, alpha, beta=None, *, W, kind="gdn", rot=False, qk_int8=Fals
                      W=W, kind=kind, rot=rot, qk_int8=qk_int8,
                      codes0=None if codes0 is None else np.asarray(codes0).reshape(B * H, dv, dk),
                      scale0=None if scale0 is None else np.asarray(scale0).reshape(B * H, dv),
-                     dtype=dtype)
+                     dtype=dtype, qmax=qmax)
     o = np.moveaxis(r["o"].reshape(T, B, H, dv), 0, 1)
     out = {"o": o, "n": r["n"], "S": r["S"].reshape(B, H, dv, dk)}
     out["codes"] = None if r["codes"] is None else r["codes"].reshape(B, H, dv, dk)

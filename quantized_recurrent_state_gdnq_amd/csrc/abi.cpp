@@ -185,7 +185,8 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
       return fail(GDNQ_ERR_FLAGS, "SSD: GDNQ_FLAG_WHT requires GDNQ_FLAG_INT8_QK");
     if (dk != 128 || (dv != 64 && dv != 128)) return fail(GDNQ_ERR_SHAPE, "SSD: d_k = %d (128), d_v = %d (64 or 128)", dk, dv);
   } else {
-    if (p->flags) return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill takes no flags", p->flags);
+    if (p->flags & ~uint32_t(GDNQ_FLAG_STATE_4BIT))
+      return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill takes only GDNQ_FLAG_STATE_4BIT", p->flags);
     if (dk != 128 || dv != 128) return fail(GDNQ_ERR_SHAPE, "GDN prefill: d_k = d_v = 128 required (got %d, %d)", dk, dv);
     if (p->window != p->chunk) return fail(GDNQ_ERR_SHAPE, "GDN prefill: window = %d must equal chunk = %d", p->window, p->chunk);
   }
@@ -196,6 +197,7 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   L.wht = (p->flags & GDNQ_FLAG_WHT) != 0;
   L.ssd = ssd;
   L.int8_qk = (p->flags & GDNQ_FLAG_INT8_QK) != 0;
+  L.q4 = !ssd && (p->flags & GDNQ_FLAG_STATE_4BIT) != 0;
   L.handoff = handoff;
   return GDNQ_OK;
 }
@@ -238,7 +240,7 @@ gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, co
     const Span sp[] = {{"q", q, bth * L.d_k * 2},         {"k", k, bth * L.d_k * 2},
                        {"v", v, bth * L.d_v * 2},         {"alpha", alpha, bth * 4},
                        {"beta", beta, bth * 4},           {"o", o, bth * L.d_v * eo},
-                       {"codes", codes, bh * L.d_v * L.d_k}, {"scales", scales, bh * L.d_v * 4}};
+                       {"codes", codes, bh * L.d_v * L.d_k / (L.q4 ? 2 : 1)}, {"scales", scales, bh * L.d_v * 4}};
     constexpr int N = sizeof(sp) / sizeof(sp[0]);
     if (L.T > 0) {
       if (gdnq_status st = check_ptrs(sp, N)) return st;
@@ -246,7 +248,8 @@ gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, co
       if (gdnq_status st = check_ptrs(sp + 6, 2)) return st;
     }
     if (init_codes) {
-      const Span ip[] = {{"init_codes", init_codes, bh * L.d_v * L.d_k}, {"init_scales", init_scales, bh * L.d_v * 4}};
+      const Span ip[] = {{"init_codes", init_codes, bh * L.d_v * L.d_k / (L.q4 ? 2 : 1)},
+                         {"init_scales", init_scales, bh * L.d_v * 4}};
       if (gdnq_status st = check_ptrs(ip, 2)) return st;
       // an in-place continuation (init == final) is allowed; partial overlap is not
       if (init_codes != codes && overlap(ip[0], sp[6])) return fail(GDNQ_ERR_ALIAS, "init_codes partially overlaps codes");
@@ -306,7 +309,7 @@ static gdnq_status prefill_handoff_impl(gdnq::PrefillLaunch& L, const int32_t* c
   const Span sp[] = {{"q", q, bth * L.d_k * 2},          {"k", k, bth * L.d_k * 2},
                      {"v", v, bth * L.d_v * 2},          {"alpha", alpha, bth * 4},
                      {"beta", beta, bth * 4},            {"o", o, bth * L.d_v * eo},
-                     {"codes", codes, bh * L.d_v * L.d_k}, {"scales", scales, bh * L.d_v * 4},
+                     {"codes", codes, bh * L.d_v * L.d_k / (L.q4 ? 2 : 1)}, {"scales", scales, bh * L.d_v * 4},
                      {"buf_k", buf_k, bh * W * L.d_k * 4}, {"buf_v", buf_v, bh * W * L.d_v * 4},
                      {"buf_alpha", buf_alpha, bh * W * 4}, {"buf_beta", buf_beta, bh * W * 4},
                      {"fill_out", fill_out, size_t(L.B) * 4}};
@@ -317,7 +320,8 @@ static gdnq_status prefill_handoff_impl(gdnq::PrefillLaunch& L, const int32_t* c
     if (gdnq_status st = check_ptrs(sp + 6, N - 6)) return st;
   }
   if (init_codes) {
-    const Span ip[] = {{"init_codes", init_codes, bh * L.d_v * L.d_k}, {"init_scales", init_scales, bh * L.d_v * 4}};
+    const Span ip[] = {{"init_codes", init_codes, bh * L.d_v * L.d_k / (L.q4 ? 2 : 1)},
+                       {"init_scales", init_scales, bh * L.d_v * 4}};
     if (gdnq_status st = check_ptrs(ip, 2)) return st;
     if (init_codes != codes && overlap(ip[0], sp[6])) return fail(GDNQ_ERR_ALIAS, "init_codes partially overlaps codes");
     if (init_scales != scales && overlap(ip[1], sp[7])) return fail(GDNQ_ERR_ALIAS, "init_scales partially overlaps scales");

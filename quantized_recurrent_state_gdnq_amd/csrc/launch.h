@@ -64,6 +64,7 @@ struct PrefillLaunch {
   const int32_t* fill_in;     // resuming (GDN hand-over): writes each sequence's window buffer holds
   int B, T, H, d_k, d_v, C, W;
   bool out_bf16, wht, ssd, int8_qk, handoff, varlen, resume;
+  bool q4;  // GDN: the state as packed 4-bit codes
 };
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream);
 hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream);

@@ -331,8 +331,11 @@ __device__ __forceinline__ uint2 as_u2(const bf16x4& v) { return __builtin_bit_c
 constexpr int SNT = 1024;   // state-pass threads
 constexpr int NCRIT = 512;  // threads of the chain waves
 
-template <bool OUT_BF16>
+// QB: the state's code width, 8 (int8) or 4 (packed 4-bit, scale absmax / 7)
+template <bool OUT_BF16, int QB>
 __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
+  constexpr int QMAX = QB == 8 ? 127 : 7;
+  constexpr int RB = PD * QB / 8;  // bytes per stored row
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __bf16* Kl = reinterpret_cast<__bf16*>(lds + OFF_K);
   __bf16* Ql = reinterpret_cast<__bf16*>(lds + OFF_Q);
@@ -406,9 +409,18 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
     const int i0 = it * 16 + 4 * lq;
     {  // stored rows at the start (zero state without init)
       const int rq = tid >> 4, seg = tid & 15;  // 32 rows x 16 segments of 8 codes
-      uint2 w = make_uint2(0u, 0u);
-      if (a.init_codes) w = *reinterpret_cast<const uint2*>(a.init_codes + (state_row0 + rq) * PD + seg * 8);
-      *reinterpret_cast<bf16x8*>(Cb + rq * CBP + seg * 8) = i8x8_to_bf16(w);
+      bf16x8 cv;
+      if constexpr (QB == 8) {
+        uint2 w = make_uint2(0u, 0u);
+        if (a.init_codes) w = *reinterpret_cast<const uint2*>(a.init_codes + (state_row0 + rq) * RB + seg * 8);
+        cv = i8x8_to_bf16(w);
+      } else {
+        uint32_t w = 0u;
+        if (a.init_codes) w = *reinterpret_cast<const uint32_t*>(a.init_codes + (state_row0 + rq) * RB + seg * 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cv[e] = (__bf16)i4_at(w, e);
+      }
+      *reinterpret_cast<bf16x8*>(Cb + rq * CBP + seg * 8) = cv;
       if (seg == 0) sl[rq] = a.init_scales ? a.init_scales[state_row0 + rq] : 0.f;
     }
     if (NC > 0) {
@@ -529,9 +541,9 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
         amax = group_max<16>(amax);
-        const float scale = codec_scale(amax);
+        const float scale = codec_scale<QMAX>(amax);
         float cf[8];
-        codec_codes(x, scale, cf);
+        codec_codes<8, QMAX>(x, scale, cf);
         bf16x8 cv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) cv[e] = (__bf16)cf[e];
@@ -542,13 +554,20 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
       __syncthreads();
     }
 
-    {  // final rows (codes back to int8)
+    {  // final rows (codes back to int8, or packed 4-bit)
       const int rq = tid >> 4, seg = tid & 15;
       const bf16x8 cv = lds_bf16x8(Cb + rq * CBP + seg * 8);
-      uint2 w;
-      w.x = pack4_i8(int(float(cv[0])), int(float(cv[1])), int(float(cv[2])), int(float(cv[3])));
-      w.y = pack4_i8(int(float(cv[4])), int(float(cv[5])), int(float(cv[6])), int(float(cv[7])));
-      *reinterpret_cast<uint2*>(a.codes + (state_row0 + rq) * PD + seg * 8) = w;
+      if constexpr (QB == 8) {
+        uint2 w;
+        w.x = pack4_i8(int(float(cv[0])), int(float(cv[1])), int(float(cv[2])), int(float(cv[3])));
+        w.y = pack4_i8(int(float(cv[4])), int(float(cv[5])), int(float(cv[6])), int(float(cv[7])));
+        *reinterpret_cast<uint2*>(a.codes + (state_row0 + rq) * RB + seg * 8) = w;
+      } else {
+        int c4[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c4[e] = int(float(cv[e]));
+        *reinterpret_cast<uint32_t*>(a.codes + (state_row0 + rq) * RB + seg * 4) = pack8_i4(c4);
+      }
       if (seg == 0) a.scales[state_row0 + rq] = sl[rq];
     }
     return;
@@ -980,7 +999,8 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
               static_cast<const uint16_t*>(L.v), L.beta, T_ws, g_ws, L.init_codes, L.init_scales,
               L.o, L.codes, L.scales, sm, L.B, L.H};
   const unsigned grid = unsigned(L.B) * L.H * (PD / RWS);
-  auto kern = L.out_bf16 ? &gdn_state_kernel<true> : &gdn_state_kernel<false>;
+  auto kern = L.q4 ? (L.out_bf16 ? &gdn_state_kernel<true, 4> : &gdn_state_kernel<false, 4>)
+                   : (L.out_bf16 ? &gdn_state_kernel<true, 8> : &gdn_state_kernel<false, 8>);
   if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, STATE_LDS))
     return e;

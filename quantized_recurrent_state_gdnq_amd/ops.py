@@ -133,11 +133,12 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
     return o
 
 
-def _prefill_params(q, v, *, window, chunk, wht, ssd, int8_qk, out_dtype):
+def _prefill_params(q, v, *, window, chunk, wht, ssd, int8_qk, out_dtype, state_bits=8):
     B, T, H, d_k = q.shape
     d_v = v.shape[-1]
     flags = ((_lib.GDNQ_FLAG_WHT if wht else 0) | (_lib.GDNQ_FLAG_SSD if ssd else 0)
-             | (_lib.GDNQ_FLAG_INT8_QK if int8_qk else 0))
+             | (_lib.GDNQ_FLAG_INT8_QK if int8_qk else 0)
+             | (_lib.GDNQ_FLAG_STATE_4BIT if state_bits == 4 else 0))
     return _lib.PrefillParams(B, T, H, d_k, d_v, chunk, window, _DT[q.dtype], _DT[out_dtype], flags)
 
 
@@ -151,11 +152,13 @@ def prefill_workspace_size(q, v, *, window=64, chunk=64, wht=False, ssd=False, i
 def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_codes=None,
                     init_scales=None, wht=False, ssd=False, int8_qk=False,
                     out_dtype=torch.bfloat16, o=None, codes=None, scales=None, state_f32=None,
-                    workspace=None):
+                    workspace=None, state_bits=8):
     """Chunkwise prefill (see gdnq_prefill_chunked in include/gdnq.h).
 
     q, k [B,T,H,d_k], v [B,T,H,d_v] bf16; alpha (and beta for GDN) [B,T,H] fp32.
     GDN returns (o, codes, scales); SSD (ssd=True) returns (o, state_f32).
+    GDN with state_bits=4: the uniform 4-bit state, codes [B,H,d_v,d_k/2]
+    packed two per byte (init_codes likewise).
     """
     dev = q.device
     B, T, H, d_k = q.shape
@@ -166,7 +169,7 @@ def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_code
     if tuple(k.shape) != (B, T, H, d_k) or tuple(v.shape) != (B, T, H, d_v) or tuple(alpha.shape) != (B, T, H):
         raise ValueError("inconsistent prefill shapes")
     p = _prefill_params(q, v, window=window, chunk=chunk, wht=wht, ssd=ssd, int8_qk=int8_qk,
-                        out_dtype=out_dtype)
+                        out_dtype=out_dtype, state_bits=state_bits)
     if o is None:
         o = torch.empty((B, T, H, d_v), dtype=out_dtype, device=dev)
     _need(o, "o", out_dtype, dev)
@@ -179,7 +182,7 @@ def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_code
         if tuple(beta.shape) != (B, T, H):
             raise ValueError("beta must be [B,T,H]")
         if codes is None:
-            codes = torch.empty((B, H, d_v, d_k), dtype=torch.int8, device=dev)
+            codes = torch.empty((B, H, d_v, d_k * state_bits // 8), dtype=torch.int8, device=dev)
         if scales is None:
             scales = torch.empty((B, H, d_v), dtype=torch.float32, device=dev)
         _need(codes, "codes", torch.int8, dev)
@@ -208,7 +211,7 @@ def prefill_handoff_workspace_size(q, v, *, window=64, out_dtype=torch.bfloat16)
 
 
 def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_scales=None,
-                    out_dtype=torch.bfloat16, o=None, state=None, workspace=None):
+                    out_dtype=torch.bfloat16, o=None, state=None, workspace=None, state_bits=8):
     """GDN prefill of any T tokens handed over to decode (see
     gdnq_prefill_handoff in include/gdnq.h): returns (o, DecodeState) whose
     codes/scales are the state at the last window boundary and whose fp32
@@ -226,7 +229,7 @@ def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_sc
             or tuple(alpha.shape) != (B, T, H) or tuple(beta.shape) != (B, T, H)):
         raise ValueError("inconsistent prefill shapes")
     p = _prefill_params(q, v, window=window, chunk=64, wht=False, ssd=False, int8_qk=False,
-                        out_dtype=out_dtype)
+                        out_dtype=out_dtype, state_bits=state_bits)
     if o is None:
         o = torch.empty((B, T, H, d_v), dtype=out_dtype, device=dev)
     _need(o, "o", out_dtype, dev)
@@ -235,10 +238,10 @@ def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_sc
         _need(init_scales, "init_scales", torch.float32, dev)
     st = state
     if st is None:
-        st = DecodeState(torch.empty((B, H, d_v, d_k), dtype=torch.int8, device=dev),
+        st = DecodeState(torch.empty((B, H, d_v, d_k * state_bits // 8), dtype=torch.int8, device=dev),
                          torch.empty((B, H, d_v), dtype=torch.float32, device=dev), window,
-                         fill=torch.zeros(B, dtype=torch.int32, device=dev))
-    if st.buf_k.dtype != torch.float32 or tuple(st.codes.shape) != (B, H, d_v, d_k):
+                         fill=torch.zeros(B, dtype=torch.int32, device=dev), state_bits=state_bits)
+    if st.buf_k.dtype != torch.float32 or tuple(st.codes.shape) != (B, H, d_v, d_k * state_bits // 8):
         raise ValueError("state: a DecodeState of matching shape with an fp32 window buffer")
     need = int(_lib.prefill_handoff_workspace_size(p))
     if need and workspace is None:
@@ -252,10 +255,10 @@ def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_sc
     return o, st
 
 
-def _varlen_params(q, v, n_seqs, *, window, out_dtype):
+def _varlen_params(q, v, n_seqs, *, window, out_dtype, state_bits=8):
     T, H, d_k = q.shape
     return _lib.PrefillParams(n_seqs, T, H, d_k, v.shape[-1], 64, window, _DT[q.dtype],
-                              _DT[out_dtype], 0)
+                              _DT[out_dtype], _lib.GDNQ_FLAG_STATE_4BIT if state_bits == 4 else 0)
 
 
 def prefill_varlen_workspace_size(q, v, n_seqs, *, window=64, out_dtype=torch.bfloat16):
@@ -265,7 +268,7 @@ def prefill_varlen_workspace_size(q, v, n_seqs, *, window=64, out_dtype=torch.bf
 
 def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=None,
                    init_scales=None, out_dtype=torch.bfloat16, o=None, state=None,
-                   workspace=None):
+                   workspace=None, state_bits=8):
     """GDN prefill of a packed batch of variable-length sequences handed over
     to decode (see gdnq_prefill_varlen in include/gdnq.h).  q, k [T,H,d_k],
     v [T,H,d_v] bf16 and alpha, beta [T,H] fp32 hold the sequences back to
@@ -285,7 +288,7 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=No
     if (tuple(k.shape) != (T, H, d_k) or tuple(v.shape) != (T, H, d_v)
             or tuple(alpha.shape) != (T, H) or tuple(beta.shape) != (T, H)):
         raise ValueError("inconsistent packed prefill shapes")
-    p = _varlen_params(q, v, B, window=window, out_dtype=out_dtype)
+    p = _varlen_params(q, v, B, window=window, out_dtype=out_dtype, state_bits=state_bits)
     if o is None:
         o = torch.empty((T, H, d_v), dtype=out_dtype, device=dev)
     _need(o, "o", out_dtype, dev)
@@ -294,10 +297,10 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=No
         _need(init_scales, "init_scales", torch.float32, dev)
     st = state
     if st is None:
-        st = DecodeState(torch.empty((B, H, d_v, d_k), dtype=torch.int8, device=dev),
+        st = DecodeState(torch.empty((B, H, d_v, d_k * state_bits // 8), dtype=torch.int8, device=dev),
                          torch.empty((B, H, d_v), dtype=torch.float32, device=dev), window,
-                         fill=torch.zeros(B, dtype=torch.int32, device=dev))
-    if st.buf_k.dtype != torch.float32 or tuple(st.codes.shape) != (B, H, d_v, d_k):
+                         fill=torch.zeros(B, dtype=torch.int32, device=dev), state_bits=state_bits)
+    if st.buf_k.dtype != torch.float32 or tuple(st.codes.shape) != (B, H, d_v, d_k * state_bits // 8):
         raise ValueError("state: a DecodeState of matching shape with an fp32 window buffer")
     need = int(_lib.prefill_varlen_workspace_size(p))
     if need and workspace is None:
@@ -331,6 +334,7 @@ def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=to
     dev = q.device
     st = state
     B, H, d_v, d_k = st.codes.shape
+    d_k = d_k * 8 // st.state_bits
     if st.buf_k.dtype != torch.float32 or st.window != 64:
         raise ValueError("state: a DecodeState with an fp32 window buffer of 64 slots")
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -352,7 +356,8 @@ def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=to
             or tuple(v.shape) != lead + (H, d_v) or tuple(alpha.shape) != lead + (H,)
             or tuple(beta.shape) != lead + (H,)):
         raise ValueError("inconsistent resume shapes")
-    p = _lib.PrefillParams(B, T, H, d_k, d_v, 64, 64, _DT[q.dtype], _DT[out_dtype], 0)
+    p = _lib.PrefillParams(B, T, H, d_k, d_v, 64, 64, _DT[q.dtype], _DT[out_dtype],
+                           _lib.GDNQ_FLAG_STATE_4BIT if st.state_bits == 4 else 0)
     if o is None:
         o = torch.empty(lead + (H, d_v), dtype=out_dtype, device=dev)
     _need(o, "o", out_dtype, dev)
@@ -394,6 +399,7 @@ class DecodeState:
         d_k = d_k * 8 // state_bits
         dev = codes.device
         self.codes, self.scales, self.window, self.wht = codes, scales, window, wht
+        self.state_bits = state_bits
         if buf_dtype == torch.float8_e4m3fn:
             self.buf_k, self.buf_k_scale = fp8_window_buffer(B, H, window, d_k, dev)
             self.buf_v, self.buf_v_scale = fp8_window_buffer(B, H, window, d_v, dev)

@@ -1,6 +1,7 @@
 """GPU parity of the uniform 4-bit state (GDNQ_FLAG_STATE_4BIT: codec with
-scale = absmax / 7 and codes in [-7, 7], two per byte) for the codec and the
-decode step, against the oracle's qmax = 7 option.  Codes are compared after
+scale = absmax / 7 and codes in [-7, 7], two per byte) for the codec, the
+decode step and the GDN prefill (chunked, hand-over, resume), against the
+oracle's qmax = 7 option.  Codes are compared after
 unpacking the nibbles here; the bars are those of the 8-bit state (codes
 bitwise where the decision is exact, +-1 on <= 0.1% after a replayed close;
 scales 1e-5; outputs 1e-3 / 2e-2)."""
@@ -195,3 +196,90 @@ def test_decode4_batch64_heads32_window64():
     assert_codes(unpack4(host(st.codes))[closing], rc[closing], "closing codes")
     assert_scales(host(st.scales)[closing], rs[closing], "closing scales")
     assert np.array_equal(unpack4(host(st.codes))[~closing], codes[~closing])
+
+
+# ---------------------------------------------------------------- GDN prefill with the 4-bit state
+W64 = 64
+KEYS = ("q", "k", "v", "alpha", "beta")
+
+
+def _pf_inputs(x):
+    return [dev(x[key], torch.bfloat16 if key in ("q", "k", "v") else None) for key in KEYS]
+
+
+def test_prefill4_teacher_forced_chunks():
+    """B=2, H=3, four chunks, one per call from the GPU's previous 4-bit
+    state (the first from a random stored one): every window's 4-bit
+    requantization against the oracle on identical inputs."""
+    B, H, d, T = 2, 3, 128, 256
+    x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=21)
+    g = np.random.default_rng(22)
+    codes, scales = O.quantize_rows((g.standard_normal((B, H, d, d)) * 0.5).astype(np.float32), qmax=7)
+    for c in range(T // W64):
+        xs = {k: np.ascontiguousarray(v[:, c * W64:(c + 1) * W64]) for k, v in x.items()}
+        cg = Guarded((B, H, d, d // 2), torch.int8)
+        sg = Guarded((B, H, d), torch.float32)
+        o, _, _ = ops.prefill_chunked(*_pf_inputs(xs), init_codes=dev(pack4(codes)),
+                                      init_scales=dev(scales), out_dtype=torch.float32, codes=cg.t,
+                                      scales=sg.t, state_bits=4)
+        torch.cuda.synchronize()
+        assert cg.guards_intact() and sg.guards_intact()
+        ref = O.prefill(xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], W=W64, codes0=codes,
+                        scale0=scales, qmax=7)
+        err = max_rel_err(host(o), ref["o"])
+        assert err <= OUT_TOL_F32, f"chunk {c}: o max relative error {err:.3e}"
+        got = unpack4(host(cg.t))
+        assert np.abs(got).max() <= 7
+        assert_codes(got, ref["codes"], f"chunk {c} codes")
+        assert_scales(host(sg.t), ref["scale"], f"chunk {c} scales")
+        codes, scales = got, host(sg.t)
+
+
+def test_prefill4_handoff_then_decode4():
+    """4-bit hand-over of T = 100 tokens (one close, 36 open writes), then
+    40 decode steps on the same 4-bit DecodeState across the next close,
+    each teacher-forced against the oracle."""
+    B, H, d, T = 2, 2, 128, 100
+    x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=23)
+    o, st = ops.prefill_handoff(*_pf_inputs(x), out_dtype=torch.float32, state_bits=4)
+    torch.cuda.synchronize()
+    ref = O.prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], W=W64, qmax=7)
+    assert max_rel_err(host(o), ref["o"]) <= OUT_TOL_BF16
+    assert np.all(host(st.fill) == T % W64)
+    assert_codes(unpack4(host(st.codes)), ref["codes"], "hand-over codes")
+    assert_scales(host(st.scales), ref["scale"], "hand-over scales")
+    n_close = 0
+    for t in range(40):
+        y = wl.decode_tokens(B=B, H=H, dk=d, dv=d, step=t, seed=24)
+        before = [unpack4(host(st.codes)), host(st.scales).copy(), host(st.buf_k).copy(),
+                  host(st.buf_v).copy(), host(st.buf_alpha).copy(), host(st.buf_beta).copy(),
+                  host(st.fill).copy()]
+        go = host(st.step(dev(y["q"], torch.bfloat16), dev(y["k"], torch.bfloat16),
+                          dev(y["v"], torch.bfloat16), dev(y["alpha"]), dev(y["beta"]),
+                          out_dtype=torch.float32))
+        ro, rc, rs, *_ = O.decode_step(y["q"], y["k"], y["v"], y["alpha"], y["beta"], *before, W64,
+                                      qmax=7)
+        assert max_rel_err(go, ro) <= OUT_TOL_BF16, t
+        closing = before[6] + 1 == W64
+        if closing.any():
+            n_close += 1
+            assert_codes(unpack4(host(st.codes))[closing], rc[closing], f"step {t} codes")
+            assert_scales(host(st.scales)[closing], rs[closing], f"step {t} scales")
+    assert n_close == 1
+
+
+def test_prefill4_resume_split_equals_one_call():
+    """With the 4-bit state too, a hand-over of 37 tokens then resuming
+    with the rest equals one hand-over call bitwise."""
+    B, H, d, T, T1 = 2, 2, 128, 230, 37
+    x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=25)
+    t = dict(zip(KEYS, _pf_inputs(x)))
+    a_o, a_st = ops.prefill_handoff(*(t[key] for key in KEYS), out_dtype=torch.float32, state_bits=4)
+    _, b_st = ops.prefill_handoff(*(t[key][:, :T1].contiguous() for key in KEYS),
+                                  out_dtype=torch.float32, state_bits=4)
+    b_o = ops.prefill_resume(b_st, *(t[key][:, T1:].contiguous() for key in KEYS),
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a_o[:, T1:], b_o)
+    for name in ("codes", "scales", "fill"):
+        assert torch.equal(getattr(a_st, name), getattr(b_st, name)), name
