@@ -284,7 +284,7 @@ gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, co
  *   A sequence of length 0 copies its initial state (or zeros) to codes,
  *   scales and sets its fill to 0.
  *   workspace: gdnq_prefill_varlen_workspace_size(p) bytes (bounded by
- *   floor(T/64) + B chunks per head, plus 4 (3B+2) bytes of sequence map).
+ *   floor(T/64) + B chunks per head, plus 4 (4B+2) bytes of sequence map).
  *   Errors: NULL, SHAPE, DTYPE, ALIGN (cu_seqlens: 4 bytes), ALIAS, FLAGS,
  *   WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */

@@ -72,6 +72,7 @@ struct SeqMap {
   const uint16_t* sv;
   const float* sa;
   const float* sb;
+  const int32_t* order;  // sequences by chunk count, most first (nullptr: in order)
   int T;               // tokens per sequence (uniform) or in total
   __device__ size_t tok0(int b) const { return tok ? size_t(tok[b]) : size_t(b) * T; }
   __device__ int ntok(int b) const { return tok ? tok[b + 1] - tok[b] : T; }
@@ -355,7 +356,16 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   const int logical = xcd_swizzle(blockIdx.x, nblk);  // the 4 row blocks of a head share an XCD
   const int chain = logical / (PD / RWS);
   const int rb = logical % (PD / RWS);
-  const int b = chain / a.H, h = chain % a.H;
+  // With a length order, the chains go round robin over the eight XCD
+  // segments of the swizzle, so every XCD takes its share longest first
+  // (a contiguous slice of the order would give one XCD all the long ones).
+  int cr = chain;
+  if (a.sm.order && (nblk & 31) == 0) {
+    const int seg = nblk >> 5;  // chains per XCD segment
+    cr = (chain % seg) * 8 + chain / seg;
+  }
+  const int b = a.sm.order && (nblk & 31) == 0 ? a.sm.order[cr / a.H] : chain / a.H;
+  const int h = cr % a.H;
   const int r0 = rb * RWS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
@@ -777,7 +787,8 @@ static size_t gdn_ws_stage(const PrefillLaunch& L) {
   return L.resume ? size_t(L.B) * PC * L.H * (3 * PD * 2 + 2 * 4) : 0;
 }
 static bool gdn_mapped(const PrefillLaunch& L) { return L.varlen || L.resume; }
-static size_t gdn_ws_map(const PrefillLaunch& L) { return gdn_mapped(L) ? (3 * size_t(L.B) + 2) * 4 : 0; }
+static size_t gdn_ws_map(const PrefillLaunch& L) { return gdn_mapped(L) ? (4 * size_t(L.B) + 2) * 4 : 0; }
+constexpr int ORDER_MAXB = 1024;  // sequences ranked by length (more: taken in order)
 
 // Sequence map, one workgroup.  Token offsets tok[i]: with cu, the running
 // maximum of cu[i] clamped to [0, T] (so lengths are never negative and
@@ -791,12 +802,14 @@ struct SeqMapArgs {
   int32_t* tok;
   int32_t* ch;
   int32_t* pre;
+  int32_t* order;  // [B]: sequence of rank r (most chunks first, ties by index)
   int B, T;
 };
 
 __global__ __launch_bounds__(1024) void gdn_seqmap_kernel(SeqMapArgs a) {
   __shared__ int32_t sv[1025];
   __shared__ int32_t sc[1024];
+  __shared__ int32_t nb[ORDER_MAXB];  // chunks per sequence, for the ranking
   const int t = threadIdx.x;
   auto off = [&](int i) { return a.cu ? min(max(a.cu[i], 0), a.T) : i * a.T; };
   int carry_tok = 0, carry_ch = 0;
@@ -831,9 +844,24 @@ __global__ __launch_bounds__(1024) void gdn_seqmap_kernel(SeqMapArgs a) {
       a.ch[i] = carry_ch + sc[t] - n;
     }
     if (i < a.B) a.pre[i] = p;
+    if (i < a.B && i < ORDER_MAXB) nb[i] = n;
     carry_tok = sv[1023];
     carry_ch += sc[1023];
     __syncthreads();
+  }
+  // longest first: rank = sequences with more chunks, or as many and a lower index
+  if (a.B <= ORDER_MAXB) {
+    for (int i = t; i < a.B; i += 1024) {
+      const int n = nb[i];
+      int r = 0;
+      for (int j = 0; j < a.B; ++j) {
+        const int m = nb[j];
+        r += (m > n) || (m == n && j < i);
+      }
+      a.order[r] = i;
+    }
+  } else {
+    for (int i = t; i < a.B; i += 1024) a.order[i] = i;
   }
 }
 
@@ -967,11 +995,13 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
     int32_t* tok = reinterpret_cast<int32_t*>(st + gdn_ws_stage(L));
     int32_t* ch = tok + (L.B + 1);
     int32_t* pre = ch + (L.B + 1);
-    SeqMapArgs m{L.cu_seqlens, L.resume ? L.fill_in : nullptr, tok, ch, pre, L.B, L.T};
+    int32_t* order = pre + L.B;
+    SeqMapArgs m{L.cu_seqlens, L.resume ? L.fill_in : nullptr, tok, ch, pre, order, L.B, L.T};
     hipLaunchKernelGGL(gdn_seqmap_kernel, dim3(1), dim3(1024), 0, stream, m);
     if (hipError_t e = hipGetLastError()) return e;
     sm.tok = tok;
     sm.ch = ch;
+    sm.order = order;  // read by the state kernel only
     if (L.resume) {
       const size_t nstage = size_t(L.B) * PC * L.H;
       uint16_t* sk = reinterpret_cast<uint16_t*>(st);

@@ -295,7 +295,7 @@ def test_varlen_contract():
     f = Fake()
     B, T, H = 5, 300, 3
     p = _pp(B=B, T=T, H=H)
-    assert _lib.prefill_varlen_workspace_size(p) == (T // 64 + B) * H * (3 * 64 * 64 * 2 + 64 * 4) + (3 * B + 2) * 4
+    assert _lib.prefill_varlen_workspace_size(p) == (T // 64 + B) * H * (3 * 64 * 64 * 2 + 64 * 4) + (4 * B + 2) * 4
     ws = f()
     need = _lib.prefill_varlen_workspace_size(p)
     assert _varlen(p, f) == 6                                   # workspace missing
@@ -347,9 +347,9 @@ def test_resume_contract():
     B, T, H = 3, 100, 2
     p = _pp(B=B, T=T, H=H)
     stage = B * 64 * H * (3 * 128 * 2 + 2 * 4)
-    need = (B * T // 64 + 2 * B) * H * (3 * 64 * 64 * 2 + 64 * 4) + stage + (3 * B + 2) * 4
+    need = (B * T // 64 + 2 * B) * H * (3 * 64 * 64 * 2 + 64 * 4) + stage + (4 * B + 2) * 4
     assert _lib.prefill_resume_workspace_size(p, 0) == need
-    need_v = (T // 64 + 2 * B) * H * (3 * 64 * 64 * 2 + 64 * 4) + stage + (3 * B + 2) * 4
+    need_v = (T // 64 + 2 * B) * H * (3 * 64 * 64 * 2 + 64 * 4) + stage + (4 * B + 2) * 4
     assert _lib.prefill_resume_workspace_size(p, 1) == need_v
     ws = f()
     assert _resume(p, f) == 6                                    # workspace missing

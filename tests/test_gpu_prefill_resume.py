@@ -137,3 +137,21 @@ def test_resume_varlen():
     for b, f in enumerate(fills):
         t0, t1 = int(cu[b]), int(cu[b + 1])
         _check_seq(st, o[t0:t1], pre, f, {key: x[key][t0:t1] for key in KEYS}, b, codes, scales)
+
+
+def test_resume_varlen_longest_first_order():
+    """Eight packed sequences at mixed fills with H = 2 (B * H a multiple of
+    8: the state pass runs them longest first): each against the oracle."""
+    H, d = 2, 128
+    fills = [3, 0, 63, 10, 40, 0, 22, 5]
+    lengths = [150, 7, 0, 64, 1, 120, 42, 90]
+    B = len(fills)
+    st, codes, scales, pre = _decode_state(fills, H, d, seed=90)
+    x = wl.gdn_prefill_varlen(lengths, H=H, dk=d, dv=d, seed=91)
+    cu = x["cu_seqlens"]
+    o = ops.prefill_resume(st, *(dev(x[key], torch.bfloat16 if key in ("q", "k", "v") else None)
+                                 for key in KEYS), cu_seqlens=dev(cu), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b, f in enumerate(fills):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        _check_seq(st, o[t0:t1], pre, f, {key: x[key][t0:t1] for key in KEYS}, b, codes, scales)

@@ -174,3 +174,21 @@ def test_varlen_malformed_offsets_are_clamped():
                 assert torch.equal(a[i, :, :r[i]], b[i, :, :r[i]]), name
         else:
             assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("H", [2, 4])
+def test_varlen_longest_first_order(H):
+    """B = 8 sequences (B * H a multiple of 8, so the state pass takes them
+    longest first, interleaved over the XCD segments): every sequence
+    against the oracle from a stored state, whatever its place in the order."""
+    d = 128
+    lengths = [5, 200, 64, 0, 130, 33, 1, 90]
+    B = len(lengths)
+    x = wl.gdn_prefill_varlen(lengths, H=H, dk=d, dv=d, seed=H + 60)
+    codes, scales = _random_state(B, H, d, H + 61)
+    cu = x["cu_seqlens"]
+    o, st = ops.prefill_varlen(*_inputs(x), dev(cu), init_codes=dev(codes),
+                               init_scales=dev(scales), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        _check_seq(x, cu, b, o, st, codes, scales)
