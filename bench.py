@@ -189,6 +189,57 @@ def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None, state_bits=8):
             "gbps": gbps}
 
 
+def bench_decode_long(torch, ops, wl, B2=256, steps=1024, warmup=16, n_tok=8):
+    """Large-batch decode: B2 sequences x H heads, `steps` consecutive decode
+    steps of one state (every sequence crosses window ends), timed end to
+    end.  n_tok token sets are bound once and reused in turn."""
+    dev = torch.device("cuda:0")
+    d = wl.decode_batch(B=B2, H=H, dk=DK, dv=DV, W=W, seed=2)
+    codes, scales = ops.quantize_state(torch.from_numpy(d["state"]).to(dev))
+    st = ops.DecodeState(codes, scales, W, fill=torch.from_numpy(d["fill"]).to(dev))
+    st.buf_k.copy_(torch.from_numpy(d["buf_k"]))
+    st.buf_v.copy_(torch.from_numpy(d["buf_v"]))
+    st.buf_alpha.copy_(torch.from_numpy(d["buf_alpha"]))
+    st.buf_beta.copy_(torch.from_numpy(d["buf_beta"]))
+    fills = d["fill"].astype(np.int64)
+    del d
+    o = torch.empty((B2, H, DV), dtype=torch.bfloat16, device=dev)
+    launchers = []
+    for s in range(n_tok):
+        x = wl.decode_tokens(B=B2, H=H, dk=DK, dv=DV, step=s, seed=3)
+        tok = [torch.from_numpy(x["q"]).to(dev).bfloat16(), torch.from_numpy(x["k"]).to(dev).bfloat16(),
+               torch.from_numpy(x["v"]).to(dev).bfloat16(), torch.from_numpy(x["alpha"]).to(dev),
+               torch.from_numpy(x["beta"]).to(dev)]
+        launchers.append((st.bind(*tok, o=o), tok))
+    for i in range(warmup):
+        launchers[i % n_tok][0]()
+        fills = np.where(fills + 1 == W, 0, fills + 1)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    total = 0
+    e0.record(stream)
+    for i in range(steps):
+        launchers[i % n_tok][0]()
+        total += decode_bytes(fills)
+        fills = np.where(fills + 1 == W, 0, fills + 1)
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1)
+    gbps = total / (ms * 1e-3) / 1e9
+    return {
+        "workload": f"{steps} consecutive decode steps, B={B2} H={H} d_k=d_v={DK} W={W}, int8 state, "
+                    "fp32 window buffer, fills from U{0..63} advancing (every sequence crosses window "
+                    "ends), timed end to end",
+        "ms_total": round(ms, 3), "ms_per_step": round(ms / steps, 5),
+        "tokens_s": round(B2 * steps / (ms * 1e-3), 1), "gbps": round(gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(total / steps)},
+    }
+
+
 def gdn_prefill_flops(B, T, H, dk=DK, dv=DV, C=64):
     """Useful FLOPs of the chunked GDN prefill (2 per multiply-add): per
     chunk-head K K^T (strictly lower), T = (I + A)^-1 (C^3/6), K S0^T, Q S0^T,
@@ -378,6 +429,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurements")
     ap.add_argument("--no-fp8-buffer", action="store_true", help="skip the FP8 window-buffer line")
     ap.add_argument("--no-state4", action="store_true", help="skip the 4-bit state line")
+    ap.add_argument("--no-long-decode", action="store_true", help="skip the B=256, 1024-step decode line")
     ap.add_argument("--no-bf16-buffer", action="store_true",
                     help="skip the decode measurement with the bf16 window buffer")
     ap.add_argument("--skip-decode", action="store_true",
@@ -469,6 +521,8 @@ def main():
                                                  DECODE_SOURCES + ["decode_q4.hip"], 1),
                          "algorithmic_bytes_per_launch": int(r4["bytes_per_launch"])},
         }
+    if not args.no_long_decode:
+        line["decode_b256_1024_steps"] = bench_decode_long(torch, ops, wl)
     if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, ops, wl)
     if not args.no_cpu_baseline:
