@@ -43,6 +43,12 @@ design notes):
     buffered writes are replayed on top of the dequantized state (the
     low-bit state takes the window's transitions, [PW]).
   * q and k are used as given (no 1/sqrt(d) scaling, no normalisation).
+  * the uniform 4-bit state (qmax = 7): the same codec with 15 levels
+    (scale = absmax/7, codes in [-7, 7]); windows and replay unchanged.
+  * continuing a sequence by prefill when f writes are buffered: the
+    buffered writes followed by the new tokens are one sequence whose
+    windows start at the first buffered write (the tests compose run_windowed
+    that way).
   * low-precision window buffers (variants): bf16 keys and values rounded to
     nearest even, or [PW]'s FP8 vector pairs as OCP E4M3 with one fp32
     scale absmax/448 per vector (IEEE divisions, ties to even); either way
