@@ -89,6 +89,7 @@ struct SeqMap {
 // ---------------------------------------------------------------- prep
 constexpr int KP = 136;  // bf16 pitch of [token][dim] tiles
 constexpr int AP = 65;   // fp32 pitch of A
+constexpr int PREP_GRID = 4 * 256;  // prep workgroups: four per CU
 constexpr int PREP_KT = PC * KP * 2 > (PC * PC + 3 * 256) * 4 ? PC * KP * 2 : (PC * PC + 3 * 256) * 4;
 
 struct PrepArgs {
@@ -99,6 +100,7 @@ struct PrepArgs {
   float* g_ws;  // [chunks*H][64]
   SeqMap sm;
   int B, H;
+  int total;  // chunk-heads the grid covers (an upper bound when mapped)
 };
 
 __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
@@ -109,46 +111,84 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
   __bf16* Kl = reinterpret_cast<__bf16*>(kt_raw);
   float* Tl = reinterpret_cast<float*>(kt_raw);
   float* Pl = Tl + PC * PC;
-  const int idx = blockIdx.x;  // chunk * H + h, chunks numbered across the sequences
-  const int h = idx % a.H;
-  const int g = idx / a.H;
-  int b;
-  if (a.sm.tok) {  // variable lengths: the grid covers an upper bound of the chunk count
-    if (g >= a.sm.ch[a.B]) return;
-    int lo = 0, hi = a.B - 1;  // last b with ch[b] <= g
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.sm.ch[mid] <= g) lo = mid; else hi = mid - 1;
+  // Each workgroup takes chunk-heads blockIdx.x, + gridDim.x, ... (index
+  // chunk * H + h, chunks numbered across the sequences) and loads the next
+  // one's keys, alpha and beta into registers while it works on the current.
+  struct Src {
+    const uint16_t* k;
+    const float* al;
+    const float* be;
+    size_t tok0;  // row of the chunk's first position in its source
+    int h, nvalid;  // tokens of the chunk in the sequence (< 64 only in a last, partial chunk)
+    bool ok;
+  };
+  auto locate = [&](int idx) {
+    Src r{};
+    r.ok = idx < a.total;
+    if (!r.ok) return r;
+    r.h = idx % a.H;
+    const int g = idx / a.H;
+    int b;
+    if (a.sm.tok) {  // mapped: the chunk count is only bounded by the grid
+      if (g >= a.sm.ch[a.B]) {
+        r.ok = false;
+        return r;
+      }
+      int lo = 0, hi = a.B - 1;  // last b with ch[b] <= g
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.sm.ch[mid] <= g) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+    } else {
+      b = g / ((a.sm.T + PC - 1) / PC);
     }
-    b = lo;
-  } else {
-    b = g / ((a.sm.T + PC - 1) / PC);
-  }
-  const int c = g - a.sm.chunk0(b);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lq = lane >> 4;
-  const size_t tok0 = a.sm.row0(b, c);
-  const bool stg = a.sm.staged(c);
-  const uint16_t* ksrc = stg ? a.sm.sk : a.k;
-  const float* asrc = stg ? a.sm.sa : a.alpha;
-  const float* bsrc = stg ? a.sm.sb : a.beta;
-
-  const int nvalid = a.sm.len(b) - c * PC;  // tokens of this chunk in the sequence (< 64 only in a last, partial chunk)
-  {  // keys of the chunk: thread -> token tid / 4, dims [(tid % 4) * 32, +32); padding keys are 0
+    const int c = g - a.sm.chunk0(b);
+    r.tok0 = a.sm.row0(b, c);
+    const bool stg = a.sm.staged(c);
+    r.k = stg ? a.sm.sk : a.k;
+    r.al = stg ? a.sm.sa : a.alpha;
+    r.be = stg ? a.sm.sb : a.beta;
+    r.nvalid = a.sm.len(b) - c * PC;
+    return r;
+  };
+  // keys: thread -> token tid / 4, dims [(tid % 4) * 32, +32); padding keys
+  // are 0.  alpha, beta: thread tid < 64 -> token tid (padding: 1 and 0).
+  uint4 w[4];
+  float al_t = 1.f, be_t = 0.f;
+  auto load = [&](const Src& r) {
+    const int tid = threadIdx.x;
     const int i = tid >> 2, qq = tid & 3;
-    const int ic = i < nvalid ? i : nvalid - 1;
-    const uint4* src = reinterpret_cast<const uint4*>(ksrc + ((tok0 + ic) * a.H + h) * PD + qq * 32);
-    uint4 w[4];
+    const int ic = i < r.nvalid ? i : r.nvalid - 1;
+    const uint4* src = reinterpret_cast<const uint4*>(r.k + ((r.tok0 + ic) * a.H + r.h) * PD + qq * 32);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = i < nvalid ? src[e] : make_uint4(0u, 0u, 0u, 0u);
+    for (int e = 0; e < 4; ++e) w[e] = i < r.nvalid ? src[e] : make_uint4(0u, 0u, 0u, 0u);
+    if (tid < 64) {
+      const size_t t = (r.tok0 + (tid < r.nvalid ? tid : r.nvalid - 1)) * a.H + r.h;
+      al_t = tid < r.nvalid ? r.al[t] : 1.f;
+      be_t = tid < r.nvalid ? r.be[t] : 0.f;
+    }
+  };
+  int idx = blockIdx.x;
+  Src cur = locate(idx);
+  if (!cur.ok) return;
+  load(cur);
+  for (;;) {
+  // per-thread offsets recomputed each round: hoisted out of the loop, the
+  // LDS addresses of the unrolled products would hold ~130 registers
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  {
+    const int i = tid >> 2, qq = tid & 3;
     uint4* dst = reinterpret_cast<uint4*>(Kl + i * KP + qq * 32);
 #pragma unroll
     for (int e = 0; e < 4; ++e) dst[e] = w[e];
   }
-  if (tid < 64) {  // g = inclusive prefix sum of log alpha (padding: alpha = 1, beta = 0)
-    const size_t r = (tok0 + (tid < nvalid ? tid : nvalid - 1)) * a.H + h;
-    float la = tid < nvalid ? logf(asrc[r]) : 0.f;
-    bl[tid] = tid < nvalid ? bsrc[r] : 0.f;
+  if (tid < 64) {  // g = inclusive prefix sum of log alpha
+    float la = logf(al_t);
+    bl[tid] = be_t;
 #pragma unroll
     for (int s = 1; s < 64; s <<= 1) {
       const float o = __shfl_up(la, s, 64);
@@ -157,6 +197,10 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
     gl[tid] = la;
     a.g_ws[size_t(idx) * PC + tid] = la;
   }
+  // the next chunk-head's loads fly during this one's work
+  const int nidx = idx + int(gridDim.x);
+  const Src nxt = locate(nidx);
+  if (nxt.ok) load(nxt);
   __syncthreads();
 
   // A from the lower 16x16 tiles of K K^T (kept in registers until K is dead)
@@ -272,6 +316,11 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
       *reinterpret_cast<bf16x8*>(dst + pl * PC * PC) = p[pl][0];
       *reinterpret_cast<bf16x8*>(dst + pl * PC * PC + 8) = p[pl][1];
     }
+  }
+  if (!nxt.ok) break;
+  idx = nidx;
+  cur = nxt;
+  __syncthreads();  // the next chunk's keys overwrite T's space
   }
 }
 
@@ -1021,8 +1070,11 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
   }
   const size_t nch = gdn_chunks(L);
   if (nch > 0) {
-    PrepArgs p{static_cast<const uint16_t*>(L.k), L.alpha, L.beta, T_ws, g_ws, sm, L.B, L.H};
-    hipLaunchKernelGGL(gdn_prep_kernel, dim3(unsigned(nch * L.H)), dim3(256), 0, stream, p);
+    const size_t total = nch * L.H;
+    PrepArgs p{static_cast<const uint16_t*>(L.k), L.alpha, L.beta, T_ws, g_ws, sm, L.B, L.H, int(total)};
+    // four resident workgroups per CU (LDS): each loops over chunk-heads
+    const unsigned grid = unsigned(total < PREP_GRID ? total : PREP_GRID);
+    hipLaunchKernelGGL(gdn_prep_kernel, dim3(grid), dim3(256), 0, stream, p);
     if (hipError_t e = hipGetLastError()) return e;
   }
   StateArgs s{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k),
