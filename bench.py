@@ -235,7 +235,8 @@ def bench_decode_long(torch, ops, wl, B2=256, steps=1024, warmup=16, n_tok=8):
         "ms_total": round(ms, 3), "ms_per_step": round(ms / steps, 5),
         "tokens_s": round(B2 * steps / (ms * 1e-3), 1), "gbps": round(gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic("decode_b256_h32_1024steps_traffic.json", DECODE_SOURCES, 1),
                      "algorithmic_bytes_per_launch": int(total / steps)},
     }
 
