@@ -283,3 +283,30 @@ def test_prefill4_resume_split_equals_one_call():
     assert torch.equal(a_o[:, T1:], b_o)
     for name in ("codes", "scales", "fill"):
         assert torch.equal(getattr(a_st, name), getattr(b_st, name)), name
+
+
+def test_prefill4_varlen_matches_oracle():
+    """A packed batch with the 4-bit state (eight sequences, B * H a
+    multiple of 8, so the longest-first order runs too): every sequence's
+    outputs, boundary state and open writes against the oracle."""
+    H, d = 2, 128
+    lengths = [5, 200, 64, 0, 130, 33, 1, 90]
+    B = len(lengths)
+    x = wl.gdn_prefill_varlen(lengths, H=H, dk=d, dv=d, seed=70)
+    cu = x["cu_seqlens"]
+    o, st = ops.prefill_varlen(*_pf_inputs(x), dev(cu), out_dtype=torch.float32, state_bits=4)
+    torch.cuda.synchronize()
+    codes = unpack4(host(st.codes))
+    for b in range(B):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        n = t1 - t0
+        ref = O.prefill(*(x[key][None, t0:t1] for key in KEYS), W=W64, qmax=7)
+        assert host(st.fill)[b] == n % W64
+        if n:
+            err = max_rel_err(host(o)[t0:t1], ref["o"][0])
+            assert err <= (OUT_TOL_F32 if n < W64 else OUT_TOL_BF16), (b, err)
+        assert_codes(codes[b], ref["codes"][0], f"sequence {b} codes")
+        if n < 2 * W64:
+            assert_scales(host(st.scales)[b], ref["scale"][0], f"sequence {b} scales")
+        r = n % W64
+        assert np.array_equal(host(st.buf_k)[b, :, :r], ref["buf"]["k"][0]), b
