@@ -39,6 +39,30 @@ def _need(t, name, dtype=None, device=None):
     return t
 
 
+def _shape(t, shape, name):
+    """The library sees raw pointers only: every buffer a caller passes must
+    have exactly the shape the kernels address."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _state_shapes(st, B, H, d_k, d_v, window):
+    """A DecodeState handed to a prefill entry point: fp32 window buffer of
+    `window` slots, codes/scales/fill of B sequences."""
+    if st.buf_k.dtype != torch.float32:
+        raise ValueError("state: the prefill hand-over writes an fp32 window buffer")
+    if st.window != window:
+        raise ValueError(f"state: window {st.window}, the prefill hand-over needs {window}")
+    _shape(st.codes, (B, H, d_v, d_k * st.state_bits // 8), "state.codes")
+    _shape(st.scales, (B, H, d_v), "state.scales")
+    _shape(st.buf_k, (B, H, window, d_k), "state.buf_k")
+    _shape(st.buf_v, (B, H, window, d_v), "state.buf_v")
+    _shape(st.buf_alpha, (B, H, window), "state.buf_alpha")
+    _shape(st.buf_beta, (B, H, window), "state.buf_beta")
+    _shape(st.fill, (B,), "state.fill")
+
+
 def quantize_state(S, codes=None, scales=None, wht=False, state_bits=8):
     """Per-row codec of S[..., d_k] (fp32): returns (codes, scales fp32[...]).
     state_bits 8: int8 codes [..., d_k]; 4: packed 4-bit codes [..., d_k/2]
@@ -172,11 +196,11 @@ def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_code
                         out_dtype=out_dtype, state_bits=state_bits)
     if o is None:
         o = torch.empty((B, T, H, d_v), dtype=out_dtype, device=dev)
-    _need(o, "o", out_dtype, dev)
+    _shape(_need(o, "o", out_dtype, dev), (B, T, H, d_v), "o")
     if ssd:
         if state_f32 is None:
             state_f32 = torch.empty((B, H, d_v, d_k), dtype=torch.float32, device=dev)
-        _need(state_f32, "state_f32", torch.float32, dev)
+        _shape(_need(state_f32, "state_f32", torch.float32, dev), (B, H, d_v, d_k), "state_f32")
     else:
         _need(beta, "beta", torch.float32, dev)
         if tuple(beta.shape) != (B, T, H):
@@ -185,11 +209,14 @@ def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_code
             codes = torch.empty((B, H, d_v, d_k * state_bits // 8), dtype=torch.int8, device=dev)
         if scales is None:
             scales = torch.empty((B, H, d_v), dtype=torch.float32, device=dev)
-        _need(codes, "codes", torch.int8, dev)
-        _need(scales, "scales", torch.float32, dev)
+        cshape = (B, H, d_v, d_k * state_bits // 8)
+        _shape(_need(codes, "codes", torch.int8, dev), cshape, "codes")
+        _shape(_need(scales, "scales", torch.float32, dev), (B, H, d_v), "scales")
+        if (init_codes is None) != (init_scales is None):
+            raise ValueError("init_codes and init_scales: both or neither")
         if init_codes is not None:
-            _need(init_codes, "init_codes", torch.int8, dev)
-            _need(init_scales, "init_scales", torch.float32, dev)
+            _shape(_need(init_codes, "init_codes", torch.int8, dev), cshape, "init_codes")
+            _shape(_need(init_scales, "init_scales", torch.float32, dev), (B, H, d_v), "init_scales")
     need = int(_lib.prefill_workspace_size(p))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -202,6 +229,14 @@ def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_code
     if ssd:
         return o, state_f32
     return o, codes, scales
+
+
+def _init_shapes(init_codes, init_scales, cshape, dev):
+    if (init_codes is None) != (init_scales is None):
+        raise ValueError("init_codes and init_scales: both or neither")
+    if init_codes is not None:
+        _shape(_need(init_codes, "init_codes", torch.int8, dev), cshape, "init_codes")
+        _shape(_need(init_scales, "init_scales", torch.float32, dev), cshape[:3], "init_scales")
 
 
 def prefill_handoff_workspace_size(q, v, *, window=64, out_dtype=torch.bfloat16):
@@ -232,17 +267,16 @@ def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_sc
                         out_dtype=out_dtype, state_bits=state_bits)
     if o is None:
         o = torch.empty((B, T, H, d_v), dtype=out_dtype, device=dev)
-    _need(o, "o", out_dtype, dev)
-    if init_codes is not None:
-        _need(init_codes, "init_codes", torch.int8, dev)
-        _need(init_scales, "init_scales", torch.float32, dev)
+    _shape(_need(o, "o", out_dtype, dev), (B, T, H, d_v), "o")
+    _init_shapes(init_codes, init_scales, (B, H, d_v, d_k * state_bits // 8), dev)
     st = state
     if st is None:
         st = DecodeState(torch.empty((B, H, d_v, d_k * state_bits // 8), dtype=torch.int8, device=dev),
                          torch.empty((B, H, d_v), dtype=torch.float32, device=dev), window,
                          fill=torch.zeros(B, dtype=torch.int32, device=dev), state_bits=state_bits)
-    if st.buf_k.dtype != torch.float32 or tuple(st.codes.shape) != (B, H, d_v, d_k * state_bits // 8):
-        raise ValueError("state: a DecodeState of matching shape with an fp32 window buffer")
+    if st.state_bits != state_bits:
+        raise ValueError("state: its code width differs from state_bits")
+    _state_shapes(st, B, H, d_k, d_v, 64)
     need = int(_lib.prefill_handoff_workspace_size(p))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -291,17 +325,16 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=No
     p = _varlen_params(q, v, B, window=window, out_dtype=out_dtype, state_bits=state_bits)
     if o is None:
         o = torch.empty((T, H, d_v), dtype=out_dtype, device=dev)
-    _need(o, "o", out_dtype, dev)
-    if init_codes is not None:
-        _need(init_codes, "init_codes", torch.int8, dev)
-        _need(init_scales, "init_scales", torch.float32, dev)
+    _shape(_need(o, "o", out_dtype, dev), (T, H, d_v), "o")
+    _init_shapes(init_codes, init_scales, (B, H, d_v, d_k * state_bits // 8), dev)
     st = state
     if st is None:
         st = DecodeState(torch.empty((B, H, d_v, d_k * state_bits // 8), dtype=torch.int8, device=dev),
                          torch.empty((B, H, d_v), dtype=torch.float32, device=dev), window,
                          fill=torch.zeros(B, dtype=torch.int32, device=dev), state_bits=state_bits)
-    if st.buf_k.dtype != torch.float32 or tuple(st.codes.shape) != (B, H, d_v, d_k * state_bits // 8):
-        raise ValueError("state: a DecodeState of matching shape with an fp32 window buffer")
+    if st.state_bits != state_bits:
+        raise ValueError("state: its code width differs from state_bits")
+    _state_shapes(st, B, H, d_k, d_v, 64)
     need = int(_lib.prefill_varlen_workspace_size(p))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -335,8 +368,7 @@ def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=to
     st = state
     B, H, d_v, d_k = st.codes.shape
     d_k = d_k * 8 // st.state_bits
-    if st.buf_k.dtype != torch.float32 or st.window != 64:
-        raise ValueError("state: a DecodeState with an fp32 window buffer of 64 slots")
+    _state_shapes(st, B, H, d_k, d_v, 64)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, torch.bfloat16, dev)
     for name, t in (("alpha", alpha), ("beta", beta)):
@@ -360,7 +392,7 @@ def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=to
                            _lib.GDNQ_FLAG_STATE_4BIT if st.state_bits == 4 else 0)
     if o is None:
         o = torch.empty(lead + (H, d_v), dtype=out_dtype, device=dev)
-    _need(o, "o", out_dtype, dev)
+    _shape(_need(o, "o", out_dtype, dev), lead + (H, d_v), "o")
     need = int(_lib.prefill_resume_workspace_size(p, cu_seqlens is not None))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
