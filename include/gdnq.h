@@ -336,6 +336,18 @@ gdnq_status gdnq_prefill_resume(const gdnq_prefill_params* p, const int32_t* cu_
                                 float* buf_v, float* buf_alpha, float* buf_beta, int32_t* fill_out,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * gdnq_decode_set_schedule -- tuning hook of gdnq_decode_step's persistent
+ *   launch (not part of the method; results do not depend on it).
+ *   grid: workgroups of the persistent grid; open_waves: waves that take the
+ *   sequences whose window stays open.  0 restores the default of either.
+ *   The initial values come from the environment variables GDNQ_DECODE_GRID
+ *   and GDNQ_DECODE_OPEN_WAVES, read once when the library is loaded.  The
+ *   setting is process-wide and applies to launches made after the call.
+ *   Errors: SHAPE (a negative value).
+ * ------------------------------------------------------------------------ */
+gdnq_status gdnq_decode_set_schedule(int32_t grid, int32_t open_waves);
+
 /* Status text, last error detail (thread-local, "" if none), library version. */
 const char* gdnq_status_string(gdnq_status s);
 const char* gdnq_last_error(void);

@@ -26,7 +26,7 @@ EXPORTS = ("gdnq_quantize_state", "gdnq_decode_step", "gdnq_prefill_workspace_si
            "gdnq_prefill_chunked", "gdnq_prefill_handoff_workspace_size", "gdnq_prefill_handoff",
            "gdnq_prefill_varlen_workspace_size", "gdnq_prefill_varlen",
            "gdnq_prefill_resume_workspace_size", "gdnq_prefill_resume",
-           "gdnq_status_string", "gdnq_last_error", "gdnq_version")
+           "gdnq_decode_set_schedule", "gdnq_status_string", "gdnq_last_error", "gdnq_version")
 
 
 class DecodeParams(ctypes.Structure):
@@ -81,6 +81,8 @@ def _load():
     lib.gdnq_prefill_resume_workspace_size.restype = sz
     lib.gdnq_prefill_resume.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 16 + [sz, vp]
     lib.gdnq_prefill_resume.restype = i32
+    lib.gdnq_decode_set_schedule.argtypes = [i32, i32]
+    lib.gdnq_decode_set_schedule.restype = i32
     lib.gdnq_status_string.argtypes = [i32]
     lib.gdnq_status_string.restype = ctypes.c_char_p
     lib.gdnq_last_error.argtypes = []
@@ -97,6 +99,10 @@ def check(status):
     if status != GDNQ_OK:
         raise GdnqError(status, lib.gdnq_last_error().decode())
     return status
+
+
+def decode_set_schedule(grid, open_waves):
+    return lib.gdnq_decode_set_schedule(grid, open_waves)
 
 
 def quantize_state(S, rows, d_k, codes, scales, flags, stream):

@@ -84,7 +84,14 @@ const char* gdnq_status_string(gdnq_status s) {
 
 const char* gdnq_last_error(void) { return g_err; }
 
-int32_t gdnq_version(void) { return 100; }
+int32_t gdnq_version(void) { return 101; }
+
+gdnq_status gdnq_decode_set_schedule(int32_t grid, int32_t open_waves) {
+  if (grid < 0 || open_waves < 0)
+    return fail(GDNQ_ERR_SHAPE, "grid = %d, open_waves = %d: 0 (default) or positive", grid, open_waves);
+  gdnq::set_decode_schedule(grid, open_waves);
+  return ok();
+}
 
 gdnq_status gdnq_quantize_state(const float* S, int64_t rows, int32_t d_k, int8_t* codes,
                                 float* scales, uint32_t flags, void* stream) {

@@ -910,24 +910,29 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void decode_kernel(Deco
   }
 }
 
+// Schedule overrides (tuning and the schedule tests): the persistent grid
+// size and the number of waves that take open heads, 0 = the defaults below.
+// They start from GDNQ_DECODE_GRID / GDNQ_DECODE_OPEN_WAVES, read once when
+// the library is loaded, and gdnq_decode_set_schedule replaces them.
+struct DecodeSchedule {
+  int grid, open_waves;
+};
+DecodeSchedule decode_schedule();
+
 // Persistent grid: DEC_WG_PER_CU resident workgroups per CU on 256 CUs, never
-// more workgroups than jobs.  GDNQ_DECODE_GRID overrides it (tuning).
+// more workgroups than jobs.
 inline unsigned decode_grid(int B, int H, int rc) {
   const long jobs_max = long(B) * H * rc;
   long g = 256 * DEC_WG_PER_CU;  // resident workgroups on 256 CUs
-  if (const char* e = getenv("GDNQ_DECODE_GRID")) {
-    const long v = atol(e);
-    if (v > 0) g = v;
-  }
+  const int o = decode_schedule().grid;
+  if (o > 0) g = o;
   return unsigned(jobs_max < g ? jobs_max : g);
 }
 
-// Waves that take open heads.  GDNQ_DECODE_OPEN_WAVES overrides it (tuning,
-// and the schedule tests).
+// Waves that take open heads.
 inline int decode_open_waves() {
-  const char* e = getenv("GDNQ_DECODE_OPEN_WAVES");
-  const long v = e ? atol(e) : 0;
-  return v > 0 && v < (1L << 30) ? int(v) : DEC_OPEN_WAVES;
+  const int o = decode_schedule().open_waves;
+  return o > 0 ? o : DEC_OPEN_WAVES;
 }
 
 template <int DK, int DV, bool IB, bool OB, bool WHT, int BB, int QB>

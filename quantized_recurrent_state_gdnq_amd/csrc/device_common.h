@@ -226,10 +226,12 @@ __device__ __forceinline__ int codec_code(float x, float scale) {
 // |x/scale| * 2^-23 <= 1.6e-5 of the exact quotient and fl(x/scale) within
 // 7.6e-6 of it, so their nearest integers can differ only when q lies within
 // 2.4e-5 of a half-integer; only then (rarely) the IEEE divisions are done.
+// A subnormal scale below 2^-128 has no finite reciprocal (and subnormal
+// scales carry fewer significant bits): such rows always divide.
 template <int N, int QMAX = 127>
 __device__ __forceinline__ void codec_codes(const float (&x)[N], float scale, float (&c)[N]) {
   const float inv = scale > 0.0f ? __frcp_rn(scale) : 0.0f;
-  bool near = false;
+  bool near = scale > 0.0f && scale < 1.17549435e-38f;  // subnormal: divide
 #pragma unroll
   for (int e = 0; e < N; ++e) {
     const float q = x[e] * inv;

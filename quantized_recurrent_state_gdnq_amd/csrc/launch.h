@@ -41,6 +41,7 @@ struct DecodeLaunch {
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 int decode_row_split();
 int decode_max_batch();
+void set_decode_schedule(int grid, int open_waves);  // 0 = default
 
 struct PrefillLaunch {
   const void* q;

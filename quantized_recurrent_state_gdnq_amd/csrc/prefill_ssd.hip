@@ -16,12 +16,14 @@
 //   operand -- (int8 mode) four lanes per token row of q or k: FWHT in
 //              registers, row absmax, codec; codes and scales to the
 //              workspace (one launch for both operands).
-//   state   -- one workgroup per (sequence, head, 64 rows of d_v), the state
-//              rows held in LDS as three bf16 parts (hi + mid + lo equals the
-//              fp32 value exactly), three barriers per chunk.  All products on
+//   state   -- one workgroup per (sequence, head, 64 rows of d_v), two
+//              barriers per chunk.  Four state waves hold 16 rows each of the
+//              fp32 state as MFMA accumulators (eight 16x16 tiles of S^T) and
+//              update them in place; four aux waves build the decay matrix,
+//              form the output and stage the next chunk.  All products on
 //              bf16 MFMA: codes are exact in bf16; the state and the decayed,
-//              scaled V are split into three parts, the output-only decay
-//              matrix into two.
+//              scaled V are split into three bf16 parts (hi + mid + lo equals
+//              the fp32 value exactly), the output-only decay matrix into two.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"

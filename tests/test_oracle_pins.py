@@ -34,6 +34,20 @@ def test_codec_golden_rows():
         assert codes[0].tolist() == [int(v) for v in cd.split()]
 
 
+def test_codec_subnormal_scale_golden():
+    """A row whose scale is an fp32 subnormal (2^-140, beyond the range where
+    1/scale is finite): the codes are the exact quotients.  Catches a codec
+    that multiplies by a reciprocal, or that flushes subnormals to zero."""
+    g = read_golden("codec_subnormal.txt")
+    for p2, row, sc, cd in zip(g["pow2"], g["row"], g["scale"], g["codes"]):
+        f = 2.0 ** int(p2)
+        x = (np.array([float(v) for v in row.split()], F64) * f).astype(F32)[None]
+        assert np.array_equal(x[0].astype(F64), np.array([float(v) for v in row.split()]) * f)  # exact
+        codes, scale = O.quantize_rows(x)
+        assert scale[0] == F32(float(sc) * f) and scale[0] < np.finfo(F32).tiny
+        assert codes[0].tolist() == [int(v) for v in cd.split()]
+
+
 def test_codec_properties_random():
     """P4: |x - deq(quant(x))| <= scale/2 per entry; every nonzero row reaches
     |code| = 127; quant(-x) = -quant(x); codes in [-127, 127]."""
