@@ -7,9 +7,8 @@ Bars (the ones the decode tests use):
     inputs are exact in both), <= 2e-2 with bf16 output;
   * teacher-forced requantization (the oracle starts from the GPU's state):
     codes +-1 on <= 0.1%, scales 1e-5;
-  * free-running over several windows: codes +-1 on <= 0.1%, scales within
-    2/127 (a +-1 code flip moves the next window's row absmax by at most one
-    old code unit, and the transitions are non-expansive).
+  * free-running over several windows (a diagnostic): codes +-1 on <= 0.1%,
+    scales within the drift bound of gpu_util.FREE_SCALE_DRIFT.
 """
 
 import numpy as np
@@ -17,8 +16,9 @@ import pytest
 import torch
 
 import oracle as O
+import oracle_pool
 import workloads as wl
-from gpu_util import (DEV, OUT_TOL_BF16, OUT_TOL_F32, Guarded, assert_codes, assert_scales,
+from gpu_util import (DEV, assert_free_scales, OUT_TOL_BF16, OUT_TOL_F32, Guarded, assert_codes, assert_scales,
                       dev, host, max_rel_err)
 
 pytestmark = pytest.mark.gpu
@@ -41,8 +41,32 @@ def _random_state(B, H, d, seed):
     return O.quantize_rows(S)
 
 
-def _free_scale_rel(got, ref):
-    return float(np.max(np.abs(got - ref) / np.where(ref > 0, ref, 1)))
+def test_prefill_requantizes_subnormal_scale_rows():
+    """A stored state whose row 5 has a subnormal scale (the golden row of
+    tests/golden/codec_subnormal.txt) carried through one window with
+    alpha = 1, beta = 0 (the state does not change): the window-end
+    requantization must give back the same codes and scales, for the tiny
+    row and for the ordinary rows, as the oracle does."""
+    from conftest import read_golden
+    g = read_golden("codec_subnormal.txt")
+    f = 2.0 ** int(g["pow2"][0])
+    B, H, d, T = 1, 2, 128, 64
+    x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=31)
+    x["alpha"][:] = 1.0
+    x["beta"][:] = 0.0
+    S = (np.random.default_rng(32).standard_normal((B, H, d, d)) * 0.5).astype(np.float32)
+    vals = np.array([float(v) for v in g["row"][0].split()]) * f
+    S[0, 1, 5] = 0.0
+    S[0, 1, 5, :len(vals)] = vals
+    codes, scales = O.quantize_rows(S)
+    assert scales[0, 1, 5] == np.float32(f)
+    ref = O.prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], W=W, codes0=codes, scale0=scales)
+    o, cg, sg = ops.prefill_chunked(*_inputs(x), init_codes=dev(codes), init_scales=dev(scales),
+                                    out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(ref["codes"], codes) and np.array_equal(ref["scale"], scales)
+    assert np.array_equal(host(cg), codes)
+    assert np.array_equal(host(sg), scales)
 
 
 @pytest.mark.parametrize("out_dt", [torch.float32, torch.bfloat16])
@@ -89,7 +113,7 @@ def test_prefill_free_running(init):
     err = max_rel_err(host(o), ref["o"])
     assert err <= OUT_TOL_BF16, err
     assert_codes(host(cg), ref["codes"], "final codes")
-    assert _free_scale_rel(host(sg), ref["scale"]) <= 2.0 / 127.0
+    assert_free_scales(host(sg), ref["scale"], f"prefill 5 windows init={init}")
 
 
 def test_prefill_matches_fp64_chunk_form():
@@ -155,22 +179,79 @@ def test_prefill_state_rows_independent_of_batch():
     assert np.array_equal(host(c)[1:2], host(c1)) and np.array_equal(host(s)[1:2], host(s1))
 
 
-def test_prefill_batch4_seq8192_heads16_sampled():
+def test_prefill_batch4_seq8192_heads16_every_window_teacher_forced():
     """The prefill workload at its full size (B=4, T=8192, H=16, d=128,
-    chunk = window = 64, bf16 output) in one call, as it is timed.  Three
-    sampled (sequence, head) pairs are recomputed by the oracle over all
-    8192 tokens (free-running, 128 windows): outputs within 2e-2, final codes
-    +-1 on <= 0.1%, scales within 2/127.  Every output is finite."""
+    chunk = window = 64) in one call, as it is timed (bf16 output), and the
+    same tokens again one window per call, each call from the state the
+    previous one left on the GPU.
+
+    * The window-per-call run ends in the one-call run's codes and scales,
+      bitwise, and its outputs round to the one-call bf16 outputs: so the
+      checks below are checks of the timed call.
+    * Every one of the 128 windows, on all 64 (sequence, head) pairs, is
+      compared with the oracle started from the GPU's state before that
+      window (teacher-forced): outputs (fp32) within 1e-3, requantized
+      codes +-1 on <= 0.1%, scales within 1e-5."""
+    B, T, H, d = 4, 8192, 16, 128
+    x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=0)
+    q, k, v, a, b = _inputs(x)
+    o_all, c_all, s_all = ops.prefill_chunked(q, k, v, a, b, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o_all_h = host(o_all)
+    assert np.isfinite(o_all_h).all()
+    codes = torch.zeros((B, H, d, d), dtype=torch.int8, device=DEV)
+    scales = torch.zeros((B, H, d), dtype=torch.float32, device=DEV)
+    ws = torch.empty(ops.prefill_workspace_size(q[:, :W], v[:, :W]), dtype=torch.uint8, device=DEV)
+    jobs = []
+    with oracle_pool.pool() as ex:
+        for c in range(T // W):
+            sl = slice(c * W, (c + 1) * W)
+            before_c, before_s = host(codes), host(scales)
+            cn = torch.empty_like(codes)
+            sn = torch.empty_like(scales)
+            o, _, _ = ops.prefill_chunked(q[:, sl].contiguous(), k[:, sl].contiguous(),
+                                          v[:, sl].contiguous(), a[:, sl].contiguous(),
+                                          b[:, sl].contiguous(), init_codes=codes, init_scales=scales,
+                                          codes=cn, scales=sn, out_dtype=torch.float32, workspace=ws)
+            torch.cuda.synchronize()
+            go = host(o)
+            # the one-call bf16 outputs are these fp32 outputs rounded once
+            ob = o_all_h[:, sl]
+            assert np.all(np.abs(ob - go) <= np.abs(go) * 2.0 ** -8 + 1e-30), f"window {c}: bf16 outputs"
+            xs = {n: np.ascontiguousarray(x[n][:, sl]) for n in ("q", "k", "v", "alpha", "beta")}
+            fut = oracle_pool.submit(ex, "prefill_window", xs, before_c, before_s, W, 127)
+            jobs.append((c, fut, go, host(cn), host(sn)))
+            codes, scales = cn, sn
+        assert torch.equal(codes, c_all) and torch.equal(scales, s_all)
+        worst_o = worst_flip = 0.0
+        for c, fut, go, gc, gs in jobs:
+            ro, rc, rs = fut.result()
+            err = max_rel_err(go, ro)
+            assert err <= OUT_TOL_F32, f"window {c}: o max relative error {err:.3e}"
+            worst_o = max(worst_o, err)
+            worst_flip = max(worst_flip, assert_codes(gc, rc, f"window {c} codes"))
+            assert_scales(gs, rs, f"window {c} scales")
+    print(f"B4 T8192 H16: 128 windows x 64 heads teacher-forced, worst o {worst_o:.2e}, "
+          f"worst flip fraction {worst_flip:.2e}")
+
+
+def test_prefill_batch4_seq8192_heads16_free_running_sampled():
+    """Diagnostic beside the gate above: three sampled (sequence, head) pairs
+    of the full-size call followed by the oracle on its own over all 8192
+    tokens (128 windows).  Outputs within 2e-2 and final codes +-1 on
+    <= 0.1%; scales within the free-running drift bound of two code units
+    relative (2/127): once an admitted +-1 difference exists the two runs
+    carry different states, so the per-requantization scale bar does not
+    apply (the design notes derive the bound)."""
     B, T, H, d = 4, 8192, 16, 128
     x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=0)
     o, cg, sg = ops.prefill_chunked(*_inputs(x), out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     go, gc, gs = host(o), host(cg), host(sg)
-    assert np.isfinite(go).all()
     for b, h in ((0, 0), (2, 7), (3, 15)):
         xs = {k: np.ascontiguousarray(v[b:b + 1, :, h:h + 1]) for k, v in x.items()}
         ref = O.prefill(xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], W=W)
         err = max_rel_err(go[b, :, h], ref["o"][0, :, 0])
         assert err <= OUT_TOL_BF16, f"(b={b}, h={h}) o error {err:.3e}"
         assert_codes(gc[b, h], ref["codes"][0, 0], f"(b={b}, h={h}) codes")
-        assert _free_scale_rel(gs[b, h], ref["scale"][0, 0]) <= 2.0 / 127.0
+        assert_free_scales(gs[b, h], ref["scale"][0, 0], f"prefill 128 windows (b={b}, h={h})")

@@ -16,7 +16,7 @@ import torch
 
 import oracle as O
 import workloads as wl
-from gpu_util import (DEV, OUT_TOL_BF16, OUT_TOL_F32, assert_codes, assert_scales, dev, host,
+from gpu_util import (assert_free_scales, DEV, OUT_TOL_BF16, OUT_TOL_F32, assert_codes, assert_scales, dev, host,
                       max_rel_err)
 
 pytestmark = pytest.mark.gpu
@@ -49,8 +49,7 @@ def _check(st, o, ref, T, tol, teacher_codes):
         assert_scales(host(st.scales), ref["scale"], "scales at the last boundary")
     else:
         assert_codes(host(st.codes), ref["codes"], "codes at the last boundary")
-        rel = np.max(np.abs(host(st.scales) - ref["scale"]) / np.where(ref["scale"] > 0, ref["scale"], 1))
-        assert rel <= 2.0 / 127.0, rel
+        assert_free_scales(host(st.scales), ref["scale"], "hand-over scales at the last boundary")
     for name, key in (("buf_k", "k"), ("buf_v", "v"), ("buf_alpha", "alpha"), ("buf_beta", "beta")):
         assert np.array_equal(host(getattr(st, name))[:, :, :r], ref["buf"][key]), name
 

@@ -19,7 +19,7 @@ import torch
 
 import oracle as O
 import workloads as wl
-from gpu_util import (DEV, OUT_TOL_BF16, OUT_TOL_F32, assert_codes, assert_scales, dev, host,
+from gpu_util import (assert_free_scales, DEV, OUT_TOL_BF16, OUT_TOL_F32, assert_codes, assert_scales, dev, host,
                       max_rel_err)
 
 pytestmark = pytest.mark.gpu
@@ -74,9 +74,7 @@ def _check_seq(st, o_new, pre, f, new, b, codes0, scales0):
     if total < 2 * W:
         assert_scales(scales, ref["scale"][0], f"sequence {b} scales")
     else:
-        sc = ref["scale"][0]
-        rel = np.max(np.abs(scales - sc) / np.where(sc > 0, sc, 1))
-        assert rel <= 2.0 / 127.0, (b, rel)
+        assert_free_scales(scales, ref["scale"][0], f"resume sequence {b}")
     for name, key in (("buf_k", "k"), ("buf_v", "v"), ("buf_alpha", "alpha"), ("buf_beta", "beta")):
         assert np.array_equal(host(getattr(st, name))[b, :, :r], ref["buf"][key][0]), (b, name)
 

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import oracle as O
+import oracle_pool
 import workloads as wl
 from gpu_util import DEV, OUT_TOL_BF16, OUT_TOL_F32, Guarded, assert_codes, assert_scales, dev, host, max_rel_err
 
@@ -106,21 +107,42 @@ def test_ssd_empty_sequence():
     assert not host(S).any()
 
 
-def test_ssd_batch2_seq4096_heads80_sampled():
+def test_ssd_batch2_seq4096_heads80_every_head():
     """The SSD workload at its full size (B=2, T=4096, H=80, d_k=128,
-    d_v=64, rotated int8 q/k, bf16 output) in one call, as it is timed; three
-    sampled (sequence, head) pairs recomputed by the oracle over all 4096
-    tokens."""
+    d_v=64, rotated int8 q/k, bf16 output) in one call, as it is timed.  The
+    state is never quantized, so the oracle run on its own is the gate: every
+    (sequence, head) pair, all 4096 outputs and the final fp32 state, within
+    2e-2; and every quantized operand row the kernel used (read back from
+    the workspace) to the code bar (+-1 on <= 0.1%, scales 1e-5)."""
     B, T, H, dv = 2, 4096, 80, 64
     x = wl.ssd_prefill(B=B, T=T, H=H, dk=128, dv=dv, seed=0)
-    o, S = _run(x, int8=True, wht=True, out_dt=torch.bfloat16)
+    q = dev(x["q"], torch.bfloat16)
+    need = ops.prefill_workspace_size(q, dev(x["v"], torch.bfloat16), ssd=True, int8_qk=True, wht=True)
+    ws = torch.empty(need, dtype=torch.int8, device=DEV)
+    o, S = _run(x, int8=True, wht=True, out_dt=torch.bfloat16, workspace=ws)
     torch.cuda.synchronize()
     go, gs = host(o), host(S)
     assert np.isfinite(go).all() and np.isfinite(gs).all()
-    for b, h in ((0, 0), (1, 41), (1, 79)):
-        xs = {n: np.ascontiguousarray(x[n][b:b + 1, :, h:h + 1]) for n in ("q", "k", "v", "alpha")}
-        ref = _ref(xs, int8=True, wht=True)
-        err_o = max_rel_err(go[b, :, h], ref["o"][0, :, 0])
-        err_s = max_rel_err(gs[b, h], ref["S"][0, 0])
-        assert err_o <= OUT_TOL_BF16, f"(b={b}, h={h}) o error {err_o:.3e}"
-        assert err_s <= OUT_TOL_BF16, f"(b={b}, h={h}) state error {err_s:.3e}"
+    HB = 10  # heads per oracle task
+    with oracle_pool.pool() as ex:
+        futs = [(b, h0, oracle_pool.submit(ex, "ssd_sequence",
+                                           {n: np.ascontiguousarray(x[n][b:b + 1, :, h0:h0 + HB])
+                                            for n in ("q", "k", "v", "alpha")}))
+                for b in range(B) for h0 in range(0, H, HB)]
+        rows = B * T * H
+        w = host(ws)
+        for name, off, soff in (("q", 0, 2 * rows * 128), ("k", rows * 128, 2 * rows * 128 + 4 * rows)):
+            c = w[off:off + rows * 128].view(np.int8).reshape(B, T, H, 128)
+            sc = w[soff:soff + 4 * rows].view(np.float32).reshape(B, T, H)
+            rc, rs = O.quantize_rows(O.gdnq_oracle.rotate(x[name], np.float32))
+            assert_codes(c, rc, f"{name} operand codes")
+            assert_scales(sc, rs, f"{name} operand scales")
+        worst_o = worst_s = 0.0
+        for b, h0, fut in futs:
+            ro, rS = fut.result()
+            err_o = max_rel_err(go[b, :, h0:h0 + HB], ro[0])
+            err_s = max_rel_err(gs[b, h0:h0 + HB], rS[0])
+            assert err_o <= OUT_TOL_BF16, f"(b={b}, heads {h0}..) o error {err_o:.3e}"
+            assert err_s <= OUT_TOL_BF16, f"(b={b}, heads {h0}..) state error {err_s:.3e}"
+            worst_o, worst_s = max(worst_o, err_o), max(worst_s, err_s)
+    print(f"SSD B2 T4096 H80: all 160 heads, worst o {worst_o:.2e}, state {worst_s:.2e}")
