@@ -56,8 +56,21 @@ def decode_bytes_per_head(f, W=W, dk=DK, dv=DV, e_in=2, e_out=2, e_buf=4, state_
 
 def decode_bytes(fills, heads=H, e_buf=4, state_bits=8):
     per_seq_fill = 8  # fill_in read + fill_out write
-    return int(sum(heads * decode_bytes_per_head(int(f), e_buf=e_buf, state_bits=state_bits) + per_seq_fill
-                   for f in fills))
+    table = np.array([decode_bytes_per_head(f, e_buf=e_buf, state_bits=state_bits) for f in range(W)],
+                     np.int64)
+    return int(heads * table[np.asarray(fills, np.int64)].sum() + per_seq_fill * len(fills))
+
+
+def decode_schedule_bytes(fills0, n_steps, heads=H, e_buf=4, state_bits=8):
+    """Algorithmic bytes of each of n_steps consecutive launches of one state
+    whose fills start at fills0 and advance by one per step (0 after a
+    window close); computed before anything is timed."""
+    fills = np.asarray(fills0, np.int64).copy()
+    out = []
+    for _ in range(n_steps):
+        out.append(decode_bytes(fills, heads=heads, e_buf=e_buf, state_bits=state_bits))
+        fills = np.where(fills + 1 == W, 0, fills + 1)
+    return out
 
 
 # the sources of the decode kernel (a traffic summary is stale once they change)
@@ -85,6 +98,63 @@ def load_traffic(name, kernel_sources, per_launch_units):
     return d.get("bytes_per_launch")
 
 
+def host_cpu_info():
+    """The host the CPU oracle runs on: model, cores this process may use,
+    logical CPUs, and the BLAS threads numpy runs with."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
+    except Exception:
+        pass
+    return {"cpu_model": model, "affinity_cores": affinity, "cpu_count": os.cpu_count(),
+            "blas_threads": blas}
+
+
+def _cores_used(info):
+    """Threads the oracle can use: numpy's BLAS threads, within the affinity."""
+    b = info["blas_threads"] or 1
+    return min(b, info["affinity_cores"] or b)
+
+
+def cpu_baseline_prefill(kind, seconds_cap=20.0):
+    """The CPU oracle on one whole sequence of a prefill workload (all heads,
+    every token): GDN B=4 T=8192 H=16 (one of the 4 sequences), SSD B=2
+    T=4096 H=80 with rotated int8 q/k (one of the 2 sequences)."""
+    import oracle
+    import workloads as wl
+
+    if kind == "gdn":
+        x = wl.gdn_prefill(B=1, T=8192, H=16, dk=128, dv=128, seed=0)
+        t0 = time.perf_counter()
+        oracle.prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], W=64)
+        el = time.perf_counter() - t0
+        T, sample = 8192, "1 of 4 sequences (all 16 heads, all 8192 tokens)"
+    else:
+        x = wl.ssd_prefill(B=1, T=4096, H=80, dk=128, dv=64, seed=0)
+        t0 = time.perf_counter()
+        oracle.prefill(x["q"], x["k"], x["v"], x["alpha"], None, W=None, kind="ssd", rot=True,
+                       qk_int8=True)
+        el = time.perf_counter() - t0
+        T, sample = 4096, "1 of 2 sequences (all 80 heads, all 4096 tokens)"
+    info = host_cpu_info()
+    return {"value": round(T / el, 1), "unit": "tokens/s", "cores": _cores_used(info), "kind": "oracle",
+            "sample": f"{sample}, numpy fp32 oracle token by token ({el:.1f} s)", **info}
+
+
 def cpu_baseline_decode(seconds=12.0):
     """The CPU oracle on a bounded sample: the first sequences of the same
     workload, one decode call at a time, until `seconds` have elapsed."""
@@ -107,15 +177,10 @@ def cpu_baseline_decode(seconds=12.0):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    return {"value": nseq * steps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    info = host_cpu_info()
+    return {"value": nseq * steps / el, "unit": "tokens/s", "cores": _cores_used(info), "kind": "oracle",
             "sample": f"{nseq} of {B} sequences x {H} heads, {steps} consecutive decode steps "
-                      f"({el:.1f} s), numpy fp32 oracle"}
+                      f"({el:.1f} s), numpy fp32 oracle", **info}
 
 
 def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None, state_bits=8):
@@ -159,24 +224,24 @@ def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None, state_bits=8):
                torch.from_numpy(x["alpha"]).to(dev), torch.from_numpy(x["beta"]).to(dev)]
         launchers.append((reps[s].bind(*tok, o=o), tok))
 
-    def step(i):
-        r = i % rep_count
-        launchers[r][0]()
-        f = host_fills[r]
-        nbytes = decode_bytes(f, e_buf=e_buf, state_bits=state_bits)
-        host_fills[r] = np.where(f + 1 == W, 0, f + 1)
-        return nbytes
+    # every launch's algorithmic bytes, from the fills each replica will have,
+    # before anything is timed: the timed loop only launches
+    n_all = args.warmup + args.steps
+    per_rep = [decode_schedule_bytes(host_fills[r], (n_all + rep_count - 1 - r) // rep_count,
+                                     e_buf=e_buf, state_bits=state_bits) for r in range(rep_count)]
+    step_bytes = [per_rep[i % rep_count][i // rep_count] for i in range(n_all)]
+    total_bytes = sum(step_bytes[args.warmup:])
+    launch = [lc[0] for lc in launchers]
 
     for i in range(args.warmup):
-        step(i)
+        launch[i % rep_count]()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    total_bytes = 0
     e0.record(stream)
-    for i in range(args.warmup, args.warmup + args.steps):
-        total_bytes += step(i)
+    for i in range(args.warmup, n_all):
+        launch[i % rep_count]()
     e1.record(stream)
     e1.synchronize()
     torch.cuda.synchronize()
@@ -211,19 +276,18 @@ def bench_decode_long(torch, ops, wl, B2=256, steps=1024, warmup=16, n_tok=8):
                torch.from_numpy(x["v"]).to(dev).bfloat16(), torch.from_numpy(x["alpha"]).to(dev),
                torch.from_numpy(x["beta"]).to(dev)]
         launchers.append((st.bind(*tok, o=o), tok))
+    step_bytes = decode_schedule_bytes(fills, warmup + steps)
+    total = sum(step_bytes[warmup:])
+    launch = [lc[0] for lc in launchers]
     for i in range(warmup):
-        launchers[i % n_tok][0]()
-        fills = np.where(fills + 1 == W, 0, fills + 1)
+        launch[i % n_tok]()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    total = 0
     e0.record(stream)
     for i in range(steps):
-        launchers[i % n_tok][0]()
-        total += decode_bytes(fills)
-        fills = np.where(fills + 1 == W, 0, fills + 1)
+        launch[i % n_tok]()
     e1.record(stream)
     e1.synchronize()
     ms = e0.elapsed_time(e1)
@@ -242,21 +306,28 @@ def bench_decode_long(torch, ops, wl, B2=256, steps=1024, warmup=16, n_tok=8):
 
 
 def gdn_prefill_flops(B, T, H, dk=DK, dv=DV, C=64):
-    """Useful FLOPs of the chunked GDN prefill (2 per multiply-add): per
-    chunk-head K K^T (strictly lower), T = (I + A)^-1 (C^3/6), K S0^T, Q S0^T,
-    T rhs (lower), Q K^T (lower with diagonal), M U (lower), state update."""
+    """Useful FLOPs of the chunked GDN prefill, counted as full C x C tiles as
+    MFMA executes them: per token-head 6 dk dv (K S0^T, Q S0^T and the state
+    update U^T K, one multiply-add each) + C (6 dk + 4 dv) (K K^T, T K and
+    Q K^T over dk; T V and (L o Q K^T) U over dv).  180,224 at d = 128,
+    C = 64."""
+    return 2.0 * B * T * H * (3 * dk * dv + C * (3 * dk + 2 * dv))
+
+
+def gdn_prefill_flops_triangular(B, T, H, dk=DK, dv=DV, C=64):
+    """The same products counted over their causal (triangular) parts only,
+    plus the C^3/6 of the inverse: what the algorithm needs at the least."""
     tri, tri0 = C * (C + 1) // 2, C * (C - 1) // 2
     macs = dk * tri0 + C ** 3 / 6 + 3 * C * dk * dv + dv * tri + dk * tri + dv * tri
     return 2.0 * macs * B * (T // C) * H
 
 
 def ssd_prefill_flops(B, T, H, dk=128, dv=64, C=64):
-    """Useful FLOPs of the chunked SSD prefill: Q K^T (lower with diagonal),
-    Q S0^T, M V (lower), state update (the rotation and operand quantization
-    are O(d log d) per row and not counted)."""
-    tri = C * (C + 1) // 2
-    macs = dk * tri + 2 * C * dk * dv + dv * tri
-    return 2.0 * macs * B * (T // C) * H
+    """Useful FLOPs of the chunked SSD prefill as full tiles: per token-head
+    4 dk dv (Q S0^T and the state update) + C (2 dk + 2 dv) (Q K^T and
+    M V).  57,344 at dk = 128, dv = 64, C = 64 (the rotation and operand
+    quantization are O(d log d) per row and not counted)."""
+    return 2.0 * B * T * H * (2 * dk * dv + C * (dk + dv))
 
 
 def gdn_prefill_bytes(B, T, H, dk=DK, dv=DV):
@@ -270,7 +341,12 @@ def ssd_prefill_bytes(B, T, H, dk=128, dv=64):
     return B * T * H * (2 * (2 * dk + dv) + 4 + 2 * dv) + B * H * dv * dk * 4
 
 
-def bench_prefill(torch, ops, wl, steps=5, warmup=2):
+# the sources of each prefill's kernels (GDN, SSD)
+PREFILL_SOURCES = {False: ["prefill_gdn.hip", "device_common.h", "mfma.h"],
+                   True: ["prefill_ssd.hip", "device_common.h", "mfma.h"]}
+
+
+def bench_prefill(torch, ops, wl, steps=5, warmup=2, with_cpu=True):
     """Secondary: GDN chunked prefill B=4, T=8192, H=16, d=128, C=W=64 (bf16
     output, zero initial state); SSD prefill B=2, T=4096, H=80, d_k=128,
     d_v=64 with WHT-rotated int8 q/k (bf16 output); the GDN hand-over to
@@ -399,9 +475,15 @@ def bench_prefill(torch, ops, wl, steps=5, warmup=2):
             "tflops": round(tflops, 2), "gbps": round(gbps, 1),
             "flops_per_call": flops, "bytes_per_call": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)},
-            "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                         "traffic": load_traffic(f"{name}_traffic.json", PREFILL_SOURCES[ssd], 1)},
+            "roofline_mfma": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
         }
+        if not ssd:
+            res[name]["flops_triangular_per_call"] = gdn_prefill_flops_triangular(1, 64 * chunks, Hh, dk, dv)
+        if with_cpu and name in ("gdn_prefill", "ssd_prefill"):
+            res[name]["cpu_baseline"] = cpu_baseline_prefill("ssd" if ssd else "gdn")
         del q, k, v, a, bt, o, call
         torch.cuda.empty_cache()
     return res
@@ -451,7 +533,7 @@ def main():
     if args.copy_probe:
         copy_probe(torch, args.copy_probe)
     if args.skip_decode:
-        print(json.dumps({"prefill": bench_prefill(torch, ops, wl)}), flush=True)
+        print(json.dumps({"prefill": bench_prefill(torch, ops, wl, with_cpu=False)}), flush=True)
         return
 
     r = bench_decode(args, torch, ops, wl, max(1, args.replicas))
@@ -525,7 +607,7 @@ def main():
     if not args.no_long_decode:
         line["decode_b256_1024_steps"] = bench_decode_long(torch, ops, wl)
     if not args.no_prefill:
-        line["prefill"] = bench_prefill(torch, ops, wl)
+        line["prefill"] = bench_prefill(torch, ops, wl, with_cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(args.cpu_seconds)
     print(json.dumps(line), flush=True)
