@@ -234,6 +234,36 @@ gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, co
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * gdnq_prefill_chunked_noalloc -- gdnq_prefill_chunked for callers that
+ *   cannot allocate device memory: code under HIP graph capture, tight
+ *   serving loops, harnesses that forbid hipMalloc.  Same parameters,
+ *   results, layouts and errors as gdnq_prefill_chunked, without the
+ *   workspace arguments: the workspace is a fixed array of
+ *   GDNQ_NOALLOC_SCRATCH_BYTES in device memory that the library holds on
+ *   every GPU it runs on, from load until the process ends.  The call uses
+ *   the array of the current device (the stream must belong to it) and
+ *   allocates nothing, neither device nor host memory.
+ *     - A call whose gdnq_prefill_workspace_size(p) exceeds
+ *       GDNQ_NOALLOC_SCRATCH_BYTES is rejected with GDNQ_ERR_WORKSPACE
+ *       before anything is launched (e.g. GDN: 24,832 bytes per chunk-head,
+ *       so B * (T / 64) * H <= 2702; SSD with GDNQ_FLAG_INT8_QK: 264 bytes
+ *       per token-head).
+ *     - Every call on one GPU shares that GPU's array: calls that overlap
+ *       in time on one GPU (on different streams, or from different host
+ *       threads without ordering) race and give unspecified results.
+ *       Calls ordered on one stream are safe.  Nothing in the array needs
+ *       to start at zero; it keeps the last call's contents.
+ *   Errors: as gdnq_prefill_chunked (WORKSPACE: too large for the array;
+ *   HIP: the array's device address could not be queried).
+ * ------------------------------------------------------------------------ */
+#define GDNQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+gdnq_status gdnq_prefill_chunked_noalloc(const gdnq_prefill_params* p, const void* q, const void* k,
+                                         const void* v, const float* alpha, const float* beta,
+                                         const int8_t* init_codes, const float* init_scales, void* o,
+                                         int8_t* codes, float* scales, float* state_f32, void* stream);
+
+/* ------------------------------------------------------------------------
  * gdnq_prefill_handoff -- GDN prefill of T tokens (any T >= 0) that leaves
  *   its last, open window in decode's window buffer, so that
  *   gdnq_decode_step continues the sequence.  LeapQuant, abstract (outputs

@@ -23,7 +23,7 @@ GDNQ_FLAG_STATE_4BIT = 64
 
 # Every function the header declares.
 EXPORTS = ("gdnq_quantize_state", "gdnq_decode_step", "gdnq_prefill_workspace_size",
-           "gdnq_prefill_chunked", "gdnq_prefill_handoff_workspace_size", "gdnq_prefill_handoff",
+           "gdnq_prefill_chunked", "gdnq_prefill_chunked_noalloc", "gdnq_prefill_handoff_workspace_size", "gdnq_prefill_handoff",
            "gdnq_prefill_varlen_workspace_size", "gdnq_prefill_varlen",
            "gdnq_prefill_resume_workspace_size", "gdnq_prefill_resume",
            "gdnq_decode_set_schedule", "gdnq_status_string", "gdnq_last_error", "gdnq_version")
@@ -69,6 +69,8 @@ def _load():
     lib.gdnq_prefill_workspace_size.restype = sz
     lib.gdnq_prefill_chunked.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 12 + [sz, vp]
     lib.gdnq_prefill_chunked.restype = i32
+    lib.gdnq_prefill_chunked_noalloc.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 12
+    lib.gdnq_prefill_chunked_noalloc.restype = i32
     lib.gdnq_prefill_handoff_workspace_size.argtypes = [ctypes.POINTER(PrefillParams)]
     lib.gdnq_prefill_handoff_workspace_size.restype = sz
     lib.gdnq_prefill_handoff.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 16 + [sz, vp]
@@ -124,6 +126,15 @@ def prefill_chunked(params, q, k, v, alpha, beta, init_codes, init_scales, o, co
     return lib.gdnq_prefill_chunked(ctypes.byref(params), q, k, v, alpha, beta, init_codes,
                                     init_scales, o, codes, scales, state_f32, workspace,
                                     workspace_bytes, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDNQ_NOALLOC_SCRATCH_BYTES
+
+
+def prefill_chunked_noalloc(params, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales,
+                            state_f32, stream):
+    return lib.gdnq_prefill_chunked_noalloc(ctypes.byref(params), q, k, v, alpha, beta, init_codes,
+                                            init_scales, o, codes, scales, state_f32, stream)
 
 
 def prefill_handoff_workspace_size(params):

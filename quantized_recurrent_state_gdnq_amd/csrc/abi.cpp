@@ -215,11 +215,14 @@ size_t gdnq_prefill_workspace_size(const gdnq_prefill_params* p) {
   return gdnq::prefill_workspace_bytes(L);
 }
 
-gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, const void* k,
-                                 const void* v, const float* alpha, const float* beta,
-                                 const int8_t* init_codes, const float* init_scales, void* o,
-                                 int8_t* codes, float* scales, float* state_f32,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+// gdnq_prefill_chunked and its allocation-free variant: with noalloc, the
+// workspace is the current device's scratch array (checked against its size
+// after every other argument, before the one HIP query of its address).
+static gdnq_status prefill_chunked_impl(const gdnq_prefill_params* p, const void* q, const void* k,
+                                        const void* v, const float* alpha, const float* beta,
+                                        const int8_t* init_codes, const float* init_scales, void* o,
+                                        int8_t* codes, float* scales, float* state_f32,
+                                        void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
   gdnq::PrefillLaunch L;
   if (gdnq_status st = prefill_validate(p, L)) return st;
   if (L.B == 0) return ok();
@@ -272,6 +275,21 @@ gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, co
     L.scales = scales;
   }
   const size_t need = gdnq::prefill_workspace_bytes(L);
+  if (noalloc) {
+    if (need > gdnq::scratch_capacity())
+      return fail(GDNQ_ERR_WORKSPACE,
+                  "this call needs %zu bytes of workspace; the allocation-free entry point holds at most %zu "
+                  "(use gdnq_prefill_chunked with a workspace, or split the batch)",
+                  need, gdnq::scratch_capacity());
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      clear_stale_hip_error();
+      if (gdnq_status st = hip_status(gdnq::scratch_for_current_device(&workspace), "device scratch lookup"))
+        return st;
+      workspace_bytes = gdnq::scratch_capacity();
+    }
+  }
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDNQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace_bytes);
   if (workspace && !aligned16(workspace)) return fail(GDNQ_ERR_ALIGN, "workspace is not 16-byte aligned");
@@ -279,6 +297,23 @@ gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_hip_error();
   return hip_status(L.ssd ? gdnq::launch_prefill_ssd(L, s) : gdnq::launch_prefill_gdn(L, s), "prefill launch");
+}
+
+gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const int8_t* init_codes, const float* init_scales, void* o,
+                                 int8_t* codes, float* scales, float* state_f32,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_chunked_impl(p, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales, state_f32,
+                              workspace, workspace_bytes, stream, false);
+}
+
+gdnq_status gdnq_prefill_chunked_noalloc(const gdnq_prefill_params* p, const void* q, const void* k,
+                                         const void* v, const float* alpha, const float* beta,
+                                         const int8_t* init_codes, const float* init_scales, void* o,
+                                         int8_t* codes, float* scales, float* state_f32, void* stream) {
+  return prefill_chunked_impl(p, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales, state_f32,
+                              nullptr, 0, stream, true);
 }
 
 size_t gdnq_prefill_handoff_workspace_size(const gdnq_prefill_params* p) {

@@ -71,6 +71,11 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream);
 hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream);
 size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L);
 size_t prefill_ssd_workspace_bytes(const PrefillLaunch& L);
+// Device scratch of the allocation-free prefill (scratch.hip): its size, and
+// its address on the current device (looked up once per device).
+size_t scratch_capacity();
+hipError_t scratch_for_current_device(void** out);
+
 inline size_t prefill_workspace_bytes(const PrefillLaunch& L) {
   return L.ssd ? prefill_ssd_workspace_bytes(L) : prefill_gdn_workspace_bytes(L);
 }

@@ -176,13 +176,16 @@ def prefill_workspace_size(q, v, *, window=64, chunk=64, wht=False, ssd=False, i
 def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_codes=None,
                     init_scales=None, wht=False, ssd=False, int8_qk=False,
                     out_dtype=torch.bfloat16, o=None, codes=None, scales=None, state_f32=None,
-                    workspace=None, state_bits=8):
+                    workspace=None, state_bits=8, noalloc=False):
     """Chunkwise prefill (see gdnq_prefill_chunked in include/gdnq.h).
 
     q, k [B,T,H,d_k], v [B,T,H,d_v] bf16; alpha (and beta for GDN) [B,T,H] fp32.
     GDN returns (o, codes, scales); SSD (ssd=True) returns (o, state_f32).
     GDN with state_bits=4: the uniform 4-bit state, codes [B,H,d_v,d_k/2]
     packed two per byte (init_codes likewise).
+    noalloc=True calls gdnq_prefill_chunked_noalloc (the library's own device
+    scratch instead of a workspace; pass o and the state outputs to keep the
+    call free of allocations).
     """
     dev = q.device
     B, T, H, d_k = q.shape
@@ -217,6 +220,15 @@ def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_code
         if init_codes is not None:
             _shape(_need(init_codes, "init_codes", torch.int8, dev), cshape, "init_codes")
             _shape(_need(init_scales, "init_scales", torch.float32, dev), (B, H, d_v), "init_scales")
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc: no workspace is taken")
+        _lib.check(_lib.prefill_chunked_noalloc(p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                                None if ssd else _ptr(beta), _ptr(init_codes),
+                                                _ptr(init_scales), _ptr(o), None if ssd else _ptr(codes),
+                                                None if ssd else _ptr(scales),
+                                                _ptr(state_f32) if ssd else None, _stream(dev)))
+        return (o, state_f32) if ssd else (o, codes, scales)
     need = int(_lib.prefill_workspace_size(p))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -361,3 +361,21 @@ def test_resume_contract():
     assert _resume(p, f, fill_in=fo, fill_out=fo) == 6           # same array: past the alias checks
     assert _resume(p, f, codes=None, workspace=ws, ws=need) == 1
     assert _resume(_pp(B=0, T=0), f) == 0                       # no sequences: no-op
+
+
+def test_prefill_noalloc_refuses_more_than_its_array():
+    """gdnq_prefill_chunked_noalloc: a call whose workspace would exceed the
+    library's device scratch array is refused during validation (fake
+    pointers: nothing is looked up or launched); the reason names the limit."""
+    fake = Fake()
+    p = _lib.PrefillParams(4, 8192, 16, 128, 128, 64, 64, 1, 1, 0)
+    assert L.gdnq_prefill_workspace_size(p) > _lib.NOALLOC_SCRATCH_BYTES
+    big = [fake(1 << 30) for _ in range(6)]  # q, k, v, alpha, beta, o: disjoint spans
+    st = _lib.prefill_chunked_noalloc(p, *big[:5], None, None, big[5], fake(), fake(), None, None)
+    assert st == 6
+    assert b"allocation-free" in L.gdnq_last_error()
+    # the same shapes with a workspace argument are accepted up to the pointer checks
+    p_ok = _lib.PrefillParams(1, 128, 2, 128, 128, 64, 64, 1, 1, 0)
+    assert L.gdnq_prefill_workspace_size(p_ok) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert _lib.prefill_chunked_noalloc(p_ok, None, fake(), fake(), fake(), fake(), None, None, fake(),
+                                        fake(), fake(), None, None) == 1  # q is NULL
