@@ -23,4 +23,9 @@ from .gdnq_oracle import (  # noqa: F401
     chunked_fp64,
     ssd_closed_form,
     sweep_mirror,
+    gdn_transition,
+    propagate_key,
+    run_sliding,
+    sliding_ring_slots,
+    decode_step_sliding,
 )

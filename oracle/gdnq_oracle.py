@@ -53,6 +53,13 @@ design notes):
     nearest even, or [PW]'s FP8 vector pairs as OCP E4M3 with one fp32
     scale absmax/448 per vector (IEEE divisions, ties to even); either way
     a token's own write enters its step exactly and is stored rounded.
+  * the Pure-Write sliding window ([PW], run_sliding): the last W writes are
+    kept raw, each contributing beta v k~^T with its key propagated through
+    every later transition; the low-bit historical state takes every
+    token's transition, absorbs each write as it leaves the window, and is
+    requantized at every token (a state that changes every token is stored
+    low-bit only by requantizing it); outputs come from the fp32 state
+    before that requantization.
 
 Pins (tests/test_oracle_*.py): every function below is checked against a
 closed form, an invariant, a special case or a hand-derived worked example
@@ -408,6 +415,157 @@ def prefill(q, k, v, alpha, beta=None, *, W, kind="gdn", rot=False, qk_int8=Fals
         "beta": np.moveaxis(r["buf"]["beta"].reshape(n, B, H), 0, 2),
     }
     return out
+
+
+# --------------------------------------------------------------------------
+# Pure-Write sliding window ([PW])
+# --------------------------------------------------------------------------
+def gdn_transition(X, k, a, b):
+    """Rows X[..., m, dk] through one token's transition, without its write:
+    X <- a (X - b (X k) k^T), i.e. X A with A = a (I - b k k^T).  A is
+    symmetric, so a key x[..., dk] propagates as A x = the same map on the
+    row x^T (pass x[..., None, :])."""
+    Xk = np.matmul(X, k[..., :, None])[..., 0]
+    erase = b[..., None, None] * (Xk[..., :, None] * k[..., None, :])
+    return a[..., None, None] * (X - erase)
+
+
+def propagate_key(x, k, a, b):
+    """A key x[..., dk] through one token's transition: A x = a (x - b (k . x) k)."""
+    kx = np.sum(k * x, axis=-1)
+    return a[..., None] * (x - b[..., None] * kx[..., None] * k)
+
+
+def run_sliding(q, k, v, alpha, beta, *, W, codes0=None, scale0=None, window0=None,
+                dtype=F32, qmax=127):
+    """T tokens of the Pure-Write sliding window for N heads ([PW]: recent
+    pure writes are kept apart, propagated through the full GDN transition,
+    and merged into the low-bit historical state once they leave the window).
+
+    q, k: [T, N, dk]; v: [T, N, dv]; alpha, beta: [T, N].  The state is a
+    low-bit historical part H (codes0 / scale0, None = zero) plus a window
+    of at most W pure writes beta_i v_i k_i^T, each carried with its key
+    propagated through every later transition.  window0 = dict(k, v, alpha,
+    beta) of [n0, N, ...] holds the raw writes already in the window, oldest
+    first (n0 <= W).  W = None: no write ever leaves; W = 0: a write merges
+    at once.
+
+    Per token t, in this order:
+      1. H = dequantize(codes); H <- H A_t (every row takes the transition);
+      2. every window key takes the transition, k~ <- A_t k~;
+      3. the token's write joins the window with its own key (a write does
+         not take its own token's transition);
+      4. while the window holds more than W writes, the oldest leaves:
+         H <- H + beta v k~^T;
+      5. S = H + sum over the window (oldest first) of beta v k~^T;
+         o_t = S q_t (the fp32 state, before the requantization);
+      6. codes, scale = quantize(H): the historical state is requantized at
+         every token.
+    Returns dict(o [T,N,dv], codes, scale, window (raw writes oldest first),
+    n (writes in the window), S (fp32 state at the last token))."""
+    q = np.asarray(q).astype(dtype)
+    k = np.asarray(k).astype(dtype)
+    v = np.asarray(v).astype(dtype)
+    alpha = np.asarray(alpha).astype(dtype)
+    beta = np.asarray(beta).astype(dtype)
+    T, N, dk = k.shape
+    dv = v.shape[-1]
+    if codes0 is None:
+        codes = np.zeros((N, dv, dk), np.int8)
+        scale = np.zeros((N, dv), F32)
+    else:
+        codes = np.array(codes0, dtype=np.int8, copy=True)
+        scale = np.array(scale0, dtype=F32, copy=True)
+
+    # window entries: raw write (k, v, alpha, beta) and the propagated key
+    win = []
+
+    def join(kk, vv, aa, bb):
+        for w in win:
+            w["kt"] = propagate_key(w["kt"], kk, aa, bb)
+        win.append({"k": kk, "v": vv, "alpha": aa, "beta": bb, "kt": kk.copy()})
+
+    if window0 is not None:
+        for i in range(len(window0["k"])):
+            join(np.asarray(window0["k"][i]).astype(dtype), np.asarray(window0["v"][i]).astype(dtype),
+                 np.asarray(window0["alpha"][i]).astype(dtype), np.asarray(window0["beta"][i]).astype(dtype))
+
+    def outer(a_, b_):
+        return a_[..., :, None] * b_[..., None, :]
+
+    o = np.zeros((T, N, dv), dtype)
+    S = dequantize(codes, scale, dtype)
+    for t in range(T):
+        H = dequantize(codes, scale, dtype)
+        H = gdn_transition(H, k[t], alpha[t], beta[t])
+        join(k[t], v[t], alpha[t], beta[t])
+        while W is not None and len(win) > W:
+            w = win.pop(0)
+            H = H + w["beta"][:, None, None] * outer(w["v"], w["kt"])
+        S = H
+        for w in win:
+            S = S + w["beta"][:, None, None] * outer(w["v"], w["kt"])
+        o[t] = np.matmul(S, q[t][..., :, None])[..., 0]
+        codes, scale = quantize_rows(H, qmax)
+
+    def _stack(key, shape):
+        return np.stack([w[key] for w in win]) if win else np.zeros((0,) + shape, dtype)
+
+    window = {"k": _stack("k", (N, dk)), "v": _stack("v", (N, dv)), "alpha": _stack("alpha", (N,)),
+              "beta": _stack("beta", (N,))}
+    return {"o": o, "codes": codes, "scale": scale, "window": window, "n": len(win), "S": S}
+
+
+def sliding_ring_slots(fill, W):
+    """Ring buffer of the sliding window (the layout decode keeps): fill in
+    [0, 2W).  Below W the window holds `fill` writes in slots 0 .. fill-1;
+    from W on it is full and its oldest write sits in slot fill - W.
+    Returns (slots oldest first, the slot the next write takes, fill after
+    one more write)."""
+    fill = int(fill)
+    if fill < W:
+        return list(range(fill)), fill, fill + 1
+    p = fill - W
+    return [(p + i) % W for i in range(W)], p, W + (p + 1) % W
+
+
+def decode_step_sliding(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, buf_beta,
+                        fill, W, dtype=F32, qmax=127):
+    """One decode token per sequence of the Pure-Write sliding window ([PW]).
+
+    Shapes as decode_step; the buffer is a ring of W raw writes per head
+    (sliding_ring_slots gives their order); fill [B] in [0, 2W).  The token's
+    write goes into the slot the ring names (over the write that leaves);
+    the historical codes and scales are rewritten every token.
+    Returns (o, codes_out, scales_out, buf_k, buf_v, buf_alpha, buf_beta,
+    fill_out)."""
+    B, H, dk = np.shape(k)
+    dv = np.shape(v)[-1]
+    o = np.zeros((B, H, dv), dtype)
+    codes_out = np.array(codes, copy=True)
+    scales_out = np.array(scales, copy=True)
+    bufs = [np.array(x, dtype=F32, copy=True) for x in (buf_k, buf_v, buf_alpha, buf_beta)]
+    fill = np.asarray(fill)
+    fill_out = np.zeros_like(fill)
+    for b in range(B):
+        slots, nxt, fo = sliding_ring_slots(fill[b], W)
+        window0 = {"k": np.asarray(buf_k)[b][:, slots].transpose(1, 0, 2),
+                   "v": np.asarray(buf_v)[b][:, slots].transpose(1, 0, 2),
+                   "alpha": np.asarray(buf_alpha)[b][:, slots].T,
+                   "beta": np.asarray(buf_beta)[b][:, slots].T}
+        r = run_sliding(np.asarray(q)[b][None], np.asarray(k)[b][None], np.asarray(v)[b][None],
+                        np.asarray(alpha)[b][None], np.asarray(beta)[b][None], W=W,
+                        codes0=np.asarray(codes)[b], scale0=np.asarray(scales)[b], window0=window0,
+                        dtype=dtype, qmax=qmax)
+        o[b] = r["o"][0]
+        codes_out[b] = r["codes"]
+        scales_out[b] = r["scale"]
+        bufs[0][b, :, nxt] = np.asarray(k)[b]
+        bufs[1][b, :, nxt] = np.asarray(v)[b]
+        bufs[2][b, :, nxt] = np.asarray(alpha)[b]
+        bufs[3][b, :, nxt] = np.asarray(beta)[b]
+        fill_out[b] = fo
+    return (o, codes_out, scales_out, *bufs, fill_out)
 
 
 # --------------------------------------------------------------------------

@@ -276,7 +276,7 @@ def test_decode_multi_window(wht):
     assert_free_scales(host(st.scales), fr[1], f"decode 5 windows wht={wht}")
 
 
-@pytest.mark.parametrize("grid,open_waves", [(768, 1024), (3, 1), (5, 6), (2, 1000), (40, 7)])
+@pytest.mark.parametrize("grid,open_waves", [(0, 0), (768, 1024), (3, 1), (5, 6), (2, 1000), (40, 7)])
 def test_decode_schedules(grid, open_waves):
     """The same mixed open/closing batch under different persistent grids and
     open-wave counts (gdnq_decode_set_schedule): one wave running every open
@@ -290,6 +290,16 @@ def test_decode_schedules(grid, open_waves):
         got, codes, scales = _run_decode(d, 16, torch.bfloat16, torch.float32)
     finally:
         _lib.check(_lib.decode_set_schedule(0, 0))
+    _check_decode(d, 16, got, codes, scales, OUT_TOL_BF16)
+
+
+@pytest.mark.parametrize("H,fill", [(5, [2, 15]), (3, [9, 15, 0]), (1, [4])])
+def test_decode_odd_open_heads(H, fill):
+    """Odd numbers of heads and open heads (H=5 with one closing sequence: 5
+    open heads; H=3: 6; H=1, one sequence: 1).  W = 16, d = 128, bf16
+    inputs."""
+    d = wl.decode_batch(B=len(fill), H=H, dk=128, dv=128, W=16, seed=40 + H, fill=np.array(fill))
+    got, codes, scales = _run_decode(d, 16, torch.bfloat16, torch.float32)
     _check_decode(d, 16, got, codes, scales, OUT_TOL_BF16)
 
 
