@@ -99,6 +99,25 @@ enum {
                              buf_k = B*H*W*d_k code bytes, then B*H*W fp32
                              scales; buf_v likewise with d_v.  Exclusive with
                              GDNQ_FLAG_BUF_BF16.                            */
+  GDNQ_FLAG_SLIDING = 128u, /* decode only: the Pure-Write sliding window
+                             (Low-Bit GDN ..., abstract) instead of the
+                             tumbling one.  The buffer is a ring of the last W
+                             raw writes per head; codes/scales hold the
+                             historical state H.  Per token: H' = deq(H) A_t,
+                             plus beta_l v_l k~_l^T for the write l that leaves
+                             a full window (k~_l: its key through every later
+                             transition, A_j = alpha_j (I - beta_j k_j
+                             k_j^T)); o = (H' + window) q; H = quantize(H')
+                             at every token (codes and scales of every
+                             sequence are rewritten); the token's write takes
+                             the ring slot of the write that left.  fill is
+                             in [0, 2W): below W the window holds `fill`
+                             writes in slots 0..fill-1; from W on it is full
+                             and its oldest write is in slot fill - W.
+                             fill_out = fill + 1 below W, else W + (fill - W
+                             + 1) mod W.  fp32 window buffer and 8-bit state
+                             only (exclusive with GDNQ_FLAG_BUF_BF16,
+                             GDNQ_FLAG_BUF_FP8, GDNQ_FLAG_STATE_4BIT).      */
   GDNQ_FLAG_STATE_4BIT = 64u /* quantize, decode and GDN prefill (all its
                              entry points): the uniform 4-bit state
                              (Low-Bit GDN ..., abstract: the "@4" budget of
@@ -152,7 +171,8 @@ gdnq_status gdnq_quantize_state(const float* S, int64_t rows, int32_t d_k, int8_
  *   most one of GDNQ_FLAG_BUF_BF16, GDNQ_FLAG_BUF_FP8 (the low-precision
  *   window buffers; the Low-Bit GDN page keeps recent writes in FP8), and
  *   GDNQ_FLAG_STATE_4BIT (the state as packed 4-bit codes, requantized
- *   with the 4-bit codec when a window closes).
+ *   with the 4-bit codec when a window closes), or GDNQ_FLAG_SLIDING (the
+ *   Pure-Write sliding window; see the flag: fill_in in [0, 2W) then).
  *     q, k      [B,H,d_k] in_dtype      v [B,H,d_v] in_dtype
  *     alpha, beta [B,H] fp32
  *     codes     [B,H,d_v,d_k] int8      scales [B,H,d_v] fp32   (in/out)

@@ -126,10 +126,15 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
   if ((p->in_dtype != GDNQ_F32 && p->in_dtype != GDNQ_BF16) ||
       (p->out_dtype != GDNQ_F32 && p->out_dtype != GDNQ_BF16))
     return fail(GDNQ_ERR_DTYPE, "in_dtype = %d, out_dtype = %d", p->in_dtype, p->out_dtype);
-  if (p->flags & ~uint32_t(GDNQ_FLAG_WHT | GDNQ_FLAG_BUF_BF16 | GDNQ_FLAG_BUF_FP8 | GDNQ_FLAG_STATE_4BIT))
+  if (p->flags & ~uint32_t(GDNQ_FLAG_WHT | GDNQ_FLAG_BUF_BF16 | GDNQ_FLAG_BUF_FP8 | GDNQ_FLAG_STATE_4BIT |
+                           GDNQ_FLAG_SLIDING))
     return fail(GDNQ_ERR_FLAGS,
-                "flags 0x%x: decode accepts GDNQ_FLAG_WHT, GDNQ_FLAG_BUF_BF16, GDNQ_FLAG_BUF_FP8, GDNQ_FLAG_STATE_4BIT",
+                "flags 0x%x: decode accepts GDNQ_FLAG_WHT, GDNQ_FLAG_BUF_BF16, GDNQ_FLAG_BUF_FP8, "
+                "GDNQ_FLAG_STATE_4BIT, GDNQ_FLAG_SLIDING",
                 p->flags);
+  const bool sliding = (p->flags & GDNQ_FLAG_SLIDING) != 0;
+  if (sliding && (p->flags & (GDNQ_FLAG_BUF_BF16 | GDNQ_FLAG_BUF_FP8 | GDNQ_FLAG_STATE_4BIT)))
+    return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDNQ_FLAG_SLIDING keeps an fp32 window and an 8-bit state", p->flags);
   const bool q4 = (p->flags & GDNQ_FLAG_STATE_4BIT) != 0;
   const bool buf_bf16 = (p->flags & GDNQ_FLAG_BUF_BF16) != 0;
   const bool buf_fp8 = (p->flags & GDNQ_FLAG_BUF_FP8) != 0;
@@ -168,7 +173,8 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
   gdnq::DecodeLaunch L{q,        k,        v,       alpha, beta, codes, scales, buf_k,
                        buf_v,    buf_alpha, buf_beta, fill_in, fill_out, o,   B,      H,
                        dk,       dv,       W,       p->in_dtype == GDNQ_BF16,
-                       p->out_dtype == GDNQ_BF16, (p->flags & GDNQ_FLAG_WHT) != 0, buf_bf16, buf_fp8, q4};
+                       p->out_dtype == GDNQ_BF16, (p->flags & GDNQ_FLAG_WHT) != 0, buf_bf16, buf_fp8, q4,
+                       sliding};
   return hip_status(gdnq::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch");
 }
 

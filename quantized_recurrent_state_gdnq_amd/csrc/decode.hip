@@ -29,6 +29,7 @@ void set_decode_schedule(int grid, int open_waves) {
 int decode_row_split() { return 8; }  // close jobs per head at most (grid validation)
 int decode_max_batch() { return DEC_MAXB; }
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
+  if (L.sliding) return launch_decode_sliding(L, stream);
   DecodeArgs a{L.q,        L.k,        L.v,       L.alpha,   L.beta,   L.codes, L.scales, L.buf_k,
                L.buf_v,    L.buf_alpha, L.buf_beta, L.fill_in, L.fill_out, L.o,   L.B,      L.H,
                L.W,        decode_open_waves(), nullptr,   nullptr};

@@ -37,8 +37,10 @@ struct DecodeLaunch {
   int B, H, d_k, d_v, W;
   bool in_bf16, out_bf16, wht, buf_bf16, buf_fp8;
   bool q4;  // 4-bit state codes, two per byte
+  bool sliding;  // the Pure-Write sliding window (ring buffer, requantize every token)
 };
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
+hipError_t launch_decode_sliding(const DecodeLaunch& L, hipStream_t stream);
 int decode_row_split();
 int decode_max_batch();
 void set_decode_schedule(int grid, int open_waves);  // 0 = default

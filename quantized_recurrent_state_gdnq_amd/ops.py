@@ -88,7 +88,7 @@ def quantize_state(S, codes=None, scales=None, wht=False, state_bits=8):
 
 
 def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, buf_beta,
-                fill_in, fill_out, o=None, *, wht=False, out_dtype=None, _bind_only=False):
+                fill_in, fill_out, o=None, *, wht=False, out_dtype=None, sliding=False, _bind_only=False):
     """One decode token per sequence (see gdnq_decode_step in include/gdnq.h).
 
     q, k [B,H,d_k], v [B,H,d_v] (fp32 or bf16); alpha, beta [B,H] fp32;
@@ -104,6 +104,10 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
 
     4-bit state: codes [B,H,d_v,d_k/2] int8 holding packed 4-bit codes
     (inferred from the shape).
+
+    sliding=True: the Pure-Write sliding window (GDNQ_FLAG_SLIDING): the
+    buffer is a ring of the last W raw writes, fill in [0, 2W), and codes /
+    scales (the historical state) are rewritten at every token.
     """
     dev = q.device
     B, H, d_k = q.shape
@@ -147,7 +151,8 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
     p = _lib.DecodeParams(B, H, d_k, d_v, W, _DT[q.dtype], _DT[o.dtype],
                           (_lib.GDNQ_FLAG_WHT if wht else 0) | (_lib.GDNQ_FLAG_BUF_BF16 if buf_bf16 else 0)
                           | (_lib.GDNQ_FLAG_BUF_FP8 if buf_fp8 else 0)
-                          | (_lib.GDNQ_FLAG_STATE_4BIT if codes.shape[-1] != d_k else 0))
+                          | (_lib.GDNQ_FLAG_STATE_4BIT if codes.shape[-1] != d_k else 0)
+                          | (_lib.GDNQ_FLAG_SLIDING if sliding else 0))
     args = (p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(codes), _ptr(scales),
             _ptr(buf_k), _ptr(buf_v), _ptr(buf_alpha), _ptr(buf_beta), _ptr(fill_in), _ptr(fill_out),
             _ptr(o), _stream(dev))
@@ -434,7 +439,7 @@ class DecodeState:
     since every head of a sequence reads the fill while the step runs)."""
 
     def __init__(self, codes, scales, window, fill=None, wht=False, buf_dtype=torch.float32,
-                 state_bits=8):
+                 state_bits=8, sliding=False):
         """buf_dtype: torch.float32 (the method's fp32 window buffer),
         torch.bfloat16 (writes stored rounded) or torch.float8_e4m3fn (FP8
         vector pairs: E4M3 codes with a per-vector scale, buf_k_scale and
@@ -444,6 +449,7 @@ class DecodeState:
         dev = codes.device
         self.codes, self.scales, self.window, self.wht = codes, scales, window, wht
         self.state_bits = state_bits
+        self.sliding = sliding
         if buf_dtype == torch.float8_e4m3fn:
             self.buf_k, self.buf_k_scale = fp8_window_buffer(B, H, window, d_k, dev)
             self.buf_v, self.buf_v_scale = fp8_window_buffer(B, H, window, d_v, dev)
@@ -462,10 +468,10 @@ class DecodeState:
         and advances the fill ping-pong."""
         _, a0 = decode_step(q, k, v, alpha, beta, self.codes, self.scales, self.buf_k, self.buf_v,
                             self.buf_alpha, self.buf_beta, self.fill, self._fill_next, o,
-                            wht=self.wht, _bind_only=True)
+                            wht=self.wht, sliding=self.sliding, _bind_only=True)
         _, a1 = decode_step(q, k, v, alpha, beta, self.codes, self.scales, self.buf_k, self.buf_v,
                             self.buf_alpha, self.buf_beta, self._fill_next, self.fill, o,
-                            wht=self.wht, _bind_only=True)
+                            wht=self.wht, sliding=self.sliding, _bind_only=True)
         f0 = self.fill
         orient = [(ctypes.byref(a[0]),) + tuple(a[1:]) for a in (a0, a1)]
         fn = _lib.lib.gdnq_decode_step
@@ -480,6 +486,6 @@ class DecodeState:
     def step(self, q, k, v, alpha, beta, o=None, out_dtype=None):
         o = decode_step(q, k, v, alpha, beta, self.codes, self.scales, self.buf_k, self.buf_v,
                         self.buf_alpha, self.buf_beta, self.fill, self._fill_next, o,
-                        wht=self.wht, out_dtype=out_dtype)
+                        wht=self.wht, out_dtype=out_dtype, sliding=self.sliding)
         self.fill, self._fill_next = self._fill_next, self.fill
         return o
