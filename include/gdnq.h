@@ -213,11 +213,12 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
  *   NULL), requantizing at every window end, windows aligned to token 0.
  *   Supported: d_k = d_v = 128, chunk = window = 64, T a multiple of 64.
  *   Writes o and the final codes/scales (the state after the last window).
- *   state_f32 must be NULL.  Flags: 0 or GDNQ_FLAG_STATE_4BIT (init_codes and
+ *   state_f32 must be NULL.  Flags: GDNQ_FLAG_STATE_4BIT (init_codes and
  *   codes then hold packed 4-bit codes, [B,H,d_v,d_k/2] bytes, and every
- *   window end requantizes with the 4-bit codec).  A rotated GDN state is
- *   produced by rotating q and k before the call and the state with
- *   gdnq_quantize_state.
+ *   window end requantizes with the 4-bit codec) and/or GDNQ_FLAG_WHT: every
+ *   q and k row is rotated by H/sqrt(128) in fp32 and rounded to bf16
+ *   (nearest even), the operand precision of the chunk products; the state
+ *   (init_codes in, codes out) lives in the rotated basis S H.
  *
  *   SSD (GDNQ_FLAG_SSD): S_t = a_t S_{t-1} + v_t k_t^T from a zero state, no
  *   requantization (window ignored); beta, init_codes, init_scales, codes and

@@ -156,12 +156,16 @@ def ssd_step(S, k, v, a):
 # --------------------------------------------------------------------------
 # The windowed algorithm ([LQ] per-window quantization; [PW] merge on exit)
 # --------------------------------------------------------------------------
-def _prepare_qk(q, k, rot, qk_int8, dtype):
+def _prepare_qk(q, k, rot, qk_int8, dtype, qk_bf16=False):
     q = np.asarray(q).astype(dtype)
     k = np.asarray(k).astype(dtype)
     if rot:
         q = rotate(q, dtype)
         k = rotate(k, dtype)
+    if qk_bf16:
+        # the rotated operands rounded to bf16, the prefill's operand precision
+        q = round_bf16(q.astype(F32)).astype(dtype)
+        k = round_bf16(k.astype(F32)).astype(dtype)
     if qk_int8:
         # per-token-row int8 operand quantization of the (rotated) q and k
         cq, sq = quantize_rows(q)
@@ -172,7 +176,8 @@ def _prepare_qk(q, k, rot, qk_int8, dtype):
 
 
 def run_windowed(q, k, v, alpha, beta=None, *, W, codes0=None, scale0=None,
-                 buffer0=None, kind="gdn", rot=False, qk_int8=False, dtype=F32, qmax=127):
+                 buffer0=None, kind="gdn", rot=False, qk_int8=False, dtype=F32, qmax=127,
+                 qk_bf16=False):
     """Run T tokens of the windowed recurrence for N independent heads.
 
     q, k: [T, N, dk]; v: [T, N, dv]; alpha, beta: [T, N].
@@ -182,8 +187,11 @@ def run_windowed(q, k, v, alpha, beta=None, *, W, codes0=None, scale0=None,
     window (stored in the basis the state lives in).  W: window length, or
     None for no quantization at all (the fp reference recurrence).
 
+    qk_bf16: the rotated q, k are rounded to bf16 (the GDN prefill's
+    operand precision under the rotation).
+
     Steps (each one a plain reading of [LQ]/[PW]):
-      1. optional rotation and int8 operand quantization of q, k;
+      1. optional rotation (then bf16 rounding or int8 operand quantization) of q, k;
       2. S = dequantize(stored codes);
       3. replay the buffered writes on top of S, oldest first;
       4. per token: S = step(S, token); o_t = S q_t; the window counter
@@ -192,7 +200,7 @@ def run_windowed(q, k, v, alpha, beta=None, *, W, codes0=None, scale0=None,
          write joins the buffer.
     Returns dict(o [T,N,dv], codes, scale, buf dict, n, S).
     """
-    q, k = _prepare_qk(q, k, rot, qk_int8, dtype)
+    q, k = _prepare_qk(q, k, rot, qk_int8, dtype, qk_bf16)
     v = np.asarray(v).astype(dtype)
     alpha = np.asarray(alpha).astype(dtype)
     beta = None if beta is None else np.asarray(beta).astype(dtype)
@@ -383,7 +391,7 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha,
 
 
 def prefill(q, k, v, alpha, beta=None, *, W, kind="gdn", rot=False, qk_int8=False,
-            codes0=None, scale0=None, dtype=F32, qmax=127):
+            codes0=None, scale0=None, dtype=F32, qmax=127, qk_bf16=False):
     """Prefill of a batch from a stored (or zero) state, token by token.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; alpha, beta: [B,T,H].
@@ -399,7 +407,7 @@ def prefill(q, k, v, alpha, beta=None, *, W, kind="gdn", rot=False, qk_int8=Fals
         return x.reshape((T, B * H) + x.shape[3:])
 
     r = run_windowed(tn(q), tn(k), tn(v), tn(alpha), None if beta is None else tn(beta),
-                     W=W, kind=kind, rot=rot, qk_int8=qk_int8,
+                     W=W, kind=kind, rot=rot, qk_int8=qk_int8, qk_bf16=qk_bf16,
                      codes0=None if codes0 is None else np.asarray(codes0).reshape(B * H, dv, dk),
                      scale0=None if scale0 is None else np.asarray(scale0).reshape(B * H, dv),
                      dtype=dtype, qmax=qmax)

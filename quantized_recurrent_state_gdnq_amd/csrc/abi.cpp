@@ -198,8 +198,10 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
       return fail(GDNQ_ERR_FLAGS, "SSD: GDNQ_FLAG_WHT requires GDNQ_FLAG_INT8_QK");
     if (dk != 128 || (dv != 64 && dv != 128)) return fail(GDNQ_ERR_SHAPE, "SSD: d_k = %d (128), d_v = %d (64 or 128)", dk, dv);
   } else {
-    if (p->flags & ~uint32_t(GDNQ_FLAG_STATE_4BIT))
-      return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill takes only GDNQ_FLAG_STATE_4BIT", p->flags);
+    if (p->flags & ~uint32_t(GDNQ_FLAG_STATE_4BIT | GDNQ_FLAG_WHT))
+      return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill takes GDNQ_FLAG_STATE_4BIT and GDNQ_FLAG_WHT", p->flags);
+    if ((p->flags & GDNQ_FLAG_WHT) && handoff)
+      return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_WHT: gdnq_prefill_chunked only (not the hand-over, varlen or resume calls)");
     if (dk != 128 || dv != 128) return fail(GDNQ_ERR_SHAPE, "GDN prefill: d_k = d_v = 128 required (got %d, %d)", dk, dv);
     if (p->window != p->chunk) return fail(GDNQ_ERR_SHAPE, "GDN prefill: window = %d must equal chunk = %d", p->window, p->chunk);
   }

@@ -825,6 +825,61 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
 // + B, and with a buffered prefix of at most 63 writes per sequence,
 // sum ceil((pre + n) / 64) <= floor(N / 64) + 2 B.
 static size_t gdn_new_tokens(const PrefillLaunch& L) { return L.varlen ? size_t(L.T) : size_t(L.B) * L.T; }
+// Rotation of q and k (GDNQ_FLAG_WHT): every token row x -> H x / sqrt(128)
+// (Sylvester order) in fp32, rounded to bf16 (nearest even): the operand
+// precision of the chunk products.  Four lanes per row: five butterfly
+// stages inside a lane, the last two across the lane quad through DPP.
+// Rows past the end are not written.
+struct RotateArgs {
+  const uint16_t* x[2];  // q, k [rows][128] bf16
+  uint16_t* y[2];        // rotated rows [rows][128] bf16
+  int64_t rows;
+};
+
+__global__ __launch_bounds__(256) void gdn_rotate_kernel(RotateArgs a) {
+  constexpr int LPR = 4, E = PD / LPR;
+  const int op = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int li = tid % LPR;
+  const int64_t row = int64_t(blockIdx.x) * (256 / LPR) + tid / LPR;
+  const bool valid = row < a.rows;
+  float v[E];
+  const uint4* src = reinterpret_cast<const uint4*>(a.x[op] + row * PD + li * E);
+#pragma unroll
+  for (int p = 0; p < E / 8; ++p) {
+    const uint4 w = valid ? src[p] : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[8 * p + 2 * i] = bf16_lo(ww[i]);
+      v[8 * p + 2 * i + 1] = bf16_hi(ww[i]);
+    }
+  }
+  fwht_local<E>(v);
+  const bool up1 = (li & 1) != 0, up2 = (li & 2) != 0;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const float o = dpp<DPP_XOR1>(v[i]);
+    v[i] = up1 ? (o - v[i]) : (v[i] + o);
+  }
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const float o = dpp<DPP_XOR2>(v[i]);
+    v[i] = up2 ? (o - v[i]) : (v[i] + o);
+  }
+  if (!valid) return;
+  uint4* dst = reinterpret_cast<uint4*>(a.y[op] + row * PD + li * E);
+#pragma unroll
+  for (int p = 0; p < E / 8; ++p) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = f32_to_bf16_bits(v[8 * p + 2 * i] * 0.08838834764831845f) |
+             (f32_to_bf16_bits(v[8 * p + 2 * i + 1] * 0.08838834764831845f) << 16);
+    dst[p] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 static size_t gdn_chunks(const PrefillLaunch& L) {
   if (L.resume) return gdn_new_tokens(L) / PC + 2 * size_t(L.B);
   return L.varlen ? size_t(L.T / PC) + size_t(L.B) : size_t(L.B) * ((L.T + PC - 1) / PC);
@@ -837,6 +892,8 @@ static size_t gdn_ws_stage(const PrefillLaunch& L) {
 }
 static bool gdn_mapped(const PrefillLaunch& L) { return L.varlen || L.resume; }
 static size_t gdn_ws_map(const PrefillLaunch& L) { return gdn_mapped(L) ? (4 * size_t(L.B) + 2) * 4 : 0; }
+// rotated q and k (GDNQ_FLAG_WHT, whole windows only): [2][B*T*H][128] bf16
+static size_t gdn_ws_rot(const PrefillLaunch& L) { return L.wht ? 2 * size_t(L.B) * L.T * L.H * PD * 2 : 0; }
 constexpr int ORDER_MAXB = 1024;  // sequences ranked by length (more: taken in order)
 
 // Sequence map, one workgroup.  Token offsets tok[i]: with cu, the running
@@ -1030,11 +1087,22 @@ __global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
 }
 
 size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L) {
-  return gdn_ws_T(L) + gdn_ws_g(L) + gdn_ws_stage(L) + gdn_ws_map(L);
+  return gdn_ws_T(L) + gdn_ws_g(L) + gdn_ws_stage(L) + gdn_ws_map(L) + gdn_ws_rot(L);
 }
 
-hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
+hipError_t launch_prefill_gdn(const PrefillLaunch& Lin, hipStream_t stream) {
+  PrefillLaunch L = Lin;
   char* ws = static_cast<char*>(L.workspace);
+  if (L.wht && L.B > 0 && L.T > 0) {  // rotate q and k once; the chunk kernels read the rotated rows
+    uint16_t* rq = reinterpret_cast<uint16_t*>(ws + gdn_ws_T(L) + gdn_ws_g(L) + gdn_ws_stage(L) + gdn_ws_map(L));
+    const int64_t rows = int64_t(L.B) * L.T * L.H;
+    uint16_t* rk = rq + rows * PD;
+    RotateArgs ra{{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k)}, {rq, rk}, rows};
+    hipLaunchKernelGGL(gdn_rotate_kernel, dim3(unsigned((rows + 63) / 64), 2), dim3(256), 0, stream, ra);
+    if (hipError_t e = hipGetLastError()) return e;
+    L.q = rq;
+    L.k = rk;
+  }
   __bf16* T_ws = reinterpret_cast<__bf16*>(ws);
   float* g_ws = reinterpret_cast<float*>(ws + gdn_ws_T(L));
   SeqMap sm{};

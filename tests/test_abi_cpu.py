@@ -166,11 +166,22 @@ def _prefill(params, fake, **over):
     (_pp(C=32, W=32), 2), (_pp(T=100), 2), (_pp(dk=64, dv=64), 2), (_pp(W=128), 2),
     (_pp(ind=0), 3), (_pp(outd=3), 3), (_pp(flags=4), 8), (_pp(flags=8), 8), (_pp(flags=16), 8),
     (_pp(flags=32), 8),
-    (_pp(flags=1), 8),                   # GDN prefill takes no rotation flag
     (_pp(dv=64, flags=2 | 1), 8),        # SSD rotation only on the way to int8 operands
 ])
 def test_prefill_rejects_bad_params(params, status):
     assert _prefill(params, Fake()) == status
+
+
+def test_prefill_gdn_rotation_flag():
+    """GDNQ_FLAG_WHT is accepted by the chunked GDN prefill (it needs a larger
+    workspace: the rotated q and k) and refused by the hand-over, varlen and
+    resume calls."""
+    p0, p1 = _pp(), _pp(flags=1)
+    assert L.gdnq_prefill_workspace_size(p1) == L.gdnq_prefill_workspace_size(p0) + 2 * 1 * 128 * 2 * 128 * 2
+    f = Fake()
+    assert _prefill(p1, f, ws=L.gdnq_prefill_workspace_size(p0), workspace=f()) == 6  # too small
+    assert L.gdnq_prefill_handoff_workspace_size(p1) == 0
+    assert L.gdnq_prefill_varlen_workspace_size(p1) == 0
 
 
 def test_prefill_gdn_contract():

@@ -116,6 +116,88 @@ def test_prefill_free_running(init):
     assert_free_scales(host(sg), ref["scale"], f"prefill 5 windows init={init}")
 
 
+@pytest.mark.parametrize("state_bits", [8, 4])
+def test_prefill_rotated_teacher_forced_chunks(state_bits):
+    """GDNQ_FLAG_WHT on the chunked prefill (reading R23: q and k rotated by
+    H/sqrt(128) in fp32 and rounded to bf16): B=2, H=3, four chunks, one per
+    call, each from the GPU's previous state, the first from a random state
+    quantized in the rotated basis.  Teacher-forced stage by stage:
+      * the rotated operands the kernels used (read back from the workspace)
+        against the oracle's rotation and rounding: bitwise, except +-1 bf16
+        step on <= 0.1% of the elements (the fp32 sums run in different
+        orders, so a value on a bf16 rounding tie may round either way);
+      * the recurrence on those same operands: outputs (fp32) within 1e-3,
+        codes +-1 on <= 0.1%, scales within 1e-5."""
+    B, H, d, T = 2, 3, 128, 256
+    qmax = 127 if state_bits == 8 else 7
+    x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=41)
+    S = (np.random.default_rng(42).standard_normal((B, H, d, d)) * 0.5).astype(np.float32)
+    codes, scales = O.quantize_rows(O.gdnq_oracle.rotate(S, np.float32), qmax=qmax)
+
+    def pack(c):
+        if state_bits == 8:
+            return c
+        u = (c[..., 0::2].astype(np.int16) & 0xF) | ((c[..., 1::2].astype(np.int16) & 0xF) << 4)
+        return u.astype(np.uint8).view(np.int8)
+
+    def unpack(c):
+        if state_bits == 8:
+            return c
+        u = c.view(np.uint8).astype(np.int16)
+        lo, hi = u & 0xF, u >> 4
+        return np.stack([np.where(lo > 7, lo - 16, lo), np.where(hi > 7, hi - 16, hi)], -1).reshape(
+            c.shape[:-1] + (2 * c.shape[-1],)).astype(np.int8)
+
+    rows = B * W * H
+    for c in range(T // W):
+        xs = {k: np.ascontiguousarray(v[:, c * W:(c + 1) * W]) for k, v in x.items()}
+        q_, k_, v_, a_, b_ = _inputs(xs)
+        need = ops.prefill_workspace_size(q_, v_, wht=True)
+        ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        o, cg, sg = ops.prefill_chunked(q_, k_, v_, a_, b_, init_codes=dev(pack(codes)), init_scales=dev(scales),
+                                        wht=True, out_dtype=torch.float32, state_bits=state_bits, workspace=ws)
+        torch.cuda.synchronize()
+        # the rotated q and k are the last 2 * rows * 128 bf16 of the workspace
+        rot = host(ws[need - 2 * rows * d * 2:]).view(np.uint16).reshape(2, B, W, H, d)
+        qr, kr = (wl.bf16_to_f32(rot[i]) for i in range(2))
+        for name, got, src in (("q", qr, xs["q"]), ("k", kr, xs["k"])):
+            r32 = O.gdnq_oracle.rotate(src, np.float32)
+            ref = O.round_bf16(r32)
+            diff = got != ref
+            assert np.mean(diff) <= 1e-3, f"chunk {c}: {name} rotated operands differ on {np.mean(diff):.3%}"
+            # every element is a bf16 rounding (half a bf16 step) of a value within
+            # fp32 summation error (2^-20 of the row's norm) of the oracle's rotation
+            half = np.spacing(np.abs(r32)).astype(np.float64) * 2.0 ** 15
+            tol = half + 2.0 ** -20 * np.linalg.norm(src, axis=-1, keepdims=True)
+            assert np.all(np.abs(got.astype(np.float64) - r32) <= tol), f"chunk {c}: rotated {name} off"
+        ref = O.prefill(qr, kr, xs["v"], xs["alpha"], xs["beta"], W=W, codes0=codes, scale0=scales, qmax=qmax)
+        err = max_rel_err(host(o), ref["o"])
+        assert err <= OUT_TOL_F32, f"chunk {c}: o max relative error {err:.3e}"
+        assert_codes(unpack(host(cg)), ref["codes"], f"chunk {c} codes")
+        assert_scales(host(sg), ref["scale"], f"chunk {c} scales")
+        codes, scales = unpack(host(cg)), host(sg)
+
+
+def test_prefill_rotated_free_running_and_rotation_invariance():
+    """B=2, H=2, T=320 in one call with the rotation, from a zero state,
+    against the oracle's rotation and recurrence run on its own (outputs
+    2e-2, codes +-1 on <= 0.1%, scales within the free-running drift bound:
+    rotated operands on a bf16 tie may round apart, see above); and the
+    outputs agree with the unrotated call within 2e-2 (the rotation keeps
+    S q, up to the bf16 rounding of the rotated operands and the different
+    requantization basis)."""
+    B, H, d, T = 2, 2, 128, 320
+    x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=43)
+    o, cg, sg = ops.prefill_chunked(*_inputs(x), wht=True, out_dtype=torch.float32)
+    o0, _, _ = ops.prefill_chunked(*_inputs(x), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = O.prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], W=W, rot=True, qk_bf16=True)
+    assert max_rel_err(host(o), ref["o"]) <= OUT_TOL_BF16
+    assert_codes(host(cg), ref["codes"], "final codes")
+    assert_free_scales(host(sg), ref["scale"], "rotated prefill 5 windows")
+    assert max_rel_err(host(o), host(o0)) <= OUT_TOL_BF16
+
+
 def test_prefill_matches_fp64_chunk_form():
     """Single head from zero state, T=192: the fp64 chunk (UT) form of the
     oracle, requantizing per window, gives the same outputs."""

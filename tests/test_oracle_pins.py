@@ -394,6 +394,24 @@ def test_p7_rotation_invariance():
     assert np.max(np.abs(s0["o"] - s1["o"])) < 1e-12
 
 
+def test_rotated_operands_rounded_to_bf16_golden():
+    """The GDN prefill's rotated operands (reading R23: rotate in fp32, round
+    to bf16), by hand: H e0 / sqrt(128) has every entry 2^-3.5 =
+    0.0883883..., whose nearest bf16 is 181/2048 = 0.08837890625 (8
+    significant bits: 1.41421 x 128 = 181.02 -> 181); H (e0 + e1) / sqrt(128)
+    has 2^-2.5 = 0.1767767 on even indices, nearest bf16 181/1024, and 0 on
+    odd ones.  Catches rounding before the rotation and a missing 1/sqrt(d)."""
+    d = 128
+    x = np.zeros((2, d), F32)
+    x[0, 0] = 1.0
+    x[1, 0] = x[1, 1] = 1.0
+    q, k = O.gdnq_oracle._prepare_qk(x, x, True, False, F32, qk_bf16=True)
+    assert np.all(k[0] == F32(181 / 2048)) and np.all(q[0] == F32(181 / 2048))
+    assert np.all(k[1, 0::2] == F32(181 / 1024)) and np.all(k[1, 1::2] == 0)
+    q0, _ = O.gdnq_oracle._prepare_qk(x, x, True, False, F32)
+    assert np.all(np.abs(q0[0] - F32(2 ** -3.5)) <= 2e-8)
+
+
 def test_qk_int8_operands_within_half_scale():
     """Int8 operand quantization of rotated q, k: every operand entry moves by
     at most half its row scale, and the run equals one on pre-quantized inputs."""
