@@ -202,7 +202,12 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
       return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill takes GDNQ_FLAG_STATE_4BIT and GDNQ_FLAG_WHT", p->flags);
     if ((p->flags & GDNQ_FLAG_WHT) && handoff)
       return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_WHT: gdnq_prefill_chunked only (not the hand-over, varlen or resume calls)");
-    if (dk != 128 || dv != 128) return fail(GDNQ_ERR_SHAPE, "GDN prefill: d_k = d_v = 128 required (got %d, %d)", dk, dv);
+    if (!((dk == 128 && dv == 128) || (dk == 64 && dv == 64)))
+      return fail(GDNQ_ERR_SHAPE, "GDN prefill: d_k = d_v = 128 or 64 required (got %d, %d)", dk, dv);
+    if (dk == 64 && handoff)
+      return fail(GDNQ_ERR_SHAPE, "GDN prefill at d = 64: gdnq_prefill_chunked only (not the hand-over, varlen or resume calls)");
+    if (dk == 64 && (p->flags & GDNQ_FLAG_WHT))
+      return fail(GDNQ_ERR_FLAGS, "GDN prefill at d = 64 takes no GDNQ_FLAG_WHT");
     if (p->window != p->chunk) return fail(GDNQ_ERR_SHAPE, "GDN prefill: window = %d must equal chunk = %d", p->window, p->chunk);
   }
   if (int64_t(B) * H * 8 > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "batch * heads too large");

@@ -825,6 +825,78 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
 // + B, and with a buffered prefix of at most 63 writes per sequence,
 // sum ceil((pre + n) / 64) <= floor(N / 64) + 2 B.
 static size_t gdn_new_tokens(const PrefillLaunch& L) { return L.varlen ? size_t(L.T) : size_t(L.B) * L.T; }
+// d_k = d_v = 64: the head runs as a d = 128 head whose extra key
+// dimensions and value rows are zero.  Keys padded with zeros get and erase
+// nothing in the extra columns, zero value rows write nothing, and every
+// product and row absmax only gains +0 terms, so the padded head carries the
+// d = 64 state exactly in its first 64 rows and columns.  gdn_pad_kernel
+// widens q, k, v (and the stored state) into the workspace; gdn_unpad_kernel
+// copies the outputs and the final state back.
+struct PadArgs {
+  const uint16_t* x[3];  // q, k, v [rows][64] bf16
+  uint16_t* y[3];        // [rows][128] bf16
+  int64_t rows;
+  const int8_t* c0;      // stored state [bh][64][RB64] (NULL: zero state)
+  const float* s0;       // [bh][64]
+  int8_t* pc0;           // [bh][128][RB128]
+  float* ps0;            // [bh][128]
+  int64_t bh;
+  int rb64;              // bytes per stored row: 64 (8-bit) or 32 (4-bit)
+};
+
+__global__ __launch_bounds__(256) void gdn_pad_kernel(PadArgs a) {
+  const int64_t n = a.rows * 3 * 16;  // 16-byte granules of the padded rows
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n; e += int64_t(gridDim.x) * 256) {
+    const int64_t row = e / 48;
+    const int op = int(e % 48) / 16, g = int(e % 16);
+    const uint4 w = g < 8 ? reinterpret_cast<const uint4*>(a.x[op] + row * 64)[g] : make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4*>(a.y[op] + row * PD)[g] = w;
+  }
+  if (!a.pc0) return;
+  const int rb128 = 2 * a.rb64;
+  const int64_t ns = a.bh * PD * (rb128 / 16);
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < ns; e += int64_t(gridDim.x) * 256) {
+    const int64_t r = e / (rb128 / 16);  // padded state row (bh * 128 + row)
+    const int g = int(e % (rb128 / 16));
+    const int64_t bh = r / PD, rr = r % PD;
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (rr < 64 && g < a.rb64 / 16) w = reinterpret_cast<const uint4*>(a.c0 + (bh * 64 + rr) * a.rb64)[g];
+    reinterpret_cast<uint4*>(a.pc0 + r * rb128)[g] = w;
+    if (g == 0) a.ps0[r] = rr < 64 ? a.s0[bh * 64 + rr] : 0.f;
+  }
+}
+
+struct UnpadArgs {
+  const char* po;  // [rows][128] outputs (eo bytes each)
+  char* o;         // [rows][64]
+  int64_t rows;
+  int eo;
+  const int8_t* pc;  // [bh][128][RB128]
+  const float* ps;
+  int8_t* c;         // [bh][64][RB64]
+  float* sc;
+  int64_t bh;
+  int rb64;
+};
+
+__global__ __launch_bounds__(256) void gdn_unpad_kernel(UnpadArgs a) {
+  const int gpr = 64 * a.eo / 16;  // 16-byte granules per output row
+  const int64_t n = a.rows * gpr;
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n; e += int64_t(gridDim.x) * 256) {
+    const int64_t row = e / gpr;
+    const int g = int(e % gpr);
+    reinterpret_cast<uint4*>(a.o + row * 64 * a.eo)[g] = reinterpret_cast<const uint4*>(a.po + row * PD * a.eo)[g];
+  }
+  const int64_t ns = a.bh * 64 * (a.rb64 / 16);
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < ns; e += int64_t(gridDim.x) * 256) {
+    const int64_t r = e / (a.rb64 / 16);  // bh * 64 + row
+    const int g = int(e % (a.rb64 / 16));
+    const int64_t bh = r / 64, rr = r % 64;
+    reinterpret_cast<uint4*>(a.c + r * a.rb64)[g] = reinterpret_cast<const uint4*>(a.pc + (bh * PD + rr) * 2 * a.rb64)[g];
+    if (g == 0) a.sc[r] = a.ps[bh * PD + rr];
+  }
+}
+
 // Rotation of q and k (GDNQ_FLAG_WHT): every token row x -> H x / sqrt(128)
 // (Sylvester order) in fp32, rounded to bf16 (nearest even): the operand
 // precision of the chunk products.  Four lanes per row: five butterfly
@@ -1086,11 +1158,74 @@ __global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
   if (h == 0 && threadIdx.x == 0) a.fill_out[b] = r;
 }
 
-size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L) {
+static size_t gdn_ws_128(const PrefillLaunch& L) {
   return gdn_ws_T(L) + gdn_ws_g(L) + gdn_ws_stage(L) + gdn_ws_map(L) + gdn_ws_rot(L);
 }
+// d = 64 through a padded d = 128 head: q, k, v [3][rows][128] bf16, the
+// padded stored state and final state ([bh][128][RB128] + [bh][128] each),
+// the padded outputs [rows][128]; then the d = 128 workspace
+struct PadLayout {
+  size_t qkv, c0, s0, o, c, sc, inner, total;
+};
+static PadLayout gdn_pad_layout(const PrefillLaunch& L) {
+  const size_t rows = size_t(L.B) * L.T * L.H, bh = size_t(L.B) * L.H;
+  const size_t rb = L.q4 ? PD / 2 : PD, eo = L.out_bf16 ? 2 : 4;
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  PadLayout p{};
+  p.qkv = 0;
+  p.c0 = p.qkv + up(3 * rows * PD * 2);
+  p.s0 = p.c0 + up(bh * PD * rb);
+  p.o = p.s0 + up(bh * PD * 4);
+  p.c = p.o + up(rows * PD * eo);
+  p.sc = p.c + up(bh * PD * rb);
+  p.inner = p.sc + up(bh * PD * 4);
+  PrefillLaunch L2 = L;
+  L2.d_k = L2.d_v = PD;
+  p.total = p.inner + gdn_ws_128(L2);
+  return p;
+}
 
-hipError_t launch_prefill_gdn(const PrefillLaunch& Lin, hipStream_t stream) {
+size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L) {
+  if (L.d_k == 64) return gdn_pad_layout(L).total;
+  return gdn_ws_128(L);
+}
+
+static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t stream);
+
+hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
+  if (L.d_k != 64) return launch_prefill_gdn128(L, stream);
+  // d = 64: pad, run the d = 128 kernels on the workspace copies, unpad
+  const PadLayout P = gdn_pad_layout(L);
+  char* ws = static_cast<char*>(L.workspace);
+  const int64_t rows = int64_t(L.B) * L.T * L.H, bh = int64_t(L.B) * L.H;
+  const int rb64 = L.q4 ? 32 : 64;
+  uint16_t* pq = reinterpret_cast<uint16_t*>(ws + P.qkv);
+  PadArgs pa{{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v)},
+             {pq, pq + rows * PD, pq + 2 * rows * PD}, rows, L.init_codes, L.init_scales,
+             L.init_codes ? reinterpret_cast<int8_t*>(ws + P.c0) : nullptr, reinterpret_cast<float*>(ws + P.s0), bh, rb64};
+  const int64_t work = rows * 48 > bh * PD * 8 ? rows * 48 : bh * PD * 8;
+  const unsigned grid = unsigned(work / 256 + 1 < 4096 ? work / 256 + 1 : 4096);
+  hipLaunchKernelGGL(gdn_pad_kernel, dim3(grid), dim3(256), 0, stream, pa);
+  if (hipError_t e = hipGetLastError()) return e;
+  PrefillLaunch L2 = L;
+  L2.d_k = L2.d_v = PD;
+  L2.q = pa.y[0];
+  L2.k = pa.y[1];
+  L2.v = pa.y[2];
+  L2.init_codes = pa.pc0;
+  L2.init_scales = L.init_codes ? pa.ps0 : nullptr;
+  L2.o = ws + P.o;
+  L2.codes = reinterpret_cast<int8_t*>(ws + P.c);
+  L2.scales = reinterpret_cast<float*>(ws + P.sc);
+  L2.workspace = ws + P.inner;
+  if (hipError_t e = launch_prefill_gdn128(L2, stream)) return e;
+  UnpadArgs ua{ws + P.o, static_cast<char*>(L.o), rows, L.out_bf16 ? 2 : 4, L2.codes, L2.scales, L.codes, L.scales,
+               bh, rb64};
+  hipLaunchKernelGGL(gdn_unpad_kernel, dim3(grid), dim3(256), 0, stream, ua);
+  return hipGetLastError();
+}
+
+static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t stream) {
   PrefillLaunch L = Lin;
   char* ws = static_cast<char*>(L.workspace);
   if (L.wht && L.B > 0 && L.T > 0) {  // rotate q and k once; the chunk kernels read the rotated rows

@@ -163,7 +163,8 @@ def _prefill(params, fake, **over):
 
 
 @pytest.mark.parametrize("params,status", [
-    (_pp(C=32, W=32), 2), (_pp(T=100), 2), (_pp(dk=64, dv=64), 2), (_pp(W=128), 2),
+    (_pp(C=32, W=32), 2), (_pp(T=100), 2), (_pp(dk=64, dv=128), 2), (_pp(W=128), 2),
+    (_pp(dk=64, dv=64, flags=1), 8),       # no rotation at d = 64
     (_pp(ind=0), 3), (_pp(outd=3), 3), (_pp(flags=4), 8), (_pp(flags=8), 8), (_pp(flags=16), 8),
     (_pp(flags=32), 8),
     (_pp(dv=64, flags=2 | 1), 8),        # SSD rotation only on the way to int8 operands

@@ -198,6 +198,68 @@ def test_prefill_rotated_free_running_and_rotation_invariance():
     assert max_rel_err(host(o), host(o0)) <= OUT_TOL_BF16
 
 
+@pytest.mark.parametrize("state_bits", [8, 4])
+def test_prefill_d64_teacher_forced_chunks(state_bits):
+    """d_k = d_v = 64 (the library runs it as a zero-padded d = 128 head):
+    B=2, H=3, four chunks, one per call, each from the GPU's previous state,
+    the first from a random stored state.  Outputs (fp32) within 1e-3,
+    codes +-1 on <= 0.1%, scales 1e-5; guard zones around every output."""
+    B, H, d, T = 2, 3, 64, 256
+    qmax = 127 if state_bits == 8 else 7
+    x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=45)
+    S = (np.random.default_rng(46).standard_normal((B, H, d, d)) * 0.5).astype(np.float32)
+    S[1, 2, 7] = 0.0  # a zero row
+    codes, scales = O.quantize_rows(S, qmax=qmax)
+
+    def pack(c):
+        if state_bits == 8:
+            return c
+        u = (c[..., 0::2].astype(np.int16) & 0xF) | ((c[..., 1::2].astype(np.int16) & 0xF) << 4)
+        return u.astype(np.uint8).view(np.int8)
+
+    def unpack(c):
+        if state_bits == 8:
+            return c
+        u = c.view(np.uint8).astype(np.int16)
+        lo, hi = u & 0xF, u >> 4
+        return np.stack([np.where(lo > 7, lo - 16, lo), np.where(hi > 7, hi - 16, hi)], -1).reshape(
+            c.shape[:-1] + (2 * c.shape[-1],)).astype(np.int8)
+
+    cb = d * state_bits // 8
+    for c in range(T // W):
+        xs = {k: np.ascontiguousarray(v[:, c * W:(c + 1) * W]) for k, v in x.items()}
+        o = Guarded((B, W, H, d), torch.float32)
+        cg = Guarded((B, H, d, cb), torch.int8)
+        sg = Guarded((B, H, d), torch.float32)
+        ops.prefill_chunked(*_inputs(xs), init_codes=dev(pack(codes)), init_scales=dev(scales),
+                            out_dtype=torch.float32, o=o.t, codes=cg.t, scales=sg.t, state_bits=state_bits)
+        torch.cuda.synchronize()
+        assert o.guards_intact() and cg.guards_intact() and sg.guards_intact()
+        ref = O.prefill(xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], W=W, codes0=codes, scale0=scales,
+                        qmax=qmax)
+        err = max_rel_err(host(o.t), ref["o"])
+        assert err <= OUT_TOL_F32, f"chunk {c}: o max relative error {err:.3e}"
+        assert_codes(unpack(host(cg.t)), ref["codes"], f"chunk {c} codes")
+        assert_scales(host(sg.t), ref["scale"], f"chunk {c} scales")
+        codes, scales = unpack(host(cg.t)), host(sg.t)
+
+
+def test_prefill_d64_single_head_from_zero():
+    """The single-head d = 64 recurrence of the parity workload (q, k
+    L2-normalized, fp32 inputs rounded to bf16 for the prefill), 256 tokens
+    from a zero state in one call with bf16 output: free-running against the
+    oracle (outputs 2e-2, final codes +-1 on <= 0.1%)."""
+    x = wl.single_head_fp32(T=256, d=64, seed=0)
+    xs = {n: wl.bf16_round(x[n])[None, :, None] for n in ("q", "k", "v")}
+    xs.update({n: x[n][None, :, None] for n in ("alpha", "beta")})
+    o, cg, sg = ops.prefill_chunked(*_inputs(xs), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = O.prefill(xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], W=W)
+    assert max_rel_err(host(o), ref["o"]) <= OUT_TOL_BF16
+    assert_codes(host(cg), ref["codes"], "final codes")
+    assert_free_scales(host(sg), ref["scale"], "d = 64 single head, 4 windows")
+
+
 def test_prefill_matches_fp64_chunk_form():
     """Single head from zero state, T=192: the fp64 chunk (UT) form of the
     oracle, requantizing per window, gives the same outputs."""
