@@ -75,6 +75,7 @@ def decode_schedule_bytes(fills0, n_steps, heads=H, e_buf=4, state_bits=8):
 
 # the sources of the decode kernel (a traffic summary is stale once they change)
 DECODE_SOURCES = ["decode.hip", "decode_impl.h", "device_common.h"]
+SLIDING_SOURCES = ["decode_sliding.hip", "decode_impl.h", "device_common.h"]
 
 
 def source_hash(*names):
@@ -305,6 +306,76 @@ def bench_decode_long(torch, ops, wl, B2=256, steps=1024, warmup=16, n_tok=8):
     }
 
 
+def sliding_bytes_per_head(fill, W, dk=DK, dv=DV, e_in=2, e_out=2):
+    """Algorithmic HBM bytes of one sliding-window decode token for one head:
+    the historical rows + scales read and rewritten (requantized every
+    token), the n = min(fill, W) window writes read (fp32 k, v, alpha,
+    beta), the token's q, k, v, alpha, beta read, o written, and the token's
+    write stored in the ring."""
+    n = min(fill, W)
+    state = dv * dk + 4 * dv
+    w = 4 * (dk + dv) + 8
+    return 2 * state + n * w + e_in * (2 * dk + dv) + 8 + e_out * dv + w
+
+
+def bench_decode_sliding(args, torch, ops, wl, rep_count, Ws=8):
+    """The Pure-Write sliding-window decode (GDNQ_FLAG_SLIDING) on the decode
+    batch: B=64, H=32, d=128, window of Ws writes, ring fills drawn
+    U{0..2Ws-1} (about half the sequences with a full window), bf16 q/k/v,
+    rotating state replicas.  Every token rewrites every head's codes."""
+    dev = torch.device("cuda:0")
+    g = np.random.default_rng(70)
+    fills0 = g.integers(0, 2 * Ws, B).astype(np.int32)
+    d = wl.decode_batch(B=B, H=H, dk=DK, dv=DV, W=Ws, seed=71, fill=np.minimum(fills0, Ws - 1), poison=False)
+    state = torch.from_numpy(d["state"]).to(dev)
+    codes0, scales0 = ops.quantize_state(state)
+    del state
+    o = torch.empty((B, H, DV), dtype=torch.bfloat16, device=dev)
+    launchers, fills = [], []
+    for r in range(rep_count):
+        st = ops.DecodeState(codes0.clone(), scales0.clone(), Ws, fill=torch.from_numpy(fills0).to(dev),
+                             sliding=True)
+        for name in ("buf_k", "buf_v", "buf_alpha", "buf_beta"):
+            getattr(st, name).copy_(torch.from_numpy(d[name]))
+        x = wl.decode_tokens(B=B, H=H, dk=DK, dv=DV, step=r, seed=72)
+        tok = [torch.from_numpy(x["q"]).to(dev).bfloat16(), torch.from_numpy(x["k"]).to(dev).bfloat16(),
+               torch.from_numpy(x["v"]).to(dev).bfloat16(), torch.from_numpy(x["alpha"]).to(dev),
+               torch.from_numpy(x["beta"]).to(dev)]
+        launchers.append((st.bind(*tok, o=o), tok))
+        fills.append(fills0.astype(np.int64).copy())
+    n_all = args.warmup + args.steps
+    step_bytes = []
+    for i in range(n_all):
+        f = fills[i % rep_count]
+        step_bytes.append(int(sum(H * sliding_bytes_per_head(int(x), Ws) + 8 for x in f)))
+        fills[i % rep_count] = np.where(f < Ws, f + 1, Ws + (f - Ws + 1) % Ws)
+    total = sum(step_bytes[args.warmup:])
+    launch = [lc[0] for lc in launchers]
+    for i in range(args.warmup):
+        launch[i % rep_count]()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.warmup, n_all):
+        launch[i % rep_count]()
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbps = total / args.steps / (ms * 1e-3) / 1e9
+    return {
+        "workload": f"Pure-Write sliding-window decode step B={B} H={H} d_k=d_v={DK} window of {Ws} writes, "
+                    f"ring fills U{{0..{2 * Ws - 1}}}, bf16 q/k/v, int8 historical state requantized every "
+                    f"token, fp32 window, {rep_count} state replicas",
+        "ms_per_step": round(ms, 5), "tokens_s": round(B / (ms * 1e-3), 1), "gbps": round(gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic("decode_b64_h32_sliding_traffic.json", SLIDING_SOURCES, 1),
+                     "algorithmic_bytes_per_launch": int(total / args.steps)},
+    }
+
+
 def gdn_prefill_flops(B, T, H, dk=DK, dv=DV, C=64):
     """Useful FLOPs of the chunked GDN prefill, counted as full C x C tiles as
     MFMA executes them: per token-head 6 dk dv (K S0^T, Q S0^T and the state
@@ -357,7 +428,7 @@ def bench_prefill(torch, ops, wl, steps=5, warmup=2, with_cpu=True):
     dev = torch.device("cuda:0")
     res = {}
     names = ["gdn_prefill", "ssd_prefill", "gdn_prefill_handoff", "gdn_prefill_varlen",
-             "gdn_prefill_resume"]
+             "gdn_prefill_resume", "gdn_prefill_wht"]
     H16, d = 16, 128
     state_bytes = d * (d + 4)  # int8 rows + fp32 scales of one head
 
@@ -432,6 +503,8 @@ def bench_prefill(torch, ops, wl, steps=5, warmup=2, with_cpu=True):
                     ops.prefill_handoff(q, k, v, a, bt, o=o, state=st, workspace=ws)
             else:
                 kw = dict(ssd=True, wht=True, int8_qk=True) if ssd else dict(window=64)
+                if name == "gdn_prefill_wht":
+                    kw["wht"] = True
                 kw["workspace"] = torch.empty(ops.prefill_workspace_size(q, v, **kw), dtype=torch.uint8,
                                               device=dev)
                 kw["o"] = o
@@ -445,6 +518,7 @@ def bench_prefill(torch, ops, wl, steps=5, warmup=2, with_cpu=True):
                     ops.prefill_chunked(q, k, v, a, bt, **kw)
             workload = (f"B={Bq} T={T} H={Hh} d_k={dk} d_v={dv} chunk=64"
                         + (" WHT+int8 q/k, fp32 state" if ssd else " window=64, int8 state")
+                        + (", q and k rotated (WHT) and rounded to bf16" if name == "gdn_prefill_wht" else "")
                         + (f", the last {T % 64} tokens' writes handed to decode's window buffer"
                            if name == "gdn_prefill_handoff" else ""))
             tokens = N
@@ -513,6 +587,7 @@ def main():
     ap.add_argument("--no-fp8-buffer", action="store_true", help="skip the FP8 window-buffer line")
     ap.add_argument("--no-state4", action="store_true", help="skip the 4-bit state line")
     ap.add_argument("--no-long-decode", action="store_true", help="skip the B=256, 1024-step decode line")
+    ap.add_argument("--no-sliding", action="store_true", help="skip the sliding-window decode line")
     ap.add_argument("--no-bf16-buffer", action="store_true",
                     help="skip the decode measurement with the bf16 window buffer")
     ap.add_argument("--skip-decode", action="store_true",
@@ -604,6 +679,8 @@ def main():
                                                  DECODE_SOURCES + ["decode_q4.hip"], 1),
                          "algorithmic_bytes_per_launch": int(r4["bytes_per_launch"])},
         }
+    if not args.no_sliding:
+        line["decode_sliding_window"] = bench_decode_sliding(args, torch, ops, wl, max(1, args.replicas))
     if not args.no_long_decode:
         line["decode_b256_1024_steps"] = bench_decode_long(torch, ops, wl)
     if not args.no_prefill:
