@@ -1,8 +1,9 @@
 """ctypes binding of libgdnq.so (the C ABI declared in include/gdnq.h).
 
 Argument marshalling only.  The shared library is loaded from this package's
-directory; if it is missing, importing this module raises -- there is no
-fallback path.
+directory (or from the path in GDNQ_LIBRARY, which the host-sanitizer test
+uses for its instrumented build); if it is missing, importing this module
+raises -- there is no fallback path.
 """
 
 from __future__ import annotations
@@ -11,7 +12,7 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdnq.so")
+LIB_PATH = os.environ.get("GDNQ_LIBRARY") or os.path.join(_HERE, "libgdnq.so")
 
 GDNQ_OK = 0
 STATUS_NAMES = {0: "GDNQ_OK", 1: "GDNQ_ERR_NULL", 2: "GDNQ_ERR_SHAPE", 3: "GDNQ_ERR_DTYPE",
