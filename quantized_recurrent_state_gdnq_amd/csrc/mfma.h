@@ -64,4 +64,43 @@ __device__ __forceinline__ void split2(const float (&x)[N], V& hi, V& lo) {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
+// The same splits taken by truncation, for even N: hi keeps the upper 16 bits
+// of x, mid those of r = x - hi (exact), lo is r - mid (exact, at most eight
+// significant bits left).  hi + mid + lo equals x exactly; hi + mid keeps 16
+// significant bits.  One AND and one subtraction per part and element, and a
+// byte permute per pair packs the upper halves.
+template <int N, typename V>
+__device__ __forceinline__ void split3t(const float (&x)[N], V& hi, V& mid, V& lo) {
+  typedef uint32_t W __attribute__((ext_vector_type(N / 2)));
+  W h2, m2, l2;
+#pragma unroll
+  for (int e = 0; e < N; e += 2) {
+    const uint32_t a0 = __float_as_uint(x[e]), a1 = __float_as_uint(x[e + 1]);
+    const float r0 = x[e] - __uint_as_float(a0 & 0xffff0000u), r1 = x[e + 1] - __uint_as_float(a1 & 0xffff0000u);
+    const uint32_t b0 = __float_as_uint(r0), b1 = __float_as_uint(r1);
+    const float s0 = r0 - __uint_as_float(b0 & 0xffff0000u), s1 = r1 - __uint_as_float(b1 & 0xffff0000u);
+    h2[e / 2] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+    m2[e / 2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+    l2[e / 2] = __builtin_amdgcn_perm(__float_as_uint(s1), __float_as_uint(s0), 0x07060302u);
+  }
+  hi = __builtin_bit_cast(V, h2);
+  mid = __builtin_bit_cast(V, m2);
+  lo = __builtin_bit_cast(V, l2);
+}
+
+template <int N, typename V>
+__device__ __forceinline__ void split2t(const float (&x)[N], V& hi, V& lo) {
+  typedef uint32_t W __attribute__((ext_vector_type(N / 2)));
+  W h2, l2;
+#pragma unroll
+  for (int e = 0; e < N; e += 2) {
+    const uint32_t a0 = __float_as_uint(x[e]), a1 = __float_as_uint(x[e + 1]);
+    const float r0 = x[e] - __uint_as_float(a0 & 0xffff0000u), r1 = x[e + 1] - __uint_as_float(a1 & 0xffff0000u);
+    h2[e / 2] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+    l2[e / 2] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
+  }
+  hi = __builtin_bit_cast(V, h2);
+  lo = __builtin_bit_cast(V, l2);
+}
+
 }  // namespace gdnq

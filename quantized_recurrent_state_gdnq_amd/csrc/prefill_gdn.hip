@@ -20,15 +20,18 @@
 //   prep  -- one workgroup per chunk-head, all in parallel: K K^T on bf16
 //            MFMA (bf16 inputs, exact products), A, and T by blocked forward
 //            substitution (diagonal 16x16 blocks on the VALU, off-diagonal
-//            blocks on fp32 MFMA); T (as three bf16 parts) and g go to the
-//            workspace.
+//            blocks on fp32 MFMA); T's ten lower 16x16 tiles (as three bf16
+//            parts) and g go to the workspace.
 //   state -- one workgroup per (sequence, head, block of 32 rows): rows of
 //            the state evolve independently, so each workgroup carries its
-//            rows (codes + scales in LDS) through all chunks, four barriers
-//            per chunk, the next chunk's inputs prefetched into registers.
-//            Every product runs on bf16 MFMA: K S0^T and Q S0^T take the codes
-//            exactly; T (rhs), (U o d)^T K and M U split their fp32 operands
-//            into two or three bf16 parts, which keeps fp32-level accuracy.
+//            rows through all chunks.  Two chain waves hold 16 rows each
+//            entirely in registers (codes, rhs, U, U o d) and run a chunk's
+//            recurrence without waiting on any other wave; side waves form
+//            the output one chunk behind, staging waves load and stage the
+//            next chunk; one barrier per chunk.  Every product runs on bf16
+//            MFMA: K S0^T and Q S0^T take the codes exactly; T (rhs),
+//            K^T (U o d) and M U split their fp32 operands into two or three
+//            bf16 parts, which keeps fp32-level accuracy.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -40,6 +43,7 @@ namespace gdnq {
 constexpr int PC = 64;    // chunk = window
 constexpr int PD = 128;   // d_k = d_v
 constexpr int RWS = 32;   // state rows per state-pass workgroup
+constexpr int TT = 10;    // lower 16x16 tiles of a 64x64 matrix (T is kept as these)
 
 __device__ __forceinline__ void tile_of(int tt, int& it, int& jt) {
   it = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;  // lower 16x16 tiles (it >= jt), row-major
@@ -96,7 +100,7 @@ struct PrepArgs {
   const uint16_t* k;
   const float* alpha;
   const float* beta;
-  __bf16* T_ws;  // [chunks*H][3][64][64]: T as hi/mid/lo bf16 planes
+  __bf16* T_ws;  // [chunks*H][3][10][16][16]: T's lower tiles as hi/mid/lo bf16 parts
   float* g_ws;  // [chunks*H][64]
   SeqMap sm;
   int B, H;
@@ -288,8 +292,10 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
     __syncthreads();
   }
 
-  {  // T as three bf16 planes: thread -> row tid / 4, columns [(tid % 4) * 16, +16)
+  {  // T's ten lower 16x16 tiles as three bf16 parts [part][tile][16][16]:
+     // thread -> row tid / 4, columns [(tid % 4) * 16, +16), tiles on or below the diagonal
     const int i = tid >> 2, c0 = (tid & 3) * 16;
+    const int ti = i >> 4, tj = c0 >> 4;
     float x[16];
 #pragma unroll
     for (int e = 0; e < 16; e += 4) {
@@ -310,11 +316,13 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
       split3(lo8, p[0][0], p[1][0], p[2][0]);
       split3(hi8, p[0][1], p[1][1], p[2][1]);
     }
-    __bf16* dst = a.T_ws + size_t(idx) * 3 * PC * PC + i * PC + c0;
+    if (tj <= ti) {
+      __bf16* dst = a.T_ws + size_t(idx) * 3 * TT * 256 + (ti * (ti + 1) / 2 + tj) * 256 + (i & 15) * 16;
 #pragma unroll
-    for (int pl = 0; pl < 3; ++pl) {
-      *reinterpret_cast<bf16x8*>(dst + pl * PC * PC) = p[pl][0];
-      *reinterpret_cast<bf16x8*>(dst + pl * PC * PC + 8) = p[pl][1];
+      for (int pl = 0; pl < 3; ++pl) {
+        *reinterpret_cast<bf16x8*>(dst + pl * TT * 256) = p[pl][0];
+        *reinterpret_cast<bf16x8*>(dst + pl * TT * 256 + 8) = p[pl][1];
+      }
     }
   }
   if (!nxt.ok) break;
@@ -341,65 +349,71 @@ struct StateArgs {
   int B, H;
 };
 
-constexpr int TP = 72;    // bf16 pitch of [64][64] planes (T, M) and [32][64] planes (rhs^T, U^T)
-constexpr int SNP = 132;  // fp32 pitch of the new rows [32][128]
-constexpr int CBP = 136;  // bf16 pitch of the codes [32][128]
+constexpr int SNT = 512;  // state-pass threads: 2 chain, 4 side and 2 staging waves
+constexpr int VTP = 72;   // bf16 pitch of the V^T rows
 
-// LDS carve (bytes)
-constexpr int OFF_K = 0;                           // K  [64][KP] bf16
-constexpr int OFF_Q = OFF_K + PC * KP * 2;         // Q  [64][KP] bf16
-constexpr int OFF_KT = OFF_Q + PC * KP * 2;        // K^T [128][64] bf16, 16-byte granules xor-swizzled
-constexpr int OFF_T = OFF_KT + PD * PC * 2;        // T   hi/mid/lo [3][64][TP] bf16
-constexpr int OFF_M = OFF_T + 3 * PC * TP * 2;     // M   hi/lo [2][64][TP] bf16
-constexpr int OFF_R = OFF_M + 2 * PC * TP * 2;     // rhs^T hi/mid/lo [3][32][TP] bf16 (plane 0 holds V^T until rhs)
-constexpr int OFF_UD = OFF_R + 3 * RWS * TP * 2;   // (U o d)^T hi/mid/lo [3][32][TP] bf16
-constexpr int OFF_U = OFF_UD + 3 * RWS * TP * 2;   // U^T hi/lo [2][32][TP] bf16
-constexpr int OFF_SN = OFF_U + 2 * RWS * TP * 2;   // new rows [32][SNP] fp32
-constexpr int OFF_CB = OFF_SN + RWS * SNP * 4;     // codes [32][CBP] bf16 (exact)
-constexpr int OFF_G = OFF_CB + RWS * CBP * 2;      // per chunk parity: g, exp(g), beta [2][3][64]
-constexpr int OFF_D = OFF_G + 2 * 3 * PC * 4;      // exp(g_C - g) [64], row scales [32]
-constexpr int STATE_LDS = OFF_D + (PC + RWS) * 4;
+// LDS carve (bytes); [2] = by chunk parity
+constexpr int L_K = 0;                               // K [2][64][KP] bf16
+constexpr int L_Q = L_K + 2 * PC * KP * 2;           // Q [64][KP] bf16 (restaged in place)
+constexpr int L_KT = L_Q + PC * KP * 2;              // K^T [2][128][64] bf16, 16-byte granules xor-swizzled
+constexpr int L_T = L_KT + 2 * PD * PC * 2;          // T [2][3 parts][10 tiles][16][16] bf16
+constexpr int L_V = L_T + 2 * 3 * TT * 256 * 2;      // V^T [2][32][VTP] bf16
+constexpr int L_U = L_V + 2 * RWS * VTP * 2;         // U [2][2 parts][2 waves][2 steps][64 lanes] bf16x8
+constexpr int L_C = L_U + 2 * 2 * 2 * 2 * 64 * 16;   // codes [2][2 waves][4 steps][64 lanes] bf16x8
+constexpr int L_F = L_C + 2 * 2 * 4 * 64 * 16;       // g, exp(g), beta, exp(g_C - g) [2][4][64] fp32
+constexpr int L_S = L_F + 2 * 4 * PC * 4;            // row scales [2][32] fp32
+constexpr int STATE_LDS = L_S + 2 * RWS * 4;
 static_assert(STATE_LDS <= 160 * 1024, "state-pass LDS");
 
 __device__ __forceinline__ int kt_index(int d, int j) {  // bf16 index of K^T[d][j]
   return d * PC + ((((j >> 3) ^ (d >> 3)) & 7) << 3) + (j & 7);
 }
 
-__device__ __forceinline__ uint2 as_u2(const bf16x4& v) { return __builtin_bit_cast(uint2, v); }
+__device__ __forceinline__ int tile_index(int it, int jt) { return it * (it + 1) / 2 + jt; }  // jt <= it
 
-// Per chunk the state pass runs four phases between barriers, on two roles:
-//   eight chain waves (the recurrence itself)      eight side waves
-//   A  X = K S0^T; rhs                             Q S0^T, scaled: output base
-//   B  U = T rhs; U^T and (U o d)^T parts          stage K, Q of the next chunk; load two ahead
-//   C  S_C^T = gamma_C S0^T + K^T (U o d)          O = base + M U; stage T, V, g, beta of the
-//                                                  next chunk; load two ahead
-//   D  requantize S_C (and two tiles of M)         next chunk's K^T and M = L o Q K^T
-// Everything the recurrence does not wait on (the output, staging, memory
-// traffic, the next chunk's K^T and M) runs on the side waves, so a phase
-// lasts as long as the longer of the two roles' work, not their sum.  Every
-// prefetched register is consumed one chunk after it is loaded.
-constexpr int SNT = 1024;   // state-pass threads
-constexpr int NCRIT = 512;  // threads of the chain waves
+__device__ __forceinline__ bf16x4 lds4(const __bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& lo, const bf16x4& hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// A 32-wide k step of a 16x16x32 product takes its operands in the order
+//   slot 4h + q of lane group g  <->  index (2 ks + h) 16 + 4 g + q,
+// the order in which a 16x16 output tile holds four consecutive rows per lane
+// group.  Output tiles therefore feed the next product's B operand straight
+// from registers, and A operands are read from LDS as two 8-byte halves.
+//
+// Per workgroup (sequence, head, 32 state rows), eight waves:
+// (Waves are placed on the four SIMDs round robin: each chain wave shares its
+// SIMD with a staging wave, the lightest role.)
+//   chain waves 0, 1 -- 16 rows each, all in registers: the codes and scale
+//     of S0, then per chunk X = K codes^T, rhs = beta (v - gamma s X),
+//     U = T rhs, S_C^T = gamma_C S0^T + K^T (U o d) and the requantization.
+//   side waves 2, 3, 6, 7 -- token tile it = 0, 1, 2, 3: M = L o Q K^T for the tiles
+//     (it, <= it) and the output base gamma s Q S0^T, kept in registers, and
+//     a chunk later O = base + M U.  Each restages its own 16 rows of Q.
+//   staging waves 4, 5 -- K, K^T, T, V^T and the per-token scalars of the
+//     next chunk into the other buffer; loads two chunks ahead.
+// One barrier per chunk.  In chunk c the chain reads buffer c & 1 and writes
+// U_c and the codes of S0_{c+1}; the side waves read U_{c-1} and the codes
+// of S0_c; staging fills buffer (c + 1) & 1.
 // QB: the state's code width, 8 (int8) or 4 (packed 4-bit, scale absmax / 7)
 template <bool OUT_BF16, int QB>
 __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   constexpr int QMAX = QB == 8 ? 127 : 7;
   constexpr int RB = PD * QB / 8;  // bytes per stored row
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  __bf16* Kl = reinterpret_cast<__bf16*>(lds + OFF_K);
-  __bf16* Ql = reinterpret_cast<__bf16*>(lds + OFF_Q);
-  __bf16* KT = reinterpret_cast<__bf16*>(lds + OFF_KT);
-  __bf16* Tp = reinterpret_cast<__bf16*>(lds + OFF_T);
-  __bf16* Mp = reinterpret_cast<__bf16*>(lds + OFF_M);
-  __bf16* Rp = reinterpret_cast<__bf16*>(lds + OFF_R);
-  __bf16* Dp = reinterpret_cast<__bf16*>(lds + OFF_UD);
-  __bf16* Up = reinterpret_cast<__bf16*>(lds + OFF_U);
-  float* Sn = reinterpret_cast<float*>(lds + OFF_SN);
-  __bf16* Cb = reinterpret_cast<__bf16*>(lds + OFF_CB);
-  float* G = reinterpret_cast<float*>(lds + OFF_G);  // parity p: g at G + 192 p, exp(g) +64, beta +128
-  float* dl = reinterpret_cast<float*>(lds + OFF_D);
-  float* sl = dl + PC;
+  __bf16* const Kl = reinterpret_cast<__bf16*>(lds + L_K);
+  __bf16* const Ql = reinterpret_cast<__bf16*>(lds + L_Q);
+  __bf16* const KTl = reinterpret_cast<__bf16*>(lds + L_KT);
+  __bf16* const Tl = reinterpret_cast<__bf16*>(lds + L_T);
+  __bf16* const Vl = reinterpret_cast<__bf16*>(lds + L_V);
+  bf16x8* const Ul = reinterpret_cast<bf16x8*>(lds + L_U);
+  bf16x8* const Cl = reinterpret_cast<bf16x8*>(lds + L_C);
+  float* const Fl = reinterpret_cast<float*>(lds + L_F);
+  float* const Sl = reinterpret_cast<float*>(lds + L_S);
+  auto u_at = [&](int par, int part, int w, int ks) { return Ul + (((par * 2 + part) * 2 + w) * 2 + ks) * 64; };
+  auto c_at = [&](int par, int w, int ks) { return Cl + ((par * 2 + w) * 4 + ks) * 64; };
 
   const int nblk = a.B * a.H * (PD / RWS);
   const int logical = xcd_swizzle(blockIdx.x, nblk);  // the 4 row blocks of a head share an XCD
@@ -413,409 +427,459 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
     const int seg = nblk >> 5;  // chains per XCD segment
     cr = (chain % seg) * 8 + chain / seg;
   }
-  const int b = a.sm.order && (nblk & 31) == 0 ? a.sm.order[cr / a.H] : chain / a.H;
+  const int bs = a.sm.order && (nblk & 31) == 0 ? a.sm.order[cr / a.H] : chain / a.H;
   const int h = cr % a.H;
   const int r0 = rb * RWS;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lq = lane >> 4;
-  const int Tb = a.sm.len(b);  // this sequence's positions (buffered prefix and new tokens)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, g4 = lane >> 4;
+  const int Tb = a.sm.len(bs);  // this sequence's positions (buffered prefix and new tokens)
   const int NC = (Tb + PC - 1) / PC;
   const bool partial_last = (Tb % PC) != 0;  // the last chunk holds fewer than 64 tokens
   const size_t HD = size_t(a.H) * PD;
-  const size_t state_row0 = (size_t(b) * a.H + h) * PD + r0;
-  const size_t tokb = a.sm.tok0(b);
-
-  // one 16x16 tile of M = L o Q K^T of the staged chunk: tiles 0..9 are the
-  // lower tiles, D[j][i] = k_j . q_i stored as M[i][j] (hi and lo parts);
-  // tiles 10 and 11 the two zero tiles above the diagonal that the 32-token
-  // steps of M U reach
-  auto build_m_tile = [&](int tt, const float* gc) __attribute__((always_inline)) {
-    int mi, mj;
-    float m4[4] = {0.f, 0.f, 0.f, 0.f};
-    if (tt < 10) {
-      tile_of(tt, mi, mj);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kk = ks * 32 + 8 * lq;
-        acc = mfma16(lds_bf16x8(Kl + (mj * 16 + lr) * KP + kk), lds_bf16x8(Ql + (mi * 16 + lr) * KP + kk), acc);
-      }
-      const int i = mi * 16 + lr;
-      const float gi = gc[i];
-      const float4 g4 = *reinterpret_cast<const float4*>(gc + mj * 16 + 4 * lq);
-      const float gj[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = mj * 16 + 4 * lq + q;
-        m4[q] = (j <= i) ? exp_out(gi - gj[q]) * acc[q] : 0.f;
-      }
-    } else {
-      mi = tt == 10 ? 0 : 2;
-      mj = mi + 1;
-    }
-    bf16x4 h1, h2;
-    split2(m4, h1, h2);
-    const int i = mi * 16 + lr, j0 = mj * 16 + 4 * lq;
-    *reinterpret_cast<uint2*>(Mp + i * TP + j0) = as_u2(h1);
-    *reinterpret_cast<uint2*>(Mp + PC * TP + i * TP + j0) = as_u2(h2);
-  };
-
-  if (tid < NCRIT) {
-    // ================================================================ chain waves
-    const int it = wave >> 1, rt = wave & 1;  // this wave's (token tile, row tile) of X and U
-    const int nks = (it >> 1) + 1;            // 32-token steps reaching the diagonal of tile it
-    const int r = rt * 16 + lr;
-    const int i0 = it * 16 + 4 * lq;
-    {  // stored rows at the start (zero state without init)
-      const int rq = tid >> 4, seg = tid & 15;  // 32 rows x 16 segments of 8 codes
-      bf16x8 cv;
-      if constexpr (QB == 8) {
-        uint2 w = make_uint2(0u, 0u);
-        if (a.init_codes) w = *reinterpret_cast<const uint2*>(a.init_codes + (state_row0 + rq) * RB + seg * 8);
-        cv = i8x8_to_bf16(w);
-      } else {
-        uint32_t w = 0u;
-        if (a.init_codes) w = *reinterpret_cast<const uint32_t*>(a.init_codes + (state_row0 + rq) * RB + seg * 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cv[e] = (__bf16)i4_at(w, e);
-      }
-      *reinterpret_cast<bf16x8*>(Cb + rq * CBP + seg * 8) = cv;
-      if (seg == 0) sl[rq] = a.init_scales ? a.init_scales[state_row0 + rq] : 0.f;
-    }
-    if (NC > 0) {
-      __syncthreads();  // the side waves stage chunk 0
-      if (wave < 2) build_m_tile(8 + wave, G);
-    }
-    __syncthreads();  // ... and build its K^T and the rest of M
-
-    for (int c = 0; c < NC; ++c) {
-      const float* gc = G + 192 * (c & 1);
-      // ---- A: X = K S0^T (codes exact), rhs
-      {
-        f32x4 xacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int kk = ks * 32 + 8 * lq;
-          xacc = mfma16(lds_bf16x8(Kl + (it * 16 + lr) * KP + kk), lds_bf16x8(Cb + r * CBP + kk), xacc);
-        }
-        const float sr = sl[r];
-        const float4 e4 = *reinterpret_cast<const float4*>(gc + 64 + i0);
-        const float4 b4 = *reinterpret_cast<const float4*>(gc + 128 + i0);
-        const float ge[4] = {e4.x, e4.y, e4.z, e4.w}, be[4] = {b4.x, b4.y, b4.z, b4.w};
-        const uint2 vw = *reinterpret_cast<const uint2*>(Rp + r * TP + i0);
-        const float vv[4] = {__uint_as_float(vw.x << 16), __uint_as_float(vw.x & 0xffff0000u),
-                             __uint_as_float(vw.y << 16), __uint_as_float(vw.y & 0xffff0000u)};
-        float rh[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) rh[q] = be[q] * (vv[q] - ge[q] * (sr * xacc[q]));
-        bf16x4 h1, h2, h3;
-        split3(rh, h1, h2, h3);
-        *reinterpret_cast<uint2*>(Rp + r * TP + i0) = as_u2(h1);
-        *reinterpret_cast<uint2*>(Rp + RWS * TP + r * TP + i0) = as_u2(h2);
-        *reinterpret_cast<uint2*>(Rp + 2 * RWS * TP + r * TP + i0) = as_u2(h3);
-      }
-      if (tid < 64) dl[tid] = expf(gc[PC - 1] - gc[tid]);
-      __syncthreads();
-
-      // ---- B: U = T rhs (T unit lower triangular; six split products), then
-      //      U^T (two parts) and (U o d)^T (three parts)
-      {
-        f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = {0.f, 0.f, 0.f, 0.f};
-        for (int ks = 0; ks < nks; ++ks) {
-          const int kk = ks * 32 + 8 * lq;
-          const __bf16* tr = Tp + (it * 16 + lr) * TP + kk;
-          const __bf16* rr = Rp + r * TP + kk;
-          const bf16x8 t1 = lds_bf16x8(tr), t2 = lds_bf16x8(tr + PC * TP), t3 = lds_bf16x8(tr + 2 * PC * TP);
-          const bf16x8 b1 = lds_bf16x8(rr), b2 = lds_bf16x8(rr + RWS * TP), b3 = lds_bf16x8(rr + 2 * RWS * TP);
-          ua = mfma16(t2, b2, ua);
-          ub = mfma16(t3, b1, ub);
-          ua = mfma16(t1, b3, ua);
-          ub = mfma16(t2, b1, ub);
-          ua = mfma16(t1, b2, ua);
-          ub = mfma16(t1, b1, ub);
-        }
-        const float4 d4 = *reinterpret_cast<const float4*>(dl + i0);
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-        float u[4], ud[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          u[q] = ua[q] + ub[q];
-          ud[q] = u[q] * dd[q];
-        }
-        bf16x4 h1, h2, h3;
-        split2(u, h1, h2);
-        *reinterpret_cast<uint2*>(Up + r * TP + i0) = as_u2(h1);
-        *reinterpret_cast<uint2*>(Up + RWS * TP + r * TP + i0) = as_u2(h2);
-        split3(ud, h1, h2, h3);
-        *reinterpret_cast<uint2*>(Dp + r * TP + i0) = as_u2(h1);
-        *reinterpret_cast<uint2*>(Dp + RWS * TP + r * TP + i0) = as_u2(h2);
-        *reinterpret_cast<uint2*>(Dp + 2 * RWS * TP + r * TP + i0) = as_u2(h3);
-      }
-      __syncthreads();
-
-      // ---- C: new rows S_C^T = gamma_C S0^T + K^T (U o d) (not for a partial last chunk:
-      //      its window stays open and the stored state stays at the last boundary)
-      const bool update = !(partial_last && c == NC - 1);
-      if (update) {
-        const int dt0 = (wave >> 1) * 2;
-        bf16x8 u1[2], u2[2], u3[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const __bf16* dp = Dp + r * TP + ks * 32 + 8 * lq;
-          u1[ks] = lds_bf16x8(dp);
-          u2[ks] = lds_bf16x8(dp + RWS * TP);
-          u3[ks] = lds_bf16x8(dp + 2 * RWS * TP);
-        }
-        const float gs = gc[64 + PC - 1] * sl[r];
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const int dt = dt0 + cc;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 ak = lds_bf16x8(KT + kt_index(dt * 16 + lr, ks * 32 + 8 * lq));
-            acc = mfma16(ak, u3[ks], acc);
-            acc = mfma16(ak, u2[ks], acc);
-            acc = mfma16(ak, u1[ks], acc);
-          }
-          const int d0 = dt * 16 + 4 * lq;
-          const bf16x4 c4 = *reinterpret_cast<const bf16x4*>(Cb + r * CBP + d0);
-          float4 sn;
-          sn.x = gs * float(c4[0]) + acc[0];
-          sn.y = gs * float(c4[1]) + acc[1];
-          sn.z = gs * float(c4[2]) + acc[2];
-          sn.w = gs * float(c4[3]) + acc[3];
-          *reinterpret_cast<float4*>(Sn + r * SNP + d0) = sn;
-        }
-      }
-      __syncthreads();
-
-      // ---- D: requantize the new rows
-      if (update) {
-        const int rq = tid >> 4, seg = tid & 15;
-        const float4 s0 = *reinterpret_cast<const float4*>(Sn + rq * SNP + seg * 8);
-        const float4 s1 = *reinterpret_cast<const float4*>(Sn + rq * SNP + seg * 8 + 4);
-        const float x[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        float amax = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-        amax = group_max<16>(amax);
-        const float scale = codec_scale<QMAX>(amax);
-        float cf[8];
-        codec_codes<8, QMAX>(x, scale, cf);
-        bf16x8 cv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cv[e] = (__bf16)cf[e];
-        *reinterpret_cast<bf16x8*>(Cb + rq * CBP + seg * 8) = cv;
-        if (seg == 0) sl[rq] = scale;
-      }
-      if (wave < 2 && c + 1 < NC) build_m_tile(8 + wave, G + 192 * ((c + 1) & 1));
-      __syncthreads();
-    }
-
-    {  // final rows (codes back to int8, or packed 4-bit)
-      const int rq = tid >> 4, seg = tid & 15;
-      const bf16x8 cv = lds_bf16x8(Cb + rq * CBP + seg * 8);
-      if constexpr (QB == 8) {
-        uint2 w;
-        w.x = pack4_i8(int(float(cv[0])), int(float(cv[1])), int(float(cv[2])), int(float(cv[3])));
-        w.y = pack4_i8(int(float(cv[4])), int(float(cv[5])), int(float(cv[6])), int(float(cv[7])));
-        *reinterpret_cast<uint2*>(a.codes + (state_row0 + rq) * RB + seg * 8) = w;
-      } else {
-        int c4[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) c4[e] = int(float(cv[e]));
-        *reinterpret_cast<uint32_t*>(a.codes + (state_row0 + rq) * RB + seg * 4) = pack8_i4(c4);
-      }
-      if (seg == 0) a.scales[state_row0 + rq] = sl[rq];
-    }
-    return;
-  }
-
-  // ================================================================ side waves
-  const int st = tid - NCRIT;  // 0 .. 511
-  const int sw = st >> 6;      // side wave 0 .. 7: the chain wave whose (token tile, row tile) it outputs
-  // load mapping: K/Q token pair pm, dims [8 ps, +8); T row ti, columns
-  // [8 tc, +8) of each plane; V for chain lane st, in its MFMA output layout
-  const int pm = st & 31, ps = st >> 5;
-  const int ti = st >> 3, tc = st & 7;
-  const int vr = (sw & 1) * 16 + lr, vi = (sw >> 1) * 16 + 4 * lq;
-  const size_t kq_off = size_t(h) * PD + 8 * ps, v_off = size_t(h) * PD + r0 + vr;
-  const size_t wsc = size_t(a.sm.chunk0(b)) * a.H + h;  // workspace index of the first chunk
-  const __bf16* tb = a.T_ws + wsc * 3 * PC * PC + ti * PC + 8 * tc;
-  const float* gb = a.g_ws + wsc * PC + (st & 63);
-  const size_t ch_step = size_t(a.H) * 3 * PC * PC;  // T elements per chunk (all heads)
-  // position i of chunk c: whether it is in the sequence, and the row the
-  // loads read (clamped into the sequence; padding is zeroed when staged)
-  // the sequence map is read once, here: in the loop a scalar load's wait
-  // would also wait for every LDS access in flight
-  const int npre = a.sm.npre(b);
-  const bool stg0 = a.sm.pre != nullptr;  // chunk 0 is read from the staged copy
-  const size_t row_c0 = stg0 ? size_t(b) * PC : tokb;
-  const size_t row_t = tokb - size_t(npre);  // chunk c >= 1 starts at row row_t + 64 c (wraps back for c >= 1)
-  const uint16_t* const k_c0 = stg0 ? a.sm.sk : a.k;
-  const uint16_t* const q_c0 = stg0 ? a.sm.sq : a.q;
-  const uint16_t* const v_c0 = stg0 ? a.sm.sv : a.v;
-  const float* const b_c0 = stg0 ? a.sm.sb : a.beta;
   const uint32_t HD32 = uint32_t(HD);
-  auto tok_ok = [&](int c, int i) { return c * PC + i < Tb; };
-  // chunk c's first row (scalar, 64-bit) and the in-chunk row a lane reads
-  // (32-bit, clamped into the sequence)
+  const size_t state_row0 = (size_t(bs) * a.H + h) * PD + r0;
+  const size_t tokb = a.sm.tok0(bs);
+  // where chunk c's positions are read (the sequence map is read once, here)
+  const int npre = a.sm.npre(bs);
+  const bool stg0 = a.sm.pre != nullptr;  // chunk 0 is read from the staged copy
+  const size_t row_c0 = stg0 ? size_t(bs) * PC : tokb;
+  const size_t row_t = tokb - size_t(npre);  // chunk c >= 1 starts at row row_t + 64 c (wraps back for c >= 1)
   auto chunk_row = [&](int c) { return c == 0 ? row_c0 : row_t + size_t(c) * PC; };
-  auto in_row = [&](int c, int i) {
+  auto tok_ok = [&](int c, int i) { return c * PC + i < Tb; };
+  auto in_row = [&](int c, int i) {  // in-chunk row a load reads, clamped into the sequence
     const int lim = Tb - 1 - c * PC;
     return uint32_t(i < lim ? i : lim);
   };
-  int kq_c = 0, tv_c = 0;  // the chunks the prefetch registers hold
-
-  // (clang vector types: arrays of HIP's uint4 are copied through memory)
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 k0, k1, q0, q1;  // K, Q of the next chunk (or the one after)
-  u32x4 t0, t1, t2;      // T parts, V, g, beta likewise
-  uint32_t v4[4];
-  float gv = 0.f, bv = 0.f;
-  auto load_kq = [&](int c) {
-    kq_c = c;
-    const size_t cr = chunk_row(c) * HD + kq_off;
-    const uint16_t* kb = (c == 0 ? k_c0 : a.k) + cr;
-    const uint16_t* qb = (c == 0 ? q_c0 : a.q) + cr;
-    const uint32_t o0 = in_row(c, 2 * pm) * HD32, o1 = in_row(c, 2 * pm + 1) * HD32;
-    k0 = *reinterpret_cast<const u32x4*>(kb + o0);
-    k1 = *reinterpret_cast<const u32x4*>(kb + o1);
-    q0 = *reinterpret_cast<const u32x4*>(qb + o0);
-    q1 = *reinterpret_cast<const u32x4*>(qb + o1);
-  };
-  auto load_tv = [&](int c) {
-    tv_c = c;
-    const __bf16* tp = tb + size_t(c) * ch_step;
-    t0 = *reinterpret_cast<const u32x4*>(tp);
-    t1 = *reinterpret_cast<const u32x4*>(tp + PC * PC);
-    t2 = *reinterpret_cast<const u32x4*>(tp + 2 * PC * PC);
-    const size_t cr = chunk_row(c);
-    const uint16_t* vb = (c == 0 ? v_c0 : a.v) + cr * HD + v_off;
-    const float* bb = (c == 0 ? b_c0 : a.beta) + cr * a.H + h;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+  if (wave < 2) {
+    // ================================================================ chain waves
+    const int rl = wave * 16 + lr;  // this lane's row of the block
+    const size_t grow = state_row0 + rl;
+    float cf[8][4];  // codes of S0: dims dt 16 + 4 g4 + q
+    float s = 0.f;
+    if (a.init_codes) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v4[q] = vb[in_row(c, vi + q) * HD32];
-    gv = gb[size_t(c) * a.H * PC];  // every side lane loads (one wave's worth is used): no branch
+      for (int dt = 0; dt < 8; ++dt) {
+        const int d0 = dt * 16 + 4 * g4;
+        uint32_t w;
+        if constexpr (QB == 8) w = *reinterpret_cast<const uint32_t*>(a.init_codes + grow * RB + d0);
+        else w = *reinterpret_cast<const uint16_t*>(a.init_codes + grow * RB + d0 / 2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cf[dt][q] = code_at<QB>(w, q);
+      }
+      s = a.init_scales[grow];
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cf[dt][q] = 0.f;
+    }
+    bf16x8 cb[4];  // the codes as B operands of X, one per 32-dim step
+    auto pack_codes = [&]() {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cb[ks][e] = (__bf16)cf[2 * ks + (e >> 2)][e & 3];
+    };
+    auto publish = [&](int par) {  // codes and scale of S0 for the side waves' output base
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) c_at(par, wave, ks)[lane] = cb[ks];
+      if (g4 == 0) Sl[par * RWS + rl] = s;
+    };
+    pack_codes();
+    publish(0);
+    __syncthreads();  // chunk 0 staged
+
+    for (int c = 0; c < NC; ++c) {
+      const int par = c & 1;
+      const __bf16* K = Kl + par * PC * KP;
+      const __bf16* KT = KTl + par * PD * PC;
+      const __bf16* T = Tl + par * 3 * TT * 256;
+      const __bf16* V = Vl + par * RWS * VTP;
+      const float* F = Fl + par * 4 * PC;
+      // The A operands of X (K) and of U (T) are read up front, so the
+      // products issue back to back instead of each waiting for its read.
+      bf16x8 ka[4][4];  // K rows of tile jt, step ks
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const __bf16* kr = K + (jt * 16 + lr) * KP + ks * 32 + 4 * g4;
+          ka[jt][ks] = cat8(lds4(kr), lds4(kr + 16));
+        }
+      bf16x8 ta[6][3];  // T parts for (it, ks) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int ks = 0; ks <= (it >> 1); ++ks) {
+          const int n = it == 0 ? 0 : it == 1 ? 1 : it == 2 ? 2 + ks : 4 + ks;
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            const __bf16* tp = T + p * TT * 256 + lr * 16 + 4 * g4;
+            const bf16x4 lo = lds4(tp + tile_index(it, 2 * ks) * 256);
+            bf16x4 hi = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+            if (2 * ks + 1 <= it) hi = lds4(tp + tile_index(it, 2 * ks + 1) * 256);
+            ta[n][p] = cat8(lo, hi);
+          }
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- X = K codes^T: tile jt holds tokens jt 16 + 4 g4 + q of row rl
+      f32x4 x[4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) x[jt] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) x[jt] = mfma16(ka[jt][ks], cb[ks], x[jt]);
+      // ---- rhs = beta (v - gamma s X) in three bf16 parts
+      bf16x8 rp[3][2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float rh[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int jt = 2 * ks + hh, i0 = jt * 16 + 4 * g4;
+          const float4 ga = *reinterpret_cast<const float4*>(F + PC + i0);
+          const float4 be = *reinterpret_cast<const float4*>(F + 2 * PC + i0);
+          const uint2 vw = *reinterpret_cast<const uint2*>(V + rl * VTP + i0);
+          const float vv[4] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y)};
+          const float gg[4] = {ga.x, ga.y, ga.z, ga.w}, bt[4] = {be.x, be.y, be.z, be.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) rh[4 * hh + q] = bt[q] * (vv[q] - gg[q] * (s * x[jt][q]));
+        }
+        split3t(rh, rp[0][ks], rp[1][ks], rp[2][ks]);
+      }
+      // ---- U = T rhs (T unit lower triangular, three parts; six split products)
+      f32x4 u[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks <= (it >> 1); ++ks) {
+          const bf16x8* t = ta[it == 0 ? 0 : it == 1 ? 1 : it == 2 ? 2 + ks : 4 + ks];
+          ua = mfma16(t[1], rp[1][ks], ua);
+          ub = mfma16(t[2], rp[0][ks], ub);
+          ua = mfma16(t[0], rp[2][ks], ua);
+          ub = mfma16(t[1], rp[0][ks], ub);
+          ua = mfma16(t[0], rp[1][ks], ua);
+          ub = mfma16(t[0], rp[0][ks], ub);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) u[it][q] = ua[q] + ub[q];
+      }
+      // the update's A operands (K^T), read while U is formed
+      bf16x8 kta[8][2];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int d = dt * 16 + lr, j = ks * 32 + 4 * g4;
+          kta[dt][ks] = cat8(lds4(KT + kt_index(d, j)), lds4(KT + kt_index(d, j + 16)));
+        }
+      // ---- U (two parts) for the side waves; U o d (three parts) for the update
+      bf16x8 dp[3][2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float uu[8], ud[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float4 d4 = *reinterpret_cast<const float4*>(F + 3 * PC + (2 * ks + hh) * 16 + 4 * g4);
+          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uu[4 * hh + q] = u[2 * ks + hh][q];
+            ud[4 * hh + q] = u[2 * ks + hh][q] * dd[q];
+          }
+        }
+        bf16x8 u1, u2;
+        split2t(uu, u1, u2);
+        u_at(par, 0, wave, ks)[lane] = u1;
+        u_at(par, 1, wave, ks)[lane] = u2;
+        split3t(ud, dp[0][ks], dp[1][ks], dp[2][ks]);
+      }
+      // ---- S_C^T = gamma_C S0^T + K^T (U o d), then requantize the row (not
+      //      for a partial last chunk: its window stays open and the stored
+      //      state stays at the last boundary)
+      if (!(partial_last && c == NC - 1)) {
+        const float gs = F[PC + PC - 1] * s;
+        float sn[32];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 ak = kta[dt][ks];
+            acc = mfma16(ak, dp[2][ks], acc);
+            acc = mfma16(ak, dp[1][ks], acc);
+            acc = mfma16(ak, dp[0][ks], acc);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sn[4 * dt + q] = gs * cf[dt][q] + acc[q];
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(sn[e]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));  // the row's other three lane groups
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const float scale = codec_scale<QMAX>(amax);
+        float cn[32];
+        codec_codes<32, QMAX>(sn, scale, cn);
+#pragma unroll
+        for (int e = 0; e < 32; ++e) cf[e >> 2][e & 3] = cn[e];
+        s = scale;
+        pack_codes();
+        if (c + 1 < NC) publish(par ^ 1);
+      }
+      __syncthreads();
+    }
+    // final rows (codes back to int8, or packed 4-bit)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d0 = dt * 16 + 4 * g4;
+      const int c0 = int(cf[dt][0]), c1 = int(cf[dt][1]), c2 = int(cf[dt][2]), c3 = int(cf[dt][3]);
+      if constexpr (QB == 8)
+        *reinterpret_cast<uint32_t*>(a.codes + grow * RB + d0) = pack4_i8(c0, c1, c2, c3);
+      else
+        *reinterpret_cast<uint16_t*>(a.codes + grow * RB + d0 / 2) =
+            uint16_t((c0 & 0xf) | ((c1 & 0xf) << 4) | ((c2 & 0xf) << 8) | ((c3 & 0xf) << 12));
+    }
+    if (g4 == 0) a.scales[grow] = s;
+    return;
+  }
+
+  if (wave != 4 && wave != 5) {
+    // ================================================================ side waves
+    const int it = wave < 4 ? wave - 2 : wave - 4;  // token tile
+    // Q rows it 16 + qrow, 64-byte segment qseg: four 16-byte loads per lane
+    const int qrow = lane >> 2, qseg = lane & 3;
+    const uint16_t* const q_c0 = stg0 ? a.sm.sq : a.q;
+    u32x4 qv[4];
+    int q_c = 0;  // the chunk qv holds
+    auto load_q = [&](int c) {
+      q_c = c;
+      const uint16_t* qb = (c == 0 ? q_c0 : a.q) + chunk_row(c) * HD + size_t(h) * PD + qseg * 32;
+      const uint32_t o = in_row(c, it * 16 + qrow) * HD32;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[e] = *reinterpret_cast<const u32x4*>(qb + o + 8 * e);
+    };
+    auto stage_q = [&]() {
+      const bool ok = tok_ok(q_c, it * 16 + qrow);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(Ql + (it * 16 + qrow) * KP + qseg * 32 + 8 * e) = ok ? qv[e] : z4;
+    };
+    if (NC > 0) {
+      load_q(0);
+      stage_q();
+      load_q(NC > 1 ? 1 : 0);
+    }
+    __syncthreads();
+
+    bf16x8 mA[2][2];  // M (tiles (it, 2 ks), (it, 2 ks + 1)) as A operands, hi and lo parts
+    f32x4 os[2];      // output base of the two row tiles
+    // this sequence's outputs, bounded at its new tokens (a buffered prefix has
+    // no outputs here: decode gave them)
+    const rsrc_t o_rsrc = make_rsrc(static_cast<char*>(a.o) + tokb * HD * (OUT_BF16 ? 2 : 4),
+                                    uint32_t(size_t(Tb - npre) * HD * (OUT_BF16 ? 2 : 4)));
+    auto output = [&](int c) {  // O of chunk c = base + M U
+      const int par = c & 1;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks <= (it >> 1)) {  // the steps that reach the diagonal of tile it
+            const bf16x8 u1 = u_at(par, 0, rt, ks)[lane], u2 = u_at(par, 1, rt, ks)[lane];
+            acc = mfma16(mA[ks][1], u1, acc);
+            acc = mfma16(mA[ks][0], u2, acc);
+            acc = mfma16(mA[ks][0], u1, acc);
+          }
+        }
+        // a 4x4 transpose inside each quad of lanes (two DPP butterfly
+        // stages): lane (tokens 4 g4 .. +4, row lr) -> (token 4 g4 + lane % 4,
+        // rows lr - lane % 4 .. +4), one vector store per lane.  Stores past
+        // the sequence (padding) and of buffered positions are dropped.
+        float ov[4] = {os[rt][0] + acc[0], os[rt][1] + acc[1], os[rt][2] + acc[2], os[rt][3] + acc[3]};
+        const bool x1 = lane & 1, x2 = lane & 2;
+#pragma unroll
+        for (int p = 0; p < 4; p += 2) {  // slot bit 0 <-> lane bit 0
+          const float w = dpp<DPP_XOR1>(x1 ? ov[p] : ov[p + 1]);
+          if (x1) ov[p] = w;
+          else ov[p + 1] = w;
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {  // slot bit 1 <-> lane bit 1
+          const float w = dpp<DPP_XOR2>(x2 ? ov[p] : ov[p + 2]);
+          if (x2) ov[p] = w;
+          else ov[p + 2] = w;
+        }
+        const int tk = c * PC + it * 16 + 4 * g4 + (lane & 3) - npre;  // new token (< 0: buffered)
+        const uint32_t oi = uint32_t(tk) * HD32 + uint32_t(h * PD + r0 + rt * 16 + 4 * (lr >> 2));
+        if constexpr (OUT_BF16) {
+          const u32x2 w = {f32_to_bf16_bits(ov[0]) | (f32_to_bf16_bits(ov[1]) << 16),
+                           f32_to_bf16_bits(ov[2]) | (f32_to_bf16_bits(ov[3]) << 16)};
+          __builtin_amdgcn_raw_buffer_store_b64(w, o_rsrc, tk >= 0 ? oi * 2 : 0xffffffe0u, 0, 0);
+        } else {
+          const u32x4 w = {__float_as_uint(ov[0]), __float_as_uint(ov[1]), __float_as_uint(ov[2]),
+                           __float_as_uint(ov[3])};
+          __builtin_amdgcn_raw_buffer_store_b128(w, o_rsrc, tk >= 0 ? oi * 4 : 0xffffffe0u, 0, 0);
+        }
+      }
+    };
+    for (int c = 0; c < NC; ++c) {
+      const int par = c & 1;
+      const __bf16* K = Kl + par * PC * KP;
+      const float* F = Fl + par * 4 * PC;
+      if (c > 0) output(c - 1);
+      // ---- M = L o Q K^T for tiles (it, jt <= it): the tile D[j][i] = k_j . q_i
+      //      holds tokens j = jt 16 + 4 g4 + q for query i = it 16 + lr
+      {
+        const int i = it * 16 + lr;
+        const float gi = F[i];
+        float m[4][4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) m[jt][q] = 0.f;
+          if (jt <= it) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+              const int kk = ks * 32 + 8 * g4;
+              acc = mfma16(lds_bf16x8(K + (jt * 16 + lr) * KP + kk), lds_bf16x8(Ql + i * KP + kk), acc);
+            }
+            const float4 g4v = *reinterpret_cast<const float4*>(F + jt * 16 + 4 * g4);
+            const float gj[4] = {g4v.x, g4v.y, g4v.z, g4v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int j = jt * 16 + 4 * g4 + q;
+              m[jt][q] = (j <= i) ? exp_out(gi - gj[q]) * acc[q] : 0.f;
+            }
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          float mm[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mm[e] = m[2 * ks + (e >> 2)][e & 3];
+          split2t(mm, mA[ks][0], mA[ks][1]);
+        }
+      }
+      // ---- output base gamma_i s_r Q S0^T for the two row tiles
+      {
+        const float4 ga = *reinterpret_cast<const float4*>(F + PC + it * 16 + 4 * g4);
+        const float ge[4] = {ga.x, ga.y, ga.z, ga.w};
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const __bf16* qr = Ql + (it * 16 + lr) * KP + ks * 32 + 4 * g4;
+            acc = mfma16(cat8(lds4(qr), lds4(qr + 16)), c_at(par, rt, ks)[lane], acc);
+          }
+          const float sr = Sl[par * RWS + rt * 16 + lr];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) os[rt][q] = ge[q] * (sr * acc[q]);
+        }
+      }
+      // ---- this wave's Q rows of the next chunk (the loads are unconditional,
+      //      the chunk index clamped, so the in-order load counter never has to
+      //      assume the shorter path)
+      if (c + 1 < NC) stage_q();
+      load_q(c + 2 < NC ? c + 2 : NC - 1);
+      __syncthreads();
+    }
+    if (NC > 0) output(NC - 1);
+    return;
+  }
+
+  // ================================================================ staging waves
+  const int st = tid - 4 * 64;  // 0 .. 127
+  const uint16_t* const k_c0 = stg0 ? a.sm.sk : a.k;
+  const uint16_t* const v_c0 = stg0 ? a.sm.sv : a.v;
+  const float* const b_c0 = stg0 ? a.sm.sb : a.beta;
+  const size_t wsc = size_t(a.sm.chunk0(bs)) * a.H + h;  // workspace index of the first chunk
+  // K: units u = st + 128 m (m < 4) of token pair u % 32 and dims [8 (u / 32), +8);
+  // T: granules st + 128 m (m < 8) of the chunk's 960; V: token pair st % 32,
+  // rows [8 (st / 32), +8) of the block; g and beta: token st % 64
+  u32x4 kw[4][2], tw[8], vw[2];
+  float gv = 0.f, bv = 0.f;
+  int kc = 0;  // the chunk the registers hold
+  auto load_in = [&](int c) {
+    kc = c;
+    const size_t crow = chunk_row(c);
+    const uint16_t* kb = (c == 0 ? k_c0 : a.k) + crow * HD + size_t(h) * PD;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int u = st + 128 * m, p = u & 31, s8 = (u >> 5) * 8;
+      kw[m][0] = *reinterpret_cast<const u32x4*>(kb + in_row(c, 2 * p) * HD32 + s8);
+      kw[m][1] = *reinterpret_cast<const u32x4*>(kb + in_row(c, 2 * p + 1) * HD32 + s8);
+    }
+    const __bf16* tb = a.T_ws + (wsc + size_t(c) * a.H) * (3 * TT * 256);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int gi = st + 128 * m < 3 * TT * 32 ? st + 128 * m : 3 * TT * 32 - 1;
+      tw[m] = *reinterpret_cast<const u32x4*>(tb + gi * 8);
+    }
+    const int p = st & 31;
+    const uint16_t* vb = (c == 0 ? v_c0 : a.v) + crow * HD + size_t(h) * PD + r0 + 8 * (st >> 5);
+    vw[0] = *reinterpret_cast<const u32x4*>(vb + in_row(c, 2 * p) * HD32);
+    vw[1] = *reinterpret_cast<const u32x4*>(vb + in_row(c, 2 * p + 1) * HD32);
+    gv = a.g_ws[(wsc + size_t(c) * a.H) * PC + (st & 63)];
+    const float* bb = (c == 0 ? b_c0 : a.beta) + crow * a.H + h;
     bv = bb[in_row(c, st & 63) * uint32_t(a.H)];
   };
-  auto stage_kq = [&]() {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const bool ok0 = tok_ok(kq_c, 2 * pm), ok1 = tok_ok(kq_c, 2 * pm + 1);
-    *reinterpret_cast<u32x4*>(Kl + (2 * pm) * KP + 8 * ps) = ok0 ? k0 : z;
-    *reinterpret_cast<u32x4*>(Kl + (2 * pm + 1) * KP + 8 * ps) = ok1 ? k1 : z;
-    *reinterpret_cast<u32x4*>(Ql + (2 * pm) * KP + 8 * ps) = ok0 ? q0 : z;
-    *reinterpret_cast<u32x4*>(Ql + (2 * pm + 1) * KP + 8 * ps) = ok1 ? q1 : z;
-  };
-  auto stage_tv = [&](int par) {
-    *reinterpret_cast<u32x4*>(Tp + ti * TP + 8 * tc) = t0;
-    *reinterpret_cast<u32x4*>(Tp + PC * TP + ti * TP + 8 * tc) = t1;
-    *reinterpret_cast<u32x4*>(Tp + 2 * PC * TP + ti * TP + 8 * tc) = t2;
-    // V^T of the chain lane's (row, 4 tokens) into the slots of the first rhs^T
-    // plane: the chain lane reads them back and overwrites them with rhs
-    uint32_t vz[4];
+  auto stage_in = [&](int par) {
+    __bf16* K = Kl + par * PC * KP;
+    uint32_t* kt = reinterpret_cast<uint32_t*>(KTl + par * PD * PC);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) vz[q] = tok_ok(tv_c, vi + q) ? v4[q] : 0u;
-    *reinterpret_cast<uint2*>(Rp + vr * TP + vi) = make_uint2(vz[0] | (vz[1] << 16), vz[2] | (vz[3] << 16));
-    if (st < 64) {
-      float* gp = G + 192 * par;
-      gp[st] = gv;
-      gp[64 + st] = expf(gv);
-      gp[128 + st] = tok_ok(tv_c, st) ? bv : 0.f;  // padding: beta = 0
+    for (int m = 0; m < 4; ++m) {
+      const int u = st + 128 * m, p = u & 31, s8 = (u >> 5) * 8;
+      const u32x4 w0 = tok_ok(kc, 2 * p) ? kw[m][0] : z4;  // padding keys are 0
+      const u32x4 w1 = tok_ok(kc, 2 * p + 1) ? kw[m][1] : z4;
+      *reinterpret_cast<u32x4*>(K + (2 * p) * KP + s8) = w0;
+      *reinterpret_cast<u32x4*>(K + (2 * p + 1) * KP + s8) = w1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // K^T dword: tokens (2 p, 2 p + 1) of dim s8 + e
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        kt[kt_index(s8 + e, 2 * p) >> 1] = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
+      }
     }
-  };
-  // K^T of the staged K (tokens 2 pm, 2 pm + 1 of dims [8 ps, +8) per thread)
-  auto stage_kt = [&]() {
-    const u32x4 w0 = *reinterpret_cast<const u32x4*>(Kl + (2 * pm) * KP + 8 * ps);
-    const u32x4 w1 = *reinterpret_cast<const u32x4*>(Kl + (2 * pm + 1) * KP + 8 * ps);
-    uint32_t* kt = reinterpret_cast<uint32_t*>(KT);
+    __bf16* T = Tl + par * 3 * TT * 256;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of both words
-      kt[kt_index(8 * ps + e, 2 * pm) >> 1] = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
+    for (int m = 0; m < 8; ++m)
+      if (st + 128 * m < 3 * TT * 32) *reinterpret_cast<u32x4*>(T + (st + 128 * m) * 8) = tw[m];
+    {  // V^T dwords: rows 8 (st / 32) + e, tokens (2 p, 2 p + 1)
+      const int p = st & 31, o = st >> 5;
+      const u32x4 w0 = tok_ok(kc, 2 * p) ? vw[0] : z4, w1 = tok_ok(kc, 2 * p + 1) ? vw[1] : z4;
+      uint32_t* vt = reinterpret_cast<uint32_t*>(Vl + par * RWS * VTP);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        vt[((8 * o + e) * VTP + 2 * p) >> 1] = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
+      }
+    }
+    if (wave == 4) {  // per-token scalars, lane = token (padding: beta = 0)
+      float* F = Fl + par * 4 * PC;
+      const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 63));
+      F[lane] = gv;
+      F[PC + lane] = expf(gv);
+      F[2 * PC + lane] = tok_ok(kc, lane) ? bv : 0.f;
+      F[3 * PC + lane] = expf(gC - gv);
     }
   };
   if (NC > 0) {
-    load_kq(0);
-    load_tv(0);
-    stage_kq();
-    stage_tv(0);
-    load_kq(NC > 1 ? 1 : 0);
-    load_tv(NC > 1 ? 1 : 0);
-    __syncthreads();
-    stage_kt();
-    build_m_tile(sw, G);
-    if (sw == 2 || sw == 3) build_m_tile(sw + 8, G);
+    load_in(0);
+    stage_in(0);
+    load_in(NC > 1 ? 1 : 0);
   }
   __syncthreads();
-
-  const int it = sw >> 1, i0 = it * 16 + 4 * lq, nks = (it >> 1) + 1;
-  // this sequence's outputs, bounded at its new tokens (a buffered prefix has
-  // no outputs here: decode gave them)
-  const rsrc_t o_rsrc = make_rsrc(static_cast<char*>(a.o) + tokb * HD * (OUT_BF16 ? 2 : 4),
-                                  uint32_t(size_t(Tb - npre) * HD * (OUT_BF16 ? 2 : 4)));
   for (int c = 0; c < NC; ++c) {
-    const float* gc = G + 192 * (c & 1);
-    // ---- A: output base diag(gamma s) Q S0^T of this wave's (token tile, row tile)
-    float os[4];
-    {
-      f32x4 qacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kk = ks * 32 + 8 * lq;
-        qacc = mfma16(lds_bf16x8(Ql + (it * 16 + lr) * KP + kk), lds_bf16x8(Cb + vr * CBP + kk), qacc);
-      }
-      const float sr = sl[vr];
-      const float4 e4 = *reinterpret_cast<const float4*>(gc + 64 + i0);
-      const float ge[4] = {e4.x, e4.y, e4.z, e4.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) os[q] = ge[q] * (sr * qacc[q]);
-    }
-    __syncthreads();
-
-    // ---- B: K and Q of this chunk are no longer read.  The loads are
-    //      unconditional (the chunk index is clamped), so the in-order load
-    //      counter never has to assume the shorter path.
-    stage_kq();
-    load_kq(c + 2 < NC ? c + 2 : NC - 1);
-    __syncthreads();
-
-    // ---- C: O = base + M U; T and the rhs planes were last read in B, and
-    //      the other g parity is free
-    {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < nks; ++ks) {
-        const int kk = ks * 32 + 8 * lq;
-        const bf16x8 m1 = lds_bf16x8(Mp + (it * 16 + lr) * TP + kk);
-        const bf16x8 m2 = lds_bf16x8(Mp + PC * TP + (it * 16 + lr) * TP + kk);
-        const bf16x8 v1 = lds_bf16x8(Up + vr * TP + kk);
-        const bf16x8 v2 = lds_bf16x8(Up + RWS * TP + vr * TP + kk);
-        acc = mfma16(m2, v1, acc);
-        acc = mfma16(m1, v2, acc);
-        acc = mfma16(m1, v1, acc);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {  // stores past the sequence (padding tokens) are dropped
-        const int tk = c * PC + i0 + q - npre;  // new token of this position (< 0: buffered, no output)
-        const uint32_t oi = uint32_t(tk) * HD32 + uint32_t(h * PD + r0 + vr);
-        const float ov = os[q] + acc[q];
-        if constexpr (OUT_BF16)
-          __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_bits(ov)), o_rsrc, tk >= 0 ? oi * 2 : 0xfffffff0u, 0, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), o_rsrc, tk >= 0 ? oi * 4 : 0xfffffff0u, 0, 0);
-      }
-    }
-    stage_tv((c + 1) & 1);
-    load_tv(c + 2 < NC ? c + 2 : NC - 1);
-    __syncthreads();
-
-    // ---- D: K^T and eight tiles of M of the next chunk (the chain waves 0
-    //      and 1 take tiles 8 and 9 beside the requantization)
-    if (c + 1 < NC) {
-      stage_kt();
-      build_m_tile(sw, G + 192 * ((c + 1) & 1));
-      if (sw == 2 || sw == 3) build_m_tile(sw + 8, G + 192 * ((c + 1) & 1));
-    }
+    if (c + 1 < NC) stage_in((c + 1) & 1);
+    load_in(c + 2 < NC ? c + 2 : NC - 1);
     __syncthreads();
   }
 }
@@ -956,7 +1020,7 @@ static size_t gdn_chunks(const PrefillLaunch& L) {
   if (L.resume) return gdn_new_tokens(L) / PC + 2 * size_t(L.B);
   return L.varlen ? size_t(L.T / PC) + size_t(L.B) : size_t(L.B) * ((L.T + PC - 1) / PC);
 }
-static size_t gdn_ws_T(const PrefillLaunch& L) { return gdn_chunks(L) * L.H * 3 * PC * PC * 2; }
+static size_t gdn_ws_T(const PrefillLaunch& L) { return gdn_chunks(L) * L.H * 3 * TT * 256 * 2; }
 static size_t gdn_ws_g(const PrefillLaunch& L) { return gdn_chunks(L) * L.H * PC * 4; }
 // staged chunk 0 when resuming: k, q, v bf16 [B][64][H][128], alpha, beta fp32 [B][64][H]
 static size_t gdn_ws_stage(const PrefillLaunch& L) {

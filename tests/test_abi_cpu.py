@@ -212,11 +212,12 @@ def test_workspace_size_is_queryable():
 
 
 def test_workspace_sizes():
-    """GDN: per chunk-head, T as three bf16 planes (24 KiB) and g (256 B);
+    """GDN: per chunk-head, T's ten lower 16x16 tiles as three bf16 parts
+    (15 KiB) and g (256 B);
     SSD int8: codes and scales of q and k per token row; plain SSD: none."""
     B, T, H = 2, 256, 3
     nch = B * (T // 64) * H
-    assert _lib.prefill_workspace_size(_pp(B=B, T=T, H=H)) == nch * (3 * 64 * 64 * 2 + 64 * 4)
+    assert _lib.prefill_workspace_size(_pp(B=B, T=T, H=H)) == nch * (3 * 10 * 256 * 2 + 64 * 4)
     rows = B * T * H
     assert _lib.prefill_workspace_size(_pp(B=B, T=T, H=H, dv=64, flags=2 | 4 | 1)) == rows * (2 * 128 + 8)
     assert _lib.prefill_workspace_size(_pp(B=B, T=T, H=H, dv=64, flags=2)) == 0
@@ -265,7 +266,7 @@ def test_handoff_contract():
     workspace covers ceil(T / 64) chunks."""
     f = Fake()
     p = _pp(B=2, T=100, H=3)
-    assert _lib.prefill_handoff_workspace_size(p) == 2 * 2 * 3 * (3 * 64 * 64 * 2 + 64 * 4)
+    assert _lib.prefill_handoff_workspace_size(p) == 2 * 2 * 3 * (3 * 10 * 256 * 2 + 64 * 4)
     assert _handoff(p, f) == 6                                  # workspace missing
     assert _handoff(p, f, fill_out=None) == 1
     assert _handoff(p, f, buf_alpha=None) == 1
@@ -308,7 +309,7 @@ def test_varlen_contract():
     f = Fake()
     B, T, H = 5, 300, 3
     p = _pp(B=B, T=T, H=H)
-    assert _lib.prefill_varlen_workspace_size(p) == (T // 64 + B) * H * (3 * 64 * 64 * 2 + 64 * 4) + (4 * B + 2) * 4
+    assert _lib.prefill_varlen_workspace_size(p) == (T // 64 + B) * H * (3 * 10 * 256 * 2 + 64 * 4) + (4 * B + 2) * 4
     ws = f()
     need = _lib.prefill_varlen_workspace_size(p)
     assert _varlen(p, f) == 6                                   # workspace missing
@@ -360,9 +361,9 @@ def test_resume_contract():
     B, T, H = 3, 100, 2
     p = _pp(B=B, T=T, H=H)
     stage = B * 64 * H * (3 * 128 * 2 + 2 * 4)
-    need = (B * T // 64 + 2 * B) * H * (3 * 64 * 64 * 2 + 64 * 4) + stage + (4 * B + 2) * 4
+    need = (B * T // 64 + 2 * B) * H * (3 * 10 * 256 * 2 + 64 * 4) + stage + (4 * B + 2) * 4
     assert _lib.prefill_resume_workspace_size(p, 0) == need
-    need_v = (T // 64 + 2 * B) * H * (3 * 64 * 64 * 2 + 64 * 4) + stage + (4 * B + 2) * 4
+    need_v = (T // 64 + 2 * B) * H * (3 * 10 * 256 * 2 + 64 * 4) + stage + (4 * B + 2) * 4
     assert _lib.prefill_resume_workspace_size(p, 1) == need_v
     ws = f()
     assert _resume(p, f) == 6                                    # workspace missing

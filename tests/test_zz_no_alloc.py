@@ -93,7 +93,7 @@ def test_noalloc_ssd_two_calls_second_smaller():
 
 
 def test_noalloc_refuses_more_than_its_array():
-    """B=4, T=8192, H=16 needs 203 MB of workspace: refused, nothing written."""
+    """B=4, T=8192, H=16 needs 128 MB of workspace: refused, nothing written."""
     B, T, H = 4, 8192, 16
     q = torch.zeros((B, T, H, 128), dtype=torch.bfloat16, device=DEV)
     a = torch.ones((B, T, H), dtype=torch.float32, device=DEV)
