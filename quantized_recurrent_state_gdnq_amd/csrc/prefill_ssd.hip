@@ -16,14 +16,15 @@
 //   operand -- (int8 mode) four lanes per token row of q or k: FWHT in
 //              registers, row absmax, codec; codes and scales to the
 //              workspace (one launch for both operands).
-//   state   -- one workgroup per (sequence, head, 64 rows of d_v), two
-//              barriers per chunk.  Four state waves hold 16 rows each of the
-//              fp32 state as MFMA accumulators (eight 16x16 tiles of S^T) and
-//              update them in place; four aux waves build the decay matrix,
-//              form the output and stage the next chunk.  All products on
-//              bf16 MFMA: codes are exact in bf16; the state and the decayed,
-//              scaled V are split into three bf16 parts (hi + mid + lo equals
-//              the fp32 value exactly), the output-only decay matrix into two.
+//   state   -- one workgroup per (sequence, head, 64 rows of d_v), one
+//              barrier per chunk.  Four state waves hold 16 rows each of the
+//              fp32 state as MFMA accumulators (eight 16x16 tiles of S^T),
+//              form Q S0^T from them and update them in place; four helper
+//              waves build the decay matrix and M V, and write a chunk's
+//              output one chunk later.  All products on bf16 MFMA: codes and
+//              V are exact in bf16; the state, the decayed scaled V and the
+//              decay matrix enter as two bf16 parts each (16 significant
+//              bits, errors near 1e-5 relative).
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -123,16 +124,15 @@ struct SsdArgs {
 };
 
 constexpr int QP = 136;   // bf16 pitch of [64][128] (codes of q, k)
-constexpr int JP = 72;    // bf16 pitch of [64][64] planes (M parts, V^T, W parts)
+constexpr int JP = 72;    // bf16 pitch of the V^T rows
 
-constexpr int OFF_Q = 0;                          // q codes [64][QP] bf16
-constexpr int OFF_K = OFF_Q + SC * QP * 2;        // k codes [64][QP] bf16
-constexpr int OFF_KT = OFF_K + SC * QP * 2;       // [2] k codes transposed [128][64], xor-swizzled granules
-constexpr int OFF_M = OFF_KT + 2 * SDK * SC * 2;  // M hi/lo [2][64][JP] bf16
-constexpr int OFF_V = OFF_M + 2 * SC * JP * 2;    // [2] V^T [64 rows][JP] bf16
-constexpr int OFF_W = OFF_V + 2 * SRW * JP * 2;   // (V o d o sk)^T hi/mid/lo [3][64][JP] bf16
-constexpr int OFF_QS = OFF_W + 3 * SRW * JP * 2;  // Q S0^T tiles [4 it][4 rt][64 lanes] float4
-constexpr int OFF_F = OFF_QS + SC * SRW * 4;      // [2] g, exp(g), exp(g_C - g), sq, sk [5][64]
+// LDS carve (bytes); [2] = by chunk parity
+constexpr int OFF_Q = 0;                          // q codes [2][64][QP] bf16
+constexpr int OFF_K = OFF_Q + 2 * SC * QP * 2;    // k codes [2][64][QP] bf16
+constexpr int OFF_KT = OFF_K + 2 * SC * QP * 2;   // k codes transposed [2][128][64], xor-swizzled granules
+constexpr int OFF_V = OFF_KT + 2 * SDK * SC * 2;  // V^T [2][64 rows][JP] bf16
+constexpr int OFF_QS = OFF_V + 2 * SRW * JP * 2;  // Q S0^T tiles [2][4 row tiles][4 token tiles][64 lanes] float4
+constexpr int OFF_F = OFF_QS + 2 * SC * SRW * 4;  // g, exp(g), exp(g_C - g), sq, sk [2][5][64]
 constexpr int SSD_LDS = OFF_F + 2 * 5 * SC * 4;
 static_assert(SSD_LDS <= 160 * 1024, "SSD LDS");
 
@@ -147,35 +147,45 @@ __device__ __forceinline__ void tile_lower(int tt, int& it, int& jt) {
 
 __device__ __forceinline__ float exp_dec(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
-__device__ __forceinline__ uint2 u2_of(const bf16x4& v) { return __builtin_bit_cast(uint2, v); }
+__device__ __forceinline__ bf16x4 lds4(const __bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 
-// 8 int8 codes (two words) -> 8 bf16 packed in a uint4
-__device__ __forceinline__ uint4 i8x8_bf16_u4(uint32_t lo, uint32_t hi) {
-  return __builtin_bit_cast(uint4, i8x8_to_bf16(make_uint2(lo, hi)));
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& lo, const bf16x4& hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Per workgroup (sequence, head, 64 rows of d_v), eight waves:
-//   state waves 0..3 hold rows 16 rt .. +16 of the state, all 128 columns,
-//   as fp32 accumulators S^T[d][r] (eight 16x16 tiles in the MFMA output
-//   layout; two adjacent tiles form a B operand of the 16x16x32 product
-//   under a k order both operands share, so Q S0^T reads the state straight
-//   from registers, in three bf16 parts), and build W = (V o d o sk)^T;
-//   aux waves 4..7 build M = L o (sq sk Q K^T), produce the output rows of
-//   token tile it, stage the next chunk and prefetch the one after.
-// Two barriers per chunk:
-//   A  state: Q S0^T -> LDS, W            | aux: M
-//   B  state: S^T = e_C S^T + K^T W       | aux: O = e sq (Q S0^T) + M V; stage c+1, load c+2
+// 8 int8 codes (two words) -> 8 bf16 packed in four words
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4v i8x8_bf16_u4(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(u32x4v, i8x8_to_bf16(make_uint2(lo, hi)));
+}
+
+// Per workgroup (sequence, head, 64 rows of d_v), eight waves; wave w runs on
+// SIMD w % 4, so each state wave shares its SIMD with one helper wave.
+//   state waves 0..3 -- rows 16 w .. +16 of the state, all 128 columns, as
+//     fp32 accumulators S^T[d][r] (eight 16x16 tiles).  A 32-wide k step
+//     takes its eight k slots from two output tiles (slots 4h + q of lane
+//     group g <-> index (2 ks + h) 16 + 4 g + q), so the state tiles feed
+//     Q S0^T as B operands straight from registers, and so do the lanes' own
+//     W = (V o d o sk)^T values in the update; A operands (Q, K^T) are read
+//     from LDS as two 8-byte halves.  Per chunk: Q S0^T (published for the
+//     helpers), S^T = e_C S^T + K^T W.  Nothing here waits on another wave.
+//     They also stage the next chunk's k codes (as bf16), K^T and V^T and
+//     load the one after.
+//   helper waves 4..7 -- token tile it = w - 4: M = L o (sq sk Q K^T) for the
+//     tiles (it, <= it) and M V for all rows (in registers), and a chunk
+//     later the output e sq Q S0^T + M V; they also stage the next chunk's q
+//     codes and per-token scalars and load the one after.
+// The state's products take S and W as two bf16 parts each (16 significant
+// bits), M likewise; the codes and V are exact in bf16.  One barrier per chunk.
 template <bool I8, bool OUT_BF16>
 __global__ __launch_bounds__(512, 1) void ssd_state_kernel(SsdArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  __bf16* Qc = reinterpret_cast<__bf16*>(lds + OFF_Q);
-  __bf16* Kc = reinterpret_cast<__bf16*>(lds + OFF_K);
-  __bf16* KTb = reinterpret_cast<__bf16*>(lds + OFF_KT);
-  __bf16* Mp = reinterpret_cast<__bf16*>(lds + OFF_M);
-  __bf16* Vtb = reinterpret_cast<__bf16*>(lds + OFF_V);
-  __bf16* Wp = reinterpret_cast<__bf16*>(lds + OFF_W);
-  float4* QSl = reinterpret_cast<float4*>(lds + OFF_QS);
-  float* Fb = reinterpret_cast<float*>(lds + OFF_F);
+  __bf16* const Qb = reinterpret_cast<__bf16*>(lds + OFF_Q);
+  __bf16* const Kb = reinterpret_cast<__bf16*>(lds + OFF_K);
+  __bf16* const KTb = reinterpret_cast<__bf16*>(lds + OFF_KT);
+  __bf16* const Vtb = reinterpret_cast<__bf16*>(lds + OFF_V);
+  float4* const QSl = reinterpret_cast<float4*>(lds + OFF_QS);
+  float* const Fb = reinterpret_cast<float*>(lds + OFF_F);
 
   const int nrb = a.DV / SRW;
   const int chain = blockIdx.x / nrb, rb = blockIdx.x % nrb;
@@ -187,43 +197,196 @@ __global__ __launch_bounds__(512, 1) void ssd_state_kernel(SsdArgs a) {
   const int NC = a.T / SC;
   const size_t tokb = size_t(b) * a.T;
   const size_t HK = size_t(a.H) * SDK, HV = size_t(a.H) * a.DV;
-  const bool state_wave = wave < 4;
-  const int rt = wave & 3;        // state waves: row tile
-  const int it = wave & 3;        // aux waves: token tile
-  const int at = tid & 255;       // aux thread index
 
-  // ---- prefetch (aux threads): k as token pair jp, 16 dims 16 g8 .. ; q as
-  // token at / 4, 32 dims; v as token pair jp, 8 rows 8 g8 ..; scalars (at < 64)
-  const int jp = at & 31, g8 = at >> 5;
-  const int qt = at >> 2, qd = (at & 3) * 32;
-  uint4 ka[2], kb[2], qw[4], va, vb;
+  // prefetch mapping (256 lanes per role, u = tid % 256): k as token pair jp,
+  // 16 dims 16 g8 ..; v as token pair jp, rows 8 g8 ..; q as token u / 4, 32
+  // dims; the scalars of token u % 64.  The state waves load and stage k, K^T
+  // and V^T, the helper waves q and the per-token scalars.
+  const int u = tid & 255;
+  const int jp = u & 31, g8 = u >> 5;
+  const int qt = u >> 2, qd = (u & 3) * 32;
+  // (clang vector types: arrays of HIP's uint4 are copied through memory)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+  if (wave < 4) {
+    // ================================================================ state waves
+    const int rt = wave;
+    f32x4 S[8];  // S^T tiles: column r = 16 rt + lr, rows d = 16 dt + 4 lq + q
+#pragma unroll
+    for (int d = 0; d < 8; ++d) S[d] = {0.f, 0.f, 0.f, 0.f};
+    u32x4 ka[2], kb[2], va, vb;
+    auto load_kv = [&](int c) __attribute__((always_inline)) {
+      const size_t t0 = tokb + size_t(c) * SC;
+      const size_t ko = (t0 + 2 * jp) * HK + size_t(h) * SDK + 16 * g8;
+      if constexpr (I8) {
+        const int8_t* kp = static_cast<const int8_t*>(a.k) + ko;
+        ka[0] = *reinterpret_cast<const u32x4*>(kp);
+        kb[0] = *reinterpret_cast<const u32x4*>(kp + HK);
+      } else {
+        const uint16_t* kp = static_cast<const uint16_t*>(a.k) + ko;
+        ka[0] = *reinterpret_cast<const u32x4*>(kp);
+        ka[1] = *reinterpret_cast<const u32x4*>(kp + 8);
+        kb[0] = *reinterpret_cast<const u32x4*>(kp + HK);
+        kb[1] = *reinterpret_cast<const u32x4*>(kp + HK + 8);
+      }
+      const uint16_t* vp = a.v + (t0 + 2 * jp) * HV + size_t(h) * a.DV + r0 + 8 * g8;
+      va = *reinterpret_cast<const u32x4*>(vp);
+      vb = *reinterpret_cast<const u32x4*>(vp + HV);
+    };
+    auto stage_kv = [&](int par) __attribute__((always_inline)) {
+      __bf16* Kc = Kb + par * SC * QP;
+      u32x4 k0[2], k1[2];
+      if constexpr (I8) {
+        k0[0] = i8x8_bf16_u4(ka[0][0], ka[0][1]);
+        k0[1] = i8x8_bf16_u4(ka[0][2], ka[0][3]);
+        k1[0] = i8x8_bf16_u4(kb[0][0], kb[0][1]);
+        k1[1] = i8x8_bf16_u4(kb[0][2], kb[0][3]);
+      } else {
+        k0[0] = ka[0];
+        k0[1] = ka[1];
+        k1[0] = kb[0];
+        k1[1] = kb[1];
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        *reinterpret_cast<u32x4*>(Kc + (2 * jp) * QP + 16 * g8 + 8 * e) = k0[e];
+        *reinterpret_cast<u32x4*>(Kc + (2 * jp + 1) * QP + 16 * g8 + 8 * e) = k1[e];
+      }
+      {  // k^T: dword = tokens (2 jp, 2 jp + 1) of dim 16 g8 + e
+        uint32_t* kt = reinterpret_cast<uint32_t*>(KTb + par * SDK * SC);
+        const uint32_t w0[8] = {k0[0][0], k0[0][1], k0[0][2], k0[0][3], k0[1][0], k0[1][1], k0[1][2], k0[1][3]};
+        const uint32_t w1[8] = {k1[0][0], k1[0][1], k1[0][2], k1[0][3], k1[1][0], k1[1][1], k1[1][2], k1[1][3]};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          kt[kt_at(16 * g8 + e, 2 * jp) >> 1] = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
+        }
+      }
+      {  // V^T: rows 8 g8 + e, tokens (2 jp, 2 jp + 1)
+        uint32_t* vt = reinterpret_cast<uint32_t*>(Vtb + par * SRW * JP);
+        const uint32_t w0[4] = {va[0], va[1], va[2], va[3]}, w1[4] = {vb[0], vb[1], vb[2], vb[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          vt[((8 * g8 + e) * JP + 2 * jp) >> 1] = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
+        }
+      }
+    };
+    if (NC > 0) {
+      load_kv(0);
+      stage_kv(0);
+      load_kv(NC > 1 ? 1 : 0);
+    }
+    __syncthreads();  // chunk 0 staged
+    for (int c = 0; c < NC; ++c) {
+      const int par = c & 1;
+      const __bf16* Qc = Qb + par * SC * QP;
+      const __bf16* KT = KTb + par * SDK * SC;
+      const __bf16* Vt = Vtb + par * SRW * JP;
+      const float* F = Fb + par * 5 * SC;
+      // A operands are read ahead of their products, which then issue back
+      // to back: Q rows of the four token tiles here, K^T rows below
+      bf16x8 qa[4][4];
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const __bf16* qr = Qc + (ti * 16 + lr) * QP + ks * 32 + 4 * lq;
+          qa[ti][ks] = cat8(lds4(qr), lds4(qr + 16));
+        }
+      // W = V o d o sk for this row tile, tokens (2 ks + hh) 16 + 4 lq + q
+      bf16x8 wp[2][2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float x[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int j0 = (2 * ks + hh) * 16 + 4 * lq;
+          const uint2 vw = *reinterpret_cast<const uint2*>(Vt + (rt * 16 + lr) * JP + j0);
+          const float4 d4 = *reinterpret_cast<const float4*>(F + 2 * SC + j0);
+          const float4 k4 = *reinterpret_cast<const float4*>(F + 4 * SC + j0);
+          x[4 * hh + 0] = bf16_lo(vw.x) * (d4.x * k4.x);
+          x[4 * hh + 1] = bf16_hi(vw.x) * (d4.y * k4.y);
+          x[4 * hh + 2] = bf16_lo(vw.y) * (d4.z * k4.z);
+          x[4 * hh + 3] = bf16_hi(vw.y) * (d4.w * k4.w);
+        }
+        split2t(x, wp[0][ks], wp[1][ks]);
+      }
+      // S0 as B operands (two parts)
+      bf16x8 sp[2][4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const float x[8] = {S[2 * ks][0], S[2 * ks][1], S[2 * ks][2], S[2 * ks][3],
+                            S[2 * ks + 1][0], S[2 * ks + 1][1], S[2 * ks + 1][2], S[2 * ks + 1][3]};
+        split2t(x, sp[0][ks], sp[1][ks]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- Q S0^T for the four token tiles (published for the helpers)
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          acc = mfma16(qa[ti][ks], sp[1][ks], acc);
+          acc = mfma16(qa[ti][ks], sp[0][ks], acc);
+        }
+        QSl[((par * 4 + rt) * 4 + ti) * 64 + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      }
+      bf16x8 ka[8][2];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int d = dt * 16 + lr, j = ks * 32 + 4 * lq;
+          ka[dt][ks] = cat8(lds4(KT + kt_at(d, j)), lds4(KT + kt_at(d, j + 16)));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- S^T = e_C S^T + K^T W
+      const float eC = F[SC + SC - 1];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        f32x4 acc = S[dt];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] *= eC;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          acc = mfma16(ka[dt][ks], wp[1][ks], acc);
+          acc = mfma16(ka[dt][ks], wp[0][ks], acc);
+        }
+        S[dt] = acc;
+      }
+      // stage k, K^T, V^T of chunk c + 1 into the other buffer, load c + 2
+      // (unconditionally, the index clamped: every path issues the same loads)
+      if (c + 1 < NC) stage_kv(par ^ 1);
+      load_kv(c + 2 < NC ? c + 2 : NC - 1);
+      __syncthreads();
+    }
+    // final state rows r0 + 16 rt + lr, columns d: S^T tile layout
+    float* dst = a.state + ((size_t(b) * a.H + h) * a.DV + r0 + rt * 16 + lr) * SDK;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      *reinterpret_cast<float4*>(dst + d * 16 + 4 * lq) = make_float4(S[d][0], S[d][1], S[d][2], S[d][3]);
+    return;
+  }
+
+  // ================================================================ helper waves
+  const int it = wave - 4;  // token tile
+  u32x4 qw[4];
   float av = 1.f, sqv = 1.f, skv = 1.f;
   auto load = [&](int c) __attribute__((always_inline)) {
     const size_t t0 = tokb + size_t(c) * SC;
-    const size_t ko = (t0 + 2 * jp) * HK + size_t(h) * SDK + 16 * g8;
     const size_t qo = (t0 + qt) * HK + size_t(h) * SDK + qd;
     if constexpr (I8) {
-      const int8_t* kp = static_cast<const int8_t*>(a.k) + ko;
       const int8_t* qp = static_cast<const int8_t*>(a.q) + qo;
-      ka[0] = *reinterpret_cast<const uint4*>(kp);
-      kb[0] = *reinterpret_cast<const uint4*>(kp + HK);
-      qw[0] = *reinterpret_cast<const uint4*>(qp);
-      qw[1] = *reinterpret_cast<const uint4*>(qp + 16);
+      qw[0] = *reinterpret_cast<const u32x4*>(qp);
+      qw[1] = *reinterpret_cast<const u32x4*>(qp + 16);
     } else {
-      const uint16_t* kp = static_cast<const uint16_t*>(a.k) + ko;
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qo;
-      ka[0] = *reinterpret_cast<const uint4*>(kp);
-      ka[1] = *reinterpret_cast<const uint4*>(kp + 8);
-      kb[0] = *reinterpret_cast<const uint4*>(kp + HK);
-      kb[1] = *reinterpret_cast<const uint4*>(kp + HK + 8);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qw[e] = *reinterpret_cast<const uint4*>(qp + 8 * e);
+      for (int e = 0; e < 4; ++e) qw[e] = *reinterpret_cast<const u32x4*>(qp + 8 * e);
     }
-    const uint16_t* vp = a.v + (t0 + 2 * jp) * HV + size_t(h) * a.DV + r0 + 8 * g8;
-    va = *reinterpret_cast<const uint4*>(vp);
-    vb = *reinterpret_cast<const uint4*>(vp + HV);
-    {  // every aux lane loads, so each load is issued on every path; lanes at < 64 keep them
-      const size_t t = (t0 + (at & 63)) * a.H + h;
+    {  // every helper lane loads, so each load is issued on every path
+      const size_t t = (t0 + (u & 63)) * a.H + h;
       av = a.alpha[t];
       if constexpr (I8) {
         sqv = a.sq[t];
@@ -232,50 +395,19 @@ __global__ __launch_bounds__(512, 1) void ssd_state_kernel(SsdArgs a) {
     }
   };
   auto stage = [&](int par) __attribute__((always_inline)) {
-    uint4 k0[2], k1[2], q8[4];
+    __bf16* Qc = Qb + par * SC * QP;
+    u32x4 q8[4];
     if constexpr (I8) {
-      k0[0] = i8x8_bf16_u4(ka[0].x, ka[0].y);
-      k0[1] = i8x8_bf16_u4(ka[0].z, ka[0].w);
-      k1[0] = i8x8_bf16_u4(kb[0].x, kb[0].y);
-      k1[1] = i8x8_bf16_u4(kb[0].z, kb[0].w);
-      q8[0] = i8x8_bf16_u4(qw[0].x, qw[0].y);
-      q8[1] = i8x8_bf16_u4(qw[0].z, qw[0].w);
-      q8[2] = i8x8_bf16_u4(qw[1].x, qw[1].y);
-      q8[3] = i8x8_bf16_u4(qw[1].z, qw[1].w);
+      q8[0] = i8x8_bf16_u4(qw[0][0], qw[0][1]);
+      q8[1] = i8x8_bf16_u4(qw[0][2], qw[0][3]);
+      q8[2] = i8x8_bf16_u4(qw[1][0], qw[1][1]);
+      q8[3] = i8x8_bf16_u4(qw[1][2], qw[1][3]);
     } else {
-      k0[0] = ka[0];
-      k0[1] = ka[1];
-      k1[0] = kb[0];
-      k1[1] = kb[1];
 #pragma unroll
       for (int e = 0; e < 4; ++e) q8[e] = qw[e];
     }
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      *reinterpret_cast<uint4*>(Kc + (2 * jp) * QP + 16 * g8 + 8 * e) = k0[e];
-      *reinterpret_cast<uint4*>(Kc + (2 * jp + 1) * QP + 16 * g8 + 8 * e) = k1[e];
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) *reinterpret_cast<uint4*>(Qc + qt * QP + qd + 8 * e) = q8[e];
-    {  // k^T: dword = tokens (2 jp, 2 jp + 1) of dim 16 g8 + e
-      uint32_t* kt = reinterpret_cast<uint32_t*>(KTb + par * SDK * SC);
-      const uint32_t w0[8] = {k0[0].x, k0[0].y, k0[0].z, k0[0].w, k0[1].x, k0[1].y, k0[1].z, k0[1].w};
-      const uint32_t w1[8] = {k1[0].x, k1[0].y, k1[0].z, k1[0].w, k1[1].x, k1[1].y, k1[1].z, k1[1].w};
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        kt[kt_at(16 * g8 + e, 2 * jp) >> 1] = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
-      }
-    }
-    {  // V^T: rows 8 g8 + e, tokens (2 jp, 2 jp + 1)
-      uint32_t* vt = reinterpret_cast<uint32_t*>(Vtb + par * SRW * JP);
-      const uint32_t w0[4] = {va.x, va.y, va.z, va.w}, w1[4] = {vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        vt[((8 * g8 + e) * JP + 2 * jp) >> 1] = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
-      }
-    }
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(Qc + qt * QP + qd + 8 * e) = q8[e];
     if (wave == 4) {  // g = inclusive prefix sum of log a over the chunk (lane = token)
       const float g = wave_scan_incl(logf(av));
       const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 63));
@@ -288,224 +420,133 @@ __global__ __launch_bounds__(512, 1) void ssd_state_kernel(SsdArgs a) {
     }
   };
 
-  // The two roles run separate loops (same barrier count per chunk), so each
-  // gets its own register allocation: the prefetch registers of the aux
-  // waves never have to survive the state waves' code
-  if (state_wave) {
-    f32x4 S[8];  // S^T tiles
+  if (NC > 0) {
+    load(0);
+    stage(0);
+    load(NC > 1 ? 1 : 0);
+  }
+  __syncthreads();
+  bf16x8 mA[2][2];  // M (tiles (it, 2 ks), (it, 2 ks + 1)) as A operands, hi and lo parts
+  f32x4 mv[4];      // M V for the four row tiles
+  float es[4];      // e_i sq_i of this wave's tokens
+  auto output = [&](int c) {  // O of chunk c = e sq Q S0^T + M V
+    const int par = c & 1;
+    const size_t tok0 = tokb + size_t(c) * SC;
+    const bool x1 = lane & 1, x2 = lane & 2;
+    float4 qsv[4];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) S[d] = {0.f, 0.f, 0.f, 0.f};
-    __syncthreads();
-    for (int c = 0; c < NC; ++c) {
-      const int par = c & 1;
-      const float* F = Fb + par * 5 * SC;
-      const __bf16* KT = KTb + par * SDK * SC;
-      const __bf16* Vt = Vtb + par * SRW * JP;
-      // -------------------------------------------------------------- A
-      // Q S0^T for the four token tiles of row tile rt, 32 dims per product:
-      // the k slots of lane group lq are dims 32 m + 4 lq + {0..3} (tile 2m)
-      // and 32 m + 16 + 4 lq + {0..3} (tile 2m + 1), the same order in both
-      // operands, so the state tiles feed the B operand as they are
-      auto q_ops = [&](int m, bf16x8* aq) __attribute__((always_inline)) {
+    for (int rr = 0; rr < 4; ++rr) qsv[rr] = QSl[((par * 4 + rr) * 4 + it) * 64 + lane];
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          const __bf16* qr = Qc + (ti * 16 + lr) * QP + 32 * m + 4 * lq;
-          const uint2 lo = *reinterpret_cast<const uint2*>(qr);
-          const uint2 hi = *reinterpret_cast<const uint2*>(qr + 16);
-          aq[ti] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        }
-      };
-      f32x4 acc[4];
+    for (int rr = 0; rr < 4; ++rr) {
+      const float4 qs = qsv[rr];
+      float o[4] = {es[0] * qs.x + mv[rr][0], es[1] * qs.y + mv[rr][1], es[2] * qs.z + mv[rr][2],
+                    es[3] * qs.w + mv[rr][3]};
+      // a 4x4 transpose inside each quad of lanes (two DPP butterfly stages)
+      // turns lane (token 4 lq + q, row lr) into (token 4 lq + lane % 4,
+      // rows 4 (lr / 4) .. +4), one vector store per row tile
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) acc[ti] = {0.f, 0.f, 0.f, 0.f};
-      bf16x8 aq[2][4];
-      q_ops(0, aq[0]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (m < 3) q_ops(m + 1, aq[(m + 1) & 1]);
-        const float x[8] = {S[2 * m][0], S[2 * m][1], S[2 * m][2], S[2 * m][3],
-                            S[2 * m + 1][0], S[2 * m + 1][1], S[2 * m + 1][2], S[2 * m + 1][3]};
-        bf16x8 bp[3];
-        split3(x, bp[0], bp[1], bp[2]);
-#pragma unroll
-        for (int p = 2; p >= 0; --p)
-#pragma unroll
-          for (int ti = 0; ti < 4; ++ti) acc[ti] = mfma16(aq[m & 1][ti], bp[p], acc[ti]);
+      for (int p = 0; p < 4; p += 2) {  // slot bit 0 <-> lane bit 0
+        const float w = dpp<DPP_XOR1>(x1 ? o[p] : o[p + 1]);
+        if (x1) o[p] = w;
+        else o[p + 1] = w;
       }
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti)
-        QSl[(ti * 4 + rt) * 64 + lane] = make_float4(acc[ti][0], acc[ti][1], acc[ti][2], acc[ti][3]);
-      {  // W[r][j] = V[j][r] d_j sk_j for this row tile: row 16 rt + lane / 4, tokens [16 (lane % 4), +16)
-        const int rr = rt * 16 + (lane >> 2), j0 = (lane & 3) * 16;
+      for (int p = 0; p < 2; ++p) {  // slot bit 1 <-> lane bit 1
+        const float w = dpp<DPP_XOR2>(x2 ? o[p] : o[p + 2]);
+        if (x2) o[p] = w;
+        else o[p + 2] = w;
+      }
+      const size_t oi = (tok0 + it * 16 + 4 * lq + (lane & 3)) * HV + size_t(h) * a.DV + r0 + rr * 16 + 4 * (lr >> 2);
+      if constexpr (OUT_BF16)
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + oi) =
+            make_uint2(f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
+                       f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16));
+      else
+        *reinterpret_cast<float4*>(static_cast<float*>(a.o) + oi) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  };
+  for (int c = 0; c < NC; ++c) {
+    const int par = c & 1;
+    const __bf16* Qc = Qb + par * SC * QP;
+    const __bf16* Kc = Kb + par * SC * QP;
+    const __bf16* Vt = Vtb + par * SRW * JP;
+    const float* F = Fb + par * 5 * SC;
+    if (c > 0) output(c - 1);
+    // ---- M = L o (sq sk Q K^T) for tiles (it, jt <= it): the tile
+    //      D[j][i] = ck_j . cq_i holds tokens j = jt 16 + 4 lq + q of query i
+    {
+      const int i = it * 16 + lr;
+      const float gi = F[i], si = F[3 * SC + i];
+      // operands up front: the query row once, the key rows of all four
+      // tiles (every helper takes the same branch-free path; tiles above the
+      // diagonal come out zero through the mask, and the busiest helper,
+      // it = 3, needs all four anyway)
+      bf16x8 qo[4], ko[4][4];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int jb = j0 + 8 * hh;
-          const bf16x8 vv = lds_bf16x8(Vt + rr * JP + jb);
-          const float4 d0 = *reinterpret_cast<const float4*>(F + 2 * SC + jb);
-          const float4 d1 = *reinterpret_cast<const float4*>(F + 2 * SC + jb + 4);
-          const float4 k0 = *reinterpret_cast<const float4*>(F + 4 * SC + jb);
-          const float4 k1 = *reinterpret_cast<const float4*>(F + 4 * SC + jb + 4);
-          const float dk[8] = {d0.x * k0.x, d0.y * k0.y, d0.z * k0.z, d0.w * k0.w,
-                               d1.x * k1.x, d1.y * k1.y, d1.z * k1.z, d1.w * k1.w};
-          float x[8];
+      for (int ks = 0; ks < 4; ++ks) qo[ks] = lds_bf16x8(Qc + i * QP + ks * 32 + 8 * lq);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = float(vv[e]) * dk[e];
-          bf16x8 w1, w2, w3;
-          split3(x, w1, w2, w3);
-          *reinterpret_cast<bf16x8*>(Wp + rr * JP + jb) = w1;
-          *reinterpret_cast<bf16x8*>(Wp + SRW * JP + rr * JP + jb) = w2;
-          *reinterpret_cast<bf16x8*>(Wp + 2 * SRW * JP + rr * JP + jb) = w3;
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) ko[jt][ks] = lds_bf16x8(Kc + (jt * 16 + lr) * QP + ks * 32 + 8 * lq);
+      float m[4][4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16(ko[jt][ks], qo[ks], acc);
+        const float4 g4 = *reinterpret_cast<const float4*>(F + jt * 16 + 4 * lq);
+        const float4 k4 = *reinterpret_cast<const float4*>(F + 4 * SC + jt * 16 + 4 * lq);
+        const float gj[4] = {g4.x, g4.y, g4.z, g4.w}, sj[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = jt * 16 + 4 * lq + q;
+          m[jt][q] = (j <= i) ? exp_dec(gi - gj[q]) * (si * sj[q]) * acc[q] : 0.f;
         }
       }
-      __syncthreads();
-      // -------------------------------------------------------------- B
-      const float eC = F[SC + SC - 1];
-      bf16x8 w1[2], w2[2], w3[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const __bf16* wp = Wp + (rt * 16 + lr) * JP + ks * 32 + 8 * lq;
-        w1[ks] = lds_bf16x8(wp);
-        w2[ks] = lds_bf16x8(wp + SRW * JP);
-        w3[ks] = lds_bf16x8(wp + 2 * SRW * JP);
+        float mm[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mm[e] = m[2 * ks + (e >> 2)][e & 3];
+        split2t(mm, mA[ks][0], mA[ks][1]);
       }
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        f32x4 acc = S[d];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] *= eC;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 ak = lds_bf16x8(KT + kt_at(d * 16 + lr, ks * 32 + 8 * lq));
-          acc = mfma16(ak, w3[ks], acc);
-          acc = mfma16(ak, w2[ks], acc);
-          acc = mfma16(ak, w1[ks], acc);
-        }
-        S[d] = acc;
-      }
-      __syncthreads();
     }
-    // final state rows r0 + 16 rt + lr, columns d: S^T tile layout
-    float* dst = a.state + ((size_t(b) * a.H + h) * a.DV + r0 + rt * 16 + lr) * SDK;
+    // ---- M V for the four row tiles; e sq of this wave's tokens
+    bf16x8 vo[4][2];
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
-      *reinterpret_cast<float4*>(dst + d * 16 + 4 * lq) = make_float4(S[d][0], S[d][1], S[d][2], S[d][3]);
-  } else {
-    if (NC > 0) {
-      load(0);
-      stage(0);
-      load(NC > 1 ? 1 : 0);
-    }
-    __syncthreads();
-    for (int c = 0; c < NC; ++c) {
-      const int par = c & 1;
-      const float* F = Fb + par * 5 * SC;
-      const __bf16* Vt = Vtb + par * SRW * JP;
-      // -------------------------------------------------------------- A
-      // M tiles, spread over the four aux waves: the ten lower tiles, then
-      // the two zero tiles above the diagonal that the 32-token steps reach
+    for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-      for (int n = 0; n < 3; ++n) {
-        const int tt = it + 4 * n;
-        int mi, mj;
-        float m4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (tt < 10) {  // M^T tile D[j][i] = ck_j . cq_i
-          tile_lower(tt, mi, mj);
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const int kk = ks * 32 + 8 * lq;
-            acc = mfma16(lds_bf16x8(Kc + (mj * 16 + lr) * QP + kk), lds_bf16x8(Qc + (mi * 16 + lr) * QP + kk), acc);
-          }
-          const int i = mi * 16 + lr;
-          const float gi = F[i], si = F[3 * SC + i];
-          const float4 g4 = *reinterpret_cast<const float4*>(F + mj * 16 + 4 * lq);
-          const float4 k4 = *reinterpret_cast<const float4*>(F + 4 * SC + mj * 16 + 4 * lq);
-          const float gj[4] = {g4.x, g4.y, g4.z, g4.w}, sj[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int j = mj * 16 + 4 * lq + q;
-            m4[q] = (j <= i) ? exp_dec(gi - gj[q]) * (si * sj[q]) * acc[q] : 0.f;
-          }
-        } else {
-          mi = tt == 10 ? 0 : 2;
-          mj = mi + 1;
-        }
-        bf16x4 h1, h2;
-        split2(m4, h1, h2);
-        const int i = mi * 16 + lr, j0 = mj * 16 + 4 * lq;
-        *reinterpret_cast<uint2*>(Mp + i * JP + j0) = u2_of(h1);
-        *reinterpret_cast<uint2*>(Mp + SC * JP + i * JP + j0) = u2_of(h2);
+      for (int ks = 0; ks < 2; ++ks) {
+        const __bf16* vr = Vt + (rr * 16 + lr) * JP + ks * 32 + 4 * lq;
+        vo[rr][ks] = cat8(lds4(vr), lds4(vr + 16));
       }
-      __syncthreads();
-      // -------------------------------------------------------------- B
-      const size_t tok0 = tokb + size_t(c) * SC;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {  // steps past the diagonal multiply zeros of M
+        acc = mfma16(mA[ks][1], vo[rr][ks], acc);
+        acc = mfma16(mA[ks][0], vo[rr][ks], acc);
+      }
+      mv[rr] = acc;
+    }
+    {
       const int i0 = it * 16 + 4 * lq;
       const float4 e4 = *reinterpret_cast<const float4*>(F + SC + i0);
       const float4 q4 = *reinterpret_cast<const float4*>(F + 3 * SC + i0);
-      const float es[4] = {e4.x * q4.x, e4.y * q4.y, e4.z * q4.z, e4.w * q4.w};
-      f32x4 mv[4];  // (M V) for the four row tiles
-      auto mv_tiles = [&](auto nk) __attribute__((always_inline)) {
-        constexpr int NK = decltype(nk)::value;
-        bf16x8 m1[NK], m2[NK];
-#pragma unroll
-        for (int ks = 0; ks < NK; ++ks) {
-          const int kk = ks * 32 + 8 * lq;
-          m1[ks] = lds_bf16x8(Mp + (it * 16 + lr) * JP + kk);
-          m2[ks] = lds_bf16x8(Mp + SC * JP + (it * 16 + lr) * JP + kk);
-        }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < NK; ++ks) {
-            const bf16x8 vv = lds_bf16x8(Vt + (rr * 16 + lr) * JP + ks * 32 + 8 * lq);
-            acc = mfma16(m2[ks], vv, acc);
-            acc = mfma16(m1[ks], vv, acc);
-          }
-          mv[rr] = acc;
-        }
-      };
-      if (it < 2) mv_tiles(std::integral_constant<int, 1>{});
-      else mv_tiles(std::integral_constant<int, 2>{});
-      // the stores sit on the common path, so every path issues the same
-      // count after the prefetch and the stage's waits stay loose.  A 4x4
-      // transpose inside each quad of lanes (two DPP butterfly stages) turns
-      // lane (token 4 lq + q, column lr) into (token 4 lq + lane % 4,
-      // columns 4 (lr / 4) .. +4), one vector store per row tile
-      const bool x1 = lane & 1, x2 = lane & 2;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float4 qs = QSl[(it * 4 + rr) * 64 + lane];
-        float o[4] = {es[0] * qs.x + mv[rr][0], es[1] * qs.y + mv[rr][1], es[2] * qs.z + mv[rr][2],
-                      es[3] * qs.w + mv[rr][3]};
-#pragma unroll
-        for (int p = 0; p < 4; p += 2) {  // slot bit 0 <-> lane bit 0
-          const float w = dpp<DPP_XOR1>(x1 ? o[p] : o[p + 1]);
-          if (x1) o[p] = w;
-          else o[p + 1] = w;
-        }
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {  // slot bit 1 <-> lane bit 1
-          const float w = dpp<DPP_XOR2>(x2 ? o[p] : o[p + 2]);
-          if (x2) o[p] = w;
-          else o[p + 2] = w;
-        }
-        const size_t oi = (tok0 + it * 16 + 4 * lq + (lane & 3)) * HV + size_t(h) * a.DV + r0 + rr * 16 + 4 * (lr >> 2);
-        if constexpr (OUT_BF16)
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + oi) =
-              make_uint2(f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
-                         f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16));
-        else
-          *reinterpret_cast<float4*>(static_cast<float*>(a.o) + oi) = make_float4(o[0], o[1], o[2], o[3]);
-      }
-      // stage chunk c + 1, prefetch c + 2; the prefetch is issued on every
-      // path (the tail re-reads the last chunk) so the stage's waits count
-      // past the output stores on entry and in the loop alike
-      if (c + 1 < NC) stage(par ^ 1);
-      load(c + 2 < NC ? c + 2 : NC - 1);
-      __syncthreads();
+      es[0] = e4.x * q4.x;
+      es[1] = e4.y * q4.y;
+      es[2] = e4.z * q4.z;
+      es[3] = e4.w * q4.w;
     }
+    // stage chunk c + 1, prefetch c + 2; the prefetch is issued on every
+    // path (the tail re-reads the last chunk) so the stage's waits count
+    // past the output stores alike
+    if (c + 1 < NC) stage(par ^ 1);
+    load(c + 2 < NC ? c + 2 : NC - 1);
+    __syncthreads();
   }
+  if (NC > 0) output(NC - 1);
 }
 
 size_t ssd_rows(const PrefillLaunch& L) { return size_t(L.B) * L.T * L.H; }
