@@ -211,8 +211,14 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
  *   GDN (flags without GDNQ_FLAG_SSD): the gated delta rule over T tokens
  *   from the stored state (init_codes/init_scales, or zero when both are
  *   NULL), requantizing at every window end, windows aligned to token 0.
- *   Supported: d_k = d_v = 128, chunk = window = 64, T a multiple of 64.
- *   Writes o and the final codes/scales (the state after the last window).
+ *   Supported: d_k = d_v in {128, 64} (GDNQ_FLAG_WHT at 128 only), window
+ *   W in {16, 32, 64}, chunk in {16, 32, 64}, T a multiple of W.  The
+ *   kernels run every window as one 64-position chunk (a shorter window is
+ *   padded with writes that leave the state unchanged; d = 64 runs as a
+ *   zero-padded d = 128 head), so the result depends on the window, not on
+ *   the chunk, which is a blocking hint.  Padded runs need a larger
+ *   workspace.  Writes o and the final codes/scales (the state after the
+ *   last window).
  *   state_f32 must be NULL.  Flags: GDNQ_FLAG_STATE_4BIT (init_codes and
  *   codes then hold packed 4-bit codes, [B,H,d_v,d_k/2] bytes, and every
  *   window end requantizes with the 4-bit codec) and/or GDNQ_FLAG_WHT: every

@@ -184,12 +184,24 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   if (B < 0 || T < 0 || H < 1) return fail(GDNQ_ERR_SHAPE, "batch = %d, seqlen = %d, heads = %d", B, T, H);
   if (p->in_dtype != GDNQ_BF16) return fail(GDNQ_ERR_DTYPE, "prefill in_dtype must be GDNQ_BF16");
   if (p->out_dtype != GDNQ_F32 && p->out_dtype != GDNQ_BF16) return fail(GDNQ_ERR_DTYPE, "out_dtype = %d", p->out_dtype);
-  if (p->chunk != 64) return fail(GDNQ_ERR_SHAPE, "chunk = %d, expected 64", p->chunk);
-  if (T % 64 && !handoff) return fail(GDNQ_ERR_SHAPE, "seqlen = %d is not a multiple of the chunk (64)", T);
-  if ((int64_t(T) + 64) * H * 512 >= (int64_t(1) << 32))  // 32-bit output offsets, padding tokens included
+  const bool ssd = (p->flags & GDNQ_FLAG_SSD) != 0;
+  const int C = p->chunk, W = p->window;
+  // GDN: chunk and window in {16, 32, 64} (the kernels run every window as one
+  // 64-position chunk, so the result depends on the window only); the
+  // hand-over, varlen and resume calls and SSD take chunk = 64 (= window)
+  if (ssd || handoff) {
+    if (C != 64) return fail(GDNQ_ERR_SHAPE, "chunk = %d, expected 64", C);
+    if (!ssd && W != 64) return fail(GDNQ_ERR_SHAPE, "window = %d: the hand-over, varlen and resume calls take 64", W);
+  } else {
+    if (C != 16 && C != 32 && C != 64) return fail(GDNQ_ERR_SHAPE, "chunk = %d, expected 16, 32 or 64", C);
+    if (W != 16 && W != 32 && W != 64) return fail(GDNQ_ERR_SHAPE, "window = %d, expected 16, 32 or 64", W);
+  }
+  const int Wt = ssd ? 64 : W;  // whole windows (the SSD recurrence has none: whole chunks)
+  if (T % Wt && !handoff) return fail(GDNQ_ERR_SHAPE, "seqlen = %d is not a multiple of the window (%d)", T, Wt);
+  const int64_t Tk = ssd ? T : int64_t(T) / Wt * 64 + (handoff ? T % 64 : 0);  // positions the chunk kernels see
+  if ((Tk + 64) * H * 512 >= (int64_t(1) << 32))  // 32-bit output offsets, padding positions included
     return fail(GDNQ_ERR_SHAPE, "seqlen * heads = %lld: one sequence's outputs must stay under 4 GiB",
                 (long long)T * H);
-  const bool ssd = (p->flags & GDNQ_FLAG_SSD) != 0;
   if (ssd && handoff) return fail(GDNQ_ERR_FLAGS, "the hand-over to decode is for the GDN recurrence (no GDNQ_FLAG_SSD)");
   if (ssd) {
     if (p->flags & ~uint32_t(GDNQ_FLAG_SSD | GDNQ_FLAG_WHT | GDNQ_FLAG_INT8_QK))
@@ -208,7 +220,6 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
       return fail(GDNQ_ERR_SHAPE, "GDN prefill at d = 64: gdnq_prefill_chunked only (not the hand-over, varlen or resume calls)");
     if (dk == 64 && (p->flags & GDNQ_FLAG_WHT))
       return fail(GDNQ_ERR_FLAGS, "GDN prefill at d = 64 takes no GDNQ_FLAG_WHT");
-    if (p->window != p->chunk) return fail(GDNQ_ERR_SHAPE, "GDN prefill: window = %d must equal chunk = %d", p->window, p->chunk);
   }
   if (int64_t(B) * H * 8 > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "batch * heads too large");
   L = gdnq::PrefillLaunch{};

@@ -889,37 +889,72 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
 // + B, and with a buffered prefix of at most 63 writes per sequence,
 // sum ceil((pre + n) / 64) <= floor(N / 64) + 2 B.
 static size_t gdn_new_tokens(const PrefillLaunch& L) { return L.varlen ? size_t(L.T) : size_t(L.B) * L.T; }
-// d_k = d_v = 64: the head runs as a d = 128 head whose extra key
-// dimensions and value rows are zero.  Keys padded with zeros get and erase
-// nothing in the extra columns, zero value rows write nothing, and every
-// product and row absmax only gains +0 terms, so the padded head carries the
-// d = 64 state exactly in its first 64 rows and columns.  gdn_pad_kernel
-// widens q, k, v (and the stored state) into the workspace; gdn_unpad_kernel
-// copies the outputs and the final state back.
+// Shapes the chunk kernels do not take directly run on padded copies in the
+// workspace:
+//   * d_k = d_v = 64: the head runs as a d = 128 head whose extra key
+//     dimensions and value rows are zero.  Keys padded with zeros get and
+//     erase nothing in the extra columns, zero value rows write nothing, and
+//     every product and row absmax only gains +0 terms, so the padded head
+//     carries the d = 64 state exactly in its first 64 rows and columns.
+//   * a window W of 16 or 32 tokens: every window becomes one 64-position
+//     chunk whose last 64 - W positions are writes that change nothing
+//     (k = q = v = 0, alpha = 1, beta = 0): the state passes them unchanged,
+//     so each chunk end is exactly the window's end and is requantized there.
+// gdn_pad_kernel builds the padded q, k, v (and alpha, beta; and the stored
+// state at d = 64); gdn_unpad_kernel copies the real tokens' outputs (and the
+// final state at d = 64) back.
 struct PadArgs {
-  const uint16_t* x[3];  // q, k, v [rows][64] bf16
-  uint16_t* y[3];        // [rows][128] bf16
-  int64_t rows;
-  const int8_t* c0;      // stored state [bh][64][RB64] (NULL: zero state)
+  const uint16_t* x[3];  // q, k, v [B][T][H][ds] bf16
+  uint16_t* y[3];        // [B][Tp][H][128] bf16
+  const float* a;        // alpha, beta [B][T][H] (NULL: not padded, W = 64)
+  const float* be;
+  float* pa;             // [B][Tp][H]
+  float* pb;
+  int64_t B, T, H;
+  int W, ds;             // window (positions taken per 64-position chunk), source width
+  const int8_t* c0;      // stored state [bh][64][RB64] (NULL: zero state or not padded)
   const float* s0;       // [bh][64]
   int8_t* pc0;           // [bh][128][RB128]
   float* ps0;            // [bh][128]
   int64_t bh;
-  int rb64;              // bytes per stored row: 64 (8-bit) or 32 (4-bit)
+  int rb64;              // bytes per stored row at d = 64: 64 (8-bit) or 32 (4-bit)
 };
 
 __global__ __launch_bounds__(256) void gdn_pad_kernel(PadArgs a) {
-  const int64_t n = a.rows * 3 * 16;  // 16-byte granules of the padded rows
-  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n; e += int64_t(gridDim.x) * 256) {
-    const int64_t row = e / 48;
+  const int64_t Tp = a.T / a.W * PC;
+  const int64_t rows = a.B * Tp * a.H;  // padded rows
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  const int gs = a.ds / 8;  // 16-byte granules per source row
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < rows * 48; e += stride) {
+    const int64_t r = e / 48;  // padded row (b Tp + p) H + h
     const int op = int(e % 48) / 16, g = int(e % 16);
-    const uint4 w = g < 8 ? reinterpret_cast<const uint4*>(a.x[op] + row * 64)[g] : make_uint4(0u, 0u, 0u, 0u);
-    reinterpret_cast<uint4*>(a.y[op] + row * PD)[g] = w;
+    const int64_t h = r % a.H, bp = r / a.H, p = bp % Tp, b = bp / Tp;
+    const int i = int(p % PC);  // position in its chunk
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (i < a.W && g < gs) {
+      const int64_t t = p / PC * a.W + i;  // the source token
+      w = reinterpret_cast<const uint4*>(a.x[op] + ((b * a.T + t) * a.H + h) * a.ds)[g];
+    }
+    reinterpret_cast<uint4*>(a.y[op] + r * PD)[g] = w;
+  }
+  if (a.a) {
+    for (int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x; r < rows; r += stride) {
+      const int64_t h = r % a.H, bp = r / a.H, p = bp % Tp, b = bp / Tp;
+      const int i = int(p % PC);
+      float al = 1.f, bt = 0.f;
+      if (i < a.W) {
+        const int64_t src = (b * a.T + p / PC * a.W + i) * a.H + h;
+        al = a.a[src];
+        bt = a.be[src];
+      }
+      a.pa[r] = al;
+      a.pb[r] = bt;
+    }
   }
   if (!a.pc0) return;
   const int rb128 = 2 * a.rb64;
   const int64_t ns = a.bh * PD * (rb128 / 16);
-  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < ns; e += int64_t(gridDim.x) * 256) {
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < ns; e += stride) {
     const int64_t r = e / (rb128 / 16);  // padded state row (bh * 128 + row)
     const int g = int(e % (rb128 / 16));
     const int64_t bh = r / PD, rr = r % PD;
@@ -931,11 +966,11 @@ __global__ __launch_bounds__(256) void gdn_pad_kernel(PadArgs a) {
 }
 
 struct UnpadArgs {
-  const char* po;  // [rows][128] outputs (eo bytes each)
-  char* o;         // [rows][64]
-  int64_t rows;
-  int eo;
-  const int8_t* pc;  // [bh][128][RB128]
+  const char* po;  // [B][Tp][H][128] outputs (eo bytes each)
+  char* o;         // [B][T][H][ds]
+  int64_t B, T, H;
+  int W, ds, eo;
+  const int8_t* pc;  // [bh][128][RB128] (NULL: the state was not padded)
   const float* ps;
   int8_t* c;         // [bh][64][RB64]
   float* sc;
@@ -944,15 +979,20 @@ struct UnpadArgs {
 };
 
 __global__ __launch_bounds__(256) void gdn_unpad_kernel(UnpadArgs a) {
-  const int gpr = 64 * a.eo / 16;  // 16-byte granules per output row
-  const int64_t n = a.rows * gpr;
-  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n; e += int64_t(gridDim.x) * 256) {
-    const int64_t row = e / gpr;
+  const int gpr = a.ds * a.eo / 16;  // 16-byte granules per output row
+  const int64_t Tp = a.T / a.W * PC;
+  const int64_t n = a.B * a.T * a.H * gpr;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n; e += stride) {
+    const int64_t row = e / gpr;  // (b T + t) H + h
     const int g = int(e % gpr);
-    reinterpret_cast<uint4*>(a.o + row * 64 * a.eo)[g] = reinterpret_cast<const uint4*>(a.po + row * PD * a.eo)[g];
+    const int64_t h = row % a.H, bt = row / a.H, t = bt % a.T, b = bt / a.T;
+    const int64_t prow = (b * Tp + t / a.W * PC + t % a.W) * a.H + h;
+    reinterpret_cast<uint4*>(a.o + row * a.ds * a.eo)[g] = reinterpret_cast<const uint4*>(a.po + prow * PD * a.eo)[g];
   }
+  if (!a.pc) return;
   const int64_t ns = a.bh * 64 * (a.rb64 / 16);
-  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < ns; e += int64_t(gridDim.x) * 256) {
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < ns; e += stride) {
     const int64_t r = e / (a.rb64 / 16);  // bh * 64 + row
     const int g = int(e % (a.rb64 / 16));
     const int64_t bh = r / 64, rr = r % 64;
@@ -1228,63 +1268,85 @@ static size_t gdn_ws_128(const PrefillLaunch& L) {
 // d = 64 through a padded d = 128 head: q, k, v [3][rows][128] bf16, the
 // padded stored state and final state ([bh][128][RB128] + [bh][128] each),
 // the padded outputs [rows][128]; then the d = 128 workspace
+// The padded run: d = 128, 64-position chunks, T / W chunks per sequence.
+static bool gdn_padded(const PrefillLaunch& L) { return L.d_k == 64 || L.W < PC; }
+static PrefillLaunch gdn_padded_launch(const PrefillLaunch& L) {
+  PrefillLaunch L2 = L;
+  L2.d_k = L2.d_v = PD;
+  L2.T = L.T / L.W * PC;
+  L2.W = L2.C = PC;
+  return L2;
+}
 struct PadLayout {
-  size_t qkv, c0, s0, o, c, sc, inner, total;
+  size_t qkv, ab, c0, s0, o, c, sc, inner, total;
 };
 static PadLayout gdn_pad_layout(const PrefillLaunch& L) {
-  const size_t rows = size_t(L.B) * L.T * L.H, bh = size_t(L.B) * L.H;
+  const PrefillLaunch L2 = gdn_padded_launch(L);
+  const size_t rows = size_t(L.B) * L2.T * L.H, bh = size_t(L.B) * L.H;
   const size_t rb = L.q4 ? PD / 2 : PD, eo = L.out_bf16 ? 2 : 4;
+  const bool pad_ab = L.W < PC, pad_state = L.d_k == 64;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   PadLayout p{};
   p.qkv = 0;
-  p.c0 = p.qkv + up(3 * rows * PD * 2);
-  p.s0 = p.c0 + up(bh * PD * rb);
-  p.o = p.s0 + up(bh * PD * 4);
+  p.ab = p.qkv + up(3 * rows * PD * 2);
+  p.c0 = p.ab + (pad_ab ? up(2 * rows * 4) : 0);
+  p.s0 = p.c0 + (pad_state ? up(bh * PD * rb) : 0);
+  p.o = p.s0 + (pad_state ? up(bh * PD * 4) : 0);
   p.c = p.o + up(rows * PD * eo);
-  p.sc = p.c + up(bh * PD * rb);
-  p.inner = p.sc + up(bh * PD * 4);
-  PrefillLaunch L2 = L;
-  L2.d_k = L2.d_v = PD;
+  p.sc = p.c + (pad_state ? up(bh * PD * rb) : 0);
+  p.inner = p.sc + (pad_state ? up(bh * PD * 4) : 0);
   p.total = p.inner + gdn_ws_128(L2);
   return p;
 }
 
 size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L) {
-  if (L.d_k == 64) return gdn_pad_layout(L).total;
+  if (gdn_padded(L)) return gdn_pad_layout(L).total;
   return gdn_ws_128(L);
 }
 
 static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t stream);
 
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
-  if (L.d_k != 64) return launch_prefill_gdn128(L, stream);
-  // d = 64: pad, run the d = 128 kernels on the workspace copies, unpad
+  if (!gdn_padded(L)) return launch_prefill_gdn128(L, stream);
+  // pad, run the d = 128, 64-chunk kernels on the workspace copies, unpad
   const PadLayout P = gdn_pad_layout(L);
+  const PrefillLaunch L2p = gdn_padded_launch(L);
   char* ws = static_cast<char*>(L.workspace);
-  const int64_t rows = int64_t(L.B) * L.T * L.H, bh = int64_t(L.B) * L.H;
+  const int64_t rows = int64_t(L.B) * L2p.T * L.H, bh = int64_t(L.B) * L.H;
+  const bool pad_ab = L.W < PC, pad_state = L.d_k == 64;
   const int rb64 = L.q4 ? 32 : 64;
   uint16_t* pq = reinterpret_cast<uint16_t*>(ws + P.qkv);
+  float* pal = reinterpret_cast<float*>(ws + P.ab);
   PadArgs pa{{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v)},
-             {pq, pq + rows * PD, pq + 2 * rows * PD}, rows, L.init_codes, L.init_scales,
-             L.init_codes ? reinterpret_cast<int8_t*>(ws + P.c0) : nullptr, reinterpret_cast<float*>(ws + P.s0), bh, rb64};
+             {pq, pq + rows * PD, pq + 2 * rows * PD},
+             pad_ab ? L.alpha : nullptr, pad_ab ? L.beta : nullptr, pad_ab ? pal : nullptr, pad_ab ? pal + rows : nullptr,
+             L.B, L.T, L.H, L.W, L.d_k,
+             pad_state ? L.init_codes : nullptr, L.init_scales,
+             pad_state && L.init_codes ? reinterpret_cast<int8_t*>(ws + P.c0) : nullptr,
+             reinterpret_cast<float*>(ws + P.s0), bh, rb64};
   const int64_t work = rows * 48 > bh * PD * 8 ? rows * 48 : bh * PD * 8;
   const unsigned grid = unsigned(work / 256 + 1 < 4096 ? work / 256 + 1 : 4096);
   hipLaunchKernelGGL(gdn_pad_kernel, dim3(grid), dim3(256), 0, stream, pa);
   if (hipError_t e = hipGetLastError()) return e;
-  PrefillLaunch L2 = L;
-  L2.d_k = L2.d_v = PD;
+  PrefillLaunch L2 = L2p;
   L2.q = pa.y[0];
   L2.k = pa.y[1];
   L2.v = pa.y[2];
-  L2.init_codes = pa.pc0;
-  L2.init_scales = L.init_codes ? pa.ps0 : nullptr;
+  if (pad_ab) {
+    L2.alpha = pa.pa;
+    L2.beta = pa.pb;
+  }
+  if (pad_state) {
+    L2.init_codes = pa.pc0;
+    L2.init_scales = L.init_codes ? pa.ps0 : nullptr;
+    L2.codes = reinterpret_cast<int8_t*>(ws + P.c);
+    L2.scales = reinterpret_cast<float*>(ws + P.sc);
+  }
   L2.o = ws + P.o;
-  L2.codes = reinterpret_cast<int8_t*>(ws + P.c);
-  L2.scales = reinterpret_cast<float*>(ws + P.sc);
   L2.workspace = ws + P.inner;
   if (hipError_t e = launch_prefill_gdn128(L2, stream)) return e;
-  UnpadArgs ua{ws + P.o, static_cast<char*>(L.o), rows, L.out_bf16 ? 2 : 4, L2.codes, L2.scales, L.codes, L.scales,
-               bh, rb64};
+  UnpadArgs ua{ws + P.o, static_cast<char*>(L.o), L.B, L.T, L.H, L.W, L.d_k, L.out_bf16 ? 2 : 4,
+               pad_state ? L2.codes : nullptr, L2.scales, L.codes, L.scales, bh, rb64};
   hipLaunchKernelGGL(gdn_unpad_kernel, dim3(grid), dim3(256), 0, stream, ua);
   return hipGetLastError();
 }

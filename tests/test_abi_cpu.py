@@ -163,7 +163,8 @@ def _prefill(params, fake, **over):
 
 
 @pytest.mark.parametrize("params,status", [
-    (_pp(C=32, W=32), 2), (_pp(T=100), 2), (_pp(dk=64, dv=128), 2), (_pp(W=128), 2),
+    (_pp(C=8, W=8), 2), (_pp(T=100), 2), (_pp(dk=64, dv=128), 2), (_pp(W=128), 2), (_pp(W=48), 2),
+    (_pp(T=48, W=32, C=32), 2),           # not a whole number of windows
     (_pp(dk=64, dv=64, flags=1), 8),       # no rotation at d = 64
     (_pp(ind=0), 3), (_pp(outd=3), 3), (_pp(flags=4), 8), (_pp(flags=8), 8), (_pp(flags=16), 8),
     (_pp(flags=32), 8),
@@ -203,6 +204,23 @@ def test_prefill_ssd_contract():
     assert _prefill(ssd, f, codes=None, scales=None, state_f32=f()) == 2      # beta given
     assert _prefill(_pp(dk=64, dv=64, flags=2), f, beta=None, codes=None, scales=None,
                     state_f32=f()) == 2
+
+
+def test_window_and_chunk_sizes():
+    """GDN prefill takes windows and chunks of 16, 32 or 64.  A window
+    below 64 runs on padded copies (a larger workspace, growing as the window
+    shrinks); the chunk is a blocking hint that does not change the
+    workspace.  The hand-over, varlen and resume calls and SSD take 64."""
+    sz = {(W, C): L.gdnq_prefill_workspace_size(_pp(T=256, W=W, C=C)) for W in (16, 32, 64) for C in (16, 32, 64)}
+    assert all(v > 0 for v in sz.values())
+    for W in (16, 32, 64):
+        assert sz[(W, 16)] == sz[(W, 32)] == sz[(W, 64)]
+    assert sz[(16, 64)] > sz[(32, 64)] > sz[(64, 64)]
+    assert L.gdnq_prefill_workspace_size(_pp(T=48, W=16, C=16)) > 0
+    assert L.gdnq_prefill_handoff_workspace_size(_pp(T=256, W=32, C=32)) == 0
+    assert L.gdnq_prefill_handoff_workspace_size(_pp(T=256, W=64, C=32)) == 0
+    assert L.gdnq_prefill_workspace_size(_pp(T=256, dv=64, flags=2 | 4)) > 0
+    assert L.gdnq_prefill_workspace_size(_pp(T=256, dv=64, C=32, W=32, flags=2 | 4)) == 0  # SSD: chunk 64
 
 
 def test_workspace_size_is_queryable():
