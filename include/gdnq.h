@@ -81,14 +81,16 @@ enum {
   GDNQ_FLAG_INT8_QK = 4u, /* prefill + SSD only: quantize each token's
                              (rotated) q and k row to int8 with the codec
                              above and use the dequantized operands         */
-  GDNQ_FLAG_BUF_BF16 = 16u, /* decode only: the window buffer keeps keys and
+  GDNQ_FLAG_BUF_BF16 = 16u, /* decode and the prefill hand-over, varlen and
+                             resume calls: the window buffer keeps keys and
                              values as bf16 (buf_k, buf_v element type).  A
                              token's write enters its own step exactly and is
                              stored rounded to nearest even, so later steps
                              and the window's close replay the rounded write;
                              alpha and beta stay fp32.  Lossless when q, k, v
                              are bf16 and GDNQ_FLAG_WHT is off.              */
-  GDNQ_FLAG_BUF_FP8 = 32u, /* decode only: the window buffer keeps keys and
+  GDNQ_FLAG_BUF_FP8 = 32u, /* decode and the prefill hand-over, varlen and
+                             resume calls: the window buffer keeps keys and
                              values as FP8 vector pairs (Low-Bit GDN ...,
                              abstract): each buffered key and each value is
                              OCP E4M3 codes (bias 7, largest finite 448) with
@@ -303,11 +305,15 @@ gdnq_status gdnq_prefill_chunked_noalloc(const gdnq_prefill_params* p, const voi
  *   except that p->seqlen T need not be a multiple of 64.  With r = T mod 64:
  *     o          [B,T,H,128] out_dtype, every token (written)
  *     codes, scales: the state at the last window boundary (token T - r)
- *     buf_k      [B,H,W,128] fp32     buf_v [B,H,W,128] fp32   (slots < r written)
+ *     buf_k, buf_v  decode's window buffer [B,H,W,128] in the format the
+ *                flags select (slots < r written): fp32 (no flag), bf16
+ *                (GDNQ_FLAG_BUF_BF16: the bf16 inputs themselves), or FP8
+ *                vector pairs (GDNQ_FLAG_BUF_FP8: E4M3 codes, then the
+ *                per-vector fp32 scales, encoded as decode's append does)
  *     buf_alpha, buf_beta [B,H,W] fp32                        (slots < r written)
  *     fill_out   [B] int32 = r for every sequence (written)
  *   i.e. exactly decode's state after its last r steps: a decode step with
- *   fill_in = fill_out continues the sequence (fp32 window buffer).
+ *   fill_in = fill_out and the same buffer flag continues the sequence.
  *   workspace: gdnq_prefill_handoff_workspace_size(p) bytes.
  *   Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, FLAGS, WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */
@@ -316,7 +322,7 @@ size_t gdnq_prefill_handoff_workspace_size(const gdnq_prefill_params* p);
 gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, const void* k,
                                  const void* v, const float* alpha, const float* beta,
                                  const int8_t* init_codes, const float* init_scales, void* o,
-                                 int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                                 int8_t* codes, float* scales, void* buf_k, void* buf_v,
                                  float* buf_alpha, float* buf_beta, int32_t* fill_out,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
@@ -350,7 +356,7 @@ size_t gdnq_prefill_varlen_workspace_size(const gdnq_prefill_params* p);
 gdnq_status gdnq_prefill_varlen(const gdnq_prefill_params* p, const int32_t* cu_seqlens, const void* q,
                                 const void* k, const void* v, const float* alpha, const float* beta,
                                 const int8_t* init_codes, const float* init_scales, void* o,
-                                int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                                int8_t* codes, float* scales, void* buf_k, void* buf_v,
                                 float* buf_alpha, float* buf_beta, int32_t* fill_out,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
@@ -367,6 +373,7 @@ gdnq_status gdnq_prefill_varlen(const gdnq_prefill_params* p, const int32_t* cu_
  *   p->batch B = sequences; p->seqlen = new tokens per sequence (cu_seqlens
  *   NULL, q [B,T,H,128] ...) or packed new tokens in total (cu_seqlens as
  *   for gdnq_prefill_varlen, q [T,H,128] ...).  GDN mode only (flags 0 or GDNQ_FLAG_STATE_4BIT,
+ *   with one window-buffer format flag as for gdnq_prefill_handoff;
  *   d_k = d_v = 128, chunk = window = 64, in_dtype bf16).
  *     fill_in    [B] int32, device: buffered writes per sequence (0..63;
  *                other values are clamped into that range).  It may be the
@@ -374,11 +381,13 @@ gdnq_status gdnq_prefill_varlen(const gdnq_prefill_params* p, const int32_t* cu_
  *     codes, scales [B,H,128,128] int8 / [B,H,128] fp32: the state at the
  *                last window boundary on entry, at the new last boundary on
  *                return (updated in place).
- *     buf_k, buf_v [B,H,64,128] fp32, buf_alpha, buf_beta [B,H,64] fp32:
+ *     buf_k, buf_v [B,H,64,128] (fp32, bf16 or FP8 vector pairs, as the
+ *                flags select), buf_alpha, buf_beta [B,H,64] fp32:
  *                decode's window buffer on entry (slots < fill_in read; the
- *                keys and values enter the chunk products at bf16, exact
- *                when decode's inputs were bf16), the new open window's
- *                writes on return (slots < fill_out).
+ *                stored keys and values -- code * scale for FP8 -- enter the
+ *                chunk products rounded to bf16, exact when decode's inputs
+ *                were bf16 and the buffer fp32 or bf16), the new open
+ *                window's writes on return (slots < fill_out).
  *     o          new tokens' outputs, out_dtype (every new token written;
  *                the buffered writes have none: decode gave them).
  *     fill_out   [B] int32 = (fill_in + new tokens) mod 64 (written).
@@ -389,8 +398,8 @@ size_t gdnq_prefill_resume_workspace_size(const gdnq_prefill_params* p, int32_t 
 
 gdnq_status gdnq_prefill_resume(const gdnq_prefill_params* p, const int32_t* cu_seqlens, const int32_t* fill_in,
                                 const void* q, const void* k, const void* v, const float* alpha,
-                                const float* beta, void* o, int8_t* codes, float* scales, float* buf_k,
-                                float* buf_v, float* buf_alpha, float* buf_beta, int32_t* fill_out,
+                                const float* beta, void* o, int8_t* codes, float* scales, void* buf_k,
+                                void* buf_v, float* buf_alpha, float* buf_beta, int32_t* fill_out,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------

@@ -210,8 +210,12 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
       return fail(GDNQ_ERR_FLAGS, "SSD: GDNQ_FLAG_WHT requires GDNQ_FLAG_INT8_QK");
     if (dk != 128 || (dv != 64 && dv != 128)) return fail(GDNQ_ERR_SHAPE, "SSD: d_k = %d (128), d_v = %d (64 or 128)", dk, dv);
   } else {
-    if (p->flags & ~uint32_t(GDNQ_FLAG_STATE_4BIT | GDNQ_FLAG_WHT))
-      return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill takes GDNQ_FLAG_STATE_4BIT and GDNQ_FLAG_WHT", p->flags);
+    const uint32_t bufs = GDNQ_FLAG_BUF_BF16 | GDNQ_FLAG_BUF_FP8;
+    if (p->flags & ~uint32_t(GDNQ_FLAG_STATE_4BIT | GDNQ_FLAG_WHT | (handoff ? bufs : 0u)))
+      return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill takes GDNQ_FLAG_STATE_4BIT and GDNQ_FLAG_WHT (the hand-over, "
+                  "varlen and resume calls GDNQ_FLAG_STATE_4BIT and one window-buffer format flag)", p->flags);
+    if ((p->flags & bufs) == bufs)
+      return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_BUF_BF16 and GDNQ_FLAG_BUF_FP8 are exclusive");
     if ((p->flags & GDNQ_FLAG_WHT) && handoff)
       return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_WHT: gdnq_prefill_chunked only (not the hand-over, varlen or resume calls)");
     if (!((dk == 128 && dv == 128) || (dk == 64 && dv == 64)))
@@ -230,6 +234,8 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   L.int8_qk = (p->flags & GDNQ_FLAG_INT8_QK) != 0;
   L.q4 = !ssd && (p->flags & GDNQ_FLAG_STATE_4BIT) != 0;
   L.handoff = handoff;
+  L.buf_bf16 = handoff && (p->flags & GDNQ_FLAG_BUF_BF16) != 0;
+  L.buf_fp8 = handoff && (p->flags & GDNQ_FLAG_BUF_FP8) != 0;
   return GDNQ_OK;
 }
 
@@ -363,20 +369,24 @@ size_t gdnq_prefill_varlen_workspace_size(const gdnq_prefill_params* p) {
 static gdnq_status prefill_handoff_impl(gdnq::PrefillLaunch& L, const int32_t* cu_seqlens,
                                         const int32_t* fill_in, const void* q, const void* k, const void* v, const float* alpha,
                                         const float* beta, const int8_t* init_codes, const float* init_scales,
-                                        void* o, int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                                        void* o, int8_t* codes, float* scales, void* buf_k, void* buf_v,
                                         float* buf_alpha, float* buf_beta, int32_t* fill_out,
                                         void* workspace, size_t workspace_bytes, void* stream) {
   if (L.B == 0) return ok();
   // token-indexed arrays: B x T tokens, or T packed tokens of variable-length sequences
   const size_t bth = (cu_seqlens ? size_t(1) : size_t(L.B)) * L.T * L.H, bh = size_t(L.B) * L.H;
   const size_t eo = L.out_bf16 ? 2 : 4, W = size_t(L.W);
+  // window buffer bytes per key / value vector: fp32, bf16, or E4M3 codes
+  // (the per-vector fp32 scales follow all the codes in the same allocation)
+  const size_t bk_bytes = L.buf_fp8 ? bh * W * (L.d_k + 4) : bh * W * L.d_k * (L.buf_bf16 ? 2 : 4);
+  const size_t bv_bytes = L.buf_fp8 ? bh * W * (L.d_v + 4) : bh * W * L.d_v * (L.buf_bf16 ? 2 : 4);
   if ((init_codes == nullptr) != (init_scales == nullptr))
     return fail(GDNQ_ERR_NULL, "init_codes and init_scales must be both NULL or both set");
   const Span sp[] = {{"q", q, bth * L.d_k * 2},          {"k", k, bth * L.d_k * 2},
                      {"v", v, bth * L.d_v * 2},          {"alpha", alpha, bth * 4},
                      {"beta", beta, bth * 4},            {"o", o, bth * L.d_v * eo},
                      {"codes", codes, bh * L.d_v * L.d_k / (L.q4 ? 2 : 1)}, {"scales", scales, bh * L.d_v * 4},
-                     {"buf_k", buf_k, bh * W * L.d_k * 4}, {"buf_v", buf_v, bh * W * L.d_v * 4},
+                     {"buf_k", buf_k, bk_bytes},         {"buf_v", buf_v, bv_bytes},
                      {"buf_alpha", buf_alpha, bh * W * 4}, {"buf_beta", buf_beta, bh * W * 4},
                      {"fill_out", fill_out, size_t(L.B) * 4}};
   constexpr int N = sizeof(sp) / sizeof(sp[0]);
@@ -426,7 +436,7 @@ static gdnq_status prefill_handoff_impl(gdnq::PrefillLaunch& L, const int32_t* c
 gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, const void* k,
                                  const void* v, const float* alpha, const float* beta,
                                  const int8_t* init_codes, const float* init_scales, void* o,
-                                 int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                                 int8_t* codes, float* scales, void* buf_k, void* buf_v,
                                  float* buf_alpha, float* buf_beta, int32_t* fill_out,
                                  void* workspace, size_t workspace_bytes, void* stream) {
   gdnq::PrefillLaunch L;
@@ -438,7 +448,7 @@ gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, co
 gdnq_status gdnq_prefill_varlen(const gdnq_prefill_params* p, const int32_t* cu_seqlens, const void* q,
                                 const void* k, const void* v, const float* alpha, const float* beta,
                                 const int8_t* init_codes, const float* init_scales, void* o,
-                                int8_t* codes, float* scales, float* buf_k, float* buf_v,
+                                int8_t* codes, float* scales, void* buf_k, void* buf_v,
                                 float* buf_alpha, float* buf_beta, int32_t* fill_out,
                                 void* workspace, size_t workspace_bytes, void* stream) {
   gdnq::PrefillLaunch L;
@@ -468,8 +478,8 @@ size_t gdnq_prefill_resume_workspace_size(const gdnq_prefill_params* p, int32_t 
 
 gdnq_status gdnq_prefill_resume(const gdnq_prefill_params* p, const int32_t* cu_seqlens, const int32_t* fill_in,
                                 const void* q, const void* k, const void* v, const float* alpha,
-                                const float* beta, void* o, int8_t* codes, float* scales, float* buf_k,
-                                float* buf_v, float* buf_alpha, float* buf_beta, int32_t* fill_out,
+                                const float* beta, void* o, int8_t* codes, float* scales, void* buf_k,
+                                void* buf_v, float* buf_alpha, float* buf_beta, int32_t* fill_out,
                                 void* workspace, size_t workspace_bytes, void* stream) {
   gdnq::PrefillLaunch L;
   if (gdnq_status st = resume_validate(p, cu_seqlens != nullptr, L)) return st;

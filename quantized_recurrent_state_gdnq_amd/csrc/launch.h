@@ -58,8 +58,8 @@ struct PrefillLaunch {
   float* scales;
   float* state_f32;
   void* workspace;
-  float* buf_k;  // hand-over to decode (GDN): the open window's writes and the fill
-  float* buf_v;
+  void* buf_k;  // hand-over to decode (GDN): the open window's writes and the fill
+  void* buf_v;   // (fp32, bf16 or FP8 vector pairs as decode keeps them)
   float* buf_alpha;
   float* buf_beta;
   int32_t* fill_out;
@@ -68,6 +68,7 @@ struct PrefillLaunch {
   int B, T, H, d_k, d_v, C, W;
   bool out_bf16, wht, ssd, int8_qk, handoff, varlen, resume;
   bool q4;  // GDN: the state as packed 4-bit codes
+  bool buf_bf16, buf_fp8;  // hand-over: the window buffer's format
 };
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream);
 hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream);

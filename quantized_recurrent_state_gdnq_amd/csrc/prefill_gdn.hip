@@ -1152,14 +1152,19 @@ __global__ __launch_bounds__(1024) void gdn_seqmap_kernel(SeqMapArgs a) {
 // every prefill token; no query, no output), then its first new tokens, then
 // padding (k = q = v = 0, alpha = 1, beta = 0).  One workgroup per
 // (sequence, head).
+// Window-buffer formats of decode: 0 fp32, 1 bf16, 2 FP8 vector pairs (E4M3
+// codes; one fp32 scale per vector after all the codes).
 struct StageArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   const float* alpha;
   const float* beta;
-  const float* buf_k;
-  const float* buf_v;
+  const void* buf_k;
+  const void* buf_v;
+  const float* buf_ks;  // FP8: the vectors' scales
+  const float* buf_vs;
+  int fmt;
   const float* buf_alpha;
   const float* buf_beta;
   uint16_t* sk;
@@ -1179,12 +1184,26 @@ __global__ __launch_bounds__(256) void gdn_stage_kernel(StageArgs a) {
   for (int e = threadIdx.x; e < PC * PD / 2; e += 256) {  // two dims per thread
     const int pos = e / (PD / 2), d = 2 * (e % (PD / 2));
     uint32_t kw = 0u, qw = 0u, vw = 0u;
-    if (pos < pre) {
-      const size_t src = (size_t(bh) * a.W + pos) * PD + d;
-      const float2 kf = *reinterpret_cast<const float2*>(a.buf_k + src);
-      const float2 vf = *reinterpret_cast<const float2*>(a.buf_v + src);
-      kw = f32_to_bf16_bits(kf.x) | (f32_to_bf16_bits(kf.y) << 16);
-      vw = f32_to_bf16_bits(vf.x) | (f32_to_bf16_bits(vf.y) << 16);
+    if (pos < pre) {  // a buffered write enters at bf16 (exact for bf16 inputs)
+      const size_t slot = size_t(bh) * a.W + pos, src = slot * PD + d;
+      if (a.fmt == 1) {
+        kw = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.buf_k) + src);
+        vw = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.buf_v) + src);
+      } else {
+        float2 kf, vf;
+        if (a.fmt == 2) {  // the stored value: code * scale in fp32
+          const float2 kc = e4m3_unpack2(*reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.buf_k) + src), false);
+          const float2 vc = e4m3_unpack2(*reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.buf_v) + src), false);
+          const float ks = a.buf_ks[slot], vs = a.buf_vs[slot];
+          kf = make_float2(kc.x * ks, kc.y * ks);
+          vf = make_float2(vc.x * vs, vc.y * vs);
+        } else {
+          kf = *reinterpret_cast<const float2*>(static_cast<const float*>(a.buf_k) + src);
+          vf = *reinterpret_cast<const float2*>(static_cast<const float*>(a.buf_v) + src);
+        }
+        kw = f32_to_bf16_bits(kf.x) | (f32_to_bf16_bits(kf.y) << 16);
+        vw = f32_to_bf16_bits(vf.x) | (f32_to_bf16_bits(vf.y) << 16);
+      }
     } else if (pos - pre < n) {
       const size_t src = (tok0 + (pos - pre)) * HD + size_t(h) * PD + d;
       kw = *reinterpret_cast<const uint32_t*>(a.k + src);
@@ -1212,7 +1231,10 @@ __global__ __launch_bounds__(256) void gdn_stage_kernel(StageArgs a) {
 
 // Hand-over to decode: with r = len mod 64 for a sequence of len positions,
 // its last r positions' writes go to slots 0 .. r-1 of its window buffer
-// (fp32, keys in the state's basis) and its fill becomes r.  Slots that
+// (keys in the state's basis; fp32, bf16 -- the bf16 inputs themselves -- or
+// FP8 vector pairs encoded as decode's append does: scale = absmax / 448 and
+// codes nearest to x / scale, IEEE divisions, ties to even) and its fill
+// becomes r.  Slots that
 // already hold a buffered prefix write (when resuming, before any window
 // closed) are left as they are.  One workgroup per (sequence, head).
 struct HandoffArgs {
@@ -1220,8 +1242,11 @@ struct HandoffArgs {
   const uint16_t* v;
   const float* alpha;
   const float* beta;
-  float* buf_k;
-  float* buf_v;
+  void* buf_k;
+  void* buf_v;
+  float* buf_ks;  // FP8: the vectors' scales
+  float* buf_vs;
+  int fmt;
   float* buf_alpha;
   float* buf_beta;
   int32_t* fill_out;
@@ -1236,23 +1261,64 @@ __global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
   const int p0 = len - r;  // position of slot 0
   const int s0 = max(pre - p0, 0);  // first slot that takes a new token
   const size_t t0 = a.sm.tok0(b);
-  for (int e = threadIdx.x; e < (r - s0) * (PD / 8); e += 256) {  // 8 dims per thread
+  // 8 dims per thread: a slot's 16 threads are 16 consecutive lanes (the
+  // bound is a multiple of 16), so an FP8 vector's absmax is a 16-lane
+  // reduction inside one wave
+  for (int e = threadIdx.x; e < (r - s0) * (PD / 8); e += 256) {
     const int slot = s0 + e / (PD / 8), d = 8 * (e % (PD / 8));
     const size_t src = ((t0 + (p0 + slot - pre)) * a.H + h) * PD + d;
-    const size_t dst = (size_t(bh) * a.W + slot) * PD + d;
+    const size_t sl = size_t(bh) * a.W + slot, dst = sl * PD + d;
     const uint4 kw = *reinterpret_cast<const uint4*>(a.k + src);
     const uint4 vw = *reinterpret_cast<const uint4*>(a.v + src);
-    auto widen = [](uint32_t w, float& lo, float& hi) {
-      lo = __uint_as_float(w << 16);
-      hi = __uint_as_float(w & 0xffff0000u);
-    };
-    float4 k0, k1, v0, v1;
-    widen(kw.x, k0.x, k0.y); widen(kw.y, k0.z, k0.w); widen(kw.z, k1.x, k1.y); widen(kw.w, k1.z, k1.w);
-    widen(vw.x, v0.x, v0.y); widen(vw.y, v0.z, v0.w); widen(vw.z, v1.x, v1.y); widen(vw.w, v1.z, v1.w);
-    *reinterpret_cast<float4*>(a.buf_k + dst) = k0;
-    *reinterpret_cast<float4*>(a.buf_k + dst + 4) = k1;
-    *reinterpret_cast<float4*>(a.buf_v + dst) = v0;
-    *reinterpret_cast<float4*>(a.buf_v + dst + 4) = v1;
+    if (a.fmt == 1) {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.buf_k) + dst) = kw;
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.buf_v) + dst) = vw;
+      continue;
+    }
+    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, vv[4] = {vw.x, vw.y, vw.z, vw.w};
+    float kf[8], vf[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kf[2 * i] = bf16_lo(kk[i]);
+      kf[2 * i + 1] = bf16_hi(kk[i]);
+      vf[2 * i] = bf16_lo(vv[i]);
+      vf[2 * i + 1] = bf16_hi(vv[i]);
+    }
+    if (a.fmt == 2) {
+      float mk = 0.f, mv = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        mk = fmaxf(mk, fabsf(kf[i]));
+        mv = fmaxf(mv, fabsf(vf[i]));
+      }
+      const float sk = __fdiv_rn(group_max<16>(mk), 448.f);
+      const float sv = __fdiv_rn(group_max<16>(mv), 448.f);
+      uint32_t ck[2], cv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float c[4], w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c[j] = sk > 0.f ? e4m3_round(__fdiv_rn(kf[4 * i + j], sk)) : 0.f;
+          w[j] = sv > 0.f ? e4m3_round(__fdiv_rn(vf[4 * i + j], sv)) : 0.f;
+        }
+        ck[i] = e4m3_pack2(c[0], c[1]) | (e4m3_pack2(c[2], c[3]) << 16);
+        cv[i] = e4m3_pack2(w[0], w[1]) | (e4m3_pack2(w[2], w[3]) << 16);
+      }
+      *reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.buf_k) + dst) = make_uint2(ck[0], ck[1]);
+      *reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.buf_v) + dst) = make_uint2(cv[0], cv[1]);
+      if (d == 0) {
+        a.buf_ks[sl] = sk;
+        a.buf_vs[sl] = sv;
+      }
+      continue;
+    }
+    float* bk = static_cast<float*>(a.buf_k) + dst;
+    float* bv = static_cast<float*>(a.buf_v) + dst;
+    *reinterpret_cast<float4*>(bk) = make_float4(kf[0], kf[1], kf[2], kf[3]);
+    *reinterpret_cast<float4*>(bk + 4) = make_float4(kf[4], kf[5], kf[6], kf[7]);
+    *reinterpret_cast<float4*>(bv) = make_float4(vf[0], vf[1], vf[2], vf[3]);
+    *reinterpret_cast<float4*>(bv + 4) = make_float4(vf[4], vf[5], vf[6], vf[7]);
   }
   for (int slot = s0 + threadIdx.x; slot < r; slot += 256) {
     const size_t src = (t0 + (p0 + slot - pre)) * a.H + h;
@@ -1265,9 +1331,6 @@ __global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
 static size_t gdn_ws_128(const PrefillLaunch& L) {
   return gdn_ws_T(L) + gdn_ws_g(L) + gdn_ws_stage(L) + gdn_ws_map(L) + gdn_ws_rot(L);
 }
-// d = 64 through a padded d = 128 head: q, k, v [3][rows][128] bf16, the
-// padded stored state and final state ([bh][128][RB128] + [bh][128] each),
-// the padded outputs [rows][128]; then the d = 128 workspace
 // The padded run: d = 128, 64-position chunks, T / W chunks per sequence.
 static bool gdn_padded(const PrefillLaunch& L) { return L.d_k == 64 || L.W < PC; }
 static PrefillLaunch gdn_padded_launch(const PrefillLaunch& L) {
@@ -1351,6 +1414,12 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
   return hipGetLastError();
 }
 
+static int gdn_buf_fmt(const PrefillLaunch& L) { return L.buf_fp8 ? 2 : L.buf_bf16 ? 1 : 0; }
+// FP8 window buffer: the fp32 scales follow the B H W d code bytes
+static float* gdn_fp8_scales(const PrefillLaunch& L, void* codes) {
+  return L.buf_fp8 ? reinterpret_cast<float*>(static_cast<uint8_t*>(codes) + size_t(L.B) * L.H * L.W * PD) : nullptr;
+}
+
 static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t stream) {
   PrefillLaunch L = Lin;
   char* ws = static_cast<char*>(L.workspace);
@@ -1388,7 +1457,8 @@ static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t st
       float* sa = reinterpret_cast<float*>(sv + nstage * PD);
       float* sb = sa + nstage;
       StageArgs g{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k),
-                  static_cast<const uint16_t*>(L.v), L.alpha, L.beta, L.buf_k, L.buf_v, L.buf_alpha,
+                  static_cast<const uint16_t*>(L.v), L.alpha, L.beta, L.buf_k, L.buf_v,
+                  gdn_fp8_scales(L, L.buf_k), gdn_fp8_scales(L, L.buf_v), gdn_buf_fmt(L), L.buf_alpha,
                   L.buf_beta, sk, sq, sv, sa, sb, sm, L.B, L.H, L.W};
       g.sm.pre = pre;  // the staging kernel reads the prefixes, not yet the staged copy
       hipLaunchKernelGGL(gdn_stage_kernel, dim3(unsigned(L.B) * L.H), dim3(256), 0, stream, g);
@@ -1419,7 +1489,8 @@ static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t st
   if (hipError_t e = hipGetLastError()) return e;
   if (L.handoff && L.B > 0) {
     HandoffArgs h{static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v), L.alpha, L.beta,
-                  L.buf_k, L.buf_v, L.buf_alpha, L.buf_beta, L.fill_out, sm, L.B, L.H, L.W};
+                  L.buf_k, L.buf_v, gdn_fp8_scales(L, L.buf_k), gdn_fp8_scales(L, L.buf_v), gdn_buf_fmt(L),
+                  L.buf_alpha, L.buf_beta, L.fill_out, sm, L.B, L.H, L.W};
     hipLaunchKernelGGL(gdn_handoff_kernel, dim3(unsigned(L.B) * L.H), dim3(256), 0, stream, h);
     return hipGetLastError();
   }

@@ -47,11 +47,20 @@ def _shape(t, shape, name):
     return t
 
 
+_BUF_FLAGS = {torch.float32: 0, torch.bfloat16: _lib.GDNQ_FLAG_BUF_BF16,
+              torch.float8_e4m3fn: _lib.GDNQ_FLAG_BUF_FP8}
+
+
 def _state_shapes(st, B, H, d_k, d_v, window):
-    """A DecodeState handed to a prefill entry point: fp32 window buffer of
-    `window` slots, codes/scales/fill of B sequences."""
-    if st.buf_k.dtype != torch.float32:
-        raise ValueError("state: the prefill hand-over writes an fp32 window buffer")
+    """A DecodeState handed to a prefill entry point: a window buffer of
+    `window` slots (fp32, bf16 or FP8 vector pairs), codes/scales/fill of B
+    sequences.  Returns the window-buffer format flag."""
+    if st.buf_k.dtype not in _BUF_FLAGS or st.buf_v.dtype != st.buf_k.dtype:
+        raise ValueError("state: window buffers of fp32, bf16 or float8_e4m3fn (both alike)")
+    if getattr(st, "sliding", False):
+        raise ValueError("state: the prefill hand-over fills a tumbling window, not a sliding one")
+    if st.wht:
+        raise ValueError("state: the prefill hand-over runs without the rotation (its keys stay unrotated)")
     if st.window != window:
         raise ValueError(f"state: window {st.window}, the prefill hand-over needs {window}")
     _shape(st.codes, (B, H, d_v, d_k * st.state_bits // 8), "state.codes")
@@ -61,6 +70,7 @@ def _state_shapes(st, B, H, d_k, d_v, window):
     _shape(st.buf_alpha, (B, H, window), "state.buf_alpha")
     _shape(st.buf_beta, (B, H, window), "state.buf_beta")
     _shape(st.fill, (B,), "state.fill")
+    return _BUF_FLAGS[st.buf_k.dtype]
 
 
 def quantize_state(S, codes=None, scales=None, wht=False, state_bits=8):
@@ -162,12 +172,12 @@ def decode_step(q, k, v, alpha, beta, codes, scales, buf_k, buf_v, buf_alpha, bu
     return o
 
 
-def _prefill_params(q, v, *, window, chunk, wht, ssd, int8_qk, out_dtype, state_bits=8):
+def _prefill_params(q, v, *, window, chunk, wht, ssd, int8_qk, out_dtype, state_bits=8, extra_flags=0):
     B, T, H, d_k = q.shape
     d_v = v.shape[-1]
     flags = ((_lib.GDNQ_FLAG_WHT if wht else 0) | (_lib.GDNQ_FLAG_SSD if ssd else 0)
              | (_lib.GDNQ_FLAG_INT8_QK if int8_qk else 0)
-             | (_lib.GDNQ_FLAG_STATE_4BIT if state_bits == 4 else 0))
+             | (_lib.GDNQ_FLAG_STATE_4BIT if state_bits == 4 else 0) | extra_flags)
     return _lib.PrefillParams(B, T, H, d_k, d_v, chunk, window, _DT[q.dtype], _DT[out_dtype], flags)
 
 
@@ -263,13 +273,14 @@ def prefill_handoff_workspace_size(q, v, *, window=64, out_dtype=torch.bfloat16)
 
 
 def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_scales=None,
-                    out_dtype=torch.bfloat16, o=None, state=None, workspace=None, state_bits=8):
+                    out_dtype=torch.bfloat16, o=None, state=None, workspace=None, state_bits=8,
+                    buf_dtype=torch.float32):
     """GDN prefill of any T tokens handed over to decode (see
     gdnq_prefill_handoff in include/gdnq.h): returns (o, DecodeState) whose
-    codes/scales are the state at the last window boundary and whose fp32
-    window buffer holds the last T mod 64 writes, with that fill.  o, state
-    (a DecodeState with an fp32 buffer) and workspace may be given to reuse
-    their memory."""
+    codes/scales are the state at the last window boundary and whose window
+    buffer (fp32, bf16 or FP8 vector pairs: buf_dtype, or the given state's)
+    holds the last T mod 64 writes, with that fill.  o, state and workspace
+    may be given to reuse their memory."""
     dev = q.device
     B, T, H, d_k = q.shape
     d_v = v.shape[-1]
@@ -280,8 +291,6 @@ def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_sc
     if (tuple(k.shape) != (B, T, H, d_k) or tuple(v.shape) != (B, T, H, d_v)
             or tuple(alpha.shape) != (B, T, H) or tuple(beta.shape) != (B, T, H)):
         raise ValueError("inconsistent prefill shapes")
-    p = _prefill_params(q, v, window=window, chunk=64, wht=False, ssd=False, int8_qk=False,
-                        out_dtype=out_dtype, state_bits=state_bits)
     if o is None:
         o = torch.empty((B, T, H, d_v), dtype=out_dtype, device=dev)
     _shape(_need(o, "o", out_dtype, dev), (B, T, H, d_v), "o")
@@ -290,10 +299,13 @@ def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_sc
     if st is None:
         st = DecodeState(torch.empty((B, H, d_v, d_k * state_bits // 8), dtype=torch.int8, device=dev),
                          torch.empty((B, H, d_v), dtype=torch.float32, device=dev), window,
-                         fill=torch.zeros(B, dtype=torch.int32, device=dev), state_bits=state_bits)
+                         fill=torch.zeros(B, dtype=torch.int32, device=dev), state_bits=state_bits,
+                         buf_dtype=buf_dtype)
     if st.state_bits != state_bits:
         raise ValueError("state: its code width differs from state_bits")
-    _state_shapes(st, B, H, d_k, d_v, 64)
+    p = _prefill_params(q, v, window=window, chunk=64, wht=False, ssd=False, int8_qk=False,
+                        out_dtype=out_dtype, state_bits=state_bits,
+                        extra_flags=_state_shapes(st, B, H, d_k, d_v, 64))
     need = int(_lib.prefill_handoff_workspace_size(p))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -306,10 +318,10 @@ def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_sc
     return o, st
 
 
-def _varlen_params(q, v, n_seqs, *, window, out_dtype, state_bits=8):
+def _varlen_params(q, v, n_seqs, *, window, out_dtype, state_bits=8, extra_flags=0):
     T, H, d_k = q.shape
     return _lib.PrefillParams(n_seqs, T, H, d_k, v.shape[-1], 64, window, _DT[q.dtype],
-                              _DT[out_dtype], _lib.GDNQ_FLAG_STATE_4BIT if state_bits == 4 else 0)
+                              _DT[out_dtype], (_lib.GDNQ_FLAG_STATE_4BIT if state_bits == 4 else 0) | extra_flags)
 
 
 def prefill_varlen_workspace_size(q, v, n_seqs, *, window=64, out_dtype=torch.bfloat16):
@@ -319,12 +331,13 @@ def prefill_varlen_workspace_size(q, v, n_seqs, *, window=64, out_dtype=torch.bf
 
 def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=None,
                    init_scales=None, out_dtype=torch.bfloat16, o=None, state=None,
-                   workspace=None, state_bits=8):
+                   workspace=None, state_bits=8, buf_dtype=torch.float32):
     """GDN prefill of a packed batch of variable-length sequences handed over
     to decode (see gdnq_prefill_varlen in include/gdnq.h).  q, k [T,H,d_k],
     v [T,H,d_v] bf16 and alpha, beta [T,H] fp32 hold the sequences back to
     back; cu_seqlens (int32 on the device, B+1 entries) gives where each
-    starts.  Returns (o [T,H,d_v], DecodeState of B sequences)."""
+    starts.  Returns (o [T,H,d_v], DecodeState of B sequences; its window
+    buffer of buf_dtype, or the given state's)."""
     dev = q.device
     T, H, d_k = q.shape
     d_v = v.shape[-1]
@@ -339,7 +352,6 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=No
     if (tuple(k.shape) != (T, H, d_k) or tuple(v.shape) != (T, H, d_v)
             or tuple(alpha.shape) != (T, H) or tuple(beta.shape) != (T, H)):
         raise ValueError("inconsistent packed prefill shapes")
-    p = _varlen_params(q, v, B, window=window, out_dtype=out_dtype, state_bits=state_bits)
     if o is None:
         o = torch.empty((T, H, d_v), dtype=out_dtype, device=dev)
     _shape(_need(o, "o", out_dtype, dev), (T, H, d_v), "o")
@@ -348,10 +360,12 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=No
     if st is None:
         st = DecodeState(torch.empty((B, H, d_v, d_k * state_bits // 8), dtype=torch.int8, device=dev),
                          torch.empty((B, H, d_v), dtype=torch.float32, device=dev), window,
-                         fill=torch.zeros(B, dtype=torch.int32, device=dev), state_bits=state_bits)
+                         fill=torch.zeros(B, dtype=torch.int32, device=dev), state_bits=state_bits,
+                         buf_dtype=buf_dtype)
     if st.state_bits != state_bits:
         raise ValueError("state: its code width differs from state_bits")
-    _state_shapes(st, B, H, d_k, d_v, 64)
+    p = _varlen_params(q, v, B, window=window, out_dtype=out_dtype, state_bits=state_bits,
+                       extra_flags=_state_shapes(st, B, H, d_k, d_v, 64))
     need = int(_lib.prefill_varlen_workspace_size(p))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -375,8 +389,8 @@ def prefill_resume_workspace_size(q, v, n_seqs, *, packed=False, out_dtype=torch
 
 def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=torch.bfloat16,
                    o=None, workspace=None):
-    """Continue every sequence of a DecodeState (fp32 window buffer, window
-    64) with new tokens by chunked prefill, at whatever fill each sequence
+    """Continue every sequence of a DecodeState (window 64; fp32, bf16 or FP8
+    window buffer, whose writes enter at bf16) with new tokens by chunked prefill, at whatever fill each sequence
     is (see gdnq_prefill_resume in include/gdnq.h).  Uniform: q, k
     [B,T,H,d_k], v [B,T,H,d_v], alpha, beta [B,T,H]; packed: [T,...] with
     cu_seqlens (int32, B+1 offsets).  Updates the state in place (codes,
@@ -385,7 +399,7 @@ def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=to
     st = state
     B, H, d_v, d_k = st.codes.shape
     d_k = d_k * 8 // st.state_bits
-    _state_shapes(st, B, H, d_k, d_v, 64)
+    buf_flag = _state_shapes(st, B, H, d_k, d_v, 64)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, torch.bfloat16, dev)
     for name, t in (("alpha", alpha), ("beta", beta)):
@@ -406,7 +420,7 @@ def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=to
             or tuple(beta.shape) != lead + (H,)):
         raise ValueError("inconsistent resume shapes")
     p = _lib.PrefillParams(B, T, H, d_k, d_v, 64, 64, _DT[q.dtype], _DT[out_dtype],
-                           _lib.GDNQ_FLAG_STATE_4BIT if st.state_bits == 4 else 0)
+                           (_lib.GDNQ_FLAG_STATE_4BIT if st.state_bits == 4 else 0) | buf_flag)
     if o is None:
         o = torch.empty(lead + (H, d_v), dtype=out_dtype, device=dev)
     _shape(_need(o, "o", out_dtype, dev), lead + (H, d_v), "o")

@@ -273,6 +273,8 @@ def _handoff(params, fake, **over):
     (_pp(C=32, W=32), 2), (_pp(dk=64, dv=64), 2), (_pp(W=128), 2), (_pp(ind=0), 3),
     (_pp(flags=1), 8), (_pp(dv=64, flags=2 | 1 | 4), 8),   # GDN only
     (_pp(T=1 << 20, H=8192), 2),                           # one sequence's outputs past 4 GiB
+    (_pp(flags=16 | 32), 8),                               # one window-buffer format
+    (_pp(W=32, C=64), 2),                                  # decode's window: 64
 ])
 def test_handoff_rejects_bad_params(params, status):
     assert _handoff(params, Fake()) == status
@@ -294,6 +296,41 @@ def test_handoff_contract():
     assert _handoff(p, f, k=k, fill_out=k) == 5                 # output over an input
     assert _handoff(_pp(B=0, T=100), f) == 0                    # empty batch: no-op
     assert _lib.prefill_workspace_size(p) == 0                  # the chunked prefill rejects T = 100
+
+
+def test_handoff_buffer_formats():
+    """GDNQ_FLAG_BUF_BF16 / GDNQ_FLAG_BUF_FP8 select decode's window-buffer
+    formats for the hand-over, varlen and resume calls (not the chunked
+    prefill).  The buffer spans follow the format: a buf_v placed right after
+    a bf16-sized buf_k is disjoint from it under the bf16 flag and overlaps
+    an fp32 buf_k; an FP8 buffer holds B H W d code bytes then B H W fp32
+    scales."""
+    B, T, H, d, W = 2, 100, 3, 128, 64
+    for flags in (16, 32):
+        p = _pp(B=B, T=T, H=H, flags=flags)
+        ws = _lib.prefill_handoff_workspace_size(p)
+        assert ws == _lib.prefill_handoff_workspace_size(_pp(B=B, T=T, H=H)) > 0
+        assert _lib.prefill_varlen_workspace_size(p) > 0
+        assert _lib.prefill_resume_workspace_size(p, 0) > 0
+        assert _lib.prefill_workspace_size(_pp(B=B, T=128, H=H, flags=flags)) == 0
+    f = Fake()
+    k = f(1 << 26)
+    o = f()
+    wsp = f()
+    ws = _lib.prefill_handoff_workspace_size(_pp(B=B, T=T, H=H))
+    # bf16: buf_v right after a bf16 buf_k is fine (only the planted o / fill_out overlap is reported)
+    st = _handoff(_pp(B=B, T=T, H=H, flags=16), f, buf_k=k, buf_v=k + B * H * W * d * 2, o=o, fill_out=o,
+                  workspace=wsp, ws=ws)
+    assert st == 5 and b"buf" not in L.gdnq_last_error(), L.gdnq_last_error()
+    assert _handoff(_pp(B=B, T=T, H=H, flags=0), f, buf_k=k, buf_v=k + B * H * W * d * 2, workspace=wsp,
+                    ws=ws) == 5
+    assert b"buf_k overlaps buf_v" in L.gdnq_last_error() or b"buf_v overlaps buf_k" in L.gdnq_last_error()
+    # FP8: codes then scales
+    st = _handoff(_pp(B=B, T=T, H=H, flags=32), f, buf_k=k, buf_v=k + B * H * W * (d + 4), o=o, fill_out=o,
+                  workspace=wsp, ws=ws)
+    assert st == 5 and b"buf" not in L.gdnq_last_error(), L.gdnq_last_error()
+    assert _handoff(_pp(B=B, T=T, H=H, flags=32), f, buf_k=k, buf_v=k + B * H * W * (d + 4) - 16, workspace=wsp,
+                    ws=ws) == 5
 
 
 # ---------------------------------------------------------------- variable-length prefill
