@@ -42,11 +42,22 @@ def test_state_shapes_rejects(kw, args):
         ops._state_shapes(_state(**kw), *args)
 
 
-def test_state_shapes_rejects_low_precision_buffer():
+def test_state_shapes_buffer_formats():
+    """The hand-over takes decode's fp32, bf16 and FP8 window buffers (the
+    format flag it returns goes into the call), not a rotated or a sliding
+    state, nor key and value buffers of different types."""
     codes = torch.zeros((2, 2, 128, 128), dtype=torch.int8)
+    for dt, flag in ((torch.float32, 0), (torch.bfloat16, 16), (torch.float8_e4m3fn, 32)):
+        st = ops.DecodeState(codes, torch.zeros((2, 2, 128)), 64, buf_dtype=dt)
+        assert ops._state_shapes(st, 2, 2, 128, 128, 64) == flag
     st = ops.DecodeState(codes, torch.zeros((2, 2, 128)), 64, buf_dtype=torch.bfloat16)
-    with pytest.raises(ValueError, match="fp32 window buffer"):
+    st.buf_v = torch.zeros((2, 2, 64, 128), dtype=torch.float32)
+    with pytest.raises(ValueError, match="both alike"):
         ops._state_shapes(st, 2, 2, 128, 128, 64)
+    with pytest.raises(ValueError, match="rotation"):
+        ops._state_shapes(ops.DecodeState(codes, torch.zeros((2, 2, 128)), 64, wht=True), 2, 2, 128, 128, 64)
+    with pytest.raises(ValueError, match="sliding"):
+        ops._state_shapes(ops.DecodeState(codes, torch.zeros((2, 2, 128)), 64, sliding=True), 2, 2, 128, 128, 64)
 
 
 gpu = pytest.mark.gpu
