@@ -274,8 +274,8 @@ gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, co
  *   allocates nothing, neither device nor host memory.
  *     - A call whose gdnq_prefill_workspace_size(p) exceeds
  *       GDNQ_NOALLOC_SCRATCH_BYTES is rejected with GDNQ_ERR_WORKSPACE
- *       before anything is launched (e.g. GDN: 24,832 bytes per chunk-head,
- *       so B * (T / 64) * H <= 2702; SSD with GDNQ_FLAG_INT8_QK: 264 bytes
+ *       before anything is launched (e.g. GDN: 15,616 bytes per chunk-head,
+ *       so B * (T / 64) * H <= 4297; SSD with GDNQ_FLAG_INT8_QK: 264 bytes
  *       per token-head).
  *     - Every call on one GPU shares that GPU's array: calls that overlap
  *       in time on one GPU (on different streams, or from different host
