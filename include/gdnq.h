@@ -43,7 +43,12 @@
  *   - Floating-point data errors (NaN/Inf inputs, ||k|| != 1, beta outside
  *     [0,1]) are not checked; results are then unspecified.
  *   - No C++ exception crosses this interface.  Calls are reentrant.
- *   - Device faults surface on the caller's next synchronisation.
+ *   - Device faults surface on the caller's next synchronisation, unless
+ *     the environment variable GDNQ_SYNC_DEBUG is "1" when the library is
+ *     loaded: then every call waits for its own kernels on its stream before
+ *     it returns, and reports a fault of theirs as GDNQ_ERR_HIP with the
+ *     call's name in gdnq_last_error() (a debugging aid: it serializes the
+ *     caller's stream).  gdnq_sync_debug() tells which mode is in force.
  */
 #ifndef GDNQ_H
 #define GDNQ_H
@@ -414,10 +419,13 @@ gdnq_status gdnq_prefill_resume(const gdnq_prefill_params* p, const int32_t* cu_
  * ------------------------------------------------------------------------ */
 gdnq_status gdnq_decode_set_schedule(int32_t grid, int32_t open_waves);
 
-/* Status text, last error detail (thread-local, "" if none), library version. */
+/* Status text, last error detail (thread-local, "" if none), library version,
+ * and 1 when GDNQ_SYNC_DEBUG=1 was set at load (every call synchronizes its
+ * stream and reports its kernels' faults itself), else 0. */
 const char* gdnq_status_string(gdnq_status s);
 const char* gdnq_last_error(void);
 int32_t gdnq_version(void);
+int32_t gdnq_sync_debug(void);
 
 #ifdef __cplusplus
 }

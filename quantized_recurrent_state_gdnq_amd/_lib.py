@@ -28,7 +28,8 @@ EXPORTS = ("gdnq_quantize_state", "gdnq_decode_step", "gdnq_prefill_workspace_si
            "gdnq_prefill_chunked", "gdnq_prefill_chunked_noalloc", "gdnq_prefill_handoff_workspace_size", "gdnq_prefill_handoff",
            "gdnq_prefill_varlen_workspace_size", "gdnq_prefill_varlen",
            "gdnq_prefill_resume_workspace_size", "gdnq_prefill_resume",
-           "gdnq_decode_set_schedule", "gdnq_status_string", "gdnq_last_error", "gdnq_version")
+           "gdnq_decode_set_schedule", "gdnq_status_string", "gdnq_last_error", "gdnq_version",
+           "gdnq_sync_debug")
 
 
 class DecodeParams(ctypes.Structure):
@@ -93,6 +94,8 @@ def _load():
     lib.gdnq_last_error.restype = ctypes.c_char_p
     lib.gdnq_version.argtypes = []
     lib.gdnq_version.restype = i32
+    lib.gdnq_sync_debug.argtypes = []
+    lib.gdnq_sync_debug.restype = i32
     return lib
 
 

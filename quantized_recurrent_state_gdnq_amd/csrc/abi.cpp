@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "launch.h"
@@ -60,6 +61,24 @@ gdnq_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// GDNQ_SYNC_DEBUG=1 in the environment when the library is loaded: every call
+// waits for its kernels on its stream and reports a fault of theirs as its own
+// GDNQ_ERR_HIP, naming the call, instead of leaving it to the caller's next
+// synchronization.  Read once; the default is fully asynchronous.
+const bool g_sync_debug = [] {
+  const char* e = std::getenv("GDNQ_SYNC_DEBUG");
+  return e && e[0] == '1' && e[1] == '\0';
+}();
+
+gdnq_status launched(hipError_t e, const char* what, void* stream) {
+  if (e == hipSuccess && g_sync_debug) {
+    e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return fail(GDNQ_ERR_HIP, "%s (synchronized under GDNQ_SYNC_DEBUG): %s", what, hipGetErrorString(e));
+  }
+  return hip_status(e, what);
+}
+
 bool dim_ok(int d) { return d == 64 || d == 128; }
 size_t esize(int32_t dt) { return dt == GDNQ_BF16 ? 2 : 4; }
 
@@ -86,6 +105,8 @@ const char* gdnq_last_error(void) { return g_err; }
 
 int32_t gdnq_version(void) { return 101; }
 
+int32_t gdnq_sync_debug(void) { return g_sync_debug ? 1 : 0; }
+
 gdnq_status gdnq_decode_set_schedule(int32_t grid, int32_t open_waves) {
   if (grid < 0 || open_waves < 0)
     return fail(GDNQ_ERR_SHAPE, "grid = %d, open_waves = %d: 0 (default) or positive", grid, open_waves);
@@ -109,7 +130,7 @@ gdnq_status gdnq_quantize_state(const float* S, int64_t rows, int32_t d_k, int8_
     return fail(GDNQ_ERR_ALIAS, "S, codes and scales must not overlap");
   clear_stale_hip_error();
   gdnq::QuantizeLaunch L{S, rows, d_k, codes, scales, (flags & GDNQ_FLAG_WHT) != 0, q4};
-  return hip_status(gdnq::launch_quantize(L, static_cast<hipStream_t>(stream)), "quantize launch");
+  return launched(gdnq::launch_quantize(L, static_cast<hipStream_t>(stream)), "quantize launch", stream);
 }
 
 gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const void* k,
@@ -175,7 +196,7 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
                        dk,       dv,       W,       p->in_dtype == GDNQ_BF16,
                        p->out_dtype == GDNQ_BF16, (p->flags & GDNQ_FLAG_WHT) != 0, buf_bf16, buf_fp8, q4,
                        sliding};
-  return hip_status(gdnq::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch");
+  return launched(gdnq::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch", stream);
 }
 
 static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillLaunch& L, bool handoff = false) {
@@ -326,7 +347,7 @@ static gdnq_status prefill_chunked_impl(const gdnq_prefill_params* p, const void
   L.q = q; L.k = k; L.v = v; L.alpha = alpha; L.o = o; L.state_f32 = state_f32; L.workspace = workspace;
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_stale_hip_error();
-  return hip_status(L.ssd ? gdnq::launch_prefill_ssd(L, s) : gdnq::launch_prefill_gdn(L, s), "prefill launch");
+  return launched(L.ssd ? gdnq::launch_prefill_ssd(L, s) : gdnq::launch_prefill_gdn(L, s), "prefill launch", stream);
 }
 
 gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, const void* k,
@@ -430,7 +451,7 @@ static gdnq_status prefill_handoff_impl(gdnq::PrefillLaunch& L, const int32_t* c
   L.workspace = workspace;
   L.buf_k = buf_k; L.buf_v = buf_v; L.buf_alpha = buf_alpha; L.buf_beta = buf_beta; L.fill_out = fill_out;
   clear_stale_hip_error();
-  return hip_status(gdnq::launch_prefill_gdn(L, static_cast<hipStream_t>(stream)), "prefill hand-over launch");
+  return launched(gdnq::launch_prefill_gdn(L, static_cast<hipStream_t>(stream)), "prefill hand-over launch", stream);
 }
 
 gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, const void* k,

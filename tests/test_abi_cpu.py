@@ -35,6 +35,22 @@ def test_version_and_status_strings():
         assert L.gdnq_status_string(s)
 
 
+def test_sync_debug_mode_read_at_load():
+    """GDNQ_SYNC_DEBUG=1 at load switches every call to synchronize its
+    stream; any other value, or none, leaves the library asynchronous."""
+    import subprocess
+    import sys
+    code = "from quantized_recurrent_state_gdnq_amd import _lib; print(_lib.lib.gdnq_sync_debug())"
+    for val, want in (("1", "1"), ("0", "0"), ("yes", "0"), (None, "0")):
+        env = {k: v for k, v in os.environ.items() if k != "GDNQ_SYNC_DEBUG"}
+        if val is not None:
+            env["GDNQ_SYNC_DEBUG"] = val
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT,
+                           timeout=300)
+        assert r.returncode == 0, r.stderr[-2000:]
+        assert r.stdout.strip() == want, (val, r.stdout)
+
+
 class Fake:
     """Distinct, 16-byte-aligned, never-dereferenced addresses."""
 
