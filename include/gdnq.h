@@ -72,6 +72,9 @@ typedef enum {
   GDNQ_ERR_FLAGS = 8      /* unknown or unsupported flag bits                  */
 } gdnq_status;
 
+/* Largest prefill window (tokens). */
+#define GDNQ_MAX_WINDOW (1 << 24)
+
 /* Element types of q, k, v (in_dtype) and of o (out_dtype). */
 enum { GDNQ_F32 = 0, GDNQ_BF16 = 1 };
 
@@ -86,6 +89,11 @@ enum {
   GDNQ_FLAG_INT8_QK = 4u, /* prefill + SSD only: quantize each token's
                              (rotated) q and k row to int8 with the codec
                              above and use the dequantized operands         */
+  GDNQ_FLAG_NO_REQUANT = 8u, /* gdnq_prefill_chunked, GDN only (a reference
+                             mode for tests): never requantize; the state
+                             starts from init_codes/init_scales (or zero) and
+                             the final fp32 state goes to state_f32 (codes
+                             and scales NULL); any T (window ignored)        */
   GDNQ_FLAG_BUF_BF16 = 16u, /* decode and the prefill hand-over, varlen and
                              resume calls: the window buffer keeps keys and
                              values as bf16 (buf_k, buf_v element type).  A
@@ -218,15 +226,20 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
  *   GDN (flags without GDNQ_FLAG_SSD): the gated delta rule over T tokens
  *   from the stored state (init_codes/init_scales, or zero when both are
  *   NULL), requantizing at every window end, windows aligned to token 0.
- *   Supported: d_k = d_v in {128, 64} (GDNQ_FLAG_WHT at 128 only), window
- *   W in {16, 32, 64}, chunk in {16, 32, 64}, T a multiple of W.  The
- *   kernels run every window as one 64-position chunk (a shorter window is
- *   padded with writes that leave the state unchanged; d = 64 runs as a
- *   zero-padded d = 128 head), so the result depends on the window, not on
- *   the chunk, which is a blocking hint.  Padded runs need a larger
- *   workspace.  Writes o and the final codes/scales (the state after the
- *   last window).
- *   state_f32 must be NULL.  Flags: GDNQ_FLAG_STATE_4BIT (init_codes and
+ *   Supported: d_k = d_v in {128, 64} (GDNQ_FLAG_WHT at 128 only), chunk
+ *   in {16, 32, 64}, any window 1 <= W <= GDNQ_MAX_WINDOW, T a multiple of
+ *   W.  The kernels run every window as
+ *   whole 64-position chunks (a window that is not a multiple of 64 is
+ *   padded at its end with writes that leave the state unchanged; d = 64
+ *   runs as a zero-padded d = 128 head; between the chunks of one window
+ *   the state stays fp32), so the result depends on the window, not on the
+ *   chunk, which is a blocking hint.  Padded runs need a larger workspace.
+ *   Writes o and the final codes/scales (the state after the last window);
+ *   state_f32 must be NULL, except under GDNQ_FLAG_NO_REQUANT, which
+ *   writes the final fp32 state there instead of codes/scales (which must
+ *   then be NULL; any T; init_codes must not overlap state_f32; the state
+ *   is in the rotated basis under GDNQ_FLAG_WHT).
+ *   Flags: GDNQ_FLAG_STATE_4BIT (init_codes and
  *   codes then hold packed 4-bit codes, [B,H,d_v,d_k/2] bytes, and every
  *   window end requantizes with the 4-bit codec) and/or GDNQ_FLAG_WHT: every
  *   q and k row is rotated by H/sqrt(128) in fp32 and rounded to bf16
@@ -248,7 +261,7 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
  *       alias codes/scales for an in-place continuation)
  *     o      [B,T,H,d_v] out_dtype    (written)
  *     codes  [B,H,d_v,d_k] int8, scales [B,H,d_v] fp32 (GDN, written)
- *     state_f32 [B,H,d_v,d_k] fp32 (SSD, written)
+ *     state_f32 [B,H,d_v,d_k] fp32 (SSD and GDNQ_FLAG_NO_REQUANT, written)
  *   workspace: gdnq_prefill_workspace_size(p) bytes of device memory (may be
  *   NULL when that size is 0).
  *   Errors: NULL, SHAPE, DTYPE, ALIGN, FLAGS, WORKSPACE, HIP.

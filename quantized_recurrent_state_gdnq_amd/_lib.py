@@ -21,6 +21,8 @@ STATUS_NAMES = {0: "GDNQ_OK", 1: "GDNQ_ERR_NULL", 2: "GDNQ_ERR_SHAPE", 3: "GDNQ_
 GDNQ_F32, GDNQ_BF16 = 0, 1
 GDNQ_FLAG_WHT, GDNQ_FLAG_SSD, GDNQ_FLAG_INT8_QK, GDNQ_FLAG_BUF_BF16, GDNQ_FLAG_BUF_FP8 = 1, 2, 4, 16, 32
 GDNQ_FLAG_STATE_4BIT = 64
+GDNQ_FLAG_NO_REQUANT = 8
+GDNQ_MAX_WINDOW = 1 << 24
 GDNQ_FLAG_SLIDING = 128
 
 # Every function the header declares.

@@ -206,20 +206,29 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   if (p->in_dtype != GDNQ_BF16) return fail(GDNQ_ERR_DTYPE, "prefill in_dtype must be GDNQ_BF16");
   if (p->out_dtype != GDNQ_F32 && p->out_dtype != GDNQ_BF16) return fail(GDNQ_ERR_DTYPE, "out_dtype = %d", p->out_dtype);
   const bool ssd = (p->flags & GDNQ_FLAG_SSD) != 0;
+  const bool no_rq = (p->flags & GDNQ_FLAG_NO_REQUANT) != 0;
   const int C = p->chunk, W = p->window;
-  // GDN: chunk and window in {16, 32, 64} (the kernels run every window as one
-  // 64-position chunk, so the result depends on the window only); the
-  // hand-over, varlen and resume calls and SSD take chunk = 64 (= window)
+  // GDN: chunk in {16, 32, 64} and any window (the kernels run every window
+  // as whole 64-position chunks, so the result depends on the window only and
+  // the chunk is a blocking hint); the hand-over, varlen and resume calls and
+  // SSD take chunk = 64 (= window)
   if (ssd || handoff) {
     if (C != 64) return fail(GDNQ_ERR_SHAPE, "chunk = %d, expected 64", C);
     if (!ssd && W != 64) return fail(GDNQ_ERR_SHAPE, "window = %d: the hand-over, varlen and resume calls take 64", W);
   } else {
     if (C != 16 && C != 32 && C != 64) return fail(GDNQ_ERR_SHAPE, "chunk = %d, expected 16, 32 or 64", C);
-    if (W != 16 && W != 32 && W != 64) return fail(GDNQ_ERR_SHAPE, "window = %d, expected 16, 32 or 64", W);
+    if (W < 1 || W > GDNQ_MAX_WINDOW) return fail(GDNQ_ERR_SHAPE, "window = %d, expected 1 .. %d", W, GDNQ_MAX_WINDOW);
   }
-  const int Wt = ssd ? 64 : W;  // whole windows (the SSD recurrence has none: whole chunks)
+  if (no_rq && (ssd || handoff))
+    return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_NO_REQUANT: GDN gdnq_prefill_chunked only");
+  // whole windows (the SSD recurrence has none: whole chunks; a state that
+  // is never requantized has none either: any length)
+  const int Wt = ssd ? 64 : no_rq ? 1 : W;
   if (T % Wt && !handoff) return fail(GDNQ_ERR_SHAPE, "seqlen = %d is not a multiple of the window (%d)", T, Wt);
-  const int64_t Tk = ssd ? T : int64_t(T) / Wt * 64 + (handoff ? T % 64 : 0);  // positions the chunk kernels see
+  // positions the chunk kernels see: windows padded to whole 64-position chunks
+  const int64_t Tk = ssd || handoff ? int64_t(T)
+                     : no_rq       ? (int64_t(T) + 63) / 64 * 64
+                                   : int64_t(T) / W * ((int64_t(W) + 63) / 64 * 64);
   if ((Tk + 64) * H * 512 >= (int64_t(1) << 32))  // 32-bit output offsets, padding positions included
     return fail(GDNQ_ERR_SHAPE, "seqlen * heads = %lld: one sequence's outputs must stay under 4 GiB",
                 (long long)T * H);
@@ -232,9 +241,10 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
     if (dk != 128 || (dv != 64 && dv != 128)) return fail(GDNQ_ERR_SHAPE, "SSD: d_k = %d (128), d_v = %d (64 or 128)", dk, dv);
   } else {
     const uint32_t bufs = GDNQ_FLAG_BUF_BF16 | GDNQ_FLAG_BUF_FP8;
-    if (p->flags & ~uint32_t(GDNQ_FLAG_STATE_4BIT | GDNQ_FLAG_WHT | (handoff ? bufs : 0u)))
-      return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill takes GDNQ_FLAG_STATE_4BIT and GDNQ_FLAG_WHT (the hand-over, "
-                  "varlen and resume calls GDNQ_FLAG_STATE_4BIT and one window-buffer format flag)", p->flags);
+    if (p->flags & ~uint32_t(GDNQ_FLAG_STATE_4BIT | GDNQ_FLAG_WHT | GDNQ_FLAG_NO_REQUANT | (handoff ? bufs : 0u)))
+      return fail(GDNQ_ERR_FLAGS, "flags 0x%x: GDN prefill takes GDNQ_FLAG_STATE_4BIT, GDNQ_FLAG_WHT and "
+                  "GDNQ_FLAG_NO_REQUANT (the hand-over, varlen and resume calls GDNQ_FLAG_STATE_4BIT and one "
+                  "window-buffer format flag)", p->flags);
     if ((p->flags & bufs) == bufs)
       return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_BUF_BF16 and GDNQ_FLAG_BUF_FP8 are exclusive");
     if ((p->flags & GDNQ_FLAG_WHT) && handoff)
@@ -257,6 +267,7 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   L.handoff = handoff;
   L.buf_bf16 = handoff && (p->flags & GDNQ_FLAG_BUF_BF16) != 0;
   L.buf_fp8 = handoff && (p->flags & GDNQ_FLAG_BUF_FP8) != 0;
+  L.no_requant = no_rq;
   return GDNQ_OK;
 }
 
@@ -295,26 +306,40 @@ static gdnq_status prefill_chunked_impl(const gdnq_prefill_params* p, const void
       for (int j = 0; j < N; ++j)
         if (j != i && overlap(sp[i], sp[j])) return fail(GDNQ_ERR_ALIAS, "%s overlaps %s", sp[i].name, sp[j].name);
   } else {
-    if (state_f32) return fail(GDNQ_ERR_SHAPE, "GDN prefill: state_f32 must be NULL");
+    if (L.no_requant) {
+      if (codes || scales)
+        return fail(GDNQ_ERR_SHAPE, "GDNQ_FLAG_NO_REQUANT: codes and scales must be NULL (the final state goes to state_f32)");
+    } else if (state_f32) {
+      return fail(GDNQ_ERR_SHAPE, "GDN prefill: state_f32 must be NULL (it takes the state only under GDNQ_FLAG_NO_REQUANT)");
+    }
     if ((init_codes == nullptr) != (init_scales == nullptr))
       return fail(GDNQ_ERR_NULL, "init_codes and init_scales must be both NULL or both set");
-    const Span sp[] = {{"q", q, bth * L.d_k * 2},         {"k", k, bth * L.d_k * 2},
-                       {"v", v, bth * L.d_v * 2},         {"alpha", alpha, bth * 4},
-                       {"beta", beta, bth * 4},           {"o", o, bth * L.d_v * eo},
-                       {"codes", codes, bh * L.d_v * L.d_k / (L.q4 ? 2 : 1)}, {"scales", scales, bh * L.d_v * 4}};
-    constexpr int N = sizeof(sp) / sizeof(sp[0]);
+    Span sp[] = {{"q", q, bth * L.d_k * 2},         {"k", k, bth * L.d_k * 2},
+                 {"v", v, bth * L.d_v * 2},         {"alpha", alpha, bth * 4},
+                 {"beta", beta, bth * 4},           {"o", o, bth * L.d_v * eo},
+                 {"codes", codes, bh * L.d_v * L.d_k / (L.q4 ? 2 : 1)}, {"scales", scales, bh * L.d_v * 4}};
+    int N = sizeof(sp) / sizeof(sp[0]);
+    if (L.no_requant) {  // the one state output
+      sp[6] = {"state_f32", state_f32, bh * L.d_v * L.d_k * 4};
+      N = 7;
+    }
     if (L.T > 0) {
       if (gdnq_status st = check_ptrs(sp, N)) return st;
     } else {
-      if (gdnq_status st = check_ptrs(sp + 6, 2)) return st;
+      if (gdnq_status st = check_ptrs(sp + 6, N - 6)) return st;
     }
     if (init_codes) {
       const Span ip[] = {{"init_codes", init_codes, bh * L.d_v * L.d_k / (L.q4 ? 2 : 1)},
                          {"init_scales", init_scales, bh * L.d_v * 4}};
       if (gdnq_status st = check_ptrs(ip, 2)) return st;
-      // an in-place continuation (init == final) is allowed; partial overlap is not
-      if (init_codes != codes && overlap(ip[0], sp[6])) return fail(GDNQ_ERR_ALIAS, "init_codes partially overlaps codes");
-      if (init_scales != scales && overlap(ip[1], sp[7])) return fail(GDNQ_ERR_ALIAS, "init_scales partially overlaps scales");
+      if (L.no_requant) {
+        for (int i = 0; i < 2; ++i)
+          if (overlap(ip[i], sp[6])) return fail(GDNQ_ERR_ALIAS, "%s overlaps state_f32", ip[i].name);
+      } else {
+        // an in-place continuation (init == final) is allowed; partial overlap is not
+        if (init_codes != codes && overlap(ip[0], sp[6])) return fail(GDNQ_ERR_ALIAS, "init_codes partially overlaps codes");
+        if (init_scales != scales && overlap(ip[1], sp[7])) return fail(GDNQ_ERR_ALIAS, "init_scales partially overlaps scales");
+      }
     }
     for (int i = 5; i < N; ++i)
       for (int j = 0; j < N; ++j)

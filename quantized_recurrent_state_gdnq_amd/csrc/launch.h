@@ -69,6 +69,7 @@ struct PrefillLaunch {
   bool out_bf16, wht, ssd, int8_qk, handoff, varlen, resume;
   bool q4;  // GDN: the state as packed 4-bit codes
   bool buf_bf16, buf_fp8;  // hand-over: the window buffer's format
+  bool no_requant;  // GDN: never requantize; the final fp32 state goes to state_f32
 };
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream);
 hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream);

@@ -347,6 +347,8 @@ struct StateArgs {
   float* scales;
   SeqMap sm;
   int B, H;
+  int cpw;  // chunks per window (the state is requantized after every cpw-th); 0: never
+  float* state_f32;  // the final fp32 state (never requantized), or NULL
 };
 
 constexpr int SNT = 512;  // state-pass threads: 2 chain, 4 side and 2 staging waves
@@ -398,7 +400,12 @@ __device__ __forceinline__ bf16x8 cat8(const bf16x4& lo, const bf16x4& hi) {
 // U_c and the codes of S0_{c+1}; the side waves read U_{c-1} and the codes
 // of S0_c; staging fills buffer (c + 1) & 1.
 // QB: the state's code width, 8 (int8) or 4 (packed 4-bit, scale absmax / 7)
-template <bool OUT_BF16, int QB>
+// CARRY: windows span several chunks (or the state is never requantized).
+// Between window ends the chain keeps S0 in fp32 (values in cf, s = 1) and
+// takes K S0^T in three bf16 parts; the side waves get S0 as two int8 levels,
+// row ~= s1 (c1 + c2 / 254) with s1 = max|row| / 127 (within 1.6e-5 of the
+// row's absmax: the output base only), exact where S0 is a requantized state.
+template <bool OUT_BF16, int QB, bool CARRY>
 __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
   constexpr int QMAX = QB == 8 ? 127 : 7;
   constexpr int RB = PD * QB / 8;  // bytes per stored row
@@ -459,7 +466,7 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
     // ================================================================ chain waves
     const int rl = wave * 16 + lr;  // this lane's row of the block
     const size_t grow = state_row0 + rl;
-    float cf[8][4];  // codes of S0: dims dt 16 + 4 g4 + q
+    float cf[8][4];  // S0 in units of s: dims dt 16 + 4 g4 + q (codes, or fp32 values with s = 1)
     float s = 0.f;
     if (a.init_codes) {
 #pragma unroll
@@ -485,12 +492,42 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) cb[ks][e] = (__bf16)cf[2 * ks + (e >> 2)][e & 3];
     };
-    auto publish = [&](int par) {  // codes and scale of S0 for the side waves' output base
+    auto publish = [&](int par) {  // S0 for the side waves' output base
+      if constexpr (!CARRY) {  // the codes (exact in bf16) and the row scale
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) c_at(par, wave, ks)[lane] = cb[ks];
-      if (g4 == 0) Sl[par * RWS + rl] = s;
+        for (int ks = 0; ks < 4; ++ks) c_at(par, wave, ks)[lane] = cb[ks];
+        if (g4 == 0) Sl[par * RWS + rl] = s;
+      } else {  // two int8 levels c1, c2 (bytes 0-7, 8-15 of the slot) and s1
+        float am = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) am = fmaxf(am, fabsf(cf[dt][q]));
+        am = fmaxf(am, __shfl_xor(am, 16));
+        am = fmaxf(am, __shfl_xor(am, 32));
+        const float inv = am > 0.f ? 127.f / am : 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          uint32_t w[4];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            int c1[4], c2[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float t = cf[2 * ks + hh][q] * inv, r = rintf(t);
+              c1[q] = int(r);
+              c2[q] = int(rintf((t - r) * 254.f));
+            }
+            w[hh] = pack4_i8(c1[0], c1[1], c1[2], c1[3]);
+            w[2 + hh] = pack4_i8(c2[0], c2[1], c2[2], c2[3]);
+          }
+          const u32x4 wv = {w[0], w[1], w[2], w[3]};
+          *reinterpret_cast<u32x4*>(c_at(par, wave, ks) + lane) = wv;
+        }
+        if (g4 == 0) Sl[par * RWS + rl] = s * am * (1.f / 127.f);
+      }
     };
-    pack_codes();
+    if constexpr (!CARRY) pack_codes();
     publish(0);
     __syncthreads();  // chunk 0 staged
 
@@ -527,14 +564,31 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
           }
         }
       __builtin_amdgcn_sched_barrier(0);
-      // ---- X = K codes^T: tile jt holds tokens jt 16 + 4 g4 + q of row rl
+      // ---- X = K S0^T (in units of s): tile jt holds tokens jt 16 + 4 g4 + q of row rl
       f32x4 x[4];
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) x[jt] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (CARRY) {  // S0 in three bf16 parts (exact for codes or fp32 values)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks) {
+          float xs[8];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) x[jt] = mfma16(ka[jt][ks], cb[ks], x[jt]);
+          for (int e = 0; e < 8; ++e) xs[e] = cf[2 * ks + (e >> 2)][e & 3];
+          bf16x8 ph, pm, pl;
+          split3t(xs, ph, pm, pl);
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) x[jt] = mfma16(ka[jt][ks], pl, x[jt]);
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) x[jt] = mfma16(ka[jt][ks], pm, x[jt]);
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) x[jt] = mfma16(ka[jt][ks], ph, x[jt]);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) x[jt] = mfma16(ka[jt][ks], cb[ks], x[jt]);
+      }
       // ---- rhs = beta (v - gamma s X) in three bf16 parts
       bf16x8 rp[3][2];
 #pragma unroll
@@ -601,9 +655,9 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
         u_at(par, 1, wave, ks)[lane] = u2;
         split3t(ud, dp[0][ks], dp[1][ks], dp[2][ks]);
       }
-      // ---- S_C^T = gamma_C S0^T + K^T (U o d), then requantize the row (not
-      //      for a partial last chunk: its window stays open and the stored
-      //      state stays at the last boundary)
+      // ---- S_C^T = gamma_C S0^T + K^T (U o d), then requantize the row at a
+      //      window end (not for a partial last chunk: its window stays open
+      //      and the stored state stays at the last boundary)
       if (!(partial_last && c == NC - 1)) {
         const float gs = F[PC + PC - 1] * s;
         float sn[32];
@@ -620,21 +674,34 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) sn[4 * dt + q] = gs * cf[dt][q] + acc[q];
         }
-        float amax = 0.f;
+        if (!CARRY || (a.cpw > 0 && (c + 1) % a.cpw == 0)) {
+          float amax = 0.f;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(sn[e]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16));  // the row's other three lane groups
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const float scale = codec_scale<QMAX>(amax);
-        float cn[32];
-        codec_codes<32, QMAX>(sn, scale, cn);
+          for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(sn[e]));
+          amax = fmaxf(amax, __shfl_xor(amax, 16));  // the row's other three lane groups
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          const float scale = codec_scale<QMAX>(amax);
+          float cn[32];
+          codec_codes<32, QMAX>(sn, scale, cn);
 #pragma unroll
-        for (int e = 0; e < 32; ++e) cf[e >> 2][e & 3] = cn[e];
-        s = scale;
-        pack_codes();
+          for (int e = 0; e < 32; ++e) cf[e >> 2][e & 3] = cn[e];
+          s = scale;
+        } else {  // inside a window: the state stays fp32
+#pragma unroll
+          for (int e = 0; e < 32; ++e) cf[e >> 2][e & 3] = sn[e];
+          s = 1.f;
+        }
+        if constexpr (!CARRY) pack_codes();
         if (c + 1 < NC) publish(par ^ 1);
       }
       __syncthreads();
+    }
+    if (CARRY && a.state_f32) {  // never requantized: the fp32 rows
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<float4*>(a.state_f32 + grow * PD + dt * 16 + 4 * g4) =
+            make_float4(cf[dt][0] * s, cf[dt][1] * s, cf[dt][2] * s, cf[dt][3] * s);
+      return;
     }
     // final rows (codes back to int8, or packed 4-bit)
 #pragma unroll
@@ -775,10 +842,24 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (CARRY) {  // the two int8 levels: s1 (Q c1^T + Q c2^T / 254)
+            f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const __bf16* qr = Ql + (it * 16 + lr) * KP + ks * 32 + 4 * g4;
-            acc = mfma16(cat8(lds4(qr), lds4(qr + 16)), c_at(par, rt, ks)[lane], acc);
+            for (int ks = 0; ks < 4; ++ks) {
+              const __bf16* qr = Ql + (it * 16 + lr) * KP + ks * 32 + 4 * g4;
+              const bf16x8 qa = cat8(lds4(qr), lds4(qr + 16));
+              const u32x4 w = *reinterpret_cast<const u32x4*>(c_at(par, rt, ks) + lane);
+              acc = mfma16(qa, i8x8_to_bf16(make_uint2(w[0], w[1])), acc);
+              acc2 = mfma16(qa, i8x8_to_bf16(make_uint2(w[2], w[3])), acc2);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] += acc2[q] * (1.f / 254.f);
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+              const __bf16* qr = Ql + (it * 16 + lr) * KP + ks * 32 + 4 * g4;
+              acc = mfma16(cat8(lds4(qr), lds4(qr + 16)), c_at(par, rt, ks)[lane], acc);
+            }
           }
           const float sr = Sl[par * RWS + rt * 16 + lr];
 #pragma unroll
@@ -896,10 +977,12 @@ static size_t gdn_new_tokens(const PrefillLaunch& L) { return L.varlen ? size_t(
 //     erase nothing in the extra columns, zero value rows write nothing, and
 //     every product and row absmax only gains +0 terms, so the padded head
 //     carries the d = 64 state exactly in its first 64 rows and columns.
-//   * a window W of 16 or 32 tokens: every window becomes one 64-position
-//     chunk whose last 64 - W positions are writes that change nothing
-//     (k = q = v = 0, alpha = 1, beta = 0): the state passes them unchanged,
-//     so each chunk end is exactly the window's end and is requantized there.
+//   * a window W that is not a multiple of 64 tokens: every window becomes
+//     Wp = 64 ceil(W / 64) positions whose last Wp - W are writes that change
+//     nothing (k = q = v = 0, alpha = 1, beta = 0): the state passes them
+//     unchanged, so the end of every Wp / 64-th chunk is exactly a window's
+//     end and is requantized there.  A state that is never requantized runs
+//     as one window of all T tokens.
 // gdn_pad_kernel builds the padded q, k, v (and alpha, beta; and the stored
 // state at d = 64); gdn_unpad_kernel copies the real tokens' outputs (and the
 // final state at d = 64) back.
@@ -911,7 +994,7 @@ struct PadArgs {
   float* pa;             // [B][Tp][H]
   float* pb;
   int64_t B, T, H;
-  int W, ds;             // window (positions taken per 64-position chunk), source width
+  int W, Wp, ds;         // window, its padded positions (a multiple of 64), source width
   const int8_t* c0;      // stored state [bh][64][RB64] (NULL: zero state or not padded)
   const float* s0;       // [bh][64]
   int8_t* pc0;           // [bh][128][RB128]
@@ -921,7 +1004,7 @@ struct PadArgs {
 };
 
 __global__ __launch_bounds__(256) void gdn_pad_kernel(PadArgs a) {
-  const int64_t Tp = a.T / a.W * PC;
+  const int64_t Tp = a.T / a.W * a.Wp;
   const int64_t rows = a.B * Tp * a.H;  // padded rows
   const int64_t stride = int64_t(gridDim.x) * 256;
   const int gs = a.ds / 8;  // 16-byte granules per source row
@@ -929,10 +1012,10 @@ __global__ __launch_bounds__(256) void gdn_pad_kernel(PadArgs a) {
     const int64_t r = e / 48;  // padded row (b Tp + p) H + h
     const int op = int(e % 48) / 16, g = int(e % 16);
     const int64_t h = r % a.H, bp = r / a.H, p = bp % Tp, b = bp / Tp;
-    const int i = int(p % PC);  // position in its chunk
+    const int i = int(p % a.Wp);  // position in its window
     uint4 w = make_uint4(0u, 0u, 0u, 0u);
     if (i < a.W && g < gs) {
-      const int64_t t = p / PC * a.W + i;  // the source token
+      const int64_t t = p / a.Wp * a.W + i;  // the source token
       w = reinterpret_cast<const uint4*>(a.x[op] + ((b * a.T + t) * a.H + h) * a.ds)[g];
     }
     reinterpret_cast<uint4*>(a.y[op] + r * PD)[g] = w;
@@ -940,10 +1023,10 @@ __global__ __launch_bounds__(256) void gdn_pad_kernel(PadArgs a) {
   if (a.a) {
     for (int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x; r < rows; r += stride) {
       const int64_t h = r % a.H, bp = r / a.H, p = bp % Tp, b = bp / Tp;
-      const int i = int(p % PC);
+      const int i = int(p % a.Wp);
       float al = 1.f, bt = 0.f;
       if (i < a.W) {
-        const int64_t src = (b * a.T + p / PC * a.W + i) * a.H + h;
+        const int64_t src = (b * a.T + p / a.Wp * a.W + i) * a.H + h;
         al = a.a[src];
         bt = a.be[src];
       }
@@ -969,26 +1052,36 @@ struct UnpadArgs {
   const char* po;  // [B][Tp][H][128] outputs (eo bytes each)
   char* o;         // [B][T][H][ds]
   int64_t B, T, H;
-  int W, ds, eo;
-  const int8_t* pc;  // [bh][128][RB128] (NULL: the state was not padded)
+  int W, Wp, ds, eo;
+  const int8_t* pc;  // [bh][128][RB128] (NULL: no padded codes to copy back)
   const float* ps;
   int8_t* c;         // [bh][64][RB64]
   float* sc;
+  const float* psf;  // fp32 state [bh][128][128] (NULL: none to copy back)
+  float* sf;         // [bh][64][64]
   int64_t bh;
   int rb64;
 };
 
 __global__ __launch_bounds__(256) void gdn_unpad_kernel(UnpadArgs a) {
   const int gpr = a.ds * a.eo / 16;  // 16-byte granules per output row
-  const int64_t Tp = a.T / a.W * PC;
+  const int64_t Tp = a.T / a.W * a.Wp;
   const int64_t n = a.B * a.T * a.H * gpr;
   const int64_t stride = int64_t(gridDim.x) * 256;
   for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n; e += stride) {
     const int64_t row = e / gpr;  // (b T + t) H + h
     const int g = int(e % gpr);
     const int64_t h = row % a.H, bt = row / a.H, t = bt % a.T, b = bt / a.T;
-    const int64_t prow = (b * Tp + t / a.W * PC + t % a.W) * a.H + h;
+    const int64_t prow = (b * Tp + t / a.W * a.Wp + t % a.W) * a.H + h;
     reinterpret_cast<uint4*>(a.o + row * a.ds * a.eo)[g] = reinterpret_cast<const uint4*>(a.po + prow * PD * a.eo)[g];
+  }
+  if (a.psf) {
+    for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < a.bh * 64 * 16; e += stride) {
+      const int64_t r = e / 16;  // bh * 64 + row
+      const int g = int(e % 16);
+      const int64_t bh = r / 64, rr = r % 64;
+      reinterpret_cast<float4*>(a.sf + r * 64)[g] = reinterpret_cast<const float4*>(a.psf + (bh * PD + rr) * PD)[g];
+    }
   }
   if (!a.pc) return;
   const int64_t ns = a.bh * 64 * (a.rb64 / 16);
@@ -1331,23 +1424,28 @@ __global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
 static size_t gdn_ws_128(const PrefillLaunch& L) {
   return gdn_ws_T(L) + gdn_ws_g(L) + gdn_ws_stage(L) + gdn_ws_map(L) + gdn_ws_rot(L);
 }
-// The padded run: d = 128, 64-position chunks, T / W chunks per sequence.
-static bool gdn_padded(const PrefillLaunch& L) { return L.d_k == 64 || L.W < PC; }
+// The window in tokens (a state never requantized: all T tokens as one) and
+// its padded length, a multiple of the 64-position chunk.
+static int gdn_window(const PrefillLaunch& L) { return L.no_requant ? (L.T > 0 ? L.T : PC) : L.W; }
+static int gdn_window_padded(const PrefillLaunch& L) { return (gdn_window(L) + PC - 1) / PC * PC; }
+// The padded run: d = 128, windows of whole 64-position chunks.
+static bool gdn_padded(const PrefillLaunch& L) { return L.d_k == 64 || gdn_window(L) % PC != 0; }
 static PrefillLaunch gdn_padded_launch(const PrefillLaunch& L) {
   PrefillLaunch L2 = L;
   L2.d_k = L2.d_v = PD;
-  L2.T = L.T / L.W * PC;
-  L2.W = L2.C = PC;
+  L2.T = L.T / gdn_window(L) * gdn_window_padded(L);
+  L2.W = gdn_window_padded(L);
+  L2.C = PC;
   return L2;
 }
 struct PadLayout {
-  size_t qkv, ab, c0, s0, o, c, sc, inner, total;
+  size_t qkv, ab, c0, s0, o, c, sc, sf, inner, total;
 };
 static PadLayout gdn_pad_layout(const PrefillLaunch& L) {
   const PrefillLaunch L2 = gdn_padded_launch(L);
   const size_t rows = size_t(L.B) * L2.T * L.H, bh = size_t(L.B) * L.H;
   const size_t rb = L.q4 ? PD / 2 : PD, eo = L.out_bf16 ? 2 : 4;
-  const bool pad_ab = L.W < PC, pad_state = L.d_k == 64;
+  const bool pad_ab = gdn_window(L) % PC != 0, pad_state = L.d_k == 64;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   PadLayout p{};
   p.qkv = 0;
@@ -1356,8 +1454,9 @@ static PadLayout gdn_pad_layout(const PrefillLaunch& L) {
   p.s0 = p.c0 + (pad_state ? up(bh * PD * rb) : 0);
   p.o = p.s0 + (pad_state ? up(bh * PD * 4) : 0);
   p.c = p.o + up(rows * PD * eo);
-  p.sc = p.c + (pad_state ? up(bh * PD * rb) : 0);
-  p.inner = p.sc + (pad_state ? up(bh * PD * 4) : 0);
+  p.sc = p.c + (pad_state && !L.no_requant ? up(bh * PD * rb) : 0);
+  p.sf = p.sc + (pad_state && !L.no_requant ? up(bh * PD * 4) : 0);
+  p.inner = p.sf + (pad_state && L.no_requant ? up(bh * PD * PD * 4) : 0);
   p.total = p.inner + gdn_ws_128(L2);
   return p;
 }
@@ -1376,14 +1475,15 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
   const PrefillLaunch L2p = gdn_padded_launch(L);
   char* ws = static_cast<char*>(L.workspace);
   const int64_t rows = int64_t(L.B) * L2p.T * L.H, bh = int64_t(L.B) * L.H;
-  const bool pad_ab = L.W < PC, pad_state = L.d_k == 64;
+  const bool pad_ab = gdn_window(L) % PC != 0, pad_state = L.d_k == 64;
+  const int Wt = gdn_window(L), Wp = gdn_window_padded(L);
   const int rb64 = L.q4 ? 32 : 64;
   uint16_t* pq = reinterpret_cast<uint16_t*>(ws + P.qkv);
   float* pal = reinterpret_cast<float*>(ws + P.ab);
   PadArgs pa{{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v)},
              {pq, pq + rows * PD, pq + 2 * rows * PD},
              pad_ab ? L.alpha : nullptr, pad_ab ? L.beta : nullptr, pad_ab ? pal : nullptr, pad_ab ? pal + rows : nullptr,
-             L.B, L.T, L.H, L.W, L.d_k,
+             L.B, L.T, L.H, Wt, Wp, L.d_k,
              pad_state ? L.init_codes : nullptr, L.init_scales,
              pad_state && L.init_codes ? reinterpret_cast<int8_t*>(ws + P.c0) : nullptr,
              reinterpret_cast<float*>(ws + P.s0), bh, rb64};
@@ -1402,14 +1502,20 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
   if (pad_state) {
     L2.init_codes = pa.pc0;
     L2.init_scales = L.init_codes ? pa.ps0 : nullptr;
-    L2.codes = reinterpret_cast<int8_t*>(ws + P.c);
-    L2.scales = reinterpret_cast<float*>(ws + P.sc);
+    if (L.no_requant) {
+      L2.state_f32 = reinterpret_cast<float*>(ws + P.sf);
+    } else {
+      L2.codes = reinterpret_cast<int8_t*>(ws + P.c);
+      L2.scales = reinterpret_cast<float*>(ws + P.sc);
+    }
   }
   L2.o = ws + P.o;
   L2.workspace = ws + P.inner;
   if (hipError_t e = launch_prefill_gdn128(L2, stream)) return e;
-  UnpadArgs ua{ws + P.o, static_cast<char*>(L.o), L.B, L.T, L.H, L.W, L.d_k, L.out_bf16 ? 2 : 4,
-               pad_state ? L2.codes : nullptr, L2.scales, L.codes, L.scales, bh, rb64};
+  const bool back_codes = pad_state && !L.no_requant, back_f32 = pad_state && L.no_requant;
+  UnpadArgs ua{ws + P.o, static_cast<char*>(L.o), L.B, L.T, L.H, Wt, Wp, L.d_k, L.out_bf16 ? 2 : 4,
+               back_codes ? L2.codes : nullptr, L2.scales, L.codes, L.scales,
+               back_f32 ? L2.state_f32 : nullptr, L.state_f32, bh, rb64};
   hipLaunchKernelGGL(gdn_unpad_kernel, dim3(grid), dim3(256), 0, stream, ua);
   return hipGetLastError();
 }
@@ -1476,12 +1582,18 @@ static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t st
     hipLaunchKernelGGL(gdn_prep_kernel, dim3(grid), dim3(256), 0, stream, p);
     if (hipError_t e = hipGetLastError()) return e;
   }
+  // chunks per window (0: never requantized); windows of one chunk take the
+  // kernel that keeps no fp32 state between chunks
+  const int cpw = L.no_requant ? 0 : L.W / PC;
   StateArgs s{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k),
               static_cast<const uint16_t*>(L.v), L.beta, T_ws, g_ws, L.init_codes, L.init_scales,
-              L.o, L.codes, L.scales, sm, L.B, L.H};
+              L.o, L.codes, L.scales, sm, L.B, L.H, cpw, L.no_requant ? L.state_f32 : nullptr};
   const unsigned grid = unsigned(L.B) * L.H * (PD / RWS);
-  auto kern = L.q4 ? (L.out_bf16 ? &gdn_state_kernel<true, 4> : &gdn_state_kernel<false, 4>)
-                   : (L.out_bf16 ? &gdn_state_kernel<true, 8> : &gdn_state_kernel<false, 8>);
+  auto kern = cpw == 1
+                  ? (L.q4 ? (L.out_bf16 ? &gdn_state_kernel<true, 4, false> : &gdn_state_kernel<false, 4, false>)
+                          : (L.out_bf16 ? &gdn_state_kernel<true, 8, false> : &gdn_state_kernel<false, 8, false>))
+                  : (L.q4 ? (L.out_bf16 ? &gdn_state_kernel<true, 4, true> : &gdn_state_kernel<false, 4, true>)
+                          : (L.out_bf16 ? &gdn_state_kernel<true, 8, true> : &gdn_state_kernel<false, 8, true>));
   if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, STATE_LDS))
     return e;

@@ -182,20 +182,22 @@ def _prefill_params(q, v, *, window, chunk, wht, ssd, int8_qk, out_dtype, state_
 
 
 def prefill_workspace_size(q, v, *, window=64, chunk=64, wht=False, ssd=False, int8_qk=False,
-                           out_dtype=torch.bfloat16):
+                           out_dtype=torch.bfloat16, no_requant=False):
     p = _prefill_params(q, v, window=window, chunk=chunk, wht=wht, ssd=ssd, int8_qk=int8_qk,
-                        out_dtype=out_dtype)
+                        out_dtype=out_dtype, extra_flags=_lib.GDNQ_FLAG_NO_REQUANT if no_requant else 0)
     return int(_lib.prefill_workspace_size(p))
 
 
 def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_codes=None,
                     init_scales=None, wht=False, ssd=False, int8_qk=False,
                     out_dtype=torch.bfloat16, o=None, codes=None, scales=None, state_f32=None,
-                    workspace=None, state_bits=8, noalloc=False):
+                    workspace=None, state_bits=8, noalloc=False, no_requant=False):
     """Chunkwise prefill (see gdnq_prefill_chunked in include/gdnq.h).
 
     q, k [B,T,H,d_k], v [B,T,H,d_v] bf16; alpha (and beta for GDN) [B,T,H] fp32.
-    GDN returns (o, codes, scales); SSD (ssd=True) returns (o, state_f32).
+    GDN returns (o, codes, scales); SSD (ssd=True) returns (o, state_f32), and
+    so does GDN with no_requant=True (GDNQ_FLAG_NO_REQUANT: the state is never
+    requantized and comes back in fp32).
     GDN with state_bits=4: the uniform 4-bit state, codes [B,H,d_v,d_k/2]
     packed two per byte (init_codes likewise).
     noalloc=True calls gdnq_prefill_chunked_noalloc (the library's own device
@@ -211,25 +213,32 @@ def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_code
     if tuple(k.shape) != (B, T, H, d_k) or tuple(v.shape) != (B, T, H, d_v) or tuple(alpha.shape) != (B, T, H):
         raise ValueError("inconsistent prefill shapes")
     p = _prefill_params(q, v, window=window, chunk=chunk, wht=wht, ssd=ssd, int8_qk=int8_qk,
-                        out_dtype=out_dtype, state_bits=state_bits)
+                        out_dtype=out_dtype, state_bits=state_bits,
+                        extra_flags=_lib.GDNQ_FLAG_NO_REQUANT if no_requant else 0)
     if o is None:
         o = torch.empty((B, T, H, d_v), dtype=out_dtype, device=dev)
     _shape(_need(o, "o", out_dtype, dev), (B, T, H, d_v), "o")
-    if ssd:
+    f32_state = ssd or no_requant  # the final state comes back in fp32
+    if state_f32 is not None and not f32_state:
+        raise ValueError("state_f32 is an output of SSD and no_requant calls only")
+    if f32_state:
+        if codes is not None or scales is not None:
+            raise ValueError("codes and scales are not outputs here (the state comes back as state_f32)")
         if state_f32 is None:
             state_f32 = torch.empty((B, H, d_v, d_k), dtype=torch.float32, device=dev)
         _shape(_need(state_f32, "state_f32", torch.float32, dev), (B, H, d_v, d_k), "state_f32")
-    else:
+    if not ssd:
         _need(beta, "beta", torch.float32, dev)
         if tuple(beta.shape) != (B, T, H):
             raise ValueError("beta must be [B,T,H]")
-        if codes is None:
-            codes = torch.empty((B, H, d_v, d_k * state_bits // 8), dtype=torch.int8, device=dev)
-        if scales is None:
-            scales = torch.empty((B, H, d_v), dtype=torch.float32, device=dev)
         cshape = (B, H, d_v, d_k * state_bits // 8)
-        _shape(_need(codes, "codes", torch.int8, dev), cshape, "codes")
-        _shape(_need(scales, "scales", torch.float32, dev), (B, H, d_v), "scales")
+        if not no_requant:
+            if codes is None:
+                codes = torch.empty(cshape, dtype=torch.int8, device=dev)
+            if scales is None:
+                scales = torch.empty((B, H, d_v), dtype=torch.float32, device=dev)
+            _shape(_need(codes, "codes", torch.int8, dev), cshape, "codes")
+            _shape(_need(scales, "scales", torch.float32, dev), (B, H, d_v), "scales")
         if (init_codes is None) != (init_scales is None):
             raise ValueError("init_codes and init_scales: both or neither")
         if init_codes is not None:
@@ -240,20 +249,18 @@ def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_code
             raise ValueError("noalloc: no workspace is taken")
         _lib.check(_lib.prefill_chunked_noalloc(p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                                 None if ssd else _ptr(beta), _ptr(init_codes),
-                                                _ptr(init_scales), _ptr(o), None if ssd else _ptr(codes),
-                                                None if ssd else _ptr(scales),
-                                                _ptr(state_f32) if ssd else None, _stream(dev)))
-        return (o, state_f32) if ssd else (o, codes, scales)
+                                                _ptr(init_scales), _ptr(o), _ptr(codes), _ptr(scales),
+                                                _ptr(state_f32), _stream(dev)))
+        return (o, state_f32) if f32_state else (o, codes, scales)
     need = int(_lib.prefill_workspace_size(p))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _lib.check(_lib.prefill_chunked(p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                     None if ssd else _ptr(beta), _ptr(init_codes),
-                                    _ptr(init_scales), _ptr(o), None if ssd else _ptr(codes),
-                                    None if ssd else _ptr(scales), _ptr(state_f32) if ssd else None,
+                                    _ptr(init_scales), _ptr(o), _ptr(codes), _ptr(scales), _ptr(state_f32),
                                     _ptr(workspace), ws_bytes, _stream(dev)))
-    if ssd:
+    if f32_state:
         return o, state_f32
     return o, codes, scales
 

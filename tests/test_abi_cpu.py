@@ -179,11 +179,15 @@ def _prefill(params, fake, **over):
 
 
 @pytest.mark.parametrize("params,status", [
-    (_pp(C=8, W=8), 2), (_pp(T=100), 2), (_pp(dk=64, dv=128), 2), (_pp(W=128), 2), (_pp(W=48), 2),
+    (_pp(C=8, W=8), 2), (_pp(T=100), 2), (_pp(dk=64, dv=128), 2), (_pp(W=0), 2), (_pp(W=-64), 2),
     (_pp(T=48, W=32, C=32), 2),           # not a whole number of windows
+    (_pp(T=128, W=256), 2),                # likewise
+    (_pp(T=0, W=(1 << 24) + 64), 2),       # longer than GDNQ_MAX_WINDOW
     (_pp(dk=64, dv=64, flags=1), 8),       # no rotation at d = 64
-    (_pp(ind=0), 3), (_pp(outd=3), 3), (_pp(flags=4), 8), (_pp(flags=8), 8), (_pp(flags=16), 8),
+    (_pp(ind=0), 3), (_pp(outd=3), 3), (_pp(flags=4), 8), (_pp(flags=16), 8),
     (_pp(flags=32), 8),
+    (_pp(flags=8), 2),                     # no requantization: codes and scales must be NULL
+    (_pp(dv=64, flags=2 | 4 | 8), 8),      # not for SSD
     (_pp(dv=64, flags=2 | 1), 8),        # SSD rotation only on the way to int8 operands
 ])
 def test_prefill_rejects_bad_params(params, status):
@@ -237,6 +241,40 @@ def test_window_and_chunk_sizes():
     assert L.gdnq_prefill_handoff_workspace_size(_pp(T=256, W=64, C=32)) == 0
     assert L.gdnq_prefill_workspace_size(_pp(T=256, dv=64, flags=2 | 4)) > 0
     assert L.gdnq_prefill_workspace_size(_pp(T=256, dv=64, C=32, W=32, flags=2 | 4)) == 0  # SSD: chunk 64
+
+
+def test_long_windows():
+    """Any window: a multiple of 64 runs unpadded (the same workspace as
+    W = 64); any other window is padded to whole 64-position chunks (W = 80
+    -> 128 positions per window, W = 1 -> 64); the hand-over, varlen and
+    resume calls keep decode's 64."""
+    base = L.gdnq_prefill_workspace_size(_pp(T=512))
+    for W in (128, 256, 512):
+        assert L.gdnq_prefill_workspace_size(_pp(T=512, W=W)) == base
+    # 160 tokens as two windows of 128 positions: the 256-position run plus its padded copies
+    assert L.gdnq_prefill_workspace_size(_pp(T=160, W=80, C=16)) > L.gdnq_prefill_workspace_size(_pp(T=256, W=128))
+    # two windows of 48 and one of 96 both run as 128 positions
+    assert L.gdnq_prefill_workspace_size(_pp(T=96, W=48, C=16)) == L.gdnq_prefill_workspace_size(_pp(T=96, W=96, C=32))
+    # four windows of one token and four of 16 both run as 256 padded positions
+    assert L.gdnq_prefill_workspace_size(_pp(T=4, W=1, C=16)) == L.gdnq_prefill_workspace_size(_pp(T=64, W=16, C=16))
+    assert L.gdnq_prefill_workspace_size(_pp(T=256, W=1 << 24)) == 0  # T not a multiple of W
+    assert L.gdnq_prefill_handoff_workspace_size(_pp(T=256, W=128)) == 0
+
+
+def test_no_requant_contract():
+    """GDNQ_FLAG_NO_REQUANT (gdnq_prefill_chunked, GDN): the final fp32 state
+    goes to state_f32; codes and scales must be NULL; any T (no windows)."""
+    f = Fake()
+    p = _pp(flags=8)
+    assert _prefill(p, f, codes=None, scales=None) == 1                      # state_f32 missing
+    assert _prefill(p, f, scales=None, state_f32=f()) == 2                   # codes given
+    sf = f()
+    assert _prefill(p, f, codes=None, scales=None, state_f32=sf, init_codes=sf, init_scales=f()) == 5
+    assert L.gdnq_prefill_workspace_size(_pp(T=48, C=16, W=64, flags=8)) > 0  # padded to 64 positions
+    assert L.gdnq_prefill_workspace_size(_pp(T=40, C=16, W=64, flags=8)) > 0
+    assert L.gdnq_prefill_workspace_size(_pp(T=512, W=64, flags=8)) == L.gdnq_prefill_workspace_size(_pp(T=512))
+    assert L.gdnq_prefill_handoff_workspace_size(_pp(flags=8)) == 0
+    assert L.gdnq_prefill_varlen_workspace_size(_pp(flags=8)) == 0
 
 
 def test_workspace_size_is_queryable():
