@@ -417,18 +417,22 @@ PREFILL_SOURCES = {False: ["prefill_gdn.hip", "device_common.h", "mfma.h"],
                    True: ["prefill_ssd.hip", "device_common.h", "mfma.h"]}
 
 
+W_LONG = 128  # the long-window prefill line
+
+
 def bench_prefill(torch, ops, wl, steps=5, warmup=2, with_cpu=True):
     """Secondary: GDN chunked prefill B=4, T=8192, H=16, d=128, C=W=64 (bf16
     output, zero initial state); SSD prefill B=2, T=4096, H=80, d_k=128,
     d_v=64 with WHT-rotated int8 q/k (bf16 output); the GDN hand-over to
     decode (T = 8192 + 37); a packed batch of 32 sequences of seeded lengths
-    U{1..2047} (H=16); and resuming 4 decode states at fills U{0..63} with
-    8192 new tokens each.  Inputs and workspace are resident before timing;
+    U{1..2047} (H=16); resuming 4 decode states at fills U{0..63} with
+    8192 new tokens each; the GDN prefill with q, k rotated; and with
+    windows of 128 tokens.  Inputs and workspace are resident before timing;
     each call is timed whole (all its kernels)."""
     dev = torch.device("cuda:0")
     res = {}
     names = ["gdn_prefill", "ssd_prefill", "gdn_prefill_handoff", "gdn_prefill_varlen",
-             "gdn_prefill_resume", "gdn_prefill_wht"]
+             "gdn_prefill_resume", "gdn_prefill_wht", "gdn_prefill_w128"]
     H16, d = 16, 128
     state_bytes = d * (d + 4)  # int8 rows + fp32 scales of one head
 
@@ -502,7 +506,7 @@ def bench_prefill(torch, ops, wl, steps=5, warmup=2, with_cpu=True):
                 def call():
                     ops.prefill_handoff(q, k, v, a, bt, o=o, state=st, workspace=ws)
             else:
-                kw = dict(ssd=True, wht=True, int8_qk=True) if ssd else dict(window=64)
+                kw = dict(ssd=True, wht=True, int8_qk=True) if ssd else dict(window=W_LONG if name == "gdn_prefill_w128" else 64)
                 if name == "gdn_prefill_wht":
                     kw["wht"] = True
                 kw["workspace"] = torch.empty(ops.prefill_workspace_size(q, v, **kw), dtype=torch.uint8,
@@ -517,7 +521,10 @@ def bench_prefill(torch, ops, wl, steps=5, warmup=2, with_cpu=True):
                 def call():
                     ops.prefill_chunked(q, k, v, a, bt, **kw)
             workload = (f"B={Bq} T={T} H={Hh} d_k={dk} d_v={dv} chunk=64"
-                        + (" WHT+int8 q/k, fp32 state" if ssd else " window=64, int8 state")
+                        + (" WHT+int8 q/k, fp32 state" if ssd else f" window={kw.get('window', 64)}, int8 state"
+                           if name != "gdn_prefill_handoff" else " window=64, int8 state")
+                        + (" (two chunks per window: the state stays fp32 at the chunk between window ends)"
+                           if name == "gdn_prefill_w128" else "")
                         + (", q and k rotated (WHT) and rounded to bf16" if name == "gdn_prefill_wht" else "")
                         + (f", the last {T % 64} tokens' writes handed to decode's window buffer"
                            if name == "gdn_prefill_handoff" else ""))

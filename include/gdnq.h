@@ -318,20 +318,25 @@ gdnq_status gdnq_prefill_chunked_noalloc(const gdnq_prefill_params* p, const voi
  *   requantize once at the window's end).
  *
  *   Same recurrence, parameters and layouts as gdnq_prefill_chunked in GDN
- *   mode (flags 0 or GDNQ_FLAG_STATE_4BIT, d_k = d_v = 128, chunk = window =
- *   64, in_dtype bf16),
- *   except that p->seqlen T need not be a multiple of 64.  With r = T mod 64:
- *     o          [B,T,H,128] out_dtype, every token (written)
+ *   mode (flags GDNQ_FLAG_STATE_4BIT and/or GDNQ_FLAG_WHT, d_k = d_v in
+ *   {128, 64} (the rotation at 128 only), chunk in {16, 32, 64}, in_dtype
+ *   bf16), with decode's window W in 1 .. 64, except that p->seqlen T need
+ *   not be a multiple of W.  With r = T mod W:
+ *     o          [B,T,H,d_v] out_dtype, every token (written)
  *     codes, scales: the state at the last window boundary (token T - r)
- *     buf_k, buf_v  decode's window buffer [B,H,W,128] in the format the
+ *     buf_k, buf_v  decode's window buffer [B,H,W,d] in the format the
  *                flags select (slots < r written): fp32 (no flag), bf16
  *                (GDNQ_FLAG_BUF_BF16: the bf16 inputs themselves), or FP8
  *                vector pairs (GDNQ_FLAG_BUF_FP8: E4M3 codes, then the
- *                per-vector fp32 scales, encoded as decode's append does)
+ *                per-vector fp32 scales, encoded as decode's append does);
+ *                under GDNQ_FLAG_WHT the keys are the rotated ones the
+ *                prefill used (rounded to bf16), and the state is in the
+ *                rotated basis, as decode with GDNQ_FLAG_WHT keeps them
  *     buf_alpha, buf_beta [B,H,W] fp32                        (slots < r written)
  *     fill_out   [B] int32 = r for every sequence (written)
  *   i.e. exactly decode's state after its last r steps: a decode step with
- *   fill_in = fill_out and the same buffer flag continues the sequence.
+ *   fill_in = fill_out and the same buffer and rotation flags continues the
+ *   sequence.
  *   workspace: gdnq_prefill_handoff_workspace_size(p) bytes.
  *   Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, FLAGS, WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */
@@ -350,7 +355,8 @@ gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, co
  *   recurrence, window buffer and boundary requantization per sequence).
  *
  *   p->batch B = number of sequences, p->seqlen T = total packed tokens;
- *   the other fields as for gdnq_prefill_handoff.
+ *   the other fields as for gdnq_prefill_handoff, with d_k = d_v = 128,
+ *   chunk = window = 64 and no GDNQ_FLAG_WHT.
  *     cu_seqlens [B+1] int32, device: sequence b holds packed tokens
  *                cu_seqlens[b] .. cu_seqlens[b+1]-1.  Expected
  *                0 = cu[0] <= cu[1] <= ... <= cu[B] = T.  The kernels take

@@ -199,7 +199,13 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
   return launched(gdnq::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch", stream);
 }
 
-static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillLaunch& L, bool handoff = false) {
+// What the prefill entry points take: chunked (whole windows), the uniform
+// hand-over to decode (any T; decode's window 1 .. 64), and the variable-length
+// and resuming hand-overs (window 64, d = 128, no rotation).
+enum PrefillMode { PF_CHUNKED = 0, PF_HANDOFF = 1, PF_MAPPED = 2 };
+
+static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillLaunch& L, int mode = PF_CHUNKED) {
+  const bool handoff = mode != PF_CHUNKED, mapped = mode == PF_MAPPED;
   if (!p) return fail(GDNQ_ERR_NULL, "params is NULL");
   const int B = p->batch, T = p->seqlen, H = p->heads, dk = p->d_k, dv = p->d_v;
   if (B < 0 || T < 0 || H < 1) return fail(GDNQ_ERR_SHAPE, "batch = %d, seqlen = %d, heads = %d", B, T, H);
@@ -210,14 +216,15 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   const int C = p->chunk, W = p->window;
   // GDN: chunk in {16, 32, 64} and any window (the kernels run every window
   // as whole 64-position chunks, so the result depends on the window only and
-  // the chunk is a blocking hint); the hand-over, varlen and resume calls and
-  // SSD take chunk = 64 (= window)
-  if (ssd || handoff) {
+  // the chunk is a blocking hint); the hand-over takes decode's windows
+  // (1 .. 64); the varlen and resume calls and SSD take chunk = 64 (= window)
+  if (ssd || mapped) {
     if (C != 64) return fail(GDNQ_ERR_SHAPE, "chunk = %d, expected 64", C);
-    if (!ssd && W != 64) return fail(GDNQ_ERR_SHAPE, "window = %d: the hand-over, varlen and resume calls take 64", W);
+    if (!ssd && W != 64) return fail(GDNQ_ERR_SHAPE, "window = %d: the varlen and resume calls take 64", W);
   } else {
     if (C != 16 && C != 32 && C != 64) return fail(GDNQ_ERR_SHAPE, "chunk = %d, expected 16, 32 or 64", C);
-    if (W < 1 || W > GDNQ_MAX_WINDOW) return fail(GDNQ_ERR_SHAPE, "window = %d, expected 1 .. %d", W, GDNQ_MAX_WINDOW);
+    const int wmax = handoff ? 64 : GDNQ_MAX_WINDOW;
+    if (W < 1 || W > wmax) return fail(GDNQ_ERR_SHAPE, "window = %d, expected 1 .. %d", W, wmax);
   }
   if (no_rq && (ssd || handoff))
     return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_NO_REQUANT: GDN gdnq_prefill_chunked only");
@@ -225,10 +232,11 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   // is never requantized has none either: any length)
   const int Wt = ssd ? 64 : no_rq ? 1 : W;
   if (T % Wt && !handoff) return fail(GDNQ_ERR_SHAPE, "seqlen = %d is not a multiple of the window (%d)", T, Wt);
-  // positions the chunk kernels see: windows padded to whole 64-position chunks
-  const int64_t Tk = ssd || handoff ? int64_t(T)
-                     : no_rq       ? (int64_t(T) + 63) / 64 * 64
-                                   : int64_t(T) / W * ((int64_t(W) + 63) / 64 * 64);
+  // positions the chunk kernels see: windows padded to whole 64-position
+  // chunks (the hand-over's open last window unpadded)
+  const int64_t Tk = ssd   ? int64_t(T)
+                     : no_rq ? (int64_t(T) + 63) / 64 * 64
+                             : int64_t(T) / W * ((int64_t(W) + 63) / 64 * 64) + T % W;
   if ((Tk + 64) * H * 512 >= (int64_t(1) << 32))  // 32-bit output offsets, padding positions included
     return fail(GDNQ_ERR_SHAPE, "seqlen * heads = %lld: one sequence's outputs must stay under 4 GiB",
                 (long long)T * H);
@@ -247,12 +255,12 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
                   "window-buffer format flag)", p->flags);
     if ((p->flags & bufs) == bufs)
       return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_BUF_BF16 and GDNQ_FLAG_BUF_FP8 are exclusive");
-    if ((p->flags & GDNQ_FLAG_WHT) && handoff)
-      return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_WHT: gdnq_prefill_chunked only (not the hand-over, varlen or resume calls)");
+    if ((p->flags & GDNQ_FLAG_WHT) && mapped)
+      return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_WHT: not the varlen or resume calls");
     if (!((dk == 128 && dv == 128) || (dk == 64 && dv == 64)))
       return fail(GDNQ_ERR_SHAPE, "GDN prefill: d_k = d_v = 128 or 64 required (got %d, %d)", dk, dv);
-    if (dk == 64 && handoff)
-      return fail(GDNQ_ERR_SHAPE, "GDN prefill at d = 64: gdnq_prefill_chunked only (not the hand-over, varlen or resume calls)");
+    if (dk == 64 && mapped)
+      return fail(GDNQ_ERR_SHAPE, "GDN prefill at d = 64: not the varlen or resume calls");
     if (dk == 64 && (p->flags & GDNQ_FLAG_WHT))
       return fail(GDNQ_ERR_FLAGS, "GDN prefill at d = 64 takes no GDNQ_FLAG_WHT");
   }
@@ -268,6 +276,8 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   L.buf_bf16 = handoff && (p->flags & GDNQ_FLAG_BUF_BF16) != 0;
   L.buf_fp8 = handoff && (p->flags & GDNQ_FLAG_BUF_FP8) != 0;
   L.no_requant = no_rq;
+  L.buf_W = W;
+  L.buf_d = dk;
   return GDNQ_OK;
 }
 
@@ -394,13 +404,13 @@ gdnq_status gdnq_prefill_chunked_noalloc(const gdnq_prefill_params* p, const voi
 
 size_t gdnq_prefill_handoff_workspace_size(const gdnq_prefill_params* p) {
   gdnq::PrefillLaunch L;
-  if (prefill_validate(p, L, true) != GDNQ_OK) return 0;
+  if (prefill_validate(p, L, PF_HANDOFF) != GDNQ_OK) return 0;
   return gdnq::prefill_workspace_bytes(L);
 }
 
 // Variable lengths: batch = sequences, seqlen = packed tokens in total.
 static gdnq_status varlen_validate(const gdnq_prefill_params* p, gdnq::PrefillLaunch& L) {
-  if (gdnq_status st = prefill_validate(p, L, true)) return st;
+  if (gdnq_status st = prefill_validate(p, L, PF_MAPPED)) return st;
   if ((int64_t(L.T) / 64 + L.B) * L.H > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "too many chunks");
   L.varlen = true;
   return GDNQ_OK;
@@ -486,7 +496,7 @@ gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, co
                                  float* buf_alpha, float* buf_beta, int32_t* fill_out,
                                  void* workspace, size_t workspace_bytes, void* stream) {
   gdnq::PrefillLaunch L;
-  if (gdnq_status st = prefill_validate(p, L, true)) return st;
+  if (gdnq_status st = prefill_validate(p, L, PF_HANDOFF)) return st;
   return prefill_handoff_impl(L, nullptr, nullptr, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales,
                               buf_k, buf_v, buf_alpha, buf_beta, fill_out, workspace, workspace_bytes, stream);
 }
@@ -507,7 +517,7 @@ gdnq_status gdnq_prefill_varlen(const gdnq_prefill_params* p, const int32_t* cu_
 // Resuming from decode: batch = sequences; seqlen = new tokens per sequence,
 // or packed new tokens in total with cu_seqlens.
 static gdnq_status resume_validate(const gdnq_prefill_params* p, bool varlen, gdnq::PrefillLaunch& L) {
-  if (gdnq_status st = prefill_validate(p, L, true)) return st;
+  if (gdnq_status st = prefill_validate(p, L, PF_MAPPED)) return st;
   const int64_t tokens = varlen ? int64_t(L.T) : int64_t(L.B) * L.T;
   if (tokens > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "%lld new tokens: at most 2^31 - 1", (long long)tokens);
   if ((tokens / 64 + 2 * int64_t(L.B)) * L.H > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "too many chunks");

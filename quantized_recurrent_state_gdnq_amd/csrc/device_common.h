@@ -53,6 +53,27 @@ __device__ __forceinline__ float wave_scan_incl(float x) {
   return x;
 }
 
+// Lanes l and l ^ 16 (v_permlane16_swap: rows 0 <-> 1, 2 <-> 3) and lanes l
+// and l ^ 32 (v_permlane32_swap: halves), on the VALU (gfx950): each returns
+// the pair (value of the lower lane, value of the upper lane), so a
+// commutative combination of the two is the same in both lanes.
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
 // Sum over aligned groups of N consecutive lanes (N = 1..64); every lane of a
 // group receives the group's sum.
 template <int N>
@@ -61,8 +82,8 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 4) x += dpp<DPP_XOR2>(x);
   if constexpr (N >= 8) x += dpp<DPP_ROW_HALF_MIRROR>(x);
   if constexpr (N >= 16) x += dpp<DPP_ROW_MIRROR>(x);
-  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+  if constexpr (N >= 32) x = xor16_sum(x);
+  if constexpr (N >= 64) x = xor32_sum(x);
   return x;
 }
 
@@ -72,8 +93,8 @@ __device__ __forceinline__ float group_max(float x) {
   if constexpr (N >= 4) x = fmaxf(x, dpp<DPP_XOR2>(x));
   if constexpr (N >= 8) x = fmaxf(x, dpp<DPP_ROW_HALF_MIRROR>(x));
   if constexpr (N >= 16) x = fmaxf(x, dpp<DPP_ROW_MIRROR>(x));
-  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16, 64));
-  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32, 64));
+  if constexpr (N >= 32) x = xor16_max(x);
+  if constexpr (N >= 64) x = xor32_max(x);
   return x;
 }
 
@@ -245,6 +266,33 @@ __device__ __forceinline__ void codec_codes(const float (&x)[N], float scale, fl
   }
 #pragma unroll
   for (int e = 0; e < N; ++e) c[e] = fminf(fmaxf(c[e], -float(QMAX)), float(QMAX));
+}
+
+// The same codes from the row's absmax: scale = fl(absmax / QMAX) and
+// inv = fl(QMAX / absmax), two independent divisions.  inv is within 2^-23
+// (relative) of 1 / scale, so q = fl(x * inv) is within |x/scale| 1.8e-7 <=
+// 2.3e-5 of the exact quotient and fl(x/scale) within 7.6e-6: their nearest
+// integers can differ only when q lies within 3.1e-5 of a half-integer, and
+// those rows divide.  Returns the scale.
+template <int N, int QMAX = 127>
+__device__ __forceinline__ float codec_row(const float (&x)[N], float absmax, float (&c)[N]) {
+  const float scale = codec_scale<QMAX>(absmax);
+  const float inv = absmax > 0.0f ? __fdiv_rn(float(QMAX), absmax) : 0.0f;
+  bool near = scale > 0.0f && scale < 1.17549435e-38f;  // subnormal: divide
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const float q = x[e] * inv;
+    const float r = __builtin_rintf(q);
+    near |= fabsf(fabsf(q - r) - 0.5f) < 4.0e-5f;
+    c[e] = r;
+  }
+  if (near) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) c[e] = __builtin_rintf(__fdiv_rn(x[e], scale));
+  }
+#pragma unroll
+  for (int e = 0; e < N; ++e) c[e] = fminf(fmaxf(c[e], -float(QMAX)), float(QMAX));
+  return scale;
 }
 
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {

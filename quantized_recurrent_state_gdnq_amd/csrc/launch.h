@@ -70,6 +70,7 @@ struct PrefillLaunch {
   bool q4;  // GDN: the state as packed 4-bit codes
   bool buf_bf16, buf_fp8;  // hand-over: the window buffer's format
   bool no_requant;  // GDN: never requantize; the final fp32 state goes to state_f32
+  int buf_W, buf_d;  // hand-over: decode's window (slots per head) and vector length of its buffer
 };
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream);
 hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream);

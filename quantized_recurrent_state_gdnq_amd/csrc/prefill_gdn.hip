@@ -503,8 +503,7 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
           for (int q = 0; q < 4; ++q) am = fmaxf(am, fabsf(cf[dt][q]));
-        am = fmaxf(am, __shfl_xor(am, 16));
-        am = fmaxf(am, __shfl_xor(am, 32));
+        am = xor32_max(xor16_max(am));  // the row's other three lane groups
         const float inv = am > 0.f ? 127.f / am : 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -675,17 +674,15 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
           for (int q = 0; q < 4; ++q) sn[4 * dt + q] = gs * cf[dt][q] + acc[q];
         }
         if (!CARRY || (a.cpw > 0 && (c + 1) % a.cpw == 0)) {
-          float amax = 0.f;
+          float m4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial maxima
 #pragma unroll
-          for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(sn[e]));
-          amax = fmaxf(amax, __shfl_xor(amax, 16));  // the row's other three lane groups
-          amax = fmaxf(amax, __shfl_xor(amax, 32));
-          const float scale = codec_scale<QMAX>(amax);
+          for (int e = 0; e < 32; ++e) m4[e & 3] = fmaxf(m4[e & 3], fabsf(sn[e]));
+          // the row's other three lane groups
+          const float amax = xor32_max(xor16_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))));
           float cn[32];
-          codec_codes<32, QMAX>(sn, scale, cn);
+          s = codec_row<32, QMAX>(sn, amax, cn);
 #pragma unroll
           for (int e = 0; e < 32; ++e) cf[e >> 2][e & 3] = cn[e];
-          s = scale;
         } else {  // inside a window: the state stays fp32
 #pragma unroll
           for (int e = 0; e < 32; ++e) cf[e >> 2][e & 3] = sn[e];
@@ -1003,8 +1000,12 @@ struct PadArgs {
   int rb64;              // bytes per stored row at d = 64: 64 (8-bit) or 32 (4-bit)
 };
 
+// Positions of a padded sequence: its whole windows of Wp positions, then the
+// T mod W tokens of an open last window (the hand-over) unpadded.
+__device__ __forceinline__ int64_t padded_len(int64_t T, int W, int Wp) { return T / W * Wp + T % W; }
+
 __global__ __launch_bounds__(256) void gdn_pad_kernel(PadArgs a) {
-  const int64_t Tp = a.T / a.W * a.Wp;
+  const int64_t Tp = padded_len(a.T, a.W, a.Wp);
   const int64_t rows = a.B * Tp * a.H;  // padded rows
   const int64_t stride = int64_t(gridDim.x) * 256;
   const int gs = a.ds / 8;  // 16-byte granules per source row
@@ -1065,7 +1066,7 @@ struct UnpadArgs {
 
 __global__ __launch_bounds__(256) void gdn_unpad_kernel(UnpadArgs a) {
   const int gpr = a.ds * a.eo / 16;  // 16-byte granules per output row
-  const int64_t Tp = a.T / a.W * a.Wp;
+  const int64_t Tp = padded_len(a.T, a.W, a.Wp);
   const int64_t n = a.B * a.T * a.H * gpr;
   const int64_t stride = int64_t(gridDim.x) * 256;
   for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n; e += stride) {
@@ -1344,7 +1345,8 @@ struct HandoffArgs {
   float* buf_beta;
   int32_t* fill_out;
   SeqMap sm;
-  int B, H, W;
+  int B, H, W;  // W: decode's window (buffer slots per head)
+  int ds;       // elements of a buffered key / value (64 or 128; the source rows hold 128)
 };
 
 __global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
@@ -1354,13 +1356,14 @@ __global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
   const int p0 = len - r;  // position of slot 0
   const int s0 = max(pre - p0, 0);  // first slot that takes a new token
   const size_t t0 = a.sm.tok0(b);
-  // 8 dims per thread: a slot's 16 threads are 16 consecutive lanes (the
-  // bound is a multiple of 16), so an FP8 vector's absmax is a 16-lane
-  // reduction inside one wave
-  for (int e = threadIdx.x; e < (r - s0) * (PD / 8); e += 256) {
-    const int slot = s0 + e / (PD / 8), d = 8 * (e % (PD / 8));
+  // 8 dims per thread: a slot's ds / 8 threads are consecutive lanes (the
+  // stride 256 is a multiple of that), so an FP8 vector's absmax is a 16- or
+  // 8-lane reduction inside one wave
+  const int per = a.ds / 8;
+  for (int e = threadIdx.x; e < (r - s0) * per; e += 256) {
+    const int slot = s0 + e / per, d = 8 * (e % per);
     const size_t src = ((t0 + (p0 + slot - pre)) * a.H + h) * PD + d;
-    const size_t sl = size_t(bh) * a.W + slot, dst = sl * PD + d;
+    const size_t sl = size_t(bh) * a.W + slot, dst = sl * a.ds + d;
     const uint4 kw = *reinterpret_cast<const uint4*>(a.k + src);
     const uint4 vw = *reinterpret_cast<const uint4*>(a.v + src);
     if (a.fmt == 1) {
@@ -1384,8 +1387,10 @@ __global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
         mk = fmaxf(mk, fabsf(kf[i]));
         mv = fmaxf(mv, fabsf(vf[i]));
       }
-      const float sk = __fdiv_rn(group_max<16>(mk), 448.f);
-      const float sv = __fdiv_rn(group_max<16>(mv), 448.f);
+      mk = per == 16 ? group_max<16>(mk) : group_max<8>(mk);
+      mv = per == 16 ? group_max<16>(mv) : group_max<8>(mv);
+      const float sk = __fdiv_rn(mk, 448.f);
+      const float sv = __fdiv_rn(mv, 448.f);
       uint32_t ck[2], cv[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -1433,7 +1438,7 @@ static bool gdn_padded(const PrefillLaunch& L) { return L.d_k == 64 || gdn_windo
 static PrefillLaunch gdn_padded_launch(const PrefillLaunch& L) {
   PrefillLaunch L2 = L;
   L2.d_k = L2.d_v = PD;
-  L2.T = L.T / gdn_window(L) * gdn_window_padded(L);
+  L2.T = L.T / gdn_window(L) * gdn_window_padded(L) + L.T % gdn_window(L);
   L2.W = gdn_window_padded(L);
   L2.C = PC;
   return L2;
@@ -1523,7 +1528,8 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
 static int gdn_buf_fmt(const PrefillLaunch& L) { return L.buf_fp8 ? 2 : L.buf_bf16 ? 1 : 0; }
 // FP8 window buffer: the fp32 scales follow the B H W d code bytes
 static float* gdn_fp8_scales(const PrefillLaunch& L, void* codes) {
-  return L.buf_fp8 ? reinterpret_cast<float*>(static_cast<uint8_t*>(codes) + size_t(L.B) * L.H * L.W * PD) : nullptr;
+  return L.buf_fp8 ? reinterpret_cast<float*>(static_cast<uint8_t*>(codes) + size_t(L.B) * L.H * L.buf_W * L.buf_d)
+                   : nullptr;
 }
 
 static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t stream) {
@@ -1565,7 +1571,7 @@ static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t st
       StageArgs g{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k),
                   static_cast<const uint16_t*>(L.v), L.alpha, L.beta, L.buf_k, L.buf_v,
                   gdn_fp8_scales(L, L.buf_k), gdn_fp8_scales(L, L.buf_v), gdn_buf_fmt(L), L.buf_alpha,
-                  L.buf_beta, sk, sq, sv, sa, sb, sm, L.B, L.H, L.W};
+                  L.buf_beta, sk, sq, sv, sa, sb, sm, L.B, L.H, L.buf_W};
       g.sm.pre = pre;  // the staging kernel reads the prefixes, not yet the staged copy
       hipLaunchKernelGGL(gdn_stage_kernel, dim3(unsigned(L.B) * L.H), dim3(256), 0, stream, g);
       if (hipError_t e = hipGetLastError()) return e;
@@ -1602,7 +1608,7 @@ static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t st
   if (L.handoff && L.B > 0) {
     HandoffArgs h{static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v), L.alpha, L.beta,
                   L.buf_k, L.buf_v, gdn_fp8_scales(L, L.buf_k), gdn_fp8_scales(L, L.buf_v), gdn_buf_fmt(L),
-                  L.buf_alpha, L.buf_beta, L.fill_out, sm, L.B, L.H, L.W};
+                  L.buf_alpha, L.buf_beta, L.fill_out, sm, L.B, L.H, L.buf_W, L.buf_d};
     hipLaunchKernelGGL(gdn_handoff_kernel, dim3(unsigned(L.B) * L.H), dim3(256), 0, stream, h);
     return hipGetLastError();
   }

@@ -51,16 +51,17 @@ _BUF_FLAGS = {torch.float32: 0, torch.bfloat16: _lib.GDNQ_FLAG_BUF_BF16,
               torch.float8_e4m3fn: _lib.GDNQ_FLAG_BUF_FP8}
 
 
-def _state_shapes(st, B, H, d_k, d_v, window):
+def _state_shapes(st, B, H, d_k, d_v, window, wht=False):
     """A DecodeState handed to a prefill entry point: a window buffer of
     `window` slots (fp32, bf16 or FP8 vector pairs), codes/scales/fill of B
-    sequences.  Returns the window-buffer format flag."""
+    sequences, rotated (keys and state in the rotated basis) exactly when
+    `wht`.  Returns the window-buffer format flag."""
     if st.buf_k.dtype not in _BUF_FLAGS or st.buf_v.dtype != st.buf_k.dtype:
         raise ValueError("state: window buffers of fp32, bf16 or float8_e4m3fn (both alike)")
     if getattr(st, "sliding", False):
         raise ValueError("state: the prefill hand-over fills a tumbling window, not a sliding one")
-    if st.wht:
-        raise ValueError("state: the prefill hand-over runs without the rotation (its keys stay unrotated)")
+    if bool(st.wht) != bool(wht):
+        raise ValueError("state: its rotation (wht) must match the prefill's")
     if st.window != window:
         raise ValueError(f"state: window {st.window}, the prefill hand-over needs {window}")
     _shape(st.codes, (B, H, d_v, d_k * st.state_bits // 8), "state.codes")
@@ -281,13 +282,15 @@ def prefill_handoff_workspace_size(q, v, *, window=64, out_dtype=torch.bfloat16)
 
 def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_scales=None,
                     out_dtype=torch.bfloat16, o=None, state=None, workspace=None, state_bits=8,
-                    buf_dtype=torch.float32):
+                    buf_dtype=torch.float32, wht=False, chunk=64):
     """GDN prefill of any T tokens handed over to decode (see
     gdnq_prefill_handoff in include/gdnq.h): returns (o, DecodeState) whose
     codes/scales are the state at the last window boundary and whose window
-    buffer (fp32, bf16 or FP8 vector pairs: buf_dtype, or the given state's)
-    holds the last T mod 64 writes, with that fill.  o, state and workspace
-    may be given to reuse their memory."""
+    buffer (decode's `window` of 1..64 slots; fp32, bf16 or FP8 vector pairs:
+    buf_dtype, or the given state's) holds the last T mod window writes, with
+    that fill; with wht=True q and k are rotated and the state and buffered
+    keys are in the rotated basis.  o, state and workspace may be given to
+    reuse their memory."""
     dev = q.device
     B, T, H, d_k = q.shape
     d_v = v.shape[-1]
@@ -306,13 +309,13 @@ def prefill_handoff(q, k, v, alpha, beta, *, window=64, init_codes=None, init_sc
     if st is None:
         st = DecodeState(torch.empty((B, H, d_v, d_k * state_bits // 8), dtype=torch.int8, device=dev),
                          torch.empty((B, H, d_v), dtype=torch.float32, device=dev), window,
-                         fill=torch.zeros(B, dtype=torch.int32, device=dev), state_bits=state_bits,
+                         fill=torch.zeros(B, dtype=torch.int32, device=dev), wht=wht, state_bits=state_bits,
                          buf_dtype=buf_dtype)
     if st.state_bits != state_bits:
         raise ValueError("state: its code width differs from state_bits")
-    p = _prefill_params(q, v, window=window, chunk=64, wht=False, ssd=False, int8_qk=False,
+    p = _prefill_params(q, v, window=window, chunk=chunk, wht=wht, ssd=False, int8_qk=False,
                         out_dtype=out_dtype, state_bits=state_bits,
-                        extra_flags=_state_shapes(st, B, H, d_k, d_v, 64))
+                        extra_flags=_state_shapes(st, B, H, d_k, d_v, window, wht))
     need = int(_lib.prefill_handoff_workspace_size(p))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

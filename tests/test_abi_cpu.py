@@ -195,14 +195,14 @@ def test_prefill_rejects_bad_params(params, status):
 
 
 def test_prefill_gdn_rotation_flag():
-    """GDNQ_FLAG_WHT is accepted by the chunked GDN prefill (it needs a larger
-    workspace: the rotated q and k) and refused by the hand-over, varlen and
+    """GDNQ_FLAG_WHT is accepted by the chunked GDN prefill and the hand-over
+    (a larger workspace: the rotated q and k) and refused by the varlen and
     resume calls."""
     p0, p1 = _pp(), _pp(flags=1)
     assert L.gdnq_prefill_workspace_size(p1) == L.gdnq_prefill_workspace_size(p0) + 2 * 1 * 128 * 2 * 128 * 2
     f = Fake()
     assert _prefill(p1, f, ws=L.gdnq_prefill_workspace_size(p0), workspace=f()) == 6  # too small
-    assert L.gdnq_prefill_handoff_workspace_size(p1) == 0
+    assert L.gdnq_prefill_handoff_workspace_size(p1) == L.gdnq_prefill_handoff_workspace_size(p0) + 2 * 128 * 2 * 128 * 2
     assert L.gdnq_prefill_varlen_workspace_size(p1) == 0
 
 
@@ -230,15 +230,15 @@ def test_window_and_chunk_sizes():
     """GDN prefill takes windows and chunks of 16, 32 or 64.  A window
     below 64 runs on padded copies (a larger workspace, growing as the window
     shrinks); the chunk is a blocking hint that does not change the
-    workspace.  The hand-over, varlen and resume calls and SSD take 64."""
+    workspace.  The varlen and resume calls and SSD take 64."""
     sz = {(W, C): L.gdnq_prefill_workspace_size(_pp(T=256, W=W, C=C)) for W in (16, 32, 64) for C in (16, 32, 64)}
     assert all(v > 0 for v in sz.values())
     for W in (16, 32, 64):
         assert sz[(W, 16)] == sz[(W, 32)] == sz[(W, 64)]
     assert sz[(16, 64)] > sz[(32, 64)] > sz[(64, 64)]
     assert L.gdnq_prefill_workspace_size(_pp(T=48, W=16, C=16)) > 0
-    assert L.gdnq_prefill_handoff_workspace_size(_pp(T=256, W=32, C=32)) == 0
-    assert L.gdnq_prefill_handoff_workspace_size(_pp(T=256, W=64, C=32)) == 0
+    assert L.gdnq_prefill_varlen_workspace_size(_pp(T=256, W=32, C=32)) == 0
+    assert L.gdnq_prefill_varlen_workspace_size(_pp(T=256, W=64, C=32)) == 0
     assert L.gdnq_prefill_workspace_size(_pp(T=256, dv=64, flags=2 | 4)) > 0
     assert L.gdnq_prefill_workspace_size(_pp(T=256, dv=64, C=32, W=32, flags=2 | 4)) == 0  # SSD: chunk 64
 
@@ -324,14 +324,34 @@ def _handoff(params, fake, **over):
 
 
 @pytest.mark.parametrize("params,status", [
-    (_pp(C=32, W=32), 2), (_pp(dk=64, dv=64), 2), (_pp(W=128), 2), (_pp(ind=0), 3),
-    (_pp(flags=1), 8), (_pp(dv=64, flags=2 | 1 | 4), 8),   # GDN only
+    (_pp(W=128), 2), (_pp(W=0), 2), (_pp(C=8), 2), (_pp(ind=0), 3),  # decode's windows: 1 .. 64
+    (_pp(dv=64, flags=2 | 1 | 4), 8),                      # GDN only
+    (_pp(dk=64, dv=64, flags=1), 8),                       # no rotation at d = 64
+    (_pp(flags=8), 8),                                     # the hand-over requantizes
     (_pp(T=1 << 20, H=8192), 2),                           # one sequence's outputs past 4 GiB
     (_pp(flags=16 | 32), 8),                               # one window-buffer format
-    (_pp(W=32, C=64), 2),                                  # decode's window: 64
 ])
 def test_handoff_rejects_bad_params(params, status):
     assert _handoff(params, Fake()) == status
+
+
+def test_handoff_windows_and_shapes():
+    """The uniform hand-over takes decode's windows 1 .. 64, d = 64 and the
+    rotation: a window below 64 or d = 64 runs on padded copies (a larger
+    workspace); T need not be a multiple of the window.  The varlen and
+    resume calls keep window 64, d = 128 and no rotation."""
+    base = _lib.prefill_handoff_workspace_size(_pp(T=100))
+    assert base > 0
+    for W, C in ((1, 16), (16, 16), (32, 64), (48, 16), (64, 32)):
+        assert _lib.prefill_handoff_workspace_size(_pp(T=100, W=W, C=C)) > 0, (W, C)
+    assert _lib.prefill_handoff_workspace_size(_pp(T=100, W=16)) > base
+    assert _lib.prefill_handoff_workspace_size(_pp(T=100, dk=64, dv=64)) > 0
+    assert _lib.prefill_handoff_workspace_size(_pp(T=100, flags=1)) == base + 2 * 100 * 2 * 128 * 2
+    assert _lib.prefill_varlen_workspace_size(_pp(T=100, W=32)) == 0
+    assert _lib.prefill_varlen_workspace_size(_pp(T=100, dk=64, dv=64)) == 0
+    assert _lib.prefill_varlen_workspace_size(_pp(T=100, flags=1)) == 0
+    assert _lib.prefill_resume_workspace_size(_pp(T=100, W=32), 0) == 0
+    assert _lib.prefill_resume_workspace_size(_pp(T=100, flags=1), 0) == 0
 
 
 def test_handoff_contract():
