@@ -255,8 +255,6 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
                   "window-buffer format flag)", p->flags);
     if ((p->flags & bufs) == bufs)
       return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_BUF_BF16 and GDNQ_FLAG_BUF_FP8 are exclusive");
-    if ((p->flags & GDNQ_FLAG_WHT) && mapped)
-      return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_WHT: not the varlen or resume calls");
     if (!((dk == 128 && dv == 128) || (dk == 64 && dv == 64)))
       return fail(GDNQ_ERR_SHAPE, "GDN prefill: d_k = d_v = 128 or 64 required (got %d, %d)", dk, dv);
     if (dk == 64 && mapped)

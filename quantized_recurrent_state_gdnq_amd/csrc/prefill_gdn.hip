@@ -1163,7 +1163,9 @@ static size_t gdn_ws_stage(const PrefillLaunch& L) {
 static bool gdn_mapped(const PrefillLaunch& L) { return L.varlen || L.resume; }
 static size_t gdn_ws_map(const PrefillLaunch& L) { return gdn_mapped(L) ? (4 * size_t(L.B) + 2) * 4 : 0; }
 // rotated q and k (GDNQ_FLAG_WHT, whole windows only): [2][B*T*H][128] bf16
-static size_t gdn_ws_rot(const PrefillLaunch& L) { return L.wht ? 2 * size_t(L.B) * L.T * L.H * PD * 2 : 0; }
+// token rows of q and k: B T H, or T H packed tokens (variable lengths)
+static size_t gdn_token_rows(const PrefillLaunch& L) { return (L.varlen ? size_t(1) : size_t(L.B)) * L.T * L.H; }
+static size_t gdn_ws_rot(const PrefillLaunch& L) { return L.wht ? 2 * gdn_token_rows(L) * PD * 2 : 0; }
 constexpr int ORDER_MAXB = 1024;  // sequences ranked by length (more: taken in order)
 
 // Sequence map, one workgroup.  Token offsets tok[i]: with cu, the running
@@ -1537,7 +1539,7 @@ static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t st
   char* ws = static_cast<char*>(L.workspace);
   if (L.wht && L.B > 0 && L.T > 0) {  // rotate q and k once; the chunk kernels read the rotated rows
     uint16_t* rq = reinterpret_cast<uint16_t*>(ws + gdn_ws_T(L) + gdn_ws_g(L) + gdn_ws_stage(L) + gdn_ws_map(L));
-    const int64_t rows = int64_t(L.B) * L.T * L.H;
+    const int64_t rows = int64_t(gdn_token_rows(L));
     uint16_t* rk = rq + rows * PD;
     RotateArgs ra{{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k)}, {rq, rk}, rows};
     hipLaunchKernelGGL(gdn_rotate_kernel, dim3(unsigned((rows + 63) / 64), 2), dim3(256), 0, stream, ra);

@@ -274,8 +274,8 @@ def _init_shapes(init_codes, init_scales, cshape, dev):
         _shape(_need(init_scales, "init_scales", torch.float32, dev), cshape[:3], "init_scales")
 
 
-def prefill_handoff_workspace_size(q, v, *, window=64, out_dtype=torch.bfloat16):
-    p = _prefill_params(q, v, window=window, chunk=64, wht=False, ssd=False, int8_qk=False,
+def prefill_handoff_workspace_size(q, v, *, window=64, out_dtype=torch.bfloat16, wht=False, chunk=64):
+    p = _prefill_params(q, v, window=window, chunk=chunk, wht=wht, ssd=False, int8_qk=False,
                         out_dtype=out_dtype)
     return int(_lib.prefill_handoff_workspace_size(p))
 
@@ -334,20 +334,22 @@ def _varlen_params(q, v, n_seqs, *, window, out_dtype, state_bits=8, extra_flags
                               _DT[out_dtype], (_lib.GDNQ_FLAG_STATE_4BIT if state_bits == 4 else 0) | extra_flags)
 
 
-def prefill_varlen_workspace_size(q, v, n_seqs, *, window=64, out_dtype=torch.bfloat16):
-    p = _varlen_params(q, v, n_seqs, window=window, out_dtype=out_dtype)
+def prefill_varlen_workspace_size(q, v, n_seqs, *, window=64, out_dtype=torch.bfloat16, wht=False):
+    p = _varlen_params(q, v, n_seqs, window=window, out_dtype=out_dtype,
+                       extra_flags=_lib.GDNQ_FLAG_WHT if wht else 0)
     return int(_lib.prefill_varlen_workspace_size(p))
 
 
 def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=None,
                    init_scales=None, out_dtype=torch.bfloat16, o=None, state=None,
-                   workspace=None, state_bits=8, buf_dtype=torch.float32):
+                   workspace=None, state_bits=8, buf_dtype=torch.float32, wht=False):
     """GDN prefill of a packed batch of variable-length sequences handed over
     to decode (see gdnq_prefill_varlen in include/gdnq.h).  q, k [T,H,d_k],
     v [T,H,d_v] bf16 and alpha, beta [T,H] fp32 hold the sequences back to
     back; cu_seqlens (int32 on the device, B+1 entries) gives where each
     starts.  Returns (o [T,H,d_v], DecodeState of B sequences; its window
-    buffer of buf_dtype, or the given state's)."""
+    buffer of buf_dtype, or the given state's); wht=True rotates q and k
+    (state and buffered keys in the rotated basis)."""
     dev = q.device
     T, H, d_k = q.shape
     d_v = v.shape[-1]
@@ -370,12 +372,13 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=No
     if st is None:
         st = DecodeState(torch.empty((B, H, d_v, d_k * state_bits // 8), dtype=torch.int8, device=dev),
                          torch.empty((B, H, d_v), dtype=torch.float32, device=dev), window,
-                         fill=torch.zeros(B, dtype=torch.int32, device=dev), state_bits=state_bits,
+                         fill=torch.zeros(B, dtype=torch.int32, device=dev), wht=wht, state_bits=state_bits,
                          buf_dtype=buf_dtype)
     if st.state_bits != state_bits:
         raise ValueError("state: its code width differs from state_bits")
     p = _varlen_params(q, v, B, window=window, out_dtype=out_dtype, state_bits=state_bits,
-                       extra_flags=_state_shapes(st, B, H, d_k, d_v, 64))
+                       extra_flags=_state_shapes(st, B, H, d_k, d_v, 64, wht)
+                       | (_lib.GDNQ_FLAG_WHT if wht else 0))
     need = int(_lib.prefill_varlen_workspace_size(p))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -388,12 +391,12 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=No
     return o, st
 
 
-def prefill_resume_workspace_size(q, v, n_seqs, *, packed=False, out_dtype=torch.bfloat16):
+def prefill_resume_workspace_size(q, v, n_seqs, *, packed=False, out_dtype=torch.bfloat16, wht=False):
     """Workspace of prefill_resume: q [B,T,H,d_k] (n_seqs = B), or packed
     q [T,H,d_k] of n_seqs sequences."""
     T = q.shape[0] if packed else q.shape[1]
     p = _lib.PrefillParams(n_seqs, T, q.shape[-2], q.shape[-1], v.shape[-1], 64, 64, _DT[q.dtype],
-                           _DT[out_dtype], 0)
+                           _DT[out_dtype], _lib.GDNQ_FLAG_WHT if wht else 0)
     return int(_lib.prefill_resume_workspace_size(p, packed))
 
 
@@ -409,7 +412,7 @@ def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=to
     st = state
     B, H, d_v, d_k = st.codes.shape
     d_k = d_k * 8 // st.state_bits
-    buf_flag = _state_shapes(st, B, H, d_k, d_v, 64)
+    buf_flag = _state_shapes(st, B, H, d_k, d_v, 64, st.wht)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, torch.bfloat16, dev)
     for name, t in (("alpha", alpha), ("beta", beta)):
@@ -430,7 +433,8 @@ def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=to
             or tuple(beta.shape) != lead + (H,)):
         raise ValueError("inconsistent resume shapes")
     p = _lib.PrefillParams(B, T, H, d_k, d_v, 64, 64, _DT[q.dtype], _DT[out_dtype],
-                           (_lib.GDNQ_FLAG_STATE_4BIT if st.state_bits == 4 else 0) | buf_flag)
+                           (_lib.GDNQ_FLAG_STATE_4BIT if st.state_bits == 4 else 0) | buf_flag
+                           | (_lib.GDNQ_FLAG_WHT if st.wht else 0))
     if o is None:
         o = torch.empty(lead + (H, d_v), dtype=out_dtype, device=dev)
     _shape(_need(o, "o", out_dtype, dev), lead + (H, d_v), "o")

@@ -195,15 +195,14 @@ def test_prefill_rejects_bad_params(params, status):
 
 
 def test_prefill_gdn_rotation_flag():
-    """GDNQ_FLAG_WHT is accepted by the chunked GDN prefill and the hand-over
-    (a larger workspace: the rotated q and k) and refused by the varlen and
-    resume calls."""
+    """GDNQ_FLAG_WHT is accepted by every GDN prefill call (a larger workspace:
+    the rotated q and k)."""
     p0, p1 = _pp(), _pp(flags=1)
     assert L.gdnq_prefill_workspace_size(p1) == L.gdnq_prefill_workspace_size(p0) + 2 * 1 * 128 * 2 * 128 * 2
     f = Fake()
     assert _prefill(p1, f, ws=L.gdnq_prefill_workspace_size(p0), workspace=f()) == 6  # too small
     assert L.gdnq_prefill_handoff_workspace_size(p1) == L.gdnq_prefill_handoff_workspace_size(p0) + 2 * 128 * 2 * 128 * 2
-    assert L.gdnq_prefill_varlen_workspace_size(p1) == 0
+    assert L.gdnq_prefill_varlen_workspace_size(p1) == L.gdnq_prefill_varlen_workspace_size(p0) + 2 * 128 * 2 * 128 * 2
 
 
 def test_prefill_gdn_contract():
@@ -339,7 +338,7 @@ def test_handoff_windows_and_shapes():
     """The uniform hand-over takes decode's windows 1 .. 64, d = 64 and the
     rotation: a window below 64 or d = 64 runs on padded copies (a larger
     workspace); T need not be a multiple of the window.  The varlen and
-    resume calls keep window 64, d = 128 and no rotation."""
+    resume calls take the rotation and keep window 64 and d = 128."""
     base = _lib.prefill_handoff_workspace_size(_pp(T=100))
     assert base > 0
     for W, C in ((1, 16), (16, 16), (32, 64), (48, 16), (64, 32)):
@@ -349,9 +348,10 @@ def test_handoff_windows_and_shapes():
     assert _lib.prefill_handoff_workspace_size(_pp(T=100, flags=1)) == base + 2 * 100 * 2 * 128 * 2
     assert _lib.prefill_varlen_workspace_size(_pp(T=100, W=32)) == 0
     assert _lib.prefill_varlen_workspace_size(_pp(T=100, dk=64, dv=64)) == 0
-    assert _lib.prefill_varlen_workspace_size(_pp(T=100, flags=1)) == 0
+    assert _lib.prefill_varlen_workspace_size(_pp(T=100, flags=1)) == (_lib.prefill_varlen_workspace_size(_pp(T=100))
+                                                                       + 2 * 100 * 2 * 128 * 2)  # T H packed rows
     assert _lib.prefill_resume_workspace_size(_pp(T=100, W=32), 0) == 0
-    assert _lib.prefill_resume_workspace_size(_pp(T=100, flags=1), 0) == 0
+    assert _lib.prefill_resume_workspace_size(_pp(T=100, flags=1), 0) > _lib.prefill_resume_workspace_size(_pp(T=100), 0)
 
 
 def test_handoff_contract():
@@ -422,7 +422,7 @@ def _varlen(params, fake, cu="fake", **over):
 
 @pytest.mark.parametrize("params,status", [
     (_pp(C=32, W=32), 2), (_pp(dk=64, dv=64), 2), (_pp(ind=0), 3),
-    (_pp(flags=1), 8), (_pp(dv=64, flags=2 | 1 | 4), 8),   # GDN only
+    (_pp(flags=8), 8), (_pp(dv=64, flags=2 | 1 | 4), 8),   # GDN only, requantizing
     (_pp(T=1 << 20, H=8192), 2),                           # the packed outputs past 4 GiB
 ])
 def test_varlen_rejects_bad_params(params, status):
@@ -472,7 +472,7 @@ def _resume(params, fake, cu=None, fill_in="fake", **over):
 
 @pytest.mark.parametrize("params,status", [
     (_pp(C=32, W=32), 2), (_pp(dk=64, dv=64), 2), (_pp(ind=0), 3),
-    (_pp(flags=1), 8), (_pp(dv=64, flags=2 | 1 | 4), 8),   # GDN only
+    (_pp(flags=8), 8), (_pp(dv=64, flags=2 | 1 | 4), 8),   # GDN only, requantizing
     (_pp(B=1 << 16, T=1 << 16), 2),                        # 2^32 new tokens
 ])
 def test_resume_rejects_bad_params(params, status):

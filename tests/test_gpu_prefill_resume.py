@@ -153,3 +153,43 @@ def test_resume_varlen_longest_first_order():
     for b, f in enumerate(fills):
         t0, t1 = int(cu[b]), int(cu[b + 1])
         _check_seq(st, o[t0:t1], pre, f, {key: x[key][t0:t1] for key in KEYS}, b, codes, scales)
+
+
+def test_resume_rotated():
+    """GDNQ_FLAG_WHT: a rotated decode state (stored state in the rotated
+    basis; buffered keys the rotated bf16 keys a rotated hand-over leaves) at
+    fills 0, 17 and 63 resumes with 100 new tokens each.  The new tokens'
+    rotated q and k (read back from the workspace) match the oracle's
+    rotation up to rounding ties on <= 0.1%; on those operands, after the
+    buffered writes, every sequence is held to the bars above."""
+    H, d, T = 2, 128, 100
+    fills = [0, 17, 63]
+    B = len(fills)
+    st, codes, scales, pre = _decode_state(fills, H, d, seed=450)
+    g = np.random.default_rng(451)
+    S = (g.standard_normal((B, H, d, d)) * 0.5).astype(np.float32)
+    codes, scales = O.quantize_rows(O.gdnq_oracle.rotate(S, np.float32))
+    st.codes.copy_(dev(codes))
+    st.scales.copy_(dev(scales))
+    st.wht = True
+    # the buffered keys in the rotated basis, as bf16 values (what the rotated
+    # prefill hands over)
+    pre = dict(pre, k=O.round_bf16(O.gdnq_oracle.rotate(pre["k"], np.float32)))
+    bk = np.zeros((B, H, W, d), np.float32)
+    for b, f in enumerate(fills):
+        bk[b, :, :f] = np.moveaxis(pre["k"][b, :f], 0, 1)
+    st.buf_k.copy_(dev(bk))
+    x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=452)
+    t = {key: dev(x[key], torch.bfloat16 if key in ("q", "k", "v") else None) for key in KEYS}
+    need = ops.prefill_resume_workspace_size(t["q"], t["v"], B, out_dtype=torch.float32, wht=True)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o = ops.prefill_resume(st, *(t[key] for key in KEYS), out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    rows = B * T * H
+    rot = host(ws[need - 2 * rows * d * 2:]).view(np.uint16).reshape(2, B, T, H, d)
+    qr, kr = (wl.bf16_to_f32(rot[i]) for i in range(2))
+    for name, got, src in (("q", qr, x["q"]), ("k", kr, x["k"])):
+        assert np.mean(got != O.round_bf16(O.gdnq_oracle.rotate(src, np.float32))) <= 1e-3, name
+    xr = dict(x, q=qr, k=kr)
+    for b, f in enumerate(fills):
+        _check_seq(st, o[b], pre, f, {key: xr[key][b] for key in KEYS}, b, codes, scales)

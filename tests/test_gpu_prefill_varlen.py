@@ -190,3 +190,36 @@ def test_varlen_longest_first_order(H):
     torch.cuda.synchronize()
     for b in range(B):
         _check_seq(x, cu, b, o, st, codes, scales)
+
+
+def test_varlen_rotated():
+    """GDNQ_FLAG_WHT on a packed batch (lengths 0, 37, 100, 64 and 130, H=3,
+    from stored states in the rotated basis): the rotated q and k rows the
+    kernels used (all T H packed rows, read back from the workspace) match the
+    oracle's rotation and bf16 rounding up to rounding ties on <= 0.1%; on
+    those operands every sequence is held to the bars above, its buffered
+    keys being the rotated ones."""
+    lengths = [0, 37, 100, 64, 130]
+    H, d = 3, 128
+    B = len(lengths)
+    x = wl.gdn_prefill_varlen(lengths, H=H, dk=d, dv=d, seed=333)
+    g = np.random.default_rng(334)
+    S = (g.standard_normal((B, H, d, d)) * 0.5).astype(np.float32)
+    codes, scales = O.quantize_rows(O.gdnq_oracle.rotate(S, np.float32))
+    cu = x["cu_seqlens"]
+    q_, k_, v_, a_, b_ = _inputs(x)
+    need = ops.prefill_varlen_workspace_size(q_, v_, B, out_dtype=torch.float32, wht=True)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o, st = ops.prefill_varlen(q_, k_, v_, a_, b_, dev(cu), init_codes=dev(codes), init_scales=dev(scales),
+                               out_dtype=torch.float32, wht=True, workspace=ws)
+    torch.cuda.synchronize()
+    T = int(cu[-1])
+    rows = T * H
+    rot = host(ws[need - 2 * rows * d * 2:]).view(np.uint16).reshape(2, T, H, d)
+    qr, kr = (wl.bf16_to_f32(rot[i]) for i in range(2))
+    for name, got, src in (("q", qr, x["q"]), ("k", kr, x["k"])):
+        assert np.mean(got != O.round_bf16(O.gdnq_oracle.rotate(src, np.float32))) <= 1e-3, name
+    xr = dict(x, q=qr, k=kr)
+    for b in range(B):
+        _check_seq(xr, cu, b, o, st, codes, scales)
+    assert st.wht
