@@ -51,6 +51,7 @@ struct OperandArgs {
   const uint16_t* x[2];  // q, k rows [rows][128] bf16
   int8_t* codes[2];      // [rows][128]
   float* scales[2];      // [rows]
+  uint16_t* rot[2];      // non-null: write the rotated rows as bf16 [rows][128] instead of codes
   int64_t rows;
   bool wht;
 };
@@ -88,6 +89,19 @@ __global__ __launch_bounds__(OP_THREADS) void ssd_operand_kernel(OperandArgs a) 
     }
 #pragma unroll
     for (int i = 0; i < OP_E; ++i) v[i] *= 0.08838834764831845f;  // 1/sqrt(128)
+  }
+  if (a.rot[op]) {  // rotated bf16 operands (nearest even), no quantization
+    if (!valid) return;
+    uint4* dst = reinterpret_cast<uint4*>(a.rot[op] + row * SDK + li * OP_E);
+#pragma unroll
+    for (int p = 0; p < OP_E / 8; ++p) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = f32_to_bf16_bits(v[8 * p + 2 * i]) | (f32_to_bf16_bits(v[8 * p + 2 * i + 1]) << 16);
+      dst[p] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    return;
   }
   float amax = 0.f;
 #pragma unroll
@@ -554,9 +568,10 @@ size_t ssd_rows(const PrefillLaunch& L) { return size_t(L.B) * L.T * L.H; }
 }  // namespace
 
 size_t prefill_ssd_workspace_bytes(const PrefillLaunch& L) {
-  if (!L.int8_qk) return 0;
   const size_t rows = ssd_rows(L);
-  return 2 * rows * SDK + 2 * rows * 4;  // q codes, k codes, q scales, k scales
+  if (L.int8_qk) return 2 * rows * SDK + 2 * rows * 4;  // q codes, k codes, q scales, k scales
+  if (L.wht) return 2 * rows * SDK * 2;                 // rotated q, k (bf16)
+  return 0;
 }
 
 hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream) {
@@ -572,13 +587,23 @@ hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream) {
     float* fk = fq + rows;
     const unsigned grid = unsigned((rows + OP_THREADS / OP_LPR - 1) / (OP_THREADS / OP_LPR));
     OperandArgs oa{{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k)}, {cq, ck}, {fq, fk},
-                   int64_t(rows), L.wht};
+                   {nullptr, nullptr}, int64_t(rows), L.wht};
     hipLaunchKernelGGL(ssd_operand_kernel, dim3(grid, 2), dim3(OP_THREADS), 0, stream, oa);
     if (hipError_t e = hipGetLastError()) return e;
     qsrc = cq;
     ksrc = ck;
     sq = fq;
     sk = fk;
+  } else if (L.wht && rows > 0) {  // the rotation alone: rotated bf16 operands
+    uint16_t* rq = static_cast<uint16_t*>(L.workspace);
+    uint16_t* rk = rq + rows * SDK;
+    const unsigned grid = unsigned((rows + OP_THREADS / OP_LPR - 1) / (OP_THREADS / OP_LPR));
+    OperandArgs oa{{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k)}, {nullptr, nullptr},
+                   {nullptr, nullptr}, {rq, rk}, int64_t(rows), true};
+    hipLaunchKernelGGL(ssd_operand_kernel, dim3(grid, 2), dim3(OP_THREADS), 0, stream, oa);
+    if (hipError_t e = hipGetLastError()) return e;
+    qsrc = rq;
+    ksrc = rk;
   }
   SsdArgs s{qsrc, ksrc, sq, sk, static_cast<const uint16_t*>(L.v), L.alpha, L.o, L.state_f32,
             L.B, L.T, L.H, L.d_v};

@@ -188,7 +188,6 @@ def _prefill(params, fake, **over):
     (_pp(flags=32), 8),
     (_pp(flags=8), 2),                     # no requantization: codes and scales must be NULL
     (_pp(dv=64, flags=2 | 4 | 8), 8),      # not for SSD
-    (_pp(dv=64, flags=2 | 1), 8),        # SSD rotation only on the way to int8 operands
 ])
 def test_prefill_rejects_bad_params(params, status):
     assert _prefill(params, Fake()) == status
@@ -223,6 +222,16 @@ def test_prefill_ssd_contract():
     assert _prefill(ssd, f, codes=None, scales=None, state_f32=f()) == 2      # beta given
     assert _prefill(_pp(dk=64, dv=64, flags=2), f, beta=None, codes=None, scales=None,
                     state_f32=f()) == 2
+
+
+def test_ssd_workspace_by_flags():
+    """SSD workspace: none for plain bf16 operands, the rotated bf16 rows with
+    the rotation alone, the int8 codes and scales with int8 operands."""
+    rows = 1 * 128 * 2
+    assert L.gdnq_prefill_workspace_size(_pp(dv=64, flags=2)) == 0
+    assert L.gdnq_prefill_workspace_size(_pp(dv=64, flags=2 | 1)) == 2 * rows * 128 * 2
+    assert L.gdnq_prefill_workspace_size(_pp(dv=64, flags=2 | 4)) == 2 * rows * 128 + 2 * rows * 4
+    assert L.gdnq_prefill_workspace_size(_pp(dv=64, flags=2 | 1 | 4)) == 2 * rows * 128 + 2 * rows * 4
 
 
 def test_window_and_chunk_sizes():

@@ -1,8 +1,10 @@
 """GPU parity of the SSD (scalar-decay, no delta term) chunked prefill
 against the CPU oracle, through the C ABI.
 
-  * plain bf16 q/k (no operand quantization): outputs and the final fp32
-    state within 1e-3 (max relative error per vector) with fp32 output;
+  * plain bf16 q/k (no operand quantization), also rotated (the rotated
+    bf16 operands read back from the workspace and fed to the oracle):
+    outputs and the final fp32 state within 1e-3 (max relative error per
+    vector) with fp32 output;
   * rotated + int8 q/k operands: the operand codes come from the same codec on
     rotations computed in a different summation order, so a code may flip
     (+-1) where the rotated value sits on a rounding boundary; outputs and the
@@ -84,6 +86,37 @@ def test_ssd_int8_operands(wht, out_dt):
         rc, rs = O.quantize_rows(src)
         assert_codes(c, rc, f"{name} operand codes")
         assert_scales(s, rs, f"{name} operand scales")
+
+
+@pytest.mark.parametrize("dv", [64, 128])
+def test_ssd_rotated_bf16_operands(dv):
+    """GDNQ_FLAG_WHT without int8 operands: q and k rotated in fp32 and
+    rounded to bf16 (read back from the workspace: [rotated q | rotated k])
+    match the oracle's rotation and rounding up to rounding ties on <= 0.1%,
+    each within half a bf16 step plus fp32 summation error; on those
+    operands outputs and the final state are held to the plain bar (1e-3),
+    and the state stays in the rotated basis."""
+    B, T, H = 2, 192, 3
+    x = wl.ssd_prefill(B=B, T=T, H=H, dk=128, dv=dv, seed=20 + dv)
+    q = dev(x["q"], torch.bfloat16)
+    need = ops.prefill_workspace_size(q, dev(x["v"], torch.bfloat16), ssd=True, wht=True)
+    rows = B * T * H
+    assert need == 2 * rows * 128 * 2
+    ws = Guarded((need,), torch.int8)
+    o, S = _run(x, int8=False, wht=True, out_dt=torch.float32, workspace=ws.t)
+    torch.cuda.synchronize()
+    assert ws.guards_intact()
+    rot = host(ws.t).view(np.uint16).reshape(2, B, T, H, 128)
+    qr, kr = (wl.bf16_to_f32(rot[i]) for i in range(2))
+    for name, got, src in (("q", qr, x["q"]), ("k", kr, x["k"])):
+        r32 = O.gdnq_oracle.rotate(src, np.float32)
+        assert np.mean(got != O.round_bf16(r32)) <= 1e-3, name
+        half = np.spacing(np.abs(r32)).astype(np.float64) * 2.0 ** 15
+        tol = half + 2.0 ** -20 * np.linalg.norm(src, axis=-1, keepdims=True)
+        assert np.all(np.abs(got.astype(np.float64) - r32) <= tol), f"rotated {name} off"
+    ref = O.prefill(qr, kr, x["v"], x["alpha"], None, W=None, kind="ssd")
+    assert max_rel_err(host(o), ref["o"]) <= OUT_TOL_F32
+    assert max_rel_err(host(S), ref["S"]) <= OUT_TOL_F32
 
 
 def test_ssd_outlier_channels():
