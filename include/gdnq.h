@@ -356,8 +356,10 @@ gdnq_status gdnq_prefill_handoff(const gdnq_prefill_params* p, const void* q, co
  *   recurrence, window buffer and boundary requantization per sequence).
  *
  *   p->batch B = number of sequences, p->seqlen T = total packed tokens;
- *   the other fields as for gdnq_prefill_handoff, with d_k = d_v = 128,
- *   chunk = window = 64 and no GDNQ_FLAG_WHT.
+ *   the other fields as for gdnq_prefill_handoff (decode's window W in
+ *   1 .. 64, d in {64, 128}, optional rotation).  Below W = 64 or at d = 64
+ *   every sequence is padded on the device (its whole windows to 64
+ *   positions, its open window unpadded).
  *     cu_seqlens [B+1] int32, device: sequence b holds packed tokens
  *                cu_seqlens[b] .. cu_seqlens[b+1]-1.  Expected
  *                0 = cu[0] <= cu[1] <= ... <= cu[B] = T.  The kernels take
@@ -391,23 +393,27 @@ gdnq_status gdnq_prefill_varlen(const gdnq_prefill_params* p, const int32_t* cu_
  *   (LeapQuant, abstract: outputs inside a window from the fixed low-bit
  *   state plus the buffered writes; one requantization when the window is
  *   full).  For each sequence the open window's fill_in[b] buffered writes
- *   and its new tokens form one sequence whose 64-position chunks start at
- *   the first buffered write, so the first window closes after
- *   64 - fill_in[b] new tokens, exactly as decode would close it.
+ *   and its new tokens form one sequence whose windows of W positions start
+ *   at the first buffered write, so the first window closes after
+ *   W - fill_in[b] new tokens, exactly as decode would close it.
  *
  *   p->batch B = sequences; p->seqlen = new tokens per sequence (cu_seqlens
- *   NULL, q [B,T,H,128] ...) or packed new tokens in total (cu_seqlens as
- *   for gdnq_prefill_varlen, q [T,H,128] ...).  GDN mode only (flags 0 or GDNQ_FLAG_STATE_4BIT,
- *   with one window-buffer format flag as for gdnq_prefill_handoff;
- *   d_k = d_v = 128, chunk = window = 64, in_dtype bf16).
- *     fill_in    [B] int32, device: buffered writes per sequence (0..63;
+ *   NULL, q [B,T,H,d] ...) or packed new tokens in total (cu_seqlens as for
+ *   gdnq_prefill_varlen, q [T,H,d] ...).  GDN mode only (flags
+ *   GDNQ_FLAG_STATE_4BIT and/or GDNQ_FLAG_WHT, with one window-buffer format
+ *   flag as for gdnq_prefill_handoff; d_k = d_v = d in {64, 128}, the
+ *   rotation at 128 only; p->window = decode's window W in 1 .. 64; chunk a
+ *   blocking hint in {16, 32, 64}; in_dtype bf16).  Below W = 64 or at
+ *   d = 64 every sequence is padded on the device (whole windows to 64
+ *   positions, the open window unpadded).
+ *     fill_in    [B] int32, device: buffered writes per sequence (0..W-1;
  *                other values are clamped into that range).  It may be the
  *                same array as fill_out.
- *     codes, scales [B,H,128,128] int8 / [B,H,128] fp32: the state at the
+ *     codes, scales [B,H,d,d] int8 / [B,H,d] fp32: the state at the
  *                last window boundary on entry, at the new last boundary on
  *                return (updated in place).
- *     buf_k, buf_v [B,H,64,128] (fp32, bf16 or FP8 vector pairs, as the
- *                flags select), buf_alpha, buf_beta [B,H,64] fp32:
+ *     buf_k, buf_v [B,H,W,d] (fp32, bf16 or FP8 vector pairs, as the
+ *                flags select), buf_alpha, buf_beta [B,H,W] fp32:
  *                decode's window buffer on entry (slots < fill_in read; the
  *                stored keys and values -- code * scale for FP8 -- enter the
  *                chunk products rounded to bf16, exact when decode's inputs
@@ -415,7 +421,7 @@ gdnq_status gdnq_prefill_varlen(const gdnq_prefill_params* p, const int32_t* cu_
  *                window's writes on return (slots < fill_out).
  *     o          new tokens' outputs, out_dtype (every new token written;
  *                the buffered writes have none: decode gave them).
- *     fill_out   [B] int32 = (fill_in + new tokens) mod 64 (written).
+ *     fill_out   [B] int32 = (fill_in + new tokens) mod W (written).
  *   workspace: gdnq_prefill_resume_workspace_size(p, cu_seqlens != NULL).
  *   Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, FLAGS, WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */

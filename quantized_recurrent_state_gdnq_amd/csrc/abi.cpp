@@ -199,9 +199,10 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
   return launched(gdnq::launch_decode(L, static_cast<hipStream_t>(stream)), "decode launch", stream);
 }
 
-// What the prefill entry points take: chunked (whole windows), the uniform
-// hand-over to decode (any T; decode's window 1 .. 64), and the variable-length
-// and resuming hand-overs (window 64, d = 128, no rotation).
+// What the prefill entry points take: chunked (whole windows; any window),
+// the uniform hand-over to decode (any T; decode's window 1 .. 64), and the
+// variable-length and resuming hand-overs (packed or per-sequence lengths,
+// decode's window 1 .. 64).
 enum PrefillMode { PF_CHUNKED = 0, PF_HANDOFF = 1, PF_MAPPED = 2 };
 
 static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillLaunch& L, int mode = PF_CHUNKED) {
@@ -216,11 +217,10 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   const int C = p->chunk, W = p->window;
   // GDN: chunk in {16, 32, 64} and any window (the kernels run every window
   // as whole 64-position chunks, so the result depends on the window only and
-  // the chunk is a blocking hint); the hand-over takes decode's windows
-  // (1 .. 64); the varlen and resume calls and SSD take chunk = 64 (= window)
-  if (ssd || mapped) {
+  // the chunk is a blocking hint); the hand-over calls take decode's windows
+  // (1 .. 64); SSD takes chunk = 64
+  if (ssd) {
     if (C != 64) return fail(GDNQ_ERR_SHAPE, "chunk = %d, expected 64", C);
-    if (!ssd && W != 64) return fail(GDNQ_ERR_SHAPE, "window = %d: the varlen and resume calls take 64", W);
   } else {
     if (C != 16 && C != 32 && C != 64) return fail(GDNQ_ERR_SHAPE, "chunk = %d, expected 16, 32 or 64", C);
     const int wmax = handoff ? 64 : GDNQ_MAX_WINDOW;
@@ -234,9 +234,11 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   if (T % Wt && !handoff) return fail(GDNQ_ERR_SHAPE, "seqlen = %d is not a multiple of the window (%d)", T, Wt);
   // positions the chunk kernels see: windows padded to whole 64-position
   // chunks (the hand-over's open last window unpadded)
-  const int64_t Tk = ssd   ? int64_t(T)
-                     : no_rq ? (int64_t(T) + 63) / 64 * 64
-                             : int64_t(T) / W * ((int64_t(W) + 63) / 64 * 64) + T % W;
+  const bool padded_map = mapped && (W < 64 || dk == 64);  // a sequence's padded length <= 64 (T + W - 1) / W
+  const int64_t Tk = ssd        ? int64_t(T)
+                     : no_rq      ? (int64_t(T) + 63) / 64 * 64
+                     : padded_map ? (64 * (int64_t(T) + W - 1) + W - 1) / W
+                                  : int64_t(T) / W * ((int64_t(W) + 63) / 64 * 64) + T % W;
   if ((Tk + 64) * H * 512 >= (int64_t(1) << 32))  // 32-bit output offsets, padding positions included
     return fail(GDNQ_ERR_SHAPE, "seqlen * heads = %lld: one sequence's outputs must stay under 4 GiB",
                 (long long)T * H);
@@ -255,8 +257,6 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
       return fail(GDNQ_ERR_FLAGS, "GDNQ_FLAG_BUF_BF16 and GDNQ_FLAG_BUF_FP8 are exclusive");
     if (!((dk == 128 && dv == 128) || (dk == 64 && dv == 64)))
       return fail(GDNQ_ERR_SHAPE, "GDN prefill: d_k = d_v = 128 or 64 required (got %d, %d)", dk, dv);
-    if (dk == 64 && mapped)
-      return fail(GDNQ_ERR_SHAPE, "GDN prefill at d = 64: not the varlen or resume calls");
     if (dk == 64 && (p->flags & GDNQ_FLAG_WHT))
       return fail(GDNQ_ERR_FLAGS, "GDN prefill at d = 64 takes no GDNQ_FLAG_WHT");
   }
@@ -405,9 +405,20 @@ size_t gdnq_prefill_handoff_workspace_size(const gdnq_prefill_params* p) {
 }
 
 // Variable lengths: batch = sequences, seqlen = packed tokens in total.
+// Positions the chunk kernels see for N new tokens of B sequences (resuming:
+// plus up to W - 1 buffered writes each), every window padded to 64
+// positions when the window is below 64 or d = 64.
+static int64_t mapped_positions(const gdnq::PrefillLaunch& L, int64_t N) {
+  const int64_t pre = L.resume ? int64_t(L.B) * (L.W - 1) : 0;
+  if (L.W < 64 || L.d_k == 64) return (64 * (N + pre) + L.W - 1) / L.W;
+  return N;
+}
+
 static gdnq_status varlen_validate(const gdnq_prefill_params* p, gdnq::PrefillLaunch& L) {
   if (gdnq_status st = prefill_validate(p, L, PF_MAPPED)) return st;
-  if ((int64_t(L.T) / 64 + L.B) * L.H > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "too many chunks");
+  const int64_t pos = mapped_positions(L, L.T);
+  if (pos > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "%lld padded positions: at most 2^31 - 1", (long long)pos);
+  if ((pos / 64 + L.B) * L.H > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "too many chunks");
   L.varlen = true;
   return GDNQ_OK;
 }
@@ -516,9 +527,11 @@ static gdnq_status resume_validate(const gdnq_prefill_params* p, bool varlen, gd
   if (gdnq_status st = prefill_validate(p, L, PF_MAPPED)) return st;
   const int64_t tokens = varlen ? int64_t(L.T) : int64_t(L.B) * L.T;
   if (tokens > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "%lld new tokens: at most 2^31 - 1", (long long)tokens);
-  if ((tokens / 64 + 2 * int64_t(L.B)) * L.H > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "too many chunks");
   L.varlen = varlen;
   L.resume = true;
+  const int64_t pos = mapped_positions(L, tokens);
+  if (pos > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "%lld padded positions: at most 2^31 - 1", (long long)pos);
+  if ((pos / 64 + 2 * int64_t(L.B)) * L.H > 0x7fffffffLL) return fail(GDNQ_ERR_SHAPE, "too many chunks");
   return GDNQ_OK;
 }
 

@@ -1270,6 +1270,7 @@ struct StageArgs {
   float* sb;
   SeqMap sm;
   int B, H, W;
+  int ds;  // elements of a buffered key / value (64 or 128; staged rows hold 128, zero past ds)
 };
 
 __global__ __launch_bounds__(256) void gdn_stage_kernel(StageArgs a) {
@@ -1280,25 +1281,27 @@ __global__ __launch_bounds__(256) void gdn_stage_kernel(StageArgs a) {
   for (int e = threadIdx.x; e < PC * PD / 2; e += 256) {  // two dims per thread
     const int pos = e / (PD / 2), d = 2 * (e % (PD / 2));
     uint32_t kw = 0u, qw = 0u, vw = 0u;
-    if (pos < pre) {  // a buffered write enters at bf16 (exact for bf16 inputs)
-      const size_t slot = size_t(bh) * a.W + pos, src = slot * PD + d;
-      if (a.fmt == 1) {
-        kw = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.buf_k) + src);
-        vw = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.buf_v) + src);
-      } else {
-        float2 kf, vf;
-        if (a.fmt == 2) {  // the stored value: code * scale in fp32
-          const float2 kc = e4m3_unpack2(*reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.buf_k) + src), false);
-          const float2 vc = e4m3_unpack2(*reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.buf_v) + src), false);
-          const float ks = a.buf_ks[slot], vs = a.buf_vs[slot];
-          kf = make_float2(kc.x * ks, kc.y * ks);
-          vf = make_float2(vc.x * vs, vc.y * vs);
+    if (pos < pre) {  // a buffered write enters at bf16 (exact for bf16 inputs); zero past ds
+      if (d < a.ds) {
+        const size_t slot = size_t(bh) * a.W + pos, src = slot * a.ds + d;
+        if (a.fmt == 1) {
+          kw = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.buf_k) + src);
+          vw = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.buf_v) + src);
         } else {
-          kf = *reinterpret_cast<const float2*>(static_cast<const float*>(a.buf_k) + src);
-          vf = *reinterpret_cast<const float2*>(static_cast<const float*>(a.buf_v) + src);
+          float2 kf, vf;
+          if (a.fmt == 2) {  // the stored value: code * scale in fp32
+            const float2 kc = e4m3_unpack2(*reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.buf_k) + src), false);
+            const float2 vc = e4m3_unpack2(*reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.buf_v) + src), false);
+            const float ks = a.buf_ks[slot], vs = a.buf_vs[slot];
+            kf = make_float2(kc.x * ks, kc.y * ks);
+            vf = make_float2(vc.x * vs, vc.y * vs);
+          } else {
+            kf = *reinterpret_cast<const float2*>(static_cast<const float*>(a.buf_k) + src);
+            vf = *reinterpret_cast<const float2*>(static_cast<const float*>(a.buf_v) + src);
+          }
+          kw = f32_to_bf16_bits(kf.x) | (f32_to_bf16_bits(kf.y) << 16);
+          vw = f32_to_bf16_bits(vf.x) | (f32_to_bf16_bits(vf.y) << 16);
         }
-        kw = f32_to_bf16_bits(kf.x) | (f32_to_bf16_bits(kf.y) << 16);
-        vw = f32_to_bf16_bits(vf.x) | (f32_to_bf16_bits(vf.y) << 16);
       }
     } else if (pos - pre < n) {
       const size_t src = (tok0 + (pos - pre)) * HD + size_t(h) * PD + d;
@@ -1428,6 +1431,156 @@ __global__ __launch_bounds__(256) void gdn_handoff_kernel(HandoffArgs a) {
   if (h == 0 && threadIdx.x == 0) a.fill_out[b] = r;
 }
 
+// ---- padded runs of packed (variable-length) or resumed sequences
+// Sequence b has f_b buffered writes (resuming; none otherwise) and n_b new
+// tokens: P_b = f_b + n_b positions in windows of W from its first buffered
+// write.  Its padded run has P_b / W whole windows of 64 positions (W writes,
+// then 64 - W that change nothing) and the P_b mod W positions of the open
+// window; the f_b buffered positions are staged from decode's buffer as
+// always, so it takes Np_b = 64 (P_b / W) + P_b mod W - f_b padded token rows.
+__device__ __forceinline__ int padded_token_rows(int n, int f, int W) {
+  const int P = f + n;
+  return P / W * PC + P % W - f;
+}
+
+// last b in [0, B] with off[b] <= r (off ascending from off[0] = 0)
+__device__ __forceinline__ int seq_of(const int32_t* off, int B, int64_t r) {
+  int lo = 0, hi = B;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One workgroup: token offsets tok[0..B] (cu sanitized as the sequence map
+// does it: the running maximum of cu clamped to [0, T]; uniform: b T),
+// buffered writes pre[b] = fill clamped to [0, W - 1] (or 0) and padded row
+// offsets cup[0..B] (exclusive sums of Np_b).
+struct PadMapArgs {
+  const int32_t* cu;    // [B+1] token offsets, or nullptr: T tokens per sequence
+  const int32_t* fill;  // [B] buffered writes, or nullptr
+  int32_t* tok;         // [B+1]
+  int32_t* cup;         // [B+1]
+  int32_t* pre;         // [B]
+  int B, T, W;
+};
+
+__global__ __launch_bounds__(1024) void gdn_padmap_kernel(PadMapArgs a) {
+  __shared__ int32_t sv[1025];
+  __shared__ int32_t sc[1024];
+  const int t = threadIdx.x;
+  auto off = [&](int i) { return a.cu ? min(max(a.cu[i], 0), a.T) : i * a.T; };
+  int carry_tok = 0, carry_p = 0;
+  for (int base = 0; base <= a.B; base += 1024) {
+    const int i = base + t;
+    int x = i <= a.B ? off(i) : INT_MAX;
+    if (base > 0) x = max(x, carry_tok);
+    sv[t] = x;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int y = t >= o ? sv[t - o] : 0;
+      __syncthreads();
+      sv[t] = max(sv[t], y);
+      __syncthreads();
+    }
+    if (t == 0) sv[1024] = base + 1024 <= a.B ? max(off(base + 1024), sv[1023]) : INT_MAX;
+    __syncthreads();
+    const int f = i < a.B && a.fill ? min(max(a.fill[i], 0), a.W - 1) : 0;
+    const int np = i < a.B ? padded_token_rows(sv[t + 1] - sv[t], f, a.W) : 0;
+    sc[t] = np;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int y = t >= o ? sc[t - o] : 0;
+      __syncthreads();
+      sc[t] += y;
+      __syncthreads();
+    }
+    if (i <= a.B) {
+      a.tok[i] = sv[t];
+      a.cup[i] = carry_p + sc[t] - np;
+    }
+    if (i < a.B) a.pre[i] = f;
+    carry_tok = sv[1023];
+    carry_p += sc[1023];
+    __syncthreads();
+  }
+}
+
+// Padded token rows [Tp][H][128] (and alpha, beta [Tp][H]) from the token rows
+// [.][H][ds]: row cup[b] + j of sequence b is position p = f_b + j of its
+// padded run; rows past cup[B] are zero.
+struct MapPadArgs {
+  const uint16_t* x[3];
+  uint16_t* y[3];
+  const float* a;
+  const float* be;
+  float* pa;
+  float* pb;
+  const int32_t* tok;
+  const int32_t* cup;
+  const int32_t* pre;
+  int64_t Tp;
+  int B, H, W, ds;
+};
+
+__device__ __forceinline__ int64_t padded_source(const MapPadArgs& a, int64_t rp) {  // token row, or -1
+  if (rp >= a.cup[a.B]) return -1;
+  const int b = seq_of(a.cup, a.B, rp);
+  const int f = a.pre[b], n = a.tok[b + 1] - a.tok[b];
+  const int p = f + int(rp - a.cup[b]);
+  const int nw = (f + n) / a.W, w = p / PC, i = p % PC;
+  if (w < nw && i >= a.W) return -1;  // a padding write of a whole window
+  return int64_t(a.tok[b]) + (w < nw ? w * a.W + i : nw * a.W + i) - f;
+}
+
+__global__ __launch_bounds__(256) void gdn_mappad_kernel(MapPadArgs a) {
+  const int64_t rows = a.Tp * a.H;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  const int gs = a.ds / 8;
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < rows * 48; e += stride) {
+    const int64_t r = e / 48;  // padded row rp H + h
+    const int op = int(e % 48) / 16, g = int(e % 16);
+    const int64_t h = r % a.H, src = padded_source(a, r / a.H);
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (src >= 0 && g < gs) w = reinterpret_cast<const uint4*>(a.x[op] + (src * a.H + h) * a.ds)[g];
+    reinterpret_cast<uint4*>(a.y[op] + r * PD)[g] = w;
+  }
+  for (int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x; r < rows; r += stride) {
+    const int64_t h = r % a.H, src = padded_source(a, r / a.H);
+    a.pa[r] = src >= 0 ? a.a[src * a.H + h] : 1.f;
+    a.pb[r] = src >= 0 ? a.be[src * a.H + h] : 0.f;
+  }
+}
+
+// Outputs of the token rows back from the padded rows: token tok[b] + j is
+// position p = f_b + j, padded position 64 (p / W) + p mod W.
+struct MapUnpadArgs {
+  const char* po;  // [Tp][H][128] (eo bytes each)
+  char* o;         // [rows][H][ds]
+  const int32_t* tok;
+  const int32_t* cup;
+  const int32_t* pre;
+  int64_t rows;    // token rows the output holds
+  int B, H, W, ds, eo;
+};
+
+__global__ __launch_bounds__(256) void gdn_mapunpad_kernel(MapUnpadArgs a) {
+  const int gpr = a.ds * a.eo / 16;
+  const int64_t n = a.rows * a.H * gpr, stride = int64_t(gridDim.x) * 256;
+  const int32_t T_all = a.tok[a.B];
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < n; e += stride) {
+    const int64_t row = e / gpr;  // t H + h
+    const int g = int(e % gpr);
+    const int64_t h = row % a.H, t = row / a.H;
+    if (t >= T_all) continue;  // past the (sanitized) sequences: not an output of any
+    const int b = seq_of(a.tok, a.B, t);
+    const int f = a.pre[b], p = f + int(t - a.tok[b]);
+    const int64_t prow = (int64_t(a.cup[b]) + p / a.W * PC + p % a.W - f) * a.H + h;
+    reinterpret_cast<uint4*>(a.o + row * a.ds * a.eo)[g] = reinterpret_cast<const uint4*>(a.po + prow * PD * a.eo)[g];
+  }
+}
+
 static size_t gdn_ws_128(const PrefillLaunch& L) {
   return gdn_ws_T(L) + gdn_ws_g(L) + gdn_ws_stage(L) + gdn_ws_map(L) + gdn_ws_rot(L);
 }
@@ -1468,14 +1621,57 @@ static PadLayout gdn_pad_layout(const PrefillLaunch& L) {
   return p;
 }
 
+// Packed / resumed sequences padded: the padded rows' upper bound, sum over
+// sequences of 64 (f_b + n_b) / W - f_b <= 64 (N + B (W - 1)) / W.
+static int64_t gdn_map_rows(const PrefillLaunch& L) {
+  const int64_t N = L.varlen ? int64_t(L.T) : int64_t(L.B) * L.T;  // new tokens
+  const int64_t pre_max = L.resume ? int64_t(L.B) * (L.W - 1) : 0;
+  return (PC * (N + pre_max) + L.W - 1) / L.W;
+}
+static bool gdn_map_padded(const PrefillLaunch& L) { return (L.varlen || L.resume) && gdn_padded(L); }
+static PrefillLaunch gdn_map_launch(const PrefillLaunch& L) {
+  PrefillLaunch L2 = L;
+  L2.d_k = L2.d_v = PD;
+  L2.T = int(gdn_map_rows(L));
+  L2.W = L2.C = PC;
+  L2.varlen = true;  // packed: the padded lengths differ between sequences
+  return L2;
+}
+struct MapLayout {
+  size_t qkv, ab, c0, s0, o, c, sc, map, inner, total;
+};
+static MapLayout gdn_map_layout(const PrefillLaunch& L) {
+  const PrefillLaunch L2 = gdn_map_launch(L);
+  const size_t rows = size_t(L2.T) * L.H, bh = size_t(L.B) * L.H;
+  const size_t rb = L.q4 ? PD / 2 : PD, eo = L.out_bf16 ? 2 : 4;
+  const bool pad_state = L.d_k == 64;
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  MapLayout p{};
+  p.qkv = 0;
+  p.ab = p.qkv + up(3 * rows * PD * 2);
+  p.c0 = p.ab + up(2 * rows * 4);
+  p.s0 = p.c0 + (pad_state ? up(bh * PD * rb) : 0);
+  p.o = p.s0 + (pad_state ? up(bh * PD * 4) : 0);
+  p.c = p.o + up(rows * PD * eo);
+  p.sc = p.c + (pad_state ? up(bh * PD * rb) : 0);
+  p.map = p.sc + (pad_state ? up(bh * PD * 4) : 0);
+  p.inner = p.map + up((3 * size_t(L.B) + 2) * 4);
+  p.total = p.inner + gdn_ws_128(L2);
+  return p;
+}
+
 size_t prefill_gdn_workspace_bytes(const PrefillLaunch& L) {
+  if (gdn_map_padded(L)) return gdn_map_layout(L).total;
   if (gdn_padded(L)) return gdn_pad_layout(L).total;
   return gdn_ws_128(L);
 }
 
+static hipError_t launch_prefill_gdn_mapped_padded(const PrefillLaunch& L, hipStream_t stream);
+
 static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t stream);
 
 hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
+  if (gdn_map_padded(L)) return launch_prefill_gdn_mapped_padded(L, stream);
   if (!gdn_padded(L)) return launch_prefill_gdn128(L, stream);
   // pad, run the d = 128, 64-chunk kernels on the workspace copies, unpad
   const PadLayout P = gdn_pad_layout(L);
@@ -1527,6 +1723,76 @@ hipError_t launch_prefill_gdn(const PrefillLaunch& L, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Packed or resumed sequences at d = 64 or with decode's window below 64:
+// map and pad every sequence, run the d = 128, 64-chunk kernels on the packed
+// padded rows (the hand-over writes decode's W-slot buffer of d elements),
+// then copy the outputs (and the d = 64 state) back.
+static hipError_t launch_prefill_gdn_mapped_padded(const PrefillLaunch& L, hipStream_t stream) {
+  const MapLayout P = gdn_map_layout(L);
+  const PrefillLaunch L2p = gdn_map_launch(L);
+  char* ws = static_cast<char*>(L.workspace);
+  const int64_t Tp = L2p.T, rows = Tp * L.H, bh = int64_t(L.B) * L.H;
+  const bool pad_state = L.d_k == 64;
+  const int rb64 = L.q4 ? 32 : 64;
+  int32_t* tok = reinterpret_cast<int32_t*>(ws + P.map);
+  int32_t* cup = tok + (L.B + 1);
+  int32_t* pre = cup + (L.B + 1);
+  PadMapArgs m{L.cu_seqlens, L.resume ? L.fill_in : nullptr, tok, cup, pre, L.B, L.T, L.W};
+  hipLaunchKernelGGL(gdn_padmap_kernel, dim3(1), dim3(1024), 0, stream, m);
+  if (hipError_t e = hipGetLastError()) return e;
+  uint16_t* pq = reinterpret_cast<uint16_t*>(ws + P.qkv);
+  float* pal = reinterpret_cast<float*>(ws + P.ab);
+  MapPadArgs pa{{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v)},
+                {pq, pq + rows * PD, pq + 2 * rows * PD}, L.alpha, L.beta, pal, pal + rows,
+                tok, cup, pre, Tp, L.B, L.H, L.W, L.d_k};
+  const int64_t work = rows * 48;
+  const unsigned grid = unsigned(work / 256 + 1 < 4096 ? work / 256 + 1 : 4096);
+  hipLaunchKernelGGL(gdn_mappad_kernel, dim3(grid), dim3(256), 0, stream, pa);
+  if (hipError_t e = hipGetLastError()) return e;
+  PrefillLaunch L2 = L2p;
+  L2.q = pa.y[0];
+  L2.k = pa.y[1];
+  L2.v = pa.y[2];
+  L2.alpha = pa.pa;
+  L2.beta = pa.pb;
+  L2.cu_seqlens = cup;
+  L2.fill_in = L.resume ? pre : nullptr;
+  if (pad_state) {  // the stored state widened to d = 128 (rows and columns past 64 zero)
+    PadArgs sp{{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}, nullptr, nullptr, nullptr, nullptr,
+               0, 0, 1, 1, PC, L.d_k, L.init_codes, L.init_scales,
+               L.init_codes ? reinterpret_cast<int8_t*>(ws + P.c0) : nullptr,
+               reinterpret_cast<float*>(ws + P.s0), bh, rb64};
+    if (L.init_codes) {
+      hipLaunchKernelGGL(gdn_pad_kernel, dim3(unsigned(bh * PD * 8 / 256 + 1 < 4096 ? bh * PD * 8 / 256 + 1 : 4096)),
+                         dim3(256), 0, stream, sp);
+      if (hipError_t e = hipGetLastError()) return e;
+    }
+    L2.init_codes = sp.pc0;
+    L2.init_scales = L.init_codes ? sp.ps0 : nullptr;
+    L2.codes = reinterpret_cast<int8_t*>(ws + P.c);
+    L2.scales = reinterpret_cast<float*>(ws + P.sc);
+  }
+  L2.o = ws + P.o;
+  L2.workspace = ws + P.inner;
+  if (hipError_t e = launch_prefill_gdn128(L2, stream)) return e;
+  const int64_t out_rows = L.varlen ? int64_t(L.T) : int64_t(L.B) * L.T;
+  MapUnpadArgs ua{ws + P.o, static_cast<char*>(L.o), tok, cup, pre, out_rows, L.B, L.H, L.W, L.d_k,
+                  L.out_bf16 ? 2 : 4};
+  const int64_t uwork = out_rows * L.H * (L.d_k * (L.out_bf16 ? 2 : 4) / 16);
+  if (uwork > 0) {
+    hipLaunchKernelGGL(gdn_mapunpad_kernel, dim3(unsigned(uwork / 256 + 1 < 4096 ? uwork / 256 + 1 : 4096)),
+                       dim3(256), 0, stream, ua);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  if (pad_state) {
+    UnpadArgs us{nullptr, nullptr, 0, 0, 1, 1, PC, L.d_k, 1, L2.codes, L2.scales, L.codes, L.scales, nullptr, nullptr,
+                 bh, rb64};
+    hipLaunchKernelGGL(gdn_unpad_kernel, dim3(unsigned(bh * 64 * 4 / 256 + 1)), dim3(256), 0, stream, us);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  return hipSuccess;
+}
+
 static int gdn_buf_fmt(const PrefillLaunch& L) { return L.buf_fp8 ? 2 : L.buf_bf16 ? 1 : 0; }
 // FP8 window buffer: the fp32 scales follow the B H W d code bytes
 static float* gdn_fp8_scales(const PrefillLaunch& L, void* codes) {
@@ -1573,7 +1839,7 @@ static hipError_t launch_prefill_gdn128(const PrefillLaunch& Lin, hipStream_t st
       StageArgs g{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k),
                   static_cast<const uint16_t*>(L.v), L.alpha, L.beta, L.buf_k, L.buf_v,
                   gdn_fp8_scales(L, L.buf_k), gdn_fp8_scales(L, L.buf_v), gdn_buf_fmt(L), L.buf_alpha,
-                  L.buf_beta, sk, sq, sv, sa, sb, sm, L.B, L.H, L.buf_W};
+                  L.buf_beta, sk, sq, sv, sa, sb, sm, L.B, L.H, L.buf_W, L.buf_d};
       g.sm.pre = pre;  // the staging kernel reads the prefixes, not yet the staged copy
       hipLaunchKernelGGL(gdn_stage_kernel, dim3(unsigned(L.B) * L.H), dim3(256), 0, stream, g);
       if (hipError_t e = hipGetLastError()) return e;

@@ -377,7 +377,7 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=No
     if st.state_bits != state_bits:
         raise ValueError("state: its code width differs from state_bits")
     p = _varlen_params(q, v, B, window=window, out_dtype=out_dtype, state_bits=state_bits,
-                       extra_flags=_state_shapes(st, B, H, d_k, d_v, 64, wht)
+                       extra_flags=_state_shapes(st, B, H, d_k, d_v, window, wht)
                        | (_lib.GDNQ_FLAG_WHT if wht else 0))
     need = int(_lib.prefill_varlen_workspace_size(p))
     if need and workspace is None:
@@ -391,18 +391,18 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, *, window=64, init_codes=No
     return o, st
 
 
-def prefill_resume_workspace_size(q, v, n_seqs, *, packed=False, out_dtype=torch.bfloat16, wht=False):
+def prefill_resume_workspace_size(q, v, n_seqs, *, packed=False, out_dtype=torch.bfloat16, wht=False, window=64):
     """Workspace of prefill_resume: q [B,T,H,d_k] (n_seqs = B), or packed
-    q [T,H,d_k] of n_seqs sequences."""
+    q [T,H,d_k] of n_seqs sequences, resuming states of decode's `window`."""
     T = q.shape[0] if packed else q.shape[1]
-    p = _lib.PrefillParams(n_seqs, T, q.shape[-2], q.shape[-1], v.shape[-1], 64, 64, _DT[q.dtype],
+    p = _lib.PrefillParams(n_seqs, T, q.shape[-2], q.shape[-1], v.shape[-1], 64, window, _DT[q.dtype],
                            _DT[out_dtype], _lib.GDNQ_FLAG_WHT if wht else 0)
     return int(_lib.prefill_resume_workspace_size(p, packed))
 
 
 def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=torch.bfloat16,
                    o=None, workspace=None):
-    """Continue every sequence of a DecodeState (window 64; fp32, bf16 or FP8
+    """Continue every sequence of a DecodeState (any window 1..64; fp32, bf16 or FP8
     window buffer, whose writes enter at bf16) with new tokens by chunked prefill, at whatever fill each sequence
     is (see gdnq_prefill_resume in include/gdnq.h).  Uniform: q, k
     [B,T,H,d_k], v [B,T,H,d_v], alpha, beta [B,T,H]; packed: [T,...] with
@@ -412,7 +412,8 @@ def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=to
     st = state
     B, H, d_v, d_k = st.codes.shape
     d_k = d_k * 8 // st.state_bits
-    buf_flag = _state_shapes(st, B, H, d_k, d_v, 64, st.wht)
+    W = st.window
+    buf_flag = _state_shapes(st, B, H, d_k, d_v, W, st.wht)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, torch.bfloat16, dev)
     for name, t in (("alpha", alpha), ("beta", beta)):
@@ -432,7 +433,7 @@ def prefill_resume(state, q, k, v, alpha, beta, cu_seqlens=None, *, out_dtype=to
             or tuple(v.shape) != lead + (H, d_v) or tuple(alpha.shape) != lead + (H,)
             or tuple(beta.shape) != lead + (H,)):
         raise ValueError("inconsistent resume shapes")
-    p = _lib.PrefillParams(B, T, H, d_k, d_v, 64, 64, _DT[q.dtype], _DT[out_dtype],
+    p = _lib.PrefillParams(B, T, H, d_k, d_v, 64, W, _DT[q.dtype], _DT[out_dtype],
                            (_lib.GDNQ_FLAG_STATE_4BIT if st.state_bits == 4 else 0) | buf_flag
                            | (_lib.GDNQ_FLAG_WHT if st.wht else 0))
     if o is None:

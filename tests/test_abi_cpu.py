@@ -238,15 +238,15 @@ def test_window_and_chunk_sizes():
     """GDN prefill takes windows and chunks of 16, 32 or 64.  A window
     below 64 runs on padded copies (a larger workspace, growing as the window
     shrinks); the chunk is a blocking hint that does not change the
-    workspace.  The varlen and resume calls and SSD take 64."""
+    workspace.  The hand-over calls take decode's windows; SSD takes 64."""
     sz = {(W, C): L.gdnq_prefill_workspace_size(_pp(T=256, W=W, C=C)) for W in (16, 32, 64) for C in (16, 32, 64)}
     assert all(v > 0 for v in sz.values())
     for W in (16, 32, 64):
         assert sz[(W, 16)] == sz[(W, 32)] == sz[(W, 64)]
     assert sz[(16, 64)] > sz[(32, 64)] > sz[(64, 64)]
     assert L.gdnq_prefill_workspace_size(_pp(T=48, W=16, C=16)) > 0
-    assert L.gdnq_prefill_varlen_workspace_size(_pp(T=256, W=32, C=32)) == 0
-    assert L.gdnq_prefill_varlen_workspace_size(_pp(T=256, W=64, C=32)) == 0
+    assert L.gdnq_prefill_varlen_workspace_size(_pp(T=256, W=32, C=32)) > 0
+    assert L.gdnq_prefill_varlen_workspace_size(_pp(T=256, W=128)) == 0  # decode's windows: 1 .. 64
     assert L.gdnq_prefill_workspace_size(_pp(T=256, dv=64, flags=2 | 4)) > 0
     assert L.gdnq_prefill_workspace_size(_pp(T=256, dv=64, C=32, W=32, flags=2 | 4)) == 0  # SSD: chunk 64
 
@@ -344,10 +344,9 @@ def test_handoff_rejects_bad_params(params, status):
 
 
 def test_handoff_windows_and_shapes():
-    """The uniform hand-over takes decode's windows 1 .. 64, d = 64 and the
+    """Every hand-over call takes decode's windows 1 .. 64, d = 64 and the
     rotation: a window below 64 or d = 64 runs on padded copies (a larger
-    workspace); T need not be a multiple of the window.  The varlen and
-    resume calls take the rotation and keep window 64 and d = 128."""
+    workspace); T need not be a multiple of the window."""
     base = _lib.prefill_handoff_workspace_size(_pp(T=100))
     assert base > 0
     for W, C in ((1, 16), (16, 16), (32, 64), (48, 16), (64, 32)):
@@ -355,11 +354,12 @@ def test_handoff_windows_and_shapes():
     assert _lib.prefill_handoff_workspace_size(_pp(T=100, W=16)) > base
     assert _lib.prefill_handoff_workspace_size(_pp(T=100, dk=64, dv=64)) > 0
     assert _lib.prefill_handoff_workspace_size(_pp(T=100, flags=1)) == base + 2 * 100 * 2 * 128 * 2
-    assert _lib.prefill_varlen_workspace_size(_pp(T=100, W=32)) == 0
-    assert _lib.prefill_varlen_workspace_size(_pp(T=100, dk=64, dv=64)) == 0
+    assert _lib.prefill_varlen_workspace_size(_pp(T=100, W=32)) > _lib.prefill_varlen_workspace_size(_pp(T=100))
+    assert _lib.prefill_varlen_workspace_size(_pp(T=100, dk=64, dv=64)) > 0
     assert _lib.prefill_varlen_workspace_size(_pp(T=100, flags=1)) == (_lib.prefill_varlen_workspace_size(_pp(T=100))
                                                                        + 2 * 100 * 2 * 128 * 2)  # T H packed rows
-    assert _lib.prefill_resume_workspace_size(_pp(T=100, W=32), 0) == 0
+    assert _lib.prefill_resume_workspace_size(_pp(T=100, W=32), 0) > _lib.prefill_resume_workspace_size(_pp(T=100), 0)
+    assert _lib.prefill_resume_workspace_size(_pp(T=100, dk=64, dv=64), 1) > 0
     assert _lib.prefill_resume_workspace_size(_pp(T=100, flags=1), 0) > _lib.prefill_resume_workspace_size(_pp(T=100), 0)
 
 
@@ -430,7 +430,7 @@ def _varlen(params, fake, cu="fake", **over):
 
 
 @pytest.mark.parametrize("params,status", [
-    (_pp(C=32, W=32), 2), (_pp(dk=64, dv=64), 2), (_pp(ind=0), 3),
+    (_pp(W=65), 2), (_pp(W=0), 2), (_pp(C=8), 2), (_pp(dk=64, dv=128), 2), (_pp(ind=0), 3),
     (_pp(flags=8), 8), (_pp(dv=64, flags=2 | 1 | 4), 8),   # GDN only, requantizing
     (_pp(T=1 << 20, H=8192), 2),                           # the packed outputs past 4 GiB
 ])
@@ -480,7 +480,7 @@ def _resume(params, fake, cu=None, fill_in="fake", **over):
 
 
 @pytest.mark.parametrize("params,status", [
-    (_pp(C=32, W=32), 2), (_pp(dk=64, dv=64), 2), (_pp(ind=0), 3),
+    (_pp(W=65), 2), (_pp(W=0), 2), (_pp(C=8), 2), (_pp(dk=64, dv=128), 2), (_pp(ind=0), 3),
     (_pp(flags=8), 8), (_pp(dv=64, flags=2 | 1 | 4), 8),   # GDN only, requantizing
     (_pp(B=1 << 16, T=1 << 16), 2),                        # 2^32 new tokens
 ])

@@ -159,3 +159,96 @@ def test_handoff_rotated(W):
     ref = O.prefill(qr, kr, x["v"], x["alpha"], x["beta"], W=W, codes0=codes, scale0=scales)
     _check(st, o, ref, W, T, 8, strict=True)
     assert st.wht
+
+
+KEYS = ("q", "k", "v", "alpha", "beta")
+
+
+def _check_sequence(st, b, o_new, ref, W, n_close, what):
+    """Sequence b of a packed / resumed call against the oracle's run of it
+    (ref: outputs of its new tokens, codes, scales, buffer)."""
+    r = ref["n"]
+    assert host(st.fill)[b] == r, f"{what}: fill"
+    if o_new.shape[0]:
+        err = max_rel_err(host(o_new), ref["o"])
+        assert err <= (OUT_TOL_F32 if n_close == 0 else OUT_TOL_BF16), f"{what}: o max relative error {err:.3e}"
+    assert_codes(host(st.codes)[b], ref["codes"][0], f"{what} codes")
+    if n_close <= 1:
+        assert_scales(host(st.scales)[b], ref["scale"][0], f"{what} scales")
+    else:
+        assert_free_scales(host(st.scales)[b], ref["scale"][0], f"{what} scales")
+    for name, key in (("buf_k", "k"), ("buf_v", "v"), ("buf_alpha", "alpha"), ("buf_beta", "beta")):
+        assert np.array_equal(host(getattr(st, name))[b, :, :r], ref["buf"][key][0]), (what, name)
+
+
+@pytest.mark.parametrize("W,d", [(16, 128), (16, 64), (64, 64), (37, 128)])
+def test_varlen_window(W, d):
+    """Packed sequences (empty, one token, W - 1, W, 3 W + 5, 70 and 130
+    tokens; H=3) from stored states at decode's window W: each padded on the
+    device (whole windows to 64 positions, the open one unpadded) and every
+    sequence against the oracle run on it alone."""
+    H = 3
+    lengths = [0, 1, W - 1, W, 3 * W + 5, 70, 130]
+    B = len(lengths)
+    x = wl.gdn_prefill_varlen(lengths, H=H, dk=d, dv=d, seed=140 + W + d)
+    codes, scales = _state(B, H, d, 141)
+    cu = x["cu_seqlens"]
+    o, st = ops.prefill_varlen(*_inputs(x), dev(cu), window=W, init_codes=dev(codes), init_scales=dev(scales),
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        ref = O.prefill(*(x[key][None, t0:t1] for key in KEYS), W=W, codes0=codes[b:b + 1], scale0=scales[b:b + 1])
+        ref["o"] = ref["o"][0]
+        ref["buf"] = {k: v for k, v in ref["buf"].items()}
+        _check_sequence(st, b, o[t0:t1], ref, W, (t1 - t0) // W, f"W={W} d={d} sequence {b} ({t1 - t0} tokens)")
+
+
+@pytest.mark.parametrize("W,d,packed", [(16, 128, False), (16, 64, True), (32, 64, False), (64, 64, True)])
+def test_resume_window(W, d, packed):
+    """Decode states of window W at fills 0, W / 2 and W - 1 (buffered bf16
+    writes) resume with 2 W + 7 new tokens each (packed: 0, W + 3 and 3 W
+    tokens): the open window's buffered writes and the new tokens form one
+    sequence whose windows start at the first buffered write, padded on the
+    device; every sequence against the oracle over its buffered writes and
+    new tokens from the stored state."""
+    H = 2
+    fills = [0, W // 2, W - 1]
+    B = len(fills)
+    g = np.random.default_rng(150 + W + d)
+    codes, scales = O.quantize_rows((g.standard_normal((B, H, d, d)) * 0.5).astype(np.float32))
+    pre = wl.gdn_prefill(B=B, T=W, H=H, dk=d, dv=d, seed=151)
+    st = ops.DecodeState(dev(codes), dev(scales), W, fill=dev(np.asarray(fills, np.int32)))
+    bk = np.zeros((B, H, W, d), np.float32)
+    bv = np.zeros((B, H, W, d), np.float32)
+    ba = np.zeros((B, H, W), np.float32)
+    bb = np.zeros((B, H, W), np.float32)
+    for b, f in enumerate(fills):
+        bk[b, :, :f] = np.moveaxis(pre["k"][b, :f], 0, 1)
+        bv[b, :, :f] = np.moveaxis(pre["v"][b, :f], 0, 1)
+        ba[b, :, :f] = pre["alpha"][b, :f].T
+        bb[b, :, :f] = pre["beta"][b, :f].T
+    for name, val in (("buf_k", bk), ("buf_v", bv), ("buf_alpha", ba), ("buf_beta", bb)):
+        getattr(st, name).copy_(dev(val))
+    if packed:
+        lengths = [0, W + 3, 3 * W]
+        x = wl.gdn_prefill_varlen(lengths, H=H, dk=d, dv=d, seed=152)
+        cu = x["cu_seqlens"]
+        o = ops.prefill_resume(st, *(dev(x[key], torch.bfloat16 if key in ("q", "k", "v") else None) for key in KEYS),
+                               cu_seqlens=dev(cu), out_dtype=torch.float32)
+        new = [{key: x[key][int(cu[b]):int(cu[b + 1])] for key in KEYS} for b in range(B)]
+        outs = [o[int(cu[b]):int(cu[b + 1])] for b in range(B)]
+    else:
+        T = 2 * W + 7
+        x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=152)
+        o = ops.prefill_resume(st, *(dev(x[key], torch.bfloat16 if key in ("q", "k", "v") else None) for key in KEYS),
+                               out_dtype=torch.float32)
+        new = [{key: x[key][b] for key in KEYS} for b in range(B)]
+        outs = [o[b] for b in range(B)]
+    torch.cuda.synchronize()
+    for b, f in enumerate(fills):
+        n = new[b]["q"].shape[0]
+        seq = {key: np.concatenate([pre[key][b, :f], new[b][key]])[None] for key in KEYS}
+        ref = O.prefill(*(seq[key] for key in KEYS), W=W, codes0=codes[b:b + 1], scale0=scales[b:b + 1])
+        ref["o"] = ref["o"][0, f:]
+        _check_sequence(st, b, outs[b], ref, W, (f + n) // W, f"W={W} d={d} sequence {b} (fill {f}, {n} new)")

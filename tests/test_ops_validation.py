@@ -1,7 +1,8 @@
 """Shape checks of the torch wrappers.  The C ABI sees raw pointers only, so
 the wrappers must refuse any buffer whose shape differs from what the kernels
 address (a short output, a 4-bit-sized code array on the 8-bit path, a
-decode state whose window is not 64) before anything is launched.
+decode state whose window or width is not the call's) before anything is
+launched.
 
 The CPU tests call the checking helpers on host tensors; the GPU tests call
 each prefill wrapper with one mis-shaped buffer and expect ValueError."""
@@ -139,11 +140,11 @@ def test_prefill_varlen_rejects_misshaped(what):
 
 
 @gpu
-@pytest.mark.parametrize("what", ["o", "window16"])
+@pytest.mark.parametrize("what", ["o", "d64_state"])
 def test_prefill_resume_rejects_misshaped(what):
     dev = _dev()
     q, k, v, a, b = _prefill_inputs(B=2, T=10)
-    st = _state(B=2, W=16 if what == "window16" else 64, device=dev)
+    st = _state(B=2, d=64 if what == "d64_state" else 128, device=dev)  # a d = 64 state for d = 128 tokens
     kw = {}
     if what == "o":
         kw["o"] = torch.empty((2, 10, 2, 64), dtype=torch.bfloat16, device=dev)
