@@ -249,11 +249,16 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
  *   SSD (GDNQ_FLAG_SSD): S_t = a_t S_{t-1} + v_t k_t^T from a zero state, no
  *   requantization (window ignored); beta, init_codes, init_scales, codes and
  *   scales must be NULL; writes o and the final fp32 state (in the rotated
- *   basis under GDNQ_FLAG_WHT).  Supported: d_k = 128, d_v in {64, 128},
+ *   basis under GDNQ_FLAG_WHT).  Supported: d_k, d_v in {64, 128},
  *   chunk = 64, T a multiple of 64.  Flags: GDNQ_FLAG_INT8_QK and/or
- *   GDNQ_FLAG_WHT (each q and k row rotated by H/sqrt(128) in fp32, then
+ *   GDNQ_FLAG_WHT (each q and k row rotated by H/sqrt(d_k) in fp32, then
  *   quantized to int8 with INT8_QK, else rounded to bf16 (nearest even), the
- *   operand precision of the products; workspace: the rotated rows).
+ *   operand precision of the products; workspace: the rotated rows).  At
+ *   d_k = 64 the q and k rows are widened to 128 with zeros (after the
+ *   rotation and quantization, so neither sees the zeros) and the state is
+ *   built 128 wide and its first 64 columns copied to state_f32; the
+ *   workspace then holds the widened rows (bf16 unless INT8_QK, also with
+ *   neither flag) and, from the next 256-byte boundary, B*H*d_v*128 fp32.
  *
  *   p->in_dtype must be GDNQ_BF16, p->out_dtype GDNQ_BF16 or GDNQ_F32.
  *     q, k   [B,T,H,d_k] in_dtype     v [B,T,H,d_v] in_dtype

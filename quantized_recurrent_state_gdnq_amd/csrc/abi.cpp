@@ -246,7 +246,7 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   if (ssd) {
     if (p->flags & ~uint32_t(GDNQ_FLAG_SSD | GDNQ_FLAG_WHT | GDNQ_FLAG_INT8_QK))
       return fail(GDNQ_ERR_FLAGS, "flags 0x%x", p->flags);
-    if (dk != 128 || (dv != 64 && dv != 128)) return fail(GDNQ_ERR_SHAPE, "SSD: d_k = %d (128), d_v = %d (64 or 128)", dk, dv);
+    if (!dim_ok(dk) || !dim_ok(dv)) return fail(GDNQ_ERR_SHAPE, "SSD: d_k = %d, d_v = %d: each must be 64 or 128", dk, dv);
   } else {
     const uint32_t bufs = GDNQ_FLAG_BUF_BF16 | GDNQ_FLAG_BUF_FP8;
     if (p->flags & ~uint32_t(GDNQ_FLAG_STATE_4BIT | GDNQ_FLAG_WHT | GDNQ_FLAG_NO_REQUANT | (handoff ? bufs : 0u)))

@@ -41,11 +41,12 @@ constexpr int SDK = 128;  // d_k
 constexpr int SRW = 64;   // state rows (of d_v) per workgroup
 
 // ---------------------------------------------------------------- operand
-// Four lanes per 128-element row (32 elements each): five butterfly stages
-// inside the lane, the last two across the lane quad through DPP.
+// D / 32 lanes per row of D = 128 or 64 elements (32 elements each): five
+// butterfly stages inside the lane, the last one or two across the lanes
+// through DPP.  Output rows are 128 wide; a 64-element row is widened with
+// zeros (the state kernel's operands; the zeros change no product).
 constexpr int OP_THREADS = 256;
-constexpr int OP_LPR = 4;
-constexpr int OP_E = SDK / OP_LPR;
+constexpr int OP_E = 32;
 
 struct OperandArgs {
   const uint16_t* x[2];  // q, k rows [rows][128] bf16
@@ -56,14 +57,16 @@ struct OperandArgs {
   bool wht;
 };
 
+template <int D>
 __global__ __launch_bounds__(OP_THREADS) void ssd_operand_kernel(OperandArgs a) {
+  constexpr int OP_LPR = D / OP_E;
   const int op = blockIdx.y;
   const int tid = threadIdx.x;
   const int li = tid % OP_LPR;
   const int64_t row = int64_t(blockIdx.x) * (OP_THREADS / OP_LPR) + tid / OP_LPR;
   const bool valid = row < a.rows;
   float v[OP_E];
-  const uint4* src = reinterpret_cast<const uint4*>(a.x[op] + row * SDK + li * OP_E);
+  const uint4* src = reinterpret_cast<const uint4*>(a.x[op] + row * D + li * OP_E);
 #pragma unroll
   for (int p = 0; p < OP_E / 8; ++p) {
     const uint4 w = valid ? src[p] : make_uint4(0u, 0u, 0u, 0u);
@@ -82,15 +85,18 @@ __global__ __launch_bounds__(OP_THREADS) void ssd_operand_kernel(OperandArgs a) 
       const float o = dpp<DPP_XOR1>(v[i]);
       v[i] = up1 ? (o - v[i]) : (v[i] + o);
     }
+    if constexpr (OP_LPR == 4) {
 #pragma unroll
-    for (int i = 0; i < OP_E; ++i) {
-      const float o = dpp<DPP_XOR2>(v[i]);
-      v[i] = up2 ? (o - v[i]) : (v[i] + o);
+      for (int i = 0; i < OP_E; ++i) {
+        const float o = dpp<DPP_XOR2>(v[i]);
+        v[i] = up2 ? (o - v[i]) : (v[i] + o);
+      }
     }
+    constexpr float inv_sqrt = D == 128 ? 0.08838834764831845f : 0.125f;  // 1/sqrt(D)
 #pragma unroll
-    for (int i = 0; i < OP_E; ++i) v[i] *= 0.08838834764831845f;  // 1/sqrt(128)
+    for (int i = 0; i < OP_E; ++i) v[i] *= inv_sqrt;
   }
-  if (a.rot[op]) {  // rotated bf16 operands (nearest even), no quantization
+  if (a.rot[op]) {  // bf16 operands (rotated or not; nearest even), no quantization
     if (!valid) return;
     uint4* dst = reinterpret_cast<uint4*>(a.rot[op] + row * SDK + li * OP_E);
 #pragma unroll
@@ -100,6 +106,11 @@ __global__ __launch_bounds__(OP_THREADS) void ssd_operand_kernel(OperandArgs a) 
       for (int i = 0; i < 4; ++i)
         w[i] = f32_to_bf16_bits(v[8 * p + 2 * i]) | (f32_to_bf16_bits(v[8 * p + 2 * i + 1]) << 16);
       dst[p] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    if constexpr (D == 64) {  // the zero half of the row
+      uint4* dz = reinterpret_cast<uint4*>(a.rot[op] + row * SDK + 64 + li * OP_E);
+#pragma unroll
+      for (int p = 0; p < OP_E / 8; ++p) dz[p] = make_uint4(0u, 0u, 0u, 0u);
     }
     return;
   }
@@ -120,6 +131,11 @@ __global__ __launch_bounds__(OP_THREADS) void ssd_operand_kernel(OperandArgs a) 
       w[i] = pack4_i8(int(cf[16 * p + 4 * i]), int(cf[16 * p + 4 * i + 1]), int(cf[16 * p + 4 * i + 2]),
                       int(cf[16 * p + 4 * i + 3]));
     dst[p] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if constexpr (D == 64) {  // the zero half of the row
+    uint4* dz = reinterpret_cast<uint4*>(a.codes[op] + row * SDK + 64 + li * OP_E);
+#pragma unroll
+    for (int p = 0; p < OP_E / 16; ++p) dz[p] = make_uint4(0u, 0u, 0u, 0u);
   }
   if (li == 0) a.scales[op][row] = scale;
 }
@@ -565,13 +581,35 @@ __global__ __launch_bounds__(512, 1) void ssd_state_kernel(SsdArgs a) {
 
 size_t ssd_rows(const PrefillLaunch& L) { return size_t(L.B) * L.T * L.H; }
 
+// operand rows (int8 codes and scales, or bf16 rotated / widened rows), then
+// at d_k = 64 the state of 128 columns whose first 64 are copied out
+size_t ssd_operand_bytes(const PrefillLaunch& L) {
+  const size_t rows = ssd_rows(L);
+  if (L.int8_qk) return 2 * rows * SDK + 2 * rows * 4;  // q codes, k codes, q scales, k scales
+  if (L.wht || L.d_k == 64) return 2 * rows * SDK * 2;  // rotated and/or widened q, k (bf16)
+  return 0;
+}
+size_t ssd_state_pad_bytes(const PrefillLaunch& L) {
+  return L.d_k == 64 ? size_t(L.B) * L.H * L.d_v * SDK * 4 : 0;
+}
+
+// [bh][d_v][128] -> [bh][d_v][64]: the first 64 columns of each state row
+__global__ __launch_bounds__(256) void ssd_state_unpad_kernel(const float* ps, float* s, int64_t rows) {
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < rows * 16; e += int64_t(gridDim.x) * 256)
+    reinterpret_cast<float4*>(s + (e / 16) * 64)[e % 16] = reinterpret_cast<const float4*>(ps + (e / 16) * SDK)[e % 16];
+}
+
+template <int D>
+hipError_t launch_operands(const OperandArgs& oa, size_t rows, hipStream_t stream) {
+  constexpr int rpb = OP_THREADS / (D / OP_E);  // rows per workgroup
+  hipLaunchKernelGGL(ssd_operand_kernel<D>, dim3(unsigned((rows + rpb - 1) / rpb), 2), dim3(OP_THREADS), 0, stream, oa);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t prefill_ssd_workspace_bytes(const PrefillLaunch& L) {
-  const size_t rows = ssd_rows(L);
-  if (L.int8_qk) return 2 * rows * SDK + 2 * rows * 4;  // q codes, k codes, q scales, k scales
-  if (L.wht) return 2 * rows * SDK * 2;                 // rotated q, k (bf16)
-  return 0;
+  return (ssd_operand_bytes(L) + 255) / 256 * 256 + ssd_state_pad_bytes(L);
 }
 
 hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream) {
@@ -580,32 +618,34 @@ hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream) {
   const void* ksrc = L.k;
   const float* sq = nullptr;
   const float* sk = nullptr;
+  auto operands = [&](const OperandArgs& oa) {
+    return L.d_k == 64 ? launch_operands<64>(oa, rows, stream) : launch_operands<128>(oa, rows, stream);
+  };
   if (L.int8_qk && rows > 0) {
     int8_t* cq = static_cast<int8_t*>(L.workspace);
     int8_t* ck = cq + rows * SDK;
     float* fq = reinterpret_cast<float*>(ck + rows * SDK);
     float* fk = fq + rows;
-    const unsigned grid = unsigned((rows + OP_THREADS / OP_LPR - 1) / (OP_THREADS / OP_LPR));
     OperandArgs oa{{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k)}, {cq, ck}, {fq, fk},
                    {nullptr, nullptr}, int64_t(rows), L.wht};
-    hipLaunchKernelGGL(ssd_operand_kernel, dim3(grid, 2), dim3(OP_THREADS), 0, stream, oa);
-    if (hipError_t e = hipGetLastError()) return e;
+    if (hipError_t e = operands(oa)) return e;
     qsrc = cq;
     ksrc = ck;
     sq = fq;
     sk = fk;
-  } else if (L.wht && rows > 0) {  // the rotation alone: rotated bf16 operands
+  } else if ((L.wht || L.d_k == 64) && rows > 0) {  // rotated and/or widened bf16 operands
     uint16_t* rq = static_cast<uint16_t*>(L.workspace);
     uint16_t* rk = rq + rows * SDK;
-    const unsigned grid = unsigned((rows + OP_THREADS / OP_LPR - 1) / (OP_THREADS / OP_LPR));
     OperandArgs oa{{static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k)}, {nullptr, nullptr},
-                   {nullptr, nullptr}, {rq, rk}, int64_t(rows), true};
-    hipLaunchKernelGGL(ssd_operand_kernel, dim3(grid, 2), dim3(OP_THREADS), 0, stream, oa);
-    if (hipError_t e = hipGetLastError()) return e;
+                   {nullptr, nullptr}, {rq, rk}, int64_t(rows), L.wht};
+    if (hipError_t e = operands(oa)) return e;
     qsrc = rq;
     ksrc = rk;
   }
-  SsdArgs s{qsrc, ksrc, sq, sk, static_cast<const uint16_t*>(L.v), L.alpha, L.o, L.state_f32,
+  float* state = L.state_f32;
+  if (L.d_k == 64)
+    state = reinterpret_cast<float*>(static_cast<char*>(L.workspace) + (ssd_operand_bytes(L) + 255) / 256 * 256);
+  SsdArgs s{qsrc, ksrc, sq, sk, static_cast<const uint16_t*>(L.v), L.alpha, L.o, state,
             L.B, L.T, L.H, L.d_v};
   const unsigned grid = unsigned(L.B) * L.H * (L.d_v / SRW);
   void (*kern)(SsdArgs) = L.int8_qk ? (L.out_bf16 ? &ssd_state_kernel<true, true> : &ssd_state_kernel<true, false>)
@@ -614,7 +654,14 @@ hipError_t launch_prefill_ssd(const PrefillLaunch& L, hipStream_t stream) {
                                          hipFuncAttributeMaxDynamicSharedMemorySize, SSD_LDS))
     return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(512), SSD_LDS, stream, s);
-  return hipGetLastError();
+  if (hipError_t e = hipGetLastError()) return e;
+  if (L.d_k == 64) {
+    const int64_t srows = int64_t(L.B) * L.H * L.d_v;
+    hipLaunchKernelGGL(ssd_state_unpad_kernel, dim3(unsigned(srows * 16 / 256 + 1 < 4096 ? srows * 16 / 256 + 1 : 4096)),
+                       dim3(256), 0, stream, state, L.state_f32, srows);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace gdnq

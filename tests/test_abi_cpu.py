@@ -220,18 +220,32 @@ def test_prefill_ssd_contract():
     ssd = _pp(dv=64, flags=2 | 1 | 4)
     assert _prefill(ssd, f, beta=None, codes=None, scales=None) == 1          # state_f32 missing
     assert _prefill(ssd, f, codes=None, scales=None, state_f32=f()) == 2      # beta given
+    # d_k = 64 runs on operand rows widened to 128 and a padded state: a
+    # workspace even for plain bf16 operands
     assert _prefill(_pp(dk=64, dv=64, flags=2), f, beta=None, codes=None, scales=None,
+                    state_f32=f()) == 6
+    assert _prefill(_pp(dk=96, dv=64, flags=2), f, beta=None, codes=None, scales=None,
                     state_f32=f()) == 2
 
 
 def test_ssd_workspace_by_flags():
     """SSD workspace: none for plain bf16 operands, the rotated bf16 rows with
-    the rotation alone, the int8 codes and scales with int8 operands."""
+    the rotation alone, the int8 codes and scales with int8 operands; at
+    d_k = 64 the widened operand rows and a padded fp32 state."""
     rows = 1 * 128 * 2
     assert L.gdnq_prefill_workspace_size(_pp(dv=64, flags=2)) == 0
     assert L.gdnq_prefill_workspace_size(_pp(dv=64, flags=2 | 1)) == 2 * rows * 128 * 2
     assert L.gdnq_prefill_workspace_size(_pp(dv=64, flags=2 | 4)) == 2 * rows * 128 + 2 * rows * 4
     assert L.gdnq_prefill_workspace_size(_pp(dv=64, flags=2 | 1 | 4)) == 2 * rows * 128 + 2 * rows * 4
+    # d_k = 64: operand rows widened to 128 (bf16 even with neither flag), then
+    # at a 256-byte boundary the state [B,H,d_v,128] in fp32
+    pad = lambda n: (n + 255) // 256 * 256
+    st = 1 * 2 * 64 * 128 * 4
+    assert L.gdnq_prefill_workspace_size(_pp(dk=64, dv=64, flags=2)) == pad(2 * rows * 128 * 2) + st
+    assert L.gdnq_prefill_workspace_size(_pp(dk=64, dv=64, flags=2 | 1)) == pad(2 * rows * 128 * 2) + st
+    assert L.gdnq_prefill_workspace_size(_pp(dk=64, dv=64, flags=2 | 4)) == pad(2 * rows * 128 + 2 * rows * 4) + st
+    assert (L.gdnq_prefill_workspace_size(_pp(T=64, H=3, dk=64, dv=128, flags=2 | 1 | 4))
+            == pad(2 * 192 * 128 + 2 * 192 * 4) + 3 * 128 * 128 * 4)
 
 
 def test_window_and_chunk_sizes():

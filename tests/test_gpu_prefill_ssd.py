@@ -10,7 +10,9 @@ against the CPU oracle, through the C ABI.
     (+-1) where the rotated value sits on a rounding boundary; outputs and the
     final state are held to 2e-2 (the bf16-input bar), and the quantized
     operands themselves (read from the workspace) to the code bar: +-1 on at
-    most 0.1%, scales within 1e-5.
+    most 0.1%, scales within 1e-5;
+  * d_k = 64 in each of those modes, on operand rows widened to 128 with
+    zeros and a state copied out of a padded one.
 """
 
 import numpy as np
@@ -130,11 +132,12 @@ def test_ssd_outlier_channels():
     assert max_rel_err(host(S), ref["S"]) <= OUT_TOL_BF16
 
 
-def test_ssd_empty_sequence():
-    q = torch.empty((2, 0, 3, 128), dtype=torch.bfloat16, device=DEV)
+@pytest.mark.parametrize("dk", [128, 64])
+def test_ssd_empty_sequence(dk):
+    q = torch.empty((2, 0, 3, dk), dtype=torch.bfloat16, device=DEV)
     v = torch.empty((2, 0, 3, 64), dtype=torch.bfloat16, device=DEV)
     a = torch.empty((2, 0, 3), dtype=torch.float32, device=DEV)
-    S = torch.full((2, 3, 64, 128), 7.0, device=DEV)
+    S = torch.full((2, 3, 64, dk), 7.0, device=DEV)
     ops.prefill_chunked(q, q, v, a, None, ssd=True, int8_qk=True, wht=True, state_f32=S)
     torch.cuda.synchronize()
     assert not host(S).any()
@@ -179,3 +182,53 @@ def test_ssd_batch2_seq4096_heads80_every_head():
             assert err_s <= OUT_TOL_BF16, f"(b={b}, heads {h0}..) state error {err_s:.3e}"
             worst_o, worst_s = max(worst_o, err_o), max(worst_s, err_s)
     print(f"SSD B2 T4096 H80: all 160 heads, worst o {worst_o:.2e}, state {worst_s:.2e}")
+
+
+@pytest.mark.parametrize("mode", ["plain", "rot", "int8", "int8_rot"])
+@pytest.mark.parametrize("dv", [64, 128])
+def test_ssd_dk64(mode, dv):
+    """d_k = 64: the operand kernel widens every q and k row to 128 with
+    zeros (rotating it first over its 64 elements with GDNQ_FLAG_WHT, and
+    quantizing it with GDNQ_FLAG_INT8_QK); the zero columns add nothing to
+    any product and the state comes back as [B,H,d_v,64].  Plain: 1e-3
+    against the oracle on the inputs; rotated bf16: 1e-3 on the rotated rows
+    read back (which match the oracle's rotation and rounding up to ties on
+    <= 0.1%, their upper half zero); int8: 2e-2, the operand codes to the
+    code bar and their upper half zero."""
+    B, T, H, dk = 2, 192, 3, 64
+    int8, wht = mode.startswith("int8"), mode.endswith("rot")
+    x = wl.ssd_prefill(B=B, T=T, H=H, dk=dk, dv=dv, seed=30 + dv + len(mode))
+    q = dev(x["q"], torch.bfloat16)
+    need = ops.prefill_workspace_size(q, dev(x["v"], torch.bfloat16), ssd=True, int8_qk=int8, wht=wht)
+    rows = B * T * H
+    op_bytes = 2 * rows * 128 + 8 * rows if int8 else 4 * rows * 128
+    assert need == (op_bytes + 255) // 256 * 256 + B * H * dv * 128 * 4
+    ws = Guarded((need,), torch.int8)
+    o, S = _run(x, int8=int8, wht=wht, out_dt=torch.float32, workspace=ws.t)
+    torch.cuda.synchronize()
+    assert ws.guards_intact()
+    assert S.shape == (B, H, dv, dk)
+    w = host(ws.t)
+    if int8:
+        ref = _ref(x, int8=True, wht=wht)
+        tol = OUT_TOL_BF16
+        for i, name in enumerate(("q", "k")):
+            c = w[i * rows * 128:(i + 1) * rows * 128].view(np.int8).reshape(B, T, H, 128)
+            sc = w[2 * rows * 128 + 4 * rows * i:2 * rows * 128 + 4 * rows * (i + 1)].view(np.float32)
+            assert not c[..., 64:].any(), f"{name} codes: upper half not zero"
+            src = O.gdnq_oracle.rotate(x[name], np.float32) if wht else x[name]
+            rc, rs = O.quantize_rows(src)
+            assert_codes(c[..., :64], rc, f"{name} operand codes")
+            assert_scales(sc.reshape(B, T, H), rs, f"{name} operand scales")
+    else:
+        wide = w[:4 * rows * 128].view(np.uint16).reshape(2, B, T, H, 128)
+        assert not wide[..., 64:].any(), "widened rows: upper half not zero"
+        qr, kr = (wl.bf16_to_f32(wide[i][..., :64]) for i in range(2))
+        for name, got in (("q", qr), ("k", kr)):
+            src = O.gdnq_oracle.rotate(x[name], np.float32) if wht else x[name]
+            assert np.mean(got != O.round_bf16(src)) <= 1e-3, name
+        ref = O.prefill(qr, kr, x["v"], x["alpha"], None, W=None, kind="ssd")
+        tol = OUT_TOL_F32
+    err_o, err_s = max_rel_err(host(o), ref["o"]), max_rel_err(host(S), ref["S"])
+    print(f"SSD d_k=64 d_v={dv} {mode}: o {err_o:.2e}, state {err_s:.2e}")
+    assert err_o <= tol and err_s <= tol
