@@ -528,6 +528,9 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
     };
     if constexpr (!CARRY) pack_codes();
     publish(0);
+    // CARRY: chunks since the window began (0: S0 is the stored codes, or zero;
+    // never requantizing, only chunk 0)
+    int wc = 0;
     __syncthreads();  // chunk 0 staged
 
     for (int c = 0; c < NC; ++c) {
@@ -567,7 +570,7 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
       f32x4 x[4];
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) x[jt] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (CARRY) {  // S0 in three bf16 parts (exact for codes or fp32 values)
+      if (CARRY && wc != 0) {  // fp32 S0 inside a window: three bf16 parts (exact)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           float xs[8];
@@ -581,6 +584,15 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
           for (int jt = 0; jt < 4; ++jt) x[jt] = mfma16(ka[jt][ks], pm, x[jt]);
 #pragma unroll
           for (int jt = 0; jt < 4; ++jt) x[jt] = mfma16(ka[jt][ks], ph, x[jt]);
+        }
+      } else if constexpr (CARRY) {  // a window's first chunk: S0 is codes (or zero), exact in bf16
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          bf16x8 cw;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cw[e] = (__bf16)cf[2 * ks + (e >> 2)][e & 3];
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) x[jt] = mfma16(ka[jt][ks], cw, x[jt]);
         }
       } else {
 #pragma unroll
@@ -673,7 +685,8 @@ __global__ __launch_bounds__(SNT, 1) void gdn_state_kernel(StateArgs a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) sn[4 * dt + q] = gs * cf[dt][q] + acc[q];
         }
-        if (!CARRY || (a.cpw > 0 && (c + 1) % a.cpw == 0)) {
+        if (CARRY) wc = (a.cpw > 0 && wc + 1 == a.cpw) ? 0 : wc + 1;  // 0: chunk c + 1 starts a window
+        if (!CARRY || wc == 0) {
           float m4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial maxima
 #pragma unroll
           for (int e = 0; e < 32; ++e) m4[e & 3] = fmaxf(m4[e & 3], fabsf(sn[e]));
