@@ -215,17 +215,24 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
     if (tt < 10) {
       int it, jt;
       tile_of(tt, it, jt);
+      // row offsets by 24-bit products: a 32-bit product formed with a 64-bit
+      // multiply-add reads an unrelated register as its high half, and a load
+      // of the next chunk-head still in flight there would be waited for
+      const __bf16* ki = Kl + __umul24(uint32_t(it * 16 + lr), uint32_t(KP));
+      const __bf16* kj = Kl + __umul24(uint32_t(jt * 16 + lr), uint32_t(KP));
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int kk = ks * 32 + 8 * lq;
-        acc = mfma16(lds_bf16x8(Kl + (it * 16 + lr) * KP + kk), lds_bf16x8(Kl + (jt * 16 + lr) * KP + kk), acc);
+        acc = mfma16(lds_bf16x8(ki + kk), lds_bf16x8(kj + kk), acc);
       }
       const int j = jt * 16 + lr;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = it * 16 + 4 * lq + q;
-        av[n][q] = (j < i) ? bl[i] * expf(gl[i] - gl[j]) * acc[q] : 0.f;
+        // e^(g_i - g_j) <= 1 by the hardware exp2 (the argument is <= 0; a
+        // result below fp32's normal range is 0)
+        av[n][q] = (j < i) ? bl[i] * __builtin_amdgcn_exp2f((gl[i] - gl[j]) * 1.4426950408889634f) * acc[q] : 0.f;
       }
     }
   }
