@@ -175,8 +175,18 @@ __device__ __forceinline__ float raw_to_f32(uint32_t r) {
 
 template <bool BF16>
 __device__ __forceinline__ void store_out(void* p, size_t i, float x) {
-  if constexpr (BF16) static_cast<uint16_t*>(p)[i] = uint16_t(f32_to_bf16_bits(x));
-  else static_cast<float*>(p)[i] = x;
+  if constexpr (BF16) __builtin_nontemporal_store(uint16_t(f32_to_bf16_bits(x)), static_cast<uint16_t*>(p) + i);
+  else __builtin_nontemporal_store(x, static_cast<float*>(p) + i);
+}
+// rows i, i + 1 of the output in one store
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+template <bool BF16>
+__device__ __forceinline__ void store_out2(void* p, size_t i, float x0, float x1) {
+  if constexpr (BF16)
+    __builtin_nontemporal_store(f32_to_bf16_bits(x0) | (f32_to_bf16_bits(x1) << 16),
+                                reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p) + i));
+  else
+    __builtin_nontemporal_store(f32x2v{x0, x1}, reinterpret_cast<f32x2v*>(static_cast<float*>(p) + i));
 }
 
 // A value the compiler cannot prove wave-uniform (it comes from LDS) but is:
@@ -460,9 +470,9 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
       float* bv = static_cast<float*>(a.buf_v) + (bufs_base + f) * DV + lane * RPL;
       float* bk = static_cast<float*>(a.buf_k) + (bufs_base + f) * DK + lane * EK;
 #pragma unroll
-      for (int i = 0; i < RPL; ++i) bv[i] = vcur[i];
+      for (int i = 0; i < RPL; ++i) __builtin_nontemporal_store(vcur[i], bv + i);
 #pragma unroll
-      for (int e = 0; e < EK; ++e) bk[e] = kv[e];
+      for (int e = 0; e < EK; ++e) __builtin_nontemporal_store(kv[e], bk + e);
     }
     if (lane == 0) {
       a.buf_alpha[bufs_base + f] = alpha_t;
@@ -591,10 +601,10 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
           for (int n = 0; n < CPW; ++n) d[i] = fmaf(code_at<QB>(w[q4], n), yy[CPW * q4 + n], d[i]);
       }
     }
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      const int row = lane * RPL + i;
-      store_out<OUT_BF16>(a.o, v_base + row, srow[i] * d[i] + acc[i]);
+    if constexpr (RPL == 2) {
+      store_out2<OUT_BF16>(a.o, v_base + lane * 2, srow[0] * d[0] + acc[0], srow[1] * d[1] + acc[1]);
+    } else {
+      store_out<OUT_BF16>(a.o, v_base + lane, srow[0] * d[0] + acc[0]);
     }
     __builtin_amdgcn_wave_barrier();  // the next head reuses wy
     ++k;
