@@ -173,6 +173,12 @@ __device__ __forceinline__ float raw_to_f32(uint32_t r) {
   return BF16 ? __uint_as_float(r << 16) : __uint_as_float(r);
 }
 
+// Cache policy of the buffered-write and decay loads: each is read once per
+// step, and as nontemporal loads the fp32 and bf16 buffers' steps ran faster
+// (B=64 H=32: 27.7 -> 25.0 us with the fp32 buffer); the E4M3 buffer's
+// step ran faster without.
+constexpr int dec_pol(int buf) { return buf == 2 ? 0 : BUF_STREAM; }
+
 template <bool BF16>
 __device__ __forceinline__ void store_out(void* p, size_t i, float x) {
   if constexpr (BF16) __builtin_nontemporal_store(uint16_t(f32_to_bf16_bits(x)), static_cast<uint16_t*>(p) + i);
@@ -305,15 +311,15 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
   // that consumes them
   auto load_raw = [&](const rsrc_t& r, uint32_t o, uint32_t so, int n, uint32_t* x) __attribute__((always_inline)) {
     if (BUF == 0 && n == 2) {
-      const uint2 w = bload_u2s(r, o, so);
+      const uint2 w = bload_u2s<dec_pol(BUF)>(r, o, so);
       x[0] = w.x;
       x[1] = w.y;
     } else if (BUF == 0 || (BUF == 1 && n == 2)) {
-      x[0] = __float_as_uint(bload_f1s(r, o, so));
+      x[0] = __float_as_uint(bload_f1s<dec_pol(BUF)>(r, o, so));
     } else if (BUF == 1 || n == 2) {
-      x[0] = bload_h1s(r, o, so);
+      x[0] = bload_h1s<dec_pol(BUF)>(r, o, so);
     } else {
-      x[0] = bload_b1s(r, o, so);
+      x[0] = bload_b1s<dec_pol(BUF)>(r, o, so);
     }
   };
   auto load_k = [&](int j, uint32_t (&x)[KWD]) {  // j < 0 lands past the bound: reads 0, no traffic
@@ -372,11 +378,11 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
     for (int i = 0; i < RPL; ++i) srow[i] = a.scales[size_t(bh) * DV + lane * RPL + i];
     alpha_t = a.alpha[bh];
     beta_t = a.beta[bh];
-    a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
-    b_slot = bload_f1(make_rsrc(a.buf_beta + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
+    a_slot = bload_f1<dec_pol(BUF)>(make_rsrc(a.buf_alpha + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
+    b_slot = bload_f1<dec_pol(BUF)>(make_rsrc(a.buf_beta + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
     if constexpr (BUF == 2) {
-      ks_slot = bload_f1(make_rsrc(a.ks + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
-      vs_slot = bload_f1(make_rsrc(a.vs + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
+      ks_slot = bload_f1<dec_pol(BUF)>(make_rsrc(a.ks + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
+      vs_slot = bload_f1<dec_pol(BUF)>(make_rsrc(a.vs + bufs, uint32_t(fb) * 4), uint32_t(lane) * 4);
     }
 #pragma unroll
     for (int u = 0; u < P; ++u) {
@@ -739,19 +745,19 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void decode_kernel(Deco
     // (E4M3: the codes; the caller applies the vector's scale)
     auto load4 = [&](const rsrc_t& r, uint32_t e0, uint32_t e1) __attribute__((always_inline)) {
       if constexpr (BUF == 1) {
-        const uint2 w = bload_u2s(r, e0 * 2, e1 * 2);
+        const uint2 w = bload_u2s<dec_pol(BUF)>(r, e0 * 2, e1 * 2);
         return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
       } else if constexpr (BUF == 2) {
-        const uint32_t w = __float_as_uint(bload_f1s(r, e0, e1));
+        const uint32_t w = __float_as_uint(bload_f1s<dec_pol(BUF)>(r, e0, e1));
         const float2 lo = e4m3_unpack2(w, false), hi = e4m3_unpack2(w, true);
         return make_float4(lo.x, lo.y, hi.x, hi.y);
       } else {
-        return bload_f4(r, e0 * 4, e1 * 4);
+        return bload_f4<dec_pol(BUF)>(r, e0 * 4, e1 * 4);
       }
     };
     // E4M3: the scale of slot j (slots past the fill read 0)
     auto slot_scale = [&](const float* sc, int j) __attribute__((always_inline)) {
-      return bload_f1(make_rsrc(sc + bufs_base, uint32_t(f) * 4), uint32_t(j) * 4);
+      return bload_f1<dec_pol(BUF)>(make_rsrc(sc + bufs_base, uint32_t(f) * 4), uint32_t(j) * 4);
     };
     float4 kt[S::KREG];
 #pragma unroll
@@ -766,8 +772,8 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void decode_kernel(Deco
       }
     }
     // lane j: alpha_j, beta_j of write j; the current token's in lane W - 1
-    float a_slot = bload_f1(make_rsrc(a.buf_alpha + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
-    float b_slot = bload_f1(make_rsrc(a.buf_beta + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
+    float a_slot = bload_f1<dec_pol(BUF)>(make_rsrc(a.buf_alpha + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
+    float b_slot = bload_f1<dec_pol(BUF)>(make_rsrc(a.buf_beta + bufs_base, uint32_t(f) * 4), uint32_t(lane) * 4);
     // this thread's CCOL = 8 codes of its row (8 bytes, or 4 of 4-bit codes)
     uint2 cwr;
     if constexpr (QB == 8) {

@@ -329,46 +329,57 @@ __device__ __forceinline__ float code_at(uint32_t w, int n) {
 // whose byte offset is at or past `nbytes` reads 0 and causes no memory
 // traffic.  This predicates loads without branches (dword 3 = 0x00020000 is
 // the gfx9-family raw-buffer format word).
+// POL is the load's cache policy: 0, or BUF_STREAM (nontemporal) for data
+// read once and not again soon.
 using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int BUF_STREAM = 2;  // the nontemporal cache-policy bit of a buffer load
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
 }
+template <int POL = 0>
 __device__ __forceinline__ float4 bload_f4(rsrc_t r, uint32_t off, uint32_t soff = 0) {
-  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, POL);
   float4 f;
   __builtin_memcpy(&f, &v, 16);
   return f;
 }
+template <int POL = 0>
 __device__ __forceinline__ uint4 bload_u4(rsrc_t r, uint32_t off, uint32_t soff = 0) {
-  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, POL);
   uint4 u;
   __builtin_memcpy(&u, &v, 16);
   return u;
 }
+template <int POL = 0>
 __device__ __forceinline__ uint2 bload_u2(rsrc_t r, uint32_t off) {
-  auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POL);
   uint2 u;
   __builtin_memcpy(&u, &v, 8);
   return u;
 }
+template <int POL = 0>
 __device__ __forceinline__ float bload_f1(rsrc_t r, uint32_t off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POL));
 }
 // per-lane offset plus a scalar offset (wave-uniform)
+template <int POL = 0>
 __device__ __forceinline__ uint2 bload_u2s(rsrc_t r, uint32_t off, uint32_t soff) {
-  auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+  auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, POL);
   uint2 u;
   __builtin_memcpy(&u, &v, 8);
   return u;
 }
+template <int POL = 0>
 __device__ __forceinline__ float bload_f1s(rsrc_t r, uint32_t off, uint32_t soff) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, soff, POL));
 }
+template <int POL = 0>
 __device__ __forceinline__ uint32_t bload_h1s(rsrc_t r, uint32_t off, uint32_t soff) {  // 16 bits, zero-extended
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, POL);
 }
+template <int POL = 0>
 __device__ __forceinline__ uint32_t bload_b1s(rsrc_t r, uint32_t off, uint32_t soff) {  // 8 bits, zero-extended
-  return __builtin_amdgcn_raw_buffer_load_b8(r, off, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, soff, POL);
 }
 
 // Nearest OCP FP8 E4M3 value of q (1 sign bit, 4 exponent bits with bias 7,
