@@ -7,8 +7,12 @@ window fills drawn from U{0..63} holding fp32 (k, v, alpha, beta).
 
 A "step" is one gdnq_decode_step launch over the whole batch.  The state of
 one step (codes, scales, buffer: ~106 MB) fits in the 256 MB Infinity Cache,
-so steps rotate over `--replicas` copies of it (>= 4 by default, ~424 MB)
-and every step reads its state cold from HBM.  Fills advance by one per step
+so steps rotate over `--replicas` copies of it (16 by default, ~1.7 GB).
+With the buffer read by nontemporal loads, the codes alone (35 MB per
+replica) would otherwise stay in that cache across a short rotation (with 4
+replicas a step took 25 us instead of 28); 16 replicas hold 550 MB of codes,
+so every step reads its state cold from HBM, as a step of one layer of a
+model does between the other layers' work.  Fills advance by one per step
 per replica (f -> f+1, or 0 after a window close), as in a real decode loop.
 
 Prints ONE JSON line.  `value` = tokens/s (B tokens per step); the roofline
@@ -255,54 +259,73 @@ def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None, state_bits=8):
             "gbps": gbps}
 
 
-def bench_decode_long(torch, ops, wl, B2=256, steps=1024, warmup=16, n_tok=8):
+def bench_decode_long(torch, ops, wl, B2=256, steps=1024, warmup=16, n_tok=8, n_rep=4):
     """Large-batch decode: B2 sequences x H heads, `steps` consecutive decode
-    steps of one state (every sequence crosses window ends), timed end to
-    end.  n_tok token sets are bound once and reused in turn."""
+    steps of each of n_rep copies of one state (every sequence crosses window
+    ends), the copies taken in turn so that a step reads its state cold (one
+    copy, 675 MB, would keep its 138 MB of codes in the Infinity Cache from
+    one step to the next); all n_rep * steps launches timed end to end.
+    n_tok token sets are bound once per copy and reused in turn."""
     dev = torch.device("cuda:0")
     d = wl.decode_batch(B=B2, H=H, dk=DK, dv=DV, W=W, seed=2)
     codes, scales = ops.quantize_state(torch.from_numpy(d["state"]).to(dev))
-    st = ops.DecodeState(codes, scales, W, fill=torch.from_numpy(d["fill"]).to(dev))
-    st.buf_k.copy_(torch.from_numpy(d["buf_k"]))
-    st.buf_v.copy_(torch.from_numpy(d["buf_v"]))
-    st.buf_alpha.copy_(torch.from_numpy(d["buf_alpha"]))
-    st.buf_beta.copy_(torch.from_numpy(d["buf_beta"]))
+    fill0 = torch.from_numpy(d["fill"]).to(dev)
+    sts = []
+    for r in range(n_rep):
+        st = ops.DecodeState(codes.clone(), scales.clone(), W, fill=fill0.clone())
+        if r == 0:
+            st.buf_k.copy_(torch.from_numpy(d["buf_k"]))
+            st.buf_v.copy_(torch.from_numpy(d["buf_v"]))
+            st.buf_alpha.copy_(torch.from_numpy(d["buf_alpha"]))
+            st.buf_beta.copy_(torch.from_numpy(d["buf_beta"]))
+        else:
+            for name in ("buf_k", "buf_v", "buf_alpha", "buf_beta"):
+                getattr(st, name).copy_(getattr(sts[0], name))
+        sts.append(st)
     fills = d["fill"].astype(np.int64)
-    del d
+    del d, codes, scales
     o = torch.empty((B2, H, DV), dtype=torch.bfloat16, device=dev)
-    launchers = []
+    launchers = []  # [replica][token set]
+    toks = []
     for s in range(n_tok):
         x = wl.decode_tokens(B=B2, H=H, dk=DK, dv=DV, step=s, seed=3)
-        tok = [torch.from_numpy(x["q"]).to(dev).bfloat16(), torch.from_numpy(x["k"]).to(dev).bfloat16(),
-               torch.from_numpy(x["v"]).to(dev).bfloat16(), torch.from_numpy(x["alpha"]).to(dev),
-               torch.from_numpy(x["beta"]).to(dev)]
-        launchers.append((st.bind(*tok, o=o), tok))
+        toks.append([torch.from_numpy(x["q"]).to(dev).bfloat16(), torch.from_numpy(x["k"]).to(dev).bfloat16(),
+                     torch.from_numpy(x["v"]).to(dev).bfloat16(), torch.from_numpy(x["alpha"]).to(dev),
+                     torch.from_numpy(x["beta"]).to(dev)])
+    for st in sts:
+        launchers.append([st.bind(*tok, o=o) for tok in toks])
+    # every copy advances through the same fills
     step_bytes = decode_schedule_bytes(fills, warmup + steps)
-    total = sum(step_bytes[warmup:])
-    launch = [lc[0] for lc in launchers]
+    total = n_rep * sum(step_bytes[warmup:])
     for i in range(warmup):
-        launch[i % n_tok]()
+        for r in range(n_rep):
+            launchers[r][i % n_tok]()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(steps):
-        launch[i % n_tok]()
+        for r in range(n_rep):
+            launchers[r][i % n_tok]()
     e1.record(stream)
     e1.synchronize()
     ms = e0.elapsed_time(e1)
+    n_launch = n_rep * steps
     gbps = total / (ms * 1e-3) / 1e9
+    del sts, launchers, toks, o
+    torch.cuda.empty_cache()
     return {
-        "workload": f"{steps} consecutive decode steps, B={B2} H={H} d_k=d_v={DK} W={W}, int8 state, "
+        "workload": f"{steps} consecutive decode steps of each of {n_rep} copies of one state (taken in "
+                    f"turn: every step reads its state cold), B={B2} H={H} d_k=d_v={DK} W={W}, int8 state, "
                     "fp32 window buffer, fills from U{0..63} advancing (every sequence crosses window "
                     "ends), timed end to end",
-        "ms_total": round(ms, 3), "ms_per_step": round(ms / steps, 5),
-        "tokens_s": round(B2 * steps / (ms * 1e-3), 1), "gbps": round(gbps, 1),
+        "ms_total": round(ms, 3), "ms_per_step": round(ms / n_launch, 5),
+        "tokens_s": round(B2 * n_launch / (ms * 1e-3), 1), "gbps": round(gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": load_traffic("decode_b256_h32_1024steps_traffic.json", DECODE_SOURCES, 1),
-                     "algorithmic_bytes_per_launch": int(total / steps)},
+                     "algorithmic_bytes_per_launch": int(total / n_launch)},
     }
 
 
@@ -587,7 +610,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--replicas", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurements")
@@ -635,7 +658,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"decode step B={B} H={H} d_k=d_v={DK} W={W} bf16 q/k/v, int8 "
                                f"state, fills U{{0..{W - 1}}}, {args.replicas} state replicas "
-                               "(cold HBM)",
+                               "(cold HBM and Infinity Cache)",
                    "state": "int8 codes + fp32 per-row scales", "window_buffer": "fp32"},
         "hbm_gbps": round(r["gbps"], 1),
         "roofline": {"bound": "hbm", "achieved": round(r["gbps"], 1), "peak": HBM_PEAK_GBPS,
