@@ -183,6 +183,20 @@ def test_decode_batch64_heads32_window64():
     print(f"B64 H32 decode: max rel err {err:.3e}")
 
 
+def test_decode_max_batch():
+    """The largest batch a call takes, B=1024 (H=2, d=64, W=64): the fill
+    scan runs over 16 blocks of 64 sequences, the open sequences are sorted
+    by fill across all of them, and closing sequences sit in the first, a
+    middle and the last block."""
+    B, H, d, W = 1024, 2, 64, 64
+    fill = wl.decode_batch(B=B, H=H, dk=d, dv=d, W=W, seed=11)["fill"]
+    fill[[0, 63, 64, 511, 1000, 1023]] = W - 1
+    d_ = wl.decode_batch(B=B, H=H, dk=d, dv=d, W=W, seed=11, fill=fill)
+    got, codes, scales = _run_decode(d_, W, torch.bfloat16, torch.bfloat16)
+    err = _check_decode(d_, W, got, codes, scales, OUT_TOL_BF16)
+    print(f"B1024 H2 d64 decode: max rel err {err:.3e}, {int((fill == W - 1).sum())} closing")
+
+
 @pytest.mark.parametrize("wht", [False, True])
 def test_decode_strong_decay_full_window(wht):
     """Fast-forgetting heads: decays drawn from U(0.02, 0.2), so the product
