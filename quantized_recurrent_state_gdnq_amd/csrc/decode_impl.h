@@ -289,7 +289,7 @@ __device__ __forceinline__ JobId job_id(const JobList& L, int job) {
 // measured slower: the extra in-flight loads only queue behind HBM.)
 template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT, int BUF, int QB>
 __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L, int slot, int NW, int n_open,
-                                          int lane, float* wy) {
+                                          int lane, float* wy, int* pool) {
   constexpr int EK = DK / 64;    // key / query elements per lane
   constexpr int RPL = DV / 64;   // state rows per lane
   constexpr int CPU4 = 128 / QB;   // codes per 16-byte load
@@ -390,10 +390,19 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
       load_v(J.f - 1 - u, vq[u]);
     }
   };
+  // With four waves of open heads in every workgroup, the workgroup's later
+  // heads (the positions its four waves would take in rounds 1, 2, ... of
+  // the deal) are a pool in LDS: a wave takes the next one, longest first,
+  // when its current head's code rows are loaded, so a wave that finishes
+  // early takes more of the workgroup's work.
+  const int g4 = slot & ~3;  // this workgroup's first slot
+  const bool pooled = (NW & 3) == 0;
   int k = 0;
   int o = slot;
   fetch(o);
   for (;;) {
+    unsigned gv = 0;  // lane 0: the pool index of this wave's next head
+    auto grab = [&]() { if (pooled && lane == 0) gv = unsigned(atomicAdd(pool, 1)); };
     const int f = J.f;
     const size_t v_base = size_t(bh) * DV;
     const size_t bufs_base = size_t(bh) * W;
@@ -563,7 +572,10 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
 #pragma unroll
       for (int u = 0; u < P; u += 2) step2(u, base - u, true);
     }
-    if constexpr (CODE_LEAD > 0) load_codes();  // at most CODE_LEAD blocks (plus the tail) before the rows are needed
+    if constexpr (CODE_LEAD > 0) {  // at most CODE_LEAD blocks (plus the tail) before the rows are needed
+      load_codes();
+      grab();
+    }
     for (; base >= P - 1; base -= P) {
 #pragma unroll
       for (int u = 0; u < P; u += 2) step2(u, base - u, true);
@@ -575,7 +587,10 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
 #pragma unroll
     for (int u = 0; u < P; u += 2)
       if (u == base) step(u, 0, false);
-    if constexpr (CODE_LEAD == 0) load_codes();
+    if constexpr (CODE_LEAD == 0) {
+      load_codes();
+      grab();
+    }
 #pragma unroll
     for (int e = 0; e < EK; ++e) wy[lane * EK + e] = G * yt[e];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -613,8 +628,14 @@ __device__ __forceinline__ void open_wave(const DecodeArgs& a, const JobList& L,
       store_out<OUT_BF16>(a.o, v_base + lane, srow[0] * d[0] + acc[0]);
     }
     __builtin_amdgcn_wave_barrier();  // the next head reuses wy
-    ++k;
-    o = k * NW + ((k & 1) ? NW - 1 - slot : slot);
+    if (pooled) {  // pool index i: round r = 1 + i / 4, longest first within a round
+      const int i = __builtin_amdgcn_readfirstlane(int(gv));
+      const int r = 1 + (i >> 2), w = i & 3;
+      o = r * NW + ((r & 1) ? NW - 4 - g4 + w : g4 + w);
+    } else {
+      ++k;
+      o = k * NW + ((k & 1) ? NW - 1 - slot : slot);
+    }
     if (o >= n_open) break;
     fetch(o);
   }
@@ -630,6 +651,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void decode_kernel(Deco
   __shared__ uint8_t fills[DEC_MAXB];
   __shared__ uint16_t order[DEC_MAXB];
   __shared__ int vbase[64];
+  __shared__ int pool_ctr;  // the open-head pool's next index
   extern __shared__ float4 dyn4[];  // buffered keys [W][DK]
   float* smem = reinterpret_cast<float*>(smem4);
   float* k_lds = reinterpret_cast<float*>(dyn4);
@@ -688,6 +710,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void decode_kernel(Deco
       if (open && r == 0) vbase[f] += __popcll(same);
     }
   }
+  if (threadIdx.x == 0) pool_ctr = 0;
   __syncthreads();
   JobList L;
   L.cmask = cmask;
@@ -922,7 +945,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void decode_kernel(Deco
     const int wave = uniform(tid >> 6);
     const int slot = int(blockIdx.x) * (NT / 64) + wave;
     float* wy = y_lds + wave * DK;
-    if (slot < NW) open_wave<DK, DV, IN_BF16, OUT_BF16, WHT, BUF, QB>(a, L, slot, NW, n_open, lane, wy);
+    if (slot < NW) open_wave<DK, DV, IN_BF16, OUT_BF16, WHT, BUF, QB>(a, L, slot, NW, n_open, lane, wy, &pool_ctr);
   }
 }
 
