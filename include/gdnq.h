@@ -218,7 +218,7 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
                              int32_t* fill_out, void* o, void* stream);
 
 /* ------------------------------------------------------------------------
- * gdnq_prefill_chunked -- chunkwise-parallel prefill of whole windows.
+ * gdnq_prefill_chunked -- chunkwise-parallel prefill.
  *   LinQuant, abstract (chunkwise-parallel prefill as dense matrix products;
  *   SSD prefill with int8 operands; rotations); LeapQuant, abstract
  *   (requantize once per window).
@@ -228,7 +228,7 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
  *   NULL), requantizing at every window end, windows aligned to token 0.
  *   Supported: d_k = d_v in {128, 64} (GDNQ_FLAG_WHT at 128 only), chunk
  *   in {16, 32, 64}, any window 1 <= W <= GDNQ_MAX_WINDOW, T a multiple of
- *   W.  The kernels run every window as
+ *   W when the window-buffer arguments are NULL.  The kernels run every window as
  *   whole 64-position chunks (a window that is not a multiple of 64 is
  *   padded at its end with writes that leave the state unchanged; d = 64
  *   runs as a zero-padded d = 128 head; between the chunks of one window
@@ -268,9 +268,18 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
  *     o      [B,T,H,d_v] out_dtype    (written)
  *     codes  [B,H,d_v,d_k] int8, scales [B,H,d_v] fp32 (GDN, written)
  *     state_f32 [B,H,d_v,d_k] fp32 (SSD and GDNQ_FLAG_NO_REQUANT, written)
+ *     buf_k, buf_v, buf_alpha, buf_beta, fill_out: decode's window buffer
+ *       and fills.  All NULL: whole windows only (T a multiple of W).  Any
+ *       of them set, or T not a multiple of W: all five are required and
+ *       the call is gdnq_prefill_handoff below (GDN, decode's window W in
+ *       1..64, state_f32 NULL, no GDNQ_FLAG_NO_REQUANT; the buffer format
+ *       flags GDNQ_FLAG_BUF_BF16 / GDNQ_FLAG_BUF_FP8 apply): codes/scales
+ *       take the state at the last window boundary, the T mod W writes of
+ *       the open window go to slots 0.. of the buffer and fill_out to
+ *       T mod W, so that gdnq_decode_step continues the sequence.
  *   workspace: gdnq_prefill_workspace_size(p) bytes of device memory (may be
  *   NULL when that size is 0).
- *   Errors: NULL, SHAPE, DTYPE, ALIGN, FLAGS, WORKSPACE, HIP.
+ *   Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, FLAGS, WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int32_t batch, seqlen, heads, d_k, d_v, chunk, window;
@@ -278,13 +287,17 @@ typedef struct {
   uint32_t flags;
 } gdnq_prefill_params;
 
+/* Workspace bytes of gdnq_prefill_chunked for these parameters (0 when
+ * they are invalid): with T a multiple of W, enough both without and with
+ * the window-buffer arguments. */
 size_t gdnq_prefill_workspace_size(const gdnq_prefill_params* p);
 
 gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, const void* k,
                                  const void* v, const float* alpha, const float* beta,
                                  const int8_t* init_codes, const float* init_scales, void* o,
                                  int8_t* codes, float* scales, float* state_f32,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 void* buf_k, void* buf_v, float* buf_alpha, float* buf_beta,
+                                 int32_t* fill_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * gdnq_prefill_chunked_noalloc -- gdnq_prefill_chunked for callers that
@@ -296,9 +309,9 @@ gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, co
  *   every GPU it runs on, from load until the process ends.  The call uses
  *   the array of the current device (the stream must belong to it) and
  *   allocates nothing, neither device nor host memory.
- *     - A call whose gdnq_prefill_workspace_size(p) exceeds
- *       GDNQ_NOALLOC_SCRATCH_BYTES is rejected with GDNQ_ERR_WORKSPACE
- *       before anything is launched (e.g. GDN: 15,616 bytes per chunk-head,
+ *     - A call that needs more workspace than GDNQ_NOALLOC_SCRATCH_BYTES
+ *       (gdnq_prefill_workspace_size(p) bounds it) is rejected with
+ *       GDNQ_ERR_WORKSPACE before anything is launched (e.g. GDN: 15,616 bytes per chunk-head,
  *       so B * (T / 64) * H <= 4297; SSD with GDNQ_FLAG_INT8_QK: 264 bytes
  *       per token-head).
  *     - Every call on one GPU shares that GPU's array: calls that overlap
@@ -314,7 +327,9 @@ gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, co
 gdnq_status gdnq_prefill_chunked_noalloc(const gdnq_prefill_params* p, const void* q, const void* k,
                                          const void* v, const float* alpha, const float* beta,
                                          const int8_t* init_codes, const float* init_scales, void* o,
-                                         int8_t* codes, float* scales, float* state_f32, void* stream);
+                                         int8_t* codes, float* scales, float* state_f32,
+                                         void* buf_k, void* buf_v, float* buf_alpha, float* buf_beta,
+                                         int32_t* fill_out, void* stream);
 
 /* ------------------------------------------------------------------------
  * gdnq_prefill_handoff -- GDN prefill of T tokens (any T >= 0) that leaves

@@ -72,9 +72,9 @@ def _load():
     lib.gdnq_decode_step.restype = i32
     lib.gdnq_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillParams)]
     lib.gdnq_prefill_workspace_size.restype = sz
-    lib.gdnq_prefill_chunked.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 12 + [sz, vp]
+    lib.gdnq_prefill_chunked.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 17 + [sz, vp]
     lib.gdnq_prefill_chunked.restype = i32
-    lib.gdnq_prefill_chunked_noalloc.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 12
+    lib.gdnq_prefill_chunked_noalloc.argtypes = [ctypes.POINTER(PrefillParams)] + [vp] * 17
     lib.gdnq_prefill_chunked_noalloc.restype = i32
     lib.gdnq_prefill_handoff_workspace_size.argtypes = [ctypes.POINTER(PrefillParams)]
     lib.gdnq_prefill_handoff_workspace_size.restype = sz
@@ -129,19 +129,24 @@ def prefill_workspace_size(params):
 
 
 def prefill_chunked(params, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales,
-                    state_f32, workspace, workspace_bytes, stream):
+                    state_f32, workspace, workspace_bytes, stream, buf_k=None, buf_v=None, buf_alpha=None,
+                    buf_beta=None, fill_out=None):
+    """gdnq_prefill_chunked; the window-buffer pointers come last here (they
+    sit before the workspace in the C signature)."""
     return lib.gdnq_prefill_chunked(ctypes.byref(params), q, k, v, alpha, beta, init_codes,
-                                    init_scales, o, codes, scales, state_f32, workspace,
-                                    workspace_bytes, stream)
+                                    init_scales, o, codes, scales, state_f32, buf_k, buf_v, buf_alpha,
+                                    buf_beta, fill_out, workspace, workspace_bytes, stream)
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # GDNQ_NOALLOC_SCRATCH_BYTES
 
 
 def prefill_chunked_noalloc(params, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales,
-                            state_f32, stream):
+                            state_f32, stream, buf_k=None, buf_v=None, buf_alpha=None, buf_beta=None,
+                            fill_out=None):
     return lib.gdnq_prefill_chunked_noalloc(ctypes.byref(params), q, k, v, alpha, beta, init_codes,
-                                            init_scales, o, codes, scales, state_f32, stream)
+                                            init_scales, o, codes, scales, state_f32, buf_k, buf_v,
+                                            buf_alpha, buf_beta, fill_out, stream)
 
 
 def prefill_handoff_workspace_size(params):

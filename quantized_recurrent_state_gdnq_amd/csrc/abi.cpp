@@ -277,21 +277,65 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
   return GDNQ_OK;
 }
 
+// The window-buffer arguments of gdnq_prefill_chunked make it the hand-over
+// (also when T is not a multiple of the window).
+static bool prefill_tail(const gdnq_prefill_params* p, const void* buf_k, const void* buf_v, const float* buf_alpha,
+                         const float* buf_beta, const int32_t* fill_out) {
+  if (buf_k || buf_v || buf_alpha || buf_beta || fill_out) return true;
+  return p && p->window > 0 && p->seqlen >= 0 && p->seqlen % p->window != 0;
+}
+
 size_t gdnq_prefill_workspace_size(const gdnq_prefill_params* p) {
-  gdnq::PrefillLaunch L;
-  if (prefill_validate(p, L) != GDNQ_OK) return 0;
-  return gdnq::prefill_workspace_bytes(L);
+  gdnq::PrefillLaunch L, H;
+  const bool whole = prefill_validate(p, L) == GDNQ_OK;
+  const bool handoff = !(p && (p->flags & GDNQ_FLAG_SSD)) && prefill_validate(p, H, PF_HANDOFF) == GDNQ_OK;
+  const size_t a = whole ? gdnq::prefill_workspace_bytes(L) : 0, b = handoff ? gdnq::prefill_workspace_bytes(H) : 0;
+  return a > b ? a : b;
 }
 
 // gdnq_prefill_chunked and its allocation-free variant: with noalloc, the
 // workspace is the current device's scratch array (checked against its size
 // after every other argument, before the one HIP query of its address).
+static gdnq_status prefill_handoff_impl(gdnq::PrefillLaunch& L, const int32_t* cu_seqlens,
+                                        const int32_t* fill_in, const void* q, const void* k, const void* v, const float* alpha,
+                                        const float* beta, const int8_t* init_codes, const float* init_scales,
+                                        void* o, int8_t* codes, float* scales, void* buf_k, void* buf_v,
+                                        float* buf_alpha, float* buf_beta, int32_t* fill_out,
+                                        void* workspace, size_t workspace_bytes, void* stream, bool noalloc = false);
+
+// noalloc: the workspace is the current device's scratch array, checked
+// against its size after every other argument, before the one HIP query of
+// its address
+static gdnq_status noalloc_workspace(size_t need, void*& workspace, size_t& workspace_bytes) {
+  if (need > gdnq::scratch_capacity())
+    return fail(GDNQ_ERR_WORKSPACE,
+                "this call needs %zu bytes of workspace; the allocation-free entry point holds at most %zu "
+                "(use gdnq_prefill_chunked with a workspace, or split the batch)",
+                need, gdnq::scratch_capacity());
+  workspace = nullptr;
+  workspace_bytes = 0;
+  if (need > 0) {
+    clear_stale_hip_error();
+    if (gdnq_status st = hip_status(gdnq::scratch_for_current_device(&workspace), "device scratch lookup")) return st;
+    workspace_bytes = gdnq::scratch_capacity();
+  }
+  return GDNQ_OK;
+}
+
 static gdnq_status prefill_chunked_impl(const gdnq_prefill_params* p, const void* q, const void* k,
                                         const void* v, const float* alpha, const float* beta,
                                         const int8_t* init_codes, const float* init_scales, void* o,
                                         int8_t* codes, float* scales, float* state_f32,
-                                        void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
+                                        void* buf_k, void* buf_v, float* buf_alpha, float* buf_beta,
+                                        int32_t* fill_out, void* workspace, size_t workspace_bytes, void* stream,
+                                        bool noalloc) {
   gdnq::PrefillLaunch L;
+  if (prefill_tail(p, buf_k, buf_v, buf_alpha, buf_beta, fill_out)) {  // the hand-over to decode
+    if (gdnq_status st = prefill_validate(p, L, PF_HANDOFF)) return st;
+    if (state_f32) return fail(GDNQ_ERR_SHAPE, "state_f32 must be NULL when the window buffer is given (the state goes to codes and scales)");
+    return prefill_handoff_impl(L, nullptr, nullptr, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales,
+                                buf_k, buf_v, buf_alpha, buf_beta, fill_out, workspace, workspace_bytes, stream, noalloc);
+  }
   if (gdnq_status st = prefill_validate(p, L)) return st;
   if (L.B == 0) return ok();
   const size_t bth = size_t(L.B) * L.T * L.H, bh = size_t(L.B) * L.H;
@@ -358,19 +402,7 @@ static gdnq_status prefill_chunked_impl(const gdnq_prefill_params* p, const void
   }
   const size_t need = gdnq::prefill_workspace_bytes(L);
   if (noalloc) {
-    if (need > gdnq::scratch_capacity())
-      return fail(GDNQ_ERR_WORKSPACE,
-                  "this call needs %zu bytes of workspace; the allocation-free entry point holds at most %zu "
-                  "(use gdnq_prefill_chunked with a workspace, or split the batch)",
-                  need, gdnq::scratch_capacity());
-    workspace = nullptr;
-    workspace_bytes = 0;
-    if (need > 0) {
-      clear_stale_hip_error();
-      if (gdnq_status st = hip_status(gdnq::scratch_for_current_device(&workspace), "device scratch lookup"))
-        return st;
-      workspace_bytes = gdnq::scratch_capacity();
-    }
+    if (gdnq_status st = noalloc_workspace(need, workspace, workspace_bytes)) return st;
   }
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDNQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace_bytes);
@@ -385,17 +417,20 @@ gdnq_status gdnq_prefill_chunked(const gdnq_prefill_params* p, const void* q, co
                                  const void* v, const float* alpha, const float* beta,
                                  const int8_t* init_codes, const float* init_scales, void* o,
                                  int8_t* codes, float* scales, float* state_f32,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+                                 void* buf_k, void* buf_v, float* buf_alpha, float* buf_beta,
+                                 int32_t* fill_out, void* workspace, size_t workspace_bytes, void* stream) {
   return prefill_chunked_impl(p, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales, state_f32,
-                              workspace, workspace_bytes, stream, false);
+                              buf_k, buf_v, buf_alpha, buf_beta, fill_out, workspace, workspace_bytes, stream, false);
 }
 
 gdnq_status gdnq_prefill_chunked_noalloc(const gdnq_prefill_params* p, const void* q, const void* k,
                                          const void* v, const float* alpha, const float* beta,
                                          const int8_t* init_codes, const float* init_scales, void* o,
-                                         int8_t* codes, float* scales, float* state_f32, void* stream) {
+                                         int8_t* codes, float* scales, float* state_f32,
+                                         void* buf_k, void* buf_v, float* buf_alpha, float* buf_beta,
+                                         int32_t* fill_out, void* stream) {
   return prefill_chunked_impl(p, q, k, v, alpha, beta, init_codes, init_scales, o, codes, scales, state_f32,
-                              nullptr, 0, stream, true);
+                              buf_k, buf_v, buf_alpha, buf_beta, fill_out, nullptr, 0, stream, true);
 }
 
 size_t gdnq_prefill_handoff_workspace_size(const gdnq_prefill_params* p) {
@@ -434,7 +469,7 @@ static gdnq_status prefill_handoff_impl(gdnq::PrefillLaunch& L, const int32_t* c
                                         const float* beta, const int8_t* init_codes, const float* init_scales,
                                         void* o, int8_t* codes, float* scales, void* buf_k, void* buf_v,
                                         float* buf_alpha, float* buf_beta, int32_t* fill_out,
-                                        void* workspace, size_t workspace_bytes, void* stream) {
+                                        void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
   if (L.B == 0) return ok();
   // token-indexed arrays: B x T tokens, or T packed tokens of variable-length sequences
   const size_t bth = (cu_seqlens ? size_t(1) : size_t(L.B)) * L.T * L.H, bh = size_t(L.B) * L.H;
@@ -483,6 +518,9 @@ static gdnq_status prefill_handoff_impl(gdnq::PrefillLaunch& L, const int32_t* c
         return fail(GDNQ_ERR_ALIAS, "fill_in overlaps %s", sp[i].name);
   }
   const size_t need = gdnq::prefill_workspace_bytes(L);
+  if (noalloc) {
+    if (gdnq_status st = noalloc_workspace(need, workspace, workspace_bytes)) return st;
+  }
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDNQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace_bytes);
   if (workspace && !aligned16(workspace)) return fail(GDNQ_ERR_ALIGN, "workspace is not 16-byte aligned");

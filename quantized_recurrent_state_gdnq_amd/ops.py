@@ -192,8 +192,14 @@ def prefill_workspace_size(q, v, *, window=64, chunk=64, wht=False, ssd=False, i
 def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_codes=None,
                     init_scales=None, wht=False, ssd=False, int8_qk=False,
                     out_dtype=torch.bfloat16, o=None, codes=None, scales=None, state_f32=None,
-                    workspace=None, state_bits=8, noalloc=False, no_requant=False):
+                    workspace=None, state_bits=8, noalloc=False, no_requant=False, state=None):
     """Chunkwise prefill (see gdnq_prefill_chunked in include/gdnq.h).
+
+    state (a DecodeState, GDN only): its window buffer and fills take the
+    open window's T mod window writes, as the hand-over does, and its codes
+    and scales the state at the last window boundary (codes/scales must then
+    be None); required when T is not a multiple of the window.  Returns
+    (o, state.codes, state.scales).
 
     q, k [B,T,H,d_k], v [B,T,H,d_v] bf16; alpha (and beta for GDN) [B,T,H] fp32.
     GDN returns (o, codes, scales); SSD (ssd=True) returns (o, state_f32), and
@@ -213,6 +219,40 @@ def prefill_chunked(q, k, v, alpha, beta=None, *, window=64, chunk=64, init_code
     _need(alpha, "alpha", torch.float32, dev)
     if tuple(k.shape) != (B, T, H, d_k) or tuple(v.shape) != (B, T, H, d_v) or tuple(alpha.shape) != (B, T, H):
         raise ValueError("inconsistent prefill shapes")
+    if state is not None or (not ssd and not no_requant and window > 0 and T % window != 0):
+        if state is None:
+            raise ValueError(f"T = {T} is not a multiple of the window {window}: pass state= (a DecodeState) "
+                             "to receive the open window's writes")
+        if ssd or no_requant or state_f32 is not None or codes is not None or scales is not None:
+            raise ValueError("with state=, the state goes to state.codes/state.scales (GDN, no state_f32, "
+                             "codes or scales)")
+        if state.state_bits != state_bits:
+            raise ValueError("state: its code width differs from state_bits")
+        _need(beta, "beta", torch.float32, dev)
+        if tuple(beta.shape) != (B, T, H):
+            raise ValueError("beta must be [B,T,H]")
+        p = _prefill_params(q, v, window=window, chunk=chunk, wht=wht, ssd=False, int8_qk=False,
+                            out_dtype=out_dtype, state_bits=state_bits,
+                            extra_flags=_state_shapes(state, B, H, d_k, d_v, window, wht))
+        if o is None:
+            o = torch.empty((B, T, H, d_v), dtype=out_dtype, device=dev)
+        _shape(_need(o, "o", out_dtype, dev), (B, T, H, d_v), "o")
+        _init_shapes(init_codes, init_scales, (B, H, d_v, d_k * state_bits // 8), dev)
+        bufs = dict(buf_k=_ptr(state.buf_k), buf_v=_ptr(state.buf_v), buf_alpha=_ptr(state.buf_alpha),
+                    buf_beta=_ptr(state.buf_beta), fill_out=_ptr(state.fill))
+        args = (p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(init_codes), _ptr(init_scales),
+                _ptr(o), _ptr(state.codes), _ptr(state.scales), None)
+        if noalloc:
+            if workspace is not None:
+                raise ValueError("noalloc: no workspace is taken")
+            _lib.check(_lib.prefill_chunked_noalloc(*args, _stream(dev), **bufs))
+        else:
+            need = int(_lib.prefill_workspace_size(p))
+            if need and workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+            _lib.check(_lib.prefill_chunked(*args, _ptr(workspace), ws_bytes, _stream(dev), **bufs))
+        return o, state.codes, state.scales
     p = _prefill_params(q, v, window=window, chunk=chunk, wht=wht, ssd=ssd, int8_qk=int8_qk,
                         out_dtype=out_dtype, state_bits=state_bits,
                         extra_flags=_lib.GDNQ_FLAG_NO_REQUANT if no_requant else 0)

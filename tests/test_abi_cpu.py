@@ -171,17 +171,19 @@ def _pp(B=1, T=128, H=2, dk=128, dv=128, C=64, W=64, ind=1, outd=1, flags=0):
 def _prefill(params, fake, **over):
     a = dict(q=fake(), k=fake(), v=fake(), alpha=fake(), beta=fake(), init_codes=None,
              init_scales=None, o=fake(), codes=fake(), scales=fake(), state_f32=None,
-             workspace=None, ws=0)
+             workspace=None, ws=0, buf_k=None, buf_v=None, buf_alpha=None, buf_beta=None, fill_out=None)
     a.update(over)
     return _lib.prefill_chunked(params, a["q"], a["k"], a["v"], a["alpha"], a["beta"],
                                 a["init_codes"], a["init_scales"], a["o"], a["codes"],
-                                a["scales"], a["state_f32"], a["workspace"], a["ws"], None)
+                                a["scales"], a["state_f32"], a["workspace"], a["ws"], None,
+                                buf_k=a["buf_k"], buf_v=a["buf_v"], buf_alpha=a["buf_alpha"],
+                                buf_beta=a["buf_beta"], fill_out=a["fill_out"])
 
 
 @pytest.mark.parametrize("params,status", [
-    (_pp(C=8, W=8), 2), (_pp(T=100), 2), (_pp(dk=64, dv=128), 2), (_pp(W=0), 2), (_pp(W=-64), 2),
-    (_pp(T=48, W=32, C=32), 2),           # not a whole number of windows
-    (_pp(T=128, W=256), 2),                # likewise
+    (_pp(C=8, W=8), 2), (_pp(T=100), 1), (_pp(dk=64, dv=128), 2), (_pp(W=0), 2), (_pp(W=-64), 2),
+    (_pp(T=48, W=32, C=32), 1),           # not a whole number of windows: the window buffer is required
+    (_pp(T=128, W=256), 2),                # likewise, and decode's window is at most 64
     (_pp(T=0, W=(1 << 24) + 64), 2),       # longer than GDNQ_MAX_WINDOW
     (_pp(dk=64, dv=64, flags=1), 8),       # no rotation at d = 64
     (_pp(ind=0), 3), (_pp(outd=3), 3), (_pp(flags=4), 8), (_pp(flags=16), 8),
@@ -392,13 +394,39 @@ def test_handoff_contract():
     k = f()
     assert _handoff(p, f, k=k, fill_out=k) == 5                 # output over an input
     assert _handoff(_pp(B=0, T=100), f) == 0                    # empty batch: no-op
-    assert _lib.prefill_workspace_size(p) == 0                  # the chunked prefill rejects T = 100
+    # the chunked call with T = 100 is the hand-over: same workspace
+    assert _lib.prefill_workspace_size(p) == _lib.prefill_handoff_workspace_size(p)
+
+
+def test_chunked_window_buffer_contract():
+    """gdnq_prefill_chunked with decode's window buffer (or T not a multiple
+    of the window) is the hand-over: all five buffer arguments required, GDN
+    only, no state_f32, decode's window at most 64; its workspace size
+    covers both forms when T is a multiple of the window."""
+    f = Fake()
+    bufs = lambda: dict(buf_k=f(), buf_v=f(), buf_alpha=f(), buf_beta=f(), fill_out=f())
+    p = _pp(B=2, T=100, H=3)
+    assert _prefill(p, f) == 1                                   # the open window needs the buffer
+    assert _prefill(p, f, **bufs()) == 6                         # workspace missing (the hand-over's)
+    b = bufs()
+    b["fill_out"] = None
+    assert _prefill(p, f, **b) == 1
+    assert _prefill(p, f, state_f32=f(), **bufs()) == 2
+    assert _prefill(_pp(B=2, T=128, H=3, dv=128, flags=2), f, beta=None, codes=None, scales=None,
+                    state_f32=f(), **bufs()) == 8                # not for SSD
+    assert _prefill(_pp(B=2, T=128, H=3, flags=8), f, codes=None, scales=None, **bufs()) == 8  # nor NO_REQUANT
+    assert _prefill(_pp(B=2, T=256, H=3, W=128), f, **bufs()) == 2  # decode's window is at most 64
+    p = _pp(B=2, T=128, H=3, W=32, C=32)
+    assert _prefill(p, f, **bufs()) == 6                         # whole windows and the buffer: the hand-over
+    need = _lib.prefill_workspace_size(p)
+    assert need >= _lib.prefill_handoff_workspace_size(p) > 0
+    assert _prefill(p, f, **bufs(), workspace=f(), ws=need - 1) == 6
 
 
 def test_handoff_buffer_formats():
     """GDNQ_FLAG_BUF_BF16 / GDNQ_FLAG_BUF_FP8 select decode's window-buffer
-    formats for the hand-over, varlen and resume calls (not the chunked
-    prefill).  The buffer spans follow the format: a buf_v placed right after
+    formats for the hand-over, varlen and resume calls and the chunked
+    prefill given the window buffer (not without it).  The buffer spans follow the format: a buf_v placed right after
     a bf16-sized buf_k is disjoint from it under the bf16 flag and overlaps
     an fp32 buf_k; an FP8 buffer holds B H W d code bytes then B H W fp32
     scales."""
@@ -409,7 +437,9 @@ def test_handoff_buffer_formats():
         assert ws == _lib.prefill_handoff_workspace_size(_pp(B=B, T=T, H=H)) > 0
         assert _lib.prefill_varlen_workspace_size(p) > 0
         assert _lib.prefill_resume_workspace_size(p, 0) > 0
-        assert _lib.prefill_workspace_size(_pp(B=B, T=128, H=H, flags=flags)) == 0
+        pc = _pp(B=B, T=128, H=H, flags=flags)
+        assert _lib.prefill_workspace_size(pc) == _lib.prefill_handoff_workspace_size(pc) > 0
+        assert _prefill(pc, Fake()) == 8                         # a buffer format without the buffer
     f = Fake()
     k = f(1 << 26)
     o = f()

@@ -134,3 +134,64 @@ def test_handoff_larger_batch():
     torch.cuda.synchronize()
     ref = O.prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], W=W)
     _check(st, o, ref, T, OUT_TOL_BF16, teacher_codes=False)
+
+
+STATE = ("codes", "scales", "buf_k", "buf_v", "buf_alpha", "buf_beta", "fill")
+
+
+def _fresh(B, H, d, window, buf_dtype=torch.float32):
+    return ops.DecodeState(torch.empty((B, H, d, d), dtype=torch.int8, device=DEV),
+                           torch.empty((B, H, d), dtype=torch.float32, device=DEV), window,
+                           fill=torch.zeros(B, dtype=torch.int32, device=DEV), buf_dtype=buf_dtype)
+
+
+@pytest.mark.parametrize("T,window,buf", [(100, 64, torch.float32), (37, 16, torch.bfloat16),
+                                          (90, 64, torch.float8_e4m3fn)])
+def test_chunked_with_window_buffer_is_the_handoff(T, window, buf):
+    """gdnq_prefill_chunked given decode's window buffer (T not a multiple
+    of the window) gives bitwise the results of gdnq_prefill_handoff, with
+    a workspace and through the allocation-free entry point."""
+    B, H, d = 2, 3, 128
+    x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=200 + T)
+    c0, s0 = _random_state(B, H, d, 201)
+    args = _inputs(x)
+    o1, st1 = ops.prefill_handoff(*args, window=window, init_codes=dev(c0), init_scales=dev(s0),
+                                  out_dtype=torch.float32, buf_dtype=buf)
+    st2 = _fresh(B, H, d, window, buf)
+    o2, c2, s2 = ops.prefill_chunked(*args, window=window, init_codes=dev(c0), init_scales=dev(s0),
+                                     out_dtype=torch.float32, state=st2)
+    st3 = _fresh(B, H, d, window, buf)
+    o3, _, _ = ops.prefill_chunked(*args, window=window, init_codes=dev(c0), init_scales=dev(s0),
+                                   out_dtype=torch.float32, state=st3, noalloc=True)
+    torch.cuda.synchronize()
+    assert c2 is st2.codes and s2 is st2.scales
+    r = T % window
+    names = STATE + (("buf_k_scale", "buf_v_scale") if buf == torch.float8_e4m3fn else ())
+    for o, st, what in ((o2, st2, "workspace"), (o3, st3, "allocation-free")):
+        assert np.array_equal(host(o), host(o1)), f"{what}: o"
+        for name in names:
+            a, b = host(getattr(st, name)), host(getattr(st1, name))
+            if name.startswith("buf"):  # slots past the open window's r writes are not written
+                a, b = a[:, :, :r], b[:, :, :r]
+            assert np.array_equal(a, b, equal_nan=True), f"{what}: {name}"
+    assert np.all(host(st2.fill) == r)
+
+
+def test_chunked_whole_windows_with_window_buffer():
+    """T a multiple of the window and the buffer given: the state and outputs
+    are bitwise those of the call without the buffer, and every fill is 0
+    (an empty window buffer for decode to continue from)."""
+    B, H, d, T, window = 2, 3, 128, 128, 32
+    x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=210)
+    c0, s0 = _random_state(B, H, d, 211)
+    args = _inputs(x)
+    o1, c1, s1 = ops.prefill_chunked(*args, window=window, chunk=32, init_codes=dev(c0), init_scales=dev(s0),
+                                     out_dtype=torch.float32)
+    st = _fresh(B, H, d, window)
+    st.fill.fill_(7)
+    o2, c2, s2 = ops.prefill_chunked(*args, window=window, chunk=32, init_codes=dev(c0), init_scales=dev(s0),
+                                     out_dtype=torch.float32, state=st)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o1), host(o2))
+    assert np.array_equal(host(c1), host(c2)) and np.array_equal(host(s1), host(s2))
+    assert not host(st.fill).any()
