@@ -269,8 +269,9 @@ gdnq_status gdnq_decode_step(const gdnq_decode_params* p, const void* q, const v
  *     codes  [B,H,d_v,d_k] int8, scales [B,H,d_v] fp32 (GDN, written)
  *     state_f32 [B,H,d_v,d_k] fp32 (SSD and GDNQ_FLAG_NO_REQUANT, written)
  *     buf_k, buf_v, buf_alpha, buf_beta, fill_out: decode's window buffer
- *       and fills.  All NULL: whole windows only (T a multiple of W).  Any
- *       of them set, or T not a multiple of W: all five are required and
+ *       and fills.  All NULL: whole windows only (T a multiple of W; SSD
+ *       and GDNQ_FLAG_NO_REQUANT have no windows).  Any of them set, or a
+ *       windowed GDN call with T not a multiple of W: all five required and
  *       the call is gdnq_prefill_handoff below (GDN, decode's window W in
  *       1..64, state_f32 NULL, no GDNQ_FLAG_NO_REQUANT; the buffer format
  *       flags GDNQ_FLAG_BUF_BF16 / GDNQ_FLAG_BUF_FP8 apply): codes/scales

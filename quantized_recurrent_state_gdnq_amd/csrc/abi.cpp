@@ -282,7 +282,9 @@ static gdnq_status prefill_validate(const gdnq_prefill_params* p, gdnq::PrefillL
 static bool prefill_tail(const gdnq_prefill_params* p, const void* buf_k, const void* buf_v, const float* buf_alpha,
                          const float* buf_beta, const int32_t* fill_out) {
   if (buf_k || buf_v || buf_alpha || buf_beta || fill_out) return true;
-  return p && p->window > 0 && p->seqlen >= 0 && p->seqlen % p->window != 0;
+  // SSD and GDNQ_FLAG_NO_REQUANT have no windows
+  if (!p || (p->flags & (GDNQ_FLAG_SSD | GDNQ_FLAG_NO_REQUANT))) return false;
+  return p->window > 0 && p->seqlen >= 0 && p->seqlen % p->window != 0;
 }
 
 size_t gdnq_prefill_workspace_size(const gdnq_prefill_params* p) {

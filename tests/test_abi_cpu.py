@@ -416,6 +416,9 @@ def test_chunked_window_buffer_contract():
                     state_f32=f(), **bufs()) == 8                # not for SSD
     assert _prefill(_pp(B=2, T=128, H=3, flags=8), f, codes=None, scales=None, **bufs()) == 8  # nor NO_REQUANT
     assert _prefill(_pp(B=2, T=256, H=3, W=128), f, **bufs()) == 2  # decode's window is at most 64
+    # no windows without requantization or with SSD: any T, no buffer needed
+    assert _prefill(_pp(B=2, T=100, H=3, flags=8), f, codes=None, scales=None) == 1  # (state_f32 missing)
+    assert _prefill(_pp(B=2, T=100, H=3, flags=2, dv=64), f, beta=None, codes=None, scales=None) == 2  # (T % 64)
     p = _pp(B=2, T=128, H=3, W=32, C=32)
     assert _prefill(p, f, **bufs()) == 6                         # whole windows and the buffer: the hand-over
     need = _lib.prefill_workspace_size(p)
