@@ -64,14 +64,19 @@ struct SlidingArgs {
   int B, H, W;
 };
 
+// Three workgroups per CU: the window's keys and values take W (d_k + d_v)
+// fp32 of LDS, sized by the call's window (8 KB at W = 8, d = 128), and the
+// registers are held to three waves per SIMD (at four, phase 3's 64 columns
+// per thread spill), so a CU overlaps the phases of three heads.
 template <int DK, int DV, bool IN_BF16, bool OUT_BF16, bool WHT>
-__global__ __launch_bounds__(SL_THREADS) void sliding_kernel(SlidingArgs a) {
+__global__ __launch_bounds__(SL_THREADS, 3) void sliding_kernel(SlidingArgs a) {
   constexpr int EK = DK / 64;          // key elements per lane (waves 0, 1)
   constexpr int TPR = SL_THREADS / DV; // threads per state row (phase 3)
   constexpr int CPT = DK / TPR;        // columns per thread
   static_assert(CPT % 16 == 0, "codes load in 16-byte words");
-  __shared__ float Kw[SL_WMAX * DK];  // window keys, oldest first
-  __shared__ float Vw[SL_WMAX * DV];  // window values, oldest first
+  extern __shared__ float sl_dyn[];
+  float* const Kw = sl_dyn;                // window keys [W][DK], oldest first
+  float* const Vw = sl_dyn + a.W * DK;     // window values [W][DV], oldest first
   __shared__ float aw[SL_WMAX], bw[SL_WMAX], cw[SL_WMAX + 1];
   __shared__ float qs[DK], ks[DK], y1[DK], kl[DK];
   __shared__ float cur[4];  // alpha_t, beta_t, c_t, leaving beta
@@ -265,10 +270,20 @@ __global__ __launch_bounds__(SL_THREADS) void sliding_kernel(SlidingArgs a) {
   }
 }
 
+template <int DK, int DV, bool IB, bool OB, bool WH>
+hipError_t launch_sl1(const SlidingArgs& s, hipStream_t st) {
+  const dim3 grid(unsigned(s.B) * s.H), block(SL_THREADS);
+  const unsigned lds = unsigned(s.W) * (DK + DV) * 4;
+  const void* fn = reinterpret_cast<const void*>(&sliding_kernel<DK, DV, IB, OB, WH>);
+  if (hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, SL_WMAX * (DK + DV) * 4))
+    return e;
+  hipLaunchKernelGGL((sliding_kernel<DK, DV, IB, OB, WH>), grid, block, lds, st, s);
+  return hipGetLastError();
+}
+
 template <int DK, int DV>
 hipError_t launch_sl(const SlidingArgs& s, bool ib, bool ob, bool wht, hipStream_t st) {
-  const dim3 grid(unsigned(s.B) * s.H), block(SL_THREADS);
-#define GDNQ_SL(IB, OB, WH) hipLaunchKernelGGL((sliding_kernel<DK, DV, IB, OB, WH>), grid, block, 0, st, s)
+#define GDNQ_SL(IB, OB, WH) return launch_sl1<DK, DV, IB, OB, WH>(s, st)
   if (ib) {
     if (ob) { if (wht) GDNQ_SL(true, true, true); else GDNQ_SL(true, true, false); }
     else { if (wht) GDNQ_SL(true, false, true); else GDNQ_SL(true, false, false); }
