@@ -443,7 +443,7 @@ PREFILL_SOURCES = {False: ["prefill_gdn.hip", "device_common.h", "mfma.h"],
 W_LONG = 128  # the long-window prefill line
 
 
-def bench_prefill(torch, ops, wl, steps=5, warmup=2, with_cpu=True):
+def bench_prefill(torch, ops, wl, steps=20, warmup=3, with_cpu=True):
     """Secondary: GDN chunked prefill B=4, T=8192, H=16, d=128, C=W=64 (bf16
     output, zero initial state); SSD prefill B=2, T=4096, H=80, d_k=128,
     d_v=64 with WHT-rotated int8 q/k (bf16 output); the GDN hand-over to
