@@ -92,9 +92,16 @@ struct SeqMap {
 
 // ---------------------------------------------------------------- prep
 constexpr int KP = 136;  // bf16 pitch of [token][dim] tiles
-constexpr int AP = 65;   // fp32 pitch of A
-constexpr int PREP_GRID = 4 * 256;  // prep workgroups: four per CU
-constexpr int PREP_KT = PC * KP * 2 > (PC * PC + 3 * 256) * 4 ? PC * KP * 2 : (PC * PC + 3 * 256) * 4;
+// A and T are kept as their ten lower 16x16 tiles (the upper ones are zero):
+// tile (ti, tj), ti >= tj, is tile ti (ti + 1) / 2 + tj, rows of AQ / TQ
+// floats (17: the level products read A down a column without bank
+// conflicts; 20: T's rows stay 16-byte aligned and a column read is
+// conflict-free)
+constexpr int AQ = 17, TQ = 20;
+constexpr int PREP_GRID = 5 * 256;  // prep workgroups: five per CU
+constexpr int PREP_T = (TT * 16 * TQ + 3 * 256) * 4;  // T tiles, then the level products
+constexpr int PREP_KT = PC * KP * 2 > PREP_T ? PC * KP * 2 : PREP_T;
+__device__ __forceinline__ int ltile(int ti, int tj) { return ti * (ti + 1) / 2 + tj; }  // tj <= ti
 
 struct PrepArgs {
   const uint16_t* k;
@@ -107,14 +114,14 @@ struct PrepArgs {
   int total;  // chunk-heads the grid covers (an upper bound when mapped)
 };
 
-__global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(256, 5) void gdn_prep_kernel(PrepArgs a) {
   // K is only needed for K K^T; T and the level products reuse its space
   __shared__ __attribute__((aligned(16))) unsigned char kt_raw[PREP_KT];
-  __shared__ float Al[PC * AP];
+  __shared__ float Al[TT * 16 * AQ];
   __shared__ float gl[PC], bl[PC];
   __bf16* Kl = reinterpret_cast<__bf16*>(kt_raw);
   float* Tl = reinterpret_cast<float*>(kt_raw);
-  float* Pl = Tl + PC * PC;
+  float* Pl = Tl + TT * 16 * TQ;
   // Each workgroup takes chunk-heads blockIdx.x, + gridDim.x, ... (index
   // chunk * H + h, chunks numbered across the sequences) and loads the next
   // one's keys, alpha and beta into registers while it works on the current.
@@ -244,15 +251,8 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
       int it, jt;
       tile_of(tt, it, jt);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) Al[(it * 16 + 4 * lq + q) * AP + jt * 16 + lr] = av[n][q];
+      for (int q = 0; q < 4; ++q) Al[(tt * 16 + 4 * lq + q) * AQ + lr] = av[n][q];
     }
-  }
-  // strictly upper blocks of T are zero
-  for (int e = tid; e < 6 * 256; e += 256) {
-    const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-    const int bi = blk < 3 ? 0 : blk < 5 ? 1 : 2;
-    const int bj = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-    Tl[(bi * 16 + rr) * PC + bj * 16 + cc] = 0.f;
   }
   __syncthreads();
 
@@ -264,11 +264,11 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
     for (int r = 0; r < 16; ++r) {
       float s = (r == cc) ? 1.f : 0.f;
 #pragma unroll
-      for (int j = 0; j < r; ++j) s -= Al[(bb * 16 + r) * AP + bb * 16 + j] * t[j];
+      for (int j = 0; j < r; ++j) s -= Al[(ltile(bb, bb) * 16 + r) * AQ + j] * t[j];
       t[r] = s;
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Tl[(bb * 16 + r) * PC + bb * 16 + cc] = t[r];
+    for (int r = 0; r < 16; ++r) Tl[(ltile(bb, bb) * 16 + r) * TQ + cc] = t[r];
   }
   __syncthreads();
 
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
       for (int kb = j; kb < i; ++kb)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-          acc = mfma4(Al[(i * 16 + lr) * AP + kb * 16 + 4 * kk + lq], Tl[(kb * 16 + 4 * kk + lq) * PC + j * 16 + lr], acc);
+          acc = mfma4(Al[(ltile(i, kb) * 16 + lr) * AQ + 4 * kk + lq], Tl[(ltile(kb, j) * 16 + 4 * kk + lq) * TQ + lr], acc);
 #pragma unroll
       for (int q = 0; q < 4; ++q) Pl[wave * 256 + (4 * lq + q) * 16 + lr] = acc[q];
     }
@@ -292,9 +292,9 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc = mfma4(Tl[(i * 16 + lr) * PC + i * 16 + 4 * kk + lq], Pl[wave * 256 + (4 * kk + lq) * 16 + lr], acc);
+        acc = mfma4(Tl[(ltile(i, i) * 16 + lr) * TQ + 4 * kk + lq], Pl[wave * 256 + (4 * kk + lq) * 16 + lr], acc);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) Tl[(i * 16 + 4 * lq + q) * PC + j * 16 + lr] = -acc[q];
+      for (int q = 0; q < 4; ++q) Tl[(ltile(i, j) * 16 + 4 * lq + q) * TQ + lr] = -acc[q];
     }
     __syncthreads();
   }
@@ -303,10 +303,11 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(PrepArgs a) {
      // thread -> row tid / 4, columns [(tid % 4) * 16, +16), tiles on or below the diagonal
     const int i = tid >> 2, c0 = (tid & 3) * 16;
     const int ti = i >> 4, tj = c0 >> 4;
+    const int tl = tj <= ti ? ltile(ti, tj) : 0;  // tiles above the diagonal are not stored (nor read)
     float x[16];
 #pragma unroll
     for (int e = 0; e < 16; e += 4) {
-      const float4 t4 = *reinterpret_cast<const float4*>(Tl + i * PC + c0 + e);
+      const float4 t4 = *reinterpret_cast<const float4*>(Tl + (tl * 16 + (i & 15)) * TQ + e);
       x[e] = t4.x;
       x[e + 1] = t4.y;
       x[e + 2] = t4.z;
