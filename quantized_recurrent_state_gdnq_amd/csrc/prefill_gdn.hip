@@ -272,12 +272,14 @@ __global__ __launch_bounds__(256, 5) void gdn_prep_kernel(PrepArgs a) {
   }
   __syncthreads();
 
-  // off-diagonal blocks, one block-diagonal at a time (fp32 MFMA):
-  //   P = sum_{k=j}^{i-1} A_ik T_kj,   T_ij = -T_ii P
-  for (int d = 1; d <= 3; ++d) {
-    const int nb = 4 - d;
-    if (wave < nb) {
-      const int i = d + wave, j = wave;
+  // off-diagonal blocks (fp32 MFMA), wave j the blocks of column j in turn,
+  // i = j + 1 .. 3:  P = sum_{k=j}^{i-1} A_ik T_kj,  T_ij = -T_ii P.  A block
+  // needs only its own column's blocks above it and the diagonal, so the
+  // waves exchange nothing; within a wave the LDS round trips (P, then the
+  // new block) are ordered by wavefront fences.
+  if (wave < 3) {
+    const int j = wave;
+    for (int i = j + 1; i < 4; ++i) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int kb = j; kb < i; ++kb)
 #pragma unroll
@@ -285,19 +287,21 @@ __global__ __launch_bounds__(256, 5) void gdn_prep_kernel(PrepArgs a) {
           acc = mfma4(Al[(ltile(i, kb) * 16 + lr) * AQ + 4 * kk + lq], Tl[(ltile(kb, j) * 16 + 4 * kk + lq) * TQ + lr], acc);
 #pragma unroll
       for (int q = 0; q < 4; ++q) Pl[wave * 256 + (4 * lq + q) * 16 + lr] = acc[q];
-    }
-    __syncthreads();
-    if (wave < nb) {
-      const int i = d + wave, j = wave;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc = mfma4(Tl[(ltile(i, i) * 16 + lr) * TQ + 4 * kk + lq], Pl[wave * 256 + (4 * kk + lq) * 16 + lr], acc);
+        t = mfma4(Tl[(ltile(i, i) * 16 + lr) * TQ + 4 * kk + lq], Pl[wave * 256 + (4 * kk + lq) * 16 + lr], t);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // P is read before the next block overwrites it
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int q = 0; q < 4; ++q) Tl[(ltile(i, j) * 16 + 4 * lq + q) * TQ + lr] = -acc[q];
+      for (int q = 0; q < 4; ++q) Tl[(ltile(i, j) * 16 + 4 * lq + q) * TQ + lr] = -t[q];
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   {  // T's ten lower 16x16 tiles as three bf16 parts [part][tile][16][16]:
      // thread -> row tid / 4, columns [(tid % 4) * 16, +16), tiles on or below the diagonal
