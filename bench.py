@@ -188,10 +188,11 @@ def cpu_baseline_decode(seconds=12.0):
                       f"({el:.1f} s), numpy fp32 oracle", **info}
 
 
-def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None, state_bits=8):
+def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None, state_bits=8, wht=False):
     """Timed decode steps; buf_dtype torch.bfloat16 runs the low-precision
     window buffer (writes stored as bf16) on the same workload; state_bits 4
-    the uniform 4-bit state."""
+    the uniform 4-bit state; wht=True the rotation of q and k (the state and
+    buffered keys taken as in the rotated basis)."""
     buf_dtype = buf_dtype or torch.float32
     e_buf = {torch.float32: 4, torch.bfloat16: 2, torch.float8_e4m3fn: 1}[buf_dtype]
     dev = torch.device("cuda:0")
@@ -203,7 +204,7 @@ def bench_decode(args, torch, ops, wl, rep_count, buf_dtype=None, state_bits=8):
     for i in range(rep_count):
         rep = ops.DecodeState(codes0.clone(), scales0.clone(), W,
                               fill=torch.from_numpy(d["fill"]).to(dev), buf_dtype=buf_dtype,
-                              state_bits=state_bits)
+                              state_bits=state_bits, wht=wht)
         if buf_dtype == torch.float8_e4m3fn:  # E4M3 vector pairs: scale absmax/448, codes by torch's cast
             for dst, sdst, x in ((rep.buf_k, rep.buf_k_scale, d["buf_k"]), (rep.buf_v, rep.buf_v_scale, d["buf_v"])):
                 t = torch.nan_to_num(torch.from_numpy(x).to(dev))
@@ -617,6 +618,7 @@ def main():
     ap.add_argument("--no-fp8-buffer", action="store_true", help="skip the FP8 window-buffer line")
     ap.add_argument("--no-state4", action="store_true", help="skip the 4-bit state line")
     ap.add_argument("--no-long-decode", action="store_true", help="skip the B=256, 1024-step decode line")
+    ap.add_argument("--no-wht", action="store_true", help="skip the decode line with the rotation")
     ap.add_argument("--no-sliding", action="store_true", help="skip the sliding-window decode line")
     ap.add_argument("--no-bf16-buffer", action="store_true",
                     help="skip the decode measurement with the bf16 window buffer")
@@ -708,6 +710,20 @@ def main():
                          "traffic": load_traffic("decode_b64_h32_state4_traffic.json",
                                                  DECODE_SOURCES + ["decode_q4.hip"], 1),
                          "algorithmic_bytes_per_launch": int(r4["bytes_per_launch"])},
+        }
+    if not args.no_wht:
+        rw = bench_decode(args, torch, ops, wl, max(1, args.replicas), wht=True)
+        line["decode_wht"] = {
+            "workload": "the same decode step with q and k rotated by the normalised Walsh-Hadamard "
+                        "matrix inside the kernel (GDNQ_FLAG_WHT; state and buffered keys in the "
+                        "rotated basis)",
+            "ms_per_step": round(rw["ms_per_step"], 5),
+            "tokens_s": round(rw["tokens_s"], 1),
+            "gbps": round(rw["gbps"], 1),
+            "roofline": {"bound": "hbm", "achieved": round(rw["gbps"], 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(rw["gbps"] / HBM_PEAK_GBPS, 4),
+                         "traffic": load_traffic("decode_b64_h32_wht_traffic.json", DECODE_SOURCES, 1),
+                         "algorithmic_bytes_per_launch": int(rw["bytes_per_launch"])},
         }
     if not args.no_sliding:
         line["decode_sliding_window"] = bench_decode_sliding(args, torch, ops, wl, max(1, args.replicas))
