@@ -273,11 +273,13 @@ __device__ __forceinline__ void codec_codes(const float (&x)[N], float scale, fl
 // (relative) of 1 / scale, so q = fl(x * inv) is within |x/scale| 1.8e-7 <=
 // 2.3e-5 of the exact quotient and fl(x/scale) within 7.6e-6: their nearest
 // integers can differ only when q lies within 3.1e-5 of a half-integer, and
-// those rows divide.  Returns the scale.
+// those rows divide.  A row whose scale rounds to 0 (absmax / QMAX below half
+// the smallest subnormal) gets codes 0, as codec_code gives it.  Returns the
+// scale.
 template <int N, int QMAX = 127>
 __device__ __forceinline__ float codec_row(const float (&x)[N], float absmax, float (&c)[N]) {
   const float scale = codec_scale<QMAX>(absmax);
-  const float inv = absmax > 0.0f ? __fdiv_rn(float(QMAX), absmax) : 0.0f;
+  const float inv = scale > 0.0f ? __fdiv_rn(float(QMAX), absmax) : 0.0f;
   bool near = scale > 0.0f && scale < 1.17549435e-38f;  // subnormal: divide
 #pragma unroll
   for (int e = 0; e < N; ++e) {

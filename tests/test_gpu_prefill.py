@@ -69,6 +69,31 @@ def test_prefill_requantizes_subnormal_scale_rows():
     assert np.array_equal(host(sg), scales)
 
 
+def test_prefill_requantizes_rows_whose_scale_rounds_to_zero():
+    """A stored row with codes of at most 40 in magnitude and scale 2^-149
+    (the smallest subnormal) carried through one window with alpha = 1,
+    beta = 0: its values are unchanged, absmax / 127 is below half of 2^-149,
+    so the window-end scale rounds to 0 and every code must be 0 (the codec
+    reading: a row whose scale is 0 stores codes 0), as the oracle gives."""
+    B, H, d, T = 1, 2, 128, 64
+    x = wl.gdn_prefill(B=B, T=T, H=H, dk=d, dv=d, seed=33)
+    x["alpha"][:] = 1.0
+    x["beta"][:] = 0.0
+    S = (np.random.default_rng(34).standard_normal((B, H, d, d)) * 0.5).astype(np.float32)
+    codes, scales = O.quantize_rows(S)
+    rng = np.random.default_rng(35)
+    codes[0, 0, 7] = rng.integers(-40, 41, size=d).astype(np.int8)
+    codes[0, 0, 7, 3] = 40
+    scales[0, 0, 7] = np.float32(2.0 ** -149)
+    ref = O.prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], W=W, codes0=codes, scale0=scales)
+    assert ref["scale"][0, 0, 7] == 0.0 and not ref["codes"][0, 0, 7].any()
+    o, cg, sg = ops.prefill_chunked(*_inputs(x), init_codes=dev(codes), init_scales=dev(scales),
+                                    out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(cg), ref["codes"])
+    assert np.array_equal(host(sg), ref["scale"])
+
+
 @pytest.mark.parametrize("out_dt", [torch.float32, torch.bfloat16])
 def test_prefill_teacher_forced_chunks(out_dt):
     """B=2, H=3, four chunks, one chunk per call, each call from the GPU's
