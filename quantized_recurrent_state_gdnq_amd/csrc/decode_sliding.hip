@@ -240,17 +240,21 @@ __global__ __launch_bounds__(SL_THREADS, 3) void sliding_kernel(SlidingArgs a) {
   amax = group_max<TPR>(amax);
   const float scale = codec_scale(amax);
   {
+    // the reciprocal form of the codec (divisions only next to a rounding
+    // tie): the same codes as dividing every element, at a fraction of the
+    // instructions
     int8_t* dst = a.codes + row * DK + seg * CPT;
 #pragma unroll
-    for (int w4 = 0; w4 < CPT / 16; ++w4) {
+    for (int w4 = 0; w4 < CPT / 16; ++w4) {  // 16 columns at a time (one store)
+      float x[16], cf[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) x[c] = hv[16 * w4 + c];
+      codec_codes(x, scale, cf);
       uint4 u;
       uint32_t* uw = reinterpret_cast<uint32_t*>(&u);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int c0 = 16 * w4 + 4 * qq;
-        uw[qq] = pack4_i8(codec_code(hv[c0], scale), codec_code(hv[c0 + 1], scale), codec_code(hv[c0 + 2], scale),
-                          codec_code(hv[c0 + 3], scale));
-      }
+      for (int qq = 0; qq < 4; ++qq)
+        uw[qq] = pack4_i8(int(cf[4 * qq]), int(cf[4 * qq + 1]), int(cf[4 * qq + 2]), int(cf[4 * qq + 3]));
       *reinterpret_cast<uint4*>(dst + 16 * w4) = u;
     }
   }
