@@ -216,12 +216,12 @@ __global__ __launch_bounds__(SL_THREADS, 3) void sliding_kernel(SlidingArgs a) {
         for (int bb = 0; bb < 4; ++bb) hv[16 * w4 + 4 * qq + bb] = i8_at(ww[qq], bb);
     }
   }
-  // output: deq(H) . (A_t q) + sum_j c_j v_j[r] + c_t v_t[r]
+  // output: deq(H) . (A_t q) + sum_j c_j v_j[r] + c_t v_t[r]; both products
+  // on the codes, the row scale applied once to each sum
   float po = 0.f, hk = 0.f;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     po = fmaf(hv[c], y1[seg * CPT + c], po);
-    hv[c] *= s_old;  // the dequantized row
     hk = fmaf(hv[c], ks[seg * CPT + c], hk);
   }
   po *= s_old;
@@ -229,11 +229,14 @@ __global__ __launch_bounds__(SL_THREADS, 3) void sliding_kernel(SlidingArgs a) {
   po = group_sum<TPR>(po);
   hk = group_sum<TPR>(hk);
   const float v_t = (seg == 0) ? load_in<IN_BF16>(a.v, row) : 0.f;
-  // historical row through the transition, plus the leaving write; requantize
+  // historical row through the transition, plus the leaving write; requantize:
+  // alpha (s c - beta (h . k) k) + lw kl with h . k = s (c . k), the scale
+  // folded into the per-row factors
+  const float as = alpha_t * s_old, bk = alpha_t * beta_t * (s_old * hk);
   float amax = 0.f;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const float x = alpha_t * (hv[c] - beta_t * hk * ks[seg * CPT + c]) + lw * kl[seg * CPT + c];
+    const float x = fmaf(as, hv[c], fmaf(-bk, ks[seg * CPT + c], lw * kl[seg * CPT + c]));
     hv[c] = x;
     amax = fmaxf(amax, fabsf(x));
   }
