@@ -50,12 +50,13 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_kernel(const float* __rest
   constexpr int QMAX = QB == 8 ? 127 : 7;
   const float scale = codec_scale<QMAX>(amax);
   if (!valid) return;
+  float cf[E];  // the reciprocal form: the codes of one division per element
+  codec_codes<E, QMAX>(v, scale, cf);
   if constexpr (QB == 8) {
     uint32_t w[E / 4];
 #pragma unroll
     for (int i = 0; i < E / 4; ++i)
-      w[i] = pack4_i8(codec_code(v[4 * i], scale), codec_code(v[4 * i + 1], scale),
-                      codec_code(v[4 * i + 2], scale), codec_code(v[4 * i + 3], scale));
+      w[i] = pack4_i8(int(cf[4 * i]), int(cf[4 * i + 1]), int(cf[4 * i + 2]), int(cf[4 * i + 3]));
     int8_t* dst = codes + row * DK + li * E;
     if constexpr (E == 8) {
       *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_kernel(const float* __rest
   } else {  // E codes in E / 2 bytes
     int c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < E; ++i) c[i] = codec_code<QMAX>(v[i], scale);
+    for (int i = 0; i < E; ++i) c[i] = int(cf[i]);
     const uint32_t w = pack8_i4(c);
     int8_t* dst = codes + row * (DK / 2) + li * (E / 2);
     if constexpr (E == 8) {
